@@ -1,0 +1,263 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole layer (router, softmax, top-k, dispatch,
+expert SwiGLU FFN, combine) over one batch, through the C ABI (route ->
+dispatch -> expert_ffn -> combine on one stream, the same kernels that
+moe_layer_forward launches).  Inputs and weights are resident in HBM before the
+timed region.  The headline is the Mixtral-8x7B-shaped decode layer (T=8); the
+prefill layer (T=4096, Zipf-loaded experts) runs on the same weights and is
+reported in the same JSON line.
+
+Roofline: the dominant step is the expert FFN (the GEMV gate/up and down
+kernels at decode, the MFMA gate/up and down kernels at prefill).  Its time is
+measured live with HIP events recorded on the library's stream around the
+moe_expert_ffn call; its algorithmic bytes are the weight bytes of the experts
+actually hit (batch union) plus the activation traffic, its algorithmic flops
+2*3*T*k*d*F.
+
+CPU baseline: the fp64 oracle (oracle/, test infrastructure) timed on the
+host's cores on the full decode layer, repeated to ~10 s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import moe_inputs  # noqa: E402
+import moe_layer_forward_amd as moe  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/s at decode T=8 and prefill T=4096; % of HBM/MFMA roofline"
+DEV = "cuda"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def device_layer(cfg, seed=0, layer=0, shared_weights=None):
+    inp = moe_inputs.generate(cfg, seed=seed, device=DEV) if shared_weights is None else None
+    x = moe_inputs.activations(cfg, seed).to(DEV)
+    wr = moe_inputs.router_weights(cfg, seed, layer).to(DEV)
+    br = moe_inputs.router_bias(cfg)
+    br = None if br is None else br.to(DEV)
+    if shared_weights is not None:
+        W = shared_weights
+    else:
+        L = inp["layers"][layer]
+        W = {n: (None if L.get(n) is None else L[n].to(DEV)) for n in (
+            "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+            "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down")}
+    return x, wr, br, W
+
+
+class Runner:
+    """Buffers for one workload and the four C-ABI steps of the layer."""
+
+    def __init__(self, cfg, x, wr, br, W, tau=0):
+        self.cfg, self.x, self.wr, self.br, self.W = cfg, x, wr, br, W
+        T, E, k, d = cfg.T, cfg.E, cfg.k, cfg.d
+        self.shape = moe.make_shape(T, d, E, k, cfg.F, cfg.act, cfg.wt, cfg.n_shared, tau)
+        self.wstruct = moe.make_weights(**W)
+        self.ws = torch.empty(moe.moe_workspace_bytes(self.shape), dtype=torch.uint8, device=DEV)
+        act = torch.float32 if cfg.act == "f32" else torch.bfloat16
+        self.logits = torch.empty(T, E, dtype=torch.float32, device=DEV)
+        self.idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+        self.w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+        self.counts = torch.empty(E, dtype=torch.int32, device=DEV)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+        self.perm = torch.empty(T * k, dtype=torch.int32, device=DEV)
+        self.inv = torch.empty(T * k, dtype=torch.int32, device=DEV)
+        self.yp = torch.empty(T * k, d, dtype=torch.float32, device=DEV)
+        self.ys = torch.empty(T, d, dtype=torch.float32, device=DEV) if cfg.n_shared else None
+        self.y = torch.empty(T, d, dtype=act, device=DEV)
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, ev=None):
+        s = self.stream
+        moe.moe_route(self.shape, self.x, self.wr, self.br, self.logits, self.idx, self.w, stream=s)
+        moe.moe_dispatch(self.shape, self.idx, self.counts, self.offsets, self.perm, self.inv, stream=s)
+        if ev is not None:
+            ev[0].record(s)
+        moe.moe_expert_ffn(self.shape, self.x, self.wstruct, self.counts, self.offsets, self.perm,
+                           self.yp, self.ys, self.ws, stream=s)
+        if ev is not None:
+            ev[1].record(s)
+        moe.moe_combine(self.shape, self.yp, self.inv, self.w, self.ys, None, self.y, stream=s)
+
+    def layer_call(self):
+        moe.moe_layer_forward(self.shape, self.x, self.wr, self.br, self.wstruct, None, self.y,
+                              self.counts, self.idx, self.ws, stream=self.stream)
+
+    def timed(self, steps, warmup):
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ffn_ms = [a.elapsed_time(b) for a, b in evs]
+        # the single-call path, timed the same way (same kernels)
+        t1 = time.perf_counter()
+        for _ in range(steps):
+            self.layer_call()
+        torch.cuda.synchronize()
+        wall_layer = time.perf_counter() - t1
+        return wall, float(np.mean(ffn_ms)), float(np.median(ffn_ms)), wall_layer
+
+    def ffn_algorithmic(self):
+        """Bytes and flops of one moe_expert_ffn call (batch union of weights)."""
+        cfg = self.cfg
+        c = self.counts.cpu().numpy()
+        U = int((c > 0).sum())
+        tk = cfg.T * cfg.k
+        if cfg.wt == "int4":
+            mat = cfg.F * cfg.d // 2 + cfg.F * (cfg.d // 128) * 2
+        else:
+            mat = cfg.F * cfg.d * (4 if cfg.wt == "f32" else 2)
+        ab = 4 if cfg.act == "f32" else 2
+        w_bytes = (U + cfg.n_shared) * 3 * mat
+        act_bytes = (tk * cfg.d * ab              # gathered x rows
+                     + 2 * tk * cfg.F * ab         # h written then read
+                     + tk * cfg.d * 4)             # y_perm written
+        if cfg.n_shared:
+            act_bytes += cfg.T * cfg.d * ab + 2 * cfg.T * cfg.F * ab + cfg.T * cfg.d * 4
+        flops = 2 * 3 * (tk + cfg.n_shared * cfg.T) * cfg.d * cfg.F
+        return U, w_bytes + act_bytes, flops
+
+
+def cpu_baseline(cfg, runner, target_s=10.0):
+    """The oracle timed on the host's cores on the full layer (all T tokens)."""
+    import oracle
+    oracle.build(force=False)
+
+    def st(t):
+        if t is None:
+            return None
+        t = t.detach().cpu().contiguous()
+        if t.dtype in (torch.bfloat16, torch.float16):
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    W = {n: st(runner.W[n]) for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")}
+    S = None
+    if cfg.n_shared:
+        S = {"w_gate": st(runner.W["sh_gate"]), "w_up": st(runner.W["sh_up"]),
+             "w_down": st(runner.W["sh_down"]), "s_gate": st(runner.W["sh_s_gate"]),
+             "s_up": st(runner.W["sh_s_up"]), "s_down": st(runner.W["sh_s_down"])}
+    x, wr, br = st(runner.x), st(runner.wr), st(runner.br)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.layer_forward(x, cfg.act, cfg.wt, cfg.k, wr, br, W, S)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 50:
+            break
+    return {"value": reps * cfg.T / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{cfg.name}: full layer, all {cfg.T} tokens, fp64, repeated {reps}x "
+                      f"({el:.1f} s)"}
+
+
+def roofline_obj(bound, achieved, peak, unit, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral_decode",
+                    choices=["mixtral_decode", "fine_int4_decode", "stack4_layer0"])
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tau", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is built for a single MI355X; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    moe.lib()   # fail loudly if the HIP library is not built
+
+    name = "stack4" if args.workload == "stack4_layer0" else args.workload
+    cfg = moe_inputs.CONFIGS[name]
+    if cfg.layers > 1:
+        cfg = cfg.replace(layers=1)
+    log(f"generating {cfg.name} inputs on the GPU")
+    x, wr, br, W = device_layer(cfg)
+    run = Runner(cfg, x, wr, br, W, tau=args.tau)
+    log(f"timing {cfg.name}: warmup {args.warmup}, steps {args.steps}")
+    wall, ffn_mean, ffn_med, wall_layer = run.timed(args.steps, args.warmup)
+    U, ffn_bytes, ffn_flops = run.ffn_algorithmic()
+    ms = wall * 1e3 / args.steps
+    value = cfg.T * args.steps / wall
+    achieved = ffn_bytes / (ffn_mean * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.act == "bf16" and cfg.wt == "bf16" else
+                 ("bf16/int4" if cfg.wt == "int4" else "f32"),
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
+                   "F": cfg.F, "weights": cfg.wt, "shared_experts": cfg.n_shared,
+                   "active_experts": U, "tau": args.tau, "seed": 0},
+        "roofline": dict(roofline_obj("hbm", achieved, HBM_PEAK_GBS, "GB/s"),
+                         kernel="expert FFN step (gate/up + down GEMV)",
+                         bytes_per_launch=ffn_bytes, launch_ms=round(ffn_mean, 5),
+                         launch_ms_median=round(ffn_med, 5)),
+        "layer_call_ms_per_step": round(wall_layer * 1e3 / args.steps, 4),
+    }
+    log(json.dumps(out))
+
+    if not args.no_prefill and cfg.name == "mixtral_decode":
+        pcfg = moe_inputs.CONFIGS["mixtral_prefill"]
+        log("prefill T=4096 on the same weights")
+        px, pwr, pbr, _ = device_layer(pcfg, shared_weights=W)
+        prun = Runner(pcfg, px, pwr, pbr, W, tau=args.tau)
+        psteps = max(5, args.steps // 5)
+        pwall, pffn_mean, pffn_med, pwall_layer = prun.timed(psteps, max(2, args.warmup // 2))
+        _, pbytes, pflops = prun.ffn_algorithmic()
+        ptf = pflops / (pffn_mean * 1e-3) / 1e12
+        out["prefill"] = {
+            "workload": pcfg.name, "T": pcfg.T, "value": round(pcfg.T * psteps / pwall, 1),
+            "unit": "tokens/s", "ms_per_step": round(pwall * 1e3 / psteps, 4), "steps": psteps,
+            "counts": prun.counts.cpu().tolist(),
+            "roofline": dict(roofline_obj("mfma", ptf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
+                             kernel="expert FFN step (MFMA gate/up + down)",
+                             flops_per_launch=pflops, launch_ms=round(pffn_mean, 4)),
+            "layer_call_ms_per_step": round(pwall_layer * 1e3 / psteps, 4),
+        }
+        log(json.dumps(out["prefill"]))
+        del prun, px
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(cfg, run)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,407 @@
+// extern "C" entry points of libmoe.so: argument validation, workspace carving
+// and the launch sequence of the layer.  Declared and documented in moe.h.
+//
+// Conventions follow [P4] "Colibri：轻量级MoE推理引擎的C语言实践" §3.3 (int status,
+// negative on error, caller-provided message buffer) and §3.2 (no allocation
+// during inference); the fixed scratch budget computed up front follows [P3]
+// (wzjinhao.cn) §2.3.  Validation runs before any HIP call, so a rejected call
+// has enqueued nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "common.h"
+#include "kernels.h"
+#include "moe.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kDefaultTau = 16;
+constexpr size_t kAlign = 256;
+
+int fail(char* err, size_t len, int code, const char* fmt, ...) {
+    if (err && len > 0) {
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(err, len, fmt, ap);
+        va_end(ap);
+    }
+    return code;
+}
+
+bool debug_sync() {
+    static int v = -1;
+    if (v < 0) {
+        const char* e = getenv("MOE_DEBUG_SYNC");
+        v = (e && e[0] && e[0] != '0') ? 1 : 0;
+    }
+    return v == 1;
+}
+
+int hip_check(hipError_t e, hipStream_t s, const char* what, char* err, size_t len) {
+    if (e != hipSuccess)
+        return fail(err, len, MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+    if (debug_sync()) {
+        e = hipStreamSynchronize(s);
+        if (e == hipSuccess) e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(err, len, MOE_EHIP, "%s (MOE_DEBUG_SYNC): %s", what, hipGetErrorString(e));
+    }
+    return MOE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define NEED_PTR(p, name)                                                                 \
+    do {                                                                                  \
+        if (!(p)) return fail(err, err_len, MOE_EINVAL, "%s is NULL", name);              \
+        if (!aligned16(p)) return fail(err, err_len, MOE_EINVAL, "%s is not 16-byte aligned", name); \
+    } while (0)
+#define OPT_PTR(p, name)                                                                  \
+    do {                                                                                  \
+        if ((p) && !aligned16(p))                                                         \
+            return fail(err, err_len, MOE_EINVAL, "%s is not 16-byte aligned", name);      \
+    } while (0)
+
+int check_shape(const moe_shape* s, char* err, size_t err_len) {
+    if (!s) return fail(err, err_len, MOE_EINVAL, "shape is NULL");
+    if (s->T < 0 || s->T > (1 << 24)) return fail(err, err_len, MOE_EINVAL, "T=%d out of range [0, 2^24]", s->T);
+    if (s->E < 1 || s->E > 256) return fail(err, err_len, MOE_EINVAL, "E=%d out of range [1, 256]", s->E);
+    if (s->k < 1 || s->k > s->E || s->k > 16)
+        return fail(err, err_len, MOE_EINVAL, "k=%d must satisfy 1 <= k <= min(E, 16) (E=%d)", s->k, s->E);
+    if (s->d < 8 || s->d % 8) return fail(err, err_len, MOE_EINVAL, "d=%d must be a positive multiple of 8", s->d);
+    if (s->F < 8 || s->F % 8) return fail(err, err_len, MOE_EINVAL, "F=%d must be a positive multiple of 8", s->F);
+    if (s->n_shared != 0 && s->n_shared != 1)
+        return fail(err, err_len, MOE_EINVAL, "n_shared=%d must be 0 or 1", s->n_shared);
+    if (s->act != MOE_F32 && s->act != MOE_BF16)
+        return fail(err, err_len, MOE_EINVAL, "act=%d is not MOE_F32 or MOE_BF16", s->act);
+    if (s->wt != MOE_F32 && s->wt != MOE_BF16 && s->wt != MOE_INT4_G128)
+        return fail(err, err_len, MOE_EINVAL, "wt=%d is not a moe_dtype", s->wt);
+    if (s->wt == MOE_INT4_G128 && (s->d % 128 || s->F % 128))
+        return fail(err, err_len, MOE_EINVAL, "int4-g128 weights need d and F multiples of 128 (d=%d F=%d)",
+                    s->d, s->F);
+    const bool ok_combo = (s->act == MOE_F32 && s->wt == MOE_F32) ||
+                          (s->act == MOE_BF16 && (s->wt == MOE_BF16 || s->wt == MOE_INT4_G128));
+    if (!ok_combo)
+        return fail(err, err_len, MOE_EUNSUPPORTED, "activation dtype %d with weight dtype %d is not built",
+                    s->act, s->wt);
+    const int kmax = gemv_max_k(s->wt);
+    if (s->d > kmax || s->F > kmax)
+        return fail(err, err_len, MOE_EUNSUPPORTED, "d=%d / F=%d exceed this build's limit %d for this dtype",
+                    s->d, s->F, kmax);
+    return MOE_OK;
+}
+
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t logits, idx, w, counts, offsets, perm, inv, tiles, h, yp, hs, ys, total;
+};
+
+Layout layout(const moe_shape* s) {
+    const size_t T = s->T, k = s->k, E = s->E, d = s->d, F = s->F;
+    const size_t hb = (s->act == MOE_F32) ? 4 : 2;
+    const size_t tk = T * k;
+    const size_t max_mt = (size_t)mfma_max_tiles(s->T, s->k, s->E);
+    Layout L;
+    size_t o = 0;
+    L.logits = o; o += up(T * E * 4);
+    L.idx = o; o += up(tk * 4);
+    L.w = o; o += up(tk * 4);
+    L.counts = o; o += up(E * 4);
+    L.offsets = o; o += up((E + 1) * 4);
+    L.perm = o; o += up(tk * 4);
+    L.inv = o; o += up(tk * 4);
+    L.tiles = o; o += up((3 * max_mt + 1) * 4);
+    L.h = o; o += up(tk * F * hb);
+    L.yp = o; o += up(tk * d * 4);
+    L.hs = o; o += s->n_shared ? up(T * F * hb) : 0;
+    L.ys = o; o += s->n_shared ? up(T * d * 4) : 0;
+    L.total = o;
+    return L;
+}
+
+int effective_tau(const moe_shape* s) {
+    if (s->wt != MOE_BF16) return -1;      // fp32 and int4: GEMV for every group
+    if (s->tau < 0) return -1;
+    return s->tau == 0 ? kDefaultTau : s->tau;
+}
+
+int rows_per_block(int N, int E, int T, int k) {
+    const int active = (T * k < E) ? T * k : E;
+    const long target = 2048;
+    long r = ((long)N * active + target - 1) / target;
+    if (r < 8) r = 8;
+    if (r > 256) r = 256;
+    return (int)((r + 7) / 8 * 8);
+}
+
+// The FFN launch sequence shared by moe_expert_ffn and moe_layer_forward.
+int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32_t* counts,
+            const int32_t* offsets, const int32_t* perm, float* y_perm, float* y_shared,
+            char* ws, hipStream_t st, char* err, size_t err_len) {
+    const Layout L = layout(s);
+    const int tau = effective_tau(s);
+    const bool use_mfma = tau >= 0 && s->T > tau;
+    void* h = ws + L.h;
+    int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+    const int max_mt = mfma_max_tiles(s->T, s->k, s->E);
+    const int max_rows_gemv = use_mfma ? tau : s->T;   // a group holds at most T rows
+    int rc;
+
+    if (s->T == 0) return MOE_OK;
+    if (use_mfma) {
+        rc = hip_check(launch_mfma_plan(counts, offsets, s->E, tau, tiles, max_mt, st), st,
+                       "mfma plan", err, err_len);
+        if (rc) return rc;
+    }
+    GemvArgs g{};
+    g.counts = counts;
+    g.offsets = offsets;
+    g.perm = perm;
+    g.topk = s->k;
+    g.T = s->T;
+    g.tau = use_mfma ? tau : -1;
+
+    // gate/up + SwiGLU
+    g.w0 = w->w_gate; g.w1 = w->w_up;
+    g.s0 = (const uint16_t*)w->s_gate; g.s1 = (const uint16_t*)w->s_up;
+    g.in = x; g.out = h; g.N = s->F; g.K = s->d;
+    g.rows_per_block = rows_per_block(g.N, s->E, s->T, s->k);
+    rc = hip_check(launch_gemv(s->wt, s->act, 0, g, s->E, max_rows_gemv, st), st, "gemv gate/up", err, err_len);
+    if (rc) return rc;
+    if (use_mfma) {
+        rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, st),
+                       st, "mfma gate/up", err, err_len);
+        if (rc) return rc;
+    }
+    // down
+    g.w0 = w->w_down; g.w1 = nullptr;
+    g.s0 = (const uint16_t*)w->s_down; g.s1 = nullptr;
+    g.in = h; g.out = y_perm; g.N = s->d; g.K = s->F;
+    g.rows_per_block = rows_per_block(g.N, s->E, s->T, s->k);
+    rc = hip_check(launch_gemv(s->wt, s->act, 1, g, s->E, max_rows_gemv, st), st, "gemv down", err, err_len);
+    if (rc) return rc;
+    if (use_mfma) {
+        rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, st),
+                       st, "mfma down", err, err_len);
+        if (rc) return rc;
+    }
+    // shared expert: one expert over all T rows
+    if (s->n_shared) {
+        void* hs = ws + L.hs;
+        GemvArgs q{};
+        q.counts = nullptr; q.offsets = nullptr; q.perm = nullptr;
+        q.topk = 1; q.T = s->T; q.tau = -1;
+        q.w0 = w->sh_gate; q.w1 = w->sh_up;
+        q.s0 = (const uint16_t*)w->sh_s_gate; q.s1 = (const uint16_t*)w->sh_s_up;
+        q.in = x; q.out = hs; q.N = s->F; q.K = s->d;
+        q.rows_per_block = rows_per_block(q.N, 1, 1, 1);
+        rc = hip_check(launch_gemv(s->wt, s->act, 0, q, 1, s->T, st), st, "gemv shared gate/up", err, err_len);
+        if (rc) return rc;
+        q.w0 = w->sh_down; q.w1 = nullptr;
+        q.s0 = (const uint16_t*)w->sh_s_down; q.s1 = nullptr;
+        q.in = hs; q.out = y_shared; q.N = s->d; q.K = s->F;
+        q.rows_per_block = rows_per_block(q.N, 1, 1, 1);
+        rc = hip_check(launch_gemv(s->wt, s->act, 1, q, 1, s->T, st), st, "gemv shared down", err, err_len);
+        if (rc) return rc;
+    }
+    return MOE_OK;
+}
+
+int check_weights(const moe_shape* s, const moe_weights* w, char* err, size_t err_len) {
+    if (!w) return fail(err, err_len, MOE_EINVAL, "weights is NULL");
+    NEED_PTR(w->w_gate, "w_gate");
+    NEED_PTR(w->w_up, "w_up");
+    NEED_PTR(w->w_down, "w_down");
+    if (s->wt == MOE_INT4_G128) {
+        NEED_PTR(w->s_gate, "s_gate");
+        NEED_PTR(w->s_up, "s_up");
+        NEED_PTR(w->s_down, "s_down");
+    }
+    if (s->n_shared) {
+        NEED_PTR(w->sh_gate, "sh_gate");
+        NEED_PTR(w->sh_up, "sh_up");
+        NEED_PTR(w->sh_down, "sh_down");
+        if (s->wt == MOE_INT4_G128) {
+            NEED_PTR(w->sh_s_gate, "sh_s_gate");
+            NEED_PTR(w->sh_s_up, "sh_s_up");
+            NEED_PTR(w->sh_s_down, "sh_s_down");
+        }
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_ENOMEM: return "workspace too small";
+        case MOE_EHIP: return "HIP error";
+        case MOE_EUNSUPPORTED: return "unsupported by this build";
+        default: return "unknown status";
+    }
+}
+
+size_t moe_workspace_bytes(const moe_shape* shape) {
+    if (check_shape(shape, nullptr, 0) != MOE_OK) return 0;
+    return layout(shape).total;
+}
+
+int moe_route(const moe_shape* shape, const void* x, const float* w_router, const float* b_router,
+              float* logits, int32_t* topk_idx, float* topk_w, void* stream, char* err, size_t err_len) {
+    int rc = check_shape(shape, err, err_len);
+    if (rc) return rc;
+    if (shape->T > 0) {
+        NEED_PTR(x, "x");
+        NEED_PTR(w_router, "w_router");
+        NEED_PTR(logits, "logits");
+        NEED_PTR(topk_idx, "topk_idx");
+        NEED_PTR(topk_w, "topk_w");
+    }
+    OPT_PTR(b_router, "b_router");
+    hipStream_t st = (hipStream_t)stream;
+    return hip_check(launch_route(shape->act, x, w_router, b_router, logits, topk_idx, topk_w, shape->T,
+                                  shape->d, shape->E, shape->k, st),
+                     st, "route", err, err_len);
+}
+
+int moe_dispatch(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                 int32_t* perm, int32_t* inv, void* stream, char* err, size_t err_len) {
+    int rc = check_shape(shape, err, err_len);
+    if (rc) return rc;
+    NEED_PTR(counts, "counts");
+    NEED_PTR(offsets, "offsets");
+    if (shape->T > 0) {
+        NEED_PTR(topk_idx, "topk_idx");
+        NEED_PTR(perm, "perm");
+        NEED_PTR(inv, "inv");
+    }
+    hipStream_t st = (hipStream_t)stream;
+    return hip_check(launch_dispatch(topk_idx, counts, offsets, perm, inv, shape->T, shape->k, shape->E, st),
+                     st, "dispatch", err, err_len);
+}
+
+int moe_expert_ffn(const moe_shape* shape, const void* x, const moe_weights* w, const int32_t* counts,
+                   const int32_t* offsets, const int32_t* perm, float* y_perm, float* y_shared, void* ws,
+                   size_t ws_bytes, void* stream, char* err, size_t err_len) {
+    int rc = check_shape(shape, err, err_len);
+    if (rc) return rc;
+    rc = check_weights(shape, w, err, err_len);
+    if (rc) return rc;
+    if (shape->T > 0) {
+        NEED_PTR(x, "x");
+        NEED_PTR(counts, "counts");
+        NEED_PTR(offsets, "offsets");
+        NEED_PTR(perm, "perm");
+        NEED_PTR(y_perm, "y_perm");
+        if (shape->n_shared) NEED_PTR(y_shared, "y_shared");
+    }
+    const size_t need = layout(shape).total;
+    if (!ws || ws_bytes < need)
+        return fail(err, err_len, MOE_ENOMEM, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+    if (((uintptr_t)ws & (kAlign - 1)) != 0)
+        return fail(err, err_len, MOE_EINVAL, "workspace is not 256-byte aligned");
+    return run_ffn(shape, x, w, counts, offsets, perm, y_perm, y_shared, (char*)ws, (hipStream_t)stream, err,
+                   err_len);
+}
+
+int moe_combine(const moe_shape* shape, const float* y_perm, const int32_t* inv, const float* topk_w,
+                const float* y_shared, const void* residual, void* y, void* stream, char* err,
+                size_t err_len) {
+    int rc = check_shape(shape, err, err_len);
+    if (rc) return rc;
+    if (shape->T > 0) {
+        NEED_PTR(y_perm, "y_perm");
+        NEED_PTR(inv, "inv");
+        NEED_PTR(topk_w, "topk_w");
+        NEED_PTR(y, "y");
+    }
+    OPT_PTR(y_shared, "y_shared");
+    OPT_PTR(residual, "residual");
+    hipStream_t st = (hipStream_t)stream;
+    return hip_check(launch_combine(shape->act, y_perm, inv, topk_w, y_shared, residual, y, shape->T, shape->d,
+                                    shape->k, st),
+                     st, "combine", err, err_len);
+}
+
+int moe_layer_forward(const moe_shape* shape, const void* x, const float* w_router, const float* b_router,
+                      const moe_weights* w, const void* residual, void* y, int32_t* counts_out,
+                      int32_t* topk_idx_out, void* ws, size_t ws_bytes, void* stream, char* err,
+                      size_t err_len) {
+    int rc = check_shape(shape, err, err_len);
+    if (rc) return rc;
+    rc = check_weights(shape, w, err, err_len);
+    if (rc) return rc;
+    if (shape->T > 0) {
+        NEED_PTR(x, "x");
+        NEED_PTR(w_router, "w_router");
+        NEED_PTR(y, "y");
+    }
+    OPT_PTR(b_router, "b_router");
+    OPT_PTR(residual, "residual");
+    OPT_PTR(counts_out, "counts_out");
+    OPT_PTR(topk_idx_out, "topk_idx_out");
+    const Layout L = layout(shape);
+    if (!ws || ws_bytes < L.total)
+        return fail(err, err_len, MOE_ENOMEM, "workspace of %zu bytes needed, %zu given", L.total,
+                    ws ? ws_bytes : 0);
+    if (((uintptr_t)ws & (kAlign - 1)) != 0)
+        return fail(err, err_len, MOE_EINVAL, "workspace is not 256-byte aligned");
+
+    char* W = (char*)ws;
+    hipStream_t st = (hipStream_t)stream;
+    float* logits = (float*)(W + L.logits);
+    int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)(W + L.idx);
+    float* gw = (float*)(W + L.w);
+    int32_t* counts = counts_out ? counts_out : (int32_t*)(W + L.counts);
+    int32_t* offsets = (int32_t*)(W + L.offsets);
+    int32_t* perm = (int32_t*)(W + L.perm);
+    int32_t* inv = (int32_t*)(W + L.inv);
+    float* yp = (float*)(W + L.yp);
+    float* ys = shape->n_shared ? (float*)(W + L.ys) : nullptr;
+
+    if (shape->T == 0) {
+        // no tokens: the usage histogram is all zero
+        return hip_check(launch_dispatch(idx, counts, offsets, perm, inv, 0, shape->k, shape->E, st), st,
+                         "dispatch", err, err_len);
+    }
+    rc = hip_check(launch_route(shape->act, x, w_router, b_router, logits, idx, gw, shape->T, shape->d, shape->E,
+                                shape->k, st),
+                   st, "route", err, err_len);
+    if (rc) return rc;
+    rc = hip_check(launch_dispatch(idx, counts, offsets, perm, inv, shape->T, shape->k, shape->E, st), st,
+                   "dispatch", err, err_len);
+    if (rc) return rc;
+    rc = run_ffn(shape, x, w, counts, offsets, perm, yp, ys, W, st, err, err_len);
+    if (rc) return rc;
+    return hip_check(launch_combine(shape->act, yp, inv, gw, ys, residual, y, shape->T, shape->d, shape->k, st),
+                     st, "combine", err, err_len);
+}
+
+int moe_rmsnorm(const moe_shape* shape, const void* h, const float* gamma, float eps, void* out, void* stream,
+                char* err, size_t err_len) {
+    if (!shape) return fail(err, err_len, MOE_EINVAL, "shape is NULL");
+    if (shape->T < 0 || shape->d < 8 || shape->d % 8)
+        return fail(err, err_len, MOE_EINVAL, "T=%d d=%d: need T >= 0 and d a positive multiple of 8", shape->T,
+                    shape->d);
+    if (shape->act != MOE_F32 && shape->act != MOE_BF16)
+        return fail(err, err_len, MOE_EINVAL, "act=%d is not MOE_F32 or MOE_BF16", shape->act);
+    if (!(eps >= 0.0f)) return fail(err, err_len, MOE_EINVAL, "eps must be >= 0");
+    if (shape->T > 0) {
+        NEED_PTR(h, "h");
+        NEED_PTR(out, "out");
+    }
+    OPT_PTR(gamma, "gamma");
+    hipStream_t st = (hipStream_t)stream;
+    return hip_check(launch_rmsnorm(shape->act, h, gamma, eps, out, shape->T, shape->d, st), st, "rmsnorm", err,
+                     err_len);
+}
+
+}  // extern "C"

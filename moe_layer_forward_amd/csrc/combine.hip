@@ -1,0 +1,112 @@
+// Weighted combine back into token order, and the RMSNorm of the stacked layers.
+//
+// [P1] "Colibri：专为MoE模型优化的纯C高性能推理引擎" §2.1: the experts' outputs are
+// merged with the gate weights.  [P4] "Colibri：轻量级MoE推理引擎的C语言实践" §2.3:
+// the K slot results are merged back in the original token order.
+//
+// gfx950 design: a gather-reduce, never float atomics.  One 256-thread block
+// per token reads that token's k rows of y_perm through the inverse
+// permutation with 16-byte loads, sums them in slot order j = 0..k-1 in fp32
+// (plus the shared-expert row and the residual), and writes the output row
+// once.  The result is bit-identical run to run.  HBM-bound: k*d*4 bytes read
+// and d*2 (bf16) written per token.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+template <int ACT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ yp,
+                                                     const int32_t* __restrict__ inv,
+                                                     const float* __restrict__ w,
+                                                     const float* __restrict__ ys,
+                                                     const void* __restrict__ res,
+                                                     void* __restrict__ y, int d, int k) {
+    const int t = blockIdx.x;
+    __shared__ int s_row[16];
+    __shared__ float s_w[16];
+    if (threadIdx.x < k) {
+        s_row[threadIdx.x] = inv[(size_t)t * k + threadIdx.x];
+        s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < k; ++j) {
+            const float4 v = *reinterpret_cast<const float4*>(yp + (size_t)s_row[j] * d + i);
+            const float wj = s_w[j];
+            acc.x = fmaf(wj, v.x, acc.x);
+            acc.y = fmaf(wj, v.y, acc.y);
+            acc.z = fmaf(wj, v.z, acc.z);
+            acc.w = fmaf(wj, v.w, acc.w);
+        }
+        if (ys) {
+            const float4 v = *reinterpret_cast<const float4*>(ys + (size_t)t * d + i);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        if constexpr (ACT == DT_F32) {
+            if (res) {
+                const float4 r = *reinterpret_cast<const float4*>(
+                    reinterpret_cast<const float*>(res) + (size_t)t * d + i);
+                acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
+            }
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)t * d + i) = acc;
+        } else {
+            if (res) {
+                const uint2 r = *reinterpret_cast<const uint2*>(
+                    reinterpret_cast<const uint16_t*>(res) + (size_t)t * d + i);
+                acc.x += bf16_lo(r.x); acc.y += bf16_hi(r.x); acc.z += bf16_lo(r.y); acc.w += bf16_hi(r.y);
+            }
+            uint2 o;
+            o.x = pack_bf16x2(acc.x, acc.y);
+            o.y = pack_bf16x2(acc.z, acc.w);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + (size_t)t * d + i) = o;
+        }
+    }
+}
+
+hipError_t launch_combine(int act, const float* yp, const int32_t* inv, const float* w,
+                          const float* ys, const void* res, void* y, int T, int d, int k,
+                          hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (act == DT_F32)
+        hipLaunchKernelGGL(combine_kernel<DT_F32>, dim3(T), dim3(256), 0, s, yp, inv, w, ys, res, y, d, k);
+    else
+        hipLaunchKernelGGL(combine_kernel<DT_BF16>, dim3(T), dim3(256), 0, s, yp, inv, w, ys, res, y, d, k);
+    return hipGetLastError();
+}
+
+// RMSNorm: out = h / sqrt(mean(h^2) + eps) * gamma, fp32 math.
+template <int ACT>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ h,
+                                                     const float* __restrict__ gamma, float eps,
+                                                     void* __restrict__ out, int d) {
+    const int t = blockIdx.x;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < d; i += 256) {
+        const float v = load_act<ACT>(h, (size_t)t * d + i);
+        ss = fmaf(v, v, ss);
+    }
+    ss = wave_sum(ss);
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = part[0] + part[1] + part[2] + part[3];
+    const float r = 1.0f / sqrtf(tot / (float)d + eps);
+    for (int i = threadIdx.x; i < d; i += 256) {
+        const float v = load_act<ACT>(h, (size_t)t * d + i);
+        store_act<ACT>(out, (size_t)t * d + i, v * r * (gamma ? gamma[i] : 1.0f));
+    }
+}
+
+hipError_t launch_rmsnorm(int act, const void* h, const float* gamma, float eps, void* out, int T,
+                          int d, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (act == DT_F32)
+        hipLaunchKernelGGL(rmsnorm_kernel<DT_F32>, dim3(T), dim3(256), 0, s, h, gamma, eps, out, d);
+    else
+        hipLaunchKernelGGL(rmsnorm_kernel<DT_BF16>, dim3(T), dim3(256), 0, s, h, gamma, eps, out, d);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,45 @@
+// Internal launchers of libmoe.so (host side).  Each returns the HIP error of
+// its launch; none synchronises.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Arguments of the streaming GEMV (ffn_gemv.hip).
+struct GemvArgs {
+    const void* w0;          // gate (mode 0) or down (mode 1) weights, [E][N][K]
+    const void* w1;          // up weights (mode 0), else null
+    const uint16_t* s0;      // fp16 group scales of w0 (int4)
+    const uint16_t* s1;
+    const void* in;          // x [T][K] (mode 0) or h [T*k][K] (mode 1)
+    void* out;               // h [T*k][N] (mode 0) or y_perm fp32 [T*k][N] (mode 1)
+    const int32_t* counts;   // null: shared expert, all T rows, expert 0
+    const int32_t* offsets;
+    const int32_t* perm;     // mode 0 only: token = perm[p] / topk
+    int N, K, topk, T, tau, rows_per_block;
+};
+
+hipError_t launch_route(int act, const void* x, const float* wg, const float* b, float* logits,
+                        int32_t* idx, float* w, int T, int d, int E, int k, hipStream_t s);
+hipError_t launch_dispatch(const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int32_t* inv, int T, int k, int E, hipStream_t s);
+hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, int max_rows,
+                       hipStream_t s);
+int gemv_max_k(int wt);
+int mfma_bm();
+int mfma_max_tiles(int T, int k, int E);
+int mfma_ntiles_n(int mode, int N);
+hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int E, int tau,
+                            int32_t* tiles, int max_mt, hipStream_t s);
+hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void* in, void* out,
+                           const int32_t* perm, const int32_t* tiles, int N, int K, int topk,
+                           int max_mt, hipStream_t s);
+hipError_t launch_combine(int act, const float* yp, const int32_t* inv, const float* w,
+                          const float* ys, const void* res, void* y, int T, int d, int k,
+                          hipStream_t s);
+hipError_t launch_rmsnorm(int act, const void* h, const float* gamma, float eps, void* out, int T,
+                          int d, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,187 @@
+// Router logits, softmax over experts and top-k with renormalised gate weights.
+//
+// [P1] "Colibri：专为MoE模型优化的纯C高性能推理引擎" §2.1: the gating network is a
+// linear layer followed by softmax; the top-2 expert indices are kept and their
+// gate weights renormalised.  §3.2: one gating kernel per token, a warp-level
+// shuffle reduction, maximum first then the runner-up.  [P3] (wzjinhao.cn)
+// §3.2: softmax(x W + b) with the maximum subtracted first.
+//
+// gfx950 design: the logits are a skinny [T,d]x[d,E] contraction that is at
+// most ~1% of the layer, so it runs on the VALU: a 256-thread block owns
+// 8 tokens x 4 experts, its threads split K in 4-element chunks, and the 32
+// per-lane partial sums are folded with a transposing wave reduction (32
+// shuffles instead of 192) before a cross-wave sum in LDS.  Top-k then runs
+// one wave64 per token: each lane holds up to 4 logits, and k rounds of a
+// shuffle argmax (value descending, expert index ascending on ties) pick the
+// experts.  Selection is made on the fp32 logits (softmax is monotone); the
+// weights are the softmax of the selected logits, which equals the full
+// softmax renormalised over the selection.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// Transposing reduction of N per-lane values over the 64 lanes.  Afterwards
+// lane l holds the wave total of value index (l >> (6 - log2 N)).
+template <int N>
+__device__ __forceinline__ float wave_reduce_multi(float (&v)[N], int lane) {
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N power of two");
+    int n = N;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        if (n > 1) {
+            const bool up = (lane & o) != 0;
+#pragma unroll
+            for (int i = 0; i < N / 2; ++i) {
+                if (i < n / 2) {
+                    float send = up ? v[i] : v[i + n / 2];
+                    float keep = up ? v[i + n / 2] : v[i];
+                    v[i] = keep + __shfl_xor(send, o, MOE_WAVE);
+                }
+            }
+            n >>= 1;
+        } else {
+            v[0] += __shfl_xor(v[0], o, MOE_WAVE);
+        }
+    }
+    return v[0];
+}
+
+constexpr int RT_TOK = 8;
+constexpr int RT_EXP = 4;
+constexpr int RT_THREADS = 256;
+
+template <int ACT>
+__global__ __launch_bounds__(RT_THREADS) void router_logits_kernel(
+    const void* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
+    float* __restrict__ logits, int T, int d, int E) {
+    const int t0 = blockIdx.x * RT_TOK;
+    const int e0 = blockIdx.y * RT_EXP;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    float acc[RT_TOK * RT_EXP];
+#pragma unroll
+    for (int i = 0; i < RT_TOK * RT_EXP; ++i) acc[i] = 0.f;
+
+    for (int kk = tid * 4; kk < d; kk += RT_THREADS * 4) {
+        float4 wv[RT_EXP];
+#pragma unroll
+        for (int e = 0; e < RT_EXP; ++e) {
+            if (e0 + e < E) wv[e] = *reinterpret_cast<const float4*>(wg + (size_t)(e0 + e) * d + kk);
+            else wv[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int t = 0; t < RT_TOK; ++t) {
+            if (t0 + t >= T) break;
+            float xv[4];
+            if constexpr (ACT == DT_F32) {
+                float4 q = *reinterpret_cast<const float4*>(
+                    reinterpret_cast<const float*>(x) + (size_t)(t0 + t) * d + kk);
+                xv[0] = q.x; xv[1] = q.y; xv[2] = q.z; xv[3] = q.w;
+            } else {
+                uint2 q = *reinterpret_cast<const uint2*>(
+                    reinterpret_cast<const uint16_t*>(x) + (size_t)(t0 + t) * d + kk);
+                xv[0] = bf16_lo(q.x); xv[1] = bf16_hi(q.x); xv[2] = bf16_lo(q.y); xv[3] = bf16_hi(q.y);
+            }
+#pragma unroll
+            for (int e = 0; e < RT_EXP; ++e) {
+                float a = acc[t * RT_EXP + e];
+                a = fmaf(xv[0], wv[e].x, a);
+                a = fmaf(xv[1], wv[e].y, a);
+                a = fmaf(xv[2], wv[e].z, a);
+                a = fmaf(xv[3], wv[e].w, a);
+                acc[t * RT_EXP + e] = a;
+            }
+        }
+    }
+    // fold 32 partials over the wave: lane l owns output index l >> 1
+    float r = wave_reduce_multi<RT_TOK * RT_EXP>(acc, lane);
+    __shared__ float part[RT_THREADS / 64][RT_TOK * RT_EXP];
+    if ((lane & 1) == 0) part[wave][lane >> 1] = r;
+    __syncthreads();
+    if (tid < RT_TOK * RT_EXP) {
+        const int t = tid / RT_EXP, e = tid % RT_EXP;
+        float s = part[0][tid];
+#pragma unroll
+        for (int w = 1; w < RT_THREADS / 64; ++w) s += part[w][tid];
+        if (t0 + t < T && e0 + e < E) {
+            if (bias) s += bias[e0 + e];
+            logits[(size_t)(t0 + t) * E + e0 + e] = s;
+        }
+    }
+}
+
+// (value, index) is better than (v2, i2): larger value, or equal value and
+// lower expert index.  NaN was mapped to -inf before, so every unchosen expert
+// stays comparable and exactly k distinct experts are always selected.
+__device__ __forceinline__ bool better(float v, int i, float v2, int i2) {
+    return v > v2 || (v == v2 && i < i2);
+}
+
+constexpr int TK_MAXPL = 4;   // E <= 256 -> up to 4 logits per lane
+constexpr int TK_MAXK = 16;
+
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+                                                  int32_t* __restrict__ idx,
+                                                  float* __restrict__ w, int T, int E, int k) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    __shared__ float selv[4][TK_MAXK];
+    if (t >= T) return;
+    float v[TK_MAXPL];
+    bool live[TK_MAXPL];
+#pragma unroll
+    for (int i = 0; i < TK_MAXPL; ++i) {
+        const int e = lane + 64 * i;
+        live[i] = e < E;
+        float x = live[i] ? logits[(size_t)t * E + e] : -INFINITY;
+        v[i] = (x != x) ? -INFINITY : x;
+    }
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < TK_MAXPL; ++i)
+            if (live[i] && better(v[i], lane + 64 * i, bv, bi)) { bv = v[i]; bi = lane + 64 * i; }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            float ov = __shfl_xor(bv, o, MOE_WAVE);
+            int oi = __shfl_xor(bi, o, MOE_WAVE);
+            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        }
+        // the owner retires the winner
+#pragma unroll
+        for (int i = 0; i < TK_MAXPL; ++i)
+            if (lane + 64 * i == bi) live[i] = false;
+        if (lane == 0) {
+            idx[(size_t)t * k + j] = bi;
+            selv[wave][j] = bv;
+        }
+    }
+    if (lane == 0) {
+        // softmax restricted to the selection, max-subtracted (slot 0 holds the max)
+        const float m = selv[wave][0];
+        float s = 0.f;
+        for (int j = 0; j < k; ++j) s += expf(selv[wave][j] - m);
+        const float inv = 1.0f / s;
+        for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = expf(selv[wave][j] - m) * inv;
+    }
+}
+
+hipError_t launch_route(int act, const void* x, const float* wg, const float* b, float* logits,
+                        int32_t* idx, float* w, int T, int d, int E, int k, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    dim3 g1((T + RT_TOK - 1) / RT_TOK, (E + RT_EXP - 1) / RT_EXP);
+    if (act == DT_F32)
+        hipLaunchKernelGGL(router_logits_kernel<DT_F32>, g1, dim3(RT_THREADS), 0, s, x, wg, b,
+                           logits, T, d, E);
+    else
+        hipLaunchKernelGGL(router_logits_kernel<DT_BF16>, g1, dim3(RT_THREADS), 0, s, x, wg, b,
+                           logits, T, d, E);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx, w, T, E, k);
+    return hipGetLastError();
+}
+
+}  // namespace moe

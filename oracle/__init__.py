@@ -65,6 +65,10 @@ def _check(rc, name):
         raise ValueError(f"oracle {name} rejected its arguments (rc={rc})")
 
 
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
 def dec_bf16(h: int) -> float:
     return lib().orc_dec_bf16(h)
 

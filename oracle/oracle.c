@@ -31,6 +31,7 @@
  * (k = E dense mixture, sum of gate weights, bijective dispatch, int4 = q*s).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -41,6 +42,9 @@
 
 #define ORC_OK 0
 #define ORC_EINVAL (-1)
+
+/* Threads the OpenMP loops below will use (reported beside CPU timings). */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- decoders */
 

@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_layer_forward_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = moe.lib()
+    names = declared_symbols()
+    assert set(names) == set(moe.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror():
+    assert moe.moe_strerror(0) == "ok"
+    assert moe.moe_strerror(-2) == "workspace too small"
+    assert moe.moe_strerror(-99) == "unknown status"
+
+
+def test_workspace_bytes():
+    s = moe.make_shape(8, 4096, 8, 2, 14336)
+    n = moe.moe_workspace_bytes(s)
+    # at least H (bf16) and y_perm (fp32) for the 16 assignments
+    assert n >= 16 * 14336 * 2 + 16 * 4096 * 4
+    assert n % 256 == 0
+    s1 = moe.make_shape(64, 7168, 256, 8, 2048, "bf16", "int4", n_shared=1)
+    n1 = moe.moe_workspace_bytes(s1)
+    assert n1 >= 512 * 2048 * 2 + 512 * 7168 * 4 + 64 * 2048 * 2 + 64 * 7168 * 4
+    assert moe.moe_workspace_bytes(moe.make_shape(8, 4096, 8, 9, 14336)) == 0
+
+
+BAD_SHAPES = [
+    (dict(T=-1), moe.MOE_EINVAL),
+    (dict(E=0), moe.MOE_EINVAL),
+    (dict(E=257), moe.MOE_EINVAL),
+    (dict(k=0), moe.MOE_EINVAL),
+    (dict(k=9), moe.MOE_EINVAL),
+    (dict(E=32, k=17), moe.MOE_EINVAL),
+    (dict(d=100), moe.MOE_EINVAL),
+    (dict(F=0), moe.MOE_EINVAL),
+    (dict(n_shared=2), moe.MOE_EINVAL),
+    (dict(act=7), moe.MOE_EINVAL),
+    (dict(wt=9), moe.MOE_EINVAL),
+    (dict(wt="int4", d=4104), moe.MOE_EINVAL),
+    (dict(act="f32", wt="bf16"), moe.MOE_EUNSUPPORTED),
+    (dict(act="bf16", wt="f32"), moe.MOE_EUNSUPPORTED),
+    (dict(d=20480), moe.MOE_EUNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("bad,code", BAD_SHAPES)
+def test_bad_shape_rejected_before_any_launch(bad, code):
+    args = dict(T=8, d=4096, E=8, k=2, F=14336, act="bf16", wt="bf16")
+    args.update(bad)
+    s = moe.make_shape(**args)
+    fake = 1 << 20   # never dereferenced: validation fails first
+    for call in (
+        lambda: moe.moe_route(s, fake, fake, None, fake, fake, fake, stream=0),
+        lambda: moe.moe_dispatch(s, fake, fake, fake, fake, fake, stream=0),
+        lambda: moe.moe_combine(s, fake, fake, fake, None, None, fake, stream=0),
+    ):
+        with pytest.raises(moe.MoEError) as ei:
+            call()
+        assert ei.value.status == code
+
+
+def test_null_and_misaligned_pointers():
+    s = moe.make_shape(8, 64, 8, 2, 128, "f32", "f32")
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_route(s, None, 1 << 20, None, 1 << 20, 1 << 20, 1 << 20, stream=0)
+    assert ei.value.status == moe.MOE_EINVAL and "x is NULL" in str(ei.value)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_route(s, (1 << 20) + 4, 1 << 20, None, 1 << 20, 1 << 20, 1 << 20, stream=0)
+    assert "aligned" in str(ei.value)
+
+
+def test_workspace_too_small_is_enomem():
+    s = moe.make_shape(8, 64, 8, 2, 128, "f32", "f32")
+    w = moe.make_weights(1 << 20, 1 << 20, 1 << 20)
+    p = 1 << 20
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_layer_forward(s, p, p, None, w, None, p, None, None, p, ws_bytes=256, stream=0)
+    assert ei.value.status == moe.MOE_ENOMEM
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_expert_ffn(s, p, w, p, p, p, p, None, p, ws_bytes=0, stream=0)
+    assert ei.value.status == moe.MOE_ENOMEM
+
+
+def test_int4_needs_scales():
+    s = moe.make_shape(8, 128, 8, 2, 128, "bf16", "int4")
+    w = moe.make_weights(1 << 20, 1 << 20, 1 << 20)
+    p = 1 << 20
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_layer_forward(s, p, p, None, w, None, p, None, None, p, ws_bytes=1 << 30, stream=0)
+    assert ei.value.status == moe.MOE_EINVAL and "s_gate" in str(ei.value)
+
+
+def test_error_message_truncated_to_buffer():
+    L = moe.lib()
+    s = moe.make_shape(8, 4096, 8, 9, 14336)
+    buf = ctypes.create_string_buffer(8)
+    rc = L.moe_route(ctypes.byref(s), None, None, None, None, None, None, None, buf, 8)
+    assert rc == moe.MOE_EINVAL
+    assert len(buf.value) == 7   # NUL-terminated inside the 8 bytes
+    rc = L.moe_route(ctypes.byref(s), None, None, None, None, None, None, None, None, 0)
+    assert rc == moe.MOE_EINVAL
+
+
+def test_rmsnorm_validation():
+    s = moe.make_shape(4, 12, 8, 2, 128, "f32", "f32")
+    with pytest.raises(moe.MoEError):
+        moe.moe_rmsnorm(s, 1 << 20, None, 1e-6, 1 << 20, stream=0)
+    s = moe.make_shape(4, 16, 8, 2, 128, "f32", "f32")
+    with pytest.raises(moe.MoEError):
+        moe.moe_rmsnorm(s, 1 << 20, None, -1.0, 1 << 20, stream=0)

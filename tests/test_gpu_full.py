@@ -1,0 +1,123 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the bench
+times (moe_layer_forward, default tau).  Routing is checked on every token
+(bit-exact indices on the GPU's own logits, flip rule against the oracle's fp64
+logits); outputs are checked on tokens the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import moe_layer_forward_amd as moe
+from gpu_common import (DEV, TOL, check_routing_with_flips, device_inputs, oracle_weights, run_layer,
+                        say, shape_of, tokenwise_rel)
+from helpers import np_f64, np_store
+
+pytestmark = pytest.mark.gpu
+C = moe_inputs.CONFIGS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def _sample_tokens(idx, E, per_expert=3, extra=8, seed=0):
+    """First and last tokens of every expert's group plus a few random ones."""
+    T = idx.shape[0]
+    sel = set()
+    for e in range(E):
+        toks = np.where((idx == e).any(axis=1))[0]
+        sel.update(toks[:per_expert].tolist())
+        sel.update(toks[-per_expert:].tolist())
+    rng = np.random.default_rng(seed)
+    sel.update(rng.choice(T, min(extra, T), replace=False).tolist())
+    return np.array(sorted(sel), np.int32)
+
+
+def _check_layer(orc, cfg, d, y, counts, idx, sel=None, residual=None, max_sel=None):
+    gi = idx.cpu().numpy()
+    x = np_store(d["x"])
+    wr, br = np_store(d["w_router"]), np_store(d["b_router"])
+    # routing on every token: the oracle's own fp64 logits and top-k
+    lg = orc.router_logits(x, cfg.act, wr, br)
+    oi, _ = orc.topk(lg, cfg.k)
+    flips = check_routing_with_flips(gi, oi, lg, cfg.k)
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(gi.ravel(), minlength=cfg.E))
+    # outputs of the sampled tokens with the GPU's expert choice
+    if sel is None:
+        sel = _sample_tokens(gi, cfg.E)
+    if max_sel is not None and len(sel) > max_sel:
+        sel = np.sort(np.random.default_rng(1).choice(sel, max_sel, replace=False)).astype(np.int32)
+    W, S = oracle_weights(d)
+    say(f"  oracle on {len(sel)} tokens")
+    y_f, _, _, _ = orc.layer_forward(x, cfg.act, cfg.wt, cfg.k, wr, br, W, S,
+                                     residual=None if residual is None else np_store(residual),
+                                     forced_idx=gi, sel=sel)
+    err = tokenwise_rel(np_f64(y)[sel], y_f)
+    say(f"  max rel {err.max():.3g} (mean {err.mean():.3g}) flips {flips}")
+    assert err.max() < TOL[cfg.wt]
+    return flips
+
+
+def test_mixtral_decode_full(orc):
+    cfg = C["mixtral_decode"]
+    say("full mixtral decode T=8")
+    d = device_inputs(cfg)
+    y, counts, idx = run_layer(cfg, d)
+    _check_layer(orc, cfg, d, y, counts, idx, sel=np.arange(cfg.T, dtype=np.int32))
+
+
+def test_mixtral_prefill_full(orc):
+    cfg = C["mixtral_prefill"]
+    say("full mixtral prefill T=4096 (Zipf-loaded experts)")
+    d = device_inputs(cfg)
+    y, counts, idx = run_layer(cfg, d)
+    c = counts.cpu().numpy()
+    say(f"  counts {c.tolist()}")
+    assert c[0] > 2 * c[-1]       # skewed as calibrated
+    _check_layer(orc, cfg, d, y, counts, idx, max_sel=48)
+    # bitwise run-to-run determinism at full size
+    y2, counts2, idx2 = run_layer(cfg, d)
+    assert torch.equal(y, y2) and torch.equal(idx, idx2)
+
+
+def test_fine_int4_decode_full(orc):
+    cfg = C["fine_int4_decode"]
+    say("full fine-grained int4 decode T=64 E=256 + shared")
+    d = device_inputs(cfg)
+    y, counts, idx = run_layer(cfg, d)
+    say(f"  active experts {(counts > 0).sum().item()}")
+    _check_layer(orc, cfg, d, y, counts, idx, sel=np.arange(0, cfg.T, 2, dtype=np.int32))
+
+
+def test_stack4_full_teacher_forced(orc):
+    """Four pre-norm layers with residual; each layer checked on the GPU's own
+    input (teacher forcing), plus the per-layer usage histogram."""
+    cfg = C["stack4"]
+    say("full 4-layer stack T=512 E=64 top-6")
+    inp = moe_inputs.generate(cfg, seed=0, device=DEV)
+    h = inp["x"].to(DEV)
+    hist = []
+    for l in range(cfg.layers):
+        L = inp["layers"][l]
+        d = {"w_router": L["w_router"].to(DEV), "b_router": None}
+        for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                  "sh_gate", "sh_up", "sh_down", "sh_s_gate", "sh_s_up", "sh_s_down"):
+            d[n] = None if L.get(n) is None else L[n].to(DEV)
+        gamma = inp["gamma"][l].to(DEV)
+        n_ = torch.empty_like(h)
+        moe.moe_rmsnorm(shape_of(cfg), h, gamma, inp["eps"], n_)
+        torch.cuda.synchronize()
+        ref_n = orc.rmsnorm(np_store(h), "bf16", inp["gamma"][l].numpy(), inp["eps"])
+        assert tokenwise_rel(np_f64(n_), ref_n).max() < 8e-3
+        d["x"] = n_
+        y, counts, idx = run_layer(cfg, d, residual=h)
+        say(f"  layer {l}")
+        _check_layer(orc, cfg, d, y, counts, idx, residual=h, max_sel=24)
+        c = counts.cpu().numpy()
+        hist += [(l, e, int(c[e])) for e in range(cfg.E) if c[e] > 0]
+        h = y.clone()
+    assert sum(c for (_, _, c) in hist) == cfg.layers * cfg.T * cfg.k
+    # consecutive layers' routers are correlated, so expert choices overlap
+    say(f"  histogram lines {len(hist)}")

@@ -1,0 +1,331 @@
+"""GPU parity: every step of the HIP path, called through the C ABI, against the
+fp64 oracle on the same seeded inputs.
+
+Bars: expert indices and the dispatch permutation bit-exact (given the same
+router logits); outputs within a per-token relative infinity-norm error of 1e-5
+(fp32) or 2e-2 (bf16 / int4); end-to-end index flips only where the oracle's
+fp64 k-th / (k+1)-th logit margin is below 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import moe_layer_forward_amd as moe
+from gpu_common import (DEV, TOL, act_dtype, check_routing_with_flips, device_inputs,
+                        oracle_weights, run_layer, say, shape_of, tokenwise_rel, weights_struct)
+from helpers import np_f64, np_store
+
+pytestmark = pytest.mark.gpu
+
+C = moe_inputs.CONFIGS
+SMALL = {
+    "tiny_f32": C["tiny_f32"],
+    "bf16_decode_small": moe_inputs.MoEConfig(
+        "bf16_decode_small", T=8, d=512, E=8, k=2, F=1024, act="bf16", wt="bf16",
+        model="s_bf16_dec", w_std=0.05),
+    "bf16_prefill_ragged": moe_inputs.MoEConfig(
+        "bf16_prefill_ragged", T=600, d=256, E=6, k=2, F=328, act="bf16", wt="bf16",
+        model="s_bf16_pre", w_std=0.05),
+    "int4_shared_small": moe_inputs.MoEConfig(
+        "int4_shared_small", T=16, d=512, E=16, k=4, F=256, act="bf16", wt="int4",
+        model="s_int4", n_shared=1, w_std=0.05),
+    "int4_ktail": moe_inputs.MoEConfig(
+        "int4_ktail", T=24, d=384, E=8, k=3, F=640, act="bf16", wt="int4",
+        model="s_int4_tail", n_shared=0, w_std=0.05),
+    "f32_ragged": moe_inputs.MoEConfig(
+        "f32_ragged", T=37, d=200, E=5, k=3, F=72, act="f32", wt="f32", model="s_f32"),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+# ------------------------------------------------------------------ A1-A3
+
+def _route(cfg, d, T=None):
+    T = cfg.T if T is None else T
+    shape = shape_of(cfg, T=T)
+    logits = torch.empty(T, cfg.E, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, cfg.k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, cfg.k, dtype=torch.float32, device=DEV)
+    moe.moe_route(shape, d["x"][:T], d["w_router"], d["b_router"], logits, idx, w)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def _check_route(cfg, x, wr, br, L, idx, w, orc):
+    ref = orc.router_logits(np_store(x), cfg.act, np_store(wr), np_store(br))
+    scale = np.abs(ref).max() + 1e-30
+    assert np.abs(L.astype(np.float64) - ref).max() / scale < 1e-5
+    # top-k on the GPU's own logits must match bit for bit
+    oi, ow = orc.topk(L.astype(np.float64), cfg.k)
+    assert np.array_equal(idx, oi)
+    np.testing.assert_allclose(w, ow, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(w.sum(1), 1.0, atol=1e-6)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "mixtral_decode", "mixtral_prefill",
+                                  "fine_int4_decode", "stack4"])
+def test_route_parity(orc, name):
+    cfg = C[name]
+    say(f"route parity {name}")
+    x = moe_inputs.activations(cfg, 0)
+    wr = moe_inputs.router_weights(cfg, 0, 0)
+    br = moe_inputs.router_bias(cfg)
+    d = {"x": x.to(DEV), "w_router": wr.to(DEV), "b_router": None if br is None else br.to(DEV)}
+    L, idx, w = _route(cfg, d)
+    _check_route(cfg, x, wr, br, L, idx, w, orc)
+
+
+def test_route_ties_and_degenerate(orc):
+    cfg = moe_inputs.MoEConfig("ties", T=70, d=64, E=256, k=8, F=128, act="f32", wt="f32",
+                               model="ties")
+    say("route ties E=256 k=8")
+    x = torch.zeros(70, 64)
+    x[1::2] = torch.randn(35, 64, generator=torch.Generator().manual_seed(1))
+    wr = torch.randn(256, 64, generator=torch.Generator().manual_seed(2))
+    wr[7] = wr[3]          # duplicate experts -> exact ties
+    wr[200] = wr[3]
+    d = {"x": x.to(DEV), "w_router": wr.to(DEV), "b_router": None}
+    L, idx, w = _route(cfg, d)
+    _check_route(cfg, x, wr, None, L, idx, w, orc)
+    assert (idx[0::2] == np.arange(8)).all()    # all-equal logits -> experts 0..k-1
+    # k = E
+    cfg2 = cfg.replace(E=16, k=16)
+    d2 = {"x": x.to(DEV), "w_router": wr[:16].contiguous().to(DEV), "b_router": None}
+    L2, idx2, w2 = _route(cfg2, d2)
+    _check_route(cfg2, x, wr[:16], None, L2, idx2, w2, orc)
+
+
+# --------------------------------------------------------------------- A4
+
+def _dispatch(idx, E, k):
+    T = idx.shape[0] // k if idx.ndim == 1 else idx.shape[0]
+    shape = moe.make_shape(T, 64, E, k, 64, "f32", "f32")
+    ti = torch.from_numpy(np.ascontiguousarray(idx, np.int32).reshape(-1)).to(DEV)
+    counts = torch.full((E,), -7, dtype=torch.int32, device=DEV)
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    perm = torch.full((max(T * k, 1),), -7, dtype=torch.int32, device=DEV)
+    inv = torch.full((max(T * k, 1),), -7, dtype=torch.int32, device=DEV)
+    moe.moe_dispatch(shape, ti, counts, offsets, perm, inv)
+    torch.cuda.synchronize()
+    return (counts.cpu().numpy(), offsets.cpu().numpy(), perm.cpu().numpy()[:T * k],
+            inv.cpu().numpy()[:T * k])
+
+
+@pytest.mark.parametrize("T,k,E,kind", [
+    (16, 2, 8, "random"), (8, 2, 8, "random"), (4096, 2, 8, "zipf"), (64, 8, 256, "random"),
+    (512, 6, 64, "random"), (1, 1, 1, "random"), (3, 4, 4, "random"), (1000, 3, 7, "one"),
+    (2048, 16, 256, "random"), (5, 2, 200, "random"),
+])
+def test_dispatch_bit_exact(orc, T, k, E, kind):
+    say(f"dispatch T={T} k={k} E={E} {kind}")
+    rng = np.random.default_rng(T * 7 + E)
+    if kind == "random":
+        idx = np.array([rng.choice(E, k, replace=False) for _ in range(T)], np.int32)
+    elif kind == "zipf":
+        p = np.array(moe_inputs.zipf_targets(E))
+        idx = np.array([rng.choice(E, k, replace=False, p=p) for _ in range(T)], np.int32)
+    else:   # every token on the same k experts
+        idx = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    got = _dispatch(idx, E, k)
+    ref = orc.dispatch(idx, E)
+    for g, r, name in zip(got, ref, ("counts", "offsets", "perm", "inv")):
+        assert np.array_equal(g, r), name
+
+
+def test_dispatch_empty_and_invalid(orc):
+    say("dispatch T=0 and out-of-range entries")
+    c, o, p, i = _dispatch(np.zeros((0, 2), np.int32), 8, 2)
+    assert (c == 0).all() and (o == 0).all()
+    idx = np.array([[0, 1], [9, 2], [-1, 1]], np.int32)   # 9 and -1 are ignored
+    c, o, p, i = _dispatch(idx, 8, 2)
+    assert c.tolist() == [1, 2, 1, 0, 0, 0, 0, 0] and o[-1] == 4
+    assert p[:4].tolist() == [0, 1, 5, 3]
+
+
+# ------------------------------------------------------------ A5-A8 steps
+
+def _steps(cfg, d, tau=0):
+    """route -> dispatch -> expert_ffn -> combine through the C ABI."""
+    T = cfg.T
+    shape = shape_of(cfg, tau)
+    logits = torch.empty(T, cfg.E, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, cfg.k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, cfg.k, dtype=torch.float32, device=DEV)
+    moe.moe_route(shape, d["x"], d["w_router"], d["b_router"], logits, idx, w)
+    counts = torch.empty(cfg.E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(cfg.E + 1, dtype=torch.int32, device=DEV)
+    perm = torch.empty(T * cfg.k, dtype=torch.int32, device=DEV)
+    inv = torch.empty(T * cfg.k, dtype=torch.int32, device=DEV)
+    moe.moe_dispatch(shape, idx, counts, offsets, perm, inv)
+    yp = torch.empty(T * cfg.k, cfg.d, dtype=torch.float32, device=DEV)
+    ys = torch.empty(T, cfg.d, dtype=torch.float32, device=DEV) if cfg.n_shared else None
+    ws = torch.empty(moe.moe_workspace_bytes(shape), dtype=torch.uint8, device=DEV)
+    moe.moe_expert_ffn(shape, d["x"], weights_struct(d), counts, offsets, perm, yp, ys, ws)
+    y = torch.empty(T, cfg.d, dtype=act_dtype(cfg), device=DEV)
+    moe.moe_combine(shape, yp, inv, w, ys, None, y)
+    torch.cuda.synchronize()
+    h = lambda t: None if t is None else t.cpu().numpy()
+    return dict(logits=h(logits), idx=h(idx), w=h(w), counts=h(counts), offsets=h(offsets),
+                perm=h(perm), inv=h(inv), yp=h(yp), ys=h(ys), y=np_f64(y))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("tau", [0, -1])
+def test_steps_parity(orc, name, tau):
+    cfg = SMALL[name]
+    if tau == -1 and cfg.wt != "bf16":
+        pytest.skip("tau only selects kernels for bf16 weights")
+    say(f"steps parity {name} tau={tau}")
+    d = device_inputs(cfg)
+    g = _steps(cfg, d, tau)
+    W, S = oracle_weights(d)
+    x = np_store(d["x"])
+    # route: bit-exact top-k on the GPU's logits
+    oi, ow = orc.topk(g["logits"].astype(np.float64), cfg.k)
+    assert np.array_equal(g["idx"], oi)
+    np.testing.assert_allclose(g["w"], ow, rtol=1e-6, atol=1e-7)
+    # dispatch: bit-exact on the GPU's indices
+    rc = orc.dispatch(g["idx"], cfg.E)
+    for a, b in zip((g["counts"], g["offsets"], g["perm"], g["inv"]), rc):
+        assert np.array_equal(a, b)
+    # expert FFN rows
+    yp_ref = orc.expert_ffn(x, cfg.act, cfg.wt, W, *rc[:3], cfg.k)
+    err = tokenwise_rel(g["yp"], yp_ref)
+    say(f"  y_perm max rel {err.max():.3g}")
+    assert err.max() < TOL[cfg.wt]
+    if cfg.n_shared:
+        ys_ref = orc.shared_ffn(x, cfg.act, cfg.wt, S)
+        assert tokenwise_rel(g["ys"], ys_ref).max() < TOL[cfg.wt]
+    # combine on the GPU's own y_perm: only fp32 summation order differs
+    y_ref = orc.combine(g["yp"].astype(np.float64), g["inv"], g["w"].astype(np.float64), cfg.k,
+                        ys=None if g["ys"] is None else g["ys"].astype(np.float64))
+    cmb_tol = 1e-6 if cfg.act == "f32" else 8e-3   # bf16 output rounding
+    assert tokenwise_rel(g["y"], y_ref).max() < cmb_tol
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_end_to_end_small(orc, name):
+    cfg = SMALL[name]
+    say(f"layer end-to-end {name}")
+    d = device_inputs(cfg)
+    y, counts, idx = run_layer(cfg, d)
+    W, S = oracle_weights(d)
+    x = np_store(d["x"])
+    wr, br = np_store(d["w_router"]), np_store(d["b_router"])
+    y_o, idx_o, _, lg_o = orc.layer_forward(x, cfg.act, cfg.wt, cfg.k, wr, br, W, S)
+    gi = idx.cpu().numpy()
+    flips = check_routing_with_flips(gi, idx_o, lg_o, cfg.k)
+    y_f, _, _, _ = orc.layer_forward(x, cfg.act, cfg.wt, cfg.k, wr, br, W, S, forced_idx=gi)
+    err = tokenwise_rel(np_f64(y), y_f)
+    say(f"  max rel {err.max():.3g} flips {flips}")
+    assert err.max() < TOL[cfg.wt]
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(gi.ravel(), minlength=cfg.E))
+
+
+def test_residual_and_determinism(orc):
+    cfg = SMALL["bf16_prefill_ragged"]
+    say("residual + determinism")
+    d = device_inputs(cfg)
+    res = torch.randn(cfg.T, cfg.d, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+    y1, c1, i1 = run_layer(cfg, d, residual=res)
+    y2, c2, i2 = run_layer(cfg, d, residual=res)
+    assert torch.equal(y1, y2) and torch.equal(i1, i2) and torch.equal(c1, c2)
+    W, S = oracle_weights(d)
+    y_f, _, _, _ = orc.layer_forward(np_store(d["x"]), cfg.act, cfg.wt, cfg.k, np_store(d["w_router"]),
+                                     None, W, S, residual=np_store(res), forced_idx=i1.cpu().numpy())
+    assert tokenwise_rel(np_f64(y1), y_f).max() < TOL["bf16"]
+
+
+def test_tau_does_not_change_routing():
+    cfg = SMALL["bf16_prefill_ragged"]
+    say("tau invariance")
+    d = device_inputs(cfg)
+    ref = None
+    for tau in (-1, 0, 1, 50, 10000):
+        g = _steps(cfg, d, tau)
+        if ref is None:
+            ref = g
+            continue
+        for n in ("idx", "counts", "offsets", "perm", "inv"):
+            assert np.array_equal(g[n], ref[n]), (tau, n)
+        assert tokenwise_rel(g["y"], ref["y"]).max() < 1e-2
+
+
+def test_edge_cases(orc):
+    """T = 0, T = 1, k = E, and all tokens on one expert (maximal imbalance)."""
+    say("edge cases")
+    base = SMALL["bf16_prefill_ragged"]
+    d = device_inputs(base)
+    # T = 0: nothing launched except the zero histogram
+    shape = shape_of(base, T=0)
+    ws = torch.empty(moe.moe_workspace_bytes(shape), dtype=torch.uint8, device=DEV)
+    counts = torch.full((base.E,), 5, dtype=torch.int32, device=DEV)
+    moe.moe_layer_forward(shape, d["x"], d["w_router"], None, weights_struct(d), None, d["x"],
+                          counts, None, ws)
+    torch.cuda.synchronize()
+    assert (counts.cpu() == 0).all()
+    W, S = oracle_weights(d)
+    wr = np_store(d["w_router"])
+    for T in (1, 17):
+        y, c, i = run_layer(base, d, x=d["x"][:T].contiguous())
+        y_f, _, _, _ = orc.layer_forward(np_store(d["x"][:T]), "bf16", "bf16", base.k, wr, None, W,
+                                         forced_idx=i.cpu().numpy())
+        assert tokenwise_rel(np_f64(y), y_f).max() < TOL["bf16"]
+    # k = E
+    cfgE = base.replace(k=base.E, T=40)
+    y, c, i = run_layer(cfgE, d, x=d["x"][:40].contiguous())
+    assert (c.cpu() == 40).all()
+    y_f, _, _, _ = orc.layer_forward(np_store(d["x"][:40]), "bf16", "bf16", cfgE.k, wr, None, W,
+                                     forced_idx=i.cpu().numpy())
+    assert tokenwise_rel(np_f64(y), y_f).max() < TOL["bf16"]
+    # one expert takes every token: a large bias on experts 0 and 1
+    b = torch.zeros(base.E)
+    b[0], b[1] = 1e3, 5e2
+    d1 = dict(d, b_router=b.to(DEV))
+    for tau in (0, -1):
+        y, c, i = run_layer(base, d1, tau=tau)
+        assert c.cpu().tolist()[:2] == [base.T, base.T]
+        y_f, _, _, _ = orc.layer_forward(np_store(d["x"]), "bf16", "bf16", base.k, wr, b.numpy(), W,
+                                         forced_idx=i.cpu().numpy())
+        assert tokenwise_rel(np_f64(y), y_f).max() < TOL["bf16"]
+
+
+def test_groups_straddling_tau(orc):
+    """Expert groups of tau-1, tau and tau+1 rows take different kernels."""
+    say("groups straddling tau")
+    cfg = SMALL["bf16_prefill_ragged"]
+    d = device_inputs(cfg)
+    T, tau = 17, 16
+    x = d["x"][:T].contiguous()
+    # bias chosen so expert 0 gets all 17 tokens and k=2 picks the runner-up per token
+    b = torch.zeros(cfg.E)
+    b[0] = 1e3
+    d1 = dict(d, b_router=b.to(DEV))
+    W, S = oracle_weights(d)
+    for TT in (tau - 1, tau, tau + 1):
+        y, c, i = run_layer(cfg, d1, tau=tau, x=x[:TT].contiguous())
+        assert int(c[0]) == TT
+        y_f, _, _, _ = orc.layer_forward(np_store(x[:TT]), "bf16", "bf16", cfg.k, np_store(d["w_router"]),
+                                         b.numpy(), W, forced_idx=i.cpu().numpy())
+        assert tokenwise_rel(np_f64(y), y_f).max() < TOL["bf16"]
+
+
+def test_rmsnorm_parity(orc):
+    say("rmsnorm")
+    for act in ("f32", "bf16"):
+        h = torch.randn(33, 2048, generator=torch.Generator().manual_seed(3)) * 3
+        h = h.to(torch.float32 if act == "f32" else torch.bfloat16)
+        g = torch.linspace(0.5, 1.5, 2048)
+        out = torch.empty_like(h).to(DEV)
+        shape = moe.make_shape(33, 2048, 8, 2, 64, act, act)
+        moe.moe_rmsnorm(shape, h.to(DEV), g.to(DEV), 1e-6, out)
+        torch.cuda.synchronize()
+        ref = orc.rmsnorm(np_store(h), act, g.numpy(), 1e-6)
+        tol = 1e-6 if act == "f32" else 8e-3
+        assert tokenwise_rel(np_f64(out), ref).max() < tol
