@@ -129,15 +129,6 @@ int effective_tau(const moe_shape* s) {
     return s->tau == 0 ? kDefaultTau : s->tau;
 }
 
-int rows_per_block(int N, int E, int T, int k) {
-    const int active = (T * k < E) ? T * k : E;
-    const long target = 2048;
-    long r = ((long)N * active + target - 1) / target;
-    if (r < 8) r = 8;
-    if (r > 256) r = 256;
-    return (int)((r + 7) / 8 * 8);
-}
-
 // The FFN launch sequence shared by moe_expert_ffn and moe_layer_forward.
 int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32_t* counts,
             const int32_t* offsets, const int32_t* perm, float* y_perm, float* y_shared,
@@ -163,13 +154,14 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     g.perm = perm;
     g.topk = s->k;
     g.T = s->T;
+    g.E = s->E;
     g.tau = use_mfma ? tau : -1;
 
     // gate/up + SwiGLU
     g.w0 = w->w_gate; g.w1 = w->w_up;
     g.s0 = (const uint16_t*)w->s_gate; g.s1 = (const uint16_t*)w->s_up;
     g.in = x; g.out = h; g.N = s->F; g.K = s->d;
-    g.rows_per_block = rows_per_block(g.N, s->E, s->T, s->k);
+    g.rows_per_item = gemv_rows_per_item(s->wt, 0, g.K);
     rc = hip_check(launch_gemv(s->wt, s->act, 0, g, s->E, max_rows_gemv, st), st, "gemv gate/up", err, err_len);
     if (rc) return rc;
     if (use_mfma) {
@@ -181,7 +173,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     g.w0 = w->w_down; g.w1 = nullptr;
     g.s0 = (const uint16_t*)w->s_down; g.s1 = nullptr;
     g.in = h; g.out = y_perm; g.N = s->d; g.K = s->F;
-    g.rows_per_block = rows_per_block(g.N, s->E, s->T, s->k);
+    g.rows_per_item = gemv_rows_per_item(s->wt, 1, g.K);
     rc = hip_check(launch_gemv(s->wt, s->act, 1, g, s->E, max_rows_gemv, st), st, "gemv down", err, err_len);
     if (rc) return rc;
     if (use_mfma) {
@@ -194,17 +186,17 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
         void* hs = ws + L.hs;
         GemvArgs q{};
         q.counts = nullptr; q.offsets = nullptr; q.perm = nullptr;
-        q.topk = 1; q.T = s->T; q.tau = -1;
+        q.topk = 1; q.T = s->T; q.E = 1; q.tau = -1;
         q.w0 = w->sh_gate; q.w1 = w->sh_up;
         q.s0 = (const uint16_t*)w->sh_s_gate; q.s1 = (const uint16_t*)w->sh_s_up;
         q.in = x; q.out = hs; q.N = s->F; q.K = s->d;
-        q.rows_per_block = rows_per_block(q.N, 1, 1, 1);
+        q.rows_per_item = gemv_rows_per_item(s->wt, 0, q.K);
         rc = hip_check(launch_gemv(s->wt, s->act, 0, q, 1, s->T, st), st, "gemv shared gate/up", err, err_len);
         if (rc) return rc;
         q.w0 = w->sh_down; q.w1 = nullptr;
         q.s0 = (const uint16_t*)w->sh_s_down; q.s1 = nullptr;
         q.in = hs; q.out = y_shared; q.N = s->d; q.K = s->F;
-        q.rows_per_block = rows_per_block(q.N, 1, 1, 1);
+        q.rows_per_item = gemv_rows_per_item(s->wt, 1, q.K);
         rc = hip_check(launch_gemv(s->wt, s->act, 1, q, 1, s->T, st), st, "gemv shared down", err, err_len);
         if (rc) return rc;
     }

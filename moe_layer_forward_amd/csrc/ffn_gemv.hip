@@ -8,8 +8,15 @@
 // byte is used by ~2 rows), so here nothing is staged in LDS at all.
 //
 // gfx950 design:
-//  * a wave64 streams whole weight rows with 16-byte coalesced loads (1 KiB per
-//    wave instruction), R rows at a time so that many bytes are in flight;
+//  * a persistent grid (a few blocks per CU) walks a list of equal-sized work
+//    items, (active expert, chunk of rows); every block compacts the list of
+//    active experts of its class from the counts itself, so inactive experts
+//    cost nothing and no host round trip or plan kernel is needed;
+//  * a wave64 streams whole weight rows with 16-byte coalesced buffer loads
+//    (1 KiB per wave instruction).  All loads of one iteration (R rows x MS
+//    steps) are issued before any arithmetic: the buffer descriptor's range
+//    check returns zeros for out-of-range offsets, so there is no branch
+//    between the loads and 16-32 KiB per wave are in flight;
 //  * the activation rows of the expert's group (NT tokens per pass) live in
 //    VGPRs for the lane's K positions, loaded once and reused for every row;
 //  * bf16: one v_dot2_f32_bf16 per weight pair per token, no conversions;
@@ -37,20 +44,28 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Transposing reduction of N per-lane values over the 64 lanes of a wave.
+// Each of the 6 butterfly levels halves the number of values a lane keeps.
+// Afterwards, for N >= 64 lane l holds the totals of values [l*N/64, (l+1)*N/64)
+// in v[0..N/64); for N < 64 lane l holds value l >> (6 - log2 N) in v[0].
 template <int N>
 __device__ __forceinline__ void wave_fold(float (&v)[N], int lane) {
-    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N power of two");
+    static_assert(N >= 1 && N <= 256 && (N & (N - 1)) == 0, "N power of two");
     int n = N;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         if (n > 1) {
-            const bool up = (lane & o) != 0;
+            // bit masks rather than a select of two array elements: the latter
+            // is folded into a lane-dependent array index, which spills to scratch
+            const uint32_t m = (lane & o) ? 0xffffffffu : 0u;
 #pragma unroll
             for (int i = 0; i < N / 2; ++i) {
                 if (i < n / 2) {
-                    float send = up ? v[i] : v[i + n / 2];
-                    float keep = up ? v[i + n / 2] : v[i];
-                    v[i] = keep + __shfl_xor(send, o, MOE_WAVE);
+                    const uint32_t lo = __float_as_uint(v[i]), hi = __float_as_uint(v[i + n / 2]);
+                    const uint32_t send = (lo & m) | (hi & ~m);
+                    const uint32_t keep = (hi & m) | (lo & ~m);
+                    v[i] = __uint_as_float(keep) +
+                           __uint_as_float(__builtin_amdgcn_ds_bpermute((lane ^ o) << 2, (int)send));
                 }
             }
             n >>= 1;
@@ -58,6 +73,24 @@ __device__ __forceinline__ void wave_fold(float (&v)[N], int lane) {
             v[0] += __shfl_xor(v[0], o, MOE_WAVE);
         }
     }
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over [base, base + nbytes): loads at offsets >= nbytes
+// return zero (the hardware range check), which makes masked loads branch-free.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                             0x00020000);
+}
+constexpr uint32_t kOOB = 0xffffffffu;   // an offset the range check always rejects
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2 /* nontemporal */);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
 template <int WT> struct WTraits;
@@ -126,14 +159,16 @@ __device__ __forceinline__ void load_x(uint32_t (&dst)[(XDw<WT, ACT>::v)], const
     }
 }
 
-// Partial dot product of one 16-byte weight chunk with NT activation fragments.
+// Partial dot product of one 16-byte weight chunk with the first nt of NT
+// activation fragments (nt is wave-uniform, so skipped tokens cost nothing).
 template <int WT, int ACT, int NT>
 __device__ __forceinline__ void chunk_dot(const uint4& wq, const uint32_t (*xf)[(XDw<WT, ACT>::v)],
-                                          const float* xs, float scale, float (&acc)[NT]) {
+                                          const float* xs, float scale, float (&acc)[NT], int nt) {
     const uint32_t w[4] = {wq.x, wq.y, wq.z, wq.w};
     if constexpr (WT == DT_F32) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
+            if (j >= nt) break;
             float a = acc[j];
 #pragma unroll
             for (int i = 0; i < 4; ++i) a = fmaf(__uint_as_float(w[i]), __uint_as_float(xf[j][i]), a);
@@ -142,6 +177,7 @@ __device__ __forceinline__ void chunk_dot(const uint4& wq, const uint32_t (*xf)[
     } else if constexpr (WT == DT_BF16) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
+            if (j >= nt) break;
             float a = acc[j];
 #pragma unroll
             for (int i = 0; i < 4; ++i) a = dot2_bf16(w[i], xf[j][i], a);
@@ -160,6 +196,7 @@ __device__ __forceinline__ void chunk_dot(const uint4& wq, const uint32_t (*xf)[
             for (int s = 0; s < 4; ++s) m[s] = ((u >> (4 * s)) & 0x000f000fu) | 0x43004300u;
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
+                if (j >= nt) break;
                 float a = part[j];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) a = dot2_bf16(m[s], xf[j][4 * i + s], a);
@@ -167,162 +204,214 @@ __device__ __forceinline__ void chunk_dot(const uint4& wq, const uint32_t (*xf)[
             }
         }
 #pragma unroll
-        for (int j = 0; j < NT; ++j) acc[j] = fmaf(scale, fmaf(-136.0f, xs[j], part[j]), acc[j]);
+        for (int j = 0; j < NT; ++j) {
+            if (j >= nt) break;
+            acc[j] = fmaf(scale, fmaf(-136.0f, xs[j], part[j]), acc[j]);
+        }
     }
 }
 
 template <int WT, int ACT, int MODE, int NT, int KS, int R, int MS>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a) {
     constexpr int G = (MODE == 0) ? 2 : 1;
     constexpr int EPL = WTraits<WT>::EPL;
     constexpr int DW = XDw<WT, ACT>::v;
     constexpr int RG = 4 / KS;                 // row groups per block
     constexpr int NV = R * G * NT;             // partial sums per lane
+    constexpr int PL = NV >= 64 ? NV / 64 : 1; // totals a lane holds after the fold
+    constexpr int SH = NV >= 64 ? 0 : (NV == 1 ? 6 : NV == 2 ? 5 : NV == 4 ? 4 : NV == 8 ? 3
+                                                : NV == 16 ? 2 : 1);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ks = wave % KS, rg = wave / KS;
-    const int e = blockIdx.y;
 
-    int c, o;
+    // --- the experts this kernel serves: c_e > 0 and (tau < 0 or c_e <= tau)
+    __shared__ int s_act[256];
+    __shared__ int s_wcnt[4];
+    int U = 1;
     if (a.counts) {
-        c = a.counts[e];
-        o = a.offsets[e];
-        if (c == 0 || (a.tau >= 0 && c > a.tau)) return;
-    } else {
-        c = a.T;
-        o = 0;
-        if (c == 0) return;
+        const int e = threadIdx.x;
+        const int c = (e < a.E) ? a.counts[e] : 0;
+        const bool act = c > 0 && (a.tau < 0 || c <= a.tau);
+        const uint64_t m = __ballot(act);
+        if (lane == 0) s_wcnt[wave] = __popcll(m);
+        __syncthreads();
+        int base = 0;
+        for (int w = 0; w < wave; ++w) base += s_wcnt[w];
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        if (act) s_act[base + __popcll(m & lt)] = e;
+        U = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+        __syncthreads();
     }
-    const int row0 = blockIdx.x * a.rows_per_block;
-    const int row_end = min(a.N, row0 + a.rows_per_block);
-    if (row0 >= row_end) return;
+    const int nrc = (a.N + a.rows_per_item - 1) / a.rows_per_item;
+    const long n_items = (long)U * nrc;
+    const long it_begin = n_items * blockIdx.x / gridDim.x;
+    const long it_end = n_items * (blockIdx.x + 1) / gridDim.x;
 
     const int nchunks = a.K / EPL;
-    const int nsteps = (nchunks + 63) / 64;
-    const size_t rb = row_bytes<WT>(a.K);
-    const char* W0 = reinterpret_cast<const char*>(a.w0) + (size_t)e * a.N * rb;
-    const char* W1 = (MODE == 0) ? reinterpret_cast<const char*>(a.w1) + (size_t)e * a.N * rb : nullptr;
-    const uint16_t* S0 = (WT == DT_INT4) ? a.s0 + (size_t)e * a.N * (a.K / 128) : nullptr;
-    const uint16_t* S1 = (WT == DT_INT4 && MODE == 0) ? a.s1 + (size_t)e * a.N * (a.K / 128) : nullptr;
+    const uint32_t rb = (uint32_t)row_bytes<WT>(a.K);
+    const uint32_t mat_bytes = rb * (uint32_t)a.N;
+    const uint32_t srow = (uint32_t)(a.K / 128) * 2;     // int4 scale bytes per row
     const size_t in_row = (ACT == DT_F32) ? (size_t)a.K * 4 : (size_t)a.K * 2;
     const size_t out_es = (MODE == 1 || ACT == DT_F32) ? 4 : 2;
 
     __shared__ float red[2][4][NV];
-    const int niter = (row_end - row0 + RG * R - 1) / (RG * R);
-    int gi = 0;   // row batches done so far: selects the LDS buffer (parity spans passes)
+    int gi = 0;                       // row batches so far: LDS buffer parity
+    int cur_e = -1, cur_j0 = -1;      // expert / pass the fragments below belong to
+    uint32_t xf[MS][NT][DW];
+    float xs[MS][NT];
 
-    for (int j0 = 0; j0 < c; j0 += NT) {
-        // activation fragments of this token pass, kept in VGPRs
-        uint32_t xf[MS][NT][DW];
-        float xs[MS][NT];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const bool tok_ok = j0 + j < c;
-            int src = 0;
-            if (tok_ok) {
-                const int p = o + j0 + j;
-                src = (MODE == 0 && a.perm) ? a.perm[p] / a.topk : p;
-            }
-            const char* rowp = reinterpret_cast<const char*>(a.in) + (size_t)src * in_row;
-#pragma unroll
-            for (int s = 0; s < MS; ++s) {
-                const int gs = s * KS + ks;
-                const int ch = gs * 64 + lane;
-                load_x<WT, ACT>(xf[s][j], rowp, ch * EPL, tok_ok && gs < nsteps && ch < nchunks,
-                                &xs[s][j]);
-            }
+    for (long item = it_begin; item < it_end; ++item) {
+        const int u = (int)(item / nrc);
+        const int rc = (int)(item % nrc);
+        const int e = a.counts ? s_act[u] : 0;
+        const int c = a.counts ? a.counts[e] : a.T;
+        const int o = a.counts ? a.offsets[e] : 0;
+        const int row0 = rc * a.rows_per_item;
+        const int row_end = min(a.N, row0 + a.rows_per_item);
+        const int niter = (row_end - row0 + RG * R - 1) / (RG * R);
+
+        const char* wb0 = reinterpret_cast<const char*>(a.w0) + (size_t)e * mat_bytes;
+        const __amdgpu_buffer_rsrc_t W0 = make_rsrc(wb0, mat_bytes);
+        __amdgpu_buffer_rsrc_t W1 = W0, S0 = W0, S1 = W0;
+        if constexpr (MODE == 0)
+            W1 = make_rsrc(reinterpret_cast<const char*>(a.w1) + (size_t)e * mat_bytes, mat_bytes);
+        if constexpr (WT == DT_INT4) {
+            S0 = make_rsrc(reinterpret_cast<const char*>(a.s0) + (size_t)e * a.N * srow, a.N * srow);
+            if constexpr (MODE == 0)
+                S1 = make_rsrc(reinterpret_cast<const char*>(a.s1) + (size_t)e * a.N * srow, a.N * srow);
         }
 
-        for (int it = 0; it < niter; ++it, ++gi) {
-            const int rbase = row0 + (it * RG + rg) * R;
-            float acc[R][G][NT];
+        for (int j0 = 0; j0 < c; j0 += NT) {
+            const int nt = min(NT, c - j0);
+            if (e != cur_e || j0 != cur_j0) {
+                // activation fragments of this token pass, kept in VGPRs
 #pragma unroll
-            for (int r = 0; r < R; ++r)
+                for (int j = 0; j < NT; ++j) {
+                    const bool tok_ok = j < nt;
+                    int src = 0;
+                    if (tok_ok) {
+                        const int p = o + j0 + j;
+                        src = (MODE == 0 && a.perm) ? a.perm[p] / a.topk : p;
+                    }
+                    const char* rowp = reinterpret_cast<const char*>(a.in) + (size_t)src * in_row;
 #pragma unroll
-                for (int g = 0; g < G; ++g)
-#pragma unroll
-                    for (int j = 0; j < NT; ++j) acc[r][g][j] = 0.f;
+                    for (int s = 0; s < MS; ++s) {
+                        const int ch = (s * KS + ks) * 64 + lane;
+                        load_x<WT, ACT>(xf[s][j], rowp, ch * EPL, tok_ok && ch < nchunks, &xs[s][j]);
+                    }
+                }
+                cur_e = e;
+                cur_j0 = j0;
+            }
 
+            for (int it = 0; it < niter; ++it, ++gi) {
+                const int rbase = row0 + (it * RG + rg) * R;
+                // ---- every load of this iteration first (out of range -> zeros)
+                uint4 wq[MS][R][G];
+                uint16_t sq[MS][R][G];
 #pragma unroll
-            for (int s = 0; s < MS; ++s) {
-                const int gs = s * KS + ks;
-                if (gs >= nsteps) break;
-                const int ch = gs * 64 + lane;
-                const bool kok = ch < nchunks;
-                uint4 wq[R][G];
-                float sc[R][G];
+                for (int s = 0; s < MS; ++s) {
+                    const int ch = (s * KS + ks) * 64 + lane;
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int row = rbase + r;
-                    const bool ok = kok && row < row_end;
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const char* Wm = (g == 0) ? W0 : W1;
-                        wq[r][g] = ok ? *reinterpret_cast<const uint4*>(Wm + (size_t)row * rb + (size_t)ch * 16)
-                                      : make_uint4(0u, 0u, 0u, 0u);
+                    for (int r = 0; r < R; ++r) {
+                        const int row = rbase + r;
+                        const bool ok = ch < nchunks && row < row_end;
+                        const uint32_t off = ok ? (uint32_t)row * rb + (uint32_t)ch * 16u : kOOB;
+                        wq[s][r][0] = bload16(W0, off);
+                        if constexpr (MODE == 0) wq[s][r][G - 1] = bload16(W1, off);
                         if constexpr (WT == DT_INT4) {
-                            const uint16_t* Sm = (g == 0) ? S0 : S1;
-                            sc[r][g] = ok ? f16_to_f32(Sm[(size_t)row * (a.K / 128) + (ch * EPL) / 128]) : 0.f;
-                        } else {
-                            sc[r][g] = 1.f;
+                            const uint32_t so = ok ? (uint32_t)row * srow + (uint32_t)(ch / 4) * 2u : kOOB;
+                            sq[s][r][0] = bload2(S0, so);
+                            if constexpr (MODE == 0) sq[s][r][G - 1] = bload2(S1, so);
                         }
                     }
                 }
+                // ---- arithmetic
+                float acc[R][G][NT];
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
                     for (int g = 0; g < G; ++g)
-                        chunk_dot<WT, ACT, NT>(wq[r][g], xf[s], xs[s], sc[r][g], acc[r][g]);
-            }
+#pragma unroll
+                        for (int j = 0; j < NT; ++j) acc[r][g][j] = 0.f;
+#pragma unroll
+                for (int s = 0; s < MS; ++s)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+#pragma unroll
+                        for (int g = 0; g < G; ++g) {
+                            const float sc = (WT == DT_INT4) ? f16_to_f32(sq[s][r][g]) : 1.f;
+                            chunk_dot<WT, ACT, NT>(wq[s][r][g], xf[s], xs[s], sc, acc[r][g], nt);
+                        }
 
-            // fold the R*G*NT partials across the wave: value v = (r*NT + j)*G + g
-            float v[NV];
+                // ---- fold the R*G*NT partials: value v = (r*NT + j)*G + g
+                float v[NV];
 #pragma unroll
-            for (int r = 0; r < R; ++r)
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int j = 0; j < NT; ++j)
+                    for (int j = 0; j < NT; ++j)
 #pragma unroll
-                    for (int g = 0; g < G; ++g) v[(r * NT + j) * G + g] = acc[r][g][j];
-            wave_fold<NV>(v, lane);
-            constexpr int SH = (NV == 1) ? 6 : (NV == 2) ? 5 : (NV == 4) ? 4 : (NV == 8) ? 3
-                             : (NV == 16) ? 2 : (NV == 32) ? 1 : 0;
-            const int vi = lane >> SH;               // value index this lane holds
-            const bool writer = (lane & ((1 << SH) - 1)) == 0;
-            float total;
-            if constexpr (KS == 1) {
-                total = v[0];
-            } else {
-                float* buf = red[gi & 1][wave];
-                if (writer) buf[vi] = v[0];
-                __syncthreads();
-                total = 0.f;
-                if (writer) {
+                        for (int g = 0; g < G; ++g) v[(r * NT + j) * G + g] = acc[r][g][j];
+                wave_fold<NV>(v, lane);
+                const int vi0 = NV >= 64 ? lane * PL : (lane >> SH);
+                const bool writer = NV >= 64 || (lane & ((1 << SH) - 1)) == 0;
+                float tot[PL];
 #pragma unroll
-                    for (int q = 0; q < KS; ++q) total += red[gi & 1][rg * KS + q][vi];
+                for (int i = 0; i < PL; ++i) tot[i] = v[i];
+                if constexpr (KS > 1) {
+                    float* buf = red[gi & 1][wave];
+                    if (writer) {
+#pragma unroll
+                        for (int i = 0; i < PL; ++i) buf[vi0 + i] = tot[i];
+                    }
+                    __syncthreads();
+                    if (writer) {
+#pragma unroll
+                        for (int i = 0; i < PL; ++i) {
+                            float t = 0.f;
+#pragma unroll
+                            for (int q = 0; q < KS; ++q) t += red[gi & 1][rg * KS + q][vi0 + i];
+                            tot[i] = t;
+                        }
+                    }
                 }
-            }
-            // epilogue by the ks == 0 wave of each row group
-            if (ks == 0) {
+                if (ks != 0) continue;
+                // ---- epilogue by the ks == 0 wave of each row group
                 if constexpr (MODE == 0) {
-                    // g at even value index, u at the next one (1 << SH lanes above)
-                    const float u = __shfl_down(total, 1 << SH, MOE_WAVE);
-                    if (writer && (vi & 1) == 0) {
-                        const int rj = vi >> 1;
-                        const int r = rj / NT, j = rj % NT;
-                        const int row = rbase + r;
-                        if (row < row_end && j0 + j < c) {
-                            const float h = silu(total) * u;
-                            char* op = reinterpret_cast<char*>(a.out) +
-                                       ((size_t)(o + j0 + j) * a.N + row) * out_es;
-                            if constexpr (ACT == DT_F32) *reinterpret_cast<float*>(op) = h;
-                            else *reinterpret_cast<uint16_t*>(op) = f32_to_bf16(h);
+                    // g has an even value index and u the next one: in the same
+                    // lane when a lane holds two or more totals, else 1 << SH lanes up
+                    constexpr bool IN_LANE = PL >= 2;
+                    float up_v = 0.f;
+                    if constexpr (!IN_LANE) up_v = __shfl_down(tot[0], 1 << SH, MOE_WAVE);
+                    if (writer) {
+#pragma unroll
+                        for (int i = 0; i < PL; i += (IN_LANE ? 2 : 1)) {
+                            const int vi = vi0 + i;
+                            if ((vi & 1) != 0) continue;
+                            const float g = tot[i];
+                            const float uu = IN_LANE ? tot[(i + 1) % PL] : up_v;
+                            const int rj = vi >> 1;
+                            const int r = rj / NT, j = rj % NT;
+                            const int row = rbase + r;
+                            if (row < row_end && j < nt) {
+                                const float h = silu(g) * uu;
+                                char* op = reinterpret_cast<char*>(a.out) +
+                                           ((size_t)(o + j0 + j) * a.N + row) * out_es;
+                                if constexpr (ACT == DT_F32) *reinterpret_cast<float*>(op) = h;
+                                else *reinterpret_cast<uint16_t*>(op) = f32_to_bf16(h);
+                            }
                         }
                     }
                 } else {
                     if (writer) {
-                        const int r = vi / NT, j = vi % NT;
-                        const int row = rbase + r;
-                        if (row < row_end && j0 + j < c)
-                            reinterpret_cast<float*>(a.out)[(size_t)(o + j0 + j) * a.N + row] = total;
+#pragma unroll
+                        for (int i = 0; i < PL; ++i) {
+                            const int vi = vi0 + i;
+                            const int r = vi / NT, j = vi % NT;
+                            const int row = rbase + r;
+                            if (row < row_end && j < nt)
+                                reinterpret_cast<float*>(a.out)[(size_t)(o + j0 + j) * a.N + row] = tot[i];
+                        }
                     }
                 }
             }
@@ -332,63 +421,121 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 
 // ------------------------------------------------------------------ host side
 
-template <int WT, int ACT, int MODE, int NT, int KS>
-static hipError_t launch_one(const GemvArgs& a, int nexp, hipStream_t s) {
-    constexpr int R = (WT == DT_INT4) ? 2 : 2;
-    constexpr int MS = (WT == DT_INT4) ? 4 : 8;
-    dim3 grid((a.N + a.rows_per_block - 1) / a.rows_per_block, nexp);
-    hipLaunchKernelGGL((gemv_kernel<WT, ACT, MODE, NT, KS, R, MS>), grid, dim3(256), 0, s, a);
+namespace {
+
+struct Variant {
+    int ks, ms, nt, r;
+};
+
+int epl_of(int wt) { return wt == DT_F32 ? 4 : wt == DT_BF16 ? 8 : 32; }
+int dw_of(int wt) { return wt == DT_INT4 ? 16 : 4; }
+
+// Kernel shape for a given K: K split over KS waves, MS 16-byte steps per
+// wave, NT tokens per pass, R rows per iteration.  (KS, MS) cover the K steps;
+// (NT, R) are the largest that keep activation fragments + in-flight loads +
+// partial sums within ~220 VGPRs (no scratch at 2 waves per SIMD) with 8-16
+// loads of 16 B in flight per wave.
+Variant choose(int wt, int K, int G) {
+    const int steps = (K / epl_of(wt) + 63) / 64;
+    int ks, ms;
+    if (steps <= 1) { ks = 1; ms = 1; }
+    else if (steps <= 2) { ks = wt == DT_INT4 ? 2 : 1; ms = wt == DT_INT4 ? 1 : 2; }
+    else if (steps <= 4) { ks = wt == DT_INT4 ? 4 : 1; ms = wt == DT_INT4 ? 1 : 4; }
+    else if (steps <= 8) { ks = wt == DT_INT4 ? 4 : 2; ms = wt == DT_INT4 ? 2 : 4; }
+    else if (steps <= 16) { ks = 4; ms = 4; }
+    else if (steps <= 32 && wt != DT_INT4) { ks = 4; ms = 8; }
+    else return Variant{0, 0, 0, 0};
+    int nt, r;
+    const int mi = ms == 1 ? 0 : ms == 2 ? 1 : ms == 4 ? 2 : 3;
+    if (wt == DT_INT4) {
+        static const int t2[4][2] = {{4, 8}, {4, 2}, {1, 2}, {0, 0}};   // gate/up
+        static const int t1[4][2] = {{4, 8}, {4, 4}, {1, 4}, {0, 0}};   // down
+        nt = (G == 2 ? t2 : t1)[mi][0];
+        r = (G == 2 ? t2 : t1)[mi][1];
+    } else {
+        static const int t2[4][2] = {{8, 4}, {8, 4}, {8, 2}, {4, 1}};
+        static const int t1[4][2] = {{8, 8}, {8, 8}, {8, 4}, {4, 2}};
+        nt = (G == 2 ? t2 : t1)[mi][0];
+        r = (G == 2 ? t2 : t1)[mi][1];
+    }
+    return Variant{ks, ms, nt, r};
+}
+
+}  // namespace
+
+// Largest K the register-resident activation fragments can hold: 4 waves x
+// 8 steps x 64 lanes (bf16, fp32); 4 waves x 4 steps x 64 lanes for int4.
+int gemv_max_k(int wt) { return wt == DT_INT4 ? 4 * 4 * 64 * 32 : 4 * 8 * 64 * epl_of(wt); }
+
+template <int WT, int ACT, int MODE, int NT, int KS, int R, int MS>
+static hipError_t launch_v(const GemvArgs& a, int max_items, hipStream_t s) {
+    auto k = gemv_kernel<WT, ACT, MODE, NT, KS, R, MS>;
+    static int per_cu = 0, n_cu = 0;
+    if (per_cu == 0) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, 0) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        if (n_cu < 1) n_cu = 256;
+    }
+    int grid = per_cu * n_cu;
+    if (grid > max_items) grid = max_items;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-template <int WT, int ACT, int MODE, int NT>
-static hipError_t launch_ks(const GemvArgs& a, int nexp, int ks, hipStream_t s) {
-    if (ks == 1) return launch_one<WT, ACT, MODE, NT, 1>(a, nexp, s);
-    return launch_one<WT, ACT, MODE, NT, 4>(a, nexp, s);
-}
+#define GEMV_CASE(ks_, ms_, nt_, r_)                                                    \
+    if (v.ks == ks_ && v.ms == ms_ && v.nt == nt_ && v.r == r_)                         \
+        return launch_v<WT, ACT, MODE, nt_, ks_, r_, ms_>(a, max_items, s);
 
 template <int WT, int ACT, int MODE>
-static hipError_t launch_nt(const GemvArgs& a, int nexp, int ks, int nt, hipStream_t s) {
-    if (nt <= 1) return launch_ks<WT, ACT, MODE, 1>(a, nexp, ks, s);
-    if (nt <= 2) return launch_ks<WT, ACT, MODE, 2>(a, nexp, ks, s);
-    return launch_ks<WT, ACT, MODE, 4>(a, nexp, ks, s);
+static hipError_t launch_mode(const GemvArgs& a, const Variant& v, int max_items, hipStream_t s) {
+    // exactly the (ks, ms, nt, r) tuples choose() returns
+    if constexpr (WT == DT_INT4 && MODE == 0) {
+        GEMV_CASE(1, 1, 4, 8) GEMV_CASE(2, 1, 4, 8) GEMV_CASE(4, 1, 4, 8)
+        GEMV_CASE(4, 2, 4, 2) GEMV_CASE(4, 4, 1, 2)
+    } else if constexpr (WT == DT_INT4) {
+        GEMV_CASE(1, 1, 4, 8) GEMV_CASE(2, 1, 4, 8) GEMV_CASE(4, 1, 4, 8)
+        GEMV_CASE(4, 2, 4, 4) GEMV_CASE(4, 4, 1, 4)
+    } else if constexpr (MODE == 0) {
+        GEMV_CASE(1, 1, 8, 4) GEMV_CASE(1, 2, 8, 4) GEMV_CASE(1, 4, 8, 2)
+        GEMV_CASE(2, 4, 8, 2) GEMV_CASE(4, 4, 8, 2) GEMV_CASE(4, 8, 4, 1)
+    } else {
+        GEMV_CASE(1, 1, 8, 8) GEMV_CASE(1, 2, 8, 8) GEMV_CASE(1, 4, 8, 4)
+        GEMV_CASE(2, 4, 8, 4) GEMV_CASE(4, 4, 8, 4) GEMV_CASE(4, 8, 4, 2)
+    }
+    return hipErrorInvalidConfiguration;
 }
-
-int gemv_max_steps(int wt) { return wt == DT_INT4 ? 4 : 8; }
-int gemv_epl(int wt) { return wt == DT_F32 ? 4 : wt == DT_BF16 ? 8 : 32; }
-
-// Largest K the register-resident activation fragments can hold.
-int gemv_max_k(int wt) { return gemv_max_steps(wt) * 4 * 64 * gemv_epl(wt); }
-
-static int choose_ks(int wt, int K) {
-    const int nsteps = (K / gemv_epl(wt) + 63) / 64;
-    return nsteps <= gemv_max_steps(wt) ? 1 : 4;
-}
-
-static int choose_nt(int wt, int max_rows) {
-    const int cap = (wt == DT_INT4) ? 2 : 4;
-    int nt = 1;
-    while (nt < cap && nt < max_rows) nt *= 2;
-    return nt;
-}
+#undef GEMV_CASE
 
 hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, int max_rows,
                        hipStream_t s) {
-    const int ks = choose_ks(wt, a.K);
-    const int nt = choose_nt(wt, max_rows);
-    if (wt == DT_F32 && act == DT_F32) {
-        return mode == 0 ? launch_nt<DT_F32, DT_F32, 0>(a, nexp, ks, nt, s)
-                         : launch_nt<DT_F32, DT_F32, 1>(a, nexp, ks, nt, s);
-    }
-    if (wt == DT_BF16 && act == DT_BF16) {
-        return mode == 0 ? launch_nt<DT_BF16, DT_BF16, 0>(a, nexp, ks, nt, s)
-                         : launch_nt<DT_BF16, DT_BF16, 1>(a, nexp, ks, nt, s);
-    }
-    if (wt == DT_INT4 && act == DT_BF16) {
-        return mode == 0 ? launch_nt<DT_INT4, DT_BF16, 0>(a, nexp, ks, nt, s)
-                         : launch_nt<DT_INT4, DT_BF16, 1>(a, nexp, ks, nt, s);
-    }
+    (void)max_rows;
+    const Variant v = choose(wt, a.K, mode == 0 ? 2 : 1);
+    if (v.nt == 0) return hipErrorInvalidValue;
+    const int nrc = (a.N + a.rows_per_item - 1) / a.rows_per_item;
+    const int max_items = nexp * nrc;
+    if (wt == DT_F32 && act == DT_F32)
+        return mode == 0 ? launch_mode<DT_F32, DT_F32, 0>(a, v, max_items, s)
+                         : launch_mode<DT_F32, DT_F32, 1>(a, v, max_items, s);
+    if (wt == DT_BF16 && act == DT_BF16)
+        return mode == 0 ? launch_mode<DT_BF16, DT_BF16, 0>(a, v, max_items, s)
+                         : launch_mode<DT_BF16, DT_BF16, 1>(a, v, max_items, s);
+    if (wt == DT_INT4 && act == DT_BF16)
+        return mode == 0 ? launch_mode<DT_INT4, DT_BF16, 0>(a, v, max_items, s)
+                         : launch_mode<DT_INT4, DT_BF16, 1>(a, v, max_items, s);
     return hipErrorInvalidValue;
+}
+
+// Rows of one work item: a multiple of the rows a block covers per iteration.
+int gemv_rows_per_item(int wt, int mode, int K) {
+    const Variant v = choose(wt, K, mode == 0 ? 2 : 1);
+    const int per_iter = (4 / v.ks) * v.r;
+    int rows = per_iter;
+    while (rows < 16) rows += per_iter;
+    return rows;
 }
 
 }  // namespace moe

@@ -18,7 +18,7 @@ struct GemvArgs {
     const int32_t* counts;   // null: shared expert, all T rows, expert 0
     const int32_t* offsets;
     const int32_t* perm;     // mode 0 only: token = perm[p] / topk
-    int N, K, topk, T, tau, rows_per_block;
+    int N, K, topk, T, E, tau, rows_per_item;
 };
 
 hipError_t launch_route(int act, const void* x, const float* wg, const float* b, float* logits,
@@ -28,6 +28,7 @@ hipError_t launch_dispatch(const int32_t* idx, int32_t* counts, int32_t* offsets
 hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, int max_rows,
                        hipStream_t s);
 int gemv_max_k(int wt);
+int gemv_rows_per_item(int wt, int mode, int K);
 int mfma_bm();
 int mfma_max_tiles(int T, int k, int E);
 int mfma_ntiles_n(int mode, int N);
