@@ -186,7 +186,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mixtral_decode",
-                    choices=["mixtral_decode", "fine_int4_decode", "stack4_layer0"])
+                    choices=["mixtral_decode", "mixtral_prefill", "fine_int4_decode",
+                             "stack4_layer0"])
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tau", type=int, default=0)
@@ -214,6 +215,15 @@ def main():
     ms = wall * 1e3 / args.steps
     value = cfg.T * args.steps / wall
     achieved = ffn_bytes / (ffn_mean * 1e-3) / 1e9
+    if cfg.T * cfg.k / max(U, 1) > 64:      # prefill-sized groups: MFMA-bound
+        roof = dict(roofline_obj("mfma", ffn_flops / (ffn_mean * 1e-3) / 1e12,
+                                 BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
+                    kernel="expert FFN step (MFMA gate/up + down)", flops_per_launch=ffn_flops,
+                    launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5))
+    else:
+        roof = dict(roofline_obj("hbm", achieved, HBM_PEAK_GBS, "GB/s"),
+                    kernel="expert FFN step (gate/up + down GEMV)", bytes_per_launch=ffn_bytes,
+                    launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5))
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -224,10 +234,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "F": cfg.F, "weights": cfg.wt, "shared_experts": cfg.n_shared,
                    "active_experts": U, "tau": args.tau, "seed": 0},
-        "roofline": dict(roofline_obj("hbm", achieved, HBM_PEAK_GBS, "GB/s"),
-                         kernel="expert FFN step (gate/up + down GEMV)",
-                         bytes_per_launch=ffn_bytes, launch_ms=round(ffn_mean, 5),
-                         launch_ms_median=round(ffn_med, 5)),
+        "roofline": roof,
         "layer_call_ms_per_step": round(wall_layer * 1e3 / args.steps, 4),
     }
     log(json.dumps(out))

@@ -67,7 +67,7 @@ typedef enum {
  * Limits (MOE_EINVAL otherwise): T >= 0, 1 <= k <= E <= 256, k <= 16,
  *   d, F >= 8 and multiples of 8; int4: d and F multiples of 128.
  * Limits of this build (MOE_EUNSUPPORTED otherwise): d, F <= 16384 (bf16),
- *   <= 8192 (fp32), <= 16384 (int4). */
+ *   <= 8192 (fp32), <= 16384 (int4); bf16: T*k*F*2 and T*d*2 bytes < 2 GiB. */
 typedef struct {
     int32_t T, d, E, k, F;
     int32_t n_shared;

@@ -87,6 +87,10 @@ int check_shape(const moe_shape* s, char* err, size_t err_len) {
     if (!ok_combo)
         return fail(err, err_len, MOE_EUNSUPPORTED, "activation dtype %d with weight dtype %d is not built",
                     s->act, s->wt);
+    // the MFMA path addresses x and h with 32-bit buffer offsets
+    if (s->wt == MOE_BF16 && ((size_t)s->T * s->k * s->F * 2 >= ((size_t)1 << 31) ||
+                              (size_t)s->T * s->d * 2 >= ((size_t)1 << 31)))
+        return fail(err, err_len, MOE_EUNSUPPORTED, "T*k*F and T*d bf16 buffers must stay below 2 GiB");
     const int kmax = gemv_max_k(s->wt);
     if (s->d > kmax || s->F > kmax)
         return fail(err, err_len, MOE_EUNSUPPORTED, "d=%d / F=%d exceed this build's limit %d for this dtype",
@@ -165,7 +169,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     rc = hip_check(launch_gemv(s->wt, s->act, 0, g, s->E, max_rows_gemv, st), st, "gemv gate/up", err, err_len);
     if (rc) return rc;
     if (use_mfma) {
-        rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, st),
+        rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, s->T, st),
                        st, "mfma gate/up", err, err_len);
         if (rc) return rc;
     }
@@ -177,7 +181,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     rc = hip_check(launch_gemv(s->wt, s->act, 1, g, s->E, max_rows_gemv, st), st, "gemv down", err, err_len);
     if (rc) return rc;
     if (use_mfma) {
-        rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, st),
+        rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, s->T * s->k, st),
                        st, "mfma down", err, err_len);
         if (rc) return rc;
     }

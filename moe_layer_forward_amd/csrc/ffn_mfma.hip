@@ -6,22 +6,28 @@
 // contiguous ([P2] §2.1, expert-affinity scheduling).
 //
 // gfx950 design:
-//  * a device-side tile plan (one small kernel) turns counts/offsets into a list
-//    of 128-row M-tiles, one expert per tile, so no host round trip is needed
-//    and idle grid slots exit at once;
-//  * 256 threads = 4 wave64s in a 2x2 arrangement own a 128x128 output tile;
-//    each wave computes 64x64 with v_mfma_f32_32x32x16_bf16 (fp32 accumulate);
-//  * K advances 64 at a time through double-buffered LDS tiles whose rows are
-//    padded by 16 bytes so the 16-byte fragment reads of 32 consecutive rows
-//    fall in distinct banks; the next K tile is fetched into VGPRs while the
-//    current one feeds the MFMAs;
-//  * gate and up share the A tile: the B tile holds 64 gate rows then the 64
-//    matching up rows, so every lane owns g and u of the same (row, f) and the
-//    SwiGLU epilogue needs no data exchange;
-//  * A rows of the gate/up GEMM are gathered from x through the permutation
-//    (no copy of the dispatched activations is ever made);
-//  * grid slots are remapped so consecutive tiles land on one XCD and share
-//    its L2.
+//  * a device-side plan (one small kernel) turns counts/offsets into a list of
+//    256-row M-tiles, one expert per tile: no host round trip;
+//  * a persistent grid of one 256-thread block per CU walks the (M-tile,
+//    N-tile) list.  In every round the 32 CUs of one XCD take 32 consecutive
+//    tiles, and tiles are ordered in groups of 8 M-tiles x all N-tiles with M
+//    fastest, so concurrent blocks of an XCD share A and B panels in its L2;
+//  * block tile 256 x 256; 4 wave64s in a 2x2 arrangement each own
+//    128 x 128 = 4 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (fp32);
+//  * LDS holds four stages of A and B of K = 32 each (128 KiB): tiles are
+//    copied global -> LDS by buffer_load ... lds (no VGPR staging) three K
+//    steps ahead of the MFMAs, with one barrier per K step;
+//  * the 16-byte chunks of each 64-byte LDS row are XOR-swizzled by
+//    (row/4)&3, so 16-byte fragment reads of 16 consecutive rows are
+//    conflict-free; each DMA lane simply fetches the chunk that belongs at its
+//    fixed LDS slot;
+//  * the buffer range check returns zeros for gathered token rows past the
+//    group end, weight rows past N and the K tail, so no load is branched;
+//  * gate and up share the A tile: the B tile holds 128 gate rows then the 128
+//    matching up rows, so each lane owns g and u of the same (row, f) and the
+//    SwiGLU epilogue needs no exchange;
+//  * A rows of the gate/up GEMM are gathered from x through the permutation;
+//    no copy of the dispatched activations is ever made.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,15 +35,18 @@ namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int MF_BM = 128;
-constexpr int MF_BN = 128;
-constexpr int MF_BK = 64;
-constexpr int MF_LDK = MF_BK + 8;   // padded LDS row, bf16 elements (144 bytes)
+constexpr int MF_BM = 256;
+constexpr int MF_BN = 256;
+constexpr int MF_BK = 32;         // K per LDS stage
+constexpr int MF_NS = 4;          // LDS stages (3 K steps of prefetch in flight)
+constexpr int MF_GM = 8;          // M-tiles per scheduling group
+constexpr uint32_t MF_OOB = 0x80000000u;   // beyond any buffer: the range check yields 0
 
 int mfma_bm() { return MF_BM; }
 int mfma_max_tiles(int T, int k, int E) { return (T * k + MF_BM - 1) / MF_BM + E; }
-int mfma_ntiles_n(int mode, int N) { return mode == 0 ? (N + 63) / 64 : (N + MF_BN - 1) / MF_BN; }
+int mfma_ntiles_n(int mode, int N) { return mode == 0 ? (N + 127) / 128 : (N + MF_BN - 1) / MF_BN; }
 
 __global__ __launch_bounds__(256) void mfma_plan_kernel(const int32_t* __restrict__ counts,
                                                        const int32_t* __restrict__ offsets, int E,
@@ -79,131 +88,204 @@ struct MfmaArgs {
     void* out;               // h bf16 [T*k][N] (mode 0) or y_perm fp32 [T*k][N] (mode 1)
     const int32_t* perm;
     const int32_t* tiles;    // plan: expert[max_mt], row0[max_mt], rows[max_mt], n_mt
-    int N, K, topk, max_mt;
+    int N, K, topk, max_mt, in_rows;
 };
 
-template <int MODE>
-__global__ __launch_bounds__(256, 2) void mfma_ffn_kernel(MfmaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][MF_BM][MF_LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][MF_BN][MF_LDK];
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
 
-    const uint32_t L = xcd_remap(blockIdx.x, gridDim.x);
-    const int mt = L % a.max_mt;
-    const int nt = L / a.max_mt;
-    const int n_mt = a.tiles[3 * a.max_mt];
-    if (mt >= n_mt) return;
-    const int e = a.tiles[mt];
-    const int p0 = a.tiles[a.max_mt + mt];
-    const int rows = a.tiles[2 * a.max_mt + mt];
+// Raw buffer descriptor (base, 32-bit range, default format) as four dwords.
+__device__ __forceinline__ int32x4_t make_desc(const void* base, uint32_t nbytes) {
+    const uint64_t b = (uint64_t)base;
+    int32x4_t r;   // wave-uniform by construction: keep it in SGPRs
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu));
+    r.z = __builtin_amdgcn_readfirstlane((int)nbytes);
+    r.w = 0x00020000;
+    return r;
+}
+
+// 16 bytes per lane straight from global memory into LDS: lane l of the wave
+// lands at lds_addr + 16*l; an offset the range check rejects writes zeros.
+// Issued as inline assembly so that the compiler's wait-count pass does not
+// model it: the kernel waits for these copies itself (vmcnt + s_barrier),
+// which lets LDS fragment reads of one stage proceed while later stages are
+// still being filled.
+__device__ __forceinline__ void dma16(const int32x4_t& desc, uint32_t off, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(off), "s"(desc), "s"(lds_addr)
+                 : "memory");
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(size_t)((__attribute__((address_space(3))) const T*)(p)));
+}
+
+// wait until at most n (0, 8 or 16) vector-memory operations are outstanding
+__device__ __forceinline__ void wait_vm(int n) {
+    if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
+    else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
+}
+
+__device__ __forceinline__ void block_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Swizzled element offset of logical 16-byte chunk `ch` (0..3) of tile row
+// `row` in a stage of 32-element (64-byte) rows: four rows share one 256-byte
+// bank line and the chunk is XORed with (row/4)&3, so 16 consecutive rows
+// reading the same logical chunk hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row, int ch) {
+    return row * MF_BK + ((ch ^ ((row >> 2) & 3)) << 3);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[MF_NS][MF_BM * MF_BK];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[MF_NS][MF_BN * MF_BK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int K = a.K, N = a.N;
-
-    // global -> LDS assignment: 4 rows per thread (r = tid/8 + 32q), one 16 B column chunk
-    const int lrow = tid >> 3, lchunk = tid & 7;
-    const uint16_t* arow[4];
-    const uint16_t* brow[4];
-    const size_t wbase = (size_t)e * N * K;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int r = lrow + 32 * q;
-        const int rr = (r < rows) ? r : 0;
-        if (MODE == 0) {
-            const int tok = a.perm[p0 + rr] / a.topk;
-            arow[q] = a.in + (size_t)tok * K;
-        } else {
-            arow[q] = a.in + (size_t)(p0 + rr) * K;
-        }
-        int n;
-        const uint16_t* W;
-        if (MODE == 0) {
-            const int f0 = nt * 64;
-            n = f0 + (r & 63);
-            W = (r < 64) ? a.w0 : a.w1;
-        } else {
-            n = nt * MF_BN + r;
-            W = a.w0;
-        }
-        if (n >= N) n = N - 1;
-        brow[q] = W + wbase + (size_t)n * K;
-    }
-
-    floatx16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
+    const int n_mt = a.tiles[3 * a.max_mt];
+    const int nN = (MODE == 0) ? (N + 127) / 128 : (N + MF_BN - 1) / MF_BN;
+    const int total = n_mt * nN;
+    const int nblk = gridDim.x;
+    // blocks are dealt round-robin to 8 XCDs: give XCD x the slots [x*per, (x+1)*per)
+    const int per = nblk / 8;
+    const int slot = (nblk % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
+    const uint32_t row_bytes = (uint32_t)K * 2u;
     const int nk = (K + MF_BK - 1) / MF_BK;
-    uint4 ra[4], rb[4];
-    auto gload = [&](int kt) {
-        const int kk = kt * MF_BK + lchunk * 8;
-        const bool ok = kk < K;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            ra[q] = ok ? *reinterpret_cast<const uint4*>(arow[q] + kk) : make_uint4(0, 0, 0, 0);
-            rb[q] = ok ? *reinterpret_cast<const uint4*>(brow[q] + kk) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<uint4*>(&sA[buf][lrow + 32 * q][lchunk * 8]) = ra[q];
-            *reinterpret_cast<uint4*>(&sB[buf][lrow + 32 * q][lchunk * 8]) = rb[q];
-        }
-    };
+    // DMA: each wave instruction fills 16 tile rows x 64 B; this lane owns tile
+    // row wave*64 + i*16 + lane/4, physical chunk lane%4
+    const int dma_row = wave * 64 + (lane >> 2);
+    const int32x4_t RA = make_desc(a.in, (uint32_t)a.in_rows * row_bytes);
+    const uint32_t wmat = (uint32_t)N * row_bytes;
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-        for (int ks = 0; ks < MF_BK / 16; ++ks) {
-            const int kc = ks * 16 + (lane >> 5) * 8;
-            bf16x8_t af[2], bfv[2];
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-                af[mi] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][wm * 64 + mi * 32 + (lane & 31)][kc]);
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni) {
-                const int br = (MODE == 0) ? (ni * 64 + wn * 32 + (lane & 31)) : (wn * 64 + ni * 32 + (lane & 31));
-                bfv[ni] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][br][kc]);
-            }
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfv[ni], acc[mi][ni], 0, 0, 0);
-        }
-        if (kt + 1 < nk) lstore(buf ^ 1);
-        __syncthreads();
-    }
+    for (int L = slot; L < total; L += nblk) {
+        // grouped order: GM M-tiles x all N-tiles, M fastest
+        const int grp = L / (MF_GM * nN);
+        const int gm0 = grp * MF_GM;
+        const int gsz = min(MF_GM, n_mt - gm0);
+        const int rem = L - grp * MF_GM * nN;
+        const int mt = gm0 + rem % gsz;
+        const int nt = rem / gsz;
 
-    // epilogue; accumulator element v of lane l: column l%32, row 8*(v/4) + 4*(l/32) + v%4
+        const int e = a.tiles[mt];
+        const int p0 = a.tiles[a.max_mt + mt];
+        const int rows = a.tiles[2 * a.max_mt + mt];
+
+        // B rows of this wave: mode 0 waves 0-1 hold gate rows, waves 2-3 up rows
+        const uint16_t* wsrc = (MODE == 0 && wave >= 2) ? a.w1 : a.w0;
+        const int32x4_t RB = make_desc(wsrc + (size_t)e * N * K, wmat);
+        uint32_t aoff[4], boff[4];
+        int kcol[4];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (row >= rows) continue;
-            const size_t prow = (size_t)(p0 + row) * N;
-            if (MODE == 0) {
-                const int f = nt * 64 + wn * 32 + (lane & 31);
-                if (f < N) {
-                    const float h = silu(acc[mi][0][v]) * acc[mi][1][v];
-                    reinterpret_cast<uint16_t*>(a.out)[prow + f] = f32_to_bf16(h);
-                }
+        for (int i = 0; i < 4; ++i) {
+            const int r = dma_row + i * 16;
+            const int ch = (lane & 3) ^ ((r >> 2) & 3);
+            kcol[i] = ch * 8;
+            if (r < rows) {
+                const int src = (MODE == 0) ? a.perm[p0 + r] / a.topk : p0 + r;
+                aoff[i] = (uint32_t)src * row_bytes + (uint32_t)ch * 16u;
             } else {
+                aoff[i] = MF_OOB;
+            }
+            const int n = (MODE == 0) ? nt * 128 + (r & 127) : nt * MF_BN + r;
+            boff[i] = (n < N) ? (uint32_t)n * row_bytes + (uint32_t)ch * 16u : MF_OOB;
+        }
+        auto issue = [&](int kt) {
+            const int st = kt % MF_NS;
+            const uint32_t kb = (uint32_t)kt * (MF_BK * 2);
+            const int k0 = kt * MF_BK;
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const int n = nt * MF_BN + wn * 64 + ni * 32 + (lane & 31);
-                    if (n < N) reinterpret_cast<float*>(a.out)[prow + n] = acc[mi][ni][v];
+            for (int i = 0; i < 4; ++i) {
+                const bool kok = k0 + kcol[i] < K;
+                const int r0 = wave * 64 + i * 16;
+                dma16(RA, (kok && aoff[i] != MF_OOB) ? aoff[i] + kb : MF_OOB, lds_addr(&sA[st][r0 * MF_BK]));
+                dma16(RB, (kok && boff[i] != MF_OOB) ? boff[i] + kb : MF_OOB, lds_addr(&sB[st][r0 * MF_BK]));
+            }
+        };
+
+        floatx16 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+        // drain this wave's earlier memory traffic (the previous tile's output
+        // stores share the counter) and make sure every wave is done reading
+        // the stages before they are refilled
+        wait_vm(0);
+        block_barrier();
+        for (int kt = 0; kt < MF_NS - 1 && kt < nk; ++kt) issue(kt);
+
+        for (int kt = 0; kt < nk; ++kt) {
+            // copies issued after stage kt: stages kt+1 .. min(kt+NS-2, nk-1), 8 each
+            const int later = min(MF_NS - 2, nk - 1 - kt);
+            wait_vm(8 * later);
+            block_barrier();          // stage kt landed for every wave; stage kt-1 is free
+            if (kt + MF_NS - 1 < nk) issue(kt + MF_NS - 1);
+            const uint16_t* A = sA[kt % MF_NS];
+            const uint16_t* B = sB[kt % MF_NS];
+            bf16x8_t fa[MF_BK / 16][4], fb[MF_BK / 16][4];
+#pragma unroll
+            for (int ks = 0; ks < MF_BK / 16; ++ks) {
+                const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+                    fa[ks][mi] = *reinterpret_cast<const bf16x8_t*>(&A[swz(wm * 128 + mi * 32 + (lane & 31), ch)]);
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni) {
+                    const int r = (MODE == 0) ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 + (lane & 31))
+                                              : (wn * 128 + ni * 32 + (lane & 31));
+                    fb[ks][ni] = *reinterpret_cast<const bf16x8_t*>(&B[swz(r, ch)]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);   // all 16 fragment reads go out first
+#pragma unroll
+            for (int ks = 0; ks < MF_BK / 16; ++ks)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][mi], fb[ks][ni],
+                                                                               acc[mi][ni], 0, 0, 0);
+        }
+
+        // ---- epilogue; accumulator element v of lane l: column l%32, row 8*(v/4) + 4*(l/32) + v%4
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row >= rows) continue;
+                const size_t prow = (size_t)(p0 + row) * N;
+                if (MODE == 0) {
+#pragma unroll
+                    for (int nj = 0; nj < 2; ++nj) {
+                        const int f = nt * 128 + wn * 64 + nj * 32 + (lane & 31);
+                        if (f < N) {
+                            const float h = silu(acc[mi][nj][v]) * acc[mi][nj + 2][v];
+                            reinterpret_cast<uint16_t*>(a.out)[prow + f] = f32_to_bf16(h);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        const int n = nt * MF_BN + wn * 128 + ni * 32 + (lane & 31);
+                        if (n < N) reinterpret_cast<float*>(a.out)[prow + n] = acc[mi][ni][v];
+                    }
                 }
             }
         }
@@ -219,7 +301,7 @@ hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int E
 
 hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void* in, void* out,
                            const int32_t* perm, const int32_t* tiles, int N, int K, int topk,
-                           int max_mt, hipStream_t s) {
+                           int max_mt, int in_rows, hipStream_t s) {
     MfmaArgs a;
     a.w0 = reinterpret_cast<const uint16_t*>(w0);
     a.w1 = reinterpret_cast<const uint16_t*>(w1);
@@ -231,7 +313,16 @@ hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void*
     a.K = K;
     a.topk = topk;
     a.max_mt = max_mt;
-    const int grid = max_mt * mfma_ntiles_n(mode, N);
+    a.in_rows = in_rows;
+    static int n_cu = 0;
+    if (n_cu == 0) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+            n_cu = 256;
+    }
+    const int slots = max_mt * mfma_ntiles_n(mode, N);
+    const int grid = slots < n_cu ? slots : n_cu;
     if (mode == 0)
         hipLaunchKernelGGL(mfma_ffn_kernel<0>, dim3(grid), dim3(256), 0, s, a);
     else
