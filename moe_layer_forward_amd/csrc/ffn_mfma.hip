@@ -28,6 +28,8 @@
 //    SwiGLU epilogue needs no exchange;
 //  * A rows of the gate/up GEMM are gathered from x through the permutation;
 //    no copy of the dispatched activations is ever made.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -123,9 +125,11 @@ __device__ __forceinline__ uint32_t lds_addr(const T* p) {
         (uint32_t)(size_t)((__attribute__((address_space(3))) const T*)(p)));
 }
 
-// wait until at most n (0, 8 or 16) vector-memory operations are outstanding
+// wait until at most n (0, 8, 16, 24 or 32) vector-memory operations are outstanding
 __device__ __forceinline__ void wait_vm(int n) {
-    if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);        // vmcnt(16)
+    if (n >= 32) __builtin_amdgcn_s_waitcnt(0x8F70);        // vmcnt(32)
+    else if (n >= 24) __builtin_amdgcn_s_waitcnt(0x4F78);   // vmcnt(24)
+    else if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
     else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
     else __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
 }
@@ -202,19 +206,6 @@ __global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
             const int n = (MODE == 0) ? nt * 128 + (r & 127) : nt * MF_BN + r;
             boff[i] = (n < N) ? (uint32_t)n * row_bytes + (uint32_t)ch * 16u : MF_OOB;
         }
-        auto issue = [&](int kt) {
-            const int st = kt % MF_NS;
-            const uint32_t kb = (uint32_t)kt * (MF_BK * 2);
-            const int k0 = kt * MF_BK;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool kok = k0 + kcol[i] < K;
-                const int r0 = wave * 64 + i * 16;
-                dma16(RA, (kok && aoff[i] != MF_OOB) ? aoff[i] + kb : MF_OOB, lds_addr(&sA[st][r0 * MF_BK]));
-                dma16(RB, (kok && boff[i] != MF_OOB) ? boff[i] + kb : MF_OOB, lds_addr(&sB[st][r0 * MF_BK]));
-            }
-        };
-
         floatx16 acc[4][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -223,44 +214,89 @@ __global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+        // fragments of one stage: [ks][mi] for A, [ks][ni] for B
+        bf16x8_t fa[2][MF_BK / 16][4], fb[2][MF_BK / 16][4];
+        auto read_frag = [&](int st, int sl, int q) {   // q: 0..15, A first then B per ks
+            const int ks = q >> 3, j = q & 3;
+            const int ch = ks * 2 + (lane >> 5);
+            if ((q & 4) == 0) {
+                fa[sl][ks][j] = *reinterpret_cast<const bf16x8_t*>(
+                    &sA[st][swz(wm * 128 + j * 32 + (lane & 31), ch)]);
+            } else {
+                const int r = (MODE == 0) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + (lane & 31))
+                                          : (wn * 128 + j * 32 + (lane & 31));
+                fb[sl][ks][j] = *reinterpret_cast<const bf16x8_t*>(&sB[st][swz(r, ch)]);
+            }
+        };
+        auto mma = [&](int sl, int m) {                 // m: 0..31 = (ks, mi, ni)
+            const int ks = m >> 4, mi = (m >> 2) & 3, ni = m & 3;
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][ks][mi], fb[sl][ks][ni],
+                                                                   acc[mi][ni], 0, 0, 0);
+        };
+        auto issue_one = [&](int kt, int i) {          // DMA i (0..7) of K step kt
+            const int st = kt % MF_NS;
+            const uint32_t kb = (uint32_t)kt * (MF_BK * 2);
+            const int k0 = kt * MF_BK;
+            const int ii = i >> 1;
+            const int r0 = wave * 64 + ii * 16;
+            if ((i & 1) == 0) {
+                const bool kok = k0 + kcol[ii] < K;
+                dma16(RA, (kok && aoff[ii] != MF_OOB) ? aoff[ii] + kb : MF_OOB, lds_addr(&sA[st][r0 * MF_BK]));
+            } else {
+                const bool kok = k0 + kcol[ii] < K;
+                dma16(RB, (kok && boff[ii] != MF_OOB) ? boff[ii] + kb : MF_OOB, lds_addr(&sB[st][r0 * MF_BK]));
+            }
+        };
+
         // drain this wave's earlier memory traffic (the previous tile's output
         // stores share the counter) and make sure every wave is done reading
         // the stages before they are refilled
         wait_vm(0);
         block_barrier();
-        for (int kt = 0; kt < MF_NS - 1 && kt < nk; ++kt) issue(kt);
+        // Copies of K steps >= nk read out of range and store zeros, so every
+        // step below issues exactly 8 copies and the wait counts are constant.
+#pragma unroll
+        for (int kt = 0; kt < MF_NS; ++kt)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) issue_one(kt, i);
+        wait_vm(8 * (MF_NS - 1));    // stage 0 landed; stages 1..NS-1 may still fly
+        block_barrier();
+#pragma unroll
+        for (int q = 0; q < 16; ++q) read_frag(0, 0, q);
 
-        for (int kt = 0; kt < nk; ++kt) {
-            // copies issued after stage kt: stages kt+1 .. min(kt+NS-2, nk-1), 8 each
-            const int later = min(MF_NS - 2, nk - 1 - kt);
-            wait_vm(8 * later);
-            block_barrier();          // stage kt landed for every wave; stage kt-1 is free
-            if (kt + MF_NS - 1 < nk) issue(kt + MF_NS - 1);
-            const uint16_t* A = sA[kt % MF_NS];
-            const uint16_t* B = sB[kt % MF_NS];
-            bf16x8_t fa[MF_BK / 16][4], fb[MF_BK / 16][4];
+        // Software pipeline, per K step kt (fragments of stage kt already in
+        // register slot kt&1):
+        //   8 MFMAs | wait: stage kt+1 landed (this wave), own reads done |
+        //   barrier | 24 MFMAs interleaved with the 8 copies of stage kt+4 into
+        //   the buffer stage kt vacated (one per three MFMAs) and the 16 reads
+        //   of stage kt+1.
+        // nk is rounded up to even: an extra step multiplies zero fragments.
+        auto step = [&](int kt, auto slc) {
+            constexpr int sl = decltype(slc)::value;
 #pragma unroll
-            for (int ks = 0; ks < MF_BK / 16; ++ks) {
-                const int ch = ks * 2 + (lane >> 5);
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    fa[ks][mi] = *reinterpret_cast<const bf16x8_t*>(&A[swz(wm * 128 + mi * 32 + (lane & 31), ch)]);
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni) {
-                    const int r = (MODE == 0) ? ((ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 + (lane & 31))
-                                              : (wn * 128 + ni * 32 + (lane & 31));
-                    fb[ks][ni] = *reinterpret_cast<const bf16x8_t*>(&B[swz(r, ch)]);
-                }
+            for (int m = 0; m < 8; ++m) {
+                mma(sl, m);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);   // all 16 fragment reads go out first
+            wait_vm(8 * (MF_NS - 2));                      // stage kt+1 landed
+            __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): own reads of stage kt done
+            block_barrier();
+            // one copy every third MFMA, the 16 reads in the other slots: copies
+            // in a burst overflow the texture-address FIFO and stall the MFMAs
 #pragma unroll
-            for (int ks = 0; ks < MF_BK / 16; ++ks)
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][mi], fb[ks][ni],
-                                                                               acc[mi][ni], 0, 0, 0);
+            for (int m = 8; m < 32; ++m) {
+                mma(sl, m);
+                __builtin_amdgcn_sched_barrier(0);
+                const int j = m - 8;                       // 0..23
+                if (j % 3 == 0) issue_one(kt + MF_NS, j / 3);
+                else read_frag((kt + 1) % MF_NS, sl ^ 1, j - j / 3 - 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        const int nk2 = (nk + 1) & ~1;
+        for (int kt = 0; kt < nk2; kt += 2) {
+            step(kt, std::integral_constant<int, 0>{});
+            step(kt + 1, std::integral_constant<int, 1>{});
         }
 
         // ---- epilogue; accumulator element v of lane l: column l%32, row 8*(v/4) + 4*(l/32) + v%4
