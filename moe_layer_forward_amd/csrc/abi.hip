@@ -165,7 +165,8 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     g.w0 = w->w_gate; g.w1 = w->w_up;
     g.s0 = (const uint16_t*)w->s_gate; g.s1 = (const uint16_t*)w->s_up;
     g.in = x; g.out = h; g.N = s->F; g.K = s->d;
-    g.rows_per_item = gemv_rows_per_item(s->wt, 0, g.K);
+    const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
+    g.rows_per_item = gemv_rows_per_item(s->wt, 0, g.K, g.N, active);
     rc = hip_check(launch_gemv(s->wt, s->act, 0, g, s->E, max_rows_gemv, st), st, "gemv gate/up", err, err_len);
     if (rc) return rc;
     if (use_mfma) {
@@ -177,7 +178,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     g.w0 = w->w_down; g.w1 = nullptr;
     g.s0 = (const uint16_t*)w->s_down; g.s1 = nullptr;
     g.in = h; g.out = y_perm; g.N = s->d; g.K = s->F;
-    g.rows_per_item = gemv_rows_per_item(s->wt, 1, g.K);
+    g.rows_per_item = gemv_rows_per_item(s->wt, 1, g.K, g.N, active);
     rc = hip_check(launch_gemv(s->wt, s->act, 1, g, s->E, max_rows_gemv, st), st, "gemv down", err, err_len);
     if (rc) return rc;
     if (use_mfma) {
@@ -194,13 +195,13 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
         q.w0 = w->sh_gate; q.w1 = w->sh_up;
         q.s0 = (const uint16_t*)w->sh_s_gate; q.s1 = (const uint16_t*)w->sh_s_up;
         q.in = x; q.out = hs; q.N = s->F; q.K = s->d;
-        q.rows_per_item = gemv_rows_per_item(s->wt, 0, q.K);
+        q.rows_per_item = gemv_rows_per_item(s->wt, 0, q.K, q.N, 1);
         rc = hip_check(launch_gemv(s->wt, s->act, 0, q, 1, s->T, st), st, "gemv shared gate/up", err, err_len);
         if (rc) return rc;
         q.w0 = w->sh_down; q.w1 = nullptr;
         q.s0 = (const uint16_t*)w->sh_s_down; q.s1 = nullptr;
         q.in = hs; q.out = y_shared; q.N = s->d; q.K = s->F;
-        q.rows_per_item = gemv_rows_per_item(s->wt, 1, q.K);
+        q.rows_per_item = gemv_rows_per_item(s->wt, 1, q.K, q.N, 1);
         rc = hip_check(launch_gemv(s->wt, s->act, 1, q, 1, s->T, st), st, "gemv shared down", err, err_len);
         if (rc) return rc;
     }

@@ -20,11 +20,13 @@
 //  * the activation rows of the expert's group (NT tokens per pass) live in
 //    VGPRs for the lane's K positions, loaded once and reused for every row;
 //  * bf16: one v_dot2_f32_bf16 per weight pair per token, no conversions;
-//  * int4-g128: codes are XORed with 0x8 (two's complement -> offset binary),
-//    each nibble pair is OR-ed into the mantissa of bf16 128.0 (0x4300|u is
-//    exactly 128+u), dotted with the matching activation pair, and the constant
-//    136*sum(x) is subtracted once per 32-element chunk before the fp16 group
-//    scale is applied: ~2 VALU ops per weight at 2 tokens;
+//  * int4-g128: each nibble pair is masked out of the packed dword and XORed
+//    with 0x43084308, which flips the nibbles' sign bits (two's complement ->
+//    offset binary, q+8) and writes the exponent of bf16 128.0 above them, so
+//    each half is exactly the bf16 value 128+q+8; it is dotted with the
+//    matching activation pair and 136*sum(x) is subtracted once per 32-element
+//    chunk before the fp16 group scale is applied: ~2 VALU ops per weight at
+//    2 tokens;
 //  * per-lane partials of R rows x NT tokens (x2 for gate/up) are folded with a
 //    transposing wave reduction; with KS > 1 the K range is split over KS
 //    waves of the block and summed through LDS;
@@ -32,6 +34,8 @@
 //    in the activation dtype; the down pass stores fp32 rows of y_perm.
 // Experts with c_e == 0 never touch their weights, so the bytes moved are the
 // batch union of the selected experts' weights.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -159,16 +163,17 @@ __device__ __forceinline__ void load_x(uint32_t (&dst)[(XDw<WT, ACT>::v)], const
     }
 }
 
-// Partial dot product of one 16-byte weight chunk with the first nt of NT
-// activation fragments (nt is wave-uniform, so skipped tokens cost nothing).
-template <int WT, int ACT, int NT>
+// Partial dot product of one 16-byte weight chunk with the first NA of NT
+// activation fragments (NA, the tokens present in this pass, is a template
+// parameter so the token loops carry no branches).
+template <int WT, int ACT, int NT, int NA>
 __device__ __forceinline__ void chunk_dot(const uint4& wq, const uint32_t (*xf)[(XDw<WT, ACT>::v)],
-                                          const float* xs, float scale, float (&acc)[NT], int nt) {
+                                          const float* xs, float scale, float (&acc)[NT]) {
     const uint32_t w[4] = {wq.x, wq.y, wq.z, wq.w};
     if constexpr (WT == DT_F32) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            if (j >= nt) break;
+            if (j >= NA) break;
             float a = acc[j];
 #pragma unroll
             for (int i = 0; i < 4; ++i) a = fmaf(__uint_as_float(w[i]), __uint_as_float(xf[j][i]), a);
@@ -177,7 +182,7 @@ __device__ __forceinline__ void chunk_dot(const uint4& wq, const uint32_t (*xf)[
     } else if constexpr (WT == DT_BF16) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            if (j >= nt) break;
+            if (j >= NA) break;
             float a = acc[j];
 #pragma unroll
             for (int i = 0; i < 4; ++i) a = dot2_bf16(w[i], xf[j][i], a);
@@ -190,13 +195,16 @@ __device__ __forceinline__ void chunk_dot(const uint4& wq, const uint32_t (*xf)[
         for (int j = 0; j < NT; ++j) part[j] = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t u = w[i] ^ 0x88888888u;   // q + 8 in every nibble
+            // nibbles s and s+4 of the dword as the bf16 pair (128 + q + 8): the
+            // mask keeps the two nibbles, the XOR flips their sign bit (two's
+            // complement -> offset binary) and sets the exponent of 128.0 in
+            // the zero bits above them -- one v_bitop3 per pair
             uint32_t m[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) m[s] = ((u >> (4 * s)) & 0x000f000fu) | 0x43004300u;
+            for (int s = 0; s < 4; ++s) m[s] = ((w[i] >> (4 * s)) & 0x000f000fu) ^ 0x43084308u;
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
-                if (j >= nt) break;
+                if (j >= NA) break;
                 float a = part[j];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) a = dot2_bf16(m[s], xf[j][4 * i + s], a);
@@ -205,7 +213,7 @@ __device__ __forceinline__ void chunk_dot(const uint4& wq, const uint32_t (*xf)[
         }
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-            if (j >= nt) break;
+            if (j >= NA) break;
             acc[j] = fmaf(scale, fmaf(-136.0f, xs[j], part[j]), acc[j]);
         }
     }
@@ -263,9 +271,11 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a) {
     for (long item = it_begin; item < it_end; ++item) {
         const int u = (int)(item / nrc);
         const int rc = (int)(item % nrc);
-        const int e = a.counts ? s_act[u] : 0;
-        const int c = a.counts ? a.counts[e] : a.T;
-        const int o = a.counts ? a.offsets[e] : 0;
+        // wave-uniform by construction; readfirstlane lets the compiler use
+        // scalar registers and scalar branches for everything derived from them
+        const int e = __builtin_amdgcn_readfirstlane(a.counts ? s_act[u] : 0);
+        const int c = __builtin_amdgcn_readfirstlane(a.counts ? a.counts[e] : a.T);
+        const int o = __builtin_amdgcn_readfirstlane(a.counts ? a.offsets[e] : 0);
         const int row0 = rc * a.rows_per_item;
         const int row_end = min(a.N, row0 + a.rows_per_item);
         const int niter = (row_end - row0 + RG * R - 1) / (RG * R);
@@ -304,11 +314,11 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a) {
                 cur_j0 = j0;
             }
 
-            for (int it = 0; it < niter; ++it, ++gi) {
+            // Iteration it+1's loads are issued before iteration it's arithmetic
+            // (double-buffered registers): the memory pipe stays busy through the
+            // math, the fold and the barrier.  Rows past the item read zeros.
+            auto load_iter = [&](int it, uint4 (&wq)[MS][R][G], uint16_t (&sq)[MS][R][G]) {
                 const int rbase = row0 + (it * RG + rg) * R;
-                // ---- every load of this iteration first (out of range -> zeros)
-                uint4 wq[MS][R][G];
-                uint16_t sq[MS][R][G];
 #pragma unroll
                 for (int s = 0; s < MS; ++s) {
                     const int ch = (s * KS + ks) * 64 + lane;
@@ -326,6 +336,11 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a) {
                         }
                     }
                 }
+            };
+            uint4 wqA[MS][R][G], wqB[MS][R][G];
+            uint16_t sqA[MS][R][G], sqB[MS][R][G];
+            auto body = [&](int it, const uint4 (&wq)[MS][R][G], const uint16_t (&sq)[MS][R][G]) {
+                const int rbase = row0 + (it * RG + rg) * R;
                 // ---- arithmetic
                 float acc[R][G][NT];
 #pragma unroll
@@ -334,15 +349,29 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a) {
                     for (int g = 0; g < G; ++g)
 #pragma unroll
                         for (int j = 0; j < NT; ++j) acc[r][g][j] = 0.f;
+                auto arith = [&](auto na) {
+                    constexpr int NA = decltype(na)::value;
 #pragma unroll
-                for (int s = 0; s < MS; ++s)
+                    for (int s = 0; s < MS; ++s)
 #pragma unroll
-                    for (int r = 0; r < R; ++r)
+                        for (int r = 0; r < R; ++r)
 #pragma unroll
-                        for (int g = 0; g < G; ++g) {
-                            const float sc = (WT == DT_INT4) ? f16_to_f32(sq[s][r][g]) : 1.f;
-                            chunk_dot<WT, ACT, NT>(wq[s][r][g], xf[s], xs[s], sc, acc[r][g], nt);
-                        }
+                            for (int g = 0; g < G; ++g) {
+                                const float sc = (WT == DT_INT4) ? f16_to_f32(sq[s][r][g]) : 1.f;
+                                chunk_dot<WT, ACT, NT, NA>(wq[s][r][g], xf[s], xs[s], sc, acc[r][g]);
+                            }
+                };
+                // one uniform branch per iteration picks the token count
+                switch (nt) {
+                    case 1: arith(std::integral_constant<int, 1>{}); break;
+                    case 2: if constexpr (NT >= 2) arith(std::integral_constant<int, 2>{}); break;
+                    case 3: if constexpr (NT >= 3) arith(std::integral_constant<int, 3>{}); break;
+                    case 4: if constexpr (NT >= 4) arith(std::integral_constant<int, 4>{}); break;
+                    case 5: if constexpr (NT >= 5) arith(std::integral_constant<int, 5>{}); break;
+                    case 6: if constexpr (NT >= 6) arith(std::integral_constant<int, 6>{}); break;
+                    case 7: if constexpr (NT >= 7) arith(std::integral_constant<int, 7>{}); break;
+                    default: if constexpr (NT >= 8) arith(std::integral_constant<int, 8>{}); break;
+                }
 
                 // ---- fold the R*G*NT partials: value v = (r*NT + j)*G + g
                 float v[NV];
@@ -375,7 +404,7 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a) {
                         }
                     }
                 }
-                if (ks != 0) continue;
+                if (ks != 0) return;
                 // ---- epilogue by the ks == 0 wave of each row group
                 if constexpr (MODE == 0) {
                     // g has an even value index and u the next one: in the same
@@ -414,6 +443,16 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a) {
                         }
                     }
                 }
+            };
+            load_iter(0, wqA, sqA);
+            for (int it = 0; it < niter; it += 2) {
+                load_iter(it + 1, wqB, sqB);
+                body(it, wqA, sqA);
+                ++gi;
+                if (it + 1 >= niter) break;
+                load_iter(it + 2, wqA, sqA);
+                body(it + 1, wqB, sqB);
+                ++gi;
             }
         }
     }
@@ -432,8 +471,8 @@ int dw_of(int wt) { return wt == DT_INT4 ? 16 : 4; }
 
 // Kernel shape for a given K: K split over KS waves, MS 16-byte steps per
 // wave, NT tokens per pass, R rows per iteration.  (KS, MS) cover the K steps;
-// (NT, R) are the largest that keep activation fragments + in-flight loads +
-// partial sums within ~220 VGPRs (no scratch at 2 waves per SIMD) with 8-16
+// (NT, R) keep activation fragments + two iterations of weight registers +
+// partial sums below 256 VGPRs (no scratch at 2 waves per SIMD) with 8-16
 // loads of 16 B in flight per wave.
 Variant choose(int wt, int K, int G) {
     const int steps = (K / epl_of(wt) + 63) / 64;
@@ -447,14 +486,15 @@ Variant choose(int wt, int K, int G) {
     else return Variant{0, 0, 0, 0};
     int nt, r;
     const int mi = ms == 1 ? 0 : ms == 2 ? 1 : ms == 4 ? 2 : 3;
+    // (NT, R) per MS; the weight registers are double-buffered
     if (wt == DT_INT4) {
-        static const int t2[4][2] = {{4, 8}, {4, 2}, {1, 2}, {0, 0}};   // gate/up
-        static const int t1[4][2] = {{4, 8}, {4, 4}, {1, 4}, {0, 0}};   // down
+        static const int t2[4][2] = {{4, 4}, {4, 1}, {1, 1}, {0, 0}};   // gate/up
+        static const int t1[4][2] = {{4, 4}, {4, 2}, {1, 2}, {0, 0}};   // down
         nt = (G == 2 ? t2 : t1)[mi][0];
         r = (G == 2 ? t2 : t1)[mi][1];
     } else {
-        static const int t2[4][2] = {{8, 4}, {8, 4}, {8, 2}, {4, 1}};
-        static const int t1[4][2] = {{8, 8}, {8, 8}, {8, 4}, {4, 2}};
+        static const int t2[4][2] = {{8, 4}, {8, 2}, {8, 1}, {2, 1}};
+        static const int t1[4][2] = {{8, 8}, {8, 4}, {8, 2}, {4, 1}};
         nt = (G == 2 ? t2 : t1)[mi][0];
         r = (G == 2 ? t2 : t1)[mi][1];
     }
@@ -494,17 +534,17 @@ template <int WT, int ACT, int MODE>
 static hipError_t launch_mode(const GemvArgs& a, const Variant& v, int max_items, hipStream_t s) {
     // exactly the (ks, ms, nt, r) tuples choose() returns
     if constexpr (WT == DT_INT4 && MODE == 0) {
-        GEMV_CASE(1, 1, 4, 8) GEMV_CASE(2, 1, 4, 8) GEMV_CASE(4, 1, 4, 8)
-        GEMV_CASE(4, 2, 4, 2) GEMV_CASE(4, 4, 1, 2)
+        GEMV_CASE(1, 1, 4, 4) GEMV_CASE(2, 1, 4, 4) GEMV_CASE(4, 1, 4, 4)
+        GEMV_CASE(4, 2, 4, 1) GEMV_CASE(4, 4, 1, 1)
     } else if constexpr (WT == DT_INT4) {
-        GEMV_CASE(1, 1, 4, 8) GEMV_CASE(2, 1, 4, 8) GEMV_CASE(4, 1, 4, 8)
-        GEMV_CASE(4, 2, 4, 4) GEMV_CASE(4, 4, 1, 4)
+        GEMV_CASE(1, 1, 4, 4) GEMV_CASE(2, 1, 4, 4) GEMV_CASE(4, 1, 4, 4)
+        GEMV_CASE(4, 2, 4, 2) GEMV_CASE(4, 4, 1, 2)
     } else if constexpr (MODE == 0) {
-        GEMV_CASE(1, 1, 8, 4) GEMV_CASE(1, 2, 8, 4) GEMV_CASE(1, 4, 8, 2)
-        GEMV_CASE(2, 4, 8, 2) GEMV_CASE(4, 4, 8, 2) GEMV_CASE(4, 8, 4, 1)
+        GEMV_CASE(1, 1, 8, 4) GEMV_CASE(1, 2, 8, 2) GEMV_CASE(1, 4, 8, 1)
+        GEMV_CASE(2, 4, 8, 1) GEMV_CASE(4, 4, 8, 1) GEMV_CASE(4, 8, 2, 1)
     } else {
-        GEMV_CASE(1, 1, 8, 8) GEMV_CASE(1, 2, 8, 8) GEMV_CASE(1, 4, 8, 4)
-        GEMV_CASE(2, 4, 8, 4) GEMV_CASE(4, 4, 8, 4) GEMV_CASE(4, 8, 4, 2)
+        GEMV_CASE(1, 1, 8, 8) GEMV_CASE(1, 2, 8, 4) GEMV_CASE(1, 4, 8, 2)
+        GEMV_CASE(2, 4, 8, 2) GEMV_CASE(4, 4, 8, 2) GEMV_CASE(4, 8, 4, 1)
     }
     return hipErrorInvalidConfiguration;
 }
@@ -529,12 +569,17 @@ hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, i
     return hipErrorInvalidValue;
 }
 
-// Rows of one work item: a multiple of the rows a block covers per iteration.
-int gemv_rows_per_item(int wt, int mode, int K) {
+// Rows of one work item: a multiple of the rows a block covers per iteration,
+// sized for about 8 items per block of a 512-block persistent grid (fewer,
+// longer items restart the load pipeline less often; enough items keep the
+// blocks balanced), at most 64 rows.
+int gemv_rows_per_item(int wt, int mode, int K, int N, int active) {
     const Variant v = choose(wt, K, mode == 0 ? 2 : 1);
     const int per_iter = (4 / v.ks) * v.r;
+    long want = ((long)active * N + 4095) / 4096;
+    if (want > 64) want = 64;
     int rows = per_iter;
-    while (rows < 16) rows += per_iter;
+    while (rows < want) rows += per_iter;
     return rows;
 }
 

@@ -28,7 +28,7 @@ hipError_t launch_dispatch(const int32_t* idx, int32_t* counts, int32_t* offsets
 hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, int max_rows,
                        hipStream_t s);
 int gemv_max_k(int wt);
-int gemv_rows_per_item(int wt, int mode, int K);
+int gemv_rows_per_item(int wt, int mode, int K, int N, int active);
 int mfma_bm();
 int mfma_max_tiles(int T, int k, int E);
 int mfma_ntiles_n(int mode, int N);
