@@ -175,6 +175,25 @@ def cpu_baseline(cfg, runner, target_s=10.0):
                       f"({el:.1f} s)"}
 
 
+def measured_traffic(key):
+    """HBM bytes per launch of the dominant step, from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known
+    size).  None when the kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "mixtral_decode_ffn_traffic.md")
+    src = os.path.join(ROOT, "moe_layer_forward_amd", "csrc", "ffn_gemv.hip")
+    try:
+        text = open(path).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    m = re.search(r"^%s: source=([0-9a-f]{16}) traffic_bytes=([0-9]+)" % re.escape(key), text, re.M)
+    if not m or m.group(1) != digest:
+        return None
+    return int(m.group(2))
+
+
 def roofline_obj(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -191,6 +210,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tau", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -201,6 +223,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     moe.lib()   # fail loudly if the HIP library is not built
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=DEV).fill_(1.0)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     name = "stack4" if args.workload == "stack4_layer0" else args.workload
     cfg = moe_inputs.CONFIGS[name]
@@ -221,7 +250,8 @@ def main():
                     kernel="expert FFN step (MFMA gate/up + down)", flops_per_launch=ffn_flops,
                     launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5))
     else:
-        roof = dict(roofline_obj("hbm", achieved, HBM_PEAK_GBS, "GB/s"),
+        roof = dict(roofline_obj("hbm", achieved, HBM_PEAK_GBS, "GB/s",
+                                 measured_traffic(cfg.name) if args.tau == 0 else None),
                     kernel="expert FFN step (gate/up + down GEMV)", bytes_per_launch=ffn_bytes,
                     launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5))
     out = {
