@@ -1,0 +1,439 @@
+// Expert FFN for int4-g128 weights at decode-sized groups: a skinny MFMA GEMM.
+//
+// [P1] "Colibri：专为MoE模型优化的纯C高性能推理引擎" §3.1 (w1/w3 gate and up,
+// w2 down, no bias) and §3.3 (each expert streams its own weights for the
+// tokens the dispatcher gave it); [P5] "一只蜂鸟如何喂饱九头大象" §7.3
+// (int4 experts with per-group scales).  Weight format: int4 two's complement,
+// two per byte (even K index in the low nibble), one fp16 scale per 128 K.
+//
+// Why MFMA at 1-16 tokens per expert: a dot-product GEMV spends ~7 VALU ops per
+// packed dword on dequantisation plus 4 per token, and a cross-lane fold per
+// row; at ~2-3 tokens per expert that is as slow as the HBM stream itself.
+// Here the contraction runs on the matrix cores (v_mfma_f32_16x16x32_bf16 with
+// the tokens as the 16-wide M side, padded) and the VALU only dequantises:
+//
+//  * every lane loads 16 bytes (32 nibbles) of one weight row per scale group:
+//    lane l covers row l%16, K = 128 g + 32 (l/16) + [0, 32).  Dword i of that
+//    load is the B operand of MFMA i of the group, so the 4 MFMAs of a group
+//    cover exactly its 128 K and one fp16 scale applies to their sum;
+//  * a dword becomes 8 bf16 with one shift and one mask-and-XOR per pair:
+//    ((w >> 4s) & 0x000F000F) ^ 0x43084308 is the bf16 pair (136 + q_s,
+//    136 + q_{s+4}), exact.  The token rows are kept in LDS in the matching
+//    order (elements 0,4,1,5,2,6,3,7 of every 8), so an A fragment is one
+//    16-byte LDS read, and the per-group sums of x held beside them remove the
+//    136 offset: acc += s_g (C_g - 136 sum_g x);
+//  * rows of up to P tokens (P set by K so that P rows fit the 160 KB of LDS,
+//    at most 16) are staged once per (expert, token pass) and shared by the 8
+//    waves of the block; token slots past the group read an all-zero row;
+//  * a persistent grid (one 512-thread block per CU) walks equal-sized work
+//    items (active expert, token pass, 128 rows); each wave owns 16 rows and
+//    runs a flat stream of (item, group) steps with the loads of 8 steps in
+//    flight in a register ring (16 KB per wave, 128 KB per CU), so the stream
+//    continues across item boundaries; the buffer range check returns zeros
+//    past the last row and past the block's range, so loads never branch;
+//  * gate and up share each A fragment; the SwiGLU epilogue writes h (bf16),
+//    the down pass writes fp32 rows of y_perm.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kItemRows = 16 * kWaves;      // rows of one work item
+constexpr int kRing = 8;                    // steps (scale groups) in flight per wave
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kMaxE = 256;
+constexpr int kStaticLds = 4352;            // s_act/s_cnt/s_off/s_ipref/s_tot/s_src, rounded up
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                             0x00020000);
+}
+template <int AUX>
+__device__ __forceinline__ u32x4_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+}
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(ic<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Position in the flat stream of (work item, scale group) steps of a block.
+// Every field is wave-uniform.
+struct Cursor {
+    int idx;      // step index in the block's range
+    int u;        // active-expert slot
+    int pass;     // token pass within the expert
+    int chunk;    // 128-row chunk
+    int g;        // scale group
+    int c, o;     // rows of the expert's group, its first dispatch row
+    int e;        // expert id
+};
+
+}  // namespace
+
+struct I4Args {
+    const uint8_t* w0;         // gate (mode 0) or down (mode 1): [E][N][K/2]
+    const uint8_t* w1;         // up (mode 0)
+    const uint16_t* s0;        // fp16 scales [E][N][K/128]
+    const uint16_t* s1;
+    const uint16_t* in;        // bf16 x [T][K] (mode 0) or h [T*k][K] (mode 1)
+    void* out;                 // bf16 h [T*k][N] (mode 0) or fp32 y_perm [T*k][N] (mode 1)
+    const int32_t* counts;     // null: one expert (the shared one) over all T rows
+    const int32_t* offsets;
+    const int32_t* perm;       // mode 0: token of dispatch row p = perm[p] / topk
+    int N, K, topk, T, E, tau, P;
+};
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
+    constexpr int G = MODE == 0 ? 2 : 1;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    __shared__ int s_act[kMaxE], s_cnt[kMaxE], s_off[kMaxE], s_ipref[kMaxE + 1];
+    __shared__ int s_tot[2], s_src[16];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = a.K, N = a.N, P = a.P;
+    const int NG = K / 128;                                  // scale groups per row (multiple of 8)
+    const int nrc = (N + kItemRows - 1) / kItemRows;         // 128-row chunks per matrix
+    const uint32_t rb = (uint32_t)K / 2;                     // packed bytes per row
+    const uint32_t srow = (uint32_t)NG * 2;                  // scale bytes per row
+    const uint32_t RS = (uint32_t)K * 2 + 16;                // LDS bytes per staged token row
+    char* xrows = smem;                                      // P token rows, then the zero row
+    float* xsum = reinterpret_cast<float*>(smem + (size_t)(P + 1) * RS);   // [NG][16]
+
+    // ---- the experts this launch serves, their item counts and prefix
+    if (wave == 0) {
+        int cnt[4], its[4], act[4];
+        int na = 0, ni = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * lane + j;
+            int c = 0;
+            if (a.counts) c = (e < a.E) ? a.counts[e] : 0;
+            else c = (e == 0) ? a.T : 0;
+            act[j] = c > 0 && (a.tau < 0 || c <= a.tau);
+            cnt[j] = c;
+            its[j] = act[j] ? ((c + P - 1) / P) * nrc : 0;
+            na += act[j];
+            ni += its[j];
+        }
+        const int ia = wave_incl_scan(na, lane), ii = wave_incl_scan(ni, lane);
+        int k = ia - na, p = ii - ni;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (act[j]) {
+                const int e = 4 * lane + j;
+                s_act[k] = e;
+                s_cnt[k] = cnt[j];
+                s_off[k] = a.counts ? a.offsets[e] : 0;
+                s_ipref[k] = p;
+                ++k;
+                p += its[j];
+            }
+        }
+        if (lane == 63) { s_tot[0] = ia; s_tot[1] = ii; s_ipref[ia] = ii; }
+    }
+    // the all-zero token row read by padded token slots
+    for (int i = tid; i < (int)(RS / 16); i += kThreads)
+        *reinterpret_cast<u32x4_t*>(xrows + (size_t)P * RS + (size_t)i * 16) = u32x4_t{0u, 0u, 0u, 0u};
+    __syncthreads();
+
+    const int U = s_tot[0];
+    const long n_items = s_tot[1];
+    const long ib = n_items * blockIdx.x / gridDim.x;
+    const long ie = n_items * (blockIdx.x + 1) / gridDim.x;
+    if (ib >= ie) return;
+    const int nsteps = (int)(ie - ib) * NG;
+
+    // ---- start of the block's range
+    Cursor cur;
+    {
+        int lo = 0, hi = U - 1;   // last slot whose first item is <= ib
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_ipref[mid] <= ib) lo = mid; else hi = mid - 1;
+        }
+        cur.u = lo;
+        const int rel = (int)(ib - s_ipref[lo]);
+        cur.pass = rel / nrc;
+        cur.chunk = rel - cur.pass * nrc;
+        cur.g = 0;
+        cur.idx = 0;
+        cur.e = __builtin_amdgcn_readfirstlane(s_act[lo]);
+        cur.c = __builtin_amdgcn_readfirstlane(s_cnt[lo]);
+        cur.o = __builtin_amdgcn_readfirstlane(s_off[lo]);
+    }
+    auto advance = [&](Cursor& q) {
+        ++q.idx;
+        if (++q.g < NG) return;
+        q.g = 0;
+        if (++q.chunk < nrc) return;
+        q.chunk = 0;
+        if ((++q.pass) * P < q.c) return;
+        q.pass = 0;
+        if (++q.u < U) {
+            q.e = __builtin_amdgcn_readfirstlane(s_act[q.u]);
+            q.c = __builtin_amdgcn_readfirstlane(s_cnt[q.u]);
+            q.o = __builtin_amdgcn_readfirstlane(s_off[q.u]);
+        }
+    };
+
+    const uint32_t mat_bytes = rb * (uint32_t)N;
+    const uint32_t lrow = (uint32_t)(wave * 16 + (lane & 15));
+    const uint32_t lq = (uint32_t)(lane >> 4);
+    const uint32_t woff_l = lrow * rb + lq * 16u;            // lane part of a weight offset
+    const uint32_t soff_l = lrow * srow;                      // lane part of a scale offset
+
+    // ---- loads of one step into ring slot S (zeros past the block's range)
+    u32x4_t wq[kRing][G];
+    u32x4_t sq[2][G];
+    auto issue = [&](const Cursor& q, auto slot, auto sslot, bool with_scale) {
+        constexpr int S = decltype(slot)::value, SS = decltype(sslot)::value;
+        const bool ok = q.idx < nsteps;
+        const uint32_t wo = woff_l + (uint32_t)q.chunk * kItemRows * rb + (uint32_t)q.g * 64u;
+        const size_t eb = (size_t)q.e * mat_bytes;
+        wq[S][0] = ld16<2>(rsrc(a.w0 + eb, ok ? mat_bytes : 0u), wo);
+        if constexpr (G == 2) wq[S][1] = ld16<2>(rsrc(a.w1 + eb, ok ? mat_bytes : 0u), wo);
+        if (with_scale) {
+            const uint32_t so = soff_l + (uint32_t)q.chunk * kItemRows * srow + (uint32_t)(q.g >> 3) * 16u;
+            const size_t sb = (size_t)q.e * N * srow;
+            const uint32_t sn = ok ? (uint32_t)N * srow : 0u;
+            sq[SS][0] = ld16<0>(rsrc(reinterpret_cast<const char*>(a.s0) + sb, sn), so);
+            if constexpr (G == 2) sq[SS][1] = ld16<0>(rsrc(reinterpret_cast<const char*>(a.s1) + sb, sn), so);
+        }
+    };
+
+    // ---- staging of a token pass into LDS (block-wide)
+    int tag_u = -1, tag_pass = -1;
+    auto stage = [&](const Cursor& q) {
+        __syncthreads();   // every wave is done with the previous rows
+        const int j0 = q.pass * P;
+        const int nt = min(P, q.c - j0);
+        if (tid < 16 && tid < nt) {
+            const int p = q.o + j0 + tid;
+            s_src[tid] = (MODE == 0 && a.perm) ? a.perm[p] / a.topk : p;
+        }
+        for (int i = tid; i < NG * 16; i += kThreads)   // group sums of the padded slots
+            if ((i & 15) >= nt) xsum[i] = 0.f;
+        __syncthreads();
+        // nt rows of K/8 16-byte chunks; nch is a multiple of 128, so every
+        // wave is either wholly inside or wholly past the range, and 16
+        // consecutive lanes hold the 16 chunks of one scale group
+        const int nch = K / 8;
+        const int total = nt * nch;
+        constexpr int B = 4;
+        for (int i0 = wave * 64; i0 < total; i0 += kThreads * B) {
+            uint4 v[B];
+            int t[B], ch[B];
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                const int i = i0 + j * kThreads + lane;
+                t[j] = i / nch;
+                ch[j] = i - t[j] * nch;
+                if (i0 + j * kThreads < total)
+                    v[j] = *reinterpret_cast<const uint4*>(a.in + (size_t)s_src[t[j]] * K + (size_t)ch[j] * 8);
+            }
+#pragma unroll
+            for (int j = 0; j < B; ++j) {
+                if (i0 + j * kThreads >= total) break;
+                // elements (0,1)(2,3)(4,5)(6,7) -> pairs (0,4)(1,5)(2,6)(3,7)
+                u32x4_t o;
+                o.x = (v[j].x & 0xffffu) | (v[j].z << 16);
+                o.y = (v[j].x >> 16) | (v[j].z & 0xffff0000u);
+                o.z = (v[j].y & 0xffffu) | (v[j].w << 16);
+                o.w = (v[j].y >> 16) | (v[j].w & 0xffff0000u);
+                *reinterpret_cast<u32x4_t*>(xrows + (size_t)t[j] * RS + (size_t)ch[j] * 16) = o;
+                float sum = bf16_lo(v[j].x) + bf16_hi(v[j].x) + bf16_lo(v[j].y) + bf16_hi(v[j].y) +
+                            bf16_lo(v[j].z) + bf16_hi(v[j].z) + bf16_lo(v[j].w) + bf16_hi(v[j].w);
+                sum = group_sum<16>(sum);
+                if ((ch[j] & 15) == 0) xsum[(ch[j] >> 4) * 16 + t[j]] = sum;
+            }
+        }
+        __syncthreads();
+        tag_u = q.u;
+        tag_pass = q.pass;
+    };
+
+    // per-lane LDS addresses of the A fragments and of the group sums
+    const uint32_t tok = (uint32_t)(lane & 15);
+    uint32_t xa = 0;                            // set at each stage
+    const uint32_t xs_l = lq * 16u;             // bytes: tokens 4q..4q+3 of a group's 16
+    floatx4 acc[G];
+#pragma unroll
+    for (int m = 0; m < G; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const Cursor& q, auto slot, auto sslot, auto half) {
+        constexpr int S = decltype(slot)::value, SS = decltype(sslot)::value,
+                      H = decltype(half)::value;   // group index within the scale chunk
+        const char* xg = xrows + xa + (uint32_t)q.g * 256u;
+        u32x4_t af[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4_t*>(xg + i * 16);
+        const floatx4 xs = *reinterpret_cast<const floatx4*>(
+            reinterpret_cast<const char*>(xsum) + (uint32_t)q.g * 64u + xs_l);
+#pragma unroll
+        for (int m = 0; m < G; ++m) {
+            const uint32_t wd[4] = {wq[S][m].x, wq[S][m].y, wq[S][m].z, wq[S][m].w};
+            floatx4 c = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u32x4_t b;
+                b.x = (wd[i] & 0x000f000fu) ^ 0x43084308u;
+                b.y = ((wd[i] >> 4) & 0x000f000fu) ^ 0x43084308u;
+                b.z = ((wd[i] >> 8) & 0x000f000fu) ^ 0x43084308u;
+                b.w = ((wd[i] >> 12) & 0x000f000fu) ^ 0x43084308u;
+                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
+                                                             __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+            }
+            const uint32_t sw = sq[SS][m][H >> 1];
+            const float sc = f16_to_f32((uint16_t)((H & 1) ? (sw >> 16) : (sw & 0xffffu)));
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[m][v] = fmaf(sc, fmaf(-136.0f, xs[v], c[v]), acc[m][v]);
+        }
+    };
+
+    auto epilogue = [&](const Cursor& q) {
+        const int j0 = q.pass * P;
+        const int nt = min(P, q.c - j0);
+        const int row = q.chunk * kItemRows + wave * 16 + (lane & 15);
+        if (row < N) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = (int)lq * 4 + v;
+                if (t < nt) {
+                    const size_t oi = (size_t)(q.o + j0 + t) * N + row;
+                    if constexpr (MODE == 0)
+                        reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(silu(acc[0][v]) * acc[1][v]);
+                    else
+                        reinterpret_cast<float*>(a.out)[oi] = acc[0][v];
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < G; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    // ---- prologue: kRing steps of loads in flight; L runs kRing steps ahead of C
+    Cursor L = cur;
+    static_for<0, kRing>([&](auto k) {
+        issue(L, k, ic<(k / 8) & 1>{}, (k % 8) == 0);
+        advance(L);
+    });
+
+    // One step at unrolled position k (0..15): ring slot k % 8, scale slot
+    // k / 8 for C and the other one for L (8 steps = one scale chunk ahead).
+    // Steps carry no exit test, so the compiler's wait counts see the ring.
+    Cursor C = cur;
+    auto step = [&](auto kk) {
+        constexpr int k = decltype(kk)::value;
+        if constexpr (k % 8 == 0) {
+            if (C.g == 0 && (C.u != tag_u || C.pass != tag_pass)) {
+                stage(C);
+                const int nt = min(P, C.c - C.pass * P);
+                xa = (tok < (uint32_t)nt ? tok : (uint32_t)P) * RS + lq * 64u;
+            }
+        }
+        compute(C, ic<k % kRing>{}, ic<k / 8>{}, ic<k % 8>{});
+        if constexpr (k % 8 == 7) {
+            if (C.g == NG - 1) epilogue(C);
+        }
+        // refill the slot just consumed with the step kRing ahead
+        issue(L, ic<k % kRing>{}, ic<1 - k / 8>{}, (k % 8) == 0);
+        advance(L);
+        advance(C);
+    };
+    // nsteps is a multiple of 8 (NG is)
+    for (int n = nsteps >> 4; n > 0; --n) static_for<0, 16>(step);
+    if (nsteps & 8) static_for<0, 8>(step);
+}
+
+// ------------------------------------------------------------------ host side
+
+// Token rows per pass for a given K: P rows plus the zero row plus the group
+// sums must fit the LDS of one block.
+static int i4_pass_tokens(int K) {
+    const long rs = (long)K * 2 + 16;
+    const long xs = (long)(K / 128) * 16 * 4;
+    long p = (kLdsBytes - xs - kStaticLds) / rs - 1;
+    if (p > 16) p = 16;
+    return (int)p;
+}
+
+bool i4mfma_supported(int K, int N) {
+    if (K % 1024 != 0 || K <= 0 || N <= 0) return false;
+    if (i4_pass_tokens(K) < 1) return false;
+    // 32-bit buffer offsets of a matrix, including the padded last chunk
+    return (size_t)(N + kItemRows) * (size_t)(K / 2) < ((size_t)1 << 31);
+}
+
+hipError_t launch_i4mfma(int mode, const GemvArgs& g, int max_items_hint, hipStream_t s) {
+    I4Args a;
+    a.w0 = reinterpret_cast<const uint8_t*>(g.w0);
+    a.w1 = reinterpret_cast<const uint8_t*>(g.w1);
+    a.s0 = g.s0;
+    a.s1 = g.s1;
+    a.in = reinterpret_cast<const uint16_t*>(g.in);
+    a.out = g.out;
+    a.counts = g.counts;
+    a.offsets = g.offsets;
+    a.perm = g.perm;
+    a.N = g.N;
+    a.K = g.K;
+    a.topk = g.topk;
+    a.T = g.T;
+    a.E = g.E;
+    a.tau = g.tau;
+    a.P = i4_pass_tokens(g.K);
+    if (a.E > kMaxE || a.P < 1) return hipErrorInvalidValue;
+    const size_t lds = (size_t)(a.P + 1) * ((size_t)g.K * 2 + 16) + (size_t)(g.K / 128) * 16 * 4;
+
+    static int n_cu = 0;
+    static bool attr_set[2] = {false, false};
+    if (n_cu == 0) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (n_cu < 1) n_cu = 256;
+    }
+    auto k = mode == 0 ? i4_mfma_kernel<0> : i4_mfma_kernel<1>;
+    if (!attr_set[mode]) {
+        // dynamic LDS beyond 64 KB: the budget left next to the static arrays
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)(kLdsBytes - kStaticLds));
+        attr_set[mode] = true;
+    }
+    int grid = n_cu;
+    if (max_items_hint > 0 && grid > max_items_hint) grid = max_items_hint;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

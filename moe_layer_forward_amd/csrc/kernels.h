@@ -28,6 +28,9 @@ hipError_t launch_dispatch(const int32_t* idx, int32_t* counts, int32_t* offsets
 hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, int max_rows,
                        hipStream_t s);
 int gemv_max_k(int wt);
+// int4-g128 weights on the matrix cores (ffn_i4mfma.hip): K a multiple of 1024.
+bool i4mfma_supported(int K, int N);
+hipError_t launch_i4mfma(int mode, const GemvArgs& a, int max_items_hint, hipStream_t s);
 int gemv_rows_per_item(int wt, int mode, int K, int N, int active);
 int mfma_bm();
 int mfma_max_tiles(int T, int k, int E);

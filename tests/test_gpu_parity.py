@@ -33,6 +33,18 @@ SMALL = {
     "int4_ktail": moe_inputs.MoEConfig(
         "int4_ktail", T=24, d=384, E=8, k=3, F=640, act="bf16", wt="int4",
         model="s_int4_tail", n_shared=0, w_std=0.05),
+    # int4 on the matrix cores (K a multiple of 1024): groups larger than one
+    # token pass (P = 16 rows at K = 1024 and 2048, 10 at K = 7168), k = E,
+    # and many experts holding 0-2 rows
+    "int4_mfma_multipass": moe_inputs.MoEConfig(
+        "int4_mfma_multipass", T=40, d=1024, E=4, k=2, F=2048, act="bf16", wt="int4",
+        model="s_int4_mp", n_shared=1, w_std=0.05),
+    "int4_mfma_wide_k": moe_inputs.MoEConfig(
+        "int4_mfma_wide_k", T=20, d=7168, E=4, k=4, F=1024, act="bf16", wt="int4",
+        model="s_int4_wk", n_shared=0, w_std=0.05),
+    "int4_mfma_many": moe_inputs.MoEConfig(
+        "int4_mfma_many", T=8, d=1024, E=256, k=8, F=1024, act="bf16", wt="int4",
+        model="s_int4_many", n_shared=1, w_std=0.05),
     "f32_ragged": moe_inputs.MoEConfig(
         "f32_ragged", T=37, d=200, E=5, k=3, F=72, act="f32", wt="f32", model="s_f32"),
 }
