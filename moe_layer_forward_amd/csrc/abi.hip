@@ -152,6 +152,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
                        "mfma plan", err, err_len);
         if (rc) return rc;
     }
+    // routed experts (g) and the shared expert (q: one expert over all T rows)
     GemvArgs g{};
     g.counts = counts;
     g.offsets = offsets;
@@ -160,14 +161,31 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     g.T = s->T;
     g.E = s->E;
     g.tau = use_mfma ? tau : -1;
+    GemvArgs q{};
+    q.topk = 1; q.T = s->T; q.E = 1; q.tau = -1;
+    const GemvArgs* qp = s->n_shared ? &q : nullptr;
+    const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
+    // one pass (gate/up or down) of the routed and the shared expert: int4 on
+    // the matrix cores in one launch, else one GEMV launch each
+    auto pass = [&](int mode, const char* what) -> int {
+        if (s->wt == MOE_INT4_G128 && i4mfma_supported(g.K, g.N))
+            return hip_check(launch_i4mfma(mode, &g, qp, st), st, what, err, err_len);
+        g.rows_per_item = gemv_rows_per_item(s->wt, mode, g.K, g.N, active);
+        int r = hip_check(launch_gemv(s->wt, s->act, mode, g, s->E, max_rows_gemv, st), st, what, err, err_len);
+        if (r || !qp) return r;
+        q.rows_per_item = gemv_rows_per_item(s->wt, mode, q.K, q.N, 1);
+        return hip_check(launch_gemv(s->wt, s->act, mode, q, 1, s->T, st), st, what, err, err_len);
+    };
 
     // gate/up + SwiGLU
+    void* hs = s->n_shared ? ws + L.hs : nullptr;
     g.w0 = w->w_gate; g.w1 = w->w_up;
     g.s0 = (const uint16_t*)w->s_gate; g.s1 = (const uint16_t*)w->s_up;
     g.in = x; g.out = h; g.N = s->F; g.K = s->d;
-    const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
-    g.rows_per_item = gemv_rows_per_item(s->wt, 0, g.K, g.N, active);
-    rc = hip_check(launch_gemv(s->wt, s->act, 0, g, s->E, max_rows_gemv, st), st, "gemv gate/up", err, err_len);
+    q.w0 = w->sh_gate; q.w1 = w->sh_up;
+    q.s0 = (const uint16_t*)w->sh_s_gate; q.s1 = (const uint16_t*)w->sh_s_up;
+    q.in = x; q.out = hs; q.N = s->F; q.K = s->d;
+    rc = pass(0, "gate/up");
     if (rc) return rc;
     if (use_mfma) {
         rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, s->T, st),
@@ -178,31 +196,14 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     g.w0 = w->w_down; g.w1 = nullptr;
     g.s0 = (const uint16_t*)w->s_down; g.s1 = nullptr;
     g.in = h; g.out = y_perm; g.N = s->d; g.K = s->F;
-    g.rows_per_item = gemv_rows_per_item(s->wt, 1, g.K, g.N, active);
-    rc = hip_check(launch_gemv(s->wt, s->act, 1, g, s->E, max_rows_gemv, st), st, "gemv down", err, err_len);
+    q.w0 = w->sh_down; q.w1 = nullptr;
+    q.s0 = (const uint16_t*)w->sh_s_down; q.s1 = nullptr;
+    q.in = hs; q.out = y_shared; q.N = s->d; q.K = s->F;
+    rc = pass(1, "down");
     if (rc) return rc;
     if (use_mfma) {
         rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, s->T * s->k, st),
                        st, "mfma down", err, err_len);
-        if (rc) return rc;
-    }
-    // shared expert: one expert over all T rows
-    if (s->n_shared) {
-        void* hs = ws + L.hs;
-        GemvArgs q{};
-        q.counts = nullptr; q.offsets = nullptr; q.perm = nullptr;
-        q.topk = 1; q.T = s->T; q.E = 1; q.tau = -1;
-        q.w0 = w->sh_gate; q.w1 = w->sh_up;
-        q.s0 = (const uint16_t*)w->sh_s_gate; q.s1 = (const uint16_t*)w->sh_s_up;
-        q.in = x; q.out = hs; q.N = s->F; q.K = s->d;
-        q.rows_per_item = gemv_rows_per_item(s->wt, 0, q.K, q.N, 1);
-        rc = hip_check(launch_gemv(s->wt, s->act, 0, q, 1, s->T, st), st, "gemv shared gate/up", err, err_len);
-        if (rc) return rc;
-        q.w0 = w->sh_down; q.w1 = nullptr;
-        q.s0 = (const uint16_t*)w->sh_s_down; q.s1 = nullptr;
-        q.in = hs; q.out = y_shared; q.N = s->d; q.K = s->F;
-        q.rows_per_item = gemv_rows_per_item(s->wt, 1, q.K, q.N, 1);
-        rc = hip_check(launch_gemv(s->wt, s->act, 1, q, 1, s->T, st), st, "gemv shared down", err, err_len);
         if (rc) return rc;
     }
     return MOE_OK;

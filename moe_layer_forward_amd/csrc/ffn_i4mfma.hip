@@ -27,12 +27,19 @@
 //    waves of the block; token slots past the group read an all-zero row;
 //  * a persistent grid (one 512-thread block per CU) walks equal-sized work
 //    items (active expert, token pass, 128 rows); each wave owns 16 rows and
-//    runs a flat stream of (item, group) steps with the loads of 8 steps in
-//    flight in a register ring (16 KB per wave, 128 KB per CU), so the stream
-//    continues across item boundaries; the buffer range check returns zeros
-//    past the last row and past the block's range, so loads never branch;
+//    runs a flat stream of (item, group) steps with 16 KB of weight loads in
+//    flight in a register ring (8 groups of gate+up, 16 groups of down; 128 KB
+//    per CU), so the stream continues across item boundaries; the buffer range
+//    check returns zeros past the last row and past the block's range, so
+//    loads never branch;
+//  * the lane layout gives each load instruction 16 rows x 64 bytes, half of
+//    a 128-byte line per row; the loads of two consecutive groups (the two
+//    halves of every line) are issued back to back so they meet in the cache;
+//  * a shared expert, when present, is one more slot of the same launch (all
+//    T tokens, its own weights and buffers), so its passes overlap the routed
+//    experts' instead of running as a separate small launch;
 //  * gate and up share each A fragment; the SwiGLU epilogue writes h (bf16),
-//    the down pass writes fp32 rows of y_perm.
+//    the down pass writes fp32 rows of y_perm (y_shared for the shared slot).
 #include <type_traits>
 
 #include "common.h"
@@ -49,18 +56,16 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kItemRows = 16 * kWaves;      // rows of one work item
-constexpr int kRing = 8;                    // steps (scale groups) in flight per wave
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kMaxE = 256;
-constexpr int kStaticLds = 4352;            // s_act/s_cnt/s_off/s_ipref/s_tot/s_src, rounded up
+constexpr int kStaticLds = 4608;            // the __shared__ arrays below, rounded up
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t nbytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
                                              0x00020000);
 }
-template <int AUX>
 __device__ __forceinline__ u32x4_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
 template <int I>
@@ -88,34 +93,41 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // Every field is wave-uniform.
 struct Cursor {
     int idx;      // step index in the block's range
-    int u;        // active-expert slot
+    int u;        // expert slot
     int pass;     // token pass within the expert
     int chunk;    // 128-row chunk
     int g;        // scale group
     int c, o;     // rows of the expert's group, its first dispatch row
-    int e;        // expert id
+    int e;        // expert id; -1: the shared expert
 };
 
 }  // namespace
 
 struct I4Args {
-    const uint8_t* w0;         // gate (mode 0) or down (mode 1): [E][N][K/2]
-    const uint8_t* w1;         // up (mode 0)
+    const uint8_t* w0;         // routed gate (mode 0) or down (mode 1): [E][N][K/2]
+    const uint8_t* w1;         // routed up (mode 0)
     const uint16_t* s0;        // fp16 scales [E][N][K/128]
     const uint16_t* s1;
     const uint16_t* in;        // bf16 x [T][K] (mode 0) or h [T*k][K] (mode 1)
     void* out;                 // bf16 h [T*k][N] (mode 0) or fp32 y_perm [T*k][N] (mode 1)
-    const int32_t* counts;     // null: one expert (the shared one) over all T rows
+    const int32_t* counts;     // null: no routed experts
     const int32_t* offsets;
     const int32_t* perm;       // mode 0: token of dispatch row p = perm[p] / topk
+    const uint8_t* sw0;        // shared expert ([1][N][K/2] ...), null: none
+    const uint8_t* sw1;
+    const uint16_t* ss0;
+    const uint16_t* ss1;
+    const uint16_t* sin;       // bf16 x [T][K] (mode 0) or h_shared [T][K] (mode 1)
+    void* sout;                // bf16 h_shared [T][N] (mode 0) or fp32 y_shared [T][N] (mode 1)
     int N, K, topk, T, E, tau, P;
 };
 
-template <int MODE>
+template <int MODE, int RING>
 __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     constexpr int G = MODE == 0 ? 2 : 1;
+    static_assert(RING == 8 || RING == 16, "ring of 8 or 16 steps");
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    __shared__ int s_act[kMaxE], s_cnt[kMaxE], s_off[kMaxE], s_ipref[kMaxE + 1];
+    __shared__ int s_act[kMaxE + 1], s_cnt[kMaxE + 1], s_off[kMaxE + 1], s_ipref[kMaxE + 2];
     __shared__ int s_tot[2], s_src[16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -128,16 +140,15 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     char* xrows = smem;                                      // P token rows, then the zero row
     float* xsum = reinterpret_cast<float*>(smem + (size_t)(P + 1) * RS);   // [NG][16]
 
-    // ---- the experts this launch serves, their item counts and prefix
+    // ---- the expert slots of this launch (routed experts with work, then the
+    // shared one), their item counts and the prefix over them
     if (wave == 0) {
         int cnt[4], its[4], act[4];
         int na = 0, ni = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = 4 * lane + j;
-            int c = 0;
-            if (a.counts) c = (e < a.E) ? a.counts[e] : 0;
-            else c = (e == 0) ? a.T : 0;
+            const int c = (a.counts && e < a.E) ? a.counts[e] : 0;
             act[j] = c > 0 && (a.tau < 0 || c <= a.tau);
             cnt[j] = c;
             its[j] = act[j] ? ((c + P - 1) / P) * nrc : 0;
@@ -152,13 +163,26 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
                 const int e = 4 * lane + j;
                 s_act[k] = e;
                 s_cnt[k] = cnt[j];
-                s_off[k] = a.counts ? a.offsets[e] : 0;
+                s_off[k] = a.offsets[e];
                 s_ipref[k] = p;
                 ++k;
                 p += its[j];
             }
         }
-        if (lane == 63) { s_tot[0] = ia; s_tot[1] = ii; s_ipref[ia] = ii; }
+        if (lane == 63) {
+            int u = ia, tot = ii;
+            if (a.sw0 && a.T > 0) {
+                s_act[u] = -1;
+                s_cnt[u] = a.T;
+                s_off[u] = 0;
+                s_ipref[u] = tot;
+                tot += ((a.T + P - 1) / P) * nrc;
+                ++u;
+            }
+            s_tot[0] = u;
+            s_tot[1] = tot;
+            s_ipref[u] = tot;
+        }
     }
     // the all-zero token row read by padded token slots
     for (int i = tid; i < (int)(RS / 16); i += kThreads)
@@ -190,9 +214,12 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
         cur.c = __builtin_amdgcn_readfirstlane(s_cnt[lo]);
         cur.o = __builtin_amdgcn_readfirstlane(s_off[lo]);
     }
-    auto advance = [&](Cursor& q) {
-        ++q.idx;
-        if (++q.g < NG) return;
+    // advance by n steps, n = 1 or 8 (NG is a multiple of 8, so 8 steps never
+    // cross a row-chunk boundary without landing on it)
+    auto advance = [&](Cursor& q, int n) {
+        q.idx += n;
+        q.g += n;
+        if (q.g < NG) return;
         q.g = 0;
         if (++q.chunk < nrc) return;
         q.chunk = 0;
@@ -211,22 +238,39 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     const uint32_t woff_l = lrow * rb + lq * 16u;            // lane part of a weight offset
     const uint32_t soff_l = lrow * srow;                      // lane part of a scale offset
 
-    // ---- loads of one step into ring slot S (zeros past the block's range)
-    u32x4_t wq[kRing][G];
+    // ---- weight loads of steps q and q+1 into ring slots S, S+1: the two
+    // halves of the same 128-byte lines, back to back (zeros past the range)
+    u32x4_t wq[RING][G];
     u32x4_t sq[2][G];
-    auto issue = [&](const Cursor& q, auto slot, auto sslot, bool with_scale) {
-        constexpr int S = decltype(slot)::value, SS = decltype(sslot)::value;
-        const bool ok = q.idx < nsteps;
-        const uint32_t wo = woff_l + (uint32_t)q.chunk * kItemRows * rb + (uint32_t)q.g * 64u;
-        const size_t eb = (size_t)q.e * mat_bytes;
-        wq[S][0] = ld16<2>(rsrc(a.w0 + eb, ok ? mat_bytes : 0u), wo);
-        if constexpr (G == 2) wq[S][1] = ld16<2>(rsrc(a.w1 + eb, ok ? mat_bytes : 0u), wo);
-        if (with_scale) {
-            const uint32_t so = soff_l + (uint32_t)q.chunk * kItemRows * srow + (uint32_t)(q.g >> 3) * 16u;
-            const size_t sb = (size_t)q.e * N * srow;
-            const uint32_t sn = ok ? (uint32_t)N * srow : 0u;
-            sq[SS][0] = ld16<0>(rsrc(reinterpret_cast<const char*>(a.s0) + sb, sn), so);
-            if constexpr (G == 2) sq[SS][1] = ld16<0>(rsrc(reinterpret_cast<const char*>(a.s1) + sb, sn), so);
+    auto weight_ptr = [&](const Cursor& q, int m) -> const uint8_t* {
+        if (q.e >= 0) return (m == 0 ? a.w0 : a.w1) + (size_t)q.e * mat_bytes;
+        return m == 0 ? a.sw0 : a.sw1;
+    };
+    auto issue_pair = [&](Cursor& q, auto slot) {
+        constexpr int S = decltype(slot)::value;
+        Cursor q1 = q;
+        advance(q1, 1);
+        const uint32_t n0 = q.idx < nsteps ? mat_bytes : 0u, n1 = q1.idx < nsteps ? mat_bytes : 0u;
+        const uint32_t o0 = woff_l + (uint32_t)q.chunk * kItemRows * rb + (uint32_t)q.g * 64u;
+        const uint32_t o1 = woff_l + (uint32_t)q1.chunk * kItemRows * rb + (uint32_t)q1.g * 64u;
+#pragma unroll
+        for (int m = 0; m < G; ++m) {
+            wq[S][m] = ld16(rsrc(weight_ptr(q, m), n0), o0);
+            wq[S + 1][m] = ld16(rsrc(weight_ptr(q1, m), n1), o1);
+        }
+        q = q1;
+        advance(q, 1);
+    };
+    // fp16 scales of the 8 groups starting at step q (a chunk) into slot SS
+    auto issue_scales = [&](const Cursor& q, auto sslot) {
+        constexpr int SS = decltype(sslot)::value;
+        const uint32_t so = soff_l + (uint32_t)q.chunk * kItemRows * srow + (uint32_t)(q.g >> 3) * 16u;
+        const uint32_t sn = q.idx < nsteps ? (uint32_t)N * srow : 0u;
+#pragma unroll
+        for (int m = 0; m < G; ++m) {
+            const uint16_t* sp = q.e >= 0 ? (m == 0 ? a.s0 : a.s1) + (size_t)q.e * N * NG
+                                          : (m == 0 ? a.ss0 : a.ss1);
+            sq[SS][m] = ld16(rsrc(sp, sn), so);
         }
     };
 
@@ -236,9 +280,11 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
         __syncthreads();   // every wave is done with the previous rows
         const int j0 = q.pass * P;
         const int nt = min(P, q.c - j0);
+        const bool routed = q.e >= 0;
+        const uint16_t* in = routed ? a.in : a.sin;
         if (tid < 16 && tid < nt) {
             const int p = q.o + j0 + tid;
-            s_src[tid] = (MODE == 0 && a.perm) ? a.perm[p] / a.topk : p;
+            s_src[tid] = (MODE == 0 && routed && a.perm) ? a.perm[p] / a.topk : p;
         }
         for (int i = tid; i < NG * 16; i += kThreads)   // group sums of the padded slots
             if ((i & 15) >= nt) xsum[i] = 0.f;
@@ -258,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
                 t[j] = i / nch;
                 ch[j] = i - t[j] * nch;
                 if (i0 + j * kThreads < total)
-                    v[j] = *reinterpret_cast<const uint4*>(a.in + (size_t)s_src[t[j]] * K + (size_t)ch[j] * 8);
+                    v[j] = *reinterpret_cast<const uint4*>(in + (size_t)s_src[t[j]] * K + (size_t)ch[j] * 8);
             }
 #pragma unroll
             for (int j = 0; j < B; ++j) {
@@ -323,6 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
         const int j0 = q.pass * P;
         const int nt = min(P, q.c - j0);
         const int row = q.chunk * kItemRows + wave * 16 + (lane & 15);
+        void* out = q.e >= 0 ? a.out : a.sout;
         if (row < N) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -330,9 +377,9 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
                 if (t < nt) {
                     const size_t oi = (size_t)(q.o + j0 + t) * N + row;
                     if constexpr (MODE == 0)
-                        reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(silu(acc[0][v]) * acc[1][v]);
+                        reinterpret_cast<uint16_t*>(out)[oi] = f32_to_bf16(silu(acc[0][v]) * acc[1][v]);
                     else
-                        reinterpret_cast<float*>(a.out)[oi] = acc[0][v];
+                        reinterpret_cast<float*>(out)[oi] = acc[0][v];
                 }
             }
         }
@@ -340,16 +387,18 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
         for (int m = 0; m < G; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
     };
 
-    // ---- prologue: kRing steps of loads in flight; L runs kRing steps ahead of C
-    Cursor L = cur;
-    static_for<0, kRing>([&](auto k) {
-        issue(L, k, ic<(k / 8) & 1>{}, (k % 8) == 0);
-        advance(L);
-    });
+    // ---- prologue: RING steps of weights and the first scale chunk in flight
+    Cursor L = cur;       // next step whose weights are loaded
+    Cursor Sc = cur;      // next chunk whose scales are loaded
+    issue_scales(Sc, ic<0>{});
+    advance(Sc, 8);
+    static_for<0, RING / 2>([&](auto k) { issue_pair(L, ic<2 * decltype(k)::value>{}); });
 
-    // One step at unrolled position k (0..15): ring slot k % 8, scale slot
-    // k / 8 for C and the other one for L (8 steps = one scale chunk ahead).
-    // Steps carry no exit test, so the compiler's wait counts see the ring.
+    // One step at unrolled position k (0..15): ring slot k % RING, scale slot
+    // k / 8.  Every other step refills the two slots just consumed with the
+    // steps RING ahead; the first step of a chunk loads the next chunk's
+    // scales.  Steps carry no exit test, so the compiler's wait counts see the
+    // whole ring.
     Cursor C = cur;
     auto step = [&](auto kk) {
         constexpr int k = decltype(kk)::value;
@@ -360,14 +409,16 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
                 xa = (tok < (uint32_t)nt ? tok : (uint32_t)P) * RS + lq * 64u;
             }
         }
-        compute(C, ic<k % kRing>{}, ic<k / 8>{}, ic<k % 8>{});
+        compute(C, ic<k % RING>{}, ic<k / 8>{}, ic<k % 8>{});
+        if constexpr (k % 8 == 0) {
+            issue_scales(Sc, ic<1 - k / 8>{});
+            advance(Sc, 8);
+        }
         if constexpr (k % 8 == 7) {
             if (C.g == NG - 1) epilogue(C);
         }
-        // refill the slot just consumed with the step kRing ahead
-        issue(L, ic<k % kRing>{}, ic<1 - k / 8>{}, (k % 8) == 0);
-        advance(L);
-        advance(C);
+        if constexpr (k % 2 == 1) issue_pair(L, ic<(k - 1) % RING>{});
+        advance(C, 1);
     };
     // nsteps is a multiple of 8 (NG is)
     for (int n = nsteps >> 4; n > 0; --n) static_for<0, 16>(step);
@@ -393,23 +444,36 @@ bool i4mfma_supported(int K, int N) {
     return (size_t)(N + kItemRows) * (size_t)(K / 2) < ((size_t)1 << 31);
 }
 
-hipError_t launch_i4mfma(int mode, const GemvArgs& g, int max_items_hint, hipStream_t s) {
-    I4Args a;
-    a.w0 = reinterpret_cast<const uint8_t*>(g.w0);
-    a.w1 = reinterpret_cast<const uint8_t*>(g.w1);
-    a.s0 = g.s0;
-    a.s1 = g.s1;
-    a.in = reinterpret_cast<const uint16_t*>(g.in);
-    a.out = g.out;
-    a.counts = g.counts;
-    a.offsets = g.offsets;
-    a.perm = g.perm;
+hipError_t launch_i4mfma(int mode, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s) {
+    const GemvArgs& g = routed ? *routed : *shared;
+    I4Args a{};
+    if (routed) {
+        a.w0 = reinterpret_cast<const uint8_t*>(routed->w0);
+        a.w1 = reinterpret_cast<const uint8_t*>(routed->w1);
+        a.s0 = routed->s0;
+        a.s1 = routed->s1;
+        a.in = reinterpret_cast<const uint16_t*>(routed->in);
+        a.out = routed->out;
+        a.counts = routed->counts;
+        a.offsets = routed->offsets;
+        a.perm = routed->perm;
+        a.topk = routed->topk;
+        a.E = routed->E;
+        a.tau = routed->tau;
+        if (!a.counts || !a.offsets) return hipErrorInvalidValue;
+    }
+    if (shared) {
+        a.sw0 = reinterpret_cast<const uint8_t*>(shared->w0);
+        a.sw1 = reinterpret_cast<const uint8_t*>(shared->w1);
+        a.ss0 = shared->s0;
+        a.ss1 = shared->s1;
+        a.sin = reinterpret_cast<const uint16_t*>(shared->in);
+        a.sout = shared->out;
+        if (!a.sw0) return hipErrorInvalidValue;
+    }
     a.N = g.N;
     a.K = g.K;
-    a.topk = g.topk;
     a.T = g.T;
-    a.E = g.E;
-    a.tau = g.tau;
     a.P = i4_pass_tokens(g.K);
     if (a.E > kMaxE || a.P < 1) return hipErrorInvalidValue;
     const size_t lds = (size_t)(a.P + 1) * ((size_t)g.K * 2 + 16) + (size_t)(g.K / 128) * 16 * 4;
@@ -422,7 +486,8 @@ hipError_t launch_i4mfma(int mode, const GemvArgs& g, int max_items_hint, hipStr
         (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
         if (n_cu < 1) n_cu = 256;
     }
-    auto k = mode == 0 ? i4_mfma_kernel<0> : i4_mfma_kernel<1>;
+    // gate/up: 8 steps of 2 KB per wave in flight; down: 16 steps of 1 KB
+    auto k = mode == 0 ? i4_mfma_kernel<0, 8> : i4_mfma_kernel<1, 16>;
     if (!attr_set[mode]) {
         // dynamic LDS beyond 64 KB: the budget left next to the static arrays
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
@@ -430,9 +495,7 @@ hipError_t launch_i4mfma(int mode, const GemvArgs& g, int max_items_hint, hipStr
                                   (int)(kLdsBytes - kStaticLds));
         attr_set[mode] = true;
     }
-    int grid = n_cu;
-    if (max_items_hint > 0 && grid > max_items_hint) grid = max_items_hint;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL(k, dim3(n_cu), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 

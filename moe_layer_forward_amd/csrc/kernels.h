@@ -29,8 +29,10 @@ hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, i
                        hipStream_t s);
 int gemv_max_k(int wt);
 // int4-g128 weights on the matrix cores (ffn_i4mfma.hip): K a multiple of 1024.
+// One launch serves the routed experts (counts/offsets set) and, when
+// `shared` is given, the shared expert over all T tokens; either may be null.
 bool i4mfma_supported(int K, int N);
-hipError_t launch_i4mfma(int mode, const GemvArgs& a, int max_items_hint, hipStream_t s);
+hipError_t launch_i4mfma(int mode, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s);
 int gemv_rows_per_item(int wt, int mode, int K, int N, int active);
 int mfma_bm();
 int mfma_max_tiles(int T, int k, int E);
