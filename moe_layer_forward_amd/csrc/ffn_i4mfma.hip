@@ -27,9 +27,9 @@
 //    waves of the block; token slots past the group read an all-zero row;
 //  * a persistent grid (one 512-thread block per CU) walks equal-sized work
 //    items (active expert, token pass, 128 rows); each wave owns 16 rows and
-//    runs a flat stream of (item, group) steps with 16 KB of weight loads in
-//    flight in a register ring (8 groups of gate+up, 16 groups of down; 128 KB
-//    per CU), so the stream continues across item boundaries; the buffer range
+//    runs a flat stream of (item, group) steps with the weight loads of 8
+//    groups in flight in a register ring (16 KB per wave for gate+up), so the
+//    stream continues across item boundaries; the buffer range
 //    check returns zeros past the last row and past the block's range, so
 //    loads never branch;
 //  * the lane layout gives each load instruction 16 rows x 64 bytes, half of
@@ -125,7 +125,7 @@ struct I4Args {
 template <int MODE, int RING>
 __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     constexpr int G = MODE == 0 ? 2 : 1;
-    static_assert(RING == 8 || RING == 16, "ring of 8 or 16 steps");
+    static_assert(RING == 8, "the scale prefetch runs 8 steps ahead, as far as the ring");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ int s_act[kMaxE + 1], s_cnt[kMaxE + 1], s_off[kMaxE + 1], s_ipref[kMaxE + 2];
     __shared__ int s_tot[2], s_src[16];
@@ -237,11 +237,11 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     const uint32_t lq = (uint32_t)(lane >> 4);
     const uint32_t woff_l = lrow * rb + lq * 16u;            // lane part of a weight offset
     const uint32_t soff_l = lrow * srow;                      // lane part of a scale offset
+    const uint32_t lrow16 = (uint32_t)(lane & 15);
 
     // ---- weight loads of steps q and q+1 into ring slots S, S+1: the two
     // halves of the same 128-byte lines, back to back (zeros past the range)
     u32x4_t wq[RING][G];
-    u32x4_t sq[2][G];
     auto weight_ptr = [&](const Cursor& q, int m) -> const uint8_t* {
         if (q.e >= 0) return (m == 0 ? a.w0 : a.w1) + (size_t)q.e * mat_bytes;
         return m == 0 ? a.sw0 : a.sw1;
@@ -261,16 +261,22 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
         q = q1;
         advance(q, 1);
     };
-    // fp16 scales of the 8 groups starting at step q (a chunk) into slot SS
-    auto issue_scales = [&](const Cursor& q, auto sslot) {
-        constexpr int SS = decltype(sslot)::value;
-        const uint32_t so = soff_l + (uint32_t)q.chunk * kItemRows * srow + (uint32_t)(q.g >> 3) * 16u;
+    // fp16 scales of a 16-row set (16 rows x NG x 2 bytes, contiguous): lane
+    // (row n, q) loads chunks q and q + 4 (8 groups each) of row n with two
+    // back-to-back loads that together cover every line of the set once
+    u32x4_t snext[G][2], scur[G][2];
+    auto issue_scales = [&](const Cursor& q) {
+        const uint32_t so = soff_l + (uint32_t)q.chunk * kItemRows * srow + lq * 16u;
         const uint32_t sn = q.idx < nsteps ? (uint32_t)N * srow : 0u;
 #pragma unroll
         for (int m = 0; m < G; ++m) {
             const uint16_t* sp = q.e >= 0 ? (m == 0 ? a.s0 : a.s1) + (size_t)q.e * N * NG
                                           : (m == 0 ? a.ss0 : a.ss1);
-            sq[SS][m] = ld16(rsrc(sp, sn), so);
+            snext[m][0] = ld16(rsrc(sp, sn), so);
+            // chunks 4..7 exist only past 32 groups; else an offset the range
+            // check rejects (no memory access; a conditional load would make
+            // the compiler wait for it at once)
+            snext[m][1] = ld16(rsrc(sp, sn), NG > 32 ? so + 64u : 0xffffffffu);
         }
     };
 
@@ -335,9 +341,13 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
 #pragma unroll
     for (int m = 0; m < G; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const Cursor& q, auto slot, auto sslot, auto half) {
-        constexpr int S = decltype(slot)::value, SS = decltype(sslot)::value,
-                      H = decltype(half)::value;   // group index within the scale chunk
+    auto compute = [&](const Cursor& q, auto slot, auto half) {
+        constexpr int S = decltype(slot)::value,
+                      H = decltype(half)::value;   // group index within its 8-group chunk
+        // the scale of (row n, group g) sits in lane n + 16 (c % 4), register
+        // c / 4 of the row set's scales, c = g / 8
+        const int c8 = q.g >> 3;
+        const int src = (int)((lrow16 + 16u * (uint32_t)(c8 & 3)) << 2);
         const char* xg = xrows + xa + (uint32_t)q.g * 256u;
         u32x4_t af[4];
 #pragma unroll
@@ -358,7 +368,8 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
                 c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
                                                              __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
             }
-            const uint32_t sw = sq[SS][m][H >> 1];
+            const uint32_t own = (c8 >> 2) ? scur[m][1][H >> 1] : scur[m][0][H >> 1];
+            const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)own);
             const float sc = f16_to_f32((uint16_t)((H & 1) ? (sw >> 16) : (sw & 0xffffu)));
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[m][v] = fmaf(sc, fmaf(-136.0f, xs[v], c[v]), acc[m][v]);
@@ -388,16 +399,17 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     };
 
     // ---- prologue: RING steps of weights and the first scale chunk in flight
+    // Loads complete in order, so a row set's scales go out as far ahead as
+    // the weight ring reaches (8 steps)
     Cursor L = cur;       // next step whose weights are loaded
-    Cursor Sc = cur;      // next chunk whose scales are loaded
-    issue_scales(Sc, ic<0>{});
+    Cursor Sc = cur;      // loads a row set's scales when it reaches its start
+    issue_scales(Sc);
     advance(Sc, 8);
     static_for<0, RING / 2>([&](auto k) { issue_pair(L, ic<2 * decltype(k)::value>{}); });
 
-    // One step at unrolled position k (0..15): ring slot k % RING, scale slot
-    // k / 8.  Every other step refills the two slots just consumed with the
-    // steps RING ahead; the first step of a chunk loads the next chunk's
-    // scales.  Steps carry no exit test, so the compiler's wait counts see the
+    // One step at unrolled position k (0..15): ring slot k % RING.  Every
+    // other step refills the two slots just consumed with the steps RING
+    // ahead.  Steps carry no exit test, so the compiler's wait counts see the
     // whole ring.
     Cursor C = cur;
     auto step = [&](auto kk) {
@@ -409,9 +421,15 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
                 xa = (tok < (uint32_t)nt ? tok : (uint32_t)P) * RS + lq * 64u;
             }
         }
-        compute(C, ic<k % RING>{}, ic<k / 8>{}, ic<k % 8>{});
         if constexpr (k % 8 == 0) {
-            issue_scales(Sc, ic<1 - k / 8>{});
+            if (C.g == 0) {
+#pragma unroll
+                for (int m = 0; m < G; ++m) { scur[m][0] = snext[m][0]; scur[m][1] = snext[m][1]; }
+            }
+        }
+        compute(C, ic<k % RING>{}, ic<k % 8>{});
+        if constexpr (k % 8 == 0) {
+            if (Sc.g == 0) issue_scales(Sc);
             advance(Sc, 8);
         }
         if constexpr (k % 8 == 7) {
@@ -438,7 +456,8 @@ static int i4_pass_tokens(int K) {
 }
 
 bool i4mfma_supported(int K, int N) {
-    if (K % 1024 != 0 || K <= 0 || N <= 0) return false;
+    // K a multiple of 8 groups of 128, at most 64 groups (two scale registers)
+    if (K % 1024 != 0 || K <= 0 || K > 8192 || N <= 0) return false;
     if (i4_pass_tokens(K) < 1) return false;
     // 32-bit buffer offsets of a matrix, including the padded last chunk
     return (size_t)(N + kItemRows) * (size_t)(K / 2) < ((size_t)1 << 31);
@@ -486,8 +505,8 @@ hipError_t launch_i4mfma(int mode, const GemvArgs* routed, const GemvArgs* share
         (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
         if (n_cu < 1) n_cu = 256;
     }
-    // gate/up: 8 steps of 2 KB per wave in flight; down: 16 steps of 1 KB
-    auto k = mode == 0 ? i4_mfma_kernel<0, 8> : i4_mfma_kernel<1, 16>;
+    // 8 scale groups per wave in flight: 16 KB (gate/up) or 8 KB (down)
+    auto k = mode == 0 ? i4_mfma_kernel<0, 8> : i4_mfma_kernel<1, 8>;
     if (!attr_set[mode]) {
         // dynamic LDS beyond 64 KB: the budget left next to the static arrays
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
