@@ -194,6 +194,24 @@ def measured_traffic(key):
     return int(m.group(2))
 
 
+def read_ceiling_gbs(nbytes=4 << 30, reps=5):
+    """Measured HBM read ceiling: the library's plain streaming-read kernel over
+    a 4 GiB buffer (far beyond the caches), timed with HIP events."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for _ in range(2):
+        moe.moe_read_ceiling(buf, nbytes, sink)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        moe.moe_read_ceiling(buf, nbytes, sink)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def roofline_obj(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -250,10 +268,13 @@ def main():
                     kernel="expert FFN step (MFMA gate/up + down)", flops_per_launch=ffn_flops,
                     launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5))
     else:
+        ceil = read_ceiling_gbs()
         roof = dict(roofline_obj("hbm", achieved, HBM_PEAK_GBS, "GB/s",
                                  measured_traffic(cfg.name) if args.tau == 0 else None),
                     kernel="expert FFN step (gate/up + down GEMV)", bytes_per_launch=ffn_bytes,
-                    launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5))
+                    launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5),
+                    measured_read_ceiling=round(ceil, 1),
+                    frac_of_measured_ceiling=round(achieved / ceil, 4))
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),

@@ -175,6 +175,14 @@ size_t moe_workspace_bytes(const moe_shape *shape);
 int moe_rmsnorm(const moe_shape *shape, const void *h, const float *gamma, float eps,
                 void *out, void *stream, char *err, size_t err_len);
 
+/* Measurement helper, not part of the layer: reads bytes of device memory at
+ * buf once with plain streaming loads and XORs every 32-bit word of it into
+ * *sink (device, caller-initialised), the measured HBM read ceiling beside the
+ * published peak.  bytes a multiple of 16, buf 16-byte aligned; asynchronous
+ * on stream.  MOE_EINVAL for a NULL or misaligned pointer or a bad size. */
+int moe_read_ceiling(const void *buf, size_t bytes, uint32_t *sink, void *stream, char *err,
+                     size_t err_len);
+
 /* Static text of a moe_status. */
 const char *moe_strerror(int status);
 

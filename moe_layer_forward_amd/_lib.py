@@ -19,7 +19,7 @@ MOE_F32, MOE_BF16, MOE_INT4_G128 = 0, 1, 2
 DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128}
 
 EXPORTS = ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_workspace_bytes", "moe_rmsnorm", "moe_strerror")
+           "moe_workspace_bytes", "moe_rmsnorm", "moe_read_ceiling", "moe_strerror")
 
 
 class MoEError(RuntimeError):
@@ -60,10 +60,11 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.argtypes = [sp]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_rmsnorm.argtypes = [sp, vp, vp, ctypes.c_float, vp, vp, cp, sz]
+        L.moe_read_ceiling.argtypes = [vp, sz, vp, vp, cp, sz]
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                  "moe_layer_forward", "moe_rmsnorm"):
+                  "moe_layer_forward", "moe_rmsnorm", "moe_read_ceiling"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -142,6 +143,11 @@ def moe_layer_forward(shape, x, w_router, b_router, weights, residual, y, counts
     return _call("moe_layer_forward", ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(b_router),
                  ctypes.byref(weights), _ptr(residual), _ptr(y), _ptr(counts_out),
                  _ptr(topk_idx_out), _ptr(ws), nbytes, _stream(stream))
+
+
+def moe_read_ceiling(buf, nbytes, sink, stream=None):
+    """Streaming read of nbytes at buf, XORed into sink (measurement helper)."""
+    return _call("moe_read_ceiling", _ptr(buf), int(nbytes), _ptr(sink), _stream(stream))
 
 
 def moe_rmsnorm(shape, h, gamma, eps, out, stream=None):

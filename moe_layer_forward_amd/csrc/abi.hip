@@ -402,4 +402,14 @@ int moe_rmsnorm(const moe_shape* shape, const void* h, const float* gamma, float
                      err_len);
 }
 
+int moe_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, void* stream, char* err, size_t err_len) {
+    if (bytes % 16) return fail(err, err_len, MOE_EINVAL, "bytes=%zu is not a multiple of 16", bytes);
+    if (bytes) NEED_PTR(buf, "buf");
+    if (!sink) return fail(err, err_len, MOE_EINVAL, "sink is NULL");
+    if ((uintptr_t)sink % 4) return fail(err, err_len, MOE_EINVAL, "sink is not 4-byte aligned");
+    if (!bytes) return MOE_OK;
+    hipStream_t st = (hipStream_t)stream;
+    return hip_check(launch_read_ceiling(buf, bytes, sink, st), st, "read ceiling", err, err_len);
+}
+
 }  // extern "C"

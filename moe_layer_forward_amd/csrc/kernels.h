@@ -45,6 +45,7 @@ hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void*
 hipError_t launch_combine(int act, const float* yp, const int32_t* inv, const float* w,
                           const float* ys, const void* res, void* y, int T, int d, int k,
                           hipStream_t s);
+hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_rmsnorm(int act, const void* h, const float* gamma, float eps, void* out, int T,
                           int d, hipStream_t s);
 

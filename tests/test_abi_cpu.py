@@ -128,3 +128,17 @@ def test_rmsnorm_validation():
     s = moe.make_shape(4, 16, 8, 2, 128, "f32", "f32")
     with pytest.raises(moe.MoEError):
         moe.moe_rmsnorm(s, 1 << 20, None, -1.0, 1 << 20, stream=0)
+
+
+def test_read_ceiling_validation():
+    # rejected before any HIP call
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_read_ceiling(4096, 100, 8192)
+    assert e.value.status == moe.MOE_EINVAL
+    with pytest.raises(moe.MoEError):
+        moe.moe_read_ceiling(None, 1024, 8192)
+    with pytest.raises(moe.MoEError):
+        moe.moe_read_ceiling(4096, 1024, None)
+    with pytest.raises(moe.MoEError):
+        moe.moe_read_ceiling(4104, 1024, 8192)     # misaligned buffer
+    assert moe.moe_read_ceiling(None, 0, 8192) == 0

@@ -341,3 +341,17 @@ def test_rmsnorm_parity(orc):
         ref = orc.rmsnorm(np_store(h), act, g.numpy(), 1e-6)
         tol = 1e-6 if act == "f32" else 8e-3
         assert tokenwise_rel(np_f64(out), ref).max() < tol
+
+
+def test_read_ceiling_reads_every_word():
+    # the measurement helper folds every 32-bit word into the sink: XOR check
+    say("read ceiling helper")
+    g = torch.Generator().manual_seed(5)
+    for n_words in (4, 4 * 1000 + 4, 1 << 22):
+        h = torch.randint(-2**31, 2**31 - 1, (n_words,), generator=g, dtype=torch.int64).to(torch.int32)
+        buf = h.to(DEV)
+        sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+        moe.moe_read_ceiling(buf, n_words * 4, sink)
+        torch.cuda.synchronize()
+        ref = np.bitwise_xor.reduce(h.numpy().view(np.uint32))
+        assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(ref)
