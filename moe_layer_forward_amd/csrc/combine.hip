@@ -4,11 +4,11 @@
 // merged with the gate weights.  [P4] "Colibri：轻量级MoE推理引擎的C语言实践" §2.3:
 // the K slot results are merged back in the original token order.
 //
-// gfx950 design: a gather-reduce, never float atomics.  One 256-thread block
-// per token reads that token's k rows of y_perm through the inverse
-// permutation with 16-byte loads, sums them in slot order j = 0..k-1 in fp32
-// (plus the shared-expert row and the residual), and writes the output row
-// once.  The result is bit-identical run to run.  HBM-bound: k*d*4 bytes read
+// gfx950 design: a gather-reduce, never float atomics.  Each 256-thread block
+// covers 1024 elements of one token: every thread reads its 4-element chunk of
+// the token's k rows of y_perm through the inverse permutation (16-byte loads,
+// all in flight together), sums them in slot order j = 0..k-1 in fp32 (plus
+// the shared-expert row and the residual), and writes the output once.  The result is bit-identical run to run.  HBM-bound: k*d*4 bytes read
 // and d*2 (bf16) written per token.
 #include "common.h"
 #include "kernels.h"
@@ -22,46 +22,48 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                      const float* __restrict__ ys,
                                                      const void* __restrict__ res,
                                                      void* __restrict__ y, int d, int k) {
+    // block (t, c): token t, elements [1024 c, 1024 c + 1024) -- each thread one
+    // 4-element chunk, so all of a thread's k loads are in flight together
     const int t = blockIdx.x;
-    __shared__ int s_row[16];
-    __shared__ float s_w[16];
-    if (threadIdx.x < k) {
-        s_row[threadIdx.x] = inv[(size_t)t * k + threadIdx.x];
-        s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+    const int i = blockIdx.y * 1024 + threadIdx.x * 4;
+    if (i >= d) return;
+    float4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if (j >= k) break;
+        v[j] = *reinterpret_cast<const float4*>(yp + (size_t)inv[(size_t)t * k + j] * d + i);
     }
-    __syncthreads();
-    for (int i = threadIdx.x * 4; i < d; i += 256 * 4) {
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < k; ++j) {
-            const float4 v = *reinterpret_cast<const float4*>(yp + (size_t)s_row[j] * d + i);
-            const float wj = s_w[j];
-            acc.x = fmaf(wj, v.x, acc.x);
-            acc.y = fmaf(wj, v.y, acc.y);
-            acc.z = fmaf(wj, v.z, acc.z);
-            acc.w = fmaf(wj, v.w, acc.w);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if (j >= k) break;
+        const float wj = w[(size_t)t * k + j];
+        acc.x = fmaf(wj, v[j].x, acc.x);
+        acc.y = fmaf(wj, v[j].y, acc.y);
+        acc.z = fmaf(wj, v[j].z, acc.z);
+        acc.w = fmaf(wj, v[j].w, acc.w);
+    }
+    if (ys) {
+        const float4 q = *reinterpret_cast<const float4*>(ys + (size_t)t * d + i);
+        acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
+    }
+    if constexpr (ACT == DT_F32) {
+        if (res) {
+            const float4 r = *reinterpret_cast<const float4*>(
+                reinterpret_cast<const float*>(res) + (size_t)t * d + i);
+            acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
         }
-        if (ys) {
-            const float4 v = *reinterpret_cast<const float4*>(ys + (size_t)t * d + i);
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)t * d + i) = acc;
+    } else {
+        if (res) {
+            const uint2 r = *reinterpret_cast<const uint2*>(
+                reinterpret_cast<const uint16_t*>(res) + (size_t)t * d + i);
+            acc.x += bf16_lo(r.x); acc.y += bf16_hi(r.x); acc.z += bf16_lo(r.y); acc.w += bf16_hi(r.y);
         }
-        if constexpr (ACT == DT_F32) {
-            if (res) {
-                const float4 r = *reinterpret_cast<const float4*>(
-                    reinterpret_cast<const float*>(res) + (size_t)t * d + i);
-                acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
-            }
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)t * d + i) = acc;
-        } else {
-            if (res) {
-                const uint2 r = *reinterpret_cast<const uint2*>(
-                    reinterpret_cast<const uint16_t*>(res) + (size_t)t * d + i);
-                acc.x += bf16_lo(r.x); acc.y += bf16_hi(r.x); acc.z += bf16_lo(r.y); acc.w += bf16_hi(r.y);
-            }
-            uint2 o;
-            o.x = pack_bf16x2(acc.x, acc.y);
-            o.y = pack_bf16x2(acc.z, acc.w);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + (size_t)t * d + i) = o;
-        }
+        uint2 o;
+        o.x = pack_bf16x2(acc.x, acc.y);
+        o.y = pack_bf16x2(acc.z, acc.w);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + (size_t)t * d + i) = o;
     }
 }
 
@@ -69,10 +71,12 @@ hipError_t launch_combine(int act, const float* yp, const int32_t* inv, const fl
                           const float* ys, const void* res, void* y, int T, int d, int k,
                           hipStream_t s) {
     if (T == 0) return hipSuccess;
+    if (k > 16) return hipErrorInvalidValue;
+    const dim3 g(T, (d + 1023) / 1024);
     if (act == DT_F32)
-        hipLaunchKernelGGL(combine_kernel<DT_F32>, dim3(T), dim3(256), 0, s, yp, inv, w, ys, res, y, d, k);
+        hipLaunchKernelGGL(combine_kernel<DT_F32>, g, dim3(256), 0, s, yp, inv, w, ys, res, y, d, k);
     else
-        hipLaunchKernelGGL(combine_kernel<DT_BF16>, dim3(T), dim3(256), 0, s, yp, inv, w, ys, res, y, d, k);
+        hipLaunchKernelGGL(combine_kernel<DT_BF16>, g, dim3(256), 0, s, yp, inv, w, ys, res, y, d, k);
     return hipGetLastError();
 }
 

@@ -9,8 +9,8 @@
 // layer never leaves the device.
 //
 // gfx950 design: one 1024-thread workgroup (16 wave64s).  The histogram uses
-// LDS integer atomics (order-independent, so deterministic).  A Hillis-Steele
-// scan over E <= 256 bins gives the offsets.  Placement walks the assignments
+// LDS integer atomics (order-independent, so deterministic).  One wave scans
+// the E <= 256 bins (4 per lane, a shuffle scan) for the offsets.  Placement walks the assignments
 // in chunks of 1024: inside a wave, the rank of an element among equal keys
 // comes from 8 ballots on the key bits (peer mask, popcount of lower peers);
 // per-(wave, expert) counts go to an LDS table that is scanned wave-major per
@@ -28,7 +28,6 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, int n, int E) {
     __shared__ int s_cnt[DP_MAXE];
-    __shared__ int s_scan[2][DP_MAXE];
     __shared__ int s_cursor[DP_MAXE];
     __shared__ int s_wave[DP_WAVES][DP_MAXE];
     const int tid = threadIdx.x;
@@ -45,26 +44,33 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_kernel(
     }
     __syncthreads();
 
-    // 2. exclusive scan over the E bins (Hillis-Steele, inclusive then shift)
-    int cur = 0;
-    if (tid < DP_MAXE) s_scan[0][tid] = (tid < E) ? s_cnt[tid] : 0;
-    __syncthreads();
-    for (int o = 1; o < DP_MAXE; o <<= 1) {
-        if (tid < DP_MAXE) {
-            int v = s_scan[cur][tid];
-            if (tid >= o) v += s_scan[cur][tid - o];
-            s_scan[cur ^ 1][tid] = v;
+    // 2. exclusive scan over the E bins: wave 0, 4 bins per lane, one barrier
+    if (wave == 0) {
+        int c[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * lane + j;
+            c[j] = (e < E) ? s_cnt[e] : 0;
+            sum += c[j];
         }
-        cur ^= 1;
-        __syncthreads();
-    }
-    if (tid < E) {
-        const int incl = s_scan[cur][tid];
-        const int excl = incl - s_cnt[tid];
-        counts[tid] = s_cnt[tid];
-        offsets[tid] = excl;
-        s_cursor[tid] = excl;
-        if (tid == E - 1) offsets[E] = incl;
+        int incl = sum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
+        }
+        int run = incl - sum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * lane + j;
+            if (e < E) {
+                counts[e] = c[j];
+                offsets[e] = run;
+                s_cursor[e] = run;
+            }
+            run += c[j];
+        }
+        if (lane == 63) offsets[E] = incl;
     }
     __syncthreads();
 

@@ -8,9 +8,10 @@
 //
 // gfx950 design: the logits are a skinny [T,d]x[d,E] contraction that is at
 // most ~1% of the layer, so it runs on the VALU: a 256-thread block owns
-// 8 tokens x 4 experts, its threads split K in 4-element chunks, and the 32
-// per-lane partial sums are folded with a transposing wave reduction (32
-// shuffles instead of 192) before a cross-wave sum in LDS.  Top-k then runs
+// 8 tokens (1 for small batches) x 4 experts, its threads split K in
+// 4-element chunks with four chunks of loads in flight, and the per-lane
+// partial sums are folded with a transposing wave reduction before a
+// cross-wave sum in LDS.  Top-k then runs
 // one wave64 per token: each lane holds up to 4 logits, and k rounds of a
 // shuffle argmax (value descending, expert index ascending on ties) pick the
 // experts.  Selection is made on the fp32 logits (softmax is monotone); the
@@ -47,64 +48,84 @@ __device__ __forceinline__ float wave_reduce_multi(float (&v)[N], int lane) {
     return v[0];
 }
 
-constexpr int RT_TOK = 8;
 constexpr int RT_EXP = 4;
 constexpr int RT_THREADS = 256;
+constexpr int RT_U = 4;      // K iterations whose loads are in flight together
 
-template <int ACT>
+// TT tokens x 4 experts per block; the 256 threads split K in 4-element
+// chunks, RT_U chunks of loads are issued before their arithmetic.  TT = 8
+// reuses each router row for 8 tokens (many tokens); TT = 1 gives small
+// batches (decode) T x E/4 blocks instead of a handful.
+template <int ACT, int TT>
 __global__ __launch_bounds__(RT_THREADS) void router_logits_kernel(
     const void* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     float* __restrict__ logits, int T, int d, int E) {
-    const int t0 = blockIdx.x * RT_TOK;
+    const int t0 = blockIdx.x * TT;
     const int e0 = blockIdx.y * RT_EXP;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    float acc[RT_TOK * RT_EXP];
+    constexpr int NV = TT * RT_EXP;
+    float acc[NV];
 #pragma unroll
-    for (int i = 0; i < RT_TOK * RT_EXP; ++i) acc[i] = 0.f;
+    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
+    const int ne = min(RT_EXP, E - e0);
+    const int nt = min(TT, T - t0);
 
-    for (int kk = tid * 4; kk < d; kk += RT_THREADS * 4) {
-        float4 wv[RT_EXP];
+    for (int k0 = tid * 4; k0 < d; k0 += RT_THREADS * 4 * RT_U) {
+        float4 wv[RT_U][RT_EXP];
+        float xv[RT_U][TT][4];
 #pragma unroll
-        for (int e = 0; e < RT_EXP; ++e) {
-            if (e0 + e < E) wv[e] = *reinterpret_cast<const float4*>(wg + (size_t)(e0 + e) * d + kk);
-            else wv[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int u = 0; u < RT_U; ++u) {
+            const int kk = k0 + u * RT_THREADS * 4;
+            const bool kin = kk < d;
+#pragma unroll
+            for (int e = 0; e < RT_EXP; ++e)
+                wv[u][e] = (kin && e < ne) ? *reinterpret_cast<const float4*>(wg + (size_t)(e0 + e) * d + kk)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                if (kin && t < nt) {
+                    if constexpr (ACT == DT_F32) {
+                        const float4 q = *reinterpret_cast<const float4*>(
+                            reinterpret_cast<const float*>(x) + (size_t)(t0 + t) * d + kk);
+                        xv[u][t][0] = q.x; xv[u][t][1] = q.y; xv[u][t][2] = q.z; xv[u][t][3] = q.w;
+                    } else {
+                        const uint2 q = *reinterpret_cast<const uint2*>(
+                            reinterpret_cast<const uint16_t*>(x) + (size_t)(t0 + t) * d + kk);
+                        xv[u][t][0] = bf16_lo(q.x); xv[u][t][1] = bf16_hi(q.x);
+                        xv[u][t][2] = bf16_lo(q.y); xv[u][t][3] = bf16_hi(q.y);
+                    }
+                } else {
+                    xv[u][t][0] = xv[u][t][1] = xv[u][t][2] = xv[u][t][3] = 0.f;
+                }
+            }
         }
 #pragma unroll
-        for (int t = 0; t < RT_TOK; ++t) {
-            if (t0 + t >= T) break;
-            float xv[4];
-            if constexpr (ACT == DT_F32) {
-                float4 q = *reinterpret_cast<const float4*>(
-                    reinterpret_cast<const float*>(x) + (size_t)(t0 + t) * d + kk);
-                xv[0] = q.x; xv[1] = q.y; xv[2] = q.z; xv[3] = q.w;
-            } else {
-                uint2 q = *reinterpret_cast<const uint2*>(
-                    reinterpret_cast<const uint16_t*>(x) + (size_t)(t0 + t) * d + kk);
-                xv[0] = bf16_lo(q.x); xv[1] = bf16_hi(q.x); xv[2] = bf16_lo(q.y); xv[3] = bf16_hi(q.y);
-            }
+        for (int u = 0; u < RT_U; ++u)
 #pragma unroll
-            for (int e = 0; e < RT_EXP; ++e) {
-                float a = acc[t * RT_EXP + e];
-                a = fmaf(xv[0], wv[e].x, a);
-                a = fmaf(xv[1], wv[e].y, a);
-                a = fmaf(xv[2], wv[e].z, a);
-                a = fmaf(xv[3], wv[e].w, a);
-                acc[t * RT_EXP + e] = a;
-            }
-        }
+            for (int t = 0; t < TT; ++t)
+#pragma unroll
+                for (int e = 0; e < RT_EXP; ++e) {
+                    float s = acc[t * RT_EXP + e];
+                    s = fmaf(xv[u][t][0], wv[u][e].x, s);
+                    s = fmaf(xv[u][t][1], wv[u][e].y, s);
+                    s = fmaf(xv[u][t][2], wv[u][e].z, s);
+                    s = fmaf(xv[u][t][3], wv[u][e].w, s);
+                    acc[t * RT_EXP + e] = s;
+                }
     }
-    // fold 32 partials over the wave: lane l owns output index l >> 1
-    float r = wave_reduce_multi<RT_TOK * RT_EXP>(acc, lane);
-    __shared__ float part[RT_THREADS / 64][RT_TOK * RT_EXP];
-    if ((lane & 1) == 0) part[wave][lane >> 1] = r;
+    // fold the NV partials over the wave: lane l owns output index l >> (6 - log2 NV)
+    float r = wave_reduce_multi<NV>(acc, lane);
+    constexpr int SH = NV == 32 ? 1 : NV == 16 ? 2 : NV == 8 ? 3 : 4;
+    __shared__ float part[RT_THREADS / 64][NV];
+    if ((lane & ((1 << SH) - 1)) == 0) part[wave][lane >> SH] = r;
     __syncthreads();
-    if (tid < RT_TOK * RT_EXP) {
+    if (tid < NV) {
         const int t = tid / RT_EXP, e = tid % RT_EXP;
         float s = part[0][tid];
 #pragma unroll
         for (int w = 1; w < RT_THREADS / 64; ++w) s += part[w][tid];
-        if (t0 + t < T && e0 + e < E) {
+        if (t < nt && e < ne) {
             if (bias) s += bias[e0 + e];
             logits[(size_t)(t0 + t) * E + e0 + e] = s;
         }
@@ -171,13 +192,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 hipError_t launch_route(int act, const void* x, const float* wg, const float* b, float* logits,
                         int32_t* idx, float* w, int T, int d, int E, int k, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    dim3 g1((T + RT_TOK - 1) / RT_TOK, (E + RT_EXP - 1) / RT_EXP);
-    if (act == DT_F32)
-        hipLaunchKernelGGL(router_logits_kernel<DT_F32>, g1, dim3(RT_THREADS), 0, s, x, wg, b,
-                           logits, T, d, E);
-    else
-        hipLaunchKernelGGL(router_logits_kernel<DT_BF16>, g1, dim3(RT_THREADS), 0, s, x, wg, b,
-                           logits, T, d, E);
+    // few tokens x experts (decode): one token per block for enough blocks
+    const bool small = (long)T * E < 4096;
+    const int tt = small ? 1 : 8;
+    dim3 g1((T + tt - 1) / tt, (E + RT_EXP - 1) / RT_EXP);
+    if (act == DT_F32) {
+        if (small) hipLaunchKernelGGL((router_logits_kernel<DT_F32, 1>), g1, dim3(RT_THREADS), 0, s, x, wg, b, logits, T, d, E);
+        else hipLaunchKernelGGL((router_logits_kernel<DT_F32, 8>), g1, dim3(RT_THREADS), 0, s, x, wg, b, logits, T, d, E);
+    } else {
+        if (small) hipLaunchKernelGGL((router_logits_kernel<DT_BF16, 1>), g1, dim3(RT_THREADS), 0, s, x, wg, b, logits, T, d, E);
+        else hipLaunchKernelGGL((router_logits_kernel<DT_BF16, 8>), g1, dim3(RT_THREADS), 0, s, x, wg, b, logits, T, d, E);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, logits, idx, w, T, E, k);
