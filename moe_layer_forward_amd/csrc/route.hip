@@ -50,13 +50,13 @@ __device__ __forceinline__ float wave_reduce_multi(float (&v)[N], int lane) {
 
 constexpr int RT_EXP = 4;
 constexpr int RT_THREADS = 256;
-constexpr int RT_U = 4;      // K iterations whose loads are in flight together
 
 // TT tokens x 4 experts per block; the 256 threads split K in 4-element
-// chunks, RT_U chunks of loads are issued before their arithmetic.  TT = 8
-// reuses each router row for 8 tokens (many tokens); TT = 1 gives small
-// batches (decode) T x E/4 blocks instead of a handful.
-template <int ACT, int TT>
+// chunks, U chunks of loads are issued before their arithmetic.  TT = 8
+// reuses each router row for 8 tokens (many tokens; U = 1 keeps the register
+// count low enough for two blocks per CU); TT = 1 gives small batches
+// (decode) T x E/4 blocks instead of a handful, with U = 4.
+template <int ACT, int TT, int RT_U = (TT == 1 ? 4 : 1)>
 __global__ __launch_bounds__(RT_THREADS) void router_logits_kernel(
     const void* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
     float* __restrict__ logits, int T, int d, int E) {
