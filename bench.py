@@ -175,17 +175,30 @@ def cpu_baseline(cfg, runner, target_s=10.0):
                       f"({el:.1f} s)"}
 
 
+# kernel sources of each workload's expert-FFN step: the committed counter
+# summary is only valid for the sources it was taken on
+TRAFFIC_SOURCES = {"mixtral_decode": ["ffn_gemv.hip"], "fine_int4_decode": ["ffn_i4mfma.hip"]}
+
+
+def source_digest(key):
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[key]:
+        h.update(open(os.path.join(ROOT, "moe_layer_forward_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(key):
     """HBM bytes per launch of the dominant step, from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known
     size).  None when the kernel source changed since the counters were taken."""
-    import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", "mixtral_decode_ffn_traffic.md")
-    src = os.path.join(ROOT, "moe_layer_forward_amd", "csrc", "ffn_gemv.hip")
+    if key not in TRAFFIC_SOURCES:
+        return None
+    path = os.path.join(ROOT, "profiles", f"{key}_ffn_traffic.md")
     try:
         text = open(path).read()
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        digest = source_digest(key)
     except OSError:
         return None
     m = re.search(r"^%s: source=([0-9a-f]{16}) traffic_bytes=([0-9]+)" % re.escape(key), text, re.M)

@@ -17,6 +17,8 @@
 // experts.  Selection is made on the fp32 logits (softmax is monotone); the
 // weights are the softmax of the selected logits, which equals the full
 // softmax renormalised over the selection.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -72,31 +74,41 @@ __global__ __launch_bounds__(RT_THREADS) void router_logits_kernel(
     const int nt = min(TT, T - t0);
 
     for (int k0 = tid * 4; k0 < d; k0 += RT_THREADS * 4 * RT_U) {
+        // every load is issued unconditionally (rows clamped into range, K
+        // chunks past d re-read chunk 0 and are zeroed afterwards), so all of
+        // them are in flight before the first use
         float4 wv[RT_U][RT_EXP];
-        float xv[RT_U][TT][4];
+        using XRaw = typename std::conditional<ACT == DT_F32, float4, uint2>::type;
+        XRaw xr[RT_U][TT];
 #pragma unroll
         for (int u = 0; u < RT_U; ++u) {
             const int kk = k0 + u * RT_THREADS * 4;
-            const bool kin = kk < d;
+            const int kc = kk < d ? kk : 0;
 #pragma unroll
             for (int e = 0; e < RT_EXP; ++e)
-                wv[u][e] = (kin && e < ne) ? *reinterpret_cast<const float4*>(wg + (size_t)(e0 + e) * d + kk)
-                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+                wv[u][e] = *reinterpret_cast<const float4*>(wg + (size_t)(e0 + min(e, ne - 1)) * d + kc);
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
-                if (kin && t < nt) {
-                    if constexpr (ACT == DT_F32) {
-                        const float4 q = *reinterpret_cast<const float4*>(
-                            reinterpret_cast<const float*>(x) + (size_t)(t0 + t) * d + kk);
-                        xv[u][t][0] = q.x; xv[u][t][1] = q.y; xv[u][t][2] = q.z; xv[u][t][3] = q.w;
-                    } else {
-                        const uint2 q = *reinterpret_cast<const uint2*>(
-                            reinterpret_cast<const uint16_t*>(x) + (size_t)(t0 + t) * d + kk);
-                        xv[u][t][0] = bf16_lo(q.x); xv[u][t][1] = bf16_hi(q.x);
-                        xv[u][t][2] = bf16_lo(q.y); xv[u][t][3] = bf16_hi(q.y);
-                    }
+                const size_t row = (size_t)(t0 + min(t, nt - 1)) * d + kc;
+                xr[u][t] = *reinterpret_cast<const XRaw*>(reinterpret_cast<const char*>(x) + row * sizeof(XRaw) / 4);
+            }
+        }
+        // keep the loads above together, ahead of their first use
+        __builtin_amdgcn_sched_barrier(0);
+        float xv[RT_U][TT][4];
+#pragma unroll
+        for (int u = 0; u < RT_U; ++u) {
+            if (k0 + u * RT_THREADS * 4 >= d) {
+#pragma unroll
+                for (int e = 0; e < RT_EXP; ++e) wv[u][e] = make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                if constexpr (ACT == DT_F32) {
+                    xv[u][t][0] = xr[u][t].x; xv[u][t][1] = xr[u][t].y; xv[u][t][2] = xr[u][t].z; xv[u][t][3] = xr[u][t].w;
                 } else {
-                    xv[u][t][0] = xv[u][t][1] = xv[u][t][2] = xv[u][t][3] = 0.f;
+                    xv[u][t][0] = bf16_lo(xr[u][t].x); xv[u][t][1] = bf16_hi(xr[u][t].x);
+                    xv[u][t][2] = bf16_lo(xr[u][t].y); xv[u][t][3] = bf16_hi(xr[u][t].y);
                 }
             }
         }
