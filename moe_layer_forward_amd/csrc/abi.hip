@@ -108,7 +108,6 @@ Layout layout(const moe_shape* s) {
     const size_t T = s->T, k = s->k, E = s->E, d = s->d, F = s->F;
     const size_t hb = (s->act == MOE_F32) ? 4 : 2;
     const size_t tk = T * k;
-    const size_t max_mt = (size_t)mfma_max_tiles(s->T, s->k, s->E);
     Layout L;
     size_t o = 0;
     L.logits = o; o += up(T * E * 4);
@@ -118,7 +117,7 @@ Layout layout(const moe_shape* s) {
     L.offsets = o; o += up((E + 1) * 4);
     L.perm = o; o += up(tk * 4);
     L.inv = o; o += up(tk * 4);
-    L.tiles = o; o += up((3 * max_mt + 1) * 4);
+    L.tiles = o; o += up((size_t)mfma_plan_ints(s->T, s->k, s->E) * 4);
     L.h = o; o += up(tk * F * hb);
     L.yp = o; o += up(tk * d * 4);
     L.hs = o; o += s->n_shared ? up(T * F * hb) : 0;
@@ -188,7 +187,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     rc = pass(0, "gate/up");
     if (rc) return rc;
     if (use_mfma) {
-        rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, s->T, st),
+        rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, s->E, s->T, st),
                        st, "mfma gate/up", err, err_len);
         if (rc) return rc;
     }
@@ -202,7 +201,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     rc = pass(1, "down");
     if (rc) return rc;
     if (use_mfma) {
-        rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, s->T * s->k, st),
+        rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, s->E, s->T * s->k, st),
                        st, "mfma down", err, err_len);
         if (rc) return rc;
     }

@@ -46,41 +46,74 @@ constexpr int MF_NS = 4;          // LDS stages (3 K steps of prefetch in flight
 constexpr int MF_GM = 8;          // M-tiles per scheduling group
 constexpr uint32_t MF_OOB = 0x80000000u;   // beyond any buffer: the range check yields 0
 
+constexpr int MS_BM = 64;          // rows of a small M-tile
+
 int mfma_bm() { return MF_BM; }
+// Big tiles: experts with more than 128 rows, in 256-row tiles (the tail
+// tile's weights stream with the expert's other tiles).  Small tiles: experts
+// with at most 128 rows, as one or two 64-row tiles, so a ~50-row group does
+// not pay for a 256-row tile.
 int mfma_max_tiles(int T, int k, int E) { return (T * k + MF_BM - 1) / MF_BM + E; }
+int mfma_max_small(int E) { return 2 * E; }
+int mfma_plan_ints(int T, int k, int E) {
+    return 3 * mfma_max_tiles(T, k, E) + 1 + 3 * mfma_max_small(E) + 1;
+}
 int mfma_ntiles_n(int mode, int N) { return mode == 0 ? (N + 127) / 128 : (N + MF_BN - 1) / MF_BN; }
 
+// One 256-thread block: per expert with more than tau rows, its big and small
+// tiles; exclusive scans over the experts place them.  List layout (ints):
+// big: expert[max_mt], row0[max_mt], rows[max_mt], count; then the same for
+// the small tiles with max_st entries.
 __global__ __launch_bounds__(256) void mfma_plan_kernel(const int32_t* __restrict__ counts,
                                                        const int32_t* __restrict__ offsets, int E,
                                                        int tau, int32_t* __restrict__ tiles,
-                                                       int max_mt) {
-    __shared__ int s[2][256];
+                                                       int max_mt, int max_st) {
+    __shared__ int s[2][2][256];
     const int tid = threadIdx.x;
-    int c = 0, n = 0;
+    int c = 0, nb = 0, ns = 0, rem = 0;
     if (tid < E) {
         c = counts[tid];
-        n = (c > tau) ? (c + MF_BM - 1) / MF_BM : 0;
+        if (c > tau) {
+            if (c > 2 * MS_BM) {
+                nb = (c + MF_BM - 1) / MF_BM;
+            } else {
+                rem = c;
+                ns = (c + MS_BM - 1) / MS_BM;
+            }
+        }
     }
     int cur = 0;
-    s[0][tid] = n;
+    s[0][0][tid] = nb;
+    s[0][1][tid] = ns;
     __syncthreads();
     for (int o = 1; o < 256; o <<= 1) {
-        int v = s[cur][tid];
-        if (tid >= o) v += s[cur][tid - o];
-        s[cur ^ 1][tid] = v;
+        int v0 = s[cur][0][tid], v1 = s[cur][1][tid];
+        if (tid >= o) { v0 += s[cur][0][tid - o]; v1 += s[cur][1][tid - o]; }
+        s[cur ^ 1][0][tid] = v0;
+        s[cur ^ 1][1][tid] = v1;
         cur ^= 1;
         __syncthreads();
     }
-    const int start = s[cur][tid] - n;
+    int32_t* small = tiles + 3 * max_mt + 1;
     if (tid < E) {
         const int o0 = offsets[tid];
-        for (int i = 0; i < n; ++i) {
-            tiles[start + i] = tid;
-            tiles[max_mt + start + i] = o0 + i * MF_BM;
-            tiles[2 * max_mt + start + i] = min(MF_BM, c - i * MF_BM);
+        const int sb = s[cur][0][tid] - nb, ss = s[cur][1][tid] - ns;
+        for (int i = 0; i < nb; ++i) {
+            tiles[sb + i] = tid;
+            tiles[max_mt + sb + i] = o0 + i * MF_BM;
+            tiles[2 * max_mt + sb + i] = min(MF_BM, c - i * MF_BM);
+        }
+        const int base = o0 + c - rem;
+        for (int j = 0; j < ns; ++j) {
+            small[ss + j] = tid;
+            small[max_st + ss + j] = base + j * MS_BM;
+            small[2 * max_st + ss + j] = min(MS_BM, rem - j * MS_BM);
         }
     }
-    if (tid == 255) tiles[3 * max_mt] = s[cur][255];
+    if (tid == 255) {
+        tiles[3 * max_mt] = s[cur][0][255];
+        small[3 * max_st] = s[cur][1][255];
+    }
 }
 
 struct MfmaArgs {
@@ -90,7 +123,7 @@ struct MfmaArgs {
     void* out;               // h bf16 [T*k][N] (mode 0) or y_perm fp32 [T*k][N] (mode 1)
     const int32_t* perm;
     const int32_t* tiles;    // plan: expert[max_mt], row0[max_mt], rows[max_mt], n_mt
-    int N, K, topk, max_mt, in_rows;
+    int N, K, topk, max_mt, max_st, in_rows;
 };
 
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
@@ -328,16 +361,175 @@ __global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
     }
 }
 
+// Small M-tiles (at most 64 rows: small expert groups and short remainders).
+// Block tile 64 x 256 (gate/up: 128 gate + the 128 matching up rows), four
+// waves side by side, each 64 x 64 = 2 x 2 accumulators of
+// v_mfma_f32_32x32x16_bf16; K in stages of 32 (4 KiB of A, 16 KiB of B),
+// four LDS stages with three stages of copies in flight, 80 KiB of LDS so two
+// blocks share a CU.  Such tiles stream each weight tile for few rows, so the
+// kernel is bound by the weight stream, not the matrix cores.
+constexpr int MS_NS = 4;
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void mfma_small_kernel(MfmaArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[MS_NS][MS_BM * 32];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[MS_NS][MF_BN * 32];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int K = a.K, N = a.N;
+    const int32_t* tl = a.tiles + 3 * a.max_mt + 1;
+    const int max_st = a.max_st;
+    const int n_st = tl[3 * max_st];
+    const int nN = (MODE == 0) ? (N + 127) / 128 : (N + MF_BN - 1) / MF_BN;
+    const int total = n_st * nN;
+    const uint32_t row_bytes = (uint32_t)K * 2u;
+    const int nk = (K + 31) / 32;
+    const int32x4_t RA = make_desc(a.in, (uint32_t)a.in_rows * row_bytes);
+    const uint32_t wmat = (uint32_t)N * row_bytes;
+    // copies: an instruction fills 16 tile rows x 64 B; lane -> row lane/4,
+    // physical chunk lane%4.  Wave w copies A rows 16w.. and B rows 64w + 16i..
+    const int crow = lane >> 2;
+
+    for (int L = blockIdx.x; L < total; L += gridDim.x) {
+        // small tiles of one expert next to each other: consecutive blocks
+        // share the weight tile of one N column
+        const int st_i = L % n_st, nt = L / n_st;
+        const int e = tl[st_i];
+        const int p0 = tl[max_st + st_i];
+        const int rows = tl[2 * max_st + st_i];
+
+        const uint16_t* wsrc = (MODE == 0 && wave >= 2) ? a.w1 : a.w0;
+        const int32x4_t RB = make_desc(wsrc + (size_t)e * N * K, wmat);
+        uint32_t aoff, boff[4];
+        int acol, bcol[4];
+        {
+            const int r = wave * 16 + crow;
+            const int ch = (lane & 3) ^ ((r >> 2) & 3);
+            acol = ch * 8;
+            if (r < rows) {
+                const int src = (MODE == 0) ? a.perm[p0 + r] / a.topk : p0 + r;
+                aoff = (uint32_t)src * row_bytes + (uint32_t)ch * 16u;
+            } else {
+                aoff = MF_OOB;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wave * 64 + i * 16 + crow;
+            const int ch = (lane & 3) ^ ((r >> 2) & 3);
+            bcol[i] = ch * 8;
+            const int n = (MODE == 0) ? nt * 128 + (r & 127) : nt * MF_BN + r;
+            boff[i] = (n < N) ? (uint32_t)n * row_bytes + (uint32_t)ch * 16u : MF_OOB;
+        }
+        floatx16 acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+        auto issue = [&](int kt) {                     // the 5 copies of this lane for stage kt
+            const int st = kt % MS_NS;
+            const uint32_t kb = (uint32_t)kt * 64u;
+            const int k0 = kt * 32;
+            dma16(RA, (k0 + acol < K && aoff != MF_OOB) ? aoff + kb : MF_OOB,
+                  lds_addr(&sA[st][(wave * 16) * 32]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dma16(RB, (k0 + bcol[i] < K && boff[i] != MF_OOB) ? boff[i] + kb : MF_OOB,
+                      lds_addr(&sB[st][(wave * 64 + i * 16) * 32]));
+        };
+        auto brow = [&](int ni) {
+            return (MODE == 0) ? ni * 128 + wave * 32 + (lane & 31) : wave * 64 + ni * 32 + (lane & 31);
+        };
+        bf16x8_t fa[2][2][2], fb[2][2][2];            // [slot][ks][mi or ni]
+        auto read = [&](int st, int sl) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+                    fa[sl][ks][mi] = *reinterpret_cast<const bf16x8_t*>(&sA[st][swz(mi * 32 + (lane & 31), ch)]);
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    fb[sl][ks][ni] = *reinterpret_cast<const bf16x8_t*>(&sB[st][swz(brow(ni), ch)]);
+            }
+        };
+        auto mma = [&](int sl) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][ks][mi], fb[sl][ks][ni],
+                                                                               acc[mi][ni], 0, 0, 0);
+        };
+
+        // previous tile's stores and reads are done before the stages refill
+        wait_vm(0);
+        block_barrier();
+#pragma unroll
+        for (int kt = 0; kt < MS_NS; ++kt) issue(kt);  // stages past nk copy zeros
+        __builtin_amdgcn_s_waitcnt(0x0F7F);             // vmcnt(15): stage 0 landed
+        block_barrier();
+        read(0, 0);
+        // per stage kt (its fragments in slot kt&1): stage kt+1 landed and every
+        // wave is done reading stage kt's buffer -> refill it with stage kt+4,
+        // read stage kt+1, multiply stage kt
+        auto step = [&](int kt, auto slc) {
+            constexpr int sl = decltype(slc)::value;
+            __builtin_amdgcn_s_waitcnt(0x0F7A);         // vmcnt(10): stage kt+1 landed
+            __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0): own reads of stage kt done
+            block_barrier();
+            issue(kt + MS_NS);
+            read((kt + 1) % MS_NS, sl ^ 1);
+            mma(sl);
+        };
+        const int nk2 = (nk + 1) & ~1;                  // an extra step multiplies zeros
+        for (int kt = 0; kt < nk2; kt += 2) {
+            step(kt, std::integral_constant<int, 0>{});
+            step(kt + 1, std::integral_constant<int, 1>{});
+        }
+
+        // ---- epilogue; accumulator element v of lane l: column l%32, row 8*(v/4) + 4*(l/32) + v%4
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row >= rows) continue;
+                const size_t prow = (size_t)(p0 + row) * N;
+                if (MODE == 0) {
+                    const int f = nt * 128 + wave * 32 + (lane & 31);
+                    if (f < N) {
+                        const float h = silu(acc[mi][0][v]) * acc[mi][1][v];
+                        reinterpret_cast<uint16_t*>(a.out)[prow + f] = f32_to_bf16(h);
+                    }
+                } else {
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) {
+                        const int n = nt * MF_BN + wave * 64 + ni * 32 + (lane & 31);
+                        if (n < N) reinterpret_cast<float*>(a.out)[prow + n] = acc[mi][ni][v];
+                    }
+                }
+            }
+        }
+    }
+}
+
 hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int E, int tau,
                             int32_t* tiles, int max_mt, hipStream_t s) {
     hipLaunchKernelGGL(mfma_plan_kernel, dim3(1), dim3(256), 0, s, counts, offsets, E, tau, tiles,
-                       max_mt);
+                       max_mt, mfma_max_small(E));
     return hipGetLastError();
 }
 
 hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void* in, void* out,
                            const int32_t* perm, const int32_t* tiles, int N, int K, int topk,
-                           int max_mt, int in_rows, hipStream_t s) {
+                           int max_mt, int E, int in_rows, hipStream_t s) {
     MfmaArgs a;
     a.w0 = reinterpret_cast<const uint16_t*>(w0);
     a.w1 = reinterpret_cast<const uint16_t*>(w1);
@@ -349,6 +541,7 @@ hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void*
     a.K = K;
     a.topk = topk;
     a.max_mt = max_mt;
+    a.max_st = mfma_max_small(E);
     a.in_rows = in_rows;
     static int n_cu = 0;
     if (n_cu == 0) {
@@ -357,12 +550,23 @@ hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void*
         if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
             n_cu = 256;
     }
-    const int slots = max_mt * mfma_ntiles_n(mode, N);
+    const int nN = mfma_ntiles_n(mode, N);
+    // big tiles: one 256-thread block per CU
+    const int slots = max_mt * nN;
     const int grid = slots < n_cu ? slots : n_cu;
     if (mode == 0)
         hipLaunchKernelGGL(mfma_ffn_kernel<0>, dim3(grid), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(mfma_ffn_kernel<1>, dim3(grid), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // small tiles: two blocks per CU
+    const int sslots = a.max_st * nN;
+    const int sgrid = sslots < 2 * n_cu ? sslots : 2 * n_cu;
+    if (mode == 0)
+        hipLaunchKernelGGL(mfma_small_kernel<0>, dim3(sgrid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(mfma_small_kernel<1>, dim3(sgrid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -36,12 +36,14 @@ hipError_t launch_i4mfma(int mode, const GemvArgs* routed, const GemvArgs* share
 int gemv_rows_per_item(int wt, int mode, int K, int N, int active);
 int mfma_bm();
 int mfma_max_tiles(int T, int k, int E);
+int mfma_max_small(int E);
+int mfma_plan_ints(int T, int k, int E);
 int mfma_ntiles_n(int mode, int N);
 hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int E, int tau,
                             int32_t* tiles, int max_mt, hipStream_t s);
 hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void* in, void* out,
                            const int32_t* perm, const int32_t* tiles, int N, int K, int topk,
-                           int max_mt, int in_rows, hipStream_t s);
+                           int max_mt, int E, int in_rows, hipStream_t s);
 hipError_t launch_combine(int act, const float* yp, const int32_t* inv, const float* w,
                           const float* ys, const void* res, void* y, int T, int d, int k,
                           hipStream_t s);

@@ -328,6 +328,27 @@ def test_groups_straddling_tau(orc):
         assert tokenwise_rel(np_f64(y), y_f).max() < TOL["bf16"]
 
 
+def test_mfma_tile_boundaries(orc):
+    """Expert groups around the M-tile sizes: 64-row tiles for groups of at
+    most 128 rows (one or two tiles), 256-row tiles (ragged tail) above."""
+    say("mfma tile boundaries")
+    cfg = SMALL["bf16_prefill_ragged"]
+    d = device_inputs(cfg)
+    b = torch.zeros(cfg.E)
+    b[0] = 1e3          # expert 0 takes every token; the runner-ups spread the rest
+    d1 = dict(d, b_router=b.to(DEV))
+    W, S = oracle_weights(d)
+    for TT in (64, 65, 128, 129, 257, 300, 384):
+        x = d["x"][:TT].contiguous()
+        y, c, i = run_layer(cfg, d1, tau=16, x=x)
+        assert int(c[0]) == TT
+        y_f, _, _, _ = orc.layer_forward(np_store(x), "bf16", "bf16", cfg.k, np_store(d["w_router"]),
+                                         b.numpy(), W, forced_idx=i.cpu().numpy())
+        err = tokenwise_rel(np_f64(y), y_f).max()
+        say(f"  T={TT} counts {c.cpu().tolist()} max rel {err:.3g}")
+        assert err < TOL["bf16"]
+
+
 def test_rmsnorm_parity(orc):
     say("rmsnorm")
     for act in ("f32", "bf16"):
