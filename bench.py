@@ -284,7 +284,11 @@ def main():
         ceil = read_ceiling_gbs()
         roof = dict(roofline_obj("hbm", achieved, HBM_PEAK_GBS, "GB/s",
                                  measured_traffic(cfg.name) if args.tau == 0 else None),
-                    kernel="expert FFN step (gate/up + down GEMV)", bytes_per_launch=ffn_bytes,
+                    kernel=("expert FFN step (gate/up + down, 64-row MFMA tiles)"
+                            if cfg.wt == "bf16" and args.tau >= 0 and cfg.T * cfg.k / max(U, 1) > 16
+                            else "expert FFN step (gate/up + down, int4 skinny MFMA)" if cfg.wt == "int4"
+                            else "expert FFN step (gate/up + down GEMV)"),
+                    bytes_per_launch=ffn_bytes,
                     launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5),
                     measured_read_ceiling=round(ceil, 1),
                     frac_of_measured_ceiling=round(achieved / ceil, 4))

@@ -15,55 +15,62 @@
 
 namespace moe {
 
-template <int ACT>
+template <int ACT, int KK>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ yp,
                                                      const int32_t* __restrict__ inv,
                                                      const float* __restrict__ w,
                                                      const float* __restrict__ ys,
                                                      const void* __restrict__ res,
-                                                     void* __restrict__ y, int d, int k) {
-    // block (t, c): token t, elements [1024 c, 1024 c + 1024) -- each thread one
-    // 4-element chunk, so all of a thread's k loads are in flight together
-    const int t = blockIdx.x;
-    const int i = blockIdx.y * 1024 + threadIdx.x * 4;
+                                                     void* __restrict__ y, int T, int d, int k) {
+    // block (c, t): token t, elements [1024 c, 1024 c + 1024) -- each thread one
+    // 4-element chunk, so all of a thread's k loads are in flight together;
+    // consecutive blocks walk along the same rows (tokens beyond the grid's y
+    // extent are taken in a stride)
+    // KK > 0: k known at compile time, so all k loads of a thread are issued
+    // together (a runtime trip count serialises them); KK == 0: any k <= 16
+    if constexpr (KK > 0) k = KK;
+    const int i = blockIdx.x * 1024 + threadIdx.x * 4;
     if (i >= d) return;
-    float4 v[16];
+    for (int t = blockIdx.y; t < T; t += gridDim.y) {
+        constexpr int NJ = KK > 0 ? KK : 16;
+        float4 v[NJ];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j >= k) break;
-        v[j] = *reinterpret_cast<const float4*>(yp + (size_t)inv[(size_t)t * k + j] * d + i);
-    }
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < NJ; ++j) {
+            if (KK == 0 && j >= k) break;
+            v[j] = *reinterpret_cast<const float4*>(yp + (size_t)inv[(size_t)t * k + j] * d + i);
+        }
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        if (j >= k) break;
-        const float wj = w[(size_t)t * k + j];
-        acc.x = fmaf(wj, v[j].x, acc.x);
-        acc.y = fmaf(wj, v[j].y, acc.y);
-        acc.z = fmaf(wj, v[j].z, acc.z);
-        acc.w = fmaf(wj, v[j].w, acc.w);
-    }
-    if (ys) {
-        const float4 q = *reinterpret_cast<const float4*>(ys + (size_t)t * d + i);
-        acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
-    }
-    if constexpr (ACT == DT_F32) {
-        if (res) {
-            const float4 r = *reinterpret_cast<const float4*>(
-                reinterpret_cast<const float*>(res) + (size_t)t * d + i);
-            acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
+        for (int j = 0; j < NJ; ++j) {
+            if (KK == 0 && j >= k) break;
+            const float wj = w[(size_t)t * k + j];
+            acc.x = fmaf(wj, v[j].x, acc.x);
+            acc.y = fmaf(wj, v[j].y, acc.y);
+            acc.z = fmaf(wj, v[j].z, acc.z);
+            acc.w = fmaf(wj, v[j].w, acc.w);
         }
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)t * d + i) = acc;
-    } else {
-        if (res) {
-            const uint2 r = *reinterpret_cast<const uint2*>(
-                reinterpret_cast<const uint16_t*>(res) + (size_t)t * d + i);
-            acc.x += bf16_lo(r.x); acc.y += bf16_hi(r.x); acc.z += bf16_lo(r.y); acc.w += bf16_hi(r.y);
+        if (ys) {
+            const float4 q = *reinterpret_cast<const float4*>(ys + (size_t)t * d + i);
+            acc.x += q.x; acc.y += q.y; acc.z += q.z; acc.w += q.w;
         }
-        uint2 o;
-        o.x = pack_bf16x2(acc.x, acc.y);
-        o.y = pack_bf16x2(acc.z, acc.w);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + (size_t)t * d + i) = o;
+        if constexpr (ACT == DT_F32) {
+            if (res) {
+                const float4 r = *reinterpret_cast<const float4*>(
+                    reinterpret_cast<const float*>(res) + (size_t)t * d + i);
+                acc.x += r.x; acc.y += r.y; acc.z += r.z; acc.w += r.w;
+            }
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + (size_t)t * d + i) = acc;
+        } else {
+            if (res) {
+                const uint2 r = *reinterpret_cast<const uint2*>(
+                    reinterpret_cast<const uint16_t*>(res) + (size_t)t * d + i);
+                acc.x += bf16_lo(r.x); acc.y += bf16_hi(r.x); acc.z += bf16_lo(r.y); acc.w += bf16_hi(r.y);
+            }
+            uint2 o;
+            o.x = pack_bf16x2(acc.x, acc.y);
+            o.y = pack_bf16x2(acc.z, acc.w);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + (size_t)t * d + i) = o;
+        }
     }
 }
 
@@ -72,11 +79,24 @@ hipError_t launch_combine(int act, const float* yp, const int32_t* inv, const fl
                           hipStream_t s) {
     if (T == 0) return hipSuccess;
     if (k > 16) return hipErrorInvalidValue;
-    const dim3 g(T, (d + 1023) / 1024);
-    if (act == DT_F32)
-        hipLaunchKernelGGL(combine_kernel<DT_F32>, g, dim3(256), 0, s, yp, inv, w, ys, res, y, d, k);
-    else
-        hipLaunchKernelGGL(combine_kernel<DT_BF16>, g, dim3(256), 0, s, yp, inv, w, ys, res, y, d, k);
+    const dim3 g((d + 1023) / 1024, T < 65535 ? T : 65535);
+#define MOE_COMBINE(A, KC) hipLaunchKernelGGL((combine_kernel<A, KC>), g, dim3(256), 0, s, yp, inv, w, ys, res, y, T, d, k)
+#define MOE_COMBINE_K(A)                              \
+    switch (k) {                                      \
+        case 1: MOE_COMBINE(A, 1); break;             \
+        case 2: MOE_COMBINE(A, 2); break;             \
+        case 4: MOE_COMBINE(A, 4); break;             \
+        case 6: MOE_COMBINE(A, 6); break;             \
+        case 8: MOE_COMBINE(A, 8); break;             \
+        default: MOE_COMBINE(A, 0); break;            \
+    }
+    if (act == DT_F32) {
+        MOE_COMBINE_K(DT_F32)
+    } else {
+        MOE_COMBINE_K(DT_BF16)
+    }
+#undef MOE_COMBINE_K
+#undef MOE_COMBINE
     return hipGetLastError();
 }
 

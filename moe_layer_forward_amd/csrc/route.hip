@@ -6,12 +6,12 @@
 // shuffle reduction, maximum first then the runner-up.  [P3] (wzjinhao.cn)
 // §3.2: softmax(x W + b) with the maximum subtracted first.
 //
-// gfx950 design: the logits are a skinny [T,d]x[d,E] contraction that is at
-// most ~1% of the layer, so it runs on the VALU: a 256-thread block owns
-// 8 tokens (1 for small batches) x 4 experts, its threads split K in
-// 4-element chunks with four chunks of loads in flight, and the per-lane
-// partial sums are folded with a transposing wave reduction before a
-// cross-wave sum in LDS.  Top-k then runs
+// gfx950 design: the logits are a skinny [T,d]x[d,E] contraction.  Small
+// batches (T*E < 4096) and fp32 activations run on the VALU: a 256-thread
+// block owns 1 (or 8) tokens x 4 experts, its threads split K in 4-element
+// chunks with the loads of several chunks in flight, and the per-lane partial
+// sums are folded with a transposing wave reduction before a cross-wave sum in
+// LDS.  Larger bf16 batches run on the matrix cores (router_mfma_kernel).  Top-k then runs
 // one wave64 per token: each lane holds up to 4 logits, and k rounds of a
 // shuffle argmax (value descending, expert index ascending on ties) pick the
 // experts.  Selection is made on the fp32 logits (softmax is monotone); the
@@ -144,6 +144,104 @@ __global__ __launch_bounds__(RT_THREADS) void router_logits_kernel(
     }
 }
 
+// Router logits on the matrix cores for bf16 activations and larger batches.
+// The fp32 router row w is split exactly into three bf16 terms by truncation:
+// hi = w with the low 16 bits cleared, mid = (w - hi) likewise, lo = w - hi -
+// mid (at most 8 significant bits left, so exact in bf16); each product with a
+// bf16 activation is exact in fp32, and v_mfma_f32_16x16x32_bf16 accumulates
+// x.hi + x.mid + x.lo in fp32 -- the fp32 contraction, summed in another
+// order.  A block owns 16 tokens x 16 experts; its RQ_WAVES waves split K
+// into contiguous ranges, and the partial tiles are summed in LDS in wave
+// order (deterministic).  A lane loads 8 consecutive K of one token row (A)
+// and 8 of one router row (B), as the MFMA operand layouts want.
+constexpr int RQ_WAVES = 8;
+constexpr int RQ_U = 4;     // K steps of loads in flight
+
+typedef __bf16 rq_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float rq_f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int rq_u4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split3(const float4& a, const float4& b, rq_u4& hi, rq_u4& mid, rq_u4& lo) {
+    const float w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[8], m[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t u = __float_as_uint(w[i]);
+        const uint32_t uh = u & 0xffff0000u;
+        const float r1 = w[i] - __uint_as_float(uh);
+        const uint32_t um = __float_as_uint(r1) & 0xffff0000u;
+        const float r2 = r1 - __uint_as_float(um);
+        h[i] = uh >> 16;
+        m[i] = um >> 16;
+        l[i] = __float_as_uint(r2) >> 16;      // exact: r2 has <= 8 significant bits
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = h[2 * i] | (h[2 * i + 1] << 16);
+        mid[i] = m[2 * i] | (m[2 * i + 1] << 16);
+        lo[i] = l[2 * i] | (l[2 * i + 1] << 16);
+    }
+}
+
+__global__ __launch_bounds__(64 * RQ_WAVES) void router_mfma_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
+    float* __restrict__ logits, int T, int d, int E) {
+    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, q = lane >> 4;
+    const int tr = min(t0 + r, T - 1), er = min(e0 + r, E - 1);   // clamped rows: results unused
+    const uint16_t* xrow = x + (size_t)tr * d;
+    const float* wrow = wg + (size_t)er * d;
+    // this wave's K range, in steps of 32 (the last step may be partial: d % 8 == 0)
+    const int nsteps = (d + 31) / 32;
+    const int s0 = nsteps * wave / RQ_WAVES, s1 = nsteps * (wave + 1) / RQ_WAVES;
+    rq_f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int st = s0; st < s1; st += RQ_U) {
+        uint4 xa[RQ_U];
+        float4 wa[RQ_U][2];
+#pragma unroll
+        for (int u = 0; u < RQ_U; ++u) {
+            const int k = (st + u) * 32 + q * 8;
+            const int kc = (st + u < s1 && k < d) ? k : 0;
+            xa[u] = *reinterpret_cast<const uint4*>(xrow + kc);
+            wa[u][0] = *reinterpret_cast<const float4*>(wrow + kc);
+            wa[u][1] = *reinterpret_cast<const float4*>(wrow + kc + 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < RQ_U; ++u) {
+            const int k = (st + u) * 32 + q * 8;
+            const bool ok = st + u < s1 && k < d;
+            rq_u4 av = {ok ? xa[u].x : 0u, ok ? xa[u].y : 0u, ok ? xa[u].z : 0u, ok ? xa[u].w : 0u};
+            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+            rq_u4 hi, mid, lo;
+            split3(ok ? wa[u][0] : z, ok ? wa[u][1] : z, hi, mid, lo);
+            const rq_bf16x8 A = __builtin_bit_cast(rq_bf16x8, av);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(rq_bf16x8, hi), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(rq_bf16x8, mid), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(rq_bf16x8, lo), acc, 0, 0, 0);
+        }
+    }
+    // lane l holds tokens 4(l/16)+v, expert l%16; sum the waves' tiles in order
+    __shared__ float part[RQ_WAVES][4][64];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) part[wave][v][lane] = acc[v];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float sum = part[0][v][lane];
+#pragma unroll
+            for (int w = 1; w < RQ_WAVES; ++w) sum += part[w][v][lane];
+            const int t = t0 + 4 * q + v, e = e0 + r;
+            if (t < T && e < E) {
+                if (bias) sum += bias[e];
+                logits[(size_t)t * E + e] = sum;
+            }
+        }
+    }
+}
+
 // (value, index) is better than (v2, i2): larger value, or equal value and
 // lower expert index.  NaN was mapped to -inf before, so every unchosen expert
 // stays comparable and exactly k distinct experts are always selected.
@@ -211,9 +309,12 @@ hipError_t launch_route(int act, const void* x, const float* wg, const float* b,
     if (act == DT_F32) {
         if (small) hipLaunchKernelGGL((router_logits_kernel<DT_F32, 1>), g1, dim3(RT_THREADS), 0, s, x, wg, b, logits, T, d, E);
         else hipLaunchKernelGGL((router_logits_kernel<DT_F32, 8>), g1, dim3(RT_THREADS), 0, s, x, wg, b, logits, T, d, E);
+    } else if (small) {
+        hipLaunchKernelGGL((router_logits_kernel<DT_BF16, 1>), g1, dim3(RT_THREADS), 0, s, x, wg, b, logits, T, d, E);
     } else {
-        if (small) hipLaunchKernelGGL((router_logits_kernel<DT_BF16, 1>), g1, dim3(RT_THREADS), 0, s, x, wg, b, logits, T, d, E);
-        else hipLaunchKernelGGL((router_logits_kernel<DT_BF16, 8>), g1, dim3(RT_THREADS), 0, s, x, wg, b, logits, T, d, E);
+        const dim3 g2((T + 15) / 16, (E + 15) / 16);
+        hipLaunchKernelGGL(router_mfma_kernel, g2, dim3(64 * RQ_WAVES), 0, s,
+                           reinterpret_cast<const uint16_t*>(x), wg, b, logits, T, d, E);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
