@@ -12,6 +12,8 @@
 
 #include "common.h"
 #include "kernels.h"
+
+#include <algorithm>
 #include "moe.h"
 
 using namespace moe;
@@ -101,8 +103,21 @@ int check_shape(const moe_shape* s, char* err, size_t err_len) {
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t logits, idx, w, counts, offsets, perm, inv, tiles, h, yp, hs, ys, total;
+    size_t logits, idx, w, counts, offsets, perm, inv, tiles, h, yp, hs, ys, part, total;
+    int part_cap;
 };
+
+int effective_tau(const moe_shape* s);
+
+// Partial tiles the split tail round of the 256-row MFMA kernel may use: at
+// most one per block of its grid, which never exceeds max_mt x N-tiles.
+int part_cap(const moe_shape* s) {
+    const int tau = effective_tau(s);
+    if (tau < 0 || s->T <= tau) return 0;
+    const long nn = std::max(mfma_ntiles_n(0, s->F), mfma_ntiles_n(1, s->d));
+    const long c = (long)mfma_max_tiles(s->T, s->k, s->E) * nn;
+    return (int)std::min<long>(c, mfma_part_cap());
+}
 
 Layout layout(const moe_shape* s) {
     const size_t T = s->T, k = s->k, E = s->E, d = s->d, F = s->F;
@@ -122,6 +137,8 @@ Layout layout(const moe_shape* s) {
     L.yp = o; o += up(tk * d * 4);
     L.hs = o; o += s->n_shared ? up(T * F * hb) : 0;
     L.ys = o; o += s->n_shared ? up(T * d * 4) : 0;
+    L.part_cap = part_cap(s);
+    L.part = o; o += up((size_t)L.part_cap * 256 * 256 * 4);
     L.total = o;
     return L;
 }
@@ -141,6 +158,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     const bool use_mfma = tau >= 0 && s->T > tau;
     void* h = ws + L.h;
     int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+    float* part = L.part_cap ? reinterpret_cast<float*>(ws + L.part) : nullptr;
     const int max_mt = mfma_max_tiles(s->T, s->k, s->E);
     const int max_rows_gemv = use_mfma ? tau : s->T;   // a group holds at most T rows
     int rc;
@@ -187,7 +205,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     rc = pass(0, "gate/up");
     if (rc) return rc;
     if (use_mfma) {
-        rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, s->E, s->T, st),
+        rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, s->E, s->T, part, L.part_cap, st),
                        st, "mfma gate/up", err, err_len);
         if (rc) return rc;
     }
@@ -201,7 +219,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     rc = pass(1, "down");
     if (rc) return rc;
     if (use_mfma) {
-        rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, s->E, s->T * s->k, st),
+        rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, s->E, s->T * s->k, part, L.part_cap, st),
                        st, "mfma down", err, err_len);
         if (rc) return rc;
     }

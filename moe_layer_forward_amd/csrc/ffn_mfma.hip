@@ -58,6 +58,7 @@ int mfma_max_small(int E) { return 2 * E; }
 int mfma_plan_ints(int T, int k, int E) {
     return 3 * mfma_max_tiles(T, k, E) + 1 + 3 * mfma_max_small(E) + 1;
 }
+int mfma_part_cap() { return 256; }
 int mfma_ntiles_n(int mode, int N) { return mode == 0 ? (N + 127) / 128 : (N + MF_BN - 1) / MF_BN; }
 
 // One 256-thread block: per expert with more than tau rows, its big and small
@@ -124,7 +125,32 @@ struct MfmaArgs {
     const int32_t* perm;
     const int32_t* tiles;    // plan: expert[max_mt], row0[max_mt], rows[max_mt], n_mt
     int N, K, topk, max_mt, max_st, in_rows;
+    float* part;             // partial tiles of the split tail round, [part_cap][256][256] fp32
+    int part_cap;
 };
+
+// The last, partial round of 256-row tiles: W tiles on G blocks leave
+// r = W mod G tiles for the final round.  When r <= G/2 each of them is cut
+// into S K-ranges (S = G / r, at most the K steps and the partial-buffer
+// capacity), so the final round fills the machine; the parts write fp32
+// partial tiles, and mfma_tail_reduce sums the S parts of a tile in order.
+struct TailSplit {
+    int nfull;    // tasks done as whole tiles (R * G)
+    int rtail;    // tiles of the last round
+    int S;        // parts per tail tile (1: no split)
+};
+__device__ __forceinline__ TailSplit tail_split(int W, int G, int nk, int cap) {
+    TailSplit t;
+    const int R = W / G;
+    t.rtail = W - R * G;
+    t.S = t.rtail > 0 ? G / t.rtail : 1;
+    if (t.S > nk) t.S = nk;
+    if (t.rtail > 0 && t.rtail * t.S > cap) t.S = cap / t.rtail;
+    if (t.S < 2) { t.S = 1; t.nfull = W; t.rtail = 0; }
+    else t.nfull = R * G;
+    return t;
+}
+
 
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
 
@@ -207,7 +233,20 @@ __global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
     const int32x4_t RA = make_desc(a.in, (uint32_t)a.in_rows * row_bytes);
     const uint32_t wmat = (uint32_t)N * row_bytes;
 
-    for (int L = slot; L < total; L += nblk) {
+    const TailSplit ts = tail_split(total, nblk, nk, a.part_cap);
+    const int ntasks = ts.nfull + ts.rtail * ts.S;
+
+    for (int task = slot; task < ntasks; task += nblk) {
+        // whole tile, or part s of tail tile j (K steps [kb, ke))
+        int L = task, kb = 0, ke = nk, pi = -1;
+        if (task >= ts.nfull) {
+            const int q = task - ts.nfull, j = q % ts.rtail, sp = q / ts.rtail;
+            L = ts.nfull + j;
+            kb = (int)((long)nk * sp / ts.S);
+            ke = (int)((long)nk * (sp + 1) / ts.S);
+            pi = j * ts.S + sp;
+        }
+        const int kend = min(K, ke * MF_BK);     // element bound of this task's K range
         // grouped order: GM M-tiles x all N-tiles, M fastest
         const int grp = L / (MF_GM * nN);
         const int gm0 = grp * MF_GM;
@@ -268,16 +307,16 @@ __global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
         };
         auto issue_one = [&](int kt, int i) {          // DMA i (0..7) of K step kt
             const int st = kt % MF_NS;
-            const uint32_t kb = (uint32_t)kt * (MF_BK * 2);
+            const uint32_t kbyte = (uint32_t)kt * (MF_BK * 2);
             const int k0 = kt * MF_BK;
             const int ii = i >> 1;
             const int r0 = wave * 64 + ii * 16;
             if ((i & 1) == 0) {
-                const bool kok = k0 + kcol[ii] < K;
-                dma16(RA, (kok && aoff[ii] != MF_OOB) ? aoff[ii] + kb : MF_OOB, lds_addr(&sA[st][r0 * MF_BK]));
+                const bool kok = k0 + kcol[ii] < kend;
+                dma16(RA, (kok && aoff[ii] != MF_OOB) ? aoff[ii] + kbyte : MF_OOB, lds_addr(&sA[st][r0 * MF_BK]));
             } else {
-                const bool kok = k0 + kcol[ii] < K;
-                dma16(RB, (kok && boff[ii] != MF_OOB) ? boff[ii] + kb : MF_OOB, lds_addr(&sB[st][r0 * MF_BK]));
+                const bool kok = k0 + kcol[ii] < kend;
+                dma16(RB, (kok && boff[ii] != MF_OOB) ? boff[ii] + kbyte : MF_OOB, lds_addr(&sB[st][r0 * MF_BK]));
             }
         };
 
@@ -291,11 +330,11 @@ __global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
 #pragma unroll
         for (int kt = 0; kt < MF_NS; ++kt)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) issue_one(kt, i);
-        wait_vm(8 * (MF_NS - 1));    // stage 0 landed; stages 1..NS-1 may still fly
+            for (int i = 0; i < 8; ++i) issue_one(kb + kt, i);
+        wait_vm(8 * (MF_NS - 1));    // stage kb landed; the next NS-1 may still fly
         block_barrier();
 #pragma unroll
-        for (int q = 0; q < 16; ++q) read_frag(0, 0, q);
+        for (int q = 0; q < 16; ++q) read_frag(kb % MF_NS, 0, q);
 
         // Software pipeline, per K step kt (fragments of stage kt already in
         // register slot kt&1):
@@ -326,10 +365,29 @@ __global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        const int nk2 = (nk + 1) & ~1;
-        for (int kt = 0; kt < nk2; kt += 2) {
+        const int nk2 = (ke - kb + 1) & ~1;
+        for (int kt = kb; kt < kb + nk2; kt += 2) {
             step(kt, std::integral_constant<int, 0>{});
             step(kt + 1, std::integral_constant<int, 1>{});
+        }
+
+        if (pi >= 0) {
+            // a part of a split tail tile: raw fp32 accumulators, tile-local
+            // [row][col] with col = the B-tile row the accumulator belongs to
+            float* pt = a.part + (size_t)pi * (MF_BM * MF_BN);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+#pragma unroll
+                    for (int ni = 0; ni < 4; ++ni) {
+                        const int col = (MODE == 0) ? (ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 + (lane & 31)
+                                                    : wn * 128 + ni * 32 + (lane & 31);
+                        pt[row * MF_BN + col] = acc[mi][ni][v];
+                    }
+                }
+            continue;
         }
 
         // ---- epilogue; accumulator element v of lane l: column l%32, row 8*(v/4) + 4*(l/32) + v%4
@@ -357,6 +415,56 @@ __global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
                     }
                 }
             }
+        }
+    }
+}
+
+// Sum of the S partial tiles of each split tail tile, in part order, then the
+// usual epilogue: y_perm rows (mode 1) or silu(g) * u into h (mode 0).  Block
+// (c, j): tail tile j, 1024 outputs (a thread takes 4 consecutive columns of
+// one row, reading the S parts with 16-byte loads).
+template <int MODE>
+__global__ __launch_bounds__(256) void mfma_tail_reduce(MfmaArgs a, int G) {
+    const int N = a.N;
+    const int n_mt = a.tiles[3 * a.max_mt];
+    const int nN = (MODE == 0) ? (N + 127) / 128 : (N + MF_BN - 1) / MF_BN;
+    const int nk = (a.K + MF_BK - 1) / MF_BK;
+    const TailSplit ts = tail_split(n_mt * nN, G, nk, a.part_cap);
+    const int j = blockIdx.y;
+    if (j >= ts.rtail) return;
+    constexpr int NC = MODE == 0 ? 128 : MF_BN;      // output columns of a tile
+    const int idx = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int row = idx / NC, c = idx - row * NC;
+    const int L = ts.nfull + j;
+    const int grp = L / (MF_GM * nN);
+    const int gm0 = grp * MF_GM;
+    const int gsz = min(MF_GM, n_mt - gm0);
+    const int rem = L - grp * MF_GM * nN;
+    const int mt = gm0 + rem % gsz;
+    const int nt = rem / gsz;
+    const int p0 = a.tiles[a.max_mt + mt];
+    const int rows = a.tiles[2 * a.max_mt + mt];
+    if (row >= rows) return;
+    const float* pt = a.part + (size_t)j * ts.S * (MF_BM * MF_BN) + row * MF_BN + c;
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f), u = g;
+    for (int sp = 0; sp < ts.S; ++sp) {
+        const float4 v = *reinterpret_cast<const float4*>(pt + (size_t)sp * (MF_BM * MF_BN));
+        g.x += v.x; g.y += v.y; g.z += v.z; g.w += v.w;
+        if (MODE == 0) {
+            const float4 w = *reinterpret_cast<const float4*>(pt + (size_t)sp * (MF_BM * MF_BN) + 128);
+            u.x += w.x; u.y += w.y; u.z += w.z; u.w += w.w;
+        }
+    }
+    const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
+    const size_t orow = (size_t)(p0 + row) * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (MODE == 0) {
+            const int f = nt * 128 + c + i;
+            if (f < N) reinterpret_cast<uint16_t*>(a.out)[orow + f] = f32_to_bf16(silu(gv[i]) * uv[i]);
+        } else {
+            const int n = nt * MF_BN + c + i;
+            if (n < N) reinterpret_cast<float*>(a.out)[orow + n] = gv[i];
         }
     }
 }
@@ -529,7 +637,7 @@ hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int E
 
 hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void* in, void* out,
                            const int32_t* perm, const int32_t* tiles, int N, int K, int topk,
-                           int max_mt, int E, int in_rows, hipStream_t s) {
+                           int max_mt, int E, int in_rows, float* part, int part_cap, hipStream_t s) {
     MfmaArgs a;
     a.w0 = reinterpret_cast<const uint16_t*>(w0);
     a.w1 = reinterpret_cast<const uint16_t*>(w1);
@@ -543,6 +651,8 @@ hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void*
     a.max_mt = max_mt;
     a.max_st = mfma_max_small(E);
     a.in_rows = in_rows;
+    a.part = part;
+    a.part_cap = part ? part_cap : 0;
     static int n_cu = 0;
     if (n_cu == 0) {
         int dev = 0;
@@ -560,6 +670,15 @@ hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void*
         hipLaunchKernelGGL(mfma_ffn_kernel<1>, dim3(grid), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.part_cap > 0) {
+        // sums of the split tail tiles (blocks without such a tile exit at once)
+        if (mode == 0)
+            hipLaunchKernelGGL(mfma_tail_reduce<0>, dim3(MF_BM * 128 / 1024, grid), dim3(256), 0, s, a, grid);
+        else
+            hipLaunchKernelGGL(mfma_tail_reduce<1>, dim3(MF_BM * MF_BN / 1024, grid), dim3(256), 0, s, a, grid);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     // small tiles: two blocks per CU
     const int sslots = a.max_st * nN;
     const int sgrid = sslots < 2 * n_cu ? sslots : 2 * n_cu;

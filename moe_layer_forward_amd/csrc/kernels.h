@@ -43,7 +43,9 @@ hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int E
                             int32_t* tiles, int max_mt, hipStream_t s);
 hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void* in, void* out,
                            const int32_t* perm, const int32_t* tiles, int N, int K, int topk,
-                           int max_mt, int E, int in_rows, hipStream_t s);
+                           int max_mt, int E, int in_rows, float* part, int part_cap, hipStream_t s);
+// partial tiles (256 x 256 fp32 each) the split tail round may use
+int mfma_part_cap();
 hipError_t launch_combine(int act, const float* yp, const int32_t* inv, const float* w,
                           const float* ys, const void* res, void* y, int T, int d, int k,
                           hipStream_t s);
