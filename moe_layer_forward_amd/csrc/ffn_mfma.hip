@@ -14,9 +14,13 @@
 //    fastest, so concurrent blocks of an XCD share A and B panels in its L2;
 //  * block tile 256 x 256; 4 wave64s in a 2x2 arrangement each own
 //    128 x 128 = 4 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (fp32);
-//  * LDS holds four stages of A and B of K = 32 each (128 KiB): tiles are
-//    copied global -> LDS by buffer_load ... lds (no VGPR staging) three K
-//    steps ahead of the MFMAs, with one barrier per K step;
+//  * LDS holds five stages of A and B of K = 32 each (160 KiB): tiles are
+//    copied global -> LDS by buffer_load ... lds (no VGPR staging) two to
+//    three K steps ahead of the MFMAs, with one barrier per K step; the copies
+//    of two consecutive stages (the two 64-byte halves of each 128-byte row
+//    segment) are issued within one step so they meet in the cache.  The
+//    lookahead matters more than the pairing: issuing the two halves back to
+//    back at the cost of one step of lookahead measured ~20% slower;
 //  * the 16-byte chunks of each 64-byte LDS row are XOR-swizzled by
 //    (row/4)&3, so 16-byte fragment reads of 16 consecutive rows are
 //    conflict-free; each DMA lane simply fetches the chunk that belongs at its
@@ -42,7 +46,7 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int MF_BM = 256;
 constexpr int MF_BN = 256;
 constexpr int MF_BK = 32;         // K per LDS stage
-constexpr int MF_NS = 4;          // LDS stages (3 K steps of prefetch in flight)
+constexpr int MF_NS = 5;          // LDS stages (2-3 K steps of prefetch in flight)
 constexpr int MF_GM = 8;          // M-tiles per scheduling group
 constexpr uint32_t MF_OOB = 0x80000000u;   // beyond any buffer: the range check yields 0
 
@@ -328,21 +332,27 @@ __global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
         // Copies of K steps >= nk read out of range and store zeros, so every
         // step below issues exactly 8 copies and the wait counts are constant.
 #pragma unroll
-        for (int kt = 0; kt < MF_NS; ++kt)
+        for (int kt = 0; kt < 3; ++kt)
 #pragma unroll
             for (int i = 0; i < 8; ++i) issue_one(kb + kt, i);
-        wait_vm(8 * (MF_NS - 1));    // stage kb landed; the next NS-1 may still fly
+        wait_vm(16);                 // stage kb landed; kb+1, kb+2 may still fly
         block_barrier();
 #pragma unroll
         for (int q = 0; q < 16; ++q) read_frag(kb % MF_NS, 0, q);
 
         // Software pipeline, per K step kt (fragments of stage kt already in
-        // register slot kt&1):
+        // register slot kt&1), with steps taken in pairs from kb:
         //   8 MFMAs | wait: stage kt+1 landed (this wave), own reads done |
-        //   barrier | 24 MFMAs interleaved with the 8 copies of stage kt+4 into
-        //   the buffer stage kt vacated (one per three MFMAs) and the 16 reads
-        //   of stage kt+1.
-        // nk is rounded up to even: an extra step multiplies zero fragments.
+        //   barrier | 24 MFMAs interleaved with the 16 reads of stage kt+1 and,
+        //   on the first step of a pair, the 16 copies of stages kt+3 and kt+4
+        //   (two per third MFMA, all of kt+3 first).  Stages kt+3 and kt+4 hold
+        //   the two 64-byte halves of the same 128-byte row segments, so their
+        //   copies meet in the cache; the buffers they refill held stages kt-2
+        //   and kt-1, which every wave has finished reading.
+        //   Outstanding copies at the wait: kt+1, kt+2 on the first step of a
+        //   pair (vmcnt 8), kt+2, kt+3, kt+4 on the second (vmcnt 16).
+        // The number of steps is rounded up to even: an extra step multiplies
+        // zero fragments.
         auto step = [&](int kt, auto slc) {
             constexpr int sl = decltype(slc)::value;
 #pragma unroll
@@ -350,18 +360,24 @@ __global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
                 mma(sl, m);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            wait_vm(8 * (MF_NS - 2));                      // stage kt+1 landed
+            wait_vm(sl == 0 ? 8 : 16);                     // stage kt+1 landed
             __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): own reads of stage kt done
             block_barrier();
-            // one copy every third MFMA, the 16 reads in the other slots: copies
-            // in a burst overflow the texture-address FIFO and stall the MFMAs
 #pragma unroll
             for (int m = 8; m < 32; ++m) {
                 mma(sl, m);
                 __builtin_amdgcn_sched_barrier(0);
                 const int j = m - 8;                       // 0..23
-                if (j % 3 == 0) issue_one(kt + MF_NS, j / 3);
-                else read_frag((kt + 1) % MF_NS, sl ^ 1, j - j / 3 - 1);
+                if (j % 3 == 0) {
+                    if constexpr (sl == 0) {
+                        const int c = j / 3;               // 0..7: copies 2c, 2c+1
+                        const int st = c < 4 ? kt + 3 : kt + 4;
+                        issue_one(st, (2 * c) & 7);
+                        issue_one(st, (2 * c + 1) & 7);
+                    }
+                } else {
+                    read_frag((kt + 1) % MF_NS, sl ^ 1, j - j / 3 - 1);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
