@@ -66,10 +66,11 @@ def device_layer(cfg, seed=0, layer=0, shared_weights=None):
 class Runner:
     """Buffers for one workload and the four C-ABI steps of the layer."""
 
-    def __init__(self, cfg, x, wr, br, W, tau=0):
+    def __init__(self, cfg, x, wr, br, W, tau=0, wt=None):
         self.cfg, self.x, self.wr, self.br, self.W = cfg, x, wr, br, W
         T, E, k, d = cfg.T, cfg.E, cfg.k, cfg.d
-        self.shape = moe.make_shape(T, d, E, k, cfg.F, cfg.act, cfg.wt, cfg.n_shared, tau)
+        self.wt = cfg.wt if wt is None else wt
+        self.shape = moe.make_shape(T, d, E, k, cfg.F, cfg.act, self.wt, cfg.n_shared, tau)
         self.wstruct = moe.make_weights(**W)
         self.ws = torch.empty(moe.moe_workspace_bytes(self.shape), dtype=torch.uint8, device=DEV)
         act = torch.float32 if cfg.act == "f32" else torch.bfloat16
@@ -142,8 +143,9 @@ class Runner:
         return U, w_bytes + act_bytes, flops
 
 
-def cpu_baseline(cfg, runner, target_s=10.0):
-    """The oracle timed on the host's cores on the full layer (all T tokens)."""
+def cpu_baseline(cfg, runner, Wd, target_s=10.0):
+    """The oracle timed on the host's cores on the full layer (all T tokens);
+    Wd: the device weights in the row-major layout the oracle reads."""
     import oracle
     oracle.build(force=False)
 
@@ -155,12 +157,12 @@ def cpu_baseline(cfg, runner, target_s=10.0):
             return t.view(torch.int16).numpy().view(np.uint16)
         return t.numpy()
 
-    W = {n: st(runner.W[n]) for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")}
+    W = {n: st(Wd[n]) for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")}
     S = None
     if cfg.n_shared:
-        S = {"w_gate": st(runner.W["sh_gate"]), "w_up": st(runner.W["sh_up"]),
-             "w_down": st(runner.W["sh_down"]), "s_gate": st(runner.W["sh_s_gate"]),
-             "s_up": st(runner.W["sh_s_up"]), "s_down": st(runner.W["sh_s_down"])}
+        S = {"w_gate": st(Wd["sh_gate"]), "w_up": st(Wd["sh_up"]),
+             "w_down": st(Wd["sh_down"]), "s_gate": st(Wd["sh_s_gate"]),
+             "s_up": st(Wd["sh_s_up"]), "s_down": st(Wd["sh_s_down"])}
     x, wr, br = st(runner.x), st(runner.wr), st(runner.br)
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -241,6 +243,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tau", type=int, default=0)
+    ap.add_argument("--int4-layout", choices=["tiled", "row-major"], default="tiled",
+                    help="int4 code layout the layer streams (tiled: packed once with "
+                         "moe_pack_int4_tiled before timing; needs d, F multiples of 1024)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -268,7 +273,16 @@ def main():
         cfg = cfg.replace(layers=1)
     log(f"generating {cfg.name} inputs on the GPU")
     x, wr, br, W = device_layer(cfg)
-    run = Runner(cfg, x, wr, br, W, tau=args.tau)
+    wt = cfg.wt
+    Wrun = W
+    if cfg.wt == "int4" and args.int4_layout == "tiled" and cfg.d % 1024 == 0 and cfg.F % 1024 == 0 \
+            and max(cfg.d, cfg.F) <= 8192:
+        # weight preparation, once and outside the timed region (weights are static)
+        log("packing int4 codes into the tiled layout")
+        Wrun = moe.layer.pack_int4_tiled(W)
+        torch.cuda.synchronize()
+        wt = "int4_tiled"
+    run = Runner(cfg, x, wr, br, Wrun, tau=args.tau, wt=wt)
     log(f"timing {cfg.name}: warmup {args.warmup}, steps {args.steps}")
     wall, ffn_mean, ffn_med, wall_layer = run.timed(args.steps, args.warmup)
     U, ffn_bytes, ffn_flops = run.ffn_algorithmic()
@@ -283,10 +297,12 @@ def main():
     else:
         ceil = read_ceiling_gbs()
         roof = dict(roofline_obj("hbm", achieved, HBM_PEAK_GBS, "GB/s",
-                                 measured_traffic(cfg.name) if args.tau == 0 else None),
+                                 # counters were taken on the default run (tiled int4 codes)
+                                 measured_traffic(cfg.name)
+                                 if args.tau == 0 and (cfg.wt != "int4" or wt == "int4_tiled") else None),
                     kernel=("expert FFN step (gate/up + down, 64-row MFMA tiles)"
                             if cfg.wt == "bf16" and args.tau >= 0 and cfg.T * cfg.k / max(U, 1) > 16
-                            else "expert FFN step (gate/up + down, int4 skinny MFMA)" if cfg.wt == "int4"
+                            else f"expert FFN step (gate/up + down, int4 skinny MFMA, {wt})" if cfg.wt == "int4"
                             else "expert FFN step (gate/up + down GEMV)"),
                     bytes_per_launch=ffn_bytes,
                     launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5),
@@ -300,7 +316,7 @@ def main():
                  ("bf16/int4" if cfg.wt == "int4" else "f32"),
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
-                   "F": cfg.F, "weights": cfg.wt, "shared_experts": cfg.n_shared,
+                   "F": cfg.F, "weights": wt, "shared_experts": cfg.n_shared,
                    "active_experts": U, "tau": args.tau, "seed": 0},
         "roofline": roof,
         "layer_call_ms_per_step": round(wall_layer * 1e3 / args.steps, 4),
@@ -330,7 +346,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on the host")
-        out["cpu_baseline"] = cpu_baseline(cfg, run)
+        out["cpu_baseline"] = cpu_baseline(cfg, run, W)
     print(json.dumps(out), flush=True)
 
 

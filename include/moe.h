@@ -11,6 +11,7 @@
  *   [P2] "Colibri不是一只蜂鸟，而是一套为前沿MoE模型量身定制的C语言推理引擎" (discosf.com/news/4731160)
  *   [P3] Colibri C engine walkthrough (wzjinhao.cn/news/17934)
  *   [P4] "Colibri：轻量级MoE推理引擎的C语言实践" (mhpn.cn/news/2221639)
+ *   [P5] "一只蜂鸟如何喂饱九头大象" (wth2jhl.online/blog/colibri-justvugg-deep-dive)
  *
  * Conventions (all entry points):
  *   - Every tensor pointer is a DEVICE pointer, row-major, 16-byte aligned
@@ -50,9 +51,14 @@ typedef enum {
 typedef enum {
     MOE_F32 = 0,            /* IEEE binary32 */
     MOE_BF16 = 1,           /* bfloat16 (upper half of binary32), RNE when produced */
-    MOE_INT4_G128 = 2       /* weights only: symmetric int4 codes (two's complement,
+    MOE_INT4_G128 = 2,      /* weights only: symmetric int4 codes (two's complement,
                                two per byte, even K index in the low nibble) with one
-                               fp16 scale per 128 consecutive K elements; w = q * s */
+                               fp16 scale per 128 consecutive K elements; w = q * s
+                               ([P5] §7.3: int4 experts, per-group scales) */
+    MOE_INT4_G128_TILED = 3 /* weights only: the same codes and scales, the code bytes
+                               of every [N][K/2] matrix in the tiled order that
+                               moe_pack_int4_tiled writes (scales stay [N][K/128]);
+                               needs d and F multiples of 1024, at most 8192 */
 } moe_dtype;
 
 /* Shape of one MoE layer call.
@@ -174,6 +180,23 @@ size_t moe_workspace_bytes(const moe_shape *shape);
  * the stacked workload's own definition.)  Uses shape->T and shape->d only. */
 int moe_rmsnorm(const moe_shape *shape, const void *h, const float *gamma, float eps,
                 void *out, void *stream, char *err, size_t err_len);
+
+/* Weight preparation, once per weight set: rewrite int4 code bytes from the
+ * row-major layout of MOE_INT4_G128 ([N][K/2] per matrix, [P5] §7.3) into the
+ * tiled layout of MOE_INT4_G128_TILED.  The tiled matrix cuts the rows into
+ * sets of 16; set s, 128-element group g (K = 128 g .. 128 g + 127) is 1 KB at
+ * byte ((s * K/128) + g) * 1024, made of 64 pieces of 16 bytes: piece
+ * 16 q + r (q = 0..3, r = 0..15) is bytes [64 g + 16 q, 64 g + 16 q + 16) of
+ * row 16 s + r (its K elements 128 g + 32 q .. + 31).  Nibble order inside a
+ * byte is unchanged; the matrix size (N * K/2 bytes) too.
+ *   src, dst: device, n_mats * N * K/2 bytes each, 16-byte aligned, not
+ *             overlapping (caller-owned; dst is written, src only read)
+ *   n_mats >= 0 matrices of N rows (N a positive multiple of 16) and K columns
+ *   (K a positive multiple of 128); e.g. w_gate: n_mats = E, N = F, K = d.
+ * MOE_EINVAL for a bad size, a NULL, misaligned or overlapping pointer.
+ * Asynchronous on stream. */
+int moe_pack_int4_tiled(const void *src, void *dst, int64_t n_mats, int32_t N, int32_t K,
+                        void *stream, char *err, size_t err_len);
 
 /* Measurement helper, not part of the layer: reads bytes of device memory at
  * buf once with plain streaming loads and XORs every 32-bit word of it into

@@ -79,13 +79,14 @@ int check_shape(const moe_shape* s, char* err, size_t err_len) {
         return fail(err, err_len, MOE_EINVAL, "n_shared=%d must be 0 or 1", s->n_shared);
     if (s->act != MOE_F32 && s->act != MOE_BF16)
         return fail(err, err_len, MOE_EINVAL, "act=%d is not MOE_F32 or MOE_BF16", s->act);
-    if (s->wt != MOE_F32 && s->wt != MOE_BF16 && s->wt != MOE_INT4_G128)
+    if (s->wt != MOE_F32 && s->wt != MOE_BF16 && s->wt != MOE_INT4_G128 && s->wt != MOE_INT4_G128_TILED)
         return fail(err, err_len, MOE_EINVAL, "wt=%d is not a moe_dtype", s->wt);
-    if (s->wt == MOE_INT4_G128 && (s->d % 128 || s->F % 128))
+    const bool int4 = s->wt == MOE_INT4_G128 || s->wt == MOE_INT4_G128_TILED;
+    if (int4 && (s->d % 128 || s->F % 128))
         return fail(err, err_len, MOE_EINVAL, "int4-g128 weights need d and F multiples of 128 (d=%d F=%d)",
                     s->d, s->F);
     const bool ok_combo = (s->act == MOE_F32 && s->wt == MOE_F32) ||
-                          (s->act == MOE_BF16 && (s->wt == MOE_BF16 || s->wt == MOE_INT4_G128));
+                          (s->act == MOE_BF16 && (s->wt == MOE_BF16 || int4));
     if (!ok_combo)
         return fail(err, err_len, MOE_EUNSUPPORTED, "activation dtype %d with weight dtype %d is not built",
                     s->act, s->wt);
@@ -93,7 +94,11 @@ int check_shape(const moe_shape* s, char* err, size_t err_len) {
     if (s->wt == MOE_BF16 && ((size_t)s->T * s->k * s->F * 2 >= ((size_t)1 << 31) ||
                               (size_t)s->T * s->d * 2 >= ((size_t)1 << 31)))
         return fail(err, err_len, MOE_EUNSUPPORTED, "T*k*F and T*d bf16 buffers must stay below 2 GiB");
-    const int kmax = gemv_max_k(s->wt);
+    // the tiled layout is read by the int4 MFMA kernel only
+    if (s->wt == MOE_INT4_G128_TILED && (!i4mfma_supported(s->d, s->F) || !i4mfma_supported(s->F, s->d)))
+        return fail(err, err_len, MOE_EUNSUPPORTED,
+                    "tiled int4 weights need d and F multiples of 1024 and at most 8192 (d=%d F=%d)", s->d, s->F);
+    const int kmax = gemv_max_k(int4 ? MOE_INT4_G128 : s->wt);
     if (s->d > kmax || s->F > kmax)
         return fail(err, err_len, MOE_EUNSUPPORTED, "d=%d / F=%d exceed this build's limit %d for this dtype",
                     s->d, s->F, kmax);
@@ -182,11 +187,12 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     q.topk = 1; q.T = s->T; q.E = 1; q.tau = -1;
     const GemvArgs* qp = s->n_shared ? &q : nullptr;
     const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
+    const bool tiled = s->wt == MOE_INT4_G128_TILED;
     // one pass (gate/up or down) of the routed and the shared expert: int4 on
     // the matrix cores in one launch, else one GEMV launch each
     auto pass = [&](int mode, const char* what) -> int {
-        if (s->wt == MOE_INT4_G128 && i4mfma_supported(g.K, g.N))
-            return hip_check(launch_i4mfma(mode, &g, qp, st), st, what, err, err_len);
+        if (tiled || (s->wt == MOE_INT4_G128 && i4mfma_supported(g.K, g.N)))
+            return hip_check(launch_i4mfma(mode, tiled, &g, qp, st), st, what, err, err_len);
         g.rows_per_item = gemv_rows_per_item(s->wt, mode, g.K, g.N, active);
         int r = hip_check(launch_gemv(s->wt, s->act, mode, g, s->E, max_rows_gemv, st), st, what, err, err_len);
         if (r || !qp) return r;
@@ -231,7 +237,8 @@ int check_weights(const moe_shape* s, const moe_weights* w, char* err, size_t er
     NEED_PTR(w->w_gate, "w_gate");
     NEED_PTR(w->w_up, "w_up");
     NEED_PTR(w->w_down, "w_down");
-    if (s->wt == MOE_INT4_G128) {
+    const bool int4 = s->wt == MOE_INT4_G128 || s->wt == MOE_INT4_G128_TILED;
+    if (int4) {
         NEED_PTR(w->s_gate, "s_gate");
         NEED_PTR(w->s_up, "s_up");
         NEED_PTR(w->s_down, "s_down");
@@ -240,7 +247,7 @@ int check_weights(const moe_shape* s, const moe_weights* w, char* err, size_t er
         NEED_PTR(w->sh_gate, "sh_gate");
         NEED_PTR(w->sh_up, "sh_up");
         NEED_PTR(w->sh_down, "sh_down");
-        if (s->wt == MOE_INT4_G128) {
+        if (int4) {
             NEED_PTR(w->sh_s_gate, "sh_s_gate");
             NEED_PTR(w->sh_s_up, "sh_s_up");
             NEED_PTR(w->sh_s_down, "sh_s_down");
@@ -417,6 +424,23 @@ int moe_rmsnorm(const moe_shape* shape, const void* h, const float* gamma, float
     hipStream_t st = (hipStream_t)stream;
     return hip_check(launch_rmsnorm(shape->act, h, gamma, eps, out, shape->T, shape->d, st), st, "rmsnorm", err,
                      err_len);
+}
+
+int moe_pack_int4_tiled(const void* src, void* dst, int64_t n_mats, int32_t N, int32_t K, void* stream, char* err,
+                        size_t err_len) {
+    if (n_mats < 0) return fail(err, err_len, MOE_EINVAL, "n_mats=%lld is negative", (long long)n_mats);
+    if (N < 16 || N % 16) return fail(err, err_len, MOE_EINVAL, "N=%d must be a positive multiple of 16", N);
+    if (K < 128 || K % 128) return fail(err, err_len, MOE_EINVAL, "K=%d must be a positive multiple of 128", K);
+    const size_t bytes = (size_t)n_mats * (size_t)N * (size_t)(K / 2);
+    if (n_mats > 0 && bytes / (size_t)n_mats / (size_t)N != (size_t)(K / 2))
+        return fail(err, err_len, MOE_EINVAL, "n_mats * N * K/2 overflows");
+    if (!bytes) return MOE_OK;
+    NEED_PTR(src, "src");
+    NEED_PTR(dst, "dst");
+    const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+    if (a < b + bytes && b < a + bytes) return fail(err, err_len, MOE_EINVAL, "src and dst overlap");
+    hipStream_t st = (hipStream_t)stream;
+    return hip_check(launch_pack_int4_tiled(src, dst, (size_t)n_mats, N, K, st), st, "pack int4", err, err_len);
 }
 
 int moe_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, void* stream, char* err, size_t err_len) {

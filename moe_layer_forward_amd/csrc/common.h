@@ -8,7 +8,7 @@
 
 namespace moe {
 
-enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_INT4 = 2 };
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_INT4 = 2, DT_INT4_TILED = 3 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -564,7 +564,7 @@ hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, i
         return mode == 0 ? launch_mode<DT_BF16, DT_BF16, 0>(a, v, max_items, s)
                          : launch_mode<DT_BF16, DT_BF16, 1>(a, v, max_items, s);
     if (wt == DT_INT4 && act == DT_BF16 && i4mfma_supported(a.K, a.N))
-        return a.counts ? launch_i4mfma(mode, &a, nullptr, s) : launch_i4mfma(mode, nullptr, &a, s);
+        return a.counts ? launch_i4mfma(mode, false, &a, nullptr, s) : launch_i4mfma(mode, false, nullptr, &a, s);
     if (wt == DT_INT4 && act == DT_BF16)
         return mode == 0 ? launch_mode<DT_INT4, DT_BF16, 0>(a, v, max_items, s)
                          : launch_mode<DT_INT4, DT_BF16, 1>(a, v, max_items, s);

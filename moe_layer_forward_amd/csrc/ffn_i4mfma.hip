@@ -32,9 +32,13 @@
 //    stream continues across item boundaries; the buffer range
 //    check returns zeros past the last row and past the block's range, so
 //    loads never branch;
-//  * the lane layout gives each load instruction 16 rows x 64 bytes, half of
-//    a 128-byte line per row; the loads of two consecutive groups (the two
-//    halves of every line) are issued back to back so they meet in the cache;
+//  * row-major weights give each load instruction 16 rows x 64 bytes, half
+//    of a 128-byte line per row; the loads of two consecutive groups (the two
+//    halves of every line) are issued back to back so they meet in the cache.
+//    The tiled layout (MOE_INT4_G128_TILED, written once by moe_pack_int4_tiled)
+//    stores exactly what one load instruction reads as 1 KB of consecutive
+//    bytes, and the groups of a 16-row set one after another; those loads go
+//    out non-temporal (whole lines, read once), which reads ~11% faster;
 //  * a shared expert, when present, is one more slot of the same launch (all
 //    T tokens, its own weights and buffers), so its passes overlap the routed
 //    experts' instead of running as a separate small launch;
@@ -64,8 +68,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
                                              0x00020000);
 }
+// buffer-load cache policy bit: nt (streamed, not kept in the caches)
+constexpr int kNonTemporal = 2;
+template <int AUX = 0>
 __device__ __forceinline__ u32x4_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
 }
 
 template <int I>
@@ -122,7 +129,7 @@ struct I4Args {
     int N, K, topk, T, E, tau, P;
 };
 
-template <int MODE, int RING>
+template <int MODE, int RING, bool TILED>
 __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     constexpr int G = MODE == 0 ? 2 : 1;
     static_assert(RING == 8, "the scale prefetch runs 8 steps ahead, as far as the ring");
@@ -235,7 +242,11 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     const uint32_t mat_bytes = rb * (uint32_t)N;
     const uint32_t lrow = (uint32_t)(wave * 16 + (lane & 15));
     const uint32_t lq = (uint32_t)(lane >> 4);
-    const uint32_t woff_l = lrow * rb + lq * 16u;            // lane part of a weight offset
+    // lane part of a weight offset, and the offset step from one group to the
+    // next: row-major (row lrow, bytes 64 g + 16 lq) or tiled (16-row set
+    // `wave` of the item, 1 KB per group, lane-ordered 16-byte pieces)
+    const uint32_t woff_l = TILED ? (uint32_t)wave * 16u * rb + (uint32_t)lane * 16u : lrow * rb + lq * 16u;
+    constexpr uint32_t kGroupStep = TILED ? 1024u : 64u;
     const uint32_t soff_l = lrow * srow;                      // lane part of a scale offset
     const uint32_t lrow16 = (uint32_t)(lane & 15);
 
@@ -251,12 +262,12 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
         Cursor q1 = q;
         advance(q1, 1);
         const uint32_t n0 = q.idx < nsteps ? mat_bytes : 0u, n1 = q1.idx < nsteps ? mat_bytes : 0u;
-        const uint32_t o0 = woff_l + (uint32_t)q.chunk * kItemRows * rb + (uint32_t)q.g * 64u;
-        const uint32_t o1 = woff_l + (uint32_t)q1.chunk * kItemRows * rb + (uint32_t)q1.g * 64u;
+        const uint32_t o0 = woff_l + (uint32_t)q.chunk * kItemRows * rb + (uint32_t)q.g * kGroupStep;
+        const uint32_t o1 = woff_l + (uint32_t)q1.chunk * kItemRows * rb + (uint32_t)q1.g * kGroupStep;
 #pragma unroll
         for (int m = 0; m < G; ++m) {
-            wq[S][m] = ld16(rsrc(weight_ptr(q, m), n0), o0);
-            wq[S + 1][m] = ld16(rsrc(weight_ptr(q1, m), n1), o1);
+            wq[S][m] = ld16<TILED ? kNonTemporal : 0>(rsrc(weight_ptr(q, m), n0), o0);
+            wq[S + 1][m] = ld16<TILED ? kNonTemporal : 0>(rsrc(weight_ptr(q1, m), n1), o1);
         }
         q = q1;
         advance(q, 1);
@@ -463,7 +474,7 @@ bool i4mfma_supported(int K, int N) {
     return (size_t)(N + kItemRows) * (size_t)(K / 2) < ((size_t)1 << 31);
 }
 
-hipError_t launch_i4mfma(int mode, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s) {
+hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s) {
     const GemvArgs& g = routed ? *routed : *shared;
     I4Args a{};
     if (routed) {
@@ -498,7 +509,7 @@ hipError_t launch_i4mfma(int mode, const GemvArgs* routed, const GemvArgs* share
     const size_t lds = (size_t)(a.P + 1) * ((size_t)g.K * 2 + 16) + (size_t)(g.K / 128) * 16 * 4;
 
     static int n_cu = 0;
-    static bool attr_set[2] = {false, false};
+    static bool attr_set[4] = {false, false, false, false};
     if (n_cu == 0) {
         int dev = 0;
         (void)hipGetDevice(&dev);
@@ -506,15 +517,49 @@ hipError_t launch_i4mfma(int mode, const GemvArgs* routed, const GemvArgs* share
         if (n_cu < 1) n_cu = 256;
     }
     // 8 scale groups per wave in flight: 16 KB (gate/up) or 8 KB (down)
-    auto k = mode == 0 ? i4_mfma_kernel<0, 8> : i4_mfma_kernel<1, 8>;
-    if (!attr_set[mode]) {
+    auto k = mode == 0 ? (tiled ? i4_mfma_kernel<0, 8, true> : i4_mfma_kernel<0, 8, false>)
+                       : (tiled ? i4_mfma_kernel<1, 8, true> : i4_mfma_kernel<1, 8, false>);
+    const int ki = mode * 2 + (tiled ? 1 : 0);
+    if (!attr_set[ki]) {
         // dynamic LDS beyond 64 KB: the budget left next to the static arrays
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                   hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)(kLdsBytes - kStaticLds));
-        attr_set[mode] = true;
+        attr_set[ki] = true;
     }
     hipLaunchKernelGGL(k, dim3(n_cu), dim3(kThreads), lds, s, a);
+    return hipGetLastError();
+}
+
+// Row-major int4 codes -> the tiled layout the kernel above streams: within
+// each matrix, 16-byte piece (set, g, q, r) of the output (set-major, then
+// group g, then lane q*16 + r) is bytes [64 g + 16 q, +16) of row 16 set + r.
+// A permutation of 16-byte pieces: one thread per output piece, coalesced
+// stores.
+__global__ __launch_bounds__(256) void pack_int4_tiled_kernel(const u32x4_t* __restrict__ src,
+                                                              u32x4_t* __restrict__ dst, size_t n_pieces,
+                                                              int N, int K) {
+    const size_t per_row = (size_t)K / 32;             // 16-byte pieces per row
+    const size_t per_mat = (size_t)N * per_row;
+    const int NG = K / 128;
+    for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_pieces;
+         j += (size_t)gridDim.x * blockDim.x) {
+        const size_t mat = j / per_mat, rem = j - mat * per_mat;
+        const int lane = (int)(rem & 63);
+        const size_t t = rem >> 6;
+        const size_t set = t / NG;
+        const int g = (int)(t - set * NG);
+        const size_t row = set * 16 + (lane & 15);
+        dst[j] = src[mat * per_mat + row * per_row + (size_t)g * 4 + (lane >> 4)];
+    }
+}
+
+hipError_t launch_pack_int4_tiled(const void* src, void* dst, size_t n_mats, int N, int K, hipStream_t s) {
+    const size_t n = n_mats * (size_t)N * (size_t)(K / 32);
+    if (n == 0) return hipSuccess;
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(pack_int4_tiled_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s,
+                       reinterpret_cast<const u32x4_t*>(src), reinterpret_cast<u32x4_t*>(dst), n, N, K);
     return hipGetLastError();
 }
 

@@ -31,8 +31,10 @@ int gemv_max_k(int wt);
 // int4-g128 weights on the matrix cores (ffn_i4mfma.hip): K a multiple of 1024.
 // One launch serves the routed experts (counts/offsets set) and, when
 // `shared` is given, the shared expert over all T tokens; either may be null.
+// `tiled`: the weight codes are in the layout launch_pack_int4_tiled writes.
 bool i4mfma_supported(int K, int N);
-hipError_t launch_i4mfma(int mode, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s);
+hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s);
+hipError_t launch_pack_int4_tiled(const void* src, void* dst, size_t n_mats, int N, int K, hipStream_t s);
 int gemv_rows_per_item(int wt, int mode, int K, int N, int active);
 int mfma_bm();
 int mfma_max_tiles(int T, int k, int E);

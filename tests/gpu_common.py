@@ -12,7 +12,7 @@ import moe_layer_forward_amd as moe
 from helpers import np_store
 
 DEV = "cuda"
-TOL = {"f32": 1e-5, "bf16": 2e-2, "int4": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "int4": 2e-2, "int4_tiled": 2e-2}
 FLIP_MARGIN = 1e-5
 
 
@@ -54,20 +54,29 @@ def oracle_weights(d):
     return W, S
 
 
-def shape_of(cfg, tau=0, T=None):
-    return moe.make_shape(cfg.T if T is None else T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.act, cfg.wt,
-                          cfg.n_shared, tau)
+def shape_of(cfg, tau=0, T=None, wt=None):
+    return moe.make_shape(cfg.T if T is None else T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.act,
+                          cfg.wt if wt is None else wt, cfg.n_shared, tau)
+
+
+def tiled_inputs(d):
+    """The same inputs with every int4 code tensor packed into the tiled layout
+    (moe_pack_int4_tiled through the C ABI); the oracle keeps reading d."""
+    t = moe.layer.pack_int4_tiled(d)
+    torch.cuda.synchronize()
+    return t
 
 
 def act_dtype(cfg):
     return torch.float32 if cfg.act == "f32" else torch.bfloat16
 
 
-def run_layer(cfg, d, tau=0, residual=None, x=None):
-    """moe_layer_forward through the C ABI; returns (y, counts, topk_idx)."""
+def run_layer(cfg, d, tau=0, residual=None, x=None, wt=None):
+    """moe_layer_forward through the C ABI; returns (y, counts, topk_idx).
+    wt overrides the weight dtype code (e.g. "int4_tiled" with packed codes)."""
     x = d["x"] if x is None else x
     T = x.shape[0]
-    shape = shape_of(cfg, tau, T)
+    shape = shape_of(cfg, tau, T, wt)
     ws = torch.empty(moe.moe_workspace_bytes(shape), dtype=torch.uint8, device=DEV)
     y = torch.empty(T, cfg.d, dtype=act_dtype(cfg), device=DEV)
     counts = torch.empty(cfg.E, dtype=torch.int32, device=DEV)

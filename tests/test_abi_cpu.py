@@ -15,7 +15,7 @@ def declared_symbols():
     with open(os.path.join(ROOT, "include", "moe.h")) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -60,6 +60,10 @@ BAD_SHAPES = [
     (dict(act="f32", wt="bf16"), moe.MOE_EUNSUPPORTED),
     (dict(act="bf16", wt="f32"), moe.MOE_EUNSUPPORTED),
     (dict(d=20480), moe.MOE_EUNSUPPORTED),
+    (dict(wt="int4_tiled", d=4096 + 128), moe.MOE_EUNSUPPORTED),   # K not a multiple of 1024
+    (dict(wt="int4_tiled", F=9216), moe.MOE_EUNSUPPORTED),         # K above 8192 (down)
+    (dict(wt="int4_tiled", d=4104), moe.MOE_EINVAL),
+    (dict(act="f32", wt="int4_tiled", F=4096), moe.MOE_EUNSUPPORTED),
 ]
 
 
@@ -142,3 +146,15 @@ def test_read_ceiling_validation():
     with pytest.raises(moe.MoEError):
         moe.moe_read_ceiling(4104, 1024, 8192)     # misaligned buffer
     assert moe.moe_read_ceiling(None, 0, 8192) == 0
+
+
+def test_pack_int4_tiled_validation():
+    p, q = 1 << 20, 1 << 30
+    for args in ((p, q, -1, 16, 128), (p, q, 1, 8, 128), (p, q, 1, 24, 128), (p, q, 1, 16, 100),
+                 (p, q, 1, 16, 0), (None, q, 1, 16, 128), (p, None, 1, 16, 128),
+                 (p + 8, q, 1, 16, 128),                 # misaligned
+                 (p, p + 512, 1, 16, 128)):              # overlapping (1 KB each)
+        with pytest.raises(moe.MoEError) as ei:
+            moe.moe_pack_int4_tiled(*args, stream=0)
+        assert ei.value.status == moe.MOE_EINVAL, args
+    assert moe.moe_pack_int4_tiled(None, None, 0, 16, 128, stream=0) == 0

@@ -9,7 +9,7 @@ import torch
 import moe_inputs
 import moe_layer_forward_amd as moe
 from gpu_common import (DEV, TOL, check_routing_with_flips, device_inputs, oracle_weights, run_layer,
-                        say, shape_of, tokenwise_rel)
+                        say, shape_of, tiled_inputs, tokenwise_rel)
 from helpers import np_f64, np_store
 
 pytestmark = pytest.mark.gpu
@@ -82,11 +82,13 @@ def test_mixtral_prefill_full(orc):
     assert torch.equal(y, y2) and torch.equal(idx, idx2)
 
 
-def test_fine_int4_decode_full(orc):
+@pytest.mark.parametrize("wt", ["int4", "int4_tiled"])
+def test_fine_int4_decode_full(orc, wt):
+    """Row-major codes and the tiled codes the bench streams."""
     cfg = C["fine_int4_decode"]
-    say("full fine-grained int4 decode T=64 E=256 + shared")
+    say(f"full fine-grained int4 decode T=64 E=256 + shared, {wt}")
     d = device_inputs(cfg)
-    y, counts, idx = run_layer(cfg, d)
+    y, counts, idx = run_layer(cfg, tiled_inputs(d) if wt == "int4_tiled" else d, wt=wt)
     say(f"  active experts {(counts > 0).sum().item()}")
     _check_layer(orc, cfg, d, y, counts, idx, sel=np.arange(0, cfg.T, 2, dtype=np.int32))
 

@@ -13,7 +13,8 @@ import torch
 import moe_inputs
 import moe_layer_forward_amd as moe
 from gpu_common import (DEV, TOL, act_dtype, check_routing_with_flips, device_inputs,
-                        oracle_weights, run_layer, say, shape_of, tokenwise_rel, weights_struct)
+                        oracle_weights, run_layer, say, shape_of, tiled_inputs, tokenwise_rel,
+                        weights_struct)
 from helpers import np_f64, np_store
 
 pytestmark = pytest.mark.gpu
@@ -238,6 +239,57 @@ def test_layer_end_to_end_small(orc, name):
     say(f"  max rel {err.max():.3g} flips {flips}")
     assert err.max() < TOL[cfg.wt]
     assert np.array_equal(counts.cpu().numpy(), np.bincount(gi.ravel(), minlength=cfg.E))
+
+
+def test_pack_int4_tiled_layout():
+    """moe_pack_int4_tiled against the tiled layout as moe.h defines it, written
+    out piece by piece on the host; ragged matrix count, K of 2 and 3 groups."""
+    for n_mats, N, K in ((3, 48, 256), (1, 16, 384), (2, 128, 1024)):
+        say(f"pack int4 tiled n_mats={n_mats} N={N} K={K}")
+        g = torch.Generator().manual_seed(N + K)
+        src = torch.randint(0, 256, (n_mats, N, K // 2), dtype=torch.uint8, generator=g)
+        dst = torch.full_like(src, 0xA5).to(DEV)
+        moe.moe_pack_int4_tiled(src.to(DEV), dst, n_mats, N, K)
+        torch.cuda.synchronize()
+        got = dst.cpu().numpy().reshape(n_mats, -1)
+        a = src.numpy()
+        want = np.empty_like(got)
+        NG = K // 128
+        for m in range(n_mats):
+            for s_ in range(N // 16):
+                for gi in range(NG):
+                    for q in range(4):
+                        for r in range(16):
+                            o = ((s_ * NG + gi) * 64 + 16 * q + r) * 16
+                            want[m, o:o + 16] = a[m, 16 * s_ + r, 64 * gi + 16 * q:64 * gi + 16 * q + 16]
+        assert np.array_equal(got, want)
+    # nothing to do for zero matrices
+    moe.moe_pack_int4_tiled(None, None, 0, 16, 128)
+
+
+TILED = ["int4_mfma_multipass", "int4_mfma_wide_k", "int4_mfma_many"]
+
+
+@pytest.mark.parametrize("name", TILED)
+def test_layer_int4_tiled(orc, name):
+    """Tiled int4 codes: the layer against the oracle (which reads the row-major
+    codes), and bit-identical to the row-major run (same arithmetic)."""
+    cfg = SMALL[name]
+    say(f"layer int4 tiled {name}")
+    d = device_inputs(cfg)
+    y, counts, idx = run_layer(cfg, tiled_inputs(d), wt="int4_tiled")
+    W, S = oracle_weights(d)
+    x = np_store(d["x"])
+    wr, br = np_store(d["w_router"]), np_store(d["b_router"])
+    gi = idx.cpu().numpy()
+    y_f, idx_o, _, lg_o = orc.layer_forward(x, cfg.act, cfg.wt, cfg.k, wr, br, W, S)
+    flips = check_routing_with_flips(gi, idx_o, lg_o, cfg.k)
+    y_f, _, _, _ = orc.layer_forward(x, cfg.act, cfg.wt, cfg.k, wr, br, W, S, forced_idx=gi)
+    err = tokenwise_rel(np_f64(y), y_f)
+    say(f"  max rel {err.max():.3g} flips {flips}")
+    assert err.max() < TOL["int4_tiled"]
+    y_rm, _, idx_rm = run_layer(cfg, d)
+    assert torch.equal(idx, idx_rm) and torch.equal(y, y_rm)
 
 
 def test_residual_and_determinism(orc):
