@@ -22,8 +22,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// two fp32 -> packed bf16 (lo in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 (same result as f32_to_bf16 for every non-NaN input)
+typedef __bf16 moe_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float moe_f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((moe_f32x2_t){lo, hi}, moe_bf16x2_t));
 }
 
 // IEEE binary16 -> fp32 (hardware conversion).
@@ -60,7 +64,12 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g), as g * rcp(1 + 2^(-g log2 e)) with the hardware
+// exp2 and reciprocal (each within about 1 ulp in fp32).  For very negative g
+// the exponential overflows to +inf and the result is -0.
+__device__ __forceinline__ float silu(float g) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
 
 // Blocks are dealt round-robin to the 8 XCDs of an MI355X; remap so that
 // consecutive logical ids land on the same XCD (and share its L2).

@@ -8,19 +8,26 @@
 // gfx950 design:
 //  * a device-side plan (one small kernel) turns counts/offsets into a list of
 //    256-row M-tiles, one expert per tile: no host round trip;
-//  * a persistent grid of one 256-thread block per CU walks the (M-tile,
+//  * a persistent grid of one 512-thread block per CU walks the (M-tile,
 //    N-tile) list.  In every round the 32 CUs of one XCD take 32 consecutive
 //    tiles, and tiles are ordered in groups of 8 M-tiles x all N-tiles with M
 //    fastest, so concurrent blocks of an XCD share A and B panels in its L2;
-//  * block tile 256 x 256; 4 wave64s in a 2x2 arrangement each own
-//    128 x 128 = 4 x 4 accumulators of v_mfma_f32_32x32x16_bf16 (fp32);
-//  * LDS holds five stages of A and B of K = 32 each (160 KiB): tiles are
-//    copied global -> LDS by buffer_load ... lds (no VGPR staging) two to
-//    three K steps ahead of the MFMAs, with one barrier per K step; the copies
-//    of two consecutive stages (the two 64-byte halves of each 128-byte row
-//    segment) are issued within one step so they meet in the cache.  The
-//    lookahead matters more than the pairing: issuing the two halves back to
-//    back at the cost of one step of lookahead measured ~20% slower;
+//  * block tile 256 x 256, eight wave64s in two groups of four (waves i and
+//    i+4 share a SIMD).  The groups ping-pong: while one issues the 16 MFMAs
+//    of a K step (v_mfma_f32_32x32x16_bf16, fp32 accumulators), the other
+//    reads its fragments of the step from LDS and issues its share of the
+//    global -> LDS copies; a block barrier swaps the roles.  A copy waiting
+//    for the texture-address queue therefore never holds up the matrix core.
+//    Group g owns tile rows 128g..128g+127; wave i of a group owns 64 B-tile
+//    rows (4 x 2 accumulators);
+//  * the product is computed transposed (weights as the MFMA A operand), so a
+//    lane's accumulator holds four consecutive output columns of one token
+//    row: the epilogue stores 16 (fp32) or 8 (bf16) bytes per lane straight
+//    from registers, no LDS round trip;
+//  * LDS holds five stages of A and B of K = 32 each (160 KiB), refilled by
+//    buffer_load ... lds (no VGPR staging) four K steps ahead; every wave keeps
+//    at most its 3 newer stages in flight at a barrier, so the stage read next
+//    has landed;
 //  * the 16-byte chunks of each 64-byte LDS row are XOR-swizzled by
 //    (row/4)&3, so 16-byte fragment reads of 16 consecutive rows are
 //    conflict-free; each DMA lane simply fetches the chunk that belongs at its
@@ -46,7 +53,8 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int MF_BM = 256;
 constexpr int MF_BN = 256;
 constexpr int MF_BK = 32;         // K per LDS stage
-constexpr int MF_NS = 5;          // LDS stages (2-3 K steps of prefetch in flight)
+constexpr int MF_NS = 5;          // LDS stages (copies four K steps ahead)
+constexpr int MF_STAGE = MF_BM * MF_BK;   // elements of one operand stage
 constexpr int MF_GM = 8;          // M-tiles per scheduling group
 constexpr uint32_t MF_OOB = 0x80000000u;   // beyond any buffer: the range check yields 0
 
@@ -213,14 +221,23 @@ __device__ __forceinline__ int swz(int row, int ch) {
     return row * MF_BK + ((ch ^ ((row >> 2) & 3)) << 3);
 }
 
+// wait until at most 4n of this wave's copies are outstanding (n clamped to 0..3)
+__device__ __forceinline__ void wait_stages(int n) {
+    if (n >= 3) __builtin_amdgcn_s_waitcnt(0x0F7C);         // vmcnt(12)
+    else if (n == 2) __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
+    else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0F74);    // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
+}
+
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[MF_NS][MF_BM * MF_BK];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[MF_NS][MF_BN * MF_BK];
+__global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
+    // stage s: A at s * MF_STAGE, B at (MF_NS + s) * MF_STAGE (elements); a tile
+    // fills stages 0, 1, 2, ... from its first K step
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * MF_NS * MF_STAGE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2, wi = wave & 3;
     const int K = a.K, N = a.N;
     const int n_mt = a.tiles[3 * a.max_mt];
     const int nN = (MODE == 0) ? (N + 127) / 128 : (N + MF_BN - 1) / MF_BN;
@@ -231,207 +248,196 @@ __global__ __launch_bounds__(256, 1) void mfma_ffn_kernel(MfmaArgs a) {
     const int slot = (nblk % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
     const uint32_t row_bytes = (uint32_t)K * 2u;
     const int nk = (K + MF_BK - 1) / MF_BK;
-    // DMA: each wave instruction fills 16 tile rows x 64 B; this lane owns tile
-    // row wave*64 + i*16 + lane/4, physical chunk lane%4
-    const int dma_row = wave * 64 + (lane >> 2);
+    // copies: each wave instruction fills 16 tile rows x 64 B; wave w copies A
+    // rows and B rows 32w + 16i + lane/4 (i = 0, 1), physical chunk lane%4
+    const int dma_row = wave * 32 + (lane >> 2);
     const int32x4_t RA = make_desc(a.in, (uint32_t)a.in_rows * row_bytes);
     const uint32_t wmat = (uint32_t)N * row_bytes;
+    // B rows of this wave's copies: mode 0 waves 0-3 gate rows, waves 4-7 up rows
+    const uint16_t* wsrc = (MODE == 0 && wave >= 4) ? a.w1 : a.w0;
 
     const TailSplit ts = tail_split(total, nblk, nk, a.part_cap);
     const int ntasks = ts.nfull + ts.rtail * ts.S;
 
-    for (int task = slot; task < ntasks; task += nblk) {
-        // whole tile, or part s of tail tile j (K steps [kb, ke))
-        int L = task, kb = 0, ke = nk, pi = -1;
-        if (task >= ts.nfull) {
-            const int q = task - ts.nfull, j = q % ts.rtail, sp = q / ts.rtail;
+    // B-tile row of this lane's fragment ni (mode 0: gate rows, then the
+    // matching up rows 128 further)
+    auto brow = [&](int ni) __attribute__((always_inline)) {
+        return (MODE == 0) ? ni * 128 + wi * 32 + (lane & 31) : wi * 64 + ni * 32 + (lane & 31);
+    };
+
+    // task t: whole tile, or part sp of tail tile j (K steps [kb, ke)); its tile
+    // and this lane's copy offsets (the two copy rows r and r+16 share the
+    // swizzled chunk)
+    int c_kb, c_ke, c_kend, c_pi, c_nt, c_p0, c_rows, c_e, c_kcol;
+    uint32_t c_a0, c_a1, c_b0, c_b1;
+    auto setup = [&](int t) __attribute__((always_inline)) {
+        int L = t;
+        c_kb = 0;
+        c_ke = nk;
+        c_pi = -1;
+        if (t >= ts.nfull) {
+            const int q = t - ts.nfull, j = q % ts.rtail, sp = q / ts.rtail;
             L = ts.nfull + j;
-            kb = (int)((long)nk * sp / ts.S);
-            ke = (int)((long)nk * (sp + 1) / ts.S);
-            pi = j * ts.S + sp;
+            c_kb = (int)((long)nk * sp / ts.S);
+            c_ke = (int)((long)nk * (sp + 1) / ts.S);
+            c_pi = j * ts.S + sp;
         }
-        const int kend = min(K, ke * MF_BK);     // element bound of this task's K range
+        c_kend = min(K, c_ke * MF_BK);           // element bound of the task's K range
         // grouped order: GM M-tiles x all N-tiles, M fastest
-        const int grp = L / (MF_GM * nN);
-        const int gm0 = grp * MF_GM;
+        const int grpi = L / (MF_GM * nN);
+        const int gm0 = grpi * MF_GM;
         const int gsz = min(MF_GM, n_mt - gm0);
-        const int rem = L - grp * MF_GM * nN;
+        const int rem = L - grpi * MF_GM * nN;
         const int mt = gm0 + rem % gsz;
-        const int nt = rem / gsz;
+        c_nt = rem / gsz;
+        c_e = a.tiles[mt];
+        c_p0 = a.tiles[a.max_mt + mt];
+        c_rows = a.tiles[2 * a.max_mt + mt];
+        const int r = dma_row;
+        const int ch = (lane & 3) ^ ((r >> 2) & 3);
+        c_kcol = ch * 8;
+        const int src0 = (MODE == 0) ? (r < c_rows ? a.perm[c_p0 + r] / a.topk : 0) : c_p0 + r;
+        const int src1 = (MODE == 0) ? (r + 16 < c_rows ? a.perm[c_p0 + r + 16] / a.topk : 0) : c_p0 + r + 16;
+        c_a0 = r < c_rows ? (uint32_t)src0 * row_bytes + (uint32_t)ch * 16u : MF_OOB;
+        c_a1 = r + 16 < c_rows ? (uint32_t)src1 * row_bytes + (uint32_t)ch * 16u : MF_OOB;
+        const int n0 = (MODE == 0) ? c_nt * 128 + (r & 127) : c_nt * MF_BN + r;
+        const int n1 = (MODE == 0) ? c_nt * 128 + ((r + 16) & 127) : c_nt * MF_BN + r + 16;
+        c_b0 = n0 < N ? (uint32_t)n0 * row_bytes + (uint32_t)ch * 16u : MF_OOB;
+        c_b1 = n1 < N ? (uint32_t)n1 * row_bytes + (uint32_t)ch * 16u : MF_OOB;
+    };
 
-        const int e = a.tiles[mt];
-        const int p0 = a.tiles[a.max_mt + mt];
-        const int rows = a.tiles[2 * a.max_mt + mt];
-
-        // B rows of this wave: mode 0 waves 0-1 hold gate rows, waves 2-3 up rows
-        const uint16_t* wsrc = (MODE == 0 && wave >= 2) ? a.w1 : a.w0;
-        const int32x4_t RB = make_desc(wsrc + (size_t)e * N * K, wmat);
-        uint32_t aoff[4], boff[4];
-        int kcol[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = dma_row + i * 16;
-            const int ch = (lane & 3) ^ ((r >> 2) & 3);
-            kcol[i] = ch * 8;
-            if (r < rows) {
-                const int src = (MODE == 0) ? a.perm[p0 + r] / a.topk : p0 + r;
-                aoff[i] = (uint32_t)src * row_bytes + (uint32_t)ch * 16u;
-            } else {
-                aoff[i] = MF_OOB;
-            }
-            const int n = (MODE == 0) ? nt * 128 + (r & 127) : nt * MF_BN + r;
-            boff[i] = (n < N) ? (uint32_t)n * row_bytes + (uint32_t)ch * 16u : MF_OOB;
-        }
-        floatx16 acc[4][4];
+    if (slot >= ntasks) return;
+    setup(slot);
+    for (int task = slot; task < ntasks; task += nblk) {
+        const int kb = c_kb, ke = c_ke, kend = c_kend, kcol = c_kcol;
+        const uint32_t aoff[2] = {c_a0, c_a1}, boff[2] = {c_b0, c_b1};
+        const int pi = c_pi, nt = c_nt, p0 = c_p0, rows = c_rows;
+        const int32x4_t RB = make_desc(wsrc + (size_t)c_e * N * K, wmat);
+        floatx16 acc[4][2];
+        bf16x8_t fa[2][4], fb[2][2];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-        // fragments of one stage: [ks][mi] for A, [ks][ni] for B
-        bf16x8_t fa[2][MF_BK / 16][4], fb[2][MF_BK / 16][4];
-        auto read_frag = [&](int st, int sl, int q) {   // q: 0..15, A first then B per ks
-            const int ks = q >> 3, j = q & 3;
-            const int ch = ks * 2 + (lane >> 5);
-            if ((q & 4) == 0) {
-                fa[sl][ks][j] = *reinterpret_cast<const bf16x8_t*>(
-                    &sA[st][swz(wm * 128 + j * 32 + (lane & 31), ch)]);
-            } else {
-                const int r = (MODE == 0) ? ((j >> 1) * 128 + wn * 64 + (j & 1) * 32 + (lane & 31))
-                                          : (wn * 128 + j * 32 + (lane & 31));
-                fb[sl][ks][j] = *reinterpret_cast<const bf16x8_t*>(&sB[st][swz(r, ch)]);
-            }
-        };
-        auto mma = [&](int sl, int m) {                 // m: 0..31 = (ks, mi, ni)
-            const int ks = m >> 4, mi = (m >> 2) & 3, ni = m & 3;
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][ks][mi], fb[sl][ks][ni],
-                                                                   acc[mi][ni], 0, 0, 0);
-        };
-        auto issue_one = [&](int kt, int i) {          // DMA i (0..7) of K step kt
-            const int st = kt % MF_NS;
+        auto issue = [&](int kt) __attribute__((always_inline)) {   // this wave's 4 copies of K step kt
+            const int st = (kt - kb) % MF_NS;
             const uint32_t kbyte = (uint32_t)kt * (MF_BK * 2);
-            const int k0 = kt * MF_BK;
-            const int ii = i >> 1;
-            const int r0 = wave * 64 + ii * 16;
-            if ((i & 1) == 0) {
-                const bool kok = k0 + kcol[ii] < kend;
-                dma16(RA, (kok && aoff[ii] != MF_OOB) ? aoff[ii] + kbyte : MF_OOB, lds_addr(&sA[st][r0 * MF_BK]));
-            } else {
-                const bool kok = k0 + kcol[ii] < kend;
-                dma16(RB, (kok && boff[ii] != MF_OOB) ? boff[ii] + kbyte : MF_OOB, lds_addr(&sB[st][r0 * MF_BK]));
+            const bool kok = kt * MF_BK + kcol < kend;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r0 = wave * 32 + i * 16;
+                dma16(RA, (kok && aoff[i] != MF_OOB) ? aoff[i] + kbyte : MF_OOB,
+                      lds_addr(&smem[st * MF_STAGE + r0 * MF_BK]));
+                dma16(RB, (kok && boff[i] != MF_OOB) ? boff[i] + kbyte : MF_OOB,
+                      lds_addr(&smem[(MF_NS + st) * MF_STAGE + r0 * MF_BK]));
             }
         };
-
-        // drain this wave's earlier memory traffic (the previous tile's output
-        // stores share the counter) and make sure every wave is done reading
-        // the stages before they are refilled
-        wait_vm(0);
-        block_barrier();
-        // Copies of K steps >= nk read out of range and store zeros, so every
-        // step below issues exactly 8 copies and the wait counts are constant.
+        auto read = [&](int st) __attribute__((always_inline)) {
+            const uint16_t* sa = smem + st * MF_STAGE;
+            const uint16_t* sb = smem + (MF_NS + st) * MF_STAGE;
 #pragma unroll
-        for (int kt = 0; kt < 3; ++kt)
+            for (int ks = 0; ks < 2; ++ks) {
+                const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) issue_one(kb + kt, i);
-        wait_vm(16);                 // stage kb landed; kb+1, kb+2 may still fly
-        block_barrier();
+                for (int mi = 0; mi < 4; ++mi)
+                    fa[ks][mi] = *reinterpret_cast<const bf16x8_t*>(&sa[swz(grp * 128 + mi * 32 + (lane & 31), ch)]);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) read_frag(kb % MF_NS, 0, q);
-
-        // Software pipeline, per K step kt (fragments of stage kt already in
-        // register slot kt&1), with steps taken in pairs from kb:
-        //   8 MFMAs | wait: stage kt+1 landed (this wave), own reads done |
-        //   barrier | 24 MFMAs interleaved with the 16 reads of stage kt+1 and,
-        //   on the first step of a pair, the 16 copies of stages kt+3 and kt+4
-        //   (two per third MFMA, all of kt+3 first).  Stages kt+3 and kt+4 hold
-        //   the two 64-byte halves of the same 128-byte row segments, so their
-        //   copies meet in the cache; the buffers they refill held stages kt-2
-        //   and kt-1, which every wave has finished reading.
-        //   Outstanding copies at the wait: kt+1, kt+2 on the first step of a
-        //   pair (vmcnt 8), kt+2, kt+3, kt+4 on the second (vmcnt 16).
-        // The number of steps is rounded up to even: an extra step multiplies
-        // zero fragments.
-        auto step = [&](int kt, auto slc) {
-            constexpr int sl = decltype(slc)::value;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                mma(sl, m);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int ni = 0; ni < 2; ++ni)
+                    fb[ks][ni] = *reinterpret_cast<const bf16x8_t*>(&sb[swz(brow(ni), ch)]);
             }
-            wait_vm(sl == 0 ? 8 : 16);                     // stage kt+1 landed
-            __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): own reads of stage kt done
+        };
+        // transposed product: acc[mi][ni] is (B rows of fragment ni) x (tokens of fragment mi)
+        auto mma = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][ni], fa[ks][mi],
+                                                                               acc[mi][ni], 0, 0, 0);
+        };
+
+        // Prologue: stages 0..3 take the tile's first K steps.  Vector memory
+        // operations complete in order, so the wait for step kb also covers
+        // this wave's epilogue stores of the previous tile; the barrier makes
+        // every wave's copies of step kb visible and ends all LDS reads of the
+        // previous tile.
+        for (int kt = kb; kt < kb + MF_NS - 1 && kt < ke; ++kt) issue(kt);
+        wait_stages(ke - 1 - kb);
+        block_barrier();
+        if (grp == 1) block_barrier();               // group 1 starts one phase later
+        // Per K step kt, each wave: memory phase (fragments of step kt, then the
+        // copies of step kt+4 into the buffer of step kt-1, which both groups
+        // have read), barrier, compute phase, barrier.  At each barrier a wave
+        // has landed its copies of step kt+1: only those of the (at most 3)
+        // later steps may still be in flight.
+        for (int kt = kb; kt < ke; ++kt) {
+            read((kt - kb) % MF_NS);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + MF_NS - 1 < ke) issue(kt + MF_NS - 1);
+            __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): own fragments read
+            wait_stages(ke - 2 - kt);
             block_barrier();
-#pragma unroll
-            for (int m = 8; m < 32; ++m) {
-                mma(sl, m);
-                __builtin_amdgcn_sched_barrier(0);
-                const int j = m - 8;                       // 0..23
-                if (j % 3 == 0) {
-                    if constexpr (sl == 0) {
-                        const int c = j / 3;               // 0..7: copies 2c, 2c+1
-                        const int st = c < 4 ? kt + 3 : kt + 4;
-                        issue_one(st, (2 * c) & 7);
-                        issue_one(st, (2 * c + 1) & 7);
-                    }
-                } else {
-                    read_frag((kt + 1) % MF_NS, sl ^ 1, j - j / 3 - 1);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-        const int nk2 = (ke - kb + 1) & ~1;
-        for (int kt = kb; kt < kb + nk2; kt += 2) {
-            step(kt, std::integral_constant<int, 0>{});
-            step(kt + 1, std::integral_constant<int, 1>{});
+            __builtin_amdgcn_s_setprio(1);
+            mma();
+            __builtin_amdgcn_s_setprio(0);
+            wait_stages(ke - 2 - kt);
+            block_barrier();
         }
+        // the next task's loads are issued here, not behind the stores below
+        if (task + nblk < ntasks) setup(task + nblk);
 
-        if (pi >= 0) {
-            // a part of a split tail tile: raw fp32 accumulators, tile-local
-            // [row][col] with col = the B-tile row the accumulator belongs to
-            float* pt = a.part + (size_t)pi * (MF_BM * MF_BN);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int row = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-#pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const int col = (MODE == 0) ? (ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 + (lane & 31)
-                                                    : wn * 128 + ni * 32 + (lane & 31);
-                        pt[row * MF_BN + col] = acc[mi][ni][v];
-                    }
-                }
-            continue;
-        }
-
-        // ---- epilogue; accumulator element v of lane l: column l%32, row 8*(v/4) + 4*(l/32) + v%4
+        // ---- epilogue.  Accumulator element v of lane l: token row
+        // grp*128 + mi*32 + l%32, B-tile row brow0(ni) + 8*(v/4) + 4*(l/32) + v%4,
+        // i.e. four consecutive output columns per (v/4).
+        const int c0 = 4 * (lane >> 5);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
+            const int row = grp * 128 + mi * 32 + (lane & 31);
+            if (pi >= 0) {
+                // a part of a split tail tile: raw fp32 sums, tile-local [row][B-tile row]
+                float* pt = a.part + (size_t)pi * (MF_BM * MF_BN) + row * MF_BN;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-                if (row >= rows) continue;
-                const size_t prow = (size_t)(p0 + row) * N;
-                if (MODE == 0) {
+                for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-                    for (int nj = 0; nj < 2; ++nj) {
-                        const int f = nt * 128 + wn * 64 + nj * 32 + (lane & 31);
-                        if (f < N) {
-                            const float h = silu(acc[mi][nj][v]) * acc[mi][nj + 2][v];
-                            reinterpret_cast<uint16_t*>(a.out)[prow + f] = f32_to_bf16(h);
-                        }
+                    for (int q = 0; q < 4; ++q) {
+                        const int col = ((MODE == 0) ? ni * 128 + wi * 32 : wi * 64 + ni * 32) + 8 * q + c0;
+                        *reinterpret_cast<float4*>(pt + col) = make_float4(
+                            acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
                     }
-                } else {
+            } else if (MODE == 0) {
+                // h = silu(g) * u, four bf16 (8 bytes) per lane and q
+                uint16_t* hrow = reinterpret_cast<uint16_t*>(a.out) + (size_t)(p0 + row) * N;
 #pragma unroll
-                    for (int ni = 0; ni < 4; ++ni) {
-                        const int n = nt * MF_BN + wn * 128 + ni * 32 + (lane & 31);
-                        if (n < N) reinterpret_cast<float*>(a.out)[prow + n] = acc[mi][ni][v];
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const int f = nt * 128 + wi * 32 + 8 * q + c0;
+                    float h[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) h[j] = silu(acc[mi][0][4 * q + j]) * acc[mi][1][4 * q + j];
+                    if (row < rows && f < N)
+                        *reinterpret_cast<uint2*>(hrow + f) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
                 }
+            } else {
+                float* yrow = reinterpret_cast<float*>(a.out) + (size_t)(p0 + row) * N;
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int n = nt * MF_BN + wi * 64 + ni * 32 + 8 * q + c0;
+                        if (row < rows && n < N)
+                            *reinterpret_cast<float4*>(yrow + n) = make_float4(
+                                acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
+                    }
             }
         }
+        // group 0 finished one phase earlier (its epilogue ran beside group 1's
+        // last MFMAs); its extra barrier pairs with group 1's last one, as
+        // group 1 had the extra barrier at the start
+        if (grp == 0) block_barrier();
     }
 }
 
@@ -477,7 +483,7 @@ __global__ __launch_bounds__(256) void mfma_tail_reduce(MfmaArgs a, int G) {
     for (int i = 0; i < 4; ++i) {
         if (MODE == 0) {
             const int f = nt * 128 + c + i;
-            if (f < N) reinterpret_cast<uint16_t*>(a.out)[orow + f] = f32_to_bf16(silu(gv[i]) * uv[i]);
+            if (f < N) reinterpret_cast<uint16_t*>(a.out)[orow + f] = (uint16_t)pack_bf16x2(silu(gv[i]) * uv[i], 0.f);
         } else {
             const int n = nt * MF_BN + c + i;
             if (n < N) reinterpret_cast<float*>(a.out)[orow + n] = gv[i];
@@ -677,13 +683,13 @@ hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void*
             n_cu = 256;
     }
     const int nN = mfma_ntiles_n(mode, N);
-    // big tiles: one 256-thread block per CU
+    // big tiles: one 512-thread block per CU
     const int slots = max_mt * nN;
     const int grid = slots < n_cu ? slots : n_cu;
     if (mode == 0)
-        hipLaunchKernelGGL(mfma_ffn_kernel<0>, dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(mfma_ffn_kernel<0>, dim3(grid), dim3(512), 0, s, a);
     else
-        hipLaunchKernelGGL(mfma_ffn_kernel<1>, dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(mfma_ffn_kernel<1>, dim3(grid), dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.part_cap > 0) {
