@@ -367,6 +367,9 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
         // every wave's copies of step kb visible and ends all LDS reads of the
         // previous tile.
         for (int kt = kb; kt < kb + MF_NS - 1 && kt < ke; ++kt) issue(kt);
+        // the next task's loads go out behind the prologue copies and land
+        // during the K loop (which makes the wait below slightly stricter)
+        if (task + nblk < ntasks) setup(task + nblk);
         wait_stages(ke - 1 - kb);
         block_barrier();
         if (grp == 1) block_barrier();               // group 1 starts one phase later
@@ -388,8 +391,6 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
             wait_stages(ke - 2 - kt);
             block_barrier();
         }
-        // the next task's loads are issued here, not behind the stores below
-        if (task + nblk < ntasks) setup(task + nblk);
 
         // ---- epilogue.  Accumulator element v of lane l: token row
         // grp*128 + mi*32 + l%32, B-tile row brow0(ni) + 8*(v/4) + 4*(l/32) + v%4,
