@@ -227,6 +227,26 @@ def read_ceiling_gbs(nbytes=4 << 30, reps=5):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def mfma_ceiling(iters=40000, reps=3):
+    """Measured matrix-core ceiling: the library's loop of independent bf16
+    MFMAs on every CU, timed with HIP events; also the shader clock (GHz) that
+    block 0 ran at, from its cycle and 100 MHz counters."""
+    n_sink = 4096
+    sink = torch.empty(n_sink, dtype=torch.float32, device=DEV)
+    clk = torch.zeros(2, dtype=torch.int64, device=DEV)
+    for _ in range(2):
+        moe.moe_mfma_ceiling(iters, sink, n_sink * 4)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        flops = moe.moe_mfma_ceiling(iters, sink, n_sink * 4, clk)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    cyc, ticks = clk.cpu().tolist()
+    return flops / (ms * 1e-3) / 1e12, cyc / (ticks / 100e6) / 1e9
+
+
 def roofline_obj(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -290,10 +310,13 @@ def main():
     value = cfg.T * args.steps / wall
     achieved = ffn_bytes / (ffn_mean * 1e-3) / 1e9
     if cfg.T * cfg.k / max(U, 1) > 64:      # prefill-sized groups: MFMA-bound
-        roof = dict(roofline_obj("mfma", ffn_flops / (ffn_mean * 1e-3) / 1e12,
-                                 BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
+        tf = ffn_flops / (ffn_mean * 1e-3) / 1e12
+        mceil, mclk = mfma_ceiling()
+        roof = dict(roofline_obj("mfma", tf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
                     kernel="expert FFN step (MFMA gate/up + down)", flops_per_launch=ffn_flops,
-                    launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5))
+                    launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5),
+                    measured_mfma_ceiling=round(mceil, 1), mfma_ceiling_clock_ghz=round(mclk, 3),
+                    frac_of_measured_ceiling=round(tf / mceil, 4))
     else:
         ceil = read_ceiling_gbs()
         roof = dict(roofline_obj("hbm", achieved, HBM_PEAK_GBS, "GB/s",
@@ -332,13 +355,17 @@ def main():
         pwall, pffn_mean, pffn_med, pwall_layer = prun.timed(psteps, max(2, args.warmup // 2))
         _, pbytes, pflops = prun.ffn_algorithmic()
         ptf = pflops / (pffn_mean * 1e-3) / 1e12
+        mceil, mclk = mfma_ceiling()
         out["prefill"] = {
             "workload": pcfg.name, "T": pcfg.T, "value": round(pcfg.T * psteps / pwall, 1),
             "unit": "tokens/s", "ms_per_step": round(pwall * 1e3 / psteps, 4), "steps": psteps,
             "counts": prun.counts.cpu().tolist(),
             "roofline": dict(roofline_obj("mfma", ptf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
                              kernel="expert FFN step (MFMA gate/up + down)",
-                             flops_per_launch=pflops, launch_ms=round(pffn_mean, 4)),
+                             flops_per_launch=pflops, launch_ms=round(pffn_mean, 4),
+                             measured_mfma_ceiling=round(mceil, 1),
+                             mfma_ceiling_clock_ghz=round(mclk, 3),
+                             frac_of_measured_ceiling=round(ptf / mceil, 4)),
             "layer_call_ms_per_step": round(pwall_layer * 1e3 / psteps, 4),
         }
         log(json.dumps(out["prefill"]))

@@ -443,6 +443,19 @@ int moe_pack_int4_tiled(const void* src, void* dst, int64_t n_mats, int32_t N, i
     return hip_check(launch_pack_int4_tiled(src, dst, (size_t)n_mats, N, K, st), st, "pack int4", err, err_len);
 }
 
+int moe_mfma_ceiling(int32_t iters, float* sink, size_t sink_bytes, uint64_t* clock, int64_t* flops, void* stream,
+                     char* err, size_t err_len) {
+    if (iters < 1 || iters > (1 << 24)) return fail(err, err_len, MOE_EINVAL, "iters=%d out of range [1, 2^24]", iters);
+    NEED_PTR(sink, "sink");
+    const int blocks = mfma_ceiling_blocks();
+    if (sink_bytes < (size_t)blocks * 8 * sizeof(float))
+        return fail(err, err_len, MOE_EINVAL, "sink_bytes=%zu below %zu", sink_bytes, (size_t)blocks * 8 * sizeof(float));
+    if (clock && (uintptr_t)clock % 8) return fail(err, err_len, MOE_EINVAL, "clock is not 8-byte aligned");
+    if (flops) *flops = (int64_t)blocks * 8 * iters * 8 * (2LL * 32 * 32 * 16);
+    hipStream_t st = (hipStream_t)stream;
+    return hip_check(launch_mfma_ceiling(iters, sink, clock, st), st, "mfma ceiling", err, err_len);
+}
+
 int moe_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, void* stream, char* err, size_t err_len) {
     if (bytes % 16) return fail(err, err_len, MOE_EINVAL, "bytes=%zu is not a multiple of 16", bytes);
     if (bytes) NEED_PTR(buf, "buf");

@@ -52,6 +52,8 @@ hipError_t launch_combine(int act, const float* yp, const int32_t* inv, const fl
                           const float* ys, const void* res, void* y, int T, int d, int k,
                           hipStream_t s);
 hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+int mfma_ceiling_blocks();
+hipError_t launch_mfma_ceiling(int iters, float* sink, uint64_t* clk, hipStream_t s);
 hipError_t launch_rmsnorm(int act, const void* h, const float* gamma, float eps, void* out, int T,
                           int d, hipStream_t s);
 

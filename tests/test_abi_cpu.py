@@ -158,3 +158,14 @@ def test_pack_int4_tiled_validation():
             moe.moe_pack_int4_tiled(*args, stream=0)
         assert ei.value.status == moe.MOE_EINVAL, args
     assert moe.moe_pack_int4_tiled(None, None, 0, 16, 128, stream=0) == 0
+
+
+def test_mfma_ceiling_validation():
+    p = 1 << 20
+    for args in ((0, p, 1 << 20), ((1 << 24) + 1, p, 1 << 20), (10, None, 1 << 20), (10, p + 4, 1 << 20),
+                 (10, p, 16)):
+        with pytest.raises(moe.MoEError) as ei:
+            moe.moe_mfma_ceiling(*args, stream=0)
+        assert ei.value.status == moe.MOE_EINVAL, args
+    with pytest.raises(moe.MoEError):
+        moe.moe_mfma_ceiling(10, p, 1 << 20, clock=p + 4, stream=0)   # misaligned clock

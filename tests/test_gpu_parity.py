@@ -428,3 +428,18 @@ def test_read_ceiling_reads_every_word():
         torch.cuda.synchronize()
         ref = np.bitwise_xor.reduce(h.numpy().view(np.uint32))
         assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(ref)
+
+
+def test_mfma_ceiling_runs():
+    """The matrix-core ceiling helper: every wave writes its sum (the products
+    of its constant fragments), the clock counters advance, the flop count is
+    the launch's."""
+    sink = torch.full((4096,), float("nan"), dtype=torch.float32, device=DEV)
+    clk = torch.zeros(2, dtype=torch.int64, device=DEV)
+    flops = moe.moe_mfma_ceiling(16, sink, 4096 * 4, clk)
+    torch.cuda.synchronize()
+    n = flops // (8 * 16 * 8 * 32768)
+    s = sink[: n * 8].cpu()
+    assert torch.isfinite(s).all()
+    cyc, ticks = clk.cpu().tolist()
+    assert cyc > 0 and ticks >= 0
