@@ -252,6 +252,43 @@ def roofline_obj(bound, achieved, peak, unit, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
+def extras():
+    """Decode-side sweeps printed as JSON lines (not the bench line): the GEMV /
+    MFMA crossover that sets tau (one expert holding c rows, Mixtral weights,
+    top-1 with the router biased onto expert 0), and the Mixtral layer at
+    decode batch sizes T = 8 ... 64."""
+    dcfg = moe_inputs.CONFIGS["mixtral_decode"]
+    _, wr, _, W = device_layer(dcfg)
+    bias = torch.zeros(dcfg.E, dtype=torch.float32, device=DEV)
+    bias[0] = 1000.0
+    wbytes = 3 * dcfg.d * dcfg.F * 2
+    for c in (1, 2, 4, 8, 12, 16, 20, 24, 32, 48, 64):
+        cfg = dcfg.replace(name=f"tau_sweep_c{c}", T=c, k=1)
+        x = moe_inputs.activations(cfg, 0).to(DEV)
+        for tau, path in ((-1, "gemv"), (1, "mfma")):
+            if tau == 1 and c < 2:
+                continue
+            run = Runner(cfg, x, wr, bias, W, tau=tau)
+            _, ffn_mean, ffn_med, _ = run.timed(20, 5)
+            assert int(run.counts[0]) == c
+            print(json.dumps({"sweep": "tau", "rows": c, "path": path, "ffn_ms": round(ffn_mean, 4),
+                              "ffn_ms_median": round(ffn_med, 4),
+                              "weight_GBps": round(wbytes / (ffn_mean * 1e-3) / 1e9, 1)}), flush=True)
+            del run
+    for T in (8, 16, 32, 64):
+        cfg = dcfg.replace(name=f"mixtral_decode_t{T}", T=T)
+        x = moe_inputs.activations(cfg, 0).to(DEV)
+        run = Runner(cfg, x, wr, None, W)
+        wall, ffn_mean, _, _ = run.timed(20, 5)
+        U, nbytes, _ = run.ffn_algorithmic()
+        print(json.dumps({"sweep": "decode_T", "T": T, "active_experts": U,
+                          "ms_per_step": round(wall * 1e3 / 20, 4), "tokens_per_s": round(T * 20 / wall, 1),
+                          "ffn_ms": round(ffn_mean, 4),
+                          "ffn_GBps": round(nbytes / (ffn_mean * 1e-3) / 1e9, 1),
+                          "frac_of_8TBps": round(nbytes / (ffn_mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+        del run
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +306,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--extras", action="store_true",
+                    help="print the decode sweeps (tau crossover, decode batch sizes) instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -279,6 +318,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     moe.lib()   # fail loudly if the HIP library is not built
+    if args.extras:
+        extras()
+        return
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=DEV).fill_(1.0)   # 1 GiB
         dst = torch.empty_like(src)

@@ -188,14 +188,38 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     const GemvArgs* qp = s->n_shared ? &q : nullptr;
     const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
     const bool tiled = s->wt == MOE_INT4_G128_TILED;
+    // bf16 groups between one GEMV pass and the MFMA threshold run the skinny
+    // MFMA kernel (one pass of up to 16 tokens) when such a group can occur:
+    // a group holds at most T rows, and everything below the tiles must fit
+    // one skinny pass (tau <= 16); a negative tau keeps the GEMV for all
+    const int tau_m = use_mfma ? tau : s->T;                   // largest group below the tiles
+    auto skinny_lo = [&](int mode, int K, int N, int in_rows) -> int {
+        if (s->wt != MOE_BF16 || s->act != MOE_BF16 || s->tau < 0 || tau_m > 16 ||
+            !skinny_supported(K, N, in_rows))
+            return -1;
+        const int lo = gemv_pass_tokens(s->wt, mode, K);
+        return tau_m > lo ? lo : -1;
+    };
     // one pass (gate/up or down) of the routed and the shared expert: int4 on
     // the matrix cores in one launch, else one GEMV launch each
     auto pass = [&](int mode, const char* what) -> int {
         if (tiled || (s->wt == MOE_INT4_G128 && i4mfma_supported(g.K, g.N)))
             return hip_check(launch_i4mfma(mode, tiled, &g, qp, st), st, what, err, err_len);
         g.rows_per_item = gemv_rows_per_item(s->wt, mode, g.K, g.N, active);
+        const int in_rows = mode == 0 ? s->T : s->T * s->k;
+        const int lo = skinny_lo(mode, g.K, g.N, in_rows);
+        const int gemv_tau = g.tau;
+        if (lo >= 0) g.tau = lo;                                   // the GEMV keeps groups of <= lo rows
         int r = hip_check(launch_gemv(s->wt, s->act, mode, g, s->E, max_rows_gemv, st), st, what, err, err_len);
-        if (r || !qp) return r;
+        g.tau = gemv_tau;
+        if (r) return r;
+        if (lo >= 0) {
+            r = hip_check(launch_skinny(mode, g.w0, g.w1, g.in, in_rows, g.out, g.counts, g.offsets, g.perm, g.N,
+                                        g.K, g.topk, s->E, lo, tau_m, st),
+                          st, what, err, err_len);
+            if (r) return r;
+        }
+        if (!qp) return r;
         q.rows_per_item = gemv_rows_per_item(s->wt, mode, q.K, q.N, 1);
         return hip_check(launch_gemv(s->wt, s->act, mode, q, 1, s->T, st), st, what, err, err_len);
     };

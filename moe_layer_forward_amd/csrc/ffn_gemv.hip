@@ -550,6 +550,8 @@ static hipError_t launch_mode(const GemvArgs& a, const Variant& v, int max_items
 }
 #undef GEMV_CASE
 
+int gemv_pass_tokens(int wt, int mode, int K) { return choose(wt, K, mode == 0 ? 2 : 1).nt; }
+
 hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, int max_rows,
                        hipStream_t s) {
     (void)max_rows;

@@ -68,6 +68,17 @@ def test_mixtral_decode_full(orc):
     _check_layer(orc, cfg, d, y, counts, idx, sel=np.arange(cfg.T, dtype=np.int32))
 
 
+def test_mixtral_decode_t32_full(orc):
+    """The page's 32 x 4096 x 14336 top-2 shape: groups of ~8 rows on the GEMV
+    and the skinny MFMA kernel, larger ones on the MFMA tiles."""
+    cfg = C["mixtral_decode"].replace(name="mixtral_decode_t32", T=32)
+    say("full mixtral decode T=32")
+    d = device_inputs(cfg)
+    y, counts, idx = run_layer(cfg, d)
+    say(f"  counts {counts.cpu().tolist()}")
+    _check_layer(orc, cfg, d, y, counts, idx, sel=np.arange(cfg.T, dtype=np.int32))
+
+
 def test_mixtral_prefill_full(orc):
     cfg = C["mixtral_prefill"]
     say("full mixtral prefill T=4096 (Zipf-loaded experts)")

@@ -46,6 +46,15 @@ SMALL = {
     "int4_mfma_many": moe_inputs.MoEConfig(
         "int4_mfma_many", T=8, d=1024, E=256, k=8, F=1024, act="bf16", wt="int4",
         model="s_int4_many", n_shared=1, w_std=0.05),
+    # bf16 groups of 9-16 rows on the skinny MFMA kernel beside the GEMV (<= 8
+    # rows) and the MFMA tiles (> 16 rows); N = 1600 leaves a partial last chunk
+    # (and K = 1600 keeps the down pass off the skinny kernel)
+    "bf16_skinny_mix": moe_inputs.MoEConfig(
+        "bf16_skinny_mix", T=40, d=1024, E=8, k=2, F=1536, act="bf16", wt="bf16",
+        model="s_bf16_sk", w_std=0.05),
+    "bf16_skinny_ragged": moe_inputs.MoEConfig(
+        "bf16_skinny_ragged", T=24, d=1024, E=4, k=2, F=1600, act="bf16", wt="bf16",
+        model="s_bf16_skr", w_std=0.05),
     "f32_ragged": moe_inputs.MoEConfig(
         "f32_ragged", T=37, d=200, E=5, k=3, F=72, act="f32", wt="f32", model="s_f32"),
 }
@@ -443,3 +452,13 @@ def test_mfma_ceiling_runs():
     assert torch.isfinite(s).all()
     cyc, ticks = clk.cpu().tolist()
     assert cyc > 0 and ticks >= 0
+
+
+def test_skinny_groups_exercised(orc):
+    """The mixed config really has groups on all three bf16 paths."""
+    cfg = SMALL["bf16_skinny_mix"]
+    d = device_inputs(cfg)
+    _, counts, _ = run_layer(cfg, d)
+    c = counts.cpu().numpy()
+    say(f"  counts {c.tolist()}")
+    assert (c > 8).any() and ((c > 8) & (c <= 16)).any()
