@@ -188,10 +188,14 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     const GemvArgs* qp = s->n_shared ? &q : nullptr;
     const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
     const bool tiled = s->wt == MOE_INT4_G128_TILED;
-    // bf16 groups between one GEMV pass and the MFMA threshold run the skinny
-    // MFMA kernel (one pass of up to 16 tokens) when such a group can occur:
-    // a group holds at most T rows, and everything below the tiles must fit
-    // one skinny pass (tau <= 16); a negative tau keeps the GEMV for all
+    // bf16 groups below the MFMA tiles: when one of them is larger than a
+    // GEMV pass (lo rows), the skinny MFMA kernel (one pass of up to 16
+    // tokens) takes every group below the tiles in one balanced launch and
+    // the GEMV stands aside; otherwise the GEMV serves them.  Both kernels
+    // decide from the counts on the device.  The skinny kernel is only
+    // launched when such a group can occur: a group holds at most T rows, and
+    // everything below the tiles must fit one skinny pass (tau <= 16); a
+    // negative tau keeps the GEMV for all
     const int tau_m = use_mfma ? tau : s->T;                   // largest group below the tiles
     auto skinny_lo = [&](int mode, int K, int N, int in_rows) -> int {
         if (s->wt != MOE_BF16 || s->act != MOE_BF16 || s->tau < 0 || tau_m > 16 ||
@@ -209,9 +213,13 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
         const int in_rows = mode == 0 ? s->T : s->T * s->k;
         const int lo = skinny_lo(mode, g.K, g.N, in_rows);
         const int gemv_tau = g.tau;
-        if (lo >= 0) g.tau = lo;                                   // the GEMV keeps groups of <= lo rows
+        if (lo >= 0) {
+            g.tau = lo;                                            // the GEMV keeps groups of <= lo rows
+            g.yield_hi = tau_m;                                    // unless a larger one sends all to skinny
+        }
         int r = hip_check(launch_gemv(s->wt, s->act, mode, g, s->E, max_rows_gemv, st), st, what, err, err_len);
         g.tau = gemv_tau;
+        g.yield_hi = 0;
         if (r) return r;
         if (lo >= 0) {
             r = hip_check(launch_skinny(mode, g.w0, g.w1, g.in, in_rows, g.out, g.counts, g.offsets, g.perm, g.N,

@@ -232,22 +232,29 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(GemvArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ks = wave % KS, rg = wave / KS;
 
-    // --- the experts this kernel serves: c_e > 0 and (tau < 0 or c_e <= tau)
+    // --- the experts this kernel serves: c_e > 0 and (tau < 0 or c_e <= tau);
+    // none when a group of tau < c <= yield_hi rows hands the batch to the
+    // skinny kernel
     __shared__ int s_act[256];
-    __shared__ int s_wcnt[4];
+    __shared__ int s_wcnt[4], s_wyield[4];
     int U = 1;
     if (a.counts) {
         const int e = threadIdx.x;
         const int c = (e < a.E) ? a.counts[e] : 0;
         const bool act = c > 0 && (a.tau < 0 || c <= a.tau);
         const uint64_t m = __ballot(act);
-        if (lane == 0) s_wcnt[wave] = __popcll(m);
+        const uint64_t y = __ballot(a.yield_hi > 0 && c > a.tau && c <= a.yield_hi);
+        if (lane == 0) {
+            s_wcnt[wave] = __popcll(m);
+            s_wyield[wave] = y != 0ull;
+        }
         __syncthreads();
         int base = 0;
         for (int w = 0; w < wave; ++w) base += s_wcnt[w];
         const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
         if (act) s_act[base + __popcll(m & lt)] = e;
         U = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+        if (s_wyield[0] | s_wyield[1] | s_wyield[2] | s_wyield[3]) U = 0;
         __syncthreads();
     }
     const int nrc = (a.N + a.rows_per_item - 1) / a.rows_per_item;

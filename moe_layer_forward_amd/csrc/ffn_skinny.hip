@@ -1,5 +1,6 @@
-// Expert FFN for bf16 groups a little larger than a GEMV pass: a skinny MFMA
-// kernel (tokens as the 16-wide side of v_mfma_f32_16x16x32_bf16).
+// Expert FFN for bf16 groups of up to 16 rows: a skinny MFMA kernel (tokens
+// as the 16-wide side of v_mfma_f32_16x16x32_bf16) that streams each active
+// expert's weights once.
 //
 // [P1] "Colibri：专为MoE模型优化的纯C高性能推理引擎" §3.1 (w1/w3 gate and up,
 // w2 down, no bias) and §3.3 (each expert streams its weights for the tokens
@@ -9,21 +10,32 @@
 // grouped GEMM tiles 64 or 256 rows and leaves most of a 16-row tile idle.
 // Here one pass covers up to 16 tokens and the weights stream once:
 //
-//  * a persistent grid (one 512-thread block per CU) walks equal-sized work
-//    items (expert, 128-row chunk); each wave owns 16 weight rows and runs a
-//    flat stream of (item, K step of 32) steps, 8 steps of loads in flight
-//    in a register ring, continuing across item boundaries;
-//  * per step a lane loads 16 bytes of its weight row (row l%16, K = 32 g +
-//    8 (l/16) ..+7): exactly the B operand of one MFMA; the token rows come
-//    the same way as the A operand (token slot l%16 of the pass, gathered
-//    through the permutation for gate/up), from L2 - every wave of a block
-//    reads the same token fragments;
+//  * a persistent grid (one 512-thread block per CU) splits the list of work
+//    items (active expert, tile of 32 weight rows) into equal contiguous
+//    ranges, one per block;
+//  * the eight waves of a block split K: wave w takes the 128-byte lines
+//    8 i + w of every row, so a step of the block reads 1 KiB of each of the
+//    tile's rows.  Each wave keeps a ring of loads in flight that runs on
+//    across item boundaries;
+//  * every load instruction reads whole 128-byte lines (8 rows x 128 B,
+//    lane 8a + b taking piece b ^ a of row a) with the nontemporal hint.  An
+//    MFMA operand needs 16 rows x 64 B per register, i.e. half lines; loading
+//    that shape directly left the vector L1 stalling on twice as many line
+//    requests and let the nontemporal lines leave L2 before their second
+//    half was read.  So the lines go through the wave's own LDS slot and come
+//    back in operand layout (lane 16q + n: row n, piece 4s + q); the XOR
+//    swizzle keeps both the writes and the reads free of bank conflicts;
+//  * the token rows (gathered through the permutation for gate/up) take the
+//    same route as the A operand, from L2, and serve 2 (down) or 4 (gate/up)
+//    MFMAs per piece.  Blocks start their K walk at different lines so that
+//    the token rows' lines spread over the L2 channels;
 //  * the buffer range check turns loads past the last weight row, for token
 //    slots past the group and past the block's range into zeros, so no load
 //    is branched;
-//  * gate and up share each token fragment; the SwiGLU epilogue writes h
-//    (bf16), the down pass fp32 rows of y_perm; lane l holds 4 tokens of
-//    weight row l%16.
+//  * at the end of an item each wave parks its 16x16 partial tiles in LDS
+//    (double-buffered by item parity), one barrier, and the block sums the
+//    eight K-slices in a fixed order, applies the SwiGLU (gate/up: h in bf16)
+//    or stores fp32 rows of y_perm (down).
 #include <type_traits>
 
 #include "common.h"
@@ -39,11 +51,13 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kItemRows = 16 * kWaves;      // rows of one work item
+constexpr int kR = 2;                       // 16-row halves of an item
+constexpr int kTileRows = 16 * kR;          // weight rows of one item
+constexpr int kLine = 128;                  // bytes of a row one wave takes per step
+constexpr int kStepK = kWaves * kLine / 2;  // K elements one block step covers (512)
 constexpr int kPass = 16;                   // tokens of the group (at most)
-constexpr int kRing = 8;                    // steps of loads in flight
 constexpr int kMaxE = 256;
-constexpr int kMaxPairs = 64;               // experts one block's range can touch
+constexpr int kMaxPairs = 48;               // experts one block's range can touch
 constexpr uint32_t kOob = 0x80000000u;      // past any buffer: the range check yields 0
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t nbytes) {
@@ -51,6 +65,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 }
 __device__ __forceinline__ u32x4_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+// weights are read once: nontemporal, so they do not push the token rows out of L2
+__device__ __forceinline__ u32x4_t ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+
+// LDS writes complete, then a workgroup barrier; the asm statements keep the
+// compiler from moving LDS accesses across it
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 template <int I>
@@ -73,13 +100,14 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     return v;
 }
 
-// Position in the block's flat stream of (item, K step) steps; wave-uniform.
+// Position in the block's stream of (item, step) pairs; wave-uniform.
 struct Cursor {
     int idx;      // step index in the block's range
+    int i;        // step within the item
+    int item;     // items completed since the block's first
+    int tile;     // 32-row tile of the expert
     int u;        // expert slot
-    int chunk;    // 128-row chunk
-    int g;        // K step of 32
-    int c, o, e;  // rows of the group, its first dispatch row, expert id
+    int e, c, o;  // expert id, rows of the group, its first dispatch row
 };
 
 }  // namespace
@@ -97,29 +125,40 @@ struct SkArgs {
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkArgs a) {
-    constexpr int G = MODE == 0 ? 2 : 1;
+    constexpr int G = MODE == 0 ? 2 : 1;     // matrices sharing the token rows
+    constexpr int D = MODE == 0 ? 3 : 4;     // steps of loads in flight
+    constexpr int NW = kR * G * 2;           // weight load instructions per step (8-row groups)
+    constexpr int NL = NW + 2;               // + two for the 16 token slots
     __shared__ int s_act[kMaxE], s_cnt[kMaxE], s_off[kMaxE], s_ipref[kMaxE + 1], s_tot[2];
-    __shared__ uint32_t s_rows[kMaxPairs][kPass];   // token-row byte offsets of the block's experts
+    __shared__ uint32_t s_rows[kMaxPairs][kPass];                 // token-row byte offsets
+    __shared__ float s_part[2][kWaves][kR * G][4][64];            // K-slice partial tiles
+    __shared__ u32x4_t s_lt[kWaves][NL][64];                      // each wave's line transpose slot
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = a.K, N = a.N;
-    const int NG = K / 32;                                   // K steps per item (multiple of 16)
-    const int nrc = (N + kItemRows - 1) / kItemRows;
+    const int S = K / kStepK;                                // steps of an item
+    const int ntile = (N + kTileRows - 1) / kTileRows;
     const uint32_t rowb = (uint32_t)K * 2u;                  // bytes per row
 
-    // ---- the experts of this launch (lo < c <= hi) and the item prefix over them
+    // ---- the experts of this launch and the item prefix over them: every
+    // group of 1..hi rows when one of them holds more than lo, else none
     if (wave == 0) {
         int cnt[4], act[4];
         int na = 0, ni = 0;
+        bool big = false;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = 4 * lane + j;
-            const int c = e < a.E ? a.counts[e] : 0;
-            act[j] = c > a.lo && c <= a.hi;
-            cnt[j] = c;
+            cnt[j] = e < a.E ? a.counts[e] : 0;
+            big |= cnt[j] > a.lo && cnt[j] <= a.hi;
+        }
+        const bool take = __ballot(big) != 0ull;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            act[j] = take && cnt[j] > 0 && cnt[j] <= a.hi;
             na += act[j];
-            ni += act[j] ? nrc : 0;
+            ni += act[j] ? ntile : 0;
         }
         const int ia = wave_incl_scan(na, lane), ii = wave_incl_scan(ni, lane);
         int k = ia - na, p = ii - ni;
@@ -132,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkArgs a) {
                 s_off[k] = a.offsets[e];
                 s_ipref[k] = p;
                 ++k;
-                p += nrc;
+                p += ntile;
             }
         }
         if (lane == 63) {
@@ -148,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkArgs a) {
     const long ib = n_items * blockIdx.x / gridDim.x;
     const long ie = n_items * (blockIdx.x + 1) / gridDim.x;
     if (ib >= ie) return;
-    const int nsteps = (int)(ie - ib) * NG;
+    const int nsteps = (int)(ie - ib) * S;
 
     // first expert slot of the block's range; slot u0 + q is pair q of s_rows
     int u0;
@@ -175,27 +214,34 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkArgs a) {
 
     Cursor cur;
     cur.idx = 0;
+    cur.i = 0;
+    cur.item = 0;
     cur.u = u0;
-    cur.chunk = (int)(ib - s_ipref[u0]);
-    cur.g = 0;
+    cur.tile = (int)(ib - s_ipref[u0]);
     cur.e = __builtin_amdgcn_readfirstlane(s_act[u0]);
     cur.c = __builtin_amdgcn_readfirstlane(s_cnt[u0]);
     cur.o = __builtin_amdgcn_readfirstlane(s_off[u0]);
 
-    const uint32_t lq = (uint32_t)(lane >> 4);
-    const uint32_t wrow = (uint32_t)(wave * 16 + (lane & 15));
-    const uint32_t woff_l = wrow * rowb + lq * 16u;          // lane part of a weight offset
+    // load shape: lane 8a + b reads piece b ^ a of the line of row (or token) a
+    const uint32_t la = (uint32_t)lane >> 3;
+    const uint32_t lpiece = (((uint32_t)lane & 7u) ^ la) << 4;
+    const uint32_t wlane = la * rowb + lpiece;                       // lane part of a weight offset
     const uint32_t mat_bytes = (uint32_t)N * rowb;
     const uint32_t in_bytes = (uint32_t)a.in_rows * rowb;
-    // the token-row offset of this lane for the loads' cursor
-    auto arow_of = [&](int u) { return s_rows[u - u0][lane & 15] + lq * 16u; };
+    const size_t mat_elems = (size_t)N * K;
+    const int rot = (int)((blockIdx.x >> 3) % (unsigned)S);        // this block's first line
+    // operand shape: lane 16q + n wants row n, piece 4s + q: LDS slot 8 (n%8) + (piece ^ n%8)
+    // of the load of rows 8 (n/8) ..
+    const int on = lane & 15, oq = lane >> 4, oa = on & 7, og = on >> 3;
+    auto tok_of = [&](int u, int g) { return s_rows[u - u0][8 * g + (int)la] + lpiece; };
 
     auto advance = [&](Cursor& q) {
         ++q.idx;
-        if (++q.g < NG) return;
-        q.g = 0;
-        if (++q.chunk < nrc) return;
-        q.chunk = 0;
+        if (++q.i < S) return;
+        q.i = 0;
+        ++q.item;
+        if (++q.tile < ntile) return;
+        q.tile = 0;
         if (++q.u < U) {
             q.e = __builtin_amdgcn_readfirstlane(s_act[q.u]);
             q.c = __builtin_amdgcn_readfirstlane(s_cnt[q.u]);
@@ -203,74 +249,116 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkArgs a) {
         }
     };
 
-    u32x4_t xa[kRing], wq[kRing][G];
-    uint32_t l_arow = arow_of(cur.u);
-    auto issue = [&](Cursor& q, auto slot) {
-        constexpr int S = decltype(slot)::value;
+    // ring slot: [0, NW) weights, instruction (h G + m) 2 + g for rows 16 h + 8 g ..;
+    // NW + g the token slots 8 g ..
+    u32x4_t ring[D][NL];
+    uint32_t l_tok0 = tok_of(cur.u, 0), l_tok1 = tok_of(cur.u, 1);
+    auto issue = [&](Cursor& q, auto slot) __attribute__((always_inline)) {
+        constexpr int SL = decltype(slot)::value;
         const bool live = q.idx < nsteps;
-        const uint32_t ko = (uint32_t)q.g * 64u;
-        // past the block's range (or a slot index beyond the experts): zeros
-        xa[S] = ld16(rsrc(a.in, live ? in_bytes : 0u), l_arow + ko);
-        const uint32_t wo = woff_l + (uint32_t)q.chunk * kItemRows * rowb + ko;
+        int pc = q.i + rot;
+        if (pc >= S) pc -= S;
+        const uint32_t kb = (uint32_t)(pc * kWaves + wave) * (uint32_t)kLine;
+        // past the block's range: zeros
+        const auto ri = rsrc(a.in, live ? in_bytes : 0u);
+        ring[SL][NW] = ld16(ri, l_tok0 + kb);
+        ring[SL][NW + 1] = ld16(ri, l_tok1 + kb);
+        const uint32_t wo = (uint32_t)q.tile * kTileRows * rowb + wlane + kb;
+        const size_t eo = (size_t)(live ? q.e : 0) * mat_elems;
 #pragma unroll
         for (int m = 0; m < G; ++m) {
-            const uint16_t* w = (m == 0 ? a.w0 : a.w1) + (size_t)(live ? q.e : 0) * N * K;
-            wq[S][m] = ld16(rsrc(w, live ? mat_bytes : 0u), wo);
+            const auto r = rsrc((m == 0 ? a.w0 : a.w1) + eo, live ? mat_bytes : 0u);
+#pragma unroll
+            for (int h = 0; h < kR; ++h)
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+                    ring[SL][(h * G + m) * 2 + g] = ld16_nt(r, wo + (uint32_t)(16 * h + 8 * g) * rowb);
         }
         const int u = q.u;
         advance(q);
-        if (q.u != u && q.u < U && q.u - u0 < kMaxPairs) l_arow = arow_of(q.u);
+        if (q.u != u && q.u < U && q.u - u0 < kMaxPairs) {
+            l_tok0 = tok_of(q.u, 0);
+            l_tok1 = tok_of(q.u, 1);
+        }
     };
 
-    floatx4 acc[G];
+    floatx4 acc[kR][G];
 #pragma unroll
-    for (int m = 0; m < G; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-    auto compute = [&](auto slot) {
-        constexpr int S = decltype(slot)::value;
+    for (int h = 0; h < kR; ++h)
 #pragma unroll
-        for (int m = 0; m < G; ++m)
-            acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[S]),
-                                                             __builtin_bit_cast(bf16x8_t, wq[S][m]),
-                                                             acc[m], 0, 0, 0);
-    };
-    // C layout: lane l holds weight row l%16 of its wave's 16 and tokens 4 (l/16) + v
-    auto epilogue = [&](const Cursor& q) {
-        const int n = q.chunk * kItemRows + wave * 16 + (lane & 15);
-        if (n < N) {
+        for (int m = 0; m < G; ++m) acc[h][m] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // lines -> LDS -> operands, then two K pieces of 32 x (kR halves x G matrices)
+    auto compute = [&](auto slot) __attribute__((always_inline)) {
+        constexpr int SL = decltype(slot)::value;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int t = (int)lq * 4 + v;
-                if (t < q.c) {
-                    const size_t oi = (size_t)(q.o + t) * N + n;
-                    if constexpr (MODE == 0)
-                        reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(silu(acc[0][v]) * acc[1][v]);
-                    else
-                        reinterpret_cast<float*>(a.out)[oi] = acc[0][v];
+        for (int j = 0; j < NL; ++j) s_lt[wave][j][lane] = ring[SL][j];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int sw = 8 * oa + ((4 * s + oq) ^ oa);
+            const u32x4_t xa = s_lt[wave][NW + og][sw];
+#pragma unroll
+            for (int h = 0; h < kR; ++h)
+#pragma unroll
+                for (int m = 0; m < G; ++m) {
+                    const u32x4_t wb = s_lt[wave][(h * G + m) * 2 + og][sw];
+                    acc[h][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa),
+                                                                        __builtin_bit_cast(bf16x8_t, wb),
+                                                                        acc[h][m], 0, 0, 0);
                 }
-            }
         }
-#pragma unroll
-        for (int m = 0; m < G; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
     };
+    // C layout: lane l holds weight row l%16 of its half and tokens 4 (l/16) + v.
+    // The eight K-slice partials meet in LDS and are summed in wave order.
+    auto finish = [&](const Cursor& q) __attribute__((always_inline)) {
+        float (*P)[kR * G][4][64] = s_part[q.item & 1];
+#pragma unroll
+        for (int h = 0; h < kR; ++h)
+#pragma unroll
+            for (int m = 0; m < G; ++m) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) P[wave][h * G + m][v][lane] = acc[h][m][v];
+                acc[h][m] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+        lds_barrier();
+        // kR * 256 outputs, one per thread (kR * 256 == kThreads)
+        const int h = tid >> 8, v = (tid >> 6) & 3;
+        float s[G];
+#pragma unroll
+        for (int m = 0; m < G; ++m) s[m] = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+            for (int m = 0; m < G; ++m) s[m] += P[w][h * G + m][v][lane];
+        const int t = oq * 4 + v;
+        const int n = q.tile * kTileRows + h * 16 + on;
+        if (t < q.c && n < N) {
+            const size_t oi = (size_t)(q.o + t) * N + n;
+            if constexpr (MODE == 0)
+                reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(silu(s[0]) * s[1]);
+            else
+                reinterpret_cast<float*>(a.out)[oi] = s[0];
+        }
+    };
+    static_assert(kR * 256 == kThreads, "one output per thread");
 
     Cursor L = cur;        // next step whose loads go out
     Cursor C = cur;        // step being multiplied
-    static_for<0, kRing>([&](auto k) { issue(L, k); });
-    auto step = [&](auto kk) {
+    static_for<0, D>([&](auto k) { issue(L, k); });
+    auto step = [&](auto kk) __attribute__((always_inline)) {
         constexpr int k = decltype(kk)::value;
-        compute(ic<k % kRing>{});
-        if (C.g == NG - 1) epilogue(C);
+        // steps past the range multiply zeros; only real item ends finish
+        compute(ic<k>{});
+        if (C.i == S - 1 && C.idx < nsteps) finish(C);
         advance(C);
-        issue(L, ic<k % kRing>{});
+        issue(L, ic<k>{});
     };
-    // nsteps is a multiple of 16 (NG is)
-    for (int n = nsteps >> 4; n > 0; --n) static_for<0, 16>(step);
+    for (int n = (nsteps + D - 1) / D; n > 0; --n) static_for<0, D>(step);
 }
 
 bool skinny_supported(int K, int N, int in_rows) {
-    if (K % 512 != 0 || K <= 0 || N <= 0 || in_rows < 0) return false;
-    // 32-bit buffer offsets: a weight matrix with its padded last chunk, the inputs
-    return (size_t)(N + kItemRows) * (size_t)K * 2 < ((size_t)1 << 31) &&
+    if (K % kStepK != 0 || K <= 0 || N <= 0 || in_rows < 0) return false;
+    // 32-bit buffer offsets: a weight matrix with its padded last tile, the inputs
+    return (size_t)(N + kTileRows) * (size_t)K * 2 < ((size_t)1 << 31) &&
            (size_t)in_rows * (size_t)K * 2 < ((size_t)1 << 31);
 }
 
@@ -301,9 +389,9 @@ hipError_t launch_skinny(int mode, const void* w0, const void* w1, const void* i
         (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
         if (n_cu < 1) n_cu = 256;
     }
-    // a block's range touches at most ceil(E / n_cu) + 1 experts' first
-    // chunks plus the experts it spans; kMaxPairs bounds that for E <= 256
-    // and n_cu >= 8
+    // a block's range of ceil(items / grid) items touches at most
+    // U / grid + 3 experts (each expert owns >= 1 item): kMaxPairs bounds
+    // that for E <= 256 and a grid of >= 8 blocks
     if (n_cu < 8) return hipErrorInvalidValue;
     if (mode == 0)
         hipLaunchKernelGGL(skinny_kernel<0>, dim3(n_cu), dim3(kThreads), 0, s, a);

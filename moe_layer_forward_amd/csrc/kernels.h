@@ -19,6 +19,9 @@ struct GemvArgs {
     const int32_t* offsets;
     const int32_t* perm;     // mode 0 only: token = perm[p] / topk
     int N, K, topk, T, E, tau, rows_per_item;
+    // > 0: the kernel serves no group at all when some group holds
+    // tau < c <= yield_hi rows (the skinny MFMA kernel then takes them all)
+    int yield_hi;
 };
 
 hipError_t launch_route(int act, const void* x, const float* wg, const float* b, float* logits,

@@ -47,14 +47,19 @@ SMALL = {
         "int4_mfma_many", T=8, d=1024, E=256, k=8, F=1024, act="bf16", wt="int4",
         model="s_int4_many", n_shared=1, w_std=0.05),
     # bf16 groups of 9-16 rows on the skinny MFMA kernel beside the GEMV (<= 8
-    # rows) and the MFMA tiles (> 16 rows); N = 1600 leaves a partial last chunk
-    # (and K = 1600 keeps the down pass off the skinny kernel)
+    # rows) and the MFMA tiles (> 16 rows).  The skinny kernel needs K % 256 == 0
+    # and works in tiles of 32 weight rows: F = 1616 leaves a half last tile in
+    # gate/up (and keeps down off the kernel); d = 1040 keeps gate/up off and
+    # leaves a half last tile in down
     "bf16_skinny_mix": moe_inputs.MoEConfig(
         "bf16_skinny_mix", T=40, d=1024, E=8, k=2, F=1536, act="bf16", wt="bf16",
         model="s_bf16_sk", w_std=0.05),
     "bf16_skinny_ragged": moe_inputs.MoEConfig(
-        "bf16_skinny_ragged", T=24, d=1024, E=4, k=2, F=1600, act="bf16", wt="bf16",
+        "bf16_skinny_ragged", T=24, d=1024, E=4, k=2, F=1616, act="bf16", wt="bf16",
         model="s_bf16_skr", w_std=0.05),
+    "bf16_skinny_down_ragged": moe_inputs.MoEConfig(
+        "bf16_skinny_down_ragged", T=24, d=1040, E=4, k=2, F=1536, act="bf16", wt="bf16",
+        model="s_bf16_skd", w_std=0.05),
     "f32_ragged": moe_inputs.MoEConfig(
         "f32_ragged", T=37, d=200, E=5, k=3, F=72, act="f32", wt="f32", model="s_f32"),
 }
