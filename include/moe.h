@@ -67,9 +67,14 @@ typedef enum {
  *   act: dtype of x, residual and y (MOE_F32 or MOE_BF16).
  *   wt:  dtype of expert weights (MOE_F32 with act F32; MOE_BF16 or
  *        MOE_INT4_G128 with act BF16).
- *   tau: expert groups with at most tau rows run the HBM-streaming GEMV, larger
- *        groups the MFMA grouped GEMM (bf16 weights only; fp32 and int4 always
- *        use the GEMV).  0 selects the default (16); negative forces the GEMV.
+ *   tau: bf16 expert groups with at most tau rows run the HBM-streaming
+ *        kernels (the GEMV, or, when some group is larger than one GEMV pass,
+ *        the skinny MFMA kernel, which covers up to 32 rows and needs d and F
+ *        multiples of 512), larger groups the MFMA grouped GEMM.  0 selects
+ *        the default: 32 where the skinny kernel serves both projections,
+ *        else 16.  Negative forces the GEMV for every group.  fp32 and int4
+ *        weights ignore tau (GEMV; int4 with K a multiple of 1024 on the
+ *        matrix cores).
  * Limits (MOE_EINVAL otherwise): T >= 0, 1 <= k <= E <= 256, k <= 16,
  *   d, F >= 8 and multiples of 8; int4: d and F multiples of 128.
  * Limits of this build (MOE_EUNSUPPORTED otherwise): d, F <= 16384 (bf16),

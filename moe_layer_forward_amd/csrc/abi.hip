@@ -148,10 +148,17 @@ Layout layout(const moe_shape* s) {
     return L;
 }
 
+// the skinny MFMA kernel can serve both projections of this shape
+bool skinny_applies(const moe_shape* s) {
+    return s->wt == MOE_BF16 && s->act == MOE_BF16 && skinny_supported(s->d, s->F, s->T) &&
+           skinny_supported(s->F, s->d, s->T * s->k);
+}
+
 int effective_tau(const moe_shape* s) {
     if (s->wt != MOE_BF16) return -1;      // fp32 and int4: GEMV for every group
     if (s->tau < 0) return -1;
-    return s->tau == 0 ? kDefaultTau : s->tau;
+    if (s->tau == 0) return skinny_applies(s) ? kSkinnyMaxRows : kDefaultTau;
+    return s->tau;
 }
 
 // The FFN launch sequence shared by moe_expert_ffn and moe_layer_forward.
@@ -189,16 +196,16 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
     const bool tiled = s->wt == MOE_INT4_G128_TILED;
     // bf16 groups below the MFMA tiles: when one of them is larger than a
-    // GEMV pass (lo rows), the skinny MFMA kernel (one pass of up to 16
+    // GEMV pass (lo rows), the skinny MFMA kernel (one pass of up to 32
     // tokens) takes every group below the tiles in one balanced launch and
     // the GEMV stands aside; otherwise the GEMV serves them.  Both kernels
     // decide from the counts on the device.  The skinny kernel is only
     // launched when such a group can occur: a group holds at most T rows, and
-    // everything below the tiles must fit one skinny pass (tau <= 16); a
+    // everything below the tiles must fit one skinny pass (tau <= 32); a
     // negative tau keeps the GEMV for all
     const int tau_m = use_mfma ? tau : s->T;                   // largest group below the tiles
     auto skinny_lo = [&](int mode, int K, int N, int in_rows) -> int {
-        if (s->wt != MOE_BF16 || s->act != MOE_BF16 || s->tau < 0 || tau_m > 16 ||
+        if (s->wt != MOE_BF16 || s->act != MOE_BF16 || s->tau < 0 || tau_m > kSkinnyMaxRows ||
             !skinny_supported(K, N, in_rows))
             return -1;
         const int lo = gemv_pass_tokens(s->wt, mode, K);

@@ -55,7 +55,7 @@ constexpr int kR = 2;                       // 16-row halves of an item
 constexpr int kTileRows = 16 * kR;          // weight rows of one item
 constexpr int kLine = 128;                  // bytes of a row one wave takes per step
 constexpr int kStepK = kWaves * kLine / 2;  // K elements one block step covers (512)
-constexpr int kPass = 16;                   // tokens of the group (at most)
+constexpr int kTok = 16;                    // tokens of one token tile
 constexpr int kMaxE = 256;
 constexpr int kMaxPairs = 48;               // experts one block's range can touch
 constexpr uint32_t kOob = 0x80000000u;      // past any buffer: the range check yields 0
@@ -120,19 +120,27 @@ struct SkArgs {
     const int32_t* counts;
     const int32_t* offsets;
     const int32_t* perm;       // mode 0: token of dispatch row p = perm[p] / topk
-    int N, K, topk, E, lo, hi, in_rows;
+    int N, K, topk, E, in_rows;
+    int lo, cap;               // this launch: see skinny_kernel
 };
 
-template <int MODE>
+// TT token tiles of 16: the launch serves every group of 1..cap rows when
+// the largest of them holds lo < M <= 16 TT rows, else nothing (the GEMV or
+// the launch with the other TT serves them).
+template <int MODE, int TT>
 __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkArgs a) {
     constexpr int G = MODE == 0 ? 2 : 1;     // matrices sharing the token rows
     constexpr int D = MODE == 0 ? 3 : 4;     // steps of loads in flight
     constexpr int NW = kR * G * 2;           // weight load instructions per step (8-row groups)
-    constexpr int NL = NW + 2;               // + two for the 16 token slots
+    constexpr int NT = 2 * TT;               // token load instructions per step (8-token groups)
+    constexpr int NL = NW + NT;
+    constexpr int NP = TT * kR * G;          // 16x16 partial tiles per wave
+    constexpr int NB = TT == 1 ? 2 : 1;      // partial buffers (one more barrier per item with one)
     __shared__ int s_act[kMaxE], s_cnt[kMaxE], s_off[kMaxE], s_ipref[kMaxE + 1], s_tot[2];
-    __shared__ uint32_t s_rows[kMaxPairs][kPass];                 // token-row byte offsets
-    __shared__ float s_part[2][kWaves][kR * G][4][64];            // K-slice partial tiles
-    __shared__ u32x4_t s_lt[kWaves][NL][64];                      // each wave's line transpose slot
+    __shared__ uint32_t s_rows[kMaxPairs][kTok * TT];             // token-row byte offsets
+    __shared__ float s_part[NB][kWaves][NP][4][64];               // K-slice partial tiles
+    // each wave's line transpose slot: one 16-row half's G x 2 weight loads, then the tokens
+    __shared__ u32x4_t s_lt[kWaves][2 * G + NT][64];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -141,22 +149,22 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkArgs a) {
     const int ntile = (N + kTileRows - 1) / kTileRows;
     const uint32_t rowb = (uint32_t)K * 2u;                  // bytes per row
 
-    // ---- the experts of this launch and the item prefix over them: every
-    // group of 1..hi rows when one of them holds more than lo, else none
+    // ---- the experts of this launch and the item prefix over them
     if (wave == 0) {
         int cnt[4], act[4];
-        int na = 0, ni = 0;
-        bool big = false;
+        int na = 0, ni = 0, big = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = 4 * lane + j;
             cnt[j] = e < a.E ? a.counts[e] : 0;
-            big |= cnt[j] > a.lo && cnt[j] <= a.hi;
+            if (cnt[j] <= a.cap && cnt[j] > big) big = cnt[j];
         }
-        const bool take = __ballot(big) != 0ull;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) big = max(big, __shfl_xor(big, o, 64));
+        const bool take = big > a.lo && big <= kTok * TT;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            act[j] = take && cnt[j] > 0 && cnt[j] <= a.hi;
+            act[j] = take && cnt[j] > 0 && cnt[j] <= a.cap;
             na += act[j];
             ni += act[j] ? ntile : 0;
         }
@@ -200,8 +208,8 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkArgs a) {
         u0 = lo;
     }
     // token-row byte offsets of the (at most kMaxPairs) experts of the range
-    for (int t = tid; t < kMaxPairs * kPass; t += kThreads) {
-        const int q = t / kPass, ts = t % kPass, u = u0 + q;
+    for (int t = tid; t < kMaxPairs * kTok * TT; t += kThreads) {
+        const int q = t / (kTok * TT), ts = t % (kTok * TT), u = u0 + q;
         uint32_t off = kOob;
         if (u < U && ts < s_cnt[u]) {
             const int p = s_off[u] + ts;
@@ -252,7 +260,9 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkArgs a) {
     // ring slot: [0, NW) weights, instruction (h G + m) 2 + g for rows 16 h + 8 g ..;
     // NW + g the token slots 8 g ..
     u32x4_t ring[D][NL];
-    uint32_t l_tok0 = tok_of(cur.u, 0), l_tok1 = tok_of(cur.u, 1);
+    uint32_t l_tok[NT];
+#pragma unroll
+    for (int g = 0; g < NT; ++g) l_tok[g] = tok_of(cur.u, g);
     auto issue = [&](Cursor& q, auto slot) __attribute__((always_inline)) {
         constexpr int SL = decltype(slot)::value;
         const bool live = q.idx < nsteps;
@@ -261,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkArgs a) {
         const uint32_t kb = (uint32_t)(pc * kWaves + wave) * (uint32_t)kLine;
         // past the block's range: zeros
         const auto ri = rsrc(a.in, live ? in_bytes : 0u);
-        ring[SL][NW] = ld16(ri, l_tok0 + kb);
-        ring[SL][NW + 1] = ld16(ri, l_tok1 + kb);
+#pragma unroll
+        for (int g = 0; g < NT; ++g) ring[SL][NW + g] = ld16(ri, l_tok[g] + kb);
         const uint32_t wo = (uint32_t)q.tile * kTileRows * rowb + wlane + kb;
         const size_t eo = (size_t)(live ? q.e : 0) * mat_elems;
 #pragma unroll
@@ -277,67 +287,87 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_kernel(SkArgs a) {
         const int u = q.u;
         advance(q);
         if (q.u != u && q.u < U && q.u - u0 < kMaxPairs) {
-            l_tok0 = tok_of(q.u, 0);
-            l_tok1 = tok_of(q.u, 1);
+#pragma unroll
+            for (int g = 0; g < NT; ++g) l_tok[g] = tok_of(q.u, g);
         }
     };
 
-    floatx4 acc[kR][G];
+    floatx4 acc[TT][kR][G];
 #pragma unroll
-    for (int h = 0; h < kR; ++h)
+    for (int t = 0; t < TT; ++t)
 #pragma unroll
-        for (int m = 0; m < G; ++m) acc[h][m] = floatx4{0.f, 0.f, 0.f, 0.f};
-    // lines -> LDS -> operands, then two K pieces of 32 x (kR halves x G matrices)
+        for (int h = 0; h < kR; ++h)
+#pragma unroll
+            for (int m = 0; m < G; ++m) acc[t][h][m] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // lines -> LDS -> operands: the token tiles first, then one 16-row half at
+    // a time (the wave's LDS accesses run in order, so the half's slot is free
+    // again once its operands are read); two K pieces of 32 per step
     auto compute = [&](auto slot) __attribute__((always_inline)) {
         constexpr int SL = decltype(slot)::value;
+        u32x4_t xa[2][TT];
 #pragma unroll
-        for (int j = 0; j < NL; ++j) s_lt[wave][j][lane] = ring[SL][j];
+        for (int g = 0; g < NT; ++g) s_lt[wave][2 * G + g][lane] = ring[SL][NW + g];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int sw = 8 * oa + ((4 * s + oq) ^ oa);
-            const u32x4_t xa = s_lt[wave][NW + og][sw];
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int h = 0; h < kR; ++h)
+            for (int t = 0; t < TT; ++t) xa[s][t] = s_lt[wave][2 * G + 2 * t + og][8 * oa + ((4 * s + oq) ^ oa)];
+#pragma unroll
+        for (int h = 0; h < kR; ++h) {
+#pragma unroll
+            for (int j = 0; j < 2 * G; ++j) s_lt[wave][j][lane] = ring[SL][h * 2 * G + j];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int sw = 8 * oa + ((4 * s + oq) ^ oa);
 #pragma unroll
                 for (int m = 0; m < G; ++m) {
-                    const u32x4_t wb = s_lt[wave][(h * G + m) * 2 + og][sw];
-                    acc[h][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa),
-                                                                        __builtin_bit_cast(bf16x8_t, wb),
-                                                                        acc[h][m], 0, 0, 0);
+                    const u32x4_t wb = s_lt[wave][m * 2 + og][sw];
+#pragma unroll
+                    for (int t = 0; t < TT; ++t)
+                        acc[t][h][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[s][t]),
+                                                                               __builtin_bit_cast(bf16x8_t, wb),
+                                                                               acc[t][h][m], 0, 0, 0);
                 }
+            }
         }
     };
     // C layout: lane l holds weight row l%16 of its half and tokens 4 (l/16) + v.
     // The eight K-slice partials meet in LDS and are summed in wave order.
     auto finish = [&](const Cursor& q) __attribute__((always_inline)) {
-        float (*P)[kR * G][4][64] = s_part[q.item & 1];
+        float (*P)[NP][4][64] = s_part[NB == 2 ? (q.item & 1) : 0];
 #pragma unroll
-        for (int h = 0; h < kR; ++h)
+        for (int t = 0; t < TT; ++t)
 #pragma unroll
-            for (int m = 0; m < G; ++m) {
+            for (int h = 0; h < kR; ++h)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) P[wave][h * G + m][v][lane] = acc[h][m][v];
-                acc[h][m] = floatx4{0.f, 0.f, 0.f, 0.f};
-            }
+                for (int m = 0; m < G; ++m) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) P[wave][(t * kR + h) * G + m][v][lane] = acc[t][h][m][v];
+                    acc[t][h][m] = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
         lds_barrier();
-        // kR * 256 outputs, one per thread (kR * 256 == kThreads)
+        // TT x kR x 256 outputs, TT per thread (kR * 256 == kThreads)
         const int h = tid >> 8, v = (tid >> 6) & 3;
-        float s[G];
-#pragma unroll
-        for (int m = 0; m < G; ++m) s[m] = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-            for (int m = 0; m < G; ++m) s[m] += P[w][h * G + m][v][lane];
-        const int t = oq * 4 + v;
         const int n = q.tile * kTileRows + h * 16 + on;
-        if (t < q.c && n < N) {
-            const size_t oi = (size_t)(q.o + t) * N + n;
-            if constexpr (MODE == 0)
-                reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(silu(s[0]) * s[1]);
-            else
-                reinterpret_cast<float*>(a.out)[oi] = s[0];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            float s[G];
+#pragma unroll
+            for (int m = 0; m < G; ++m) s[m] = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+                for (int m = 0; m < G; ++m) s[m] += P[w][(tt * kR + h) * G + m][v][lane];
+            const int t = kTok * tt + oq * 4 + v;
+            if (t < q.c && n < N) {
+                const size_t oi = (size_t)(q.o + t) * N + n;
+                if constexpr (MODE == 0)
+                    reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16(silu(s[0]) * s[1]);
+                else
+                    reinterpret_cast<float*>(a.out)[oi] = s[0];
+            }
         }
+        // one buffer: every wave has read it before any wave writes the next item's
+        if constexpr (NB == 1) lds_barrier();
     };
     static_assert(kR * 256 == kThreads, "one output per thread");
 
@@ -364,7 +394,7 @@ bool skinny_supported(int K, int N, int in_rows) {
 
 hipError_t launch_skinny(int mode, const void* w0, const void* w1, const void* in, int in_rows, void* out,
                          const int32_t* counts, const int32_t* offsets, const int32_t* perm, int N, int K,
-                         int topk, int E, int lo, int hi, hipStream_t s) {
+                         int topk, int E, int lo, int cap, hipStream_t s) {
     SkArgs a;
     a.w0 = reinterpret_cast<const uint16_t*>(w0);
     a.w1 = reinterpret_cast<const uint16_t*>(w1);
@@ -377,10 +407,9 @@ hipError_t launch_skinny(int mode, const void* w0, const void* w1, const void* i
     a.K = K;
     a.topk = topk;
     a.E = E;
-    a.lo = lo;
-    a.hi = hi < kPass ? hi : kPass;
     a.in_rows = in_rows;
-    if (E > kMaxE || !skinny_supported(K, N, in_rows) || !counts || !offsets || (mode == 0 && !perm))
+    if (E > kMaxE || !skinny_supported(K, N, in_rows) || !counts || !offsets || (mode == 0 && !perm) ||
+        lo < 0 || cap <= lo || cap > kSkinnyMaxRows)
         return hipErrorInvalidValue;
     static int n_cu = 0;
     if (n_cu == 0) {
@@ -393,10 +422,23 @@ hipError_t launch_skinny(int mode, const void* w0, const void* w1, const void* i
     // U / grid + 3 experts (each expert owns >= 1 item): kMaxPairs bounds
     // that for E <= 256 and a grid of >= 8 blocks
     if (n_cu < 8) return hipErrorInvalidValue;
-    if (mode == 0)
-        hipLaunchKernelGGL(skinny_kernel<0>, dim3(n_cu), dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(skinny_kernel<1>, dim3(n_cu), dim3(kThreads), 0, s, a);
+    // one token tile when the largest group holds lo < M <= 16 rows, two when
+    // 16 < M <= 32; the launch whose range M misses returns at once
+    a.cap = cap;
+    if (lo < kTok) {
+        a.lo = lo;
+        if (mode == 0)
+            hipLaunchKernelGGL((skinny_kernel<0, 1>), dim3(n_cu), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((skinny_kernel<1, 1>), dim3(n_cu), dim3(kThreads), 0, s, a);
+    }
+    if (cap > kTok) {
+        a.lo = lo > kTok ? lo : kTok;
+        if (mode == 0)
+            hipLaunchKernelGGL((skinny_kernel<0, 2>), dim3(n_cu), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((skinny_kernel<1, 2>), dim3(n_cu), dim3(kThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -46,11 +46,11 @@ SMALL = {
     "int4_mfma_many": moe_inputs.MoEConfig(
         "int4_mfma_many", T=8, d=1024, E=256, k=8, F=1024, act="bf16", wt="int4",
         model="s_int4_many", n_shared=1, w_std=0.05),
-    # bf16 groups of 9-16 rows on the skinny MFMA kernel beside the GEMV (<= 8
-    # rows) and the MFMA tiles (> 16 rows).  The skinny kernel needs K % 256 == 0
-    # and works in tiles of 32 weight rows: F = 1616 leaves a half last tile in
-    # gate/up (and keeps down off the kernel); d = 1040 keeps gate/up off and
-    # leaves a half last tile in down
+    # bf16 groups of 5-16 rows (counts 10 10 9 5 13 8 10 15): one group above a
+    # GEMV pass sends every group to the one-tile skinny MFMA kernel.  It needs
+    # K % 512 == 0 and works in tiles of 32 weight rows: F = 1616 leaves a half
+    # last tile in gate/up (and keeps down off the kernel); d = 1040 keeps
+    # gate/up off and leaves a half last tile in down
     "bf16_skinny_mix": moe_inputs.MoEConfig(
         "bf16_skinny_mix", T=40, d=1024, E=8, k=2, F=1536, act="bf16", wt="bf16",
         model="s_bf16_sk", w_std=0.05),
@@ -60,6 +60,15 @@ SMALL = {
     "bf16_skinny_down_ragged": moe_inputs.MoEConfig(
         "bf16_skinny_down_ragged", T=24, d=1040, E=4, k=2, F=1536, act="bf16", wt="bf16",
         model="s_bf16_skd", w_std=0.05),
+    # two token tiles (groups of 17-32 rows): counts 14 12 19 16 17 18, so the
+    # two-tile launch takes every group; with groups above 32 (35 39 39 18 29)
+    # those run on the MFMA tiles beside it
+    "bf16_skinny2": moe_inputs.MoEConfig(
+        "bf16_skinny2", T=48, d=1024, E=6, k=2, F=1536, act="bf16", wt="bf16",
+        model="s_bf16_sk2", w_std=0.05),
+    "bf16_skinny2_mix": moe_inputs.MoEConfig(
+        "bf16_skinny2_mix", T=80, d=1024, E=5, k=2, F=1536, act="bf16", wt="bf16",
+        model="s_bf16_sk2", w_std=0.05),
     "f32_ragged": moe_inputs.MoEConfig(
         "f32_ragged", T=37, d=200, E=5, k=3, F=72, act="f32", wt="f32", model="s_f32"),
 }
@@ -460,10 +469,36 @@ def test_mfma_ceiling_runs():
 
 
 def test_skinny_groups_exercised(orc):
-    """The mixed config really has groups on all three bf16 paths."""
-    cfg = SMALL["bf16_skinny_mix"]
+    """The skinny configs really have the group sizes their comments claim."""
+    for name, check in [("bf16_skinny_mix", lambda c: ((c > 8) & (c <= 16)).any() and (c <= 8).any()
+                         and (c <= 16).all()),
+                        ("bf16_skinny2", lambda c: ((c > 16) & (c <= 32)).any() and (c <= 16).any()
+                         and (c <= 32).all()),
+                        ("bf16_skinny2_mix", lambda c: ((c > 16) & (c <= 32)).any() and (c > 32).any())]:
+        cfg = SMALL[name]
+        d = device_inputs(cfg)
+        _, counts, _ = run_layer(cfg, d)
+        c = counts.cpu().numpy()
+        say(f"  {name} counts {c.tolist()}")
+        assert check(c), name
+
+
+def test_skinny_two_tiles_ragged(orc):
+    """Two token tiles with a half last weight tile: F = 1616 (N % 32 == 16 in
+    gate/up) and an explicit tau of 32 (the default drops to 16 because the
+    down pass, K = 1616, cannot use the kernel; down then runs on the GEMV)."""
+    cfg = moe_inputs.MoEConfig("bf16_skinny2_ragged", T=56, d=1024, E=6, k=2, F=1616, act="bf16",
+                               wt="bf16", model="s_bf16_sk2r", w_std=0.05)
     d = device_inputs(cfg)
-    _, counts, _ = run_layer(cfg, d)
+    y, counts, idx = run_layer(cfg, d, tau=32)
     c = counts.cpu().numpy()
     say(f"  counts {c.tolist()}")
-    assert (c > 8).any() and ((c > 8) & (c <= 16)).any()
+    assert ((c > 16) & (c <= 32)).any() and (c <= 32).all()
+    W, S = oracle_weights(d)
+    x = np_store(d["x"])
+    wr, br = np_store(d["w_router"]), np_store(d["b_router"])
+    gi = idx.cpu().numpy()
+    y_f, _, _, _ = orc.layer_forward(x, cfg.act, cfg.wt, cfg.k, wr, br, W, S, forced_idx=gi)
+    err = tokenwise_rel(np_f64(y), y_f)
+    say(f"  max rel {err.max():.3g}")
+    assert err.max() < TOL[cfg.wt]
