@@ -10,8 +10,9 @@ timed region.  The headline is the Mixtral-8x7B-shaped decode layer (T=8); the
 prefill layer (T=4096, Zipf-loaded experts) runs on the same weights and is
 reported in the same JSON line.
 
-Roofline: the dominant step is the expert FFN (the GEMV gate/up and down
-kernels at decode, the MFMA gate/up and down kernels at prefill).  Its time is
+Roofline: the dominant step is the expert FFN (the GEMV or skinny MFMA gate/up
+and down kernels at decode, the MFMA gate/up and down kernels at prefill; the
+bench line names the kernels the group sizes select).  Its time is
 measured live with HIP events recorded on the library's stream around the
 moe_expert_ffn call; its algorithmic bytes are the weight bytes of the experts
 actually hit (batch union) plus the activation traffic, its algorithmic flops
@@ -247,6 +248,36 @@ def mfma_ceiling(iters=40000, reps=3):
     return flops / (ms * 1e-3) / 1e12, cyc / (ticks / 100e6) / 1e9
 
 
+def ffn_paths(cfg, counts, tau):
+    """Which kernels the layer's FFN step runs, from the group sizes (the same
+    rule the library applies on the device): bf16 groups above tau take the
+    MFMA tiles; below it, when the largest group exceeds one GEMV pass, the
+    skinny MFMA kernel (one 16-token tile up to 16 rows, two up to 32) takes
+    them all, else the GEMV."""
+    if cfg.wt == "int4":
+        return "int4 skinny MFMA" if cfg.d % 1024 == 0 and cfg.F % 1024 == 0 else "int4 GEMV"
+    if cfg.wt != "bf16" or tau < 0:
+        return "GEMV"
+    skinny = cfg.act == "bf16" and cfg.d % 512 == 0 and cfg.F % 512 == 0
+    t = tau if tau > 0 else (32 if skinny else 16)
+    c = [int(v) for v in counts if v > 0]
+    small = [v for v in c if v <= t]
+    parts = []
+    for name, K in (("gate/up", cfg.d), ("down", cfg.F)):
+        npass = 8 if K <= 8192 else (2 if name == "gate/up" else 4)   # GEMV tokens per pass
+        p = []
+        if small:
+            m = max(small)
+            if skinny and t <= 32 and m > npass:
+                p.append("skinny MFMA, %d token tile%s" % ((1, "") if m <= 16 else (2, "s")))
+            else:
+                p.append("GEMV")
+        if any(v > t for v in c):
+            p.append("MFMA tiles")
+        parts.append(f"{name}: " + " + ".join(p))
+    return "; ".join(parts)
+
+
 def roofline_obj(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -300,6 +331,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tau", type=int, default=0)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload with this many tokens instead of its own T "
+                         "(the config is named <workload>_t<tokens>)")
     ap.add_argument("--int4-layout", choices=["tiled", "row-major"], default="tiled",
                     help="int4 code layout the layer streams (tiled: packed once with "
                          "moe_pack_int4_tiled before timing; needs d, F multiples of 1024)")
@@ -333,6 +367,8 @@ def main():
     cfg = moe_inputs.CONFIGS[name]
     if cfg.layers > 1:
         cfg = cfg.replace(layers=1)
+    if args.tokens > 0:
+        cfg = cfg.replace(name=f"{cfg.name}_t{args.tokens}", T=args.tokens)
     log(f"generating {cfg.name} inputs on the GPU")
     x, wr, br, W = device_layer(cfg)
     wt = cfg.wt
@@ -365,10 +401,7 @@ def main():
                                  # counters were taken on the default run (tiled int4 codes)
                                  measured_traffic(cfg.name)
                                  if args.tau == 0 and (cfg.wt != "int4" or wt == "int4_tiled") else None),
-                    kernel=("expert FFN step (gate/up + down, 64-row MFMA tiles)"
-                            if cfg.wt == "bf16" and args.tau >= 0 and cfg.T * cfg.k / max(U, 1) > 16
-                            else f"expert FFN step (gate/up + down, int4 skinny MFMA, {wt})" if cfg.wt == "int4"
-                            else "expert FFN step (gate/up + down GEMV)"),
+                    kernel=f"expert FFN step ({ffn_paths(cfg, run.counts.cpu().tolist(), args.tau)}; weights {wt})",
                     bytes_per_launch=ffn_bytes,
                     launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5),
                     measured_read_ceiling=round(ceil, 1),
