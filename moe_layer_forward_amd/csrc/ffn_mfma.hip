@@ -24,12 +24,15 @@
 //    lane's accumulator holds four consecutive output columns of one token
 //    row: the epilogue stores 16 (fp32) or 8 (bf16) bytes per lane straight
 //    from registers, no LDS round trip;
-//  * LDS holds five stages of A and B of K = 32 each (160 KiB), refilled by
-//    buffer_load ... lds (no VGPR staging) four K steps ahead; every wave keeps
-//    at most its 3 newer stages in flight at a barrier, so the stage read next
-//    has landed;
-//  * the 16-byte chunks of each 64-byte LDS row are XOR-swizzled by
-//    (row/4)&3, so 16-byte fragment reads of 16 consecutive rows are
+//  * LDS holds K in pairs of steps (K = 64, one 128-byte row per tile row):
+//    two A pair slots and three B pair slots (160 KiB), refilled by
+//    buffer_load ... lds (no VGPR staging).  Every copy instruction moves 8
+//    rows x one whole 128-byte line; copies of 16 rows x 64 B (one K step per
+//    slot) cost the texture path ~10% of the GEMM.  Step 2j issues the next A
+//    pair, step 2j+1 the B pair after next, four copies per wave per step,
+//    each landing two or more steps before its first read;
+//  * the 16-byte chunks of each 128-byte LDS row are XOR-swizzled by
+//    (row/2)&7, so 16-byte fragment reads of 16 consecutive rows are
 //    conflict-free; each DMA lane simply fetches the chunk that belongs at its
 //    fixed LDS slot;
 //  * the buffer range check returns zeros for gathered token rows past the
@@ -143,7 +146,7 @@ struct MfmaArgs {
 
 // The last, partial round of 256-row tiles: W tiles on G blocks leave
 // r = W mod G tiles for the final round.  When r <= G/2 each of them is cut
-// into S K-ranges (S = G / r, at most the K steps and the partial-buffer
+// into S K-ranges (S = G / r, at most the K pairs and the partial-buffer
 // capacity), so the final round fills the machine; the parts write fp32
 // partial tiles, and mfma_tail_reduce sums the S parts of a tile in order.
 struct TailSplit {
@@ -221,19 +224,32 @@ __device__ __forceinline__ int swz(int row, int ch) {
     return row * MF_BK + ((ch ^ ((row >> 2) & 3)) << 3);
 }
 
-// wait until at most 4n of this wave's copies are outstanding (n clamped to 0..3)
-__device__ __forceinline__ void wait_stages(int n) {
-    if (n >= 3) __builtin_amdgcn_s_waitcnt(0x0F7C);         // vmcnt(12)
-    else if (n == 2) __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
-    else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0F74);    // vmcnt(4)
+// Pair slots of the 256-row kernel: K = 64 (two K steps) per 128-byte LDS row,
+// so that every copy instruction moves whole 128-byte lines (8 rows x 128 B).
+// The 16-byte chunks of a row are XORed with (row/2)&7: rows 2j and 2j+1 share
+// a 256-byte bank line, and 16 consecutive rows reading the same logical chunk
+// land on 16 distinct 16-byte bank groups.
+constexpr int MF_PK = 2 * MF_BK;              // K per pair slot
+constexpr int MF_PSLOT = MF_BM * MF_PK;       // elements of one operand pair slot
+constexpr int MF_AS = 2;                      // A pair slots
+constexpr int MF_BS = 3;                      // B pair slots
+__device__ __forceinline__ int swz2(int row, int ch) {
+    return row * MF_PK + ((ch ^ ((row >> 1) & 7)) << 3);
+}
+
+// wait until at most n (0, 4, 8 or 12) vector-memory operations are outstanding
+__device__ __forceinline__ void wait_copies(int n) {
+    if (n >= 12) __builtin_amdgcn_s_waitcnt(0x0F7C);        // vmcnt(12)
+    else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
+    else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F74);    // vmcnt(4)
     else __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
 }
 
 template <int MODE>
 __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
-    // stage s: A at s * MF_STAGE, B at (MF_NS + s) * MF_STAGE (elements); a tile
-    // fills stages 0, 1, 2, ... from its first K step
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * MF_NS * MF_STAGE];
+    // A pair slots then B pair slots; pair j of a task (its K steps kb + 2j and
+    // kb + 2j + 1) sits in A slot j % 2 and B slot j % 3
+    __shared__ __attribute__((aligned(16))) uint16_t smem[(MF_AS + MF_BS) * MF_PSLOT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -248,15 +264,15 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
     const int slot = (nblk % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
     const uint32_t row_bytes = (uint32_t)K * 2u;
     const int nk = (K + MF_BK - 1) / MF_BK;
-    // copies: each wave instruction fills 16 tile rows x 64 B; wave w copies A
-    // rows and B rows 32w + 16i + lane/4 (i = 0, 1), physical chunk lane%4
-    const int dma_row = wave * 32 + (lane >> 2);
+    const int np = (nk + 1) / 2;                 // K pairs
+    // copies: wave w fills A rows and B rows 32w + 8i + lane/8 (i = 0..3),
+    // physical chunk lane%8 of the 128-byte row
     const int32x4_t RA = make_desc(a.in, (uint32_t)a.in_rows * row_bytes);
     const uint32_t wmat = (uint32_t)N * row_bytes;
     // B rows of this wave's copies: mode 0 waves 0-3 gate rows, waves 4-7 up rows
     const uint16_t* wsrc = (MODE == 0 && wave >= 4) ? a.w1 : a.w0;
 
-    const TailSplit ts = tail_split(total, nblk, nk, a.part_cap);
+    const TailSplit ts = tail_split(total, nblk, np, a.part_cap);
     const int ntasks = ts.nfull + ts.rtail * ts.S;
 
     // B-tile row of this lane's fragment ni (mode 0: gate rows, then the
@@ -265,11 +281,19 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
         return (MODE == 0) ? ni * 128 + wi * 32 + (lane & 31) : wi * 64 + ni * 32 + (lane & 31);
     };
 
-    // task t: whole tile, or part sp of tail tile j (K steps [kb, ke)); its tile
-    // and this lane's copy offsets (the two copy rows r and r+16 share the
-    // swizzled chunk)
-    int c_kb, c_ke, c_kend, c_pi, c_nt, c_p0, c_rows, c_e, c_kcol;
-    uint32_t c_a0, c_a1, c_b0, c_b1;
+    // task t: whole tile, or part sp of tail tile j (K steps [kb, ke), kb
+    // even); its tile and this lane's copy offsets.  Copy rows r_i = 32w + 8i
+    // + lane/8 take logical chunk (lane%8) ^ ((r_i/2)&7): chunk kc0 for even
+    // i, kc0 ^ 4 for odd i (byte offset kodd further).  Rows that follow one
+    // another in memory (B rows; A rows of the down pass) keep the offset of
+    // row r_0 and the count of rows left from it; gathered A rows (gate/up)
+    // keep one offset per i.
+    constexpr bool AG = MODE == 0;                // A rows gathered through perm
+    int c_kb, c_ke, c_kend, c_pi, c_nt, c_p0, c_rows, c_e;
+    uint32_t c_a[AG ? 4 : 1], c_b0;
+    int c_an, c_bn;
+    const int kc0 = (lane & 7) ^ ((lane >> 4) & 3);
+    const int kodd = (((kc0 ^ 4) - kc0) * 16);
     auto setup = [&](int t) __attribute__((always_inline)) {
         int L = t;
         c_kb = 0;
@@ -278,8 +302,8 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
         if (t >= ts.nfull) {
             const int q = t - ts.nfull, j = q % ts.rtail, sp = q / ts.rtail;
             L = ts.nfull + j;
-            c_kb = (int)((long)nk * sp / ts.S);
-            c_ke = (int)((long)nk * (sp + 1) / ts.S);
+            c_kb = 2 * (int)((long)np * sp / ts.S);
+            c_ke = min(nk, 2 * (int)((long)np * (sp + 1) / ts.S));
             c_pi = j * ts.S + sp;
         }
         c_kend = min(K, c_ke * MF_BK);           // element bound of the task's K range
@@ -293,26 +317,35 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
         c_e = a.tiles[mt];
         c_p0 = a.tiles[a.max_mt + mt];
         c_rows = a.tiles[2 * a.max_mt + mt];
-        const int r = dma_row;
-        const int ch = (lane & 3) ^ ((r >> 2) & 3);
-        c_kcol = ch * 8;
-        const int src0 = (MODE == 0) ? (r < c_rows ? a.perm[c_p0 + r] / a.topk : 0) : c_p0 + r;
-        const int src1 = (MODE == 0) ? (r + 16 < c_rows ? a.perm[c_p0 + r + 16] / a.topk : 0) : c_p0 + r + 16;
-        c_a0 = r < c_rows ? (uint32_t)src0 * row_bytes + (uint32_t)ch * 16u : MF_OOB;
-        c_a1 = r + 16 < c_rows ? (uint32_t)src1 * row_bytes + (uint32_t)ch * 16u : MF_OOB;
-        const int n0 = (MODE == 0) ? c_nt * 128 + (r & 127) : c_nt * MF_BN + r;
-        const int n1 = (MODE == 0) ? c_nt * 128 + ((r + 16) & 127) : c_nt * MF_BN + r + 16;
-        c_b0 = n0 < N ? (uint32_t)n0 * row_bytes + (uint32_t)ch * 16u : MF_OOB;
-        c_b1 = n1 < N ? (uint32_t)n1 * row_bytes + (uint32_t)ch * 16u : MF_OOB;
+        const int r0 = wave * 32 + (lane >> 3);
+        if constexpr (AG) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0 + 8 * i;
+                const uint32_t cb = (uint32_t)(kc0 ^ ((i & 1) << 2)) * 16u;
+                c_a[i] = r < c_rows ? (uint32_t)(a.perm[c_p0 + r] / a.topk) * row_bytes + cb : MF_OOB;
+            }
+        } else {
+            c_a[0] = (uint32_t)(c_p0 + r0) * row_bytes + (uint32_t)kc0 * 16u;
+        }
+        c_an = c_rows - r0;
+        const int n0 = (MODE == 0) ? c_nt * 128 + (r0 & 127) : c_nt * MF_BN + r0;
+        c_b0 = (uint32_t)n0 * row_bytes + (uint32_t)kc0 * 16u;
+        c_bn = N - n0;
     };
 
     if (slot >= ntasks) return;
     setup(slot);
     for (int task = slot; task < ntasks; task += nblk) {
-        const int kb = c_kb, ke = c_ke, kend = c_kend, kcol = c_kcol;
-        const uint32_t aoff[2] = {c_a0, c_a1}, boff[2] = {c_b0, c_b1};
+        const int kb = c_kb, ke = c_ke, kend = c_kend;
+        uint32_t aoff[AG ? 4 : 1];
+#pragma unroll
+        for (int i = 0; i < (AG ? 4 : 1); ++i) aoff[i] = c_a[i];
+        const uint32_t boff0 = c_b0;
+        const int an = c_an, bn = c_bn;
         const int pi = c_pi, nt = c_nt, p0 = c_p0, rows = c_rows;
         const int32x4_t RB = make_desc(wsrc + (size_t)c_e * N * K, wmat);
+        const int P = (ke - kb + 1) / 2;         // pairs of the task
         floatx16 acc[4][2];
         bf16x8_t fa[2][4], fb[2][2];
 #pragma unroll
@@ -322,31 +355,35 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-        auto issue = [&](int kt) __attribute__((always_inline)) {   // this wave's 4 copies of K step kt
-            const int st = (kt - kb) % MF_NS;
-            const uint32_t kbyte = (uint32_t)kt * (MF_BK * 2);
-            const bool kok = kt * MF_BK + kcol < kend;
+        // this wave's 4 copies of pair j of A (or B) into the pair slot at
+        // `base`: rows 32w + 8i .., the pair's 128-byte line of each
+        auto issue = [&](bool isb, int j, uint16_t* base) __attribute__((always_inline)) {
+            const int k0 = (kb + 2 * j) * MF_BK;
+            const uint32_t kbyte = (uint32_t)k0 * 2u;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r0 = wave * 32 + i * 16;
-                dma16(RA, (kok && aoff[i] != MF_OOB) ? aoff[i] + kbyte : MF_OOB,
-                      lds_addr(&smem[st * MF_STAGE + r0 * MF_BK]));
-                dma16(RB, (kok && boff[i] != MF_OOB) ? boff[i] + kbyte : MF_OOB,
-                      lds_addr(&smem[(MF_NS + st) * MF_STAGE + r0 * MF_BK]));
+            for (int i = 0; i < 4; ++i) {
+                const bool kok = k0 + 8 * (kc0 ^ ((i & 1) << 2)) < kend;
+                const uint32_t step = 8u * (uint32_t)i * row_bytes + ((i & 1) ? (uint32_t)kodd : 0u);
+                uint32_t o;
+                if (isb) o = 8 * i < bn ? boff0 + step : MF_OOB;
+                else if constexpr (AG) o = aoff[i];
+                else o = 8 * i < an ? aoff[0] + step : MF_OOB;
+                dma16(isb ? RB : RA, (kok && o != MF_OOB) ? o + kbyte : MF_OOB,
+                      lds_addr(&base[(wave * 32 + 8 * i) * MF_PK]));
             }
         };
-        auto read = [&](int st) __attribute__((always_inline)) {
-            const uint16_t* sa = smem + st * MF_STAGE;
-            const uint16_t* sb = smem + (MF_NS + st) * MF_STAGE;
+        // fragments of one K step: half h (the first or second 32 of K) of the
+        // pair slots sa (A) and sb (B)
+        auto read = [&](const uint16_t* sa, const uint16_t* sb, int h) __attribute__((always_inline)) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const int ch = ks * 2 + (lane >> 5);
+                const int ch = h * 4 + ks * 2 + (lane >> 5);
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi)
-                    fa[ks][mi] = *reinterpret_cast<const bf16x8_t*>(&sa[swz(grp * 128 + mi * 32 + (lane & 31), ch)]);
+                    fa[ks][mi] = *reinterpret_cast<const bf16x8_t*>(&sa[swz2(grp * 128 + mi * 32 + (lane & 31), ch)]);
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    fb[ks][ni] = *reinterpret_cast<const bf16x8_t*>(&sb[swz(brow(ni), ch)]);
+                    fb[ks][ni] = *reinterpret_cast<const bf16x8_t*>(&sb[swz2(brow(ni), ch)]);
             }
         };
         // transposed product: acc[mi][ni] is (B rows of fragment ni) x (tokens of fragment mi)
@@ -361,35 +398,64 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
                                                                                acc[mi][ni], 0, 0, 0);
         };
 
-        // Prologue: stages 0..3 take the tile's first K steps.  Vector memory
-        // operations complete in order, so the wait for step kb also covers
-        // this wave's epilogue stores of the previous tile; the barrier makes
-        // every wave's copies of step kb visible and ends all LDS reads of the
-        // previous tile.
-        for (int kt = kb; kt < kb + MF_NS - 1 && kt < ke; ++kt) issue(kt);
+        // Copy schedule (groups of 4 copies per wave): A0, B0, B1 before the
+        // loop; step 2j issues A(j+1) into the other A slot and step 2j+1
+        // issues B(j+2) into the third B slot, so both reuse slots whose last
+        // reads (step 2j - 1) both wave groups have passed.  The barrier that
+        // ends group 0's memory phase of step r is followed by group 1's reads
+        // of step r, the next one by group 0's reads of step r + 1, so before
+        // it a wave must have landed its copies of that step's pair.  Copies
+        // complete in order: a wave waits until the newest group needed (A(p)
+        // of pair p; B0 for p = 0) has landed, i.e. until no more than the
+        // groups issued after it are outstanding - at step 2j, after A(j):
+        // B(j+1), A(j+1); at step 2j+1, after A(j+1): B(j+2), or for group 0's
+        // first barrier (pair j) after A(j): B(j+1), A(j+1), B(j+2).  The same
+        // wait also covers this wave's epilogue stores of the previous tile;
+        // the barrier makes every wave's copies visible and ends all LDS
+        // reads of the previous tile.
+        uint16_t* const sA0 = smem;
+        uint16_t* const sB0 = smem + MF_AS * MF_PSLOT;
+        int ca = 0, cb = 0, nb = 1, tb = 2;           // current A slot; current, next, third B slot
+        issue(false, 0, sA0);
+        issue(true, 0, sB0);
+        if (P > 1) issue(true, 1, sB0 + MF_PSLOT);
         // the next task's loads go out behind the prologue copies and land
         // during the K loop (which makes the wait below slightly stricter)
         if (task + nblk < ntasks) setup(task + nblk);
-        wait_stages(ke - 1 - kb);
+        wait_copies(P > 1 ? 4 : 0);                   // A0 and B0
         block_barrier();
         if (grp == 1) block_barrier();               // group 1 starts one phase later
-        // Per K step kt, each wave: memory phase (fragments of step kt, then the
-        // copies of step kt+4 into the buffer of step kt-1, which both groups
-        // have read), barrier, compute phase, barrier.  At each barrier a wave
-        // has landed its copies of step kt+1: only those of the (at most 3)
-        // later steps may still be in flight.
-        for (int kt = kb; kt < ke; ++kt) {
-            read((kt - kb) % MF_NS);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt + MF_NS - 1 < ke) issue(kt + MF_NS - 1);
+        // Per K step, each wave: memory phase (fragments of the step, then the
+        // copies it issues), barrier, compute phase, barrier.
+        auto step = [&](int after1, int after2) __attribute__((always_inline)) {
             __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): own fragments read
-            wait_stages(ke - 2 - kt);
+            wait_copies(after1);
             block_barrier();
             __builtin_amdgcn_s_setprio(1);
             mma();
             __builtin_amdgcn_s_setprio(0);
-            wait_stages(ke - 2 - kt);
+            wait_copies(after2);
             block_barrier();
+        };
+        for (int j = 0; j < P; ++j) {
+            const uint16_t* sa = sA0 + ca * MF_PSLOT;
+            const uint16_t* sb = sB0 + cb * MF_PSLOT;
+            read(sa, sb, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j + 1 < P) issue(false, j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
+            step(j + 1 < P ? 8 : 0, j + 1 < P ? 8 : 0);
+            if (kb + 2 * j + 1 < ke) {
+                read(sa, sb, 1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j + 2 < P) issue(true, j + 2, sB0 + tb * MF_PSLOT);
+                const int later = j + 2 < P ? 4 : 0;
+                step(grp == 0 ? (j + 1 < P ? 8 : 0) + later : later, later);
+            }
+            ca ^= 1;
+            const int t = cb;
+            cb = nb;
+            nb = tb;
+            tb = t;
         }
 
         // ---- epilogue.  Accumulator element v of lane l: token row
@@ -451,8 +517,8 @@ __global__ __launch_bounds__(256) void mfma_tail_reduce(MfmaArgs a, int G) {
     const int N = a.N;
     const int n_mt = a.tiles[3 * a.max_mt];
     const int nN = (MODE == 0) ? (N + 127) / 128 : (N + MF_BN - 1) / MF_BN;
-    const int nk = (a.K + MF_BK - 1) / MF_BK;
-    const TailSplit ts = tail_split(n_mt * nN, G, nk, a.part_cap);
+    const int np = ((a.K + MF_BK - 1) / MF_BK + 1) / 2;      // K pairs, as the GEMM splits them
+    const TailSplit ts = tail_split(n_mt * nN, G, np, a.part_cap);
     const int j = blockIdx.y;
     if (j >= ts.rtail) return;
     constexpr int NC = MODE == 0 ? 128 : MF_BN;      // output columns of a tile
