@@ -30,7 +30,9 @@
 //    rows x one whole 128-byte line; copies of 16 rows x 64 B (one K step per
 //    slot) cost the texture path ~10% of the GEMM.  Step 2j issues the next A
 //    pair, step 2j+1 the B pair after next, four copies per wave per step,
-//    each landing two or more steps before its first read;
+//    each landing two or more steps before its first read.  The copy stream
+//    runs on across the block's tiles: a tile's last pairs fetch the next
+//    tile's first ones, so no tile starts on an empty pipeline;
 //  * the 16-byte chunks of each 128-byte LDS row are XOR-swizzled by
 //    (row/2)&7, so 16-byte fragment reads of 16 consecutive rows are
 //    conflict-free; each DMA lane simply fetches the chunk that belongs at its
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
     // B rows of this wave's copies: mode 0 waves 0-3 gate rows, waves 4-7 up rows
     const uint16_t* wsrc = (MODE == 0 && wave >= 4) ? a.w1 : a.w0;
 
-    const TailSplit ts = tail_split(total, nblk, np, a.part_cap);
+    const TailSplit ts = tail_split(total, nblk, np > 3 ? np / 2 : 1, a.part_cap);
     const int ntasks = ts.nfull + ts.rtail * ts.S;
 
     // B-tile row of this lane's fragment ni (mode 0: gate rows, then the
@@ -335,7 +337,17 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
     };
 
     if (slot >= ntasks) return;
+    // With two or more K pairs per task (tail parts are cut to at least two)
+    // the copy stream runs on from one task into the next: the last pairs'
+    // steps issue the next task's A0, B0 and B1 into the slots the stream
+    // reaches, so a new tile starts with its first pair already landed.  With
+    // a single pair every task fills its slots from scratch.
+    const bool stream = np >= 2;
+    uint16_t* const sA0 = smem;
+    uint16_t* const sB0 = smem + MF_AS * MF_PSLOT;
+    int ca = 0, cb = 0, nb = 1, tb = 2;               // current A slot; current, next, third B slot
     setup(slot);
+    bool first = true;
     for (int task = slot; task < ntasks; task += nblk) {
         const int kb = c_kb, ke = c_ke, kend = c_kend;
         uint32_t aoff[AG ? 4 : 1];
@@ -345,7 +357,8 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
         const int an = c_an, bn = c_bn;
         const int pi = c_pi, nt = c_nt, p0 = c_p0, rows = c_rows;
         const int32x4_t RB = make_desc(wsrc + (size_t)c_e * N * K, wmat);
-        const int P = (ke - kb + 1) / 2;         // pairs of the task
+        const int P = (ke - kb + 1) / 2;         // pairs of the task (an odd last step runs on zeros)
+        const bool has_next = task + nblk < ntasks;
         floatx16 acc[4][2];
         bf16x8_t fa[2][4], fb[2][2];
 #pragma unroll
@@ -355,22 +368,31 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-        // this wave's 4 copies of pair j of A (or B) into the pair slot at
-        // `base`: rows 32w + 8i .., the pair's 128-byte line of each
-        auto issue = [&](bool isb, int j, uint16_t* base) __attribute__((always_inline)) {
-            const int k0 = (kb + 2 * j) * MF_BK;
+        // this wave's 4 copies of pair j (K from element k0) of A (or B) of a
+        // task with the given offsets, into the pair slot at `base`: rows
+        // 32w + 8i .., the pair's 128-byte line of each
+        auto copies = [&](bool isb, int k0, int kendv, const uint32_t* ao, uint32_t bo0, int anv, int bnv,
+                          const int32x4_t& rb, uint16_t* base) __attribute__((always_inline)) {
             const uint32_t kbyte = (uint32_t)k0 * 2u;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool kok = k0 + 8 * (kc0 ^ ((i & 1) << 2)) < kend;
+                const bool kok = k0 + 8 * (kc0 ^ ((i & 1) << 2)) < kendv;
                 const uint32_t step = 8u * (uint32_t)i * row_bytes + ((i & 1) ? (uint32_t)kodd : 0u);
                 uint32_t o;
-                if (isb) o = 8 * i < bn ? boff0 + step : MF_OOB;
-                else if constexpr (AG) o = aoff[i];
-                else o = 8 * i < an ? aoff[0] + step : MF_OOB;
-                dma16(isb ? RB : RA, (kok && o != MF_OOB) ? o + kbyte : MF_OOB,
+                if (isb) o = 8 * i < bnv ? bo0 + step : MF_OOB;
+                else if constexpr (AG) o = ao[i];
+                else o = 8 * i < anv ? ao[0] + step : MF_OOB;
+                dma16(isb ? rb : RA, (kok && o != MF_OOB) ? o + kbyte : MF_OOB,
                       lds_addr(&base[(wave * 32 + 8 * i) * MF_PK]));
             }
+        };
+        auto issue = [&](bool isb, int j, uint16_t* base) __attribute__((always_inline)) {
+            copies(isb, (kb + 2 * j) * MF_BK, kend, aoff, boff0, an, bn, RB, base);
+        };
+        // pair j of the next task, from the offsets setup() left in c_*
+        auto issue_next = [&](bool isb, int j, uint16_t* base) __attribute__((always_inline)) {
+            const int32x4_t rbn = make_desc(wsrc + (size_t)c_e * N * K, wmat);
+            copies(isb, (c_kb + 2 * j) * MF_BK, c_kend, c_a, c_b0, c_an, c_bn, rbn, base);
         };
         // fragments of one K step: half h (the first or second 32 of K) of the
         // pair slots sa (A) and sb (B)
@@ -398,59 +420,67 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
                                                                                acc[mi][ni], 0, 0, 0);
         };
 
-        // Copy schedule (groups of 4 copies per wave): A0, B0, B1 before the
-        // loop; step 2j issues A(j+1) into the other A slot and step 2j+1
-        // issues B(j+2) into the third B slot, so both reuse slots whose last
-        // reads (step 2j - 1) both wave groups have passed.  The barrier that
-        // ends group 0's memory phase of step r is followed by group 1's reads
-        // of step r, the next one by group 0's reads of step r + 1, so before
-        // it a wave must have landed its copies of that step's pair.  Copies
-        // complete in order: a wave waits until the newest group needed (A(p)
-        // of pair p; B0 for p = 0) has landed, i.e. until no more than the
-        // groups issued after it are outstanding - at step 2j, after A(j):
-        // B(j+1), A(j+1); at step 2j+1, after A(j+1): B(j+2), or for group 0's
-        // first barrier (pair j) after A(j): B(j+1), A(j+1), B(j+2).  The same
-        // wait also covers this wave's epilogue stores of the previous tile;
-        // the barrier makes every wave's copies visible and ends all LDS
-        // reads of the previous tile.
-        uint16_t* const sA0 = smem;
-        uint16_t* const sB0 = smem + MF_AS * MF_PSLOT;
-        int ca = 0, cb = 0, nb = 1, tb = 2;           // current A slot; current, next, third B slot
-        issue(false, 0, sA0);
-        issue(true, 0, sB0);
-        if (P > 1) issue(true, 1, sB0 + MF_PSLOT);
-        // the next task's loads go out behind the prologue copies and land
-        // during the K loop (which makes the wait below slightly stricter)
-        if (task + nblk < ntasks) setup(task + nblk);
-        wait_copies(P > 1 ? 4 : 0);                   // A0 and B0
-        block_barrier();
-        if (grp == 1) block_barrier();               // group 1 starts one phase later
+        // Copy schedule (groups of 4 copies per wave), one stream over the
+        // pairs of the block's tasks: the first step of pair j issues A(j+1)
+        // into the other A slot, the second step issues B(j+2) into the third
+        // B slot; past the task's last pair these are the next task's A0, B0
+        // and B1.  Both reuse slots whose last reads (step 2j - 1) both wave
+        // groups have passed.  The barrier that ends group 0's memory phase of
+        // step r is followed by group 1's reads of step r, the next one by
+        // group 0's reads of step r + 1, so before it a wave must have landed
+        // its copies of that step's pair.  The first step of a pair needs only
+        // the pair itself (landed at the pair before); at the second step a
+        // wave waits for A(j+1), the newest group the next pair needs: copies
+        // complete in order, so until at most B(j+2) (if issued) is
+        // outstanding.  In-order completion also makes that wait cover this
+        // wave's epilogue stores of the previous tile; the barrier makes every
+        // wave's copies visible and ends all LDS reads of the previous pair.
+        if (first || !stream) {
+            ca = 0; cb = 0; nb = 1; tb = 2;
+            issue(false, 0, sA0);
+            issue(true, 0, sB0);
+            if (P > 1) issue(true, 1, sB0 + MF_PSLOT);
+        }
+        // the next task's loads go out behind this task's first copies and
+        // land long before its own copies are issued
+        if (has_next) setup(task + nblk);
+        if (first || !stream) {
+            wait_copies(P > 1 ? 4 : 0);                // A0 and B0
+            block_barrier();
+            if (grp == 1) block_barrier();           // group 1 starts one phase later
+        }
+        first = false;
         // Per K step, each wave: memory phase (fragments of the step, then the
         // copies it issues), barrier, compute phase, barrier.
         auto step = [&](int after1, int after2) __attribute__((always_inline)) {
             __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): own fragments read
-            wait_copies(after1);
+            if (after1 >= 0) wait_copies(after1);
             block_barrier();
             __builtin_amdgcn_s_setprio(1);
             mma();
             __builtin_amdgcn_s_setprio(0);
-            wait_copies(after2);
+            if (after2 >= 0) wait_copies(after2);
             block_barrier();
         };
+        const bool nxt = stream && has_next;
         for (int j = 0; j < P; ++j) {
             const uint16_t* sa = sA0 + ca * MF_PSLOT;
             const uint16_t* sb = sB0 + cb * MF_PSLOT;
             read(sa, sb, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (j + 1 < P) issue(false, j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
-            step(j + 1 < P ? 8 : 0, j + 1 < P ? 8 : 0);
-            if (kb + 2 * j + 1 < ke) {
-                read(sa, sb, 1);
-                __builtin_amdgcn_sched_barrier(0);
-                if (j + 2 < P) issue(true, j + 2, sB0 + tb * MF_PSLOT);
-                const int later = j + 2 < P ? 4 : 0;
-                step(grp == 0 ? (j + 1 < P ? 8 : 0) + later : later, later);
-            }
+            else if (nxt) issue_next(false, 0, sA0 + (ca ^ 1) * MF_PSLOT);
+            step(-1, -1);
+            read(sa, sb, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            bool bnew = true;
+            if (j + 2 < P) issue(true, j + 2, sB0 + tb * MF_PSLOT);
+            else if (nxt) issue_next(true, j + 2 - P, sB0 + tb * MF_PSLOT);
+            else bnew = false;
+            // A(j+1) lands before the next pair; at the task's end without a
+            // streamed successor everything lands
+            const int after = (j + 1 < P || nxt) && bnew ? 4 : 0;
+            step(grp == 0 ? -1 : after, after);
             ca ^= 1;
             const int t = cb;
             cb = nb;
@@ -502,9 +532,9 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
             }
         }
         // group 0 finished one phase earlier (its epilogue ran beside group 1's
-        // last MFMAs); its extra barrier pairs with group 1's last one, as
-        // group 1 had the extra barrier at the start
-        if (grp == 0) block_barrier();
+        // last MFMAs); when the stream ends here its extra barrier pairs with
+        // group 1's last one, as group 1 had the extra barrier at the start
+        if (!nxt && grp == 0) block_barrier();
     }
 }
 
@@ -518,7 +548,7 @@ __global__ __launch_bounds__(256) void mfma_tail_reduce(MfmaArgs a, int G) {
     const int n_mt = a.tiles[3 * a.max_mt];
     const int nN = (MODE == 0) ? (N + 127) / 128 : (N + MF_BN - 1) / MF_BN;
     const int np = ((a.K + MF_BK - 1) / MF_BK + 1) / 2;      // K pairs, as the GEMM splits them
-    const TailSplit ts = tail_split(n_mt * nN, G, np, a.part_cap);
+    const TailSplit ts = tail_split(n_mt * nN, G, np > 3 ? np / 2 : 1, a.part_cap);
     const int j = blockIdx.y;
     if (j >= ts.rtail) return;
     constexpr int NC = MODE == 0 ? 128 : MF_BN;      // output columns of a tile
