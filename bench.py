@@ -180,7 +180,7 @@ def cpu_baseline(cfg, runner, Wd, target_s=10.0):
 
 # kernel sources of each workload's expert-FFN step: the committed counter
 # summary is only valid for the sources it was taken on
-TRAFFIC_SOURCES = {"mixtral_decode": ["ffn_gemv.hip", "common.h"], "fine_int4_decode": ["ffn_i4mfma.hip", "common.h"]}
+TRAFFIC_SOURCES = {"mixtral_decode": ["ffn_gemv.hip", "ffn_skinny.hip", "common.h"], "fine_int4_decode": ["ffn_i4mfma.hip", "common.h"]}
 
 
 def source_digest(key):
