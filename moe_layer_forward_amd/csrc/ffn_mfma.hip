@@ -591,19 +591,23 @@ __global__ __launch_bounds__(256) void mfma_tail_reduce(MfmaArgs a, int G) {
 // Small M-tiles (at most 64 rows: small expert groups and short remainders).
 // Block tile 64 x 256 (gate/up: 128 gate + the 128 matching up rows), four
 // waves side by side, each 64 x 64 = 2 x 2 accumulators of
-// v_mfma_f32_32x32x16_bf16; K in stages of 32 (4 KiB of A, 16 KiB of B),
-// four LDS stages with three stages of copies in flight, 80 KiB of LDS so two
-// blocks share a CU.  Such tiles stream each weight tile for few rows, so the
-// kernel is bound by the weight stream, not the matrix cores.
-constexpr int MS_NS = 4;
+// v_mfma_f32_32x32x16_bf16.  K is staged in pairs of steps like the 256-row
+// kernel (128-byte LDS rows swizzled by (row/2)&7, every copy 8 rows x one
+// whole line): two pair slots of A (8 KiB each) and of B (32 KiB each), 80 KiB
+// of LDS so two blocks share a CU.  Pair j+1 is copied at the second step of
+// pair j-1, two steps before its first fragments are read (fragments are read
+// one step ahead of their MFMAs).  Such tiles stream each weight tile for few
+// rows, so the kernel is bound by the weight stream, not the matrix cores.
+constexpr int MS_PSLOT_A = MS_BM * MF_PK;     // elements of an A pair slot
+constexpr int MS_PSLOT_B = MF_BN * MF_PK;     // elements of a B pair slot
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void mfma_small_kernel(MfmaArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[MS_NS][MS_BM * 32];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[MS_NS][MF_BN * 32];
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][MS_PSLOT_A];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][MS_PSLOT_B];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = a.K, N = a.N;
     const int32_t* tl = a.tiles + 3 * a.max_mt + 1;
     const int max_st = a.max_st;
@@ -612,11 +616,15 @@ __global__ __launch_bounds__(256, 2) void mfma_small_kernel(MfmaArgs a) {
     const int total = n_st * nN;
     const uint32_t row_bytes = (uint32_t)K * 2u;
     const int nk = (K + 31) / 32;
+    const int P = (nk + 1) / 2;                   // K pairs (an odd last step runs on zeros)
     const int32x4_t RA = make_desc(a.in, (uint32_t)a.in_rows * row_bytes);
     const uint32_t wmat = (uint32_t)N * row_bytes;
-    // copies: an instruction fills 16 tile rows x 64 B; lane -> row lane/4,
-    // physical chunk lane%4.  Wave w copies A rows 16w.. and B rows 64w + 16i..
-    const int crow = lane >> 2;
+    // copies: wave w fills A rows 16w + 8i + lane/8 (i = 0, 1) and B rows
+    // 64w + 8i + lane/8 (i = 0..7), physical chunk lane%8 of the 128-byte row,
+    // logical chunk kc0 for even i and kc0 ^ 4 for odd i (kodd bytes further)
+    const int kc0 = (lane & 7) ^ ((lane >> 4) & 3);
+    const int kodd = (((kc0 ^ 4) - kc0) * 16);
+    const int crow = lane >> 3;
 
     for (int L = blockIdx.x; L < total; L += gridDim.x) {
         // small tiles of one expert next to each other: consecutive blocks
@@ -628,27 +636,22 @@ __global__ __launch_bounds__(256, 2) void mfma_small_kernel(MfmaArgs a) {
 
         const uint16_t* wsrc = (MODE == 0 && wave >= 2) ? a.w1 : a.w0;
         const int32x4_t RB = make_desc(wsrc + (size_t)e * N * K, wmat);
-        uint32_t aoff, boff[4];
-        int acol, bcol[4];
-        {
-            const int r = wave * 16 + crow;
-            const int ch = (lane & 3) ^ ((r >> 2) & 3);
-            acol = ch * 8;
+        uint32_t aoff[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = wave * 16 + 8 * i + crow;
+            const uint32_t cb = (uint32_t)(kc0 ^ ((i & 1) << 2)) * 16u;
             if (r < rows) {
                 const int src = (MODE == 0) ? a.perm[p0 + r] / a.topk : p0 + r;
-                aoff = (uint32_t)src * row_bytes + (uint32_t)ch * 16u;
+                aoff[i] = (uint32_t)src * row_bytes + cb;
             } else {
-                aoff = MF_OOB;
+                aoff[i] = MF_OOB;
             }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wave * 64 + i * 16 + crow;
-            const int ch = (lane & 3) ^ ((r >> 2) & 3);
-            bcol[i] = ch * 8;
-            const int n = (MODE == 0) ? nt * 128 + (r & 127) : nt * MF_BN + r;
-            boff[i] = (n < N) ? (uint32_t)n * row_bytes + (uint32_t)ch * 16u : MF_OOB;
-        }
+        const int r0 = wave * 64 + crow;
+        const int n0 = (MODE == 0) ? nt * 128 + (r0 & 127) : nt * MF_BN + r0;
+        const uint32_t boff0 = (uint32_t)n0 * row_bytes + (uint32_t)kc0 * 16u;
+        const int bn = N - n0;                    // B rows left from this lane's first
         floatx16 acc[2][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -657,68 +660,79 @@ __global__ __launch_bounds__(256, 2) void mfma_small_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-        auto issue = [&](int kt) {                     // the 5 copies of this lane for stage kt
-            const int st = kt % MS_NS;
-            const uint32_t kb = (uint32_t)kt * 64u;
-            const int k0 = kt * 32;
-            dma16(RA, (k0 + acol < K && aoff != MF_OOB) ? aoff + kb : MF_OOB,
-                  lds_addr(&sA[st][(wave * 16) * 32]));
+        // this wave's 10 copies of pair j into pair slot sl
+        auto issue = [&](int j, int sl) __attribute__((always_inline)) {
+            const int k0 = 2 * j * 32;
+            const uint32_t kbyte = (uint32_t)k0 * 2u;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dma16(RB, (k0 + bcol[i] < K && boff[i] != MF_OOB) ? boff[i] + kb : MF_OOB,
-                      lds_addr(&sB[st][(wave * 64 + i * 16) * 32]));
+            for (int i = 0; i < 2; ++i) {
+                const bool kok = k0 + 8 * (kc0 ^ ((i & 1) << 2)) < K;
+                dma16(RA, (kok && aoff[i] != MF_OOB) ? aoff[i] + kbyte : MF_OOB,
+                      lds_addr(&sA[sl][(wave * 16 + 8 * i) * MF_PK]));
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bool kok = k0 + 8 * (kc0 ^ ((i & 1) << 2)) < K;
+                const uint32_t o = boff0 + 8u * (uint32_t)i * row_bytes + ((i & 1) ? (uint32_t)kodd : 0u);
+                dma16(RB, (kok && 8 * i < bn) ? o + kbyte : MF_OOB,
+                      lds_addr(&sB[sl][(wave * 64 + 8 * i) * MF_PK]));
+            }
         };
         auto brow = [&](int ni) {
             return (MODE == 0) ? ni * 128 + wave * 32 + (lane & 31) : wave * 64 + ni * 32 + (lane & 31);
         };
         bf16x8_t fa[2][2][2], fb[2][2][2];            // [slot][ks][mi or ni]
-        auto read = [&](int st, int sl) {
+        // fragments of K step kt (pair kt/2, half kt%2) into register slot rs
+        auto read = [&](int kt, int rs) __attribute__((always_inline)) {
+            const uint16_t* a_ = sA[(kt >> 1) & 1];
+            const uint16_t* b_ = sB[(kt >> 1) & 1];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const int ch = ks * 2 + (lane >> 5);
+                const int ch = (kt & 1) * 4 + ks * 2 + (lane >> 5);
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi)
-                    fa[sl][ks][mi] = *reinterpret_cast<const bf16x8_t*>(&sA[st][swz(mi * 32 + (lane & 31), ch)]);
+                    fa[rs][ks][mi] = *reinterpret_cast<const bf16x8_t*>(&a_[swz2(mi * 32 + (lane & 31), ch)]);
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    fb[sl][ks][ni] = *reinterpret_cast<const bf16x8_t*>(&sB[st][swz(brow(ni), ch)]);
+                    fb[rs][ks][ni] = *reinterpret_cast<const bf16x8_t*>(&b_[swz2(brow(ni), ch)]);
             }
         };
-        auto mma = [&](int sl) {
+        auto mma = [&](int rs) __attribute__((always_inline)) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                     for (int ni = 0; ni < 2; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][ks][mi], fb[sl][ks][ni],
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[rs][ks][mi], fb[rs][ks][ni],
                                                                                acc[mi][ni], 0, 0, 0);
         };
 
-        // previous tile's stores and reads are done before the stages refill
+        // previous tile's stores and reads are done before the slots refill
         wait_vm(0);
         block_barrier();
-#pragma unroll
-        for (int kt = 0; kt < MS_NS; ++kt) issue(kt);  // stages past nk copy zeros
-        __builtin_amdgcn_s_waitcnt(0x0F7F);             // vmcnt(15): stage 0 landed
+        issue(0, 0);
+        if (P > 1) {
+            issue(1, 1);
+            __builtin_amdgcn_s_waitcnt(0x0F7A);         // vmcnt(10): pair 0 landed
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0)
+        }
         block_barrier();
         read(0, 0);
-        // per stage kt (its fragments in slot kt&1): stage kt+1 landed and every
-        // wave is done reading stage kt's buffer -> refill it with stage kt+4,
-        // read stage kt+1, multiply stage kt
-        auto step = [&](int kt, auto slc) {
-            constexpr int sl = decltype(slc)::value;
-            __builtin_amdgcn_s_waitcnt(0x0F7A);         // vmcnt(10): stage kt+1 landed
-            __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0): own reads of stage kt done
+        // Step 2j: read step 2j+1, multiply step 2j.  Step 2j+1: pair j+1
+        // landed (the only copies in flight), a barrier (every wave sees it and
+        // has finished reading pair j), copy pair j+2 into pair j's slot, read
+        // step 2j+2, multiply step 2j+1.
+        for (int j = 0; j < P; ++j) {
+            read(2 * j + 1, 1);
+            mma(0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): pair j+1 landed
+            __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0): own reads of pair j done
             block_barrier();
-            issue(kt + MS_NS);
-            read((kt + 1) % MS_NS, sl ^ 1);
-            mma(sl);
-        };
-        const int nk2 = (nk + 1) & ~1;                  // an extra step multiplies zeros
-        for (int kt = 0; kt < nk2; kt += 2) {
-            step(kt, std::integral_constant<int, 0>{});
-            step(kt + 1, std::integral_constant<int, 1>{});
+            if (j + 2 < P) issue(j + 2, j & 1);
+            if (j + 1 < P) read(2 * j + 2, 0);
+            mma(1);
         }
 
         // ---- epilogue; accumulator element v of lane l: column l%32, row 8*(v/4) + 4*(l/32) + v%4
