@@ -253,14 +253,14 @@ def ffn_paths(cfg, counts, tau):
     """Which kernels the layer's FFN step runs, from the group sizes (the same
     rule the library applies on the device): bf16 groups above tau take the
     MFMA tiles; below it, when the largest group exceeds one GEMV pass, the
-    skinny MFMA kernel (one 16-token tile up to 16 rows, two up to 32) takes
+    skinny MFMA kernel (ceil(rows / 16) 16-token tiles, up to 64 rows) takes
     them all, else the GEMV."""
     if cfg.wt == "int4":
         return "int4 skinny MFMA" if cfg.d % 1024 == 0 and cfg.F % 1024 == 0 else "int4 GEMV"
     if cfg.wt != "bf16" or tau < 0:
         return "GEMV"
-    skinny = cfg.act == "bf16" and cfg.d % 512 == 0 and cfg.F % 512 == 0
-    t = tau if tau > 0 else (32 if skinny else 16)
+    skinny = cfg.act == "bf16" and cfg.d % 64 == 0 and cfg.F % 64 == 0
+    t = tau if tau > 0 else (64 if skinny and min(cfg.d, cfg.F) >= 4096 else 16)
     c = [int(v) for v in counts if v > 0]
     small = [v for v in c if v <= t]
     parts = []
@@ -269,8 +269,9 @@ def ffn_paths(cfg, counts, tau):
         p = []
         if small:
             m = max(small)
-            if skinny and t <= 32 and m > npass:
-                p.append("skinny MFMA, %d token tile%s" % ((1, "") if m <= 16 else (2, "s")))
+            if skinny and t <= 64 and m > npass:
+                tt = (m + 15) // 16
+                p.append("skinny MFMA, %d token tile%s" % (tt, "" if tt == 1 else "s"))
             else:
                 p.append("GEMV")
         if any(v > t for v in c):

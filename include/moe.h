@@ -69,10 +69,10 @@ typedef enum {
  *        MOE_INT4_G128 with act BF16).
  *   tau: bf16 expert groups with at most tau rows run the HBM-streaming
  *        kernels (the GEMV, or, when some group is larger than one GEMV pass,
- *        the skinny MFMA kernel, which covers up to 32 rows and needs d and F
- *        multiples of 512), larger groups the MFMA grouped GEMM.  0 selects
- *        the default: 32 where the skinny kernel serves both projections,
- *        else 16.  Negative forces the GEMV for every group.  fp32 and int4
+ *        the skinny MFMA kernel, which covers up to 64 rows and needs d and F
+ *        multiples of 64), larger groups the MFMA grouped GEMM.  0 selects
+ *        the default: 64 where the skinny kernel serves both projections and
+ *        d and F are at least 4096, else 16.  Negative forces the GEMV for every group.  fp32 and int4
  *        weights ignore tau (GEMV; int4 with K a multiple of 1024 on the
  *        matrix cores).
  * Limits (MOE_EINVAL otherwise): T >= 0, 1 <= k <= E <= 256, k <= 16,

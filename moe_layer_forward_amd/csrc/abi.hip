@@ -157,7 +157,11 @@ bool skinny_applies(const moe_shape* s) {
 int effective_tau(const moe_shape* s) {
     if (s->wt != MOE_BF16) return -1;      // fp32 and int4: GEMV for every group
     if (s->tau < 0) return -1;
-    if (s->tau == 0) return skinny_applies(s) ? kSkinnyMaxRows : kDefaultTau;
+    // default: the skinny kernel up to 64 rows where K gives its items eight
+    // or more steps (d, F >= 4096); with shorter rows its per-item reduction
+    // and extra token reads cost more than the 64-row MFMA tiles above one
+    // token tile
+    if (s->tau == 0) return (skinny_applies(s) && s->d >= 4096 && s->F >= 4096) ? kSkinnyMaxRows : kDefaultTau;
     return s->tau;
 }
 
@@ -196,12 +200,12 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
     const bool tiled = s->wt == MOE_INT4_G128_TILED;
     // bf16 groups below the MFMA tiles: when one of them is larger than a
-    // GEMV pass (lo rows), the skinny MFMA kernel (one pass of up to 32
+    // GEMV pass (lo rows), the skinny MFMA kernel (one pass of up to 64
     // tokens) takes every group below the tiles in one balanced launch and
     // the GEMV stands aside; otherwise the GEMV serves them.  Both kernels
     // decide from the counts on the device.  The skinny kernel is only
     // launched when such a group can occur: a group holds at most T rows, and
-    // everything below the tiles must fit one skinny pass (tau <= 32); a
+    // everything below the tiles must fit one skinny pass (tau <= 64); a
     // negative tau keeps the GEMV for all
     const int tau_m = use_mfma ? tau : s->T;                   // largest group below the tiles
     auto skinny_lo = [&](int mode, int K, int N, int in_rows) -> int {

@@ -43,10 +43,10 @@ int gemv_rows_per_item(int wt, int mode, int K, int N, int active);
 // weights once per pass)
 int gemv_pass_tokens(int wt, int mode, int K);
 // bf16 groups of up to kSkinnyMaxRows rows on the matrix cores, weights
-// streamed once (ffn_skinny.hip): K a multiple of 512.  When the largest
+// streamed once (ffn_skinny.hip): K a multiple of 64.  When the largest
 // group of at most `cap` rows holds more than `lo`, every group of 1..cap
 // rows is served, else none (the GEMV then serves them).
-constexpr int kSkinnyMaxRows = 32;
+constexpr int kSkinnyMaxRows = 64;
 bool skinny_supported(int K, int N, int in_rows);
 hipError_t launch_skinny(int mode, const void* w0, const void* w1, const void* in, int in_rows, void* out,
                          const int32_t* counts, const int32_t* offsets, const int32_t* perm, int N, int K,

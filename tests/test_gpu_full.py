@@ -68,15 +68,16 @@ def test_mixtral_decode_full(orc):
     _check_layer(orc, cfg, d, y, counts, idx, sel=np.arange(cfg.T, dtype=np.int32))
 
 
-def test_mixtral_decode_t32_full(orc):
-    """The page's 32 x 4096 x 14336 top-2 shape: groups of ~8 rows on the GEMV
-    and the skinny MFMA kernel, larger ones on the MFMA tiles."""
-    cfg = C["mixtral_decode"].replace(name="mixtral_decode_t32", T=32)
-    say("full mixtral decode T=32")
+@pytest.mark.parametrize("T", [32, 96])
+def test_mixtral_decode_skinny_full(orc, T):
+    """The page's 32 x 4096 x 14336 top-2 shape (groups of 6-11 rows: the
+    one-tile skinny MFMA kernel) and 96 tokens (17-33 rows: three token tiles)."""
+    cfg = C["mixtral_decode"].replace(name=f"mixtral_decode_t{T}", T=T)
+    say(f"full mixtral decode T={T}")
     d = device_inputs(cfg)
     y, counts, idx = run_layer(cfg, d)
     say(f"  counts {counts.cpu().tolist()}")
-    _check_layer(orc, cfg, d, y, counts, idx, sel=np.arange(cfg.T, dtype=np.int32))
+    _check_layer(orc, cfg, d, y, counts, idx, sel=np.arange(0, cfg.T, max(1, cfg.T // 32), dtype=np.int32))
 
 
 def test_mixtral_prefill_full(orc):

@@ -48,7 +48,7 @@ SMALL = {
         model="s_int4_many", n_shared=1, w_std=0.05),
     # bf16 groups of 5-16 rows (counts 10 10 9 5 13 8 10 15): one group above a
     # GEMV pass sends every group to the one-tile skinny MFMA kernel.  It needs
-    # K % 512 == 0 and works in tiles of 32 weight rows: F = 1616 leaves a half
+    # K % 64 == 0 and works in tiles of 32 weight rows: F = 1616 leaves a half
     # last tile in gate/up (and keeps down off the kernel); d = 1040 keeps
     # gate/up off and leaves a half last tile in down
     "bf16_skinny_mix": moe_inputs.MoEConfig(
@@ -60,15 +60,24 @@ SMALL = {
     "bf16_skinny_down_ragged": moe_inputs.MoEConfig(
         "bf16_skinny_down_ragged", T=24, d=1040, E=4, k=2, F=1536, act="bf16", wt="bf16",
         model="s_bf16_skd", w_std=0.05),
-    # two token tiles (groups of 17-32 rows): counts 14 12 19 16 17 18, so the
-    # two-tile launch takes every group; with groups above 32 (35 39 39 18 29)
-    # those run on the MFMA tiles beside it
+    # more token tiles per weight operand: counts 14 12 19 16 17 18 (two
+    # tiles take every group), 35 39 39 18 29 (three tiles, 16-row gate/up
+    # items), 54 49 64 57 (four tiles, the largest group exactly 64) and
+    # 71 50 63 65 71 (groups above 64 on the 64-row MFMA tiles beside four
+    # skinny tiles).  F = 1408 is not a multiple of 512: the down pass's last
+    # K step has lines past the row end
     "bf16_skinny2": moe_inputs.MoEConfig(
         "bf16_skinny2", T=48, d=1024, E=6, k=2, F=1536, act="bf16", wt="bf16",
         model="s_bf16_sk2", w_std=0.05),
     "bf16_skinny2_mix": moe_inputs.MoEConfig(
         "bf16_skinny2_mix", T=80, d=1024, E=5, k=2, F=1536, act="bf16", wt="bf16",
         model="s_bf16_sk2", w_std=0.05),
+    "bf16_skinny4": moe_inputs.MoEConfig(
+        "bf16_skinny4", T=112, d=1024, E=4, k=2, F=1408, act="bf16", wt="bf16",
+        model="s_bf16_sk4", w_std=0.05),
+    "bf16_skinny4_mix": moe_inputs.MoEConfig(
+        "bf16_skinny4_mix", T=160, d=1024, E=5, k=2, F=1408, act="bf16", wt="bf16",
+        model="s_bf16_sk4", w_std=0.05),
     "f32_ragged": moe_inputs.MoEConfig(
         "f32_ragged", T=37, d=200, E=5, k=3, F=72, act="f32", wt="f32", model="s_f32"),
 }
@@ -474,7 +483,9 @@ def test_skinny_groups_exercised(orc):
                          and (c <= 16).all()),
                         ("bf16_skinny2", lambda c: ((c > 16) & (c <= 32)).any() and (c <= 16).any()
                          and (c <= 32).all()),
-                        ("bf16_skinny2_mix", lambda c: ((c > 16) & (c <= 32)).any() and (c > 32).any())]:
+                        ("bf16_skinny2_mix", lambda c: ((c > 32) & (c <= 48)).any() and (c <= 48).all()),
+                        ("bf16_skinny4", lambda c: (c == 64).any() and (c > 48).all() and (c <= 64).all()),
+                        ("bf16_skinny4_mix", lambda c: (c > 64).any() and ((c > 48) & (c <= 64)).any())]:
         cfg = SMALL[name]
         d = device_inputs(cfg)
         _, counts, _ = run_layer(cfg, d)
@@ -483,17 +494,30 @@ def test_skinny_groups_exercised(orc):
         assert check(c), name
 
 
-def test_skinny_two_tiles_ragged(orc):
-    """Two token tiles with a half last weight tile: F = 1616 (N % 32 == 16 in
-    gate/up) and an explicit tau of 32 (the default drops to 16 because the
-    down pass, K = 1616, cannot use the kernel; down then runs on the GEMV)."""
-    cfg = moe_inputs.MoEConfig("bf16_skinny2_ragged", T=56, d=1024, E=6, k=2, F=1616, act="bf16",
-                               wt="bf16", model="s_bf16_sk2r", w_std=0.05)
+SKINNY_TAU = [
+    # two token tiles with a half last weight tile: F = 1616 (N % 32 == 16 in
+    # gate/up); the default tau drops to 16 because the down pass (K = 1616)
+    # cannot use the kernel, which then runs on the GEMV
+    (moe_inputs.MoEConfig("bf16_skinny2_ragged", T=56, d=1024, E=6, k=2, F=1616, act="bf16",
+                          wt="bf16", model="s_bf16_sk2r", w_std=0.05), 32, 17, 32),
+    # three and four token tiles (16-row gate/up items) with short rows, where
+    # the default tau stops the kernel at 32 rows
+    (SMALL["bf16_skinny2_mix"], 64, 33, 48),
+    (SMALL["bf16_skinny4"], 64, 49, 64),
+    (SMALL["bf16_skinny4_mix"], 64, 49, 64),
+]
+
+
+@pytest.mark.parametrize("cfg,tau,lo,hi", SKINNY_TAU, ids=[c[0].name for c in SKINNY_TAU])
+def test_skinny_explicit_tau(orc, cfg, tau, lo, hi):
+    """Layer parity with an explicit tau that sends the largest group below the
+    MFMA tiles (lo..hi rows) to the skinny kernel's widest variant."""
     d = device_inputs(cfg)
-    y, counts, idx = run_layer(cfg, d, tau=32)
+    y, counts, idx = run_layer(cfg, d, tau=tau)
     c = counts.cpu().numpy()
-    say(f"  counts {c.tolist()}")
-    assert ((c > 16) & (c <= 32)).any() and (c <= 32).all()
+    say(f"  {cfg.name} tau {tau} counts {c.tolist()}")
+    small = c[c <= tau]
+    assert small.size and lo <= small.max() <= hi
     W, S = oracle_weights(d)
     x = np_store(d["x"])
     wr, br = np_store(d["w_router"]), np_store(d["b_router"])
