@@ -247,7 +247,11 @@ __device__ __forceinline__ void wait_copies(int n) {
     else __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
 }
 
-template <int MODE>
+// FAST (K a multiple of 64, at least two K pairs): every copy is issued from
+// the compute phase, between the MFMAs, with its offsets worked out during the
+// memory phase before; the memory phase then holds only the fragment reads.
+// Otherwise the copies go out in the memory phase (K tails, single pairs).
+template <int MODE, bool FAST>
 __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
     // A pair slots then B pair slots; pair j of a task (its K steps kb + 2j and
     // kb + 2j + 1) sits in A slot j % 2 and B slot j % 3
@@ -296,6 +300,14 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
     int c_an, c_bn;
     const int kc0 = (lane & 7) ^ ((lane >> 4) & 3);
     const int kodd = (((kc0 ^ 4) - kc0) * 16);
+    // FAST copies: the per-lane part of a copy offset does not depend on the
+    // task (row r0 of the tile and the lane's chunk; odd i take chunk ^ 4)
+    const int r0c = wave * 32 + (lane >> 3);
+    const uint32_t laneB_e = (uint32_t)((MODE == 0) ? (r0c & 127) : r0c) * row_bytes + (uint32_t)kc0 * 16u;
+    const uint32_t laneB_o = laneB_e + (uint32_t)kodd;
+    const uint32_t laneA_e = (uint32_t)r0c * row_bytes + (uint32_t)kc0 * 16u;
+    const uint32_t laneA_o = laneA_e + (uint32_t)kodd;
+    constexpr uint32_t TNB = (MODE == 0) ? 128u : (uint32_t)MF_BN;   // B-tile rows per N-tile step
     auto setup = [&](int t) __attribute__((always_inline)) {
         int L = t;
         c_kb = 0;
@@ -409,15 +421,23 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
             }
         };
         // transposed product: acc[mi][ni] is (B rows of fragment ni) x (tokens of fragment mi)
-        auto mma = [&]() __attribute__((always_inline)) {
+        // (FAST: copy i of the step goes out right after MFMA i, i < 4)
+        auto mma = [&](auto&& cp) __attribute__((always_inline)) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                    for (int ni = 0; ni < 2; ++ni)
+                    for (int ni = 0; ni < 2; ++ni) {
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][ni], fa[ks][mi],
                                                                                acc[mi][ni], 0, 0, 0);
+                        const int idx = ks * 8 + mi * 2 + ni;
+                        if (FAST && idx < 4) {
+                            __builtin_amdgcn_sched_barrier(0);
+                            cp(idx);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
         };
 
         // Copy schedule (groups of 4 copies per wave), one stream over the
@@ -435,42 +455,112 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
         // outstanding.  In-order completion also makes that wait cover this
         // wave's epilogue stores of the previous tile; the barrier makes every
         // wave's copies visible and ends all LDS reads of the previous pair.
+        //
+        // FAST schedule (copies in the compute phases, 4 per wave per step):
+        // at step 2j group 0 copies A(j+1) into the other A slot and group 1
+        // B(j+2) into the third B slot; at step 2j+1 group 0 copies B(j+2) and
+        // group 1 A(j+2) into this pair's A slot, which both groups have read
+        // by then (group 1 runs one phase behind, so its compute phase of step
+        // 2j+1 follows every read of pair j).  Group 0 waits at the end of
+        // step 2j+1 until only B(j+2) is outstanding (A(j+1) landed); group 1
+        // at the end of its memory phase of step 2j+1 until only B(j+2), its
+        // newest, is outstanding (A(j+1), issued at step 2j-1, landed).  Past
+        // the stream's end the copies are zero fills of slots nobody reads
+        // again, so every step issues exactly four.
         if (first || !stream) {
             ca = 0; cb = 0; nb = 1; tb = 2;
             issue(false, 0, sA0);
             issue(true, 0, sB0);
             if (P > 1) issue(true, 1, sB0 + MF_PSLOT);
+            if (FAST && grp == 1 && P > 1) issue(false, 1, sA0 + MF_PSLOT);
         }
         // the next task's loads go out behind this task's first copies and
         // land long before its own copies are issued
         if (has_next) setup(task + nblk);
+        int32x4_t RBN = RB;                           // B descriptor of the next task
+        if constexpr (FAST) RBN = make_desc(wsrc + (size_t)c_e * N * K, wmat);
         if (first || !stream) {
-            wait_copies(P > 1 ? 4 : 0);                // A0 and B0
+            wait_copies(P > 1 ? (FAST && grp == 1 ? 8 : 4) : 0);   // A0 and B0
             block_barrier();
             if (grp == 1) block_barrier();           // group 1 starts one phase later
         }
         first = false;
         // Per K step, each wave: memory phase (fragments of the step, then the
         // copies it issues), barrier, compute phase, barrier.
-        auto step = [&](int after1, int after2) __attribute__((always_inline)) {
+        auto step = [&](int after1, int after2, auto&& cp) __attribute__((always_inline)) {
             __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): own fragments read
             if (after1 >= 0) wait_copies(after1);
             block_barrier();
-            __builtin_amdgcn_s_setprio(1);
-            mma();
-            __builtin_amdgcn_s_setprio(0);
+            if (!FAST) __builtin_amdgcn_s_setprio(1);
+            mma(cp);
+            if (!FAST) __builtin_amdgcn_s_setprio(0);
             if (after2 >= 0) wait_copies(after2);
             block_barrier();
         };
+        auto nocp = [](int) {};
         const bool nxt = stream && has_next;
+        // FAST: offsets of this wave's four copies of A or B pair jb (this
+        // task's, the next task's, or zero fills), its descriptor and LDS row
+        uint32_t co[4];
+        int32x4_t rd = RA;
+        uint32_t lb = 0;
+        auto prepA = [&](int jb, const uint16_t* slot) __attribute__((always_inline)) {
+            const bool cur = jb < P;
+            const int kp = cur ? kb + 2 * jb : c_kb + 2 * (jb - P);
+            const bool on = cur || nxt;
+            const uint32_t kbyte = (uint32_t)kp * (uint32_t)(MF_BK * 2);
+            rd = RA;
+            if constexpr (AG) {
+                const uint32_t kadd = on ? kbyte : MF_OOB;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) co[i] = (cur ? aoff[i] : c_a[i]) + kadd;
+            } else {
+                // rows past the group read the next rows of h (or zeros past its
+                // end); their sums are never stored
+                const uint32_t ub = on ? (uint32_t)(cur ? p0 : c_p0) * row_bytes + kbyte : MF_OOB;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) co[i] = ((i & 1) ? laneA_o : laneA_e) + (ub + 8u * (uint32_t)i * row_bytes);
+            }
+            lb = lds_addr(&slot[(wave * 32) * MF_PK]);
+        };
+        auto prepB = [&](int jb, const uint16_t* slot) __attribute__((always_inline)) {
+            const bool cur = jb < P;
+            const int kp = cur ? kb + 2 * jb : c_kb + 2 * (jb - P);
+            const bool on = cur || nxt;
+            const uint32_t kbyte = (uint32_t)kp * (uint32_t)(MF_BK * 2);
+            rd.x = cur ? RB.x : RBN.x;
+            rd.y = cur ? RB.y : RBN.y;
+            rd.z = cur ? RB.z : RBN.z;
+            rd.w = RB.w;
+            // rows past N are past the expert's range: zeros
+            const uint32_t ub = on ? (uint32_t)(cur ? nt : c_nt) * TNB * row_bytes + kbyte : MF_OOB;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) co[i] = ((i & 1) ? laneB_o : laneB_e) + (ub + 8u * (uint32_t)i * row_bytes);
+            lb = lds_addr(&slot[(wave * 32) * MF_PK]);
+        };
+        auto cp = [&](int i) __attribute__((always_inline)) {
+            dma16(rd, co[i], lb + (uint32_t)(i * 8 * MF_PK * 2));
+        };
         for (int j = 0; j < P; ++j) {
             const uint16_t* sa = sA0 + ca * MF_PSLOT;
             const uint16_t* sb = sB0 + cb * MF_PSLOT;
+            if constexpr (FAST) {
+                read(sa, sb, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (grp == 0) prepA(j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
+                else prepB(j + 2, sB0 + tb * MF_PSLOT);
+                step(-1, -1, cp);
+                read(sa, sb, 1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (grp == 0) prepB(j + 2, sB0 + tb * MF_PSLOT);
+                else prepA(j + 2, sA0 + ca * MF_PSLOT);
+                step(grp == 0 ? -1 : 4, grp == 0 ? 4 : -1, cp);
+            } else {
             read(sa, sb, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (j + 1 < P) issue(false, j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
             else if (nxt) issue_next(false, 0, sA0 + (ca ^ 1) * MF_PSLOT);
-            step(-1, -1);
+            step(-1, -1, nocp);
             read(sa, sb, 1);
             __builtin_amdgcn_sched_barrier(0);
             bool bnew = true;
@@ -480,7 +570,8 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
             // A(j+1) lands before the next pair; at the task's end without a
             // streamed successor everything lands
             const int after = (j + 1 < P || nxt) && bnew ? 4 : 0;
-            step(grp == 0 ? -1 : after, after);
+            step(grp == 0 ? -1 : after, after, nocp);
+            }
             ca ^= 1;
             const int t = cb;
             cb = nb;
@@ -536,6 +627,8 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
         // group 1's last one, as group 1 had the extra barrier at the start
         if (!nxt && grp == 0) block_barrier();
     }
+    // the zero fills past the stream's end land before the block's LDS is released
+    if constexpr (FAST) wait_copies(0);
 }
 
 // Sum of the S partial tiles of each split tail tile, in part order, then the
@@ -797,10 +890,15 @@ hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void*
     // big tiles: one 512-thread block per CU
     const int slots = max_mt * nN;
     const int grid = slots < n_cu ? slots : n_cu;
-    if (mode == 0)
-        hipLaunchKernelGGL(mfma_ffn_kernel<0>, dim3(grid), dim3(512), 0, s, a);
-    else
-        hipLaunchKernelGGL(mfma_ffn_kernel<1>, dim3(grid), dim3(512), 0, s, a);
+    // copies from the compute phase need whole K pairs and at least two of them
+    const bool fast = K % (2 * MF_BK) == 0 && K >= 4 * MF_BK;
+    if (mode == 0) {
+        if (fast) hipLaunchKernelGGL((mfma_ffn_kernel<0, true>), dim3(grid), dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((mfma_ffn_kernel<0, false>), dim3(grid), dim3(512), 0, s, a);
+    } else {
+        if (fast) hipLaunchKernelGGL((mfma_ffn_kernel<1, true>), dim3(grid), dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((mfma_ffn_kernel<1, false>), dim3(grid), dim3(512), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.part_cap > 0) {

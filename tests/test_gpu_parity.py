@@ -28,6 +28,19 @@ SMALL = {
     "bf16_prefill_ragged": moe_inputs.MoEConfig(
         "bf16_prefill_ragged", T=600, d=256, E=6, k=2, F=328, act="bf16", wt="bf16",
         model="s_bf16_pre", w_std=0.05),
+    # 256-row MFMA tiles with K a multiple of 64 in both projections (copies
+    # issued from the compute phase): F = 384 gives gate/up three N-tiles,
+    # d = 320 leaves the down pass a 64-row last N-tile, ~320-row groups a
+    # ragged second M-tile, and the tail rounds are cut into K parts
+    "bf16_prefill_fast": moe_inputs.MoEConfig(
+        "bf16_prefill_fast", T=640, d=320, E=4, k=2, F=384, act="bf16", wt="bf16",
+        model="s_bf16_fast", w_std=0.05),
+    # more gate/up tiles (16 M-tiles x 20 N-tiles) than blocks: blocks run
+    # several tiles, the copy stream crosses into the next tile (and into K
+    # parts of the split last round)
+    "bf16_prefill_stream": moe_inputs.MoEConfig(
+        "bf16_prefill_stream", T=4096, d=256, E=2, k=1, F=2560, act="bf16", wt="bf16",
+        model="s_bf16_stream", w_std=0.05),
     "int4_shared_small": moe_inputs.MoEConfig(
         "int4_shared_small", T=16, d=512, E=16, k=4, F=256, act="bf16", wt="int4",
         model="s_int4", n_shared=1, w_std=0.05),
