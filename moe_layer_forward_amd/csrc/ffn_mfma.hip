@@ -421,8 +421,11 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
             }
         };
         // transposed product: acc[mi][ni] is (B rows of fragment ni) x (tokens of fragment mi)
-        // (FAST: copy i of the step goes out right after MFMA i, i < 4)
-        auto mma = [&](auto&& cp) __attribute__((always_inline)) {
+        // (FAST: copy i of the step goes out right after MFMA i * sp, i < 4:
+        // sp = 1 at the first step of a pair, whose copies include group 0's
+        // A(j+1) that must land within 1.5 phases, sp = 2 at the second)
+        auto mma = [&](auto&& cp, auto sp) __attribute__((always_inline)) {
+            constexpr int SP = decltype(sp)::value;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -432,9 +435,9 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][ni], fa[ks][mi],
                                                                                acc[mi][ni], 0, 0, 0);
                         const int idx = ks * 8 + mi * 2 + ni;
-                        if (FAST && idx < 4) {
+                        if (FAST && idx % SP == 0 && idx / SP < 4) {
                             __builtin_amdgcn_sched_barrier(0);
-                            cp(idx);
+                            cp(idx / SP);
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
@@ -487,12 +490,12 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
         first = false;
         // Per K step, each wave: memory phase (fragments of the step, then the
         // copies it issues), barrier, compute phase, barrier.
-        auto step = [&](int after1, int after2, auto&& cp) __attribute__((always_inline)) {
+        auto step = [&](int after1, int after2, auto&& cp, auto sp) __attribute__((always_inline)) {
             __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): own fragments read
             if (after1 >= 0) wait_copies(after1);
             block_barrier();
             if (!FAST) __builtin_amdgcn_s_setprio(1);
-            mma(cp);
+            mma(cp, sp);
             if (!FAST) __builtin_amdgcn_s_setprio(0);
             if (after2 >= 0) wait_copies(after2);
             block_barrier();
@@ -549,18 +552,18 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
                 __builtin_amdgcn_sched_barrier(0);
                 if (grp == 0) prepA(j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
                 else prepB(j + 2, sB0 + tb * MF_PSLOT);
-                step(-1, -1, cp);
+                step(-1, -1, cp, std::integral_constant<int, 1>{});
                 read(sa, sb, 1);
                 __builtin_amdgcn_sched_barrier(0);
                 if (grp == 0) prepB(j + 2, sB0 + tb * MF_PSLOT);
                 else prepA(j + 2, sA0 + ca * MF_PSLOT);
-                step(grp == 0 ? -1 : 4, grp == 0 ? 4 : -1, cp);
+                step(grp == 0 ? -1 : 4, grp == 0 ? 4 : -1, cp, std::integral_constant<int, 2>{});
             } else {
             read(sa, sb, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (j + 1 < P) issue(false, j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
             else if (nxt) issue_next(false, 0, sA0 + (ca ^ 1) * MF_PSLOT);
-            step(-1, -1, nocp);
+            step(-1, -1, nocp, std::integral_constant<int, 1>{});
             read(sa, sb, 1);
             __builtin_amdgcn_sched_barrier(0);
             bool bnew = true;
@@ -570,7 +573,7 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
             // A(j+1) lands before the next pair; at the task's end without a
             // streamed successor everything lands
             const int after = (j + 1 < P || nxt) && bnew ? 4 : 0;
-            step(grp == 0 ? -1 : after, after, nocp);
+            step(grp == 0 ? -1 : after, after, nocp, std::integral_constant<int, 1>{});
             }
             ca ^= 1;
             const int t = cb;
