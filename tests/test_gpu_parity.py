@@ -41,6 +41,11 @@ SMALL = {
     "bf16_prefill_stream": moe_inputs.MoEConfig(
         "bf16_prefill_stream", T=4096, d=256, E=2, k=1, F=2560, act="bf16", wt="bf16",
         model="s_bf16_stream", w_std=0.05),
+    # 128 experts of ~32 rows on the 64-row MFMA tiles, more tiles than two
+    # blocks per CU in both projections (~635 each: blocks take a second tile)
+    "bf16_small_split": moe_inputs.MoEConfig(
+        "bf16_small_split", T=512, d=1280, E=128, k=8, F=640, act="bf16", wt="bf16",
+        model="s_bf16_ssplit", w_std=0.05),
     "int4_shared_small": moe_inputs.MoEConfig(
         "int4_shared_small", T=16, d=512, E=16, k=4, F=256, act="bf16", wt="int4",
         model="s_int4", n_shared=1, w_std=0.05),
