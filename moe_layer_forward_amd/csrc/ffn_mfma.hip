@@ -15,11 +15,14 @@
 //  * block tile 256 x 256, eight wave64s in two groups of four (waves i and
 //    i+4 share a SIMD).  The groups ping-pong: while one issues the 16 MFMAs
 //    of a K step (v_mfma_f32_32x32x16_bf16, fp32 accumulators), the other
-//    reads its fragments of the step from LDS and issues its share of the
-//    global -> LDS copies; a block barrier swaps the roles.  A copy waiting
-//    for the texture-address queue therefore never holds up the matrix core.
-//    Group g owns tile rows 128g..128g+127; wave i of a group owns 64 B-tile
-//    rows (4 x 2 accumulators);
+//    reads its fragments of the step from LDS; a block barrier swaps the
+//    roles.  With K a multiple of 64 the global -> LDS copies go out between
+//    the MFMAs of the compute phase (each copy holds its wave ~60-75 cycles at
+//    issue, which the memory phase cannot spare, while an MFMA leaves room
+//    for one), their offsets worked out in the memory phase before; other K
+//    issue them at the end of the memory phase.  Group g owns tile rows
+//    128g..128g+127; wave i of a group owns 64 B-tile rows (4 x 2
+//    accumulators);
 //  * the product is computed transposed (weights as the MFMA A operand), so a
 //    lane's accumulator holds four consecutive output columns of one token
 //    row: the epilogue stores 16 (fp32) or 8 (bf16) bytes per lane straight
