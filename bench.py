@@ -116,6 +116,7 @@ class Runner:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ffn_ms = [a.elapsed_time(b) for a, b in evs]
+        self.last_ffn_p99 = float(np.percentile(ffn_ms, 99))
         # the single-call path, timed the same way (same kernels)
         t1 = time.perf_counter()
         for _ in range(steps):
@@ -395,6 +396,7 @@ def main():
         roof = dict(roofline_obj("mfma", tf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
                     kernel="expert FFN step (MFMA gate/up + down)", flops_per_launch=ffn_flops,
                     launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5),
+                    launch_ms_p99=round(run.last_ffn_p99, 5),
                     measured_mfma_ceiling=round(mceil, 1), mfma_ceiling_clock_ghz=round(mclk, 3),
                     frac_of_measured_ceiling=round(tf / mceil, 4))
     else:
@@ -406,6 +408,7 @@ def main():
                     kernel=f"expert FFN step ({ffn_paths(cfg, run.counts.cpu().tolist(), args.tau)}; weights {wt})",
                     bytes_per_launch=ffn_bytes,
                     launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5),
+                    launch_ms_p99=round(run.last_ffn_p99, 5),
                     measured_read_ceiling=round(ceil, 1),
                     frac_of_measured_ceiling=round(achieved / ceil, 4))
     out = {
@@ -440,6 +443,8 @@ def main():
             "roofline": dict(roofline_obj("mfma", ptf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
                              kernel="expert FFN step (MFMA gate/up + down)",
                              flops_per_launch=pflops, launch_ms=round(pffn_mean, 4),
+                             launch_ms_median=round(pffn_med, 4),
+                             launch_ms_p99=round(prun.last_ffn_p99, 4),
                              measured_mfma_ceiling=round(mceil, 1),
                              mfma_ceiling_clock_ghz=round(mclk, 3),
                              frac_of_measured_ceiling=round(ptf / mceil, 4)),
