@@ -562,21 +562,21 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
                 else prepA(j + 2, sA0 + ca * MF_PSLOT);
                 step(grp == 0 ? -1 : 4, grp == 0 ? 4 : -1, cp, std::integral_constant<int, 2>{});
             } else {
-            read(sa, sb, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (j + 1 < P) issue(false, j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
-            else if (nxt) issue_next(false, 0, sA0 + (ca ^ 1) * MF_PSLOT);
-            step(-1, -1, nocp, std::integral_constant<int, 1>{});
-            read(sa, sb, 1);
-            __builtin_amdgcn_sched_barrier(0);
-            bool bnew = true;
-            if (j + 2 < P) issue(true, j + 2, sB0 + tb * MF_PSLOT);
-            else if (nxt) issue_next(true, j + 2 - P, sB0 + tb * MF_PSLOT);
-            else bnew = false;
-            // A(j+1) lands before the next pair; at the task's end without a
-            // streamed successor everything lands
-            const int after = (j + 1 < P || nxt) && bnew ? 4 : 0;
-            step(grp == 0 ? -1 : after, after, nocp, std::integral_constant<int, 1>{});
+                read(sa, sb, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (j + 1 < P) issue(false, j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
+                else if (nxt) issue_next(false, 0, sA0 + (ca ^ 1) * MF_PSLOT);
+                step(-1, -1, nocp, std::integral_constant<int, 1>{});
+                read(sa, sb, 1);
+                __builtin_amdgcn_sched_barrier(0);
+                bool bnew = true;
+                if (j + 2 < P) issue(true, j + 2, sB0 + tb * MF_PSLOT);
+                else if (nxt) issue_next(true, j + 2 - P, sB0 + tb * MF_PSLOT);
+                else bnew = false;
+                // A(j+1) lands before the next pair; at the task's end without a
+                // streamed successor everything lands
+                const int after = (j + 1 < P || nxt) && bnew ? 4 : 0;
+                step(grp == 0 ? -1 : after, after, nocp, std::integral_constant<int, 1>{});
             }
             ca ^= 1;
             const int t = cb;
