@@ -192,9 +192,17 @@ __device__ __forceinline__ int32x4_t make_desc(const void* base, uint32_t nbytes
 // which lets LDS fragment reads of one stage proceed while later stages are
 // still being filled.
 __device__ __forceinline__ void dma16(const int32x4_t& desc, uint32_t off, uint32_t lds_addr) {
+    // the descriptor and the LDS address are wave-uniform; readfirstlane keeps
+    // them in scalar registers even where the compiler cannot prove it
+    int32x4_t d;
+    d.x = __builtin_amdgcn_readfirstlane(desc.x);
+    d.y = __builtin_amdgcn_readfirstlane(desc.y);
+    d.z = __builtin_amdgcn_readfirstlane(desc.z);
+    d.w = __builtin_amdgcn_readfirstlane(desc.w);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "v"(off), "s"(desc), "s"(lds_addr)
+                 : "v"(off), "s"(d), "s"(m0)
                  : "memory");
 }
 
