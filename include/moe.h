@@ -203,26 +203,6 @@ int moe_rmsnorm(const moe_shape *shape, const void *h, const float *gamma, float
 int moe_pack_int4_tiled(const void *src, void *dst, int64_t n_mats, int32_t N, int32_t K,
                         void *stream, char *err, size_t err_len);
 
-/* Measurement helper, not part of the layer: the matrix-core ceiling.  Each
- * CU runs eight waves of iters x 8 independent bf16 MFMAs (32x32x16, fp32
- * accumulate) with no memory traffic; one float per wave is written to sink
- * (device, at least 32 bytes per CU: sink_bytes is checked).  clock (device,
- * 2 x uint64, or NULL) receives block 0's shader-clock cycles and 100 MHz
- * ticks over the loop (their ratio is the shader clock).  *flops (host, or
- * NULL) receives the launch's floating-point operation count; the caller
- * times the launch.  Asynchronous on stream.  MOE_EINVAL for iters outside
- * [1, 2^24], a NULL or misaligned sink, a short sink or a misaligned clock. */
-int moe_mfma_ceiling(int32_t iters, float *sink, size_t sink_bytes, uint64_t *clock,
-                     int64_t *flops, void *stream, char *err, size_t err_len);
-
-/* Measurement helper, not part of the layer: reads bytes of device memory at
- * buf once with plain streaming loads and XORs every 32-bit word of it into
- * *sink (device, caller-initialised), the measured HBM read ceiling beside the
- * published peak.  bytes a multiple of 16, buf 16-byte aligned; asynchronous
- * on stream.  MOE_EINVAL for a NULL or misaligned pointer or a bad size. */
-int moe_read_ceiling(const void *buf, size_t bytes, uint32_t *sink, void *stream, char *err,
-                     size_t err_len);
-
 /* Static text of a moe_status. */
 const char *moe_strerror(int status);
 

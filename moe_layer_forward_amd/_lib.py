@@ -19,8 +19,7 @@ MOE_F32, MOE_BF16, MOE_INT4_G128, MOE_INT4_G128_TILED = 0, 1, 2, 3
 DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128, "int4_tiled": MOE_INT4_G128_TILED}
 
 EXPORTS = ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_workspace_bytes", "moe_rmsnorm", "moe_pack_int4_tiled", "moe_read_ceiling",
-           "moe_mfma_ceiling", "moe_strerror")
+           "moe_workspace_bytes", "moe_rmsnorm", "moe_pack_int4_tiled", "moe_strerror")
 
 
 class MoEError(RuntimeError):
@@ -61,14 +60,11 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.argtypes = [sp]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_rmsnorm.argtypes = [sp, vp, vp, ctypes.c_float, vp, vp, cp, sz]
-        L.moe_read_ceiling.argtypes = [vp, sz, vp, vp, cp, sz]
-        L.moe_mfma_ceiling.argtypes = [ctypes.c_int32, vp, sz, vp, ctypes.POINTER(ctypes.c_int64), vp, cp, sz]
         L.moe_pack_int4_tiled.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, cp, sz]
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                  "moe_layer_forward", "moe_rmsnorm", "moe_pack_int4_tiled", "moe_read_ceiling",
-                  "moe_mfma_ceiling"):
+                  "moe_layer_forward", "moe_rmsnorm", "moe_pack_int4_tiled"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -152,20 +148,6 @@ def moe_layer_forward(shape, x, w_router, b_router, weights, residual, y, counts
 def moe_pack_int4_tiled(src, dst, n_mats, N, K, stream=None):
     """Row-major int4 codes (n_mats x [N][K/2] bytes) -> the tiled layout."""
     return _call("moe_pack_int4_tiled", _ptr(src), _ptr(dst), int(n_mats), int(N), int(K), _stream(stream))
-
-
-def moe_mfma_ceiling(iters, sink, sink_bytes, clock=None, stream=None):
-    """Independent bf16 MFMAs on every CU (measurement helper); returns the
-    launch's flop count.  clock: device uint64[2] (shader cycles, 100 MHz ticks)."""
-    flops = ctypes.c_int64(0)
-    _call("moe_mfma_ceiling", int(iters), _ptr(sink), int(sink_bytes), _ptr(clock), ctypes.byref(flops),
-          _stream(stream))
-    return flops.value
-
-
-def moe_read_ceiling(buf, nbytes, sink, stream=None):
-    """Streaming read of nbytes at buf, XORed into sink (measurement helper)."""
-    return _call("moe_read_ceiling", _ptr(buf), int(nbytes), _ptr(sink), _stream(stream))
 
 
 def moe_rmsnorm(shape, h, gamma, eps, out, stream=None):

@@ -14,6 +14,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <atomic>
 #include "moe.h"
 
 using namespace moe;
@@ -33,13 +34,17 @@ int fail(char* err, size_t len, int code, const char* fmt, ...) {
     return code;
 }
 
+// MOE_DEBUG_SYNC is read once per process (a benign race: every reader
+// computes the same value)
 bool debug_sync() {
-    static int v = -1;
-    if (v < 0) {
+    static std::atomic<int> v{-1};
+    int r = v.load(std::memory_order_relaxed);
+    if (r < 0) {
         const char* e = getenv("MOE_DEBUG_SYNC");
-        v = (e && e[0] && e[0] != '0') ? 1 : 0;
+        r = (e && e[0] && e[0] != '0') ? 1 : 0;
+        v.store(r, std::memory_order_relaxed);
     }
-    return v == 1;
+    return r == 1;
 }
 
 int hip_check(hipError_t e, hipStream_t s, const char* what, char* err, size_t len) {
@@ -98,7 +103,9 @@ int check_shape(const moe_shape* s, char* err, size_t err_len) {
     if (s->wt == MOE_INT4_G128_TILED && (!i4mfma_supported(s->d, s->F) || !i4mfma_supported(s->F, s->d)))
         return fail(err, err_len, MOE_EUNSUPPORTED,
                     "tiled int4 weights need d and F multiples of 1024 and at most 8192 (d=%d F=%d)", s->d, s->F);
-    const int kmax = gemv_max_k(int4 ? MOE_INT4_G128 : s->wt);
+    // the GEMV's register-resident token fragments bound K; int4 is held to
+    // the 16384 the header states (the GEMV could take 32768)
+    const int kmax = int4 ? std::min(16384, gemv_max_k(MOE_INT4_G128)) : gemv_max_k(s->wt);
     if (s->d > kmax || s->F > kmax)
         return fail(err, err_len, MOE_EUNSUPPORTED, "d=%d / F=%d exceed this build's limit %d for this dtype",
                     s->d, s->F, kmax);
@@ -108,9 +115,15 @@ int check_shape(const moe_shape* s, char* err, size_t err_len) {
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t logits, idx, w, counts, offsets, perm, inv, tiles, h, yp, hs, ys, part, total;
+    size_t logits, idx, w, counts, offsets, perm, inv, tiles, h, yp, hs, ys, sid, part, total;
     int part_cap;
 };
+
+bool is_int4(const moe_shape* s) { return s->wt == MOE_INT4_G128 || s->wt == MOE_INT4_G128_TILED; }
+
+// The shared expert of bf16 and fp32 layers runs as a group of its own (one
+// expert that every token picks once): counts, offsets and an identity perm.
+bool shared_as_group(const moe_shape* s) { return s->n_shared && !is_int4(s); }
 
 int effective_tau(const moe_shape* s);
 
@@ -142,6 +155,7 @@ Layout layout(const moe_shape* s) {
     L.yp = o; o += up(tk * d * 4);
     L.hs = o; o += s->n_shared ? up(T * F * hb) : 0;
     L.ys = o; o += s->n_shared ? up(T * d * 4) : 0;
+    L.sid = o; o += shared_as_group(s) ? up((3 + T) * 4) : 0;
     L.part_cap = part_cap(s);
     L.part = o; o += up((size_t)L.part_cap * 256 * 256 * 4);
     L.total = o;
@@ -165,16 +179,27 @@ int effective_tau(const moe_shape* s) {
     return s->tau;
 }
 
-// The FFN launch sequence shared by moe_expert_ffn and moe_layer_forward.
-int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32_t* counts,
-            const int32_t* offsets, const int32_t* perm, float* y_perm, float* y_shared,
-            char* ws, hipStream_t st, char* err, size_t err_len) {
-    const Layout L = layout(s);
+// Workspace regions one expert-FFN pass writes: h, the MFMA tile plan and
+// the partial tiles of the split tail round.
+struct FfnBufs {
+    void* h;
+    int32_t* tiles;
+    float* part;
+    int part_cap;
+};
+
+// The FFN launch sequence of the routed experts, shared by moe_expert_ffn and
+// moe_layer_forward; an int4 shared expert rides along in the same launches,
+// a bf16 or fp32 one runs afterwards as a one-expert group (run_ffn).
+int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const int32_t* counts,
+               const int32_t* offsets, const int32_t* perm, float* y_perm, float* y_shared,
+               const FfnBufs& b, void* hs, hipStream_t st, char* err, size_t err_len) {
     const int tau = effective_tau(s);
     const bool use_mfma = tau >= 0 && s->T > tau;
-    void* h = ws + L.h;
-    int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
-    float* part = L.part_cap ? reinterpret_cast<float*>(ws + L.part) : nullptr;
+    void* h = b.h;
+    int32_t* tiles = b.tiles;
+    float* part = b.part_cap ? b.part : nullptr;
+    const int part_cap = b.part_cap;
     const int max_mt = mfma_max_tiles(s->T, s->k, s->E);
     const int max_rows_gemv = use_mfma ? tau : s->T;   // a group holds at most T rows
     int rc;
@@ -196,7 +221,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     g.tau = use_mfma ? tau : -1;
     GemvArgs q{};
     q.topk = 1; q.T = s->T; q.E = 1; q.tau = -1;
-    const GemvArgs* qp = s->n_shared ? &q : nullptr;
+    const GemvArgs* qp = (s->n_shared && is_int4(s)) ? &q : nullptr;
     const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
     const bool tiled = s->wt == MOE_INT4_G128_TILED;
     // bf16 groups below the MFMA tiles: when one of them is larger than a
@@ -244,7 +269,6 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     };
 
     // gate/up + SwiGLU
-    void* hs = s->n_shared ? ws + L.hs : nullptr;
     g.w0 = w->w_gate; g.w1 = w->w_up;
     g.s0 = (const uint16_t*)w->s_gate; g.s1 = (const uint16_t*)w->s_up;
     g.in = x; g.out = h; g.N = s->F; g.K = s->d;
@@ -254,7 +278,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     rc = pass(0, "gate/up");
     if (rc) return rc;
     if (use_mfma) {
-        rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, s->E, s->T, part, L.part_cap, st),
+        rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, s->E, s->T, part, part_cap, st),
                        st, "mfma gate/up", err, err_len);
         if (rc) return rc;
     }
@@ -268,11 +292,41 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     rc = pass(1, "down");
     if (rc) return rc;
     if (use_mfma) {
-        rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, s->E, s->T * s->k, part, L.part_cap, st),
+        rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, s->E, s->T * s->k, part, part_cap, st),
                        st, "mfma down", err, err_len);
         if (rc) return rc;
     }
     return MOE_OK;
+}
+
+// Routed experts, then (bf16 and fp32 layers) the shared expert through the
+// same kernel selection as a group of all T tokens: groups above tau on the
+// MFMA tiles, smaller ones on the skinny kernel or the GEMV.  Its y_perm is
+// y_shared (identity order) and its h the shared region of the workspace.
+int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32_t* counts,
+            const int32_t* offsets, const int32_t* perm, float* y_perm, float* y_shared,
+            char* ws, hipStream_t st, char* err, size_t err_len) {
+    const Layout L = layout(s);
+    const FfnBufs b{ws + L.h, reinterpret_cast<int32_t*>(ws + L.tiles), reinterpret_cast<float*>(ws + L.part),
+                    L.part_cap};
+    void* hs = s->n_shared ? ws + L.hs : nullptr;
+    int rc = run_groups(s, x, w, counts, offsets, perm, y_perm, y_shared, b, hs, st, err, err_len);
+    if (rc || !shared_as_group(s) || s->T == 0) return rc;
+    moe_shape sh = *s;
+    sh.E = 1;
+    sh.k = 1;
+    sh.n_shared = 0;
+    moe_weights sw{};
+    sw.w_gate = w->sh_gate;
+    sw.w_up = w->sh_up;
+    sw.w_down = w->sh_down;
+    int32_t* sid = reinterpret_cast<int32_t*>(ws + L.sid);
+    rc = hip_check(launch_identity_group(sid, sid + 1, sid + 3, s->T, st), st, "shared group", err, err_len);
+    if (rc) return rc;
+    // the routed plan and partial tiles are consumed by now (stream order); a
+    // one-expert group needs no more of either than the routed experts do
+    const FfnBufs bs{hs, b.tiles, b.part, std::min(part_cap(&sh), L.part_cap)};
+    return run_groups(&sh, x, &sw, sid, sid + 1, sid + 3, y_shared, nullptr, bs, nullptr, st, err, err_len);
 }
 
 int check_weights(const moe_shape* s, const moe_weights* w, char* err, size_t err_len) {
@@ -484,29 +538,6 @@ int moe_pack_int4_tiled(const void* src, void* dst, int64_t n_mats, int32_t N, i
     if (a < b + bytes && b < a + bytes) return fail(err, err_len, MOE_EINVAL, "src and dst overlap");
     hipStream_t st = (hipStream_t)stream;
     return hip_check(launch_pack_int4_tiled(src, dst, (size_t)n_mats, N, K, st), st, "pack int4", err, err_len);
-}
-
-int moe_mfma_ceiling(int32_t iters, float* sink, size_t sink_bytes, uint64_t* clock, int64_t* flops, void* stream,
-                     char* err, size_t err_len) {
-    if (iters < 1 || iters > (1 << 24)) return fail(err, err_len, MOE_EINVAL, "iters=%d out of range [1, 2^24]", iters);
-    NEED_PTR(sink, "sink");
-    const int blocks = mfma_ceiling_blocks();
-    if (sink_bytes < (size_t)blocks * 8 * sizeof(float))
-        return fail(err, err_len, MOE_EINVAL, "sink_bytes=%zu below %zu", sink_bytes, (size_t)blocks * 8 * sizeof(float));
-    if (clock && (uintptr_t)clock % 8) return fail(err, err_len, MOE_EINVAL, "clock is not 8-byte aligned");
-    if (flops) *flops = (int64_t)blocks * 8 * iters * 8 * (2LL * 32 * 32 * 16);
-    hipStream_t st = (hipStream_t)stream;
-    return hip_check(launch_mfma_ceiling(iters, sink, clock, st), st, "mfma ceiling", err, err_len);
-}
-
-int moe_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, void* stream, char* err, size_t err_len) {
-    if (bytes % 16) return fail(err, err_len, MOE_EINVAL, "bytes=%zu is not a multiple of 16", bytes);
-    if (bytes) NEED_PTR(buf, "buf");
-    if (!sink) return fail(err, err_len, MOE_EINVAL, "sink is NULL");
-    if ((uintptr_t)sink % 4) return fail(err, err_len, MOE_EINVAL, "sink is not 4-byte aligned");
-    if (!bytes) return MOE_OK;
-    hipStream_t st = (hipStream_t)stream;
-    return hip_check(launch_read_ceiling(buf, bytes, sink, st), st, "read ceiling", err, err_len);
 }
 
 }  // extern "C"

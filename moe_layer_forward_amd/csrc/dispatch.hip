@@ -125,4 +125,25 @@ hipError_t launch_dispatch(const int32_t* idx, int32_t* counts, int32_t* offsets
     return hipGetLastError();
 }
 
+// The always-on shared expert as one group over all n tokens in token order:
+// counts = {n}, offsets = {0, n}, perm = identity, so the expert kernels run
+// it exactly as a routed expert that every token picked with one slot.
+__global__ __launch_bounds__(256) void identity_group_kernel(int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ perm, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) perm[i] = i;
+    if (i == 0) {
+        counts[0] = n;
+        offsets[0] = 0;
+        offsets[1] = n;
+    }
+}
+
+hipError_t launch_identity_group(int32_t* counts, int32_t* offsets, int32_t* perm, int n, hipStream_t s) {
+    const int blocks = n > 0 ? (n + 255) / 256 : 1;
+    hipLaunchKernelGGL(identity_group_kernel, dim3(blocks), dim3(256), 0, s, counts, offsets, perm, n);
+    return hipGetLastError();
+}
+
 }  // namespace moe

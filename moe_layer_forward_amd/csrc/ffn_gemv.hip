@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "devinfo.h"
 #include "kernels.h"
 
 namespace moe {
@@ -517,15 +518,14 @@ int gemv_max_k(int wt) { return wt == DT_INT4 ? 4 * 4 * 64 * 32 : 4 * 8 * 64 * e
 template <int WT, int ACT, int MODE, int NT, int KS, int R, int MS>
 static hipError_t launch_v(const GemvArgs& a, int max_items, hipStream_t s) {
     auto k = gemv_kernel<WT, ACT, MODE, NT, KS, R, MS>;
-    static int per_cu = 0, n_cu = 0;
-    if (per_cu == 0) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, 256, 0) != hipSuccess || per_cu < 1)
-            per_cu = 1;
-        if (n_cu < 1) n_cu = 256;
-    }
+    // resident blocks per CU of this variant, per device
+    static std::atomic<int> occ[kMaxDevices];
+    const int per_cu = per_device_int(occ, [&] {
+        int v = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k, 256, 0) != hipSuccess) v = 1;
+        return v;
+    });
+    const int n_cu = cu_count();
     int grid = per_cu * n_cu;
     if (grid > max_items) grid = max_items;
     if (grid < 1) grid = 1;

@@ -47,6 +47,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "devinfo.h"
 #include "kernels.h"
 
 namespace moe {
@@ -508,25 +509,19 @@ hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const Gem
     if (a.E > kMaxE || a.P < 1) return hipErrorInvalidValue;
     const size_t lds = (size_t)(a.P + 1) * ((size_t)g.K * 2 + 16) + (size_t)(g.K / 128) * 16 * 4;
 
-    static int n_cu = 0;
-    static bool attr_set[4] = {false, false, false, false};
-    if (n_cu == 0) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (n_cu < 1) n_cu = 256;
-    }
+    const int n_cu = cu_count();
     // 8 scale groups per wave in flight: 16 KB (gate/up) or 8 KB (down)
     auto k = mode == 0 ? (tiled ? i4_mfma_kernel<0, 8, true> : i4_mfma_kernel<0, 8, false>)
                        : (tiled ? i4_mfma_kernel<1, 8, true> : i4_mfma_kernel<1, 8, false>);
+    // dynamic LDS beyond 64 KB: the budget left next to the static arrays,
+    // set once per device and kernel variant
+    static std::atomic<int> attr_set[4][kMaxDevices];
     const int ki = mode * 2 + (tiled ? 1 : 0);
-    if (!attr_set[ki]) {
-        // dynamic LDS beyond 64 KB: the budget left next to the static arrays
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+    per_device_int(attr_set[ki], [&] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)(kLdsBytes - kStaticLds));
-        attr_set[ki] = true;
-    }
+        return 1;
+    });
     hipLaunchKernelGGL(k, dim3(n_cu), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }

@@ -50,6 +50,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "devinfo.h"
 #include "kernels.h"
 
 namespace moe {
@@ -190,7 +191,9 @@ __device__ __forceinline__ int32x4_t make_desc(const void* base, uint32_t nbytes
 // Issued as inline assembly so that the compiler's wait-count pass does not
 // model it: the kernel waits for these copies itself (vmcnt + s_barrier),
 // which lets LDS fragment reads of one stage proceed while later stages are
-// still being filled.
+// still being filled.  The LDS address reaches the instruction through m0 as
+// an input operand bound to that register ("{m0}"), so the compiler itself
+// writes m0 and knows it is in use: no live value of its own can sit there.
 __device__ __forceinline__ void dma16(const int32x4_t& desc, uint32_t off, uint32_t lds_addr) {
     // the descriptor and the LDS address are wave-uniform; readfirstlane keeps
     // them in scalar registers even where the compiler cannot prove it
@@ -200,9 +203,9 @@ __device__ __forceinline__ void dma16(const int32x4_t& desc, uint32_t off, uint3
     d.z = __builtin_amdgcn_readfirstlane(desc.z);
     d.w = __builtin_amdgcn_readfirstlane(desc.w);
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
-                 : "v"(off), "s"(d), "s"(m0)
+                 : "v"(off), "s"(d), "{m0}"(m0)
                  : "memory");
 }
 
@@ -893,13 +896,7 @@ hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void*
     a.in_rows = in_rows;
     a.part = part;
     a.part_cap = part ? part_cap : 0;
-    static int n_cu = 0;
-    if (n_cu == 0) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
-            n_cu = 256;
-    }
+    const int n_cu = cu_count();
     const int nN = mfma_ntiles_n(mode, N);
     // big tiles: one 512-thread block per CU
     const int slots = max_mt * nN;

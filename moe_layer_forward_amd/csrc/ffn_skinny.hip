@@ -46,6 +46,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "devinfo.h"
 #include "kernels.h"
 
 namespace moe {
@@ -498,13 +499,7 @@ hipError_t launch_skinny(int mode, const void* w0, const void* w1, const void* i
     if (E > kMaxE || !skinny_supported(K, N, in_rows) || !counts || !offsets || (mode == 0 && !perm) ||
         lo < 0 || cap <= lo || cap > kSkinnyMaxRows)
         return hipErrorInvalidValue;
-    static int n_cu = 0;
-    if (n_cu == 0) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (n_cu < 1) n_cu = 256;
-    }
+    const int n_cu = cu_count();
     // a block's range of ceil(items / grid) items touches at most
     // U / grid + 3 experts (each expert owns >= 1 item): kMaxPairs bounds
     // that for E <= 256 and a grid of >= 8 blocks

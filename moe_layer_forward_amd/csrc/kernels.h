@@ -28,6 +28,8 @@ hipError_t launch_route(int act, const void* x, const float* wg, const float* b,
                         int32_t* idx, float* w, int T, int d, int E, int k, hipStream_t s);
 hipError_t launch_dispatch(const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv, int T, int k, int E, hipStream_t s);
+// counts = {n}, offsets = {0, n}, perm = 0..n-1: the shared expert as a group
+hipError_t launch_identity_group(int32_t* counts, int32_t* offsets, int32_t* perm, int n, hipStream_t s);
 hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, int max_rows,
                        hipStream_t s);
 int gemv_max_k(int wt);
@@ -66,9 +68,6 @@ int mfma_part_cap();
 hipError_t launch_combine(int act, const float* yp, const int32_t* inv, const float* w,
                           const float* ys, const void* res, void* y, int T, int d, int k,
                           hipStream_t s);
-hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
-int mfma_ceiling_blocks();
-hipError_t launch_mfma_ceiling(int iters, float* sink, uint64_t* clk, hipStream_t s);
 hipError_t launch_rmsnorm(int act, const void* h, const float* gamma, float eps, void* out, int T,
                           int d, hipStream_t s);
 

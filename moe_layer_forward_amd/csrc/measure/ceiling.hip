@@ -1,4 +1,5 @@
-// Measurement helpers, not part of the layer: a plain streaming read of a
+// libmoe_measure.so: measurement helpers, not part of the layer and not linked
+// into libmoe.so.  A plain streaming read of a
 // device buffer (the measured HBM ceiling the decode kernels are compared with
 // beside the published 8 TB/s) and a loop of independent bf16 MFMAs (the
 // measured matrix-core ceiling beside the published 2.5 PFLOP/s, with the
@@ -10,8 +11,12 @@
 // loads cannot be dropped.  Of the shapes tried on MI355X (grid-strided or
 // per-wave runs, 1-8 blocks per CU, 4-16 loads in flight, temporal or not)
 // this one read fastest: more streams in flight per CU read slower.
+#include <stdarg.h>
+#include <stdio.h>
+
 #include "common.h"
-#include "kernels.h"
+#include "devinfo.h"
+#include "moe_measure.h"
 
 namespace moe {
 
@@ -83,33 +88,56 @@ __global__ __launch_bounds__(512, 1) void mfma_ceiling_kernel(int iters, float* 
     }
 }
 
-int mfma_ceiling_blocks() {
-    static int n_cu = 0;
-    if (n_cu == 0) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (n_cu < 1) n_cu = 256;
-    }
-    return n_cu;
-}
-
-hipError_t launch_mfma_ceiling(int iters, float* sink, uint64_t* clk, hipStream_t s) {
-    hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(mfma_ceiling_blocks()), dim3(512), 0, s, iters, sink, clk);
-    return hipGetLastError();
-}
-
-hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s) {
-    static int n_cu = 0;
-    if (n_cu == 0) {
-        int dev = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (n_cu < 1) n_cu = 256;
-    }
-    hipLaunchKernelGGL(read_ceiling_kernel, dim3(n_cu), dim3(256), 0, s,
-                       reinterpret_cast<const u32x4_t*>(buf), bytes / 16, sink);
-    return hipGetLastError();
-}
-
 }  // namespace moe
+
+namespace {
+
+int fail(char* err, size_t len, int code, const char* fmt, ...) {
+    if (err && len > 0) {
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(err, len, fmt, ap);
+        va_end(ap);
+    }
+    return code;
+}
+
+int launched(char* err, size_t len, const char* what) {
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_MEASURE_OK : fail(err, len, MOE_MEASURE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_mfma_ceiling(int32_t iters, float* sink, size_t sink_bytes, uint64_t* clock, int64_t* flops, void* stream,
+                     char* err, size_t err_len) {
+    if (iters < 1 || iters > (1 << 24))
+        return fail(err, err_len, MOE_MEASURE_EINVAL, "iters=%d out of range [1, 2^24]", iters);
+    if (!sink) return fail(err, err_len, MOE_MEASURE_EINVAL, "sink is NULL");
+    if ((uintptr_t)sink % 16) return fail(err, err_len, MOE_MEASURE_EINVAL, "sink is not 16-byte aligned");
+    const int blocks = moe::cu_count();
+    if (sink_bytes < (size_t)blocks * 8 * sizeof(float))
+        return fail(err, err_len, MOE_MEASURE_EINVAL, "sink_bytes=%zu below %zu", sink_bytes,
+                    (size_t)blocks * 8 * sizeof(float));
+    if (clock && (uintptr_t)clock % 8) return fail(err, err_len, MOE_MEASURE_EINVAL, "clock is not 8-byte aligned");
+    if (flops) *flops = (int64_t)blocks * 8 * iters * 8 * (2LL * 32 * 32 * 16);
+    hipLaunchKernelGGL(moe::mfma_ceiling_kernel, dim3(blocks), dim3(512), 0, (hipStream_t)stream, iters, sink,
+                       clock);
+    return launched(err, err_len, "mfma ceiling");
+}
+
+int moe_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, void* stream, char* err, size_t err_len) {
+    if (bytes % 16) return fail(err, err_len, MOE_MEASURE_EINVAL, "bytes=%zu is not a multiple of 16", bytes);
+    if (bytes && !buf) return fail(err, err_len, MOE_MEASURE_EINVAL, "buf is NULL");
+    if (bytes && (uintptr_t)buf % 16) return fail(err, err_len, MOE_MEASURE_EINVAL, "buf is not 16-byte aligned");
+    if (!sink) return fail(err, err_len, MOE_MEASURE_EINVAL, "sink is NULL");
+    if ((uintptr_t)sink % 4) return fail(err, err_len, MOE_MEASURE_EINVAL, "sink is not 4-byte aligned");
+    if (!bytes) return MOE_MEASURE_OK;
+    hipLaunchKernelGGL(moe::read_ceiling_kernel, dim3(moe::cu_count()), dim3(256), 0, (hipStream_t)stream,
+                       reinterpret_cast<const moe::u32x4_t*>(buf), bytes / 16, sink);
+    return launched(err, err_len, "read ceiling");
+}
+
+}  // extern "C"

@@ -11,19 +11,30 @@ import moe_layer_forward_amd as moe
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_symbols():
-    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+def declared_symbols(header):
+    with open(os.path.join(ROOT, "include", header)) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
-def test_library_exports_every_declared_symbol():
-    L = moe.lib()
-    names = declared_symbols()
-    assert set(names) == set(moe.EXPORTS)
+def test_every_header_is_covered():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["moe.h", "moe_measure.h"]
+
+
+@pytest.mark.parametrize("header,binding", [("moe.h", moe), ("moe_measure.h", moe.measure)])
+def test_library_exports_every_declared_symbol(header, binding):
+    L = binding.lib()
+    names = declared_symbols(header)
+    assert set(names) == set(binding.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_measure_helpers_not_in_layer_library():
+    L = moe.lib()
+    for n in moe.measure.EXPORTS:
+        assert not hasattr(L, n), n
 
 
 def test_strerror():
@@ -60,6 +71,7 @@ BAD_SHAPES = [
     (dict(act="f32", wt="bf16"), moe.MOE_EUNSUPPORTED),
     (dict(act="bf16", wt="f32"), moe.MOE_EUNSUPPORTED),
     (dict(d=20480), moe.MOE_EUNSUPPORTED),
+    (dict(wt="int4", d=16384 + 128), moe.MOE_EUNSUPPORTED),          # int4 K above 16384
     (dict(wt="int4_tiled", d=4096 + 128), moe.MOE_EUNSUPPORTED),   # K not a multiple of 1024
     (dict(wt="int4_tiled", F=9216), moe.MOE_EUNSUPPORTED),         # K above 8192 (down)
     (dict(wt="int4_tiled", d=4104), moe.MOE_EINVAL),
@@ -137,15 +149,15 @@ def test_rmsnorm_validation():
 def test_read_ceiling_validation():
     # rejected before any HIP call
     with pytest.raises(moe.MoEError) as e:
-        moe.moe_read_ceiling(4096, 100, 8192)
+        moe.measure.moe_read_ceiling(4096, 100, 8192)
     assert e.value.status == moe.MOE_EINVAL
     with pytest.raises(moe.MoEError):
-        moe.moe_read_ceiling(None, 1024, 8192)
+        moe.measure.moe_read_ceiling(None, 1024, 8192)
     with pytest.raises(moe.MoEError):
-        moe.moe_read_ceiling(4096, 1024, None)
+        moe.measure.moe_read_ceiling(4096, 1024, None)
     with pytest.raises(moe.MoEError):
-        moe.moe_read_ceiling(4104, 1024, 8192)     # misaligned buffer
-    assert moe.moe_read_ceiling(None, 0, 8192) == 0
+        moe.measure.moe_read_ceiling(4104, 1024, 8192)     # misaligned buffer
+    assert moe.measure.moe_read_ceiling(None, 0, 8192) == 0
 
 
 def test_pack_int4_tiled_validation():
@@ -165,7 +177,7 @@ def test_mfma_ceiling_validation():
     for args in ((0, p, 1 << 20), ((1 << 24) + 1, p, 1 << 20), (10, None, 1 << 20), (10, p + 4, 1 << 20),
                  (10, p, 16)):
         with pytest.raises(moe.MoEError) as ei:
-            moe.moe_mfma_ceiling(*args, stream=0)
+            moe.measure.moe_mfma_ceiling(*args, stream=0)
         assert ei.value.status == moe.MOE_EINVAL, args
     with pytest.raises(moe.MoEError):
-        moe.moe_mfma_ceiling(10, p, 1 << 20, clock=p + 4, stream=0)   # misaligned clock
+        moe.measure.moe_mfma_ceiling(10, p, 1 << 20, clock=p + 4, stream=0)   # misaligned clock

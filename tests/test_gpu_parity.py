@@ -98,6 +98,27 @@ SMALL = {
         model="s_bf16_sk4", w_std=0.05),
     "f32_ragged": moe_inputs.MoEConfig(
         "f32_ragged", T=37, d=200, E=5, k=3, F=72, act="f32", wt="f32", model="s_f32"),
+    # an always-on shared expert with bf16 or fp32 weights runs as a one-expert
+    # group of all T tokens through the routed experts' kernel selection:
+    # 8 rows (GEMV), 40 rows (64-row MFMA tiles) and 520 rows (256-row MFMA
+    # tiles with a ragged third tile; routed groups of ~260 rows beside it)
+    "bf16_shared_decode": moe_inputs.MoEConfig(
+        "bf16_shared_decode", T=8, d=1024, E=8, k=2, F=1024, act="bf16", wt="bf16",
+        model="s_bf16_sh", n_shared=1, w_std=0.05),
+    "bf16_shared_mid": moe_inputs.MoEConfig(
+        "bf16_shared_mid", T=40, d=1024, E=4, k=2, F=1536, act="bf16", wt="bf16",
+        model="s_bf16_sh", n_shared=1, w_std=0.05),
+    "bf16_shared_prefill": moe_inputs.MoEConfig(
+        "bf16_shared_prefill", T=520, d=512, E=4, k=2, F=768, act="bf16", wt="bf16",
+        model="s_bf16_shp", n_shared=1, w_std=0.05),
+    "f32_shared": moe_inputs.MoEConfig(
+        "f32_shared", T=20, d=128, E=4, k=2, F=96, act="f32", wt="f32", model="s_f32_sh",
+        n_shared=1),
+    # int4 with K above 8192 on the GEMV (gate/up K = 9216, not a multiple of
+    # 1024 times at most 8); down K = 512 also on the GEMV
+    "int4_wide_gemv": moe_inputs.MoEConfig(
+        "int4_wide_gemv", T=12, d=9216, E=4, k=2, F=512, act="bf16", wt="int4",
+        model="s_int4_wg", n_shared=1, w_std=0.05),
 }
 
 
@@ -474,7 +495,7 @@ def test_read_ceiling_reads_every_word():
         h = torch.randint(-2**31, 2**31 - 1, (n_words,), generator=g, dtype=torch.int64).to(torch.int32)
         buf = h.to(DEV)
         sink = torch.zeros(1, dtype=torch.int32, device=DEV)
-        moe.moe_read_ceiling(buf, n_words * 4, sink)
+        moe.measure.moe_read_ceiling(buf, n_words * 4, sink)
         torch.cuda.synchronize()
         ref = np.bitwise_xor.reduce(h.numpy().view(np.uint32))
         assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(ref)
@@ -486,7 +507,7 @@ def test_mfma_ceiling_runs():
     the launch's."""
     sink = torch.full((4096,), float("nan"), dtype=torch.float32, device=DEV)
     clk = torch.zeros(2, dtype=torch.int64, device=DEV)
-    flops = moe.moe_mfma_ceiling(16, sink, 4096 * 4, clk)
+    flops = moe.measure.moe_mfma_ceiling(16, sink, 4096 * 4, clk)
     torch.cuda.synchronize()
     n = flops // (8 * 16 * 8 * 32768)
     s = sink[: n * 8].cpu()
