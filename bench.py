@@ -4,23 +4,31 @@
 
 A step is one pass of the whole layer (router, softmax, top-k, dispatch,
 expert SwiGLU FFN, combine) over one batch: one moe_layer_forward call through
-the C ABI.  A second timed loop of the same length calls the four steps one
-by one (route -> dispatch -> expert_ffn -> combine on one stream, the same
-kernels) with HIP events around the expert FFN.  Inputs and weights are resident in HBM before the
-timed region.  The headline is the Mixtral-8x7B-shaped decode layer (T=8); the
-prefill layer (T=4096, Zipf-loaded experts) runs on the same weights and is
-reported in the same JSON line.
+the C ABI.  The timed region is K back-to-back calls after W warm-up calls,
+bracketed by device synchronisation; a HIP event between calls gives the
+per-step median and p99.  A second loop of the same length (after its own
+warm-up) calls the four steps one by one (route -> dispatch -> expert_ffn ->
+combine, the same kernels) with HIP events around moe_expert_ffn.  Inputs and
+weights are resident in HBM before the timed region.
+
+The headline is the Mixtral-8x7B-shaped decode layer (T=8).  The same JSON
+line carries the prefill layer (T=4096, Zipf-loaded experts, same weights; at
+least 20 warm-ups and 50 steps whatever the flags), the fine-grained int4
+decode layer (T=64, E=256 + 1 shared expert, tiled int4 codes) and the 4-layer
+pre-norm stack (T=512, E=64, top-6) with its per-layer usage histogram.
 
 Roofline: the dominant step is the expert FFN (the GEMV or skinny MFMA gate/up
 and down kernels at decode, the MFMA gate/up and down kernels at prefill; the
-bench line names the kernels the group sizes select).  Its time is
-measured live with HIP events recorded on the library's stream around the
+bench line names the kernels the group sizes select).  Its time is measured
+live with HIP events recorded on the library's stream around the
 moe_expert_ffn call; its algorithmic bytes are the weight bytes of the experts
 actually hit (batch union) plus the activation traffic, its algorithmic flops
 2*3*T*k*d*F.
 
 CPU baseline: the fp64 oracle (oracle/, test infrastructure) timed on the
-host's cores on the full decode layer, repeated to ~10 s.
+host's cores: the full decode layer repeated to ~10 s, and a seeded sample of
+the prefill tokens (one token per thread per call) for ~10 s; each with a
+one-thread run, the threads that worked and the CPU model.
 """
 from __future__ import annotations
 
@@ -89,6 +97,7 @@ class Runner:
         self.stream = torch.cuda.current_stream()
 
     def step(self, ev=None):
+        """route -> dispatch -> expert_ffn -> combine, events around the FFN."""
         s = self.stream
         moe.moe_route(self.shape, self.x, self.wr, self.br, self.logits, self.idx, self.w, stream=s)
         moe.moe_dispatch(self.shape, self.idx, self.counts, self.offsets, self.perm, self.inv, stream=s)
@@ -104,7 +113,29 @@ class Runner:
         moe.moe_layer_forward(self.shape, self.x, self.wr, self.br, self.wstruct, None, self.y,
                               self.counts, self.idx, self.ws, stream=self.stream)
 
-    def timed(self, steps, warmup):
+    def time_layer(self, steps, warmup):
+        """The timed region: `steps` back-to-back moe_layer_forward calls,
+        bracketed by device synchronisation (host wall clock), with a HIP event
+        recorded on the library's stream between consecutive calls for the
+        per-step median and p99."""
+        for _ in range(warmup):
+            self.layer_call()
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            evs[i].record(self.stream)
+            self.layer_call()
+        evs[steps].record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+        return {"wall_s": wall, "ms_per_step": wall * 1e3 / steps, "median": float(np.median(per)),
+                "p99": float(np.percentile(per, 99)), "mean": float(np.mean(per))}
+
+    def time_ffn(self, steps, warmup):
+        """The same layer as four calls with HIP events around moe_expert_ffn
+        (the dominant step), after its own warm-up of the same length."""
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
@@ -115,69 +146,123 @@ class Runner:
             self.step(evs[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ffn_ms = [a.elapsed_time(b) for a, b in evs]
-        self.last_ffn_p99 = float(np.percentile(ffn_ms, 99))
-        # the single-call path, timed the same way (same kernels)
-        t1 = time.perf_counter()
-        for _ in range(steps):
-            self.layer_call()
-        torch.cuda.synchronize()
-        wall_layer = time.perf_counter() - t1
-        return wall, float(np.mean(ffn_ms)), float(np.median(ffn_ms)), wall_layer
+        ffn = [a.elapsed_time(b) for a, b in evs]
+        return {"four_call_ms_per_step": wall * 1e3 / steps, "mean": float(np.mean(ffn)),
+                "median": float(np.median(ffn)), "p99": float(np.percentile(ffn, 99))}
 
     def ffn_algorithmic(self):
-        """Bytes and flops of one moe_expert_ffn call (batch union of weights)."""
-        cfg = self.cfg
+        """Experts hit, bytes and flops of one moe_expert_ffn call."""
         c = self.counts.cpu().numpy()
         U = int((c > 0).sum())
-        tk = cfg.T * cfg.k
-        if cfg.wt == "int4":
-            mat = cfg.F * cfg.d // 2 + cfg.F * (cfg.d // 128) * 2
-        else:
-            mat = cfg.F * cfg.d * (4 if cfg.wt == "f32" else 2)
-        ab = 4 if cfg.act == "f32" else 2
-        w_bytes = (U + cfg.n_shared) * 3 * mat
-        act_bytes = (tk * cfg.d * ab              # gathered x rows
-                     + 2 * tk * cfg.F * ab         # h written then read
-                     + tk * cfg.d * 4)             # y_perm written
-        if cfg.n_shared:
-            act_bytes += cfg.T * cfg.d * ab + 2 * cfg.T * cfg.F * ab + cfg.T * cfg.d * 4
-        flops = 2 * 3 * (tk + cfg.n_shared * cfg.T) * cfg.d * cfg.F
-        return U, w_bytes + act_bytes, flops
+        return (U,) + ffn_work(self.cfg, U)
 
 
-def cpu_baseline(cfg, runner, Wd, target_s=10.0):
-    """The oracle timed on the host's cores on the full layer (all T tokens);
-    Wd: the device weights in the row-major layout the oracle reads."""
-    import oracle
-    oracle.build(force=False)
-
-    def st(t):
-        if t is None:
-            return None
-        t = t.detach().cpu().contiguous()
-        if t.dtype in (torch.bfloat16, torch.float16):
-            return t.view(torch.int16).numpy().view(np.uint16)
-        return t.numpy()
-
-    W = {n: st(Wd[n]) for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")}
-    S = None
+def ffn_work(cfg, U):
+    """Algorithmic bytes and flops of one expert-FFN step with U experts hit:
+    each hit expert's three matrices read once (batch union, plus the shared
+    expert's), gathered x rows read, h written and read back, y_perm written."""
+    tk = cfg.T * cfg.k
+    if cfg.wt == "int4":
+        mat = cfg.F * cfg.d // 2 + cfg.F * (cfg.d // 128) * 2
+    else:
+        mat = cfg.F * cfg.d * (4 if cfg.wt == "f32" else 2)
+    ab = 4 if cfg.act == "f32" else 2
+    w_bytes = (U + cfg.n_shared) * 3 * mat
+    act_bytes = (tk * cfg.d * ab              # gathered x rows
+                 + 2 * tk * cfg.F * ab         # h written then read
+                 + tk * cfg.d * 4)             # y_perm written
     if cfg.n_shared:
-        S = {"w_gate": st(Wd["sh_gate"]), "w_up": st(Wd["sh_up"]),
-             "w_down": st(Wd["sh_down"]), "s_gate": st(Wd["sh_s_gate"]),
-             "s_up": st(Wd["sh_s_up"]), "s_down": st(Wd["sh_s_down"])}
-    x, wr, br = st(runner.x), st(runner.wr), st(runner.br)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.layer_forward(x, cfg.act, cfg.wt, cfg.k, wr, br, W, S)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or reps >= 50:
-            break
-    return {"value": reps * cfg.T / el, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{cfg.name}: full layer, all {cfg.T} tokens, fp64, repeated {reps}x "
-                      f"({el:.1f} s)"}
+        act_bytes += cfg.T * cfg.d * ab + 2 * cfg.T * cfg.F * ab + cfg.T * cfg.d * 4
+    flops = 2 * 3 * (tk + cfg.n_shared * cfg.T) * cfg.d * cfg.F
+    return w_bytes + act_bytes, flops
+
+
+def _np_store(t):
+    if t is None:
+        return None
+    t = t.detach().cpu().contiguous()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class OracleTimer:
+    """The fp64 oracle (oracle/, test infrastructure) timed on the host's cores.
+    It parallelises over the tokens of a call (one token per thread), so a
+    call over n tokens keeps at most n threads busy: `cores` states the
+    threads that actually worked."""
+
+    def __init__(self, cfg, runner, Wd):
+        import oracle
+        oracle.build(force=False)
+        self.oracle = oracle
+        self.cfg = cfg
+        self.threads = oracle.num_threads()
+        self.W = {n: _np_store(Wd[n]) for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")}
+        self.S = None
+        if cfg.n_shared:
+            self.S = {"w_gate": _np_store(Wd["sh_gate"]), "w_up": _np_store(Wd["sh_up"]),
+                      "w_down": _np_store(Wd["sh_down"]), "s_gate": _np_store(Wd["sh_s_gate"]),
+                      "s_up": _np_store(Wd["sh_s_up"]), "s_down": _np_store(Wd["sh_s_down"])}
+        self.set_tokens(cfg, runner)
+
+    def set_tokens(self, cfg, runner):
+        """Another workload on the same weights (the prefill batch)."""
+        self.cfg = cfg
+        self.x, self.wr, self.br = _np_store(runner.x), _np_store(runner.wr), _np_store(runner.br)
+
+    def rate(self, order, chunk, target_s, threads, max_calls=50):
+        """Tokens/s of oracle layer_forward calls over consecutive chunks of
+        `order` (wrapping around) until target_s has elapsed."""
+        cfg = self.cfg
+        self.oracle.set_num_threads(threads)
+        done, calls, i, t0 = 0, 0, 0, time.perf_counter()
+        while True:
+            sel = np.array([order[(i + j) % len(order)] for j in range(chunk)], np.int32)
+            i += chunk
+            self.oracle.layer_forward(self.x, cfg.act, cfg.wt, cfg.k, self.wr, self.br, self.W, self.S,
+                                      sel=sel)
+            done += chunk
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= target_s or calls >= max_calls:
+                break
+        self.oracle.set_num_threads(self.threads)
+        return done / el, done, calls, el
+
+    def baseline(self, target_s=10.0, sample=False, single_thread_tokens=2):
+        """All T tokens per call (sample=False), or a fixed seeded random order
+        of the tokens in calls of one token per thread (sample=True), repeated
+        until target_s; plus a one-thread run on a few tokens."""
+        cfg = self.cfg
+        if not sample:
+            busy = min(self.threads, cfg.T)
+            value, done, calls, el = self.rate(list(range(cfg.T)), cfg.T, target_s, busy)
+            desc = (f"{cfg.name}: the full layer on all {cfg.T} tokens per call, fp64, {calls} calls "
+                    f"({el:.1f} s)")
+        else:
+            busy = self.threads
+            order = np.random.default_rng(0).permutation(cfg.T).tolist()
+            value, done, calls, el = self.rate(order, busy, target_s, busy)
+            desc = (f"{cfg.name}: {done} of its {cfg.T} tokens (a fixed seeded random order, {busy} per "
+                    f"call), the whole layer per token (router, top-{cfg.k}, SwiGLU experts, weighted "
+                    f"sum), fp64 ({el:.1f} s)")
+        v1, d1, _, e1 = self.rate(list(range(cfg.T)), single_thread_tokens, 0.0, 1, max_calls=1)
+        return {"value": round(value, 3), "unit": "tokens/s", "cores": busy, "kind": "oracle",
+                "sample": desc, "threads_available": self.threads, "cpu_model": cpu_model(),
+                "single_thread_value": round(v1, 3),
+                "single_thread_sample": f"{d1} tokens on one thread ({e1:.1f} s)"}
 
 
 # kernel sources of each workload's expert-FFN step: the committed counter
@@ -218,11 +303,11 @@ def read_ceiling_gbs(nbytes=4 << 30, reps=5):
     buf = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
     sink = torch.zeros(1, dtype=torch.int32, device=DEV)
     for _ in range(2):
-        moe.moe_read_ceiling(buf, nbytes, sink)
+        moe.measure.moe_read_ceiling(buf, nbytes, sink)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(reps):
-        moe.moe_read_ceiling(buf, nbytes, sink)
+        moe.measure.moe_read_ceiling(buf, nbytes, sink)
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / reps
@@ -238,11 +323,11 @@ def mfma_ceiling(iters=40000, reps=3):
     sink = torch.empty(n_sink, dtype=torch.float32, device=DEV)
     clk = torch.zeros(2, dtype=torch.int64, device=DEV)
     for _ in range(2):
-        moe.moe_mfma_ceiling(iters, sink, n_sink * 4)
+        moe.measure.moe_mfma_ceiling(iters, sink, n_sink * 4)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(reps):
-        flops = moe.moe_mfma_ceiling(iters, sink, n_sink * 4, clk)
+        flops = moe.measure.moe_mfma_ceiling(iters, sink, n_sink * 4, clk)
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / reps
@@ -286,6 +371,129 @@ def roofline_obj(bound, achieved, peak, unit, traffic=None):
             "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
+def workload_leg(run, steps, warmup, tau, ceilings, traffic_key=None, layer_first=True):
+    """Time one workload: the layer loop (the timed region) and the four-call
+    loop that times the expert-FFN step, each after its own warm-up; the
+    roofline object of that step (MFMA-bound when the groups are prefill
+    sized, else HBM-bound)."""
+    lay = run.time_layer(steps, warmup)
+    ffn = run.time_ffn(steps, warmup)
+    cfg = run.cfg
+    U, nbytes, flops = run.ffn_algorithmic()
+    common = dict(launch_ms=round(ffn["mean"], 5), launch_ms_median=round(ffn["median"], 5),
+                  launch_ms_p99=round(ffn["p99"], 5),
+                  ffn_within_layer=bool(ffn["median"] <= lay["median"]))
+    if cfg.T * cfg.k / max(U, 1) > 64:      # prefill-sized groups: MFMA-bound
+        tf = flops / (ffn["mean"] * 1e-3) / 1e12
+        mceil, mclk = ceilings("mfma")
+        roof = dict(roofline_obj("mfma", tf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
+                    kernel=f"expert FFN step ({ffn_paths(cfg, run.counts.cpu().tolist(), tau)})",
+                    flops_per_launch=flops, **common,
+                    measured_mfma_ceiling=round(mceil, 1), mfma_ceiling_clock_ghz=round(mclk, 3),
+                    frac_of_measured_ceiling=round(tf / mceil, 4))
+    else:
+        gbs = nbytes / (ffn["mean"] * 1e-3) / 1e9
+        ceil = ceilings("hbm")
+        roof = dict(roofline_obj("hbm", gbs, HBM_PEAK_GBS, "GB/s",
+                                 measured_traffic(traffic_key) if traffic_key else None),
+                    kernel=f"expert FFN step ({ffn_paths(cfg, run.counts.cpu().tolist(), tau)}; "
+                           f"weights {run.wt})",
+                    bytes_per_launch=nbytes, **common,
+                    measured_read_ceiling=round(ceil, 1),
+                    frac_of_measured_ceiling=round(gbs / ceil, 4))
+    if not common["ffn_within_layer"]:
+        log(f"warning: {cfg.name}: expert-FFN step median {ffn['median']:.4f} ms exceeds the layer's "
+            f"{lay['median']:.4f} ms")
+    return {"layer": lay, "ffn": ffn, "U": U, "roofline": roof}
+
+
+def leg_summary(cfg, leg, steps, warmup):
+    lay = leg["layer"]
+    return {"workload": cfg.name, "T": cfg.T, "value": round(cfg.T / (lay["ms_per_step"] * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_step": round(lay["ms_per_step"], 5),
+            "ms_per_step_median": round(lay["median"], 5), "ms_per_step_p99": round(lay["p99"], 5),
+            "steps": steps, "warmup": warmup, "active_experts": leg["U"],
+            "roofline": leg["roofline"],
+            "four_call_ms_per_step": round(leg["ffn"]["four_call_ms_per_step"], 5)}
+
+
+class Ceilings:
+    """Measured ceilings, taken once per process on first use."""
+
+    def __init__(self):
+        self.v = {}
+
+    def __call__(self, kind):
+        if kind not in self.v:
+            self.v[kind] = read_ceiling_gbs() if kind == "hbm" else mfma_ceiling()
+        return self.v[kind]
+
+
+def stack_leg(steps, warmup):
+    """The 4-layer pre-norm stack (T=512, d=2048, E=64, top-6, F=1408, bf16):
+    per layer h_{l+1} = h_l + MoE_l(rmsnorm(h_l)), as moe_rmsnorm then
+    moe_layer_forward with the residual.  Times the whole stack (a step is the
+    4 layers) with a HIP event between layers, and returns the per-layer usage
+    histogram (layer, expert, count) of the last step."""
+    cfg = moe_inputs.CONFIGS["stack4"]
+    log("generating the 4-layer stack on the GPU")
+    inp = moe_inputs.generate(cfg, seed=0, device=DEV)
+    layers = []
+    for l in range(cfg.layers):
+        L = inp["layers"][l]
+        W = {n: (None if L.get(n) is None else L[n].to(DEV)) for n in ("w_gate", "w_up", "w_down")}
+        layers.append(moe.layer.MoELayer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.act, cfg.wt, W,
+                                         L["w_router"].to(DEV), None))
+    gammas = [g.to(DEV) for g in inp["gamma"]]
+    hs = [inp["x"].to(DEV)] + [torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=DEV)
+                               for _ in range(cfg.layers)]
+    nrm = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=DEV)
+    st = torch.cuda.current_stream()
+    nshape = moe.make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, cfg.act, cfg.wt)
+
+    def one(evs=None):
+        for l, lay in enumerate(layers):
+            if evs is not None:
+                evs[l].record(st)
+            moe.moe_rmsnorm(nshape, hs[l], gammas[l], inp["eps"], nrm, stream=st)
+            lay.forward(nrm, residual=hs[l], out=hs[l + 1], stream=st)
+        if evs is not None:
+            evs[cfg.layers].record(st)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(cfg.layers + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_layer = np.array([[e[l].elapsed_time(e[l + 1]) for l in range(cfg.layers)] for e in ev])
+    stack = per_layer.sum(axis=1)
+    counts = [lay.counts.cpu().tolist() for lay in layers]
+    lines = [(l, e, c) for l, cs in enumerate(counts) for e, c in enumerate(cs) if c > 0]
+    for l, e, c in lines:
+        log(f"usage {l} {e} {c}")
+    med = np.median(per_layer, axis=0)
+    layer_objs = []
+    for l in range(cfg.layers):
+        U = sum(1 for c in counts[l] if c > 0)
+        nbytes, _ = ffn_work(cfg, U)
+        gbs = nbytes / (med[l] * 1e-3) / 1e9
+        layer_objs.append({"layer": l, "ms_median": round(float(med[l]), 5),
+                           "ms_p99": round(float(np.percentile(per_layer[:, l], 99)), 5),
+                           "tokens_per_s": round(cfg.T / (med[l] * 1e-3), 1), "active_experts": U,
+                           "expert_ffn_bytes": nbytes, "GBps_over_layer": round(gbs, 1),
+                           "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4)})
+    ms = wall * 1e3 / steps
+    return {"workload": "stack4", "T": cfg.T, "layers": cfg.layers,
+            "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s through the 4-layer stack",
+            "ms_per_step": round(ms, 5), "ms_per_step_median": round(float(np.median(stack)), 5),
+            "ms_per_step_p99": round(float(np.percentile(stack, 99)), 5), "steps": steps, "warmup": warmup,
+            "per_layer": layer_objs, "usage_histogram": counts, "usage_lines": len(lines)}
+
+
 def extras():
     """Decode-side sweeps printed as JSON lines (not the bench line): the GEMV /
     MFMA crossover that sets tau (one expert holding c rows, Mixtral weights,
@@ -303,23 +511,26 @@ def extras():
             if tau == 1 and c < 2:
                 continue
             run = Runner(cfg, x, wr, bias, W, tau=tau)
-            _, ffn_mean, ffn_med, _ = run.timed(20, 5)
+            ffn = run.time_ffn(20, 5)
             assert int(run.counts[0]) == c
-            print(json.dumps({"sweep": "tau", "rows": c, "path": path, "ffn_ms": round(ffn_mean, 4),
-                              "ffn_ms_median": round(ffn_med, 4),
-                              "weight_GBps": round(wbytes / (ffn_mean * 1e-3) / 1e9, 1)}), flush=True)
+            print(json.dumps({"sweep": "tau", "rows": c, "path": path, "ffn_ms": round(ffn["mean"], 4),
+                              "ffn_ms_median": round(ffn["median"], 4),
+                              "weight_GBps": round(wbytes / (ffn["mean"] * 1e-3) / 1e9, 1)}), flush=True)
             del run
     for T in (8, 16, 32, 64):
         cfg = dcfg.replace(name=f"mixtral_decode_t{T}", T=T)
         x = moe_inputs.activations(cfg, 0).to(DEV)
         run = Runner(cfg, x, wr, None, W)
-        wall, ffn_mean, _, _ = run.timed(20, 5)
+        lay = run.time_layer(20, 5)
+        ffn = run.time_ffn(20, 5)
         U, nbytes, _ = run.ffn_algorithmic()
         print(json.dumps({"sweep": "decode_T", "T": T, "active_experts": U,
-                          "ms_per_step": round(wall * 1e3 / 20, 4), "tokens_per_s": round(T * 20 / wall, 1),
-                          "ffn_ms": round(ffn_mean, 4),
-                          "ffn_GBps": round(nbytes / (ffn_mean * 1e-3) / 1e9, 1),
-                          "frac_of_8TBps": round(nbytes / (ffn_mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+                          "ms_per_step": round(lay["ms_per_step"], 4),
+                          "tokens_per_s": round(T / (lay["ms_per_step"] * 1e-3), 1),
+                          "ffn_ms": round(ffn["mean"], 4),
+                          "ffn_GBps": round(nbytes / (ffn["mean"] * 1e-3) / 1e9, 1),
+                          "frac_of_8TBps": round(nbytes / (ffn["mean"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}),
+              flush=True)
         del run
 
 
@@ -327,11 +538,13 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral_decode",
                     choices=["mixtral_decode", "mixtral_prefill", "fine_int4_decode",
-                             "stack4_layer0"])
-    ap.add_argument("--no-prefill", action="store_true")
+                             "stack4_layer0", "stack4"])
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the int4 decode and 4-layer stack legs of the default run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tau", type=int, default=0)
     ap.add_argument("--tokens", type=int, default=0,
@@ -347,9 +560,9 @@ def main():
                     help="print the decode sweeps (tau crossover, decode batch sizes) instead of the bench line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer is built for a single MI355X; see the sharding notes in DESIGN.md)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the layer is built "
+              "and measured on a single MI355X (expert-parallel sharding over several GPUs is designed "
+              "but not built)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -365,11 +578,18 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    ceilings = Ceilings()
+    steps, warmup = args.steps, args.warmup
+
+    if args.workload == "stack4":
+        out = stack_leg(steps, warmup)
+        print(json.dumps(out), flush=True)
+        return
 
     name = "stack4" if args.workload == "stack4_layer0" else args.workload
     cfg = moe_inputs.CONFIGS[name]
     if cfg.layers > 1:
-        cfg = cfg.replace(layers=1)
+        cfg = cfg.replace(layers=1, name="stack4_layer0")
     if args.tokens > 0:
         cfg = cfg.replace(name=f"{cfg.name}_t{args.tokens}", T=args.tokens)
     log(f"generating {cfg.name} inputs on the GPU")
@@ -384,78 +604,64 @@ def main():
         torch.cuda.synchronize()
         wt = "int4_tiled"
     run = Runner(cfg, x, wr, br, Wrun, tau=args.tau, wt=wt)
-    log(f"timing {cfg.name}: warmup {args.warmup}, steps {args.steps}")
-    wall, ffn_mean, ffn_med, wall_layer = run.timed(args.steps, args.warmup)
-    U, ffn_bytes, ffn_flops = run.ffn_algorithmic()
-    ms = wall_layer * 1e3 / args.steps
-    value = cfg.T * args.steps / wall_layer
-    achieved = ffn_bytes / (ffn_mean * 1e-3) / 1e9
-    if cfg.T * cfg.k / max(U, 1) > 64:      # prefill-sized groups: MFMA-bound
-        tf = ffn_flops / (ffn_mean * 1e-3) / 1e12
-        mceil, mclk = mfma_ceiling()
-        roof = dict(roofline_obj("mfma", tf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
-                    kernel="expert FFN step (MFMA gate/up + down)", flops_per_launch=ffn_flops,
-                    launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5),
-                    launch_ms_p99=round(run.last_ffn_p99, 5),
-                    measured_mfma_ceiling=round(mceil, 1), mfma_ceiling_clock_ghz=round(mclk, 3),
-                    frac_of_measured_ceiling=round(tf / mceil, 4))
-    else:
-        ceil = read_ceiling_gbs()
-        roof = dict(roofline_obj("hbm", achieved, HBM_PEAK_GBS, "GB/s",
-                                 # counters were taken on the default run (tiled int4 codes)
-                                 measured_traffic(cfg.name)
-                                 if args.tau == 0 and (cfg.wt != "int4" or wt == "int4_tiled") else None),
-                    kernel=f"expert FFN step ({ffn_paths(cfg, run.counts.cpu().tolist(), args.tau)}; weights {wt})",
-                    bytes_per_launch=ffn_bytes,
-                    launch_ms=round(ffn_mean, 5), launch_ms_median=round(ffn_med, 5),
-                    launch_ms_p99=round(run.last_ffn_p99, 5),
-                    measured_read_ceiling=round(ceil, 1),
-                    frac_of_measured_ceiling=round(achieved / ceil, 4))
+    if cfg.name == "mixtral_prefill":   # the prefill protocol, whatever the flags
+        steps, warmup = max(steps, 50), max(warmup, 20)
+    log(f"timing {cfg.name}: warmup {warmup}, steps {steps}")
+    key = cfg.name if args.tau == 0 and (cfg.wt != "int4" or wt == "int4_tiled") else None
+    leg = workload_leg(run, steps, warmup, args.tau, ceilings, key)
+    lay = leg["layer"]
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "metric": METRIC, "value": round(cfg.T / (lay["ms_per_step"] * 1e-3), 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(lay["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.act == "bf16" and cfg.wt == "bf16" else
                  ("bf16/int4" if cfg.wt == "int4" else "f32"),
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "F": cfg.F, "weights": wt, "shared_experts": cfg.n_shared,
-                   "active_experts": U, "tau": args.tau, "seed": 0},
-        "roofline": roof,
-        "four_call_ms_per_step": round(wall * 1e3 / args.steps, 4),
+                   "active_experts": leg["U"], "tau": args.tau, "seed": 0},
+        "ms_per_step_median": round(lay["median"], 5), "ms_per_step_p99": round(lay["p99"], 5),
+        "roofline": leg["roofline"],
+        "four_call_ms_per_step": round(leg["ffn"]["four_call_ms_per_step"], 5),
     }
     log(json.dumps(out))
+    orc = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on the host")
+        orc = OracleTimer(cfg, run, W)
+        out["cpu_baseline"] = orc.baseline(sample=cfg.T > 64)
 
     if not args.no_prefill and cfg.name == "mixtral_decode":
         pcfg = moe_inputs.CONFIGS["mixtral_prefill"]
         log("prefill T=4096 on the same weights")
         px, pwr, pbr, _ = device_layer(pcfg, shared_weights=W)
         prun = Runner(pcfg, px, pwr, pbr, W, tau=args.tau)
-        psteps = max(5, args.steps // 5)
-        pwall, pffn_mean, pffn_med, pwall_layer = prun.timed(psteps, max(2, args.warmup // 2))
-        _, pbytes, pflops = prun.ffn_algorithmic()
-        ptf = pflops / (pffn_mean * 1e-3) / 1e12
-        mceil, mclk = mfma_ceiling()
-        out["prefill"] = {
-            "workload": pcfg.name, "T": pcfg.T, "value": round(pcfg.T * psteps / pwall_layer, 1),
-            "unit": "tokens/s", "ms_per_step": round(pwall_layer * 1e3 / psteps, 4), "steps": psteps,
-            "counts": prun.counts.cpu().tolist(),
-            "roofline": dict(roofline_obj("mfma", ptf, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
-                             kernel="expert FFN step (MFMA gate/up + down)",
-                             flops_per_launch=pflops, launch_ms=round(pffn_mean, 4),
-                             launch_ms_median=round(pffn_med, 4),
-                             launch_ms_p99=round(prun.last_ffn_p99, 4),
-                             measured_mfma_ceiling=round(mceil, 1),
-                             mfma_ceiling_clock_ghz=round(mclk, 3),
-                             frac_of_measured_ceiling=round(ptf / mceil, 4)),
-            "four_call_ms_per_step": round(pwall * 1e3 / psteps, 4),
-        }
+        psteps, pwarm = max(50, steps), max(20, warmup)
+        pleg = workload_leg(prun, psteps, pwarm, args.tau, ceilings)
+        out["prefill"] = dict(leg_summary(pcfg, pleg, psteps, pwarm), counts=prun.counts.cpu().tolist())
         log(json.dumps(out["prefill"]))
+        if orc is not None:
+            log("cpu baseline: oracle on a sample of the prefill tokens")
+            orc.set_tokens(pcfg, prun)
+            out["prefill"]["cpu_baseline"] = orc.baseline(sample=True)
         del prun, px
+    del orc
 
-    if not args.no_cpu_baseline:
-        log("cpu baseline: oracle on the host")
-        out["cpu_baseline"] = cpu_baseline(cfg, run, W)
+    if not args.no_legs and cfg.name == "mixtral_decode":
+        icfg = moe_inputs.CONFIGS["fine_int4_decode"]
+        log("int4 decode leg (tiled codes)")
+        ix, iwr, ibr, iW = device_layer(icfg)
+        iWt = moe.layer.pack_int4_tiled(iW)
+        del iW
+        torch.cuda.synchronize()
+        irun = Runner(icfg, ix, iwr, ibr, iWt, tau=args.tau, wt="int4_tiled")
+        ileg = workload_leg(irun, steps, warmup, args.tau, ceilings, icfg.name if args.tau == 0 else None)
+        out["int4_decode"] = leg_summary(icfg, ileg, steps, warmup)
+        log(json.dumps(out["int4_decode"]))
+        del irun, iWt
+        torch.cuda.empty_cache()
+        out["stack4"] = stack_leg(steps, warmup)
+        log(json.dumps(out["stack4"]))
     print(json.dumps(out), flush=True)
 
 

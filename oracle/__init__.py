@@ -69,6 +69,11 @@ def num_threads() -> int:
     return int(lib().orc_num_threads())
 
 
+def set_num_threads(n: int) -> None:
+    """Thread count of later oracle calls (timing only; results do not depend on it)."""
+    lib().orc_set_num_threads(ctypes.c_int(int(n)))
+
+
 def dec_bf16(h: int) -> float:
     return lib().orc_dec_bf16(h)
 

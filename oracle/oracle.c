@@ -46,6 +46,14 @@
 /* Threads the OpenMP loops below will use (reported beside CPU timings). */
 int orc_num_threads(void) { return omp_get_max_threads(); }
 
+/* Thread count for later calls (n >= 1), for timing runs at a stated count.
+ * Touches no arithmetic: every loop computes the same values at any count. */
+void orc_set_num_threads(int n)
+{
+    if (n >= 1)
+        omp_set_num_threads(n);
+}
+
 /* ---------------------------------------------------------------- decoders */
 
 /* bf16 is the upper half of an IEEE binary32 word. */
