@@ -174,6 +174,24 @@ int moe_layer_forward(const moe_shape *shape, const void *x, const float *w_rout
                       void *y, int32_t *counts_out, int32_t *topk_idx_out,
                       void *ws, size_t ws_bytes, void *stream, char *err, size_t err_len);
 
+/* moe_layer_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * moe_layer_forward minus ws / ws_bytes: the workspace is a fixed device
+ * array of the library, 128 MiB on each GPU the library runs on (held until
+ * the process ends; its address is looked up once per device on the first
+ * call there, with that device current).  The call allocates nothing.
+ *   MOE_ENOMEM when moe_workspace_bytes(shape) exceeds 128 MiB (decode and
+ *   stack-layer shapes fit; a Mixtral-sized prefill batch does not: use
+ *   moe_layer_forward with a caller workspace).
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on one
+ * GPU (different streams or host threads without ordering) race. */
+int moe_layer_forward_noalloc(const moe_shape *shape, const void *x, const float *w_router,
+                              const float *b_router, const moe_weights *w, const void *residual,
+                              void *y, int32_t *counts_out, int32_t *topk_idx_out,
+                              void *stream, char *err, size_t err_len);
+
 /* Bytes of device workspace needed by moe_layer_forward (and sufficient for
  * moe_expert_ffn) for this shape; 0 when the shape is invalid.  The fixed
  * scratch budget computed up front follows [P3] §2.3.  Host-only. */

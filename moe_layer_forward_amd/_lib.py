@@ -19,7 +19,7 @@ MOE_F32, MOE_BF16, MOE_INT4_G128, MOE_INT4_G128_TILED = 0, 1, 2, 3
 DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128, "int4_tiled": MOE_INT4_G128_TILED}
 
 EXPORTS = ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_workspace_bytes", "moe_rmsnorm", "moe_pack_int4_tiled", "moe_strerror")
+           "moe_layer_forward_noalloc", "moe_workspace_bytes", "moe_rmsnorm", "moe_pack_int4_tiled", "moe_strerror")
 
 
 class MoEError(RuntimeError):
@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn.argtypes = [sp, vp, wp, i32p, i32p, i32p, vp, vp, vp, sz, vp, cp, sz]
         L.moe_combine.argtypes = [sp, vp, i32p, vp, vp, vp, vp, vp, cp, sz]
         L.moe_layer_forward.argtypes = [sp, vp, vp, vp, wp, vp, vp, i32p, i32p, vp, sz, vp, cp, sz]
+        L.moe_layer_forward_noalloc.argtypes = [sp, vp, vp, vp, wp, vp, vp, i32p, i32p, vp, cp, sz]
         L.moe_workspace_bytes.argtypes = [sp]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_rmsnorm.argtypes = [sp, vp, vp, ctypes.c_float, vp, vp, cp, sz]
@@ -64,7 +65,7 @@ def lib() -> ctypes.CDLL:
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-                  "moe_layer_forward", "moe_rmsnorm", "moe_pack_int4_tiled"):
+                  "moe_layer_forward", "moe_layer_forward_noalloc", "moe_rmsnorm", "moe_pack_int4_tiled"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -143,6 +144,14 @@ def moe_layer_forward(shape, x, w_router, b_router, weights, residual, y, counts
     return _call("moe_layer_forward", ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(b_router),
                  ctypes.byref(weights), _ptr(residual), _ptr(y), _ptr(counts_out),
                  _ptr(topk_idx_out), _ptr(ws), nbytes, _stream(stream))
+
+
+def moe_layer_forward_noalloc(shape, x, w_router, b_router, weights, residual, y, counts_out,
+                              topk_idx_out, stream=None):
+    """moe_layer_forward on the library's fixed device workspace (no allocation)."""
+    return _call("moe_layer_forward_noalloc", ctypes.byref(shape), _ptr(x), _ptr(w_router), _ptr(b_router),
+                 ctypes.byref(weights), _ptr(residual), _ptr(y), _ptr(counts_out), _ptr(topk_idx_out),
+                 _stream(stream))
 
 
 def moe_pack_int4_tiled(src, dst, n_mats, N, K, stream=None):

@@ -181,3 +181,19 @@ def test_mfma_ceiling_validation():
         assert ei.value.status == moe.MOE_EINVAL, args
     with pytest.raises(moe.MoEError):
         moe.measure.moe_mfma_ceiling(10, p, 1 << 20, clock=p + 4, stream=0)   # misaligned clock
+
+
+def test_noalloc_rejects_shapes_beyond_its_array():
+    """The allocation-free entry point refuses a workspace above its fixed
+    128 MiB device array before any HIP call, with a clear message."""
+    s = moe.make_shape(4096, 4096, 8, 2, 14336)
+    assert moe.moe_workspace_bytes(s) > 128 << 20
+    p = 1 << 20
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_layer_forward_noalloc(s, p, p, None, moe.make_weights(p, p, p), None, p, None, None, stream=0)
+    assert ei.value.status == moe.MOE_ENOMEM and "fixed device array" in str(ei.value)
+    # an invalid shape reports the shape error, not the size
+    bad = moe.make_shape(8, 4096, 8, 9, 14336)
+    with pytest.raises(moe.MoEError) as ei:
+        moe.moe_layer_forward_noalloc(bad, p, p, None, moe.make_weights(p, p, p), None, p, None, None, stream=0)
+    assert ei.value.status == moe.MOE_EINVAL
