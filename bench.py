@@ -494,6 +494,59 @@ def stack_leg(steps, warmup):
             "per_layer": layer_objs, "usage_histogram": counts, "usage_lines": len(lines)}
 
 
+def low_latency_leg(dcfg, wr, W, orc=None, steps=200, warmup=20):
+    """Small decode batches of the Mixtral-shaped layer (T = 1, 2, 4, 8): the
+    layer as eager moe_layer_forward calls and as one HIP graph replayed
+    (captured once, so a step pays no per-kernel launch from the host);
+    microseconds per layer, median and p99 over `steps` events; next to it the
+    oracle's time for the same call on the host."""
+    out = []
+    for T in (1, 2, 4, 8):
+        cfg = dcfg.replace(name=f"mixtral_decode_t{T}", T=T)
+        x = moe_inputs.activations(cfg, 0).to(DEV)
+        run = Runner(cfg, x, wr, None, W)
+        eager = run.time_layer(steps, warmup)
+        # capture one layer call on a side stream, then replay it
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                moe.moe_layer_forward(run.shape, run.x, run.wr, run.br, run.wstruct, None, run.y, run.counts,
+                                      run.idx, run.ws, stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            moe.moe_layer_forward(run.shape, run.x, run.wr, run.br, run.wstruct, None, run.y, run.counts,
+                                  run.idx, run.ws, stream=torch.cuda.current_stream())
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        cur = torch.cuda.current_stream()
+        for i in range(steps):
+            ev[i].record(cur)
+            g.replay()
+        ev[steps].record(cur)
+        torch.cuda.synchronize()
+        per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]) * 1e3
+        row = {"T": T, "active_experts": int((run.counts > 0).sum()),
+               "graph_us_median": round(float(np.median(per)), 2),
+               "graph_us_p99": round(float(np.percentile(per, 99)), 2),
+               "eager_us_median": round(eager["median"] * 1e3, 2),
+               "eager_us_p99": round(eager["p99"] * 1e3, 2),
+               "graph_tokens_per_s": round(T / (np.median(per) * 1e-6), 1)}
+        if orc is not None:
+            orc.set_tokens(cfg, run)
+            v, done, calls, el = orc.rate(list(range(T)), T, 0.0, min(orc.threads, T), max_calls=1)
+            row["oracle_ms_per_call"] = round(el * 1e3, 1)
+            row["oracle_threads"] = min(orc.threads, T)
+        out.append(row)
+        log(json.dumps(row))
+        del g, run
+    return out
+
+
 def extras():
     """Decode-side sweeps printed as JSON lines (not the bench line): the GEMV /
     MFMA crossover that sets tau (one expert holding c rows, Mixtral weights,
@@ -645,6 +698,10 @@ def main():
             orc.set_tokens(pcfg, prun)
             out["prefill"]["cpu_baseline"] = orc.baseline(sample=True)
         del prun, px
+
+    if not args.no_legs and cfg.name == "mixtral_decode":
+        log("low-latency decode: T = 1, 2, 4, 8, eager and graph-replayed")
+        out["low_latency_decode"] = low_latency_leg(cfg, wr, W, orc)
     del orc
 
     if not args.no_legs and cfg.name == "mixtral_decode":

@@ -491,13 +491,21 @@ int moe_layer_forward(const moe_shape* shape, const void* x, const float* w_rout
         return hip_check(launch_dispatch(idx, counts, offsets, perm, inv, 0, shape->k, shape->E, st), st,
                          "dispatch", err, err_len);
     }
-    rc = hip_check(launch_route(shape->act, x, w_router, b_router, logits, idx, gw, shape->T, shape->d, shape->E,
-                                shape->k, st),
-                   st, "route", err, err_len);
-    if (rc) return rc;
-    rc = hip_check(launch_dispatch(idx, counts, offsets, perm, inv, shape->T, shape->k, shape->E, st), st,
-                   "dispatch", err, err_len);
-    if (rc) return rc;
+    if (route_dispatch_small_supported(shape->T, shape->E, shape->k)) {
+        // a decode batch: router, top-k and dispatch in one launch
+        rc = hip_check(launch_route_dispatch_small(shape->act, x, w_router, b_router, logits, idx, gw, counts,
+                                                   offsets, perm, inv, shape->T, shape->d, shape->E, shape->k, st),
+                       st, "route+dispatch", err, err_len);
+        if (rc) return rc;
+    } else {
+        rc = hip_check(launch_route(shape->act, x, w_router, b_router, logits, idx, gw, shape->T, shape->d,
+                                    shape->E, shape->k, st),
+                       st, "route", err, err_len);
+        if (rc) return rc;
+        rc = hip_check(launch_dispatch(idx, counts, offsets, perm, inv, shape->T, shape->k, shape->E, st), st,
+                       "dispatch", err, err_len);
+        if (rc) return rc;
+    }
     rc = run_ffn(shape, x, w, counts, offsets, perm, yp, ys, W, st, err, err_len);
     if (rc) return rc;
     return hip_check(launch_combine(shape->act, yp, inv, gw, ys, residual, y, shape->T, shape->d, shape->k, st),

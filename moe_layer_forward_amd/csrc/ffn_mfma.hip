@@ -385,14 +385,19 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
         const int32x4_t RB = make_desc(wsrc + (size_t)c_e * N * K, wmat);
         const int P = (ke - kb + 1) / 2;         // pairs of the task (an odd last step runs on zeros)
         const bool has_next = task + nblk < ntasks;
+        // FAST: the tile's rows fill nf 32-row token fragments; group 0 takes
+        // the first ceil(nf/2) of them, group 1 the rest (a full tile: 4 and
+        // 4).  A group reads and multiplies only its own fragments, so the
+        // padding of a ragged last tile costs at most one fragment instead of
+        // up to 255 rows; the copies (and the barriers) stay the same for every
+        // tile.  Other K keep four fragments per group (their variant would
+        // not fit the register file with the smaller ones beside it).
+        const int nf = (rows + 31) >> 5;
+        const int mi0 = FAST ? (nf + 1) >> 1 : 4;
+        const int my_mi = __builtin_amdgcn_readfirstlane(grp == 0 ? mi0 : (FAST ? nf - mi0 : 4));
+        const int rbase = grp == 0 ? 0 : 32 * mi0;   // first tile row of this group
         floatx16 acc[4][2];
         bf16x8_t fa[2][4], fb[2][2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
         // this wave's 4 copies of pair j (K from element k0) of A (or B) of a
         // task with the given offsets, into the pair slot at `base`: rows
@@ -421,40 +426,57 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
             copies(isb, (c_kb + 2 * j) * MF_BK, c_kend, c_a, c_b0, c_an, c_bn, rbn, base);
         };
         // fragments of one K step: half h (the first or second 32 of K) of the
-        // pair slots sa (A) and sb (B)
-        auto read = [&](const uint16_t* sa, const uint16_t* sb, int h) __attribute__((always_inline)) {
+        // pair slots sa (A) and sb (B), for the MI token fragments of this group
+        auto read = [&](auto mic, const uint16_t* sa, const uint16_t* sb, int h) __attribute__((always_inline)) {
+            constexpr int MI = decltype(mic)::value;
+            if constexpr (MI > 0) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const int ch = h * 4 + ks * 2 + (lane >> 5);
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int ch = h * 4 + ks * 2 + (lane >> 5);
 #pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-                    fa[ks][mi] = *reinterpret_cast<const bf16x8_t*>(&sa[swz2(grp * 128 + mi * 32 + (lane & 31), ch)]);
+                    for (int mi = 0; mi < MI; ++mi)
+                        fa[ks][mi] = *reinterpret_cast<const bf16x8_t*>(&sa[swz2(rbase + mi * 32 + (lane & 31), ch)]);
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-                    fb[ks][ni] = *reinterpret_cast<const bf16x8_t*>(&sb[swz2(brow(ni), ch)]);
+                    for (int ni = 0; ni < 2; ++ni)
+                        fb[ks][ni] = *reinterpret_cast<const bf16x8_t*>(&sb[swz2(brow(ni), ch)]);
+                }
             }
         };
         // transposed product: acc[mi][ni] is (B rows of fragment ni) x (tokens of fragment mi)
         // (FAST: copy i of the step goes out right after MFMA i * sp, i < 4:
         // sp = 1 at the first step of a pair, whose copies include group 0's
-        // A(j+1) that must land within 1.5 phases, sp = 2 at the second)
-        auto mma = [&](auto&& cp, auto sp) __attribute__((always_inline)) {
-            constexpr int SP = decltype(sp)::value;
+        // A(j+1) that must land within 1.5 phases, sp = 2 at the second; a
+        // group with fewer fragments spaces them over the MFMAs it has, one
+        // with none issues them back to back)
+        auto mma = [&](auto mic, auto&& cp, auto sp) __attribute__((always_inline)) {
+            constexpr int MI = decltype(mic)::value;
+            constexpr int SP = decltype(sp)::value < (MI > 0 ? MI : 1) ? decltype(sp)::value : (MI > 0 ? MI : 1);
+            if constexpr (MI == 0) {
+                if constexpr (FAST) {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                    for (int ni = 0; ni < 2; ++ni) {
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][ni], fa[ks][mi],
-                                                                               acc[mi][ni], 0, 0, 0);
-                        const int idx = ks * 8 + mi * 2 + ni;
-                        if (FAST && idx % SP == 0 && idx / SP < 4) {
-                            __builtin_amdgcn_sched_barrier(0);
-                            cp(idx / SP);
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
+                    for (int c = 0; c < 4; ++c) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        cp(c);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                        for (int ni = 0; ni < 2; ++ni) {
+                            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks][ni], fa[ks][mi],
+                                                                                   acc[mi][ni], 0, 0, 0);
+                            const int idx = ks * 2 * MI + mi * 2 + ni;
+                            if (FAST && idx % SP == 0 && idx / SP < 4) {
+                                __builtin_amdgcn_sched_barrier(0);
+                                cp(idx / SP);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        }
+            }
         };
 
         // Copy schedule (groups of 4 copies per wave), one stream over the
@@ -504,12 +526,12 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
         first = false;
         // Per K step, each wave: memory phase (fragments of the step, then the
         // copies it issues), barrier, compute phase, barrier.
-        auto step = [&](int after1, int after2, auto&& cp, auto sp) __attribute__((always_inline)) {
+        auto step = [&](auto mic, int after1, int after2, auto&& cp, auto sp) __attribute__((always_inline)) {
             __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): own fragments read
             if (after1 >= 0) wait_copies(after1);
             block_barrier();
             if (!FAST) __builtin_amdgcn_s_setprio(1);
-            mma(cp, sp);
+            mma(mic, cp, sp);
             if (!FAST) __builtin_amdgcn_s_setprio(0);
             if (after2 >= 0) wait_copies(after2);
             block_barrier();
@@ -558,86 +580,109 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
         auto cp = [&](int i) __attribute__((always_inline)) {
             dma16(rd, co[i], lb + (uint32_t)(i * 8 * MF_PK * 2));
         };
-        for (int j = 0; j < P; ++j) {
-            const uint16_t* sa = sA0 + ca * MF_PSLOT;
-            const uint16_t* sb = sB0 + cb * MF_PSLOT;
-            if constexpr (FAST) {
-                read(sa, sb, 0);
-                __builtin_amdgcn_sched_barrier(0);
-                if (grp == 0) prepA(j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
-                else prepB(j + 2, sB0 + tb * MF_PSLOT);
-                step(-1, -1, cp, std::integral_constant<int, 1>{});
-                read(sa, sb, 1);
-                __builtin_amdgcn_sched_barrier(0);
-                if (grp == 0) prepB(j + 2, sB0 + tb * MF_PSLOT);
-                else prepA(j + 2, sA0 + ca * MF_PSLOT);
-                step(grp == 0 ? -1 : 4, grp == 0 ? 4 : -1, cp, std::integral_constant<int, 2>{});
-            } else {
-                read(sa, sb, 0);
-                __builtin_amdgcn_sched_barrier(0);
-                if (j + 1 < P) issue(false, j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
-                else if (nxt) issue_next(false, 0, sA0 + (ca ^ 1) * MF_PSLOT);
-                step(-1, -1, nocp, std::integral_constant<int, 1>{});
-                read(sa, sb, 1);
-                __builtin_amdgcn_sched_barrier(0);
-                bool bnew = true;
-                if (j + 2 < P) issue(true, j + 2, sB0 + tb * MF_PSLOT);
-                else if (nxt) issue_next(true, j + 2 - P, sB0 + tb * MF_PSLOT);
-                else bnew = false;
-                // A(j+1) lands before the next pair; at the task's end without a
-                // streamed successor everything lands
-                const int after = (j + 1 < P || nxt) && bnew ? 4 : 0;
-                step(grp == 0 ? -1 : after, after, nocp, std::integral_constant<int, 1>{});
+        // the K loop and the epilogue for a group of MI token fragments
+        auto kloop = [&](auto mic) __attribute__((always_inline)) {
+            constexpr int MI = decltype(mic)::value;
+            if constexpr (MI > 0) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) acc[i][jj][v] = 0.f;
             }
-            ca ^= 1;
-            const int t = cb;
-            cb = nb;
-            nb = tb;
-            tb = t;
-        }
-
-        // ---- epilogue.  Accumulator element v of lane l: token row
-        // grp*128 + mi*32 + l%32, B-tile row brow0(ni) + 8*(v/4) + 4*(l/32) + v%4,
-        // i.e. four consecutive output columns per (v/4).
-        const int c0 = 4 * (lane >> 5);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-            const int row = grp * 128 + mi * 32 + (lane & 31);
-            if (pi >= 0) {
-                // a part of a split tail tile: raw fp32 sums, tile-local [row][B-tile row]
-                float* pt = a.part + (size_t)pi * (MF_BM * MF_BN) + row * MF_BN;
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int col = ((MODE == 0) ? ni * 128 + wi * 32 : wi * 64 + ni * 32) + 8 * q + c0;
-                        *reinterpret_cast<float4*>(pt + col) = make_float4(
-                            acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
-                    }
-            } else if (MODE == 0) {
-                // h = silu(g) * u, four bf16 (8 bytes) per lane and q
-                uint16_t* hrow = reinterpret_cast<uint16_t*>(a.out) + (size_t)(p0 + row) * N;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int f = nt * 128 + wi * 32 + 8 * q + c0;
-                    float h[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) h[j] = silu(acc[mi][0][4 * q + j]) * acc[mi][1][4 * q + j];
-                    if (row < rows && f < N)
-                        *reinterpret_cast<uint2*>(hrow + f) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+            for (int j = 0; j < P; ++j) {
+                const uint16_t* sa = sA0 + ca * MF_PSLOT;
+                const uint16_t* sb = sB0 + cb * MF_PSLOT;
+                if constexpr (FAST) {
+                    read(mic, sa, sb, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (grp == 0) prepA(j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
+                    else prepB(j + 2, sB0 + tb * MF_PSLOT);
+                    step(mic, -1, -1, cp, std::integral_constant<int, 1>{});
+                    read(mic, sa, sb, 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (grp == 0) prepB(j + 2, sB0 + tb * MF_PSLOT);
+                    else prepA(j + 2, sA0 + ca * MF_PSLOT);
+                    step(mic, grp == 0 ? -1 : 4, grp == 0 ? 4 : -1, cp, std::integral_constant<int, 2>{});
+                } else {
+                    read(mic, sa, sb, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (j + 1 < P) issue(false, j + 1, sA0 + (ca ^ 1) * MF_PSLOT);
+                    else if (nxt) issue_next(false, 0, sA0 + (ca ^ 1) * MF_PSLOT);
+                    step(mic, -1, -1, nocp, std::integral_constant<int, 1>{});
+                    read(mic, sa, sb, 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    bool bnew = true;
+                    if (j + 2 < P) issue(true, j + 2, sB0 + tb * MF_PSLOT);
+                    else if (nxt) issue_next(true, j + 2 - P, sB0 + tb * MF_PSLOT);
+                    else bnew = false;
+                    // A(j+1) lands before the next pair; at the task's end without a
+                    // streamed successor everything lands
+                    const int after = (j + 1 < P || nxt) && bnew ? 4 : 0;
+                    step(mic, grp == 0 ? -1 : after, after, nocp, std::integral_constant<int, 1>{});
                 }
-            } else {
-                float* yrow = reinterpret_cast<float*>(a.out) + (size_t)(p0 + row) * N;
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int n = nt * MF_BN + wi * 64 + ni * 32 + 8 * q + c0;
-                        if (row < rows && n < N)
-                            *reinterpret_cast<float4*>(yrow + n) = make_float4(
-                                acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
-                    }
+                ca ^= 1;
+                const int t = cb;
+                cb = nb;
+                nb = tb;
+                tb = t;
             }
+
+            // ---- epilogue.  Accumulator element v of lane l: token row
+            // rbase + mi*32 + l%32, B-tile row brow0(ni) + 8*(v/4) + 4*(l/32) + v%4,
+            // i.e. four consecutive output columns per (v/4).
+            const int c0 = 4 * (lane >> 5);
+    #pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const int row = rbase + mi * 32 + (lane & 31);
+                if (pi >= 0) {
+                    // a part of a split tail tile: raw fp32 sums, tile-local [row][B-tile row]
+                    float* pt = a.part + (size_t)pi * (MF_BM * MF_BN) + row * MF_BN;
+    #pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+    #pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int col = ((MODE == 0) ? ni * 128 + wi * 32 : wi * 64 + ni * 32) + 8 * q + c0;
+                            *reinterpret_cast<float4*>(pt + col) = make_float4(
+                                acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
+                        }
+                } else if (MODE == 0) {
+                    // h = silu(g) * u, four bf16 (8 bytes) per lane and q
+                    uint16_t* hrow = reinterpret_cast<uint16_t*>(a.out) + (size_t)(p0 + row) * N;
+    #pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int f = nt * 128 + wi * 32 + 8 * q + c0;
+                        float h[4];
+    #pragma unroll
+                        for (int j = 0; j < 4; ++j) h[j] = silu(acc[mi][0][4 * q + j]) * acc[mi][1][4 * q + j];
+                        if (row < rows && f < N)
+                            *reinterpret_cast<uint2*>(hrow + f) = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+                    }
+                } else {
+                    float* yrow = reinterpret_cast<float*>(a.out) + (size_t)(p0 + row) * N;
+    #pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+    #pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int n = nt * MF_BN + wi * 64 + ni * 32 + 8 * q + c0;
+                            if (row < rows && n < N)
+                                *reinterpret_cast<float4*>(yrow + n) = make_float4(
+                                    acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
+                        }
+                }
+            }
+        };
+        if constexpr (FAST) {
+            switch (my_mi) {
+                case 4: kloop(std::integral_constant<int, 4>{}); break;
+                case 3: kloop(std::integral_constant<int, 3>{}); break;
+                case 2: kloop(std::integral_constant<int, 2>{}); break;
+                case 1: kloop(std::integral_constant<int, 1>{}); break;
+                default: kloop(std::integral_constant<int, 0>{}); break;
+            }
+        } else {
+            kloop(std::integral_constant<int, 4>{});
         }
         // group 0 finished one phase earlier (its epilogue ran beside group 1's
         // last MFMAs); when the stream ends here its extra barrier pairs with

@@ -28,6 +28,12 @@ hipError_t launch_route(int act, const void* x, const float* wg, const float* b,
                         int32_t* idx, float* w, int T, int d, int E, int k, hipStream_t s);
 hipError_t launch_dispatch(const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv, int T, int k, int E, hipStream_t s);
+// router + softmax + top-k + dispatch of a small decode batch in one kernel
+// (T*E within 64 register-held pairs; see route_dispatch_small_supported)
+bool route_dispatch_small_supported(int T, int E, int k);
+hipError_t launch_route_dispatch_small(int act, const void* x, const float* wg, const float* b, float* logits,
+                                       int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                                       int32_t* inv, int T, int d, int E, int k, hipStream_t s);
 // counts = {n}, offsets = {0, n}, perm = 0..n-1: the shared expert as a group
 hipError_t launch_identity_group(int32_t* counts, int32_t* offsets, int32_t* perm, int n, hipStream_t s);
 hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, int max_rows,

@@ -451,17 +451,22 @@ def test_groups_straddling_tau(orc):
         assert tokenwise_rel(np_f64(y), y_f).max() < TOL["bf16"]
 
 
-def test_mfma_tile_boundaries(orc):
+@pytest.mark.parametrize("name", ["bf16_prefill_ragged", "bf16_prefill_fast"])
+def test_mfma_tile_boundaries(orc, name):
     """Expert groups around the M-tile sizes: 64-row tiles for groups of at
-    most 128 rows (one or two tiles), 256-row tiles (ragged tail) above."""
-    say("mfma tile boundaries")
-    cfg = SMALL["bf16_prefill_ragged"]
+    most 128 rows (one or two tiles), 256-row tiles (ragged tail) above.  With
+    K a multiple of 64 (gate/up of both configs, down of the second) a ragged
+    256-row tile splits its 32-row fragments between the two wave groups:
+    129 rows (3 + 2 fragments), 200 (4 + 3), 257 (a last tile of one row:
+    1 + 0), 300 (1 + 1), 330 (2 + 1), 353 (2 + 2), 384 (2 + 2)."""
+    say(f"mfma tile boundaries {name}")
+    cfg = SMALL[name]
     d = device_inputs(cfg)
     b = torch.zeros(cfg.E)
     b[0] = 1e3          # expert 0 takes every token; the runner-ups spread the rest
     d1 = dict(d, b_router=b.to(DEV))
     W, S = oracle_weights(d)
-    for TT in (64, 65, 128, 129, 257, 300, 384):
+    for TT in (64, 65, 128, 129, 200, 257, 300, 330, 353, 384):
         x = d["x"][:TT].contiguous()
         y, c, i = run_layer(cfg, d1, tau=16, x=x)
         assert int(c[0]) == TT
@@ -564,4 +569,42 @@ def test_skinny_explicit_tau(orc, cfg, tau, lo, hi):
     y_f, _, _, _ = orc.layer_forward(x, cfg.act, cfg.wt, cfg.k, wr, br, W, S, forced_idx=gi)
     err = tokenwise_rel(np_f64(y), y_f)
     say(f"  max rel {err.max():.3g}")
+    assert err.max() < TOL[cfg.wt]
+
+
+FUSED_ROUTE = [  # (T, E, k, act, d): decode batches routed, ranked and dispatched by one kernel
+    (1, 8, 2, "bf16", 4096), (5, 8, 2, "bf16", 1024), (8, 8, 8, "bf16", 512), (4, 16, 3, "bf16", 2056),
+    (3, 13, 13, "f32", 136), (2, 5, 1, "f32", 64), (8, 7, 4, "bf16", 6144),
+]
+
+
+@pytest.mark.parametrize("T,E,k,act,d", FUSED_ROUTE, ids=[f"T{c[0]}E{c[1]}k{c[2]}{c[3]}d{c[4]}" for c in FUSED_ROUTE])
+def test_decode_fused_routing(orc, T, E, k, act, d):
+    """moe_layer_forward on decode batches, where one kernel computes the
+    router logits, the top-k and the dispatch: expert choices against the
+    oracle's (flip rule), usage counts, outputs on the GPU's choice; router
+    rows 0 and 2 are equal, so every token has an exact tie between them."""
+    cfg = moe_inputs.MoEConfig(f"fused_T{T}E{E}k{k}", T=T, d=d, E=E, k=k, F=256, act=act, wt=act,
+                               model=f"s_fused_{E}_{d}", w_std=0.05)
+    d_ = device_inputs(cfg)
+    wr = d_["w_router"].clone()
+    if E > 2:
+        wr[2] = wr[0]
+    d_["w_router"] = wr.contiguous()
+    y, counts, idx = run_layer(cfg, d_)
+    gi = idx.cpu().numpy()
+    W, S = oracle_weights(d_)
+    x = np_store(d_["x"])
+    y_o, idx_o, _, lg_o = orc.layer_forward(x, cfg.act, cfg.wt, k, np_store(wr), None, W, S)
+    flips = check_routing_with_flips(gi, idx_o, lg_o, k)
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(gi.ravel(), minlength=E))
+    if E > 2:
+        # the tie between experts 0 and 2 resolves to the lower index
+        for t in range(T):
+            row = gi[t].tolist()
+            if 2 in row:
+                assert 0 in row and row.index(0) < row.index(2)
+    y_f, _, _, _ = orc.layer_forward(x, cfg.act, cfg.wt, k, np_store(wr), None, W, S, forced_idx=gi)
+    err = tokenwise_rel(np_f64(y), y_f)
+    say(f"  fused routing T={T} E={E} k={k}: max rel {err.max():.3g} flips {flips}")
     assert err.max() < TOL[cfg.wt]
