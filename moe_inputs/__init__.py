@@ -15,9 +15,12 @@ alone and the decode and prefill workloads of one model share their weights):
 * router ``W_g`` drawn in fp32 with std ``w_std`` (or ``1/sqrt(d)``), kept fp32;
 * expert weights drawn in fp32 with std ``w_std`` (or ``1/sqrt(fan_in)``) on the
   requested device, then rounded to bf16, kept fp32, or quantised to
-  symmetric int4 with one fp16 scale per 128 consecutive K elements:
+  symmetric int4 with one fp16 scale per 128 (or 64) consecutive K elements:
   ``s = fp16(absmax/7)``, ``q = clamp(round_half_even(w/s), -8, 7)``, two codes
-  per byte, the even K index in the low nibble;
+  per byte, the even K index in the low nibble; or to an OCP MX format (E2M1
+  or E4M3 elements, one E8M0 power-of-two scale per 32 K elements,
+  ``X = 2^(floor(log2 absmax) - emax)``, elements rounded to nearest even and
+  saturated);
 * the stacked workload's routers follow ``W_{l+1} = 0.7 W_l + 0.3 N(0, 0.02)``.
 """
 from __future__ import annotations
@@ -43,7 +46,7 @@ class MoEConfig:
     k: int
     F: int
     act: str            # "f32" | "bf16"
-    wt: str             # "f32" | "bf16" | "int4"
+    wt: str             # "f32" | "bf16" | "int4" | "int4g64" | "mxfp4" | "mxfp8"
     model: str          # weight family; workloads of one model share weights
     n_shared: int = 0
     layers: int = 1
@@ -71,6 +74,18 @@ CONFIGS: Dict[str, MoEConfig] = {
         "fine_int4_decode", T=64, d=7168, E=256, k=8, F=2048, act="bf16", wt="int4",
         model="fine256", n_shared=1, w_std=0.02,
         description="fine-grained layer, T=64 d=7168 E=256 top-8 + 1 shared, int4-g128"),
+    "fine_int4_prefill": MoEConfig(
+        "fine_int4_prefill", T=4096, d=7168, E=256, k=8, F=2048, act="bf16", wt="int4",
+        model="fine256", n_shared=1, w_std=0.02,
+        description="the fine-grained int4-g128 layer at prefill, T=4096"),
+    "fine_mxfp4_prefill": MoEConfig(
+        "fine_mxfp4_prefill", T=4096, d=7168, E=256, k=8, F=2048, act="bf16", wt="mxfp4",
+        model="fine256", n_shared=1, w_std=0.02,
+        description="the fine-grained layer with MXFP4 experts (E2M1, E8M0 per 32) at prefill"),
+    "mixtral_mxfp8_prefill": MoEConfig(
+        "mixtral_mxfp8_prefill", T=4096, d=4096, E=8, k=2, F=14336, act="bf16", wt="mxfp8",
+        model="mixtral", w_std=0.02,
+        description="the Mixtral-shaped layer with MXFP8 experts (E4M3, E8M0 per 32) at prefill"),
     "stack4": MoEConfig(
         "stack4", T=512, d=2048, E=64, k=6, F=1408, act="bf16", wt="bf16",
         model="stack64", layers=4, w_std=0.02,
@@ -104,15 +119,15 @@ def randn(shape, std: float, s: int, device="cpu") -> torch.Tensor:
     return t.mul_(std)
 
 
-def quantise_int4_g128(w: torch.Tensor):
-    """Symmetric int4, 128-element groups along the last (K) axis, fp16 scales.
+def quantise_int4_g128(w: torch.Tensor, gs: int = 128):
+    """Symmetric int4, gs-element groups along the last (K) axis, fp16 scales.
 
-    Returns (packed uint8 [..., K/2], scales fp16 [..., K/128]).  Low nibble of
+    Returns (packed uint8 [..., K/2], scales fp16 [..., K/gs]).  Low nibble of
     each byte holds the even K index.
     """
     *lead, K = w.shape
-    assert K % 128 == 0
-    g = w.reshape(*lead, K // 128, 128)
+    assert K % gs == 0
+    g = w.reshape(*lead, K // gs, gs)
     s16 = (g.abs().amax(dim=-1) / 7.0).to(torch.float16)
     s32 = s16.to(torch.float32).unsqueeze(-1)
     safe = torch.where(s32 > 0, s32, torch.ones_like(s32))
@@ -123,6 +138,44 @@ def quantise_int4_g128(w: torch.Tensor):
     return packed.contiguous(), s16.contiguous()
 
 
+# OCP MX element formats: E2M1 (fp4, 2 exponent bits, bias 1, no inf/nan,
+# largest 6 = 1.5 * 2^2) and E4M3 (fp8 "fn": bias 7, largest 448 = 1.75 * 2^8)
+_E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+_MX_EMAX = {"e2m1": 2, "e4m3": 8}
+
+
+def quantise_mx(w: torch.Tensor, elem: str, block: int = 32):
+    """MX quantisation along the last (K) axis: blocks of 32 elements share an
+    E8M0 scale X = 2^(floor(log2(amax)) - emax_elem); each element is v / X
+    rounded to the nearest element value (ties to the even mantissa),
+    saturating at the element format's largest magnitude.
+
+    Returns (codes, scales): codes uint8 [..., K/2] (E2M1, two per byte, the
+    even K index in the low nibble) or [..., K] (E4M3); scales uint8 E8M0
+    codes (2^(code - 127)) [..., K/32]."""
+    *lead, K = w.shape
+    assert K % block == 0
+    g = w.reshape(*lead, K // block, block).to(torch.float64)
+    amax = g.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)                       # amax = m * 2^ex, m in [0.5, 1)
+    shared = torch.where(amax > 0, ex - 1 - _MX_EMAX[elem], torch.zeros_like(ex))
+    shared = shared.clamp(-127, 127)
+    scale_code = (shared + 127).to(torch.uint8)
+    v = g / torch.pow(2.0, shared.to(torch.float64)).unsqueeze(-1)
+    if elem == "e4m3":
+        q = v.clamp(-448.0, 448.0).to(torch.float32).to(torch.float8_e4m3fn)
+        codes = q.view(torch.uint8).reshape(*lead, K)
+    else:
+        table = torch.tensor(_E2M1_VALUES, dtype=torch.float64, device=w.device)
+        a = v.abs().clamp(max=6.0).unsqueeze(-1)
+        dist = (a - table).abs() + (torch.arange(8, device=w.device) % 2) * 1e-9   # ties: even mantissa
+        mag = dist.argmin(dim=-1).to(torch.uint8)
+        sign = ((v < 0) & (mag > 0)).to(torch.uint8) << 3
+        nib = (mag | sign).reshape(*lead, K)
+        codes = (nib[..., 0::2] | (nib[..., 1::2] << 4)).contiguous()
+    return codes.contiguous(), scale_code.reshape(*lead, K // block).contiguous()
+
+
 def _store(w32: torch.Tensor, wt: str):
     if wt == "f32":
         return {"w": w32.contiguous(), "s": None}
@@ -131,6 +184,12 @@ def _store(w32: torch.Tensor, wt: str):
     if wt == "int4":
         p, s = quantise_int4_g128(w32)
         return {"w": p, "s": s}
+    if wt == "int4g64":
+        p, s = quantise_int4_g128(w32, gs=64)
+        return {"w": p, "s": s}
+    if wt in ("mxfp4", "mxfp8"):
+        c, s = quantise_mx(w32, "e2m1" if wt == "mxfp4" else "e4m3")
+        return {"w": c, "s": s}
     raise ValueError(wt)
 
 

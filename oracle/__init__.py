@@ -20,8 +20,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, INT4_G128 = 0, 1, 2
-DTYPES = {"f32": F32, "bf16": BF16, "int4": INT4_G128}
+F32, BF16, INT4_G128, INT4_G64, MXFP4, MXFP8 = 0, 1, 2, 3, 4, 5
+DTYPES = {"f32": F32, "bf16": BF16, "int4": INT4_G128, "int4g64": INT4_G64, "mxfp4": MXFP4,
+          "mxfp8": MXFP8}
+MF_IEEE, MF_FN, MF_FINITE = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -49,6 +51,10 @@ def lib():
         L.orc_dec_f16.argtypes = [ctypes.c_uint16]
         L.orc_dec_int4.restype = ctypes.c_int
         L.orc_dec_int4.argtypes = [ctypes.c_uint8, ctypes.c_int]
+        L.orc_dec_minifloat.restype = ctypes.c_double
+        L.orc_dec_minifloat.argtypes = [ctypes.c_uint32, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.orc_dec_e8m0.restype = ctypes.c_double
+        L.orc_dec_e8m0.argtypes = [ctypes.c_uint8]
         _lib = L
     return _lib
 
@@ -84,6 +90,14 @@ def dec_f16(h: int) -> float:
 
 def dec_int4(byte: int, hi: int) -> int:
     return lib().orc_dec_int4(byte, hi)
+
+
+def dec_minifloat(code: int, ebits: int, mbits: int, bias: int, special: int) -> float:
+    return lib().orc_dec_minifloat(code, ebits, mbits, bias, special)
+
+
+def dec_e8m0(code: int) -> float:
+    return lib().orc_dec_e8m0(code)
 
 
 def router_logits(x, act, w_router, b_router=None):
@@ -188,6 +202,16 @@ def layer_forward(x, act, wt, k, w_router, b_router, W, S=None, residual=None,
         _p(S.get("s_gate")), _p(S.get("s_up")), _p(S.get("s_down")),
         _p(residual), _p(fi), n, _p(sel_a), _p(y), _p(idx), _p(w), _p(lg)), "layer_forward")
     return y, idx, w, lg
+
+
+def topk_overlap(pred, actual):
+    """hist[j] = tokens whose two top-k lists share j experts (j = 0..k)."""
+    pred = np.ascontiguousarray(pred, np.int32)
+    actual = np.ascontiguousarray(actual, np.int32)
+    T, k = pred.shape
+    hist = np.empty(k + 1, np.int32)
+    _check(lib().orc_topk_overlap(T, k, _p(pred), _p(actual), _p(hist)), "topk_overlap")
+    return hist
 
 
 def rmsnorm(h, act, gamma, eps):

@@ -39,6 +39,14 @@
 #define ORC_F32 0
 #define ORC_BF16 1
 #define ORC_INT4_G128 2
+#define ORC_INT4_G64 3
+#define ORC_MXFP4 4
+#define ORC_MXFP8 5
+
+/* special-value conventions of the small float formats decoded below */
+#define ORC_MF_IEEE 0     /* all-ones exponent: inf (zero mantissa) or NaN */
+#define ORC_MF_FN 1       /* no infinities; only all-ones exponent and mantissa is NaN */
+#define ORC_MF_FINITE 2   /* every code is a finite number */
 
 #define ORC_OK 0
 #define ORC_EINVAL (-1)
@@ -81,6 +89,36 @@ double orc_dec_f16(uint16_t h)
     return sign ? -v : v;
 }
 
+/* A small binary floating-point code: sign bit above ebits exponent bits
+ * above mbits mantissa bits, exponent bias `bias`; exponent 0 is zero or
+ * subnormal (m * 2^(1 - bias - mbits)), otherwise (2^mbits + m) *
+ * 2^(e - bias - mbits).  `special` picks the format's treatment of the
+ * all-ones exponent.  E4M3 of the OCP 8-bit formats is (4, 3, 7, FN); E2M1
+ * of the OCP MX formats is (2, 1, 1, FINITE); IEEE binary16 is (5, 10, 15, IEEE). */
+double orc_dec_minifloat(uint32_t code, int ebits, int mbits, int bias, int special)
+{
+    const uint32_t man = code & ((1u << mbits) - 1);
+    const uint32_t ex = (code >> mbits) & ((1u << ebits) - 1);
+    const int sign = (code >> (mbits + ebits)) & 1;
+    const uint32_t emax = (1u << ebits) - 1;
+    double v;
+    if (ex == emax && special == ORC_MF_IEEE)
+        v = man ? NAN : INFINITY;
+    else if (ex == emax && special == ORC_MF_FN && man == (1u << mbits) - 1)
+        v = NAN;
+    else if (ex == 0)
+        v = ldexp((double)man, 1 - bias - mbits);
+    else
+        v = ldexp((double)((1u << mbits) + man), (int)ex - bias - mbits);
+    return sign ? -v : v;
+}
+
+/* E8M0 scale of the OCP MX formats: 2^(code - 127), code 255 is NaN. */
+double orc_dec_e8m0(uint8_t code)
+{
+    return code == 255 ? NAN : ldexp(1.0, (int)code - 127);
+}
+
 /* One 4-bit two's-complement code from a packed byte: hi=0 low nibble. */
 int orc_dec_int4(uint8_t byte, int hi)
 {
@@ -96,18 +134,34 @@ static double act_at(const void *p, int dt, size_t i)
 }
 
 /* Element (row, kk) of a weight matrix stored row-major with K columns.
- * row already folds the expert index: row = e*N + n. */
-static double wt_at(const void *w, const uint16_t *s, int dt, size_t row, size_t K, size_t kk)
+ * row already folds the expert index: row = e*N + n.  Quantised formats:
+ * int4 codes q with one fp16 scale s per group of 128 (or 64) K elements,
+ * w = q * s ([P5] §7.3); MX formats: E2M1 (two codes per byte, even K in the
+ * low nibble) or E4M3 (one per byte) elements times the E8M0 scale of their
+ * block of 32 K elements (the OCP microscaling formats behind the native
+ * MXFP4 / FP8 checkpoints of [P5] §6). */
+static double wt_at(const void *w, const void *s, int dt, size_t row, size_t K, size_t kk)
 {
     if (dt == ORC_F32)
         return (double)((const float *)w)[row * K + kk];
     if (dt == ORC_BF16)
         return orc_dec_bf16(((const uint16_t *)w)[row * K + kk]);
-    {
+    if (dt == ORC_INT4_G128 || dt == ORC_INT4_G64) {
+        const size_t gs = dt == ORC_INT4_G128 ? 128 : 64;
         uint8_t b = ((const uint8_t *)w)[row * (K / 2) + kk / 2];
         int q = orc_dec_int4(b, (int)(kk & 1));
-        double sc = orc_dec_f16(s[row * (K / 128) + kk / 128]);
+        double sc = orc_dec_f16(((const uint16_t *)s)[row * (K / gs) + kk / gs]);
         return (double)q * sc;
+    }
+    {
+        const double x = orc_dec_e8m0(((const uint8_t *)s)[row * (K / 32) + kk / 32]);
+        if (dt == ORC_MXFP8)
+            return orc_dec_minifloat(((const uint8_t *)w)[row * K + kk], 4, 3, 7, ORC_MF_FN) * x;
+        {
+            uint8_t b = ((const uint8_t *)w)[row * (K / 2) + kk / 2];
+            uint32_t c = (kk & 1) ? (b >> 4) & 0xf : b & 0xf;
+            return orc_dec_minifloat(c, 2, 1, 1, ORC_MF_FINITE) * x;
+        }
     }
 }
 
@@ -258,7 +312,7 @@ int orc_dispatch(int T, int k, int E, const int32_t *idx, int32_t *counts,
  * Gate/up are [E][F][d], down is [E][d][F], K contiguous. */
 static void swiglu_row(int d, int F, int act, int wt, const void *xrow_base, size_t xrow,
                        const void *wg, const void *wu, const void *wd,
-                       const uint16_t *sg, const uint16_t *su, const uint16_t *sd,
+                       const void *sg, const void *su, const void *sd,
                        int e, double *h, double *out)
 {
     for (int f = 0; f < F; ++f) {
@@ -284,7 +338,11 @@ static int wt_ok(int wt, int d, int F)
 {
     if (wt == ORC_F32 || wt == ORC_BF16)
         return 1;
-    return wt == ORC_INT4_G128 && d % 128 == 0 && F % 128 == 0;
+    if (wt == ORC_INT4_G128)
+        return d % 128 == 0 && F % 128 == 0;
+    if (wt == ORC_INT4_G64)
+        return d % 64 == 0 && F % 64 == 0;
+    return (wt == ORC_MXFP4 || wt == ORC_MXFP8) && d % 32 == 0 && F % 32 == 0;
 }
 
 /* Expert FFN over dispatched rows: row p of expert e's segment holds token
@@ -292,7 +350,7 @@ static int wt_ok(int wt, int d, int F)
  * ([P3] §2.3, active experts only). */
 int orc_expert_ffn(int T, int d, int E, int k, int F, int act, int wt, const void *x,
                    const void *wg, const void *wu, const void *wd,
-                   const uint16_t *sg, const uint16_t *su, const uint16_t *sd,
+                   const void *sg, const void *su, const void *sd,
                    const int32_t *counts, const int32_t *offsets, const int32_t *perm,
                    double *y_perm)
 {
@@ -326,7 +384,7 @@ int orc_expert_ffn(int T, int d, int E, int k, int F, int act, int wt, const voi
 /* Always-on shared expert (a single expert applied to every token, weight 1). */
 int orc_shared_ffn(int T, int d, int F, int act, int wt, const void *x,
                    const void *wg, const void *wu, const void *wd,
-                   const uint16_t *sg, const uint16_t *su, const uint16_t *sd, double *ys)
+                   const void *sg, const void *su, const void *sd, double *ys)
 {
     if (T < 0 || d <= 0 || F <= 0 || !x || !wg || !wu || !wd || !ys || !wt_ok(wt, d, F))
         return ORC_EINVAL;
@@ -381,9 +439,9 @@ int orc_combine(int T, int d, int k, const double *y_perm, const int32_t *inv,
 int orc_layer_forward(int T, int d, int E, int k, int F, int act, int wt, const void *x,
                       const float *w_router, const float *b_router,
                       const void *wg, const void *wu, const void *wd,
-                      const uint16_t *sg, const uint16_t *su, const uint16_t *sd,
+                      const void *sg, const void *su, const void *sd,
                       const void *shg, const void *shu, const void *shd,
-                      const uint16_t *shsg, const uint16_t *shsu, const uint16_t *shsd,
+                      const void *shsg, const void *shsu, const void *shsd,
                       const void *residual, const int32_t *forced_idx,
                       int n_sel, const int32_t *sel,
                       double *y_out, int32_t *idx_out, double *w_out, double *logits_out)
@@ -459,6 +517,31 @@ int orc_layer_forward(int T, int d, int E, int k, int F, int act, int wt, const 
         free(lg); free(id); free(gw); free(h); free(o);
     }
     return bad ? ORC_EINVAL : ORC_OK;
+}
+
+/* ------------------------------------- one-layer-ahead prediction score */
+/* [P5] §4.2 (PILOT): the next layer's router, run one layer early, picks the
+ * experts to fetch ahead; [P5] §二 quotes the share of the next layer's
+ * experts it predicts.  For token t, the number of experts in both
+ * pred[t][0..k) and actual[t][0..k) (each list holds k distinct experts);
+ * hist[j] counts the tokens with j in common. */
+int orc_topk_overlap(int T, int k, const int32_t *pred, const int32_t *actual, int32_t *hist)
+{
+    if (T < 0 || k <= 0 || !pred || !actual || !hist)
+        return ORC_EINVAL;
+    for (int j = 0; j <= k; ++j)
+        hist[j] = 0;
+    for (int t = 0; t < T; ++t) {
+        int n = 0;
+        for (int j = 0; j < k; ++j)
+            for (int m = 0; m < k; ++m)
+                if (pred[(size_t)t * k + j] == actual[(size_t)t * k + m]) {
+                    ++n;
+                    break;
+                }
+        hist[n] += 1;
+    }
+    return ORC_OK;
 }
 
 /* ------------------------------------------------------------ RMSNorm (A9) */

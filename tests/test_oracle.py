@@ -409,3 +409,131 @@ def test_zipf_bias_reaches_targets(orc):
     idx, _ = orc.topk(lg, cfg.k)
     f = np.bincount(idx.ravel(), minlength=cfg.E) / idx.size
     np.testing.assert_allclose(f, moe_inputs.zipf_targets(cfg.E), atol=0.01)
+
+
+def test_topk_overlap_brute_force(orc):
+    """The one-layer-ahead prediction score against set intersections written
+    out in Python: random distinct selections, identical ones (every token
+    shares k), disjoint ones (shares 0) and reversed order (order ignored)."""
+    rng = np.random.default_rng(11)
+    for T, E, k in ((1, 4, 1), (37, 8, 2), (64, 64, 6), (9, 16, 16)):
+        pred = np.array([rng.choice(E, k, replace=False) for _ in range(T)], np.int32)
+        act = np.array([rng.choice(E, k, replace=False) for _ in range(T)], np.int32)
+        want = np.zeros(k + 1, np.int64)
+        for t in range(T):
+            want[len(set(pred[t].tolist()) & set(act[t].tolist()))] += 1
+        assert orc.topk_overlap(pred, act).tolist() == want.tolist()
+        assert orc.topk_overlap(pred, pred[:, ::-1].copy()).tolist() == [0] * k + [T]
+        if 2 * k <= E:
+            other = np.array([[e for e in range(E) if e not in row][:k] for row in pred], np.int32)
+            assert orc.topk_overlap(pred, other).tolist() == [T] + [0] * k
+
+
+# ---------------------------------------------------------- small float formats
+
+def test_minifloat_decoder_against_library_formats(orc):
+    """The oracle's generic small-float decoder, pinned on formats a library
+    implements: every IEEE binary16 code against NumPy, every E4M3 ("fn") code
+    against torch.float8_e4m3fn, and the all-finite convention against NumPy
+    on every finite binary16 code (the path E2M1 takes)."""
+    codes = np.arange(65536, dtype=np.uint32)
+    ref = codes.astype(np.uint16).view(np.float16).astype(np.float64)
+    got = np.array([orc.dec_minifloat(int(c), 5, 10, 15, orc.MF_IEEE) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    fin = ((codes >> 10) & 31) != 31
+    got_f = np.array([orc.dec_minifloat(int(c), 5, 10, 15, orc.MF_FINITE) for c in codes[fin]])
+    assert np.array_equal(got_f, ref[fin])
+    e4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got8 = np.array([orc.dec_minifloat(c, 4, 3, 7, orc.MF_FN) for c in range(256)])
+    assert np.array_equal(np.isnan(got8), np.isnan(e4))
+    assert np.array_equal(got8[~np.isnan(e4)], e4[~np.isnan(e4)])
+
+
+def test_e2m1_and_e8m0_decoders(orc):
+    """E2M1 (the OCP MX fp4 element): the sixteen codes are the eight
+    magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives (sign in bit 3);
+    E8M0 scales against torch.float8_e8m0fnu on every code."""
+    mags = [orc.dec_minifloat(c, 2, 1, 1, orc.MF_FINITE) for c in range(8)]
+    assert mags == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for c in range(8):
+        assert orc.dec_minifloat(c | 8, 2, 1, 1, orc.MF_FINITE) == -mags[c]
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = np.array([orc.dec_e8m0(c) for c in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255])
+
+
+def _dequant_np(cfg_wt, w, s, K):
+    """Dequantised fp32-representable weights, computed here with NumPy and
+    torch decoders (independently of the oracle's C decoders)."""
+    if cfg_wt in ("int4", "int4g64"):
+        gs = 128 if cfg_wt == "int4" else 64
+        lo = (w & 0xF).astype(np.int32)
+        hi = (w >> 4).astype(np.int32)
+        q = np.empty(w.shape[:-1] + (K,), np.int32)
+        q[..., 0::2], q[..., 1::2] = lo, hi
+        q = np.where(q >= 8, q - 16, q)
+        sc = s.view(np.float16).astype(np.float64)
+        return q * np.repeat(sc, gs, axis=-1)
+    x = torch.from_numpy(s.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    x = np.repeat(x, 32, axis=-1)
+    if cfg_wt == "mxfp8":
+        e = torch.from_numpy(w.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        return e * x
+    table = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    nib = np.empty(w.shape[:-1] + (K,), np.uint8)
+    nib[..., 0::2], nib[..., 1::2] = w & 0xF, w >> 4
+    v = table[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+    return v * x
+
+
+@pytest.mark.parametrize("wt", ["int4g64", "mxfp4", "mxfp8"])
+def test_quantised_layer_equals_fp32_layer_of_dequantised_weights(orc, wt):
+    """A layer with int4-g64, MXFP4 or MXFP8 experts equals the fp32 layer of
+    the weights dequantised independently (NumPy / torch decoders): pins code
+    order inside bytes, group and block indexing and scale decoding.  The
+    dequantised values are exactly representable in fp32."""
+    cfg = moe_inputs.MoEConfig(f"q_{wt}", T=9, d=128, E=3, k=2, F=192, act="bf16", wt=wt,
+                               model=f"q_{wt}", n_shared=1, w_std=0.05)
+    inp = moe_inputs.generate(cfg, seed=0)
+    L = inp["layers"][0]
+    x = np_store(inp["x"])
+    W = layer_np(L)
+    S = shared_np(L)
+    deq = {}
+    for n, K in (("gate", cfg.d), ("up", cfg.d), ("down", cfg.F)):
+        deq["w_" + n] = _dequant_np(wt, W["w_" + n], W["s_" + n], K).astype(np.float32)
+    deq_s = {("w_" + n): _dequant_np(wt, S["w_" + n], S["s_" + n], K).astype(np.float32)
+             for n, K in (("gate", cfg.d), ("up", cfg.d), ("down", cfg.F))}
+    for n in deq:
+        assert np.array_equal(deq[n].astype(np.float64), _dequant_np(wt, W[n], W["s_" + n[2:]],
+                                                                     deq[n].shape[-1]))
+    wr = np_store(L["w_router"])
+    y_q, idx_q, _, _ = orc.layer_forward(x, "bf16", wt, cfg.k, wr, None, W, S)
+    y_f, idx_f, _, _ = orc.layer_forward(x, "bf16", "f32", cfg.k, wr, None, deq, deq_s)
+    assert np.array_equal(idx_q, idx_f)
+    np.testing.assert_allclose(y_q, y_f, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("elem", ["e2m1", "e4m3"])
+def test_mx_quantiser_rounds_to_nearest(elem):
+    """The input generator's MX quantiser (not the oracle): every element lies
+    within half an element step of the value it encodes; values beyond the
+    element format's largest magnitude (possible with the shared exponent
+    floor(log2 amax) - emax) saturate to it."""
+    w = torch.randn(4, 256, generator=torch.Generator().manual_seed(3)) * 0.02
+    codes, sc = moe_inputs.quantise_mx(w, elem)
+    deq = _dequant_np("mxfp4" if elem == "e2m1" else "mxfp8", codes.numpy(), sc.numpy(), 256)
+    x = np.repeat(torch.from_numpy(sc.numpy().copy()).view(torch.float8_e8m0fnu).double().numpy(), 32, -1)
+    v = w.double().numpy() / x
+    err = np.abs(deq / x - v)
+    # the element grid's spacing at |v|: 2^(floor(log2|v|) - mbits) above the subnormals
+    mbits = 1 if elem == "e2m1" else 3
+    minexp = 0 if elem == "e2m1" else -6
+    e = np.maximum(np.floor(np.log2(np.maximum(np.abs(v), 1e-30))), minexp)
+    top = 6.0 if elem == "e2m1" else 448.0
+    inside = np.abs(v) <= top
+    assert (err[inside] <= 0.5 * 2.0 ** (e[inside] - mbits) + 1e-12).all()
+    assert np.array_equal(np.abs(deq / x)[~inside], np.full((~inside).sum(), top))
