@@ -162,8 +162,10 @@ def ffn_work(cfg, U):
     each hit expert's three matrices read once (batch union, plus the shared
     expert's), gathered x rows read, h written and read back, y_perm written."""
     tk = cfg.T * cfg.k
-    if cfg.wt == "int4":
-        mat = cfg.F * cfg.d // 2 + cfg.F * (cfg.d // 128) * 2
+    if cfg.wt in ("int4", "int4g64"):
+        mat = cfg.F * cfg.d // 2 + cfg.F * (cfg.d // (128 if cfg.wt == "int4" else 64)) * 2
+    elif cfg.wt in ("mxfp4", "mxfp8"):
+        mat = cfg.F * cfg.d // (2 if cfg.wt == "mxfp4" else 1) + cfg.F * (cfg.d // 32)
     else:
         mat = cfg.F * cfg.d * (4 if cfg.wt == "f32" else 2)
     ab = 4 if cfg.act == "f32" else 2
@@ -341,8 +343,14 @@ def ffn_paths(cfg, counts, tau):
     MFMA tiles; below it, when the largest group exceeds one GEMV pass, the
     skinny MFMA kernel (ceil(rows / 16) 16-token tiles, up to 64 rows) takes
     them all, else the GEMV."""
+    if cfg.wt in ("int4g64", "mxfp4", "mxfp8"):
+        return f"{cfg.wt} dequantising MFMA GEMM"
     if cfg.wt == "int4":
-        return "int4 skinny MFMA" if cfg.d % 1024 == 0 and cfg.F % 1024 == 0 else "int4 GEMV"
+        t = 32 if tau == 0 else tau
+        big = tau >= 0 and any(int(v) > t for v in counts)
+        skinny = "int4 skinny MFMA" if cfg.d % 1024 == 0 and cfg.F % 1024 == 0 else "int4 GEMV"
+        small = any(0 < int(v) <= t for v in counts) or tau < 0
+        return " + ".join(([skinny] if small else []) + (["int4 dequantising MFMA GEMM"] if big else []))
     if cfg.wt != "bf16" or tau < 0:
         return "GEMV"
     skinny = cfg.act == "bf16" and cfg.d % 64 == 0 and cfg.F % 64 == 0
@@ -460,6 +468,23 @@ def stack_leg(steps, warmup):
         if evs is not None:
             evs[cfg.layers].record(st)
 
+    # one-layer-ahead expert prediction (outside the timed loop): layer l+1's
+    # router on layer l's normed input, scored against layer l+1's choice
+    wrs = [inp["layers"][l]["w_router"].to(DEV) for l in range(cfg.layers)]
+    pilot = []
+    one()
+    for l in range(cfg.layers - 1):
+        moe.moe_rmsnorm(nshape, hs[l], gammas[l], inp["eps"], nrm, stream=st)
+        lg = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=DEV)
+        pred = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=DEV)
+        pw = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=DEV)
+        moe.moe_route(nshape, nrm, wrs[l + 1], None, lg, pred, pw, stream=st)
+        ov = torch.empty(cfg.k + 1, dtype=torch.int32, device=DEV)
+        moe.moe_topk_overlap(nshape, pred, layers[l + 1].topk_idx, ov, stream=st)
+        h = ov.cpu().numpy()
+        pilot.append({"from_layer": l, "to_layer": l + 1, "tokens_by_shared_experts": h.tolist(),
+                      "hit_rate": round(float((np.arange(cfg.k + 1) * h).sum()) / (cfg.T * cfg.k), 4)})
+
     for _ in range(warmup):
         one()
     torch.cuda.synchronize()
@@ -491,7 +516,8 @@ def stack_leg(steps, warmup):
             "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s through the 4-layer stack",
             "ms_per_step": round(ms, 5), "ms_per_step_median": round(float(np.median(stack)), 5),
             "ms_per_step_p99": round(float(np.percentile(stack, 99)), 5), "steps": steps, "warmup": warmup,
-            "per_layer": layer_objs, "usage_histogram": counts, "usage_lines": len(lines)}
+            "per_layer": layer_objs, "usage_histogram": counts, "usage_lines": len(lines),
+            "next_layer_prediction": pilot}
 
 
 def low_latency_leg(dcfg, wr, W, orc=None, steps=200, warmup=20):
@@ -668,7 +694,7 @@ def main():
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(lay["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg.act == "bf16" and cfg.wt == "bf16" else
-                 ("bf16/int4" if cfg.wt == "int4" else "f32"),
+                 ("f32" if cfg.wt == "f32" else f"bf16/{cfg.wt}"),
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "k": cfg.k,
                    "F": cfg.F, "weights": wt, "shared_experts": cfg.n_shared,
@@ -709,7 +735,6 @@ def main():
         log("int4 decode leg (tiled codes)")
         ix, iwr, ibr, iW = device_layer(icfg)
         iWt = moe.layer.pack_int4_tiled(iW)
-        del iW
         torch.cuda.synchronize()
         irun = Runner(icfg, ix, iwr, ibr, iWt, tau=args.tau, wt="int4_tiled")
         ileg = workload_leg(irun, steps, warmup, args.tau, ceilings, icfg.name if args.tau == 0 else None)
@@ -717,6 +742,22 @@ def main():
         log(json.dumps(out["int4_decode"]))
         del irun, iWt
         torch.cuda.empty_cache()
+        # the same int4 layer at prefill (row-major codes: the dequantising
+        # grouped GEMM), then MXFP4 experts of that shape and MXFP8 experts of
+        # the Mixtral shape
+        psteps, pwarm = max(50, steps), max(20, warmup)
+        for name, Wq in (("fine_int4_prefill", iW), ("fine_mxfp4_prefill", None),
+                         ("mixtral_mxfp8_prefill", None)):
+            qcfg = moe_inputs.CONFIGS[name]
+            log(f"{name}: quantised experts at prefill")
+            qx, qwr, qbr, qW = device_layer(qcfg, shared_weights=Wq)
+            qrun = Runner(qcfg, qx, qwr, qbr, qW, tau=args.tau)
+            qleg = workload_leg(qrun, psteps, pwarm, args.tau, ceilings)
+            out[name] = leg_summary(qcfg, qleg, psteps, pwarm)
+            log(json.dumps(out[name]))
+            del qrun, qW, qx
+            torch.cuda.empty_cache()
+        del iW
         out["stack4"] = stack_leg(steps, warmup)
         log(json.dumps(out["stack4"]))
     print(json.dumps(out), flush=True)

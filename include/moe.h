@@ -55,30 +55,48 @@ typedef enum {
                                two per byte, even K index in the low nibble) with one
                                fp16 scale per 128 consecutive K elements; w = q * s
                                ([P5] §7.3: int4 experts, per-group scales) */
-    MOE_INT4_G128_TILED = 3 /* weights only: the same codes and scales, the code bytes
+    MOE_INT4_G128_TILED = 3,/* weights only: the same codes and scales, the code bytes
                                of every [N][K/2] matrix in the tiled order that
                                moe_pack_int4_tiled writes (scales stay [N][K/128]);
                                needs d and F multiples of 1024, at most 8192 */
+    MOE_INT4_G64 = 4,       /* weights only: int4 codes as MOE_INT4_G128 with one fp16
+                               scale per 64 consecutive K elements ([P5] §7.3 weighs
+                               group size 64 against 128 and per-row) */
+    MOE_MXFP4 = 5,          /* weights only: OCP MX fp4, E2M1 codes two per byte (even K
+                               index in the low nibble), one E8M0 scale byte per 32
+                               consecutive K elements: w = e2m1 * 2^(s - 127) */
+    MOE_MXFP8 = 6           /* weights only: OCP MX fp8, E4M3 codes one per byte, one
+                               E8M0 scale byte per 32 K elements ([P5] §6: models
+                               shipped as native MXFP4 / FP8 checkpoints) */
 } moe_dtype;
 
 /* Shape of one MoE layer call.
  *   T tokens, hidden size d, E routed experts, top-k, expert FFN width F.
  *   n_shared: 0 or 1 always-on shared expert of width F (weight 1).
  *   act: dtype of x, residual and y (MOE_F32 or MOE_BF16).
- *   wt:  dtype of expert weights (MOE_F32 with act F32; MOE_BF16 or
- *        MOE_INT4_G128 with act BF16).
+ *   wt:  dtype of expert weights (MOE_F32 with act F32; MOE_BF16 or any of the
+ *        quantised formats with act BF16).  Quantised weights are widened to
+ *        bf16 in registers before the matrix cores: exactly for MXFP4/MXFP8
+ *        and for int4-g128 groups of at most tau rows; larger int4 groups and
+ *        every int4-g64 group round q*s to the nearest bf16 (<= 2^-9 relative
+ *        per weight).
  *   tau: bf16 expert groups with at most tau rows run the HBM-streaming
  *        kernels (the GEMV, or, when some group is larger than one GEMV pass,
  *        the skinny MFMA kernel, which covers up to 64 rows and needs d and F
  *        multiples of 64), larger groups the MFMA grouped GEMM.  0 selects
  *        the default: 64 where the skinny kernel serves both projections and
- *        d and F are at least 4096, else 16.  Negative forces the GEMV for every group.  fp32 and int4
- *        weights ignore tau (GEMV; int4 with K a multiple of 1024 on the
- *        matrix cores).
+ *        d and F are at least 4096, else 16.  Negative forces the GEMV for every group.
+ *        int4-g128 (row-major codes): groups of at most tau rows (0: 32) run
+ *        the skinny int4 kernels (matrix cores for K a multiple of 1024, else
+ *        the GEMV), larger ones the dequantising grouped GEMM; negative keeps
+ *        every group on the skinny kernels.  fp32, tiled int4, int4-g64 and
+ *        MX weights ignore tau.
  * Limits (MOE_EINVAL otherwise): T >= 0, 1 <= k <= E <= 256, k <= 16,
- *   d, F >= 8 and multiples of 8; int4: d and F multiples of 128.
- * Limits of this build (MOE_EUNSUPPORTED otherwise): d, F <= 16384 (bf16),
- *   <= 8192 (fp32), <= 16384 (int4); bf16: T*k*F*2 and T*d*2 bytes < 2 GiB. */
+ *   d, F >= 8 and multiples of 8; int4-g128: d and F multiples of 128;
+ *   int4-g64, MXFP4, MXFP8: multiples of 64.
+ * Limits of this build (MOE_EUNSUPPORTED otherwise): d, F <= 16384 (bf16 and
+ *   the quantised formats), <= 8192 (fp32); bf16 and quantised weights:
+ *   T*k*F*2 and T*d*2 bytes < 2 GiB. */
 typedef struct {
     int32_t T, d, E, k, F;
     int32_t n_shared;
@@ -89,9 +107,11 @@ typedef struct {
 
 /* Expert weights, [E][N][K] with K contiguous (the merged per-layer expert
  * tensor, experts contiguous, of [P3] §3.1; gate/up/down = w1/w3/w2 of [P1] §3.1):
- *   w_gate, w_up: [E][F][d]   (int4: uint8 [E][F][d/2] + fp16 scales [E][F][d/128])
- *   w_down:       [E][d][F]   (int4: uint8 [E][d][F/2] + fp16 scales [E][d][F/128])
- *   s_*: fp16 scales, NULL unless wt == MOE_INT4_G128.
+ *   w_gate, w_up: [E][F][d]   (int4, MXFP4: uint8 [E][F][d/2]; MXFP8: uint8 [E][F][d])
+ *   w_down:       [E][d][F]   (int4, MXFP4: uint8 [E][d][F/2]; MXFP8: uint8 [E][d][F])
+ *   s_*: scales of the quantised formats, NULL otherwise: fp16 [E][N][K/128]
+ *        (MOE_INT4_G128, _TILED) or [E][N][K/64] (MOE_INT4_G64); uint8 E8M0
+ *        [E][N][K/32] (MOE_MXFP4, MOE_MXFP8).
  *   sh_*: the shared expert, same layouts with E = 1; NULL when n_shared == 0. */
 typedef struct {
     const void *w_gate, *w_up, *w_down;
@@ -203,6 +223,19 @@ size_t moe_workspace_bytes(const moe_shape *shape);
  * the stacked workload's own definition.)  Uses shape->T and shape->d only. */
 int moe_rmsnorm(const moe_shape *shape, const void *h, const float *gamma, float eps,
                 void *out, void *stream, char *err, size_t err_len);
+
+/* One-layer-ahead expert prediction, scored ([P5] §4.2: the router of the next
+ * layer run one layer early chooses the experts to fetch ahead; [P5] §二
+ * quotes the share it gets right).  A prediction is moe_route with layer
+ * l+1's router on layer l's input; this call compares it with the experts
+ * layer l+1 then chose.
+ *   pred_idx, actual_idx [T][k] int32 (uses shape->T and shape->k only;
+ *   entries compared as sets per token, values not range-checked)
+ *   hist [k+1] int32 output: hist[j] = tokens whose two selections share
+ *   exactly j experts; the hit rate is sum_j j*hist[j] / (T*k).
+ * Integer work, bit-exact. */
+int moe_topk_overlap(const moe_shape *shape, const int32_t *pred_idx, const int32_t *actual_idx,
+                     int32_t *hist, void *stream, char *err, size_t err_len);
 
 /* Weight preparation, once per weight set: rewrite int4 code bytes from the
  * row-major layout of MOE_INT4_G128 ([N][K/2] per matrix, [P5] §7.3) into the

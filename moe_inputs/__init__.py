@@ -155,21 +155,27 @@ def quantise_mx(w: torch.Tensor, elem: str, block: int = 32):
     codes (2^(code - 127)) [..., K/32]."""
     *lead, K = w.shape
     assert K % block == 0
-    g = w.reshape(*lead, K // block, block).to(torch.float64)
+    g = w.reshape(*lead, K // block, block).to(torch.float32)
     amax = g.abs().amax(dim=-1)
     _, ex = torch.frexp(amax)                       # amax = m * 2^ex, m in [0.5, 1)
     shared = torch.where(amax > 0, ex - 1 - _MX_EMAX[elem], torch.zeros_like(ex))
     shared = shared.clamp(-127, 127)
     scale_code = (shared + 127).to(torch.uint8)
-    v = g / torch.pow(2.0, shared.to(torch.float64)).unsqueeze(-1)
+    # dividing by a power of two is exact in fp32 (the weights are far from
+    # the subnormal range)
+    v = torch.ldexp(g, (-shared).unsqueeze(-1).to(torch.float32))
     if elem == "e4m3":
-        q = v.clamp(-448.0, 448.0).to(torch.float32).to(torch.float8_e4m3fn)
+        q = v.clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
         codes = q.view(torch.uint8).reshape(*lead, K)
     else:
-        table = torch.tensor(_E2M1_VALUES, dtype=torch.float64, device=w.device)
-        a = v.abs().clamp(max=6.0).unsqueeze(-1)
-        dist = (a - table).abs() + (torch.arange(8, device=w.device) % 2) * 1e-9   # ties: even mantissa
-        mag = dist.argmin(dim=-1).to(torch.uint8)
+        # nearest E2M1 magnitude code: count the midpoints below |v|; a value
+        # on a midpoint goes to the neighbour with the even mantissa (code 0,
+        # 2, 4 or 6), i.e. down at 0.25, 1.25, 2.5, 5 and up at 0.75, 1.75, 3.5
+        a = v.abs()
+        mag = torch.zeros_like(a, dtype=torch.uint8)
+        for b, up in ((0.25, False), (0.75, True), (1.25, False), (1.75, True), (2.5, False), (3.5, True),
+                      (5.0, False)):
+            mag += (a >= b if up else a > b).to(torch.uint8)
         sign = ((v < 0) & (mag > 0)).to(torch.uint8) << 3
         nib = (mag | sign).reshape(*lead, K)
         codes = (nib[..., 0::2] | (nib[..., 1::2] << 4)).contiguous()

@@ -84,28 +84,33 @@ int check_shape(const moe_shape* s, char* err, size_t err_len) {
         return fail(err, err_len, MOE_EINVAL, "n_shared=%d must be 0 or 1", s->n_shared);
     if (s->act != MOE_F32 && s->act != MOE_BF16)
         return fail(err, err_len, MOE_EINVAL, "act=%d is not MOE_F32 or MOE_BF16", s->act);
-    if (s->wt != MOE_F32 && s->wt != MOE_BF16 && s->wt != MOE_INT4_G128 && s->wt != MOE_INT4_G128_TILED)
+    if (s->wt < MOE_F32 || s->wt > MOE_MXFP8)
         return fail(err, err_len, MOE_EINVAL, "wt=%d is not a moe_dtype", s->wt);
     const bool int4 = s->wt == MOE_INT4_G128 || s->wt == MOE_INT4_G128_TILED;
+    const bool quant = s->wt >= MOE_INT4_G128;
     if (int4 && (s->d % 128 || s->F % 128))
         return fail(err, err_len, MOE_EINVAL, "int4-g128 weights need d and F multiples of 128 (d=%d F=%d)",
                     s->d, s->F);
+    if (quant && !int4 && (s->d % 64 || s->F % 64))
+        return fail(err, err_len, MOE_EINVAL, "int4-g64 and MX weights need d and F multiples of 64 (d=%d F=%d)",
+                    s->d, s->F);
     const bool ok_combo = (s->act == MOE_F32 && s->wt == MOE_F32) ||
-                          (s->act == MOE_BF16 && (s->wt == MOE_BF16 || int4));
+                          (s->act == MOE_BF16 && (s->wt == MOE_BF16 || quant));
     if (!ok_combo)
         return fail(err, err_len, MOE_EUNSUPPORTED, "activation dtype %d with weight dtype %d is not built",
                     s->act, s->wt);
-    // the MFMA path addresses x and h with 32-bit buffer offsets
-    if (s->wt == MOE_BF16 && ((size_t)s->T * s->k * s->F * 2 >= ((size_t)1 << 31) ||
-                              (size_t)s->T * s->d * 2 >= ((size_t)1 << 31)))
+    // the MFMA paths address x and h with 32-bit buffer offsets
+    if ((s->wt == MOE_BF16 || quant) && ((size_t)s->T * s->k * s->F * 2 >= ((size_t)1 << 31) ||
+                                         (size_t)s->T * s->d * 2 >= ((size_t)1 << 31)))
         return fail(err, err_len, MOE_EUNSUPPORTED, "T*k*F and T*d bf16 buffers must stay below 2 GiB");
     // the tiled layout is read by the int4 MFMA kernel only
     if (s->wt == MOE_INT4_G128_TILED && (!i4mfma_supported(s->d, s->F) || !i4mfma_supported(s->F, s->d)))
         return fail(err, err_len, MOE_EUNSUPPORTED,
                     "tiled int4 weights need d and F multiples of 1024 and at most 8192 (d=%d F=%d)", s->d, s->F);
-    // the GEMV's register-resident token fragments bound K; int4 is held to
-    // the 16384 the header states (the GEMV could take 32768)
-    const int kmax = int4 ? std::min(16384, gemv_max_k(MOE_INT4_G128)) : gemv_max_k(s->wt);
+    // the GEMV's register-resident token fragments bound K; the quantised
+    // formats are held to the 16384 the header states (the int4 GEMV could
+    // take 32768; the dequantising GEMM has no such bound)
+    const int kmax = quant ? 16384 : gemv_max_k(s->wt);
     if (s->d > kmax || s->F > kmax)
         return fail(err, err_len, MOE_EUNSUPPORTED, "d=%d / F=%d exceed this build's limit %d for this dtype",
                     s->d, s->F, kmax);
@@ -121,9 +126,36 @@ struct Layout {
 
 bool is_int4(const moe_shape* s) { return s->wt == MOE_INT4_G128 || s->wt == MOE_INT4_G128_TILED; }
 
-// The shared expert of bf16 and fp32 layers runs as a group of its own (one
-// expert that every token picks once): counts, offsets and an identity perm.
-bool shared_as_group(const moe_shape* s) { return s->n_shared && !is_int4(s); }
+constexpr int kDefaultInt4Tau = 32;
+
+// Format code of the dequantising grouped GEMM for this weight dtype, or -1
+// when it does not serve it (fp32, bf16, tiled int4 codes)
+int dq_format(const moe_shape* s) {
+    if (s->wt == MOE_INT4_G128 || s->wt == MOE_INT4_G64) return 0;
+    if (s->wt == MOE_MXFP4) return 1;
+    if (s->wt == MOE_MXFP8) return 2;
+    return -1;
+}
+
+// Groups above this many rows run the dequantising GEMM (-1: none does):
+// int4-g128 keeps groups of at most tau rows (0: 32) on the skinny int4
+// kernels; int4-g64 and MX weights run every group on it.
+int dq_tau(const moe_shape* s) {
+    if (s->wt == MOE_INT4_G128) return s->tau < 0 ? -1 : (s->tau == 0 ? kDefaultInt4Tau : s->tau);
+    return dq_format(s) >= 0 ? 0 : -1;
+}
+
+// The shared expert runs as a group of its own (one expert that every token
+// picks once: counts, offsets and an identity perm) for bf16 and fp32 layers
+// and wherever the dequantising GEMM may take it; otherwise (tiled int4,
+// row-major int4 with T within the skinny kernels' range) it rides in the
+// skinny int4 launches.
+bool shared_as_group(const moe_shape* s) {
+    if (!s->n_shared) return false;
+    if (!is_int4(s)) return true;
+    const int t = dq_tau(s);
+    return t >= 0 && s->T > t;
+}
 
 int effective_tau(const moe_shape* s);
 
@@ -150,7 +182,7 @@ Layout layout(const moe_shape* s) {
     L.offsets = o; o += up((E + 1) * 4);
     L.perm = o; o += up(tk * 4);
     L.inv = o; o += up(tk * 4);
-    L.tiles = o; o += up((size_t)mfma_plan_ints(s->T, s->k, s->E) * 4);
+    L.tiles = o; o += up((size_t)std::max(mfma_plan_ints(s->T, s->k, s->E), dq_plan_ints(s->T, s->k, s->E)) * 4);
     L.h = o; o += up(tk * F * hb);
     L.yp = o; o += up(tk * d * 4);
     L.hs = o; o += s->n_shared ? up(T * F * hb) : 0;
@@ -201,6 +233,12 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     float* part = b.part_cap ? b.part : nullptr;
     const int part_cap = b.part_cap;
     const int max_mt = mfma_max_tiles(s->T, s->k, s->E);
+    // quantised groups above dqt rows: the dequantising grouped GEMM
+    const int dqf = dq_format(s), dqt = dq_tau(s);
+    const bool use_dq = dqf >= 0 && dqt >= 0 && s->T > dqt;
+    const bool skinny_q = dqt != 0;          // some groups stay on the GEMV / skinny int4 kernels
+    const int dq_mt = dq_max_tiles(s->T, s->k, s->E);
+    const int gs = s->wt == MOE_INT4_G64 ? 64 : 128;
     const int max_rows_gemv = use_mfma ? tau : s->T;   // a group holds at most T rows
     int rc;
 
@@ -208,6 +246,10 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     if (use_mfma) {
         rc = hip_check(launch_mfma_plan(counts, offsets, s->E, tau, tiles, max_mt, st), st,
                        "mfma plan", err, err_len);
+        if (rc) return rc;
+    }
+    if (use_dq) {
+        rc = hip_check(launch_dq_plan(counts, offsets, s->E, dqt, tiles, dq_mt, st), st, "dq plan", err, err_len);
         if (rc) return rc;
     }
     // routed experts (g) and the shared expert (q: one expert over all T rows)
@@ -218,10 +260,10 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     g.topk = s->k;
     g.T = s->T;
     g.E = s->E;
-    g.tau = use_mfma ? tau : -1;
+    g.tau = use_mfma ? tau : (use_dq ? dqt : -1);
     GemvArgs q{};
     q.topk = 1; q.T = s->T; q.E = 1; q.tau = -1;
-    const GemvArgs* qp = (s->n_shared && is_int4(s)) ? &q : nullptr;
+    const GemvArgs* qp = (s->n_shared && is_int4(s) && !shared_as_group(s)) ? &q : nullptr;
     const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
     const bool tiled = s->wt == MOE_INT4_G128_TILED;
     // bf16 groups below the MFMA tiles: when one of them is larger than a
@@ -275,8 +317,16 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     q.w0 = w->sh_gate; q.w1 = w->sh_up;
     q.s0 = (const uint16_t*)w->sh_s_gate; q.s1 = (const uint16_t*)w->sh_s_up;
     q.in = x; q.out = hs; q.N = s->F; q.K = s->d;
-    rc = pass(0, "gate/up");
-    if (rc) return rc;
+    if (skinny_q) {
+        rc = pass(0, "gate/up");
+        if (rc) return rc;
+    }
+    if (use_dq) {
+        rc = hip_check(launch_dq_ffn(0, dqf, gs, w->w_gate, w->w_up, w->s_gate, w->s_up, x, h, perm, tiles, s->F,
+                                     s->d, s->k, dq_mt, s->T, st),
+                       st, "dq gate/up", err, err_len);
+        if (rc) return rc;
+    }
     if (use_mfma) {
         rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, s->E, s->T, part, part_cap, st),
                        st, "mfma gate/up", err, err_len);
@@ -289,8 +339,16 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     q.w0 = w->sh_down; q.w1 = nullptr;
     q.s0 = (const uint16_t*)w->sh_s_down; q.s1 = nullptr;
     q.in = hs; q.out = y_shared; q.N = s->d; q.K = s->F;
-    rc = pass(1, "down");
-    if (rc) return rc;
+    if (skinny_q) {
+        rc = pass(1, "down");
+        if (rc) return rc;
+    }
+    if (use_dq) {
+        rc = hip_check(launch_dq_ffn(1, dqf, gs, w->w_down, nullptr, w->s_down, nullptr, h, y_perm, perm, tiles,
+                                     s->d, s->F, s->k, dq_mt, s->T * s->k, st),
+                       st, "dq down", err, err_len);
+        if (rc) return rc;
+    }
     if (use_mfma) {
         rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, s->E, s->T * s->k, part, part_cap, st),
                        st, "mfma down", err, err_len);
@@ -320,6 +378,9 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     sw.w_gate = w->sh_gate;
     sw.w_up = w->sh_up;
     sw.w_down = w->sh_down;
+    sw.s_gate = w->sh_s_gate;
+    sw.s_up = w->sh_s_up;
+    sw.s_down = w->sh_s_down;
     int32_t* sid = reinterpret_cast<int32_t*>(ws + L.sid);
     rc = hip_check(launch_identity_group(sid, sid + 1, sid + 3, s->T, st), st, "shared group", err, err_len);
     if (rc) return rc;
@@ -334,7 +395,7 @@ int check_weights(const moe_shape* s, const moe_weights* w, char* err, size_t er
     NEED_PTR(w->w_gate, "w_gate");
     NEED_PTR(w->w_up, "w_up");
     NEED_PTR(w->w_down, "w_down");
-    const bool int4 = s->wt == MOE_INT4_G128 || s->wt == MOE_INT4_G128_TILED;
+    const bool int4 = s->wt >= MOE_INT4_G128;    // every quantised format carries scales
     if (int4) {
         NEED_PTR(w->s_gate, "s_gate");
         NEED_PTR(w->s_up, "s_up");
@@ -529,6 +590,20 @@ int moe_rmsnorm(const moe_shape* shape, const void* h, const float* gamma, float
     hipStream_t st = (hipStream_t)stream;
     return hip_check(launch_rmsnorm(shape->act, h, gamma, eps, out, shape->T, shape->d, st), st, "rmsnorm", err,
                      err_len);
+}
+
+int moe_topk_overlap(const moe_shape* shape, const int32_t* pred_idx, const int32_t* actual_idx, int32_t* hist,
+                     void* stream, char* err, size_t err_len) {
+    int rc = check_shape(shape, err, err_len);
+    if (rc) return rc;
+    NEED_PTR(hist, "hist");
+    if (shape->T > 0) {
+        NEED_PTR(pred_idx, "pred_idx");
+        NEED_PTR(actual_idx, "actual_idx");
+    }
+    hipStream_t st = (hipStream_t)stream;
+    return hip_check(launch_topk_overlap(pred_idx, actual_idx, hist, shape->T, shape->k, st), st, "topk overlap",
+                     err, err_len);
 }
 
 int moe_pack_int4_tiled(const void* src, void* dst, int64_t n_mats, int32_t N, int32_t K, void* stream, char* err,

@@ -146,4 +146,37 @@ hipError_t launch_identity_group(int32_t* counts, int32_t* offsets, int32_t* per
     return hipGetLastError();
 }
 
+// One-layer-ahead expert prediction, scored: for each token, how many of the
+// k experts a prediction chose (pred) the layer then chose (actual).  [P5]
+// "一只蜂鸟如何喂饱九头大象" §4.2: the router run one layer ahead picks the
+// experts to fetch early, and the share it gets right bounds the time spent
+// waiting for the rest.  hist[j] counts the tokens sharing exactly j experts.
+// Integer work in one block: per-block LDS counts, then one write per bin.
+__global__ __launch_bounds__(256) void topk_overlap_kernel(const int32_t* __restrict__ pred,
+                                                           const int32_t* __restrict__ actual,
+                                                           int32_t* __restrict__ hist, int T, int k) {
+    __shared__ int s_h[17];
+    const int tid = threadIdx.x;
+    if (tid <= k) s_h[tid] = 0;
+    __syncthreads();
+    for (int t = tid; t < T; t += 256) {
+        int n = 0;
+        for (int j = 0; j < k; ++j) {
+            const int e = pred[(size_t)t * k + j];
+            bool hit = false;
+            for (int m = 0; m < k; ++m) hit |= actual[(size_t)t * k + m] == e;
+            n += hit;
+        }
+        atomicAdd(&s_h[n], 1);
+    }
+    __syncthreads();
+    if (tid <= k) hist[tid] = s_h[tid];
+}
+
+hipError_t launch_topk_overlap(const int32_t* pred, const int32_t* actual, int32_t* hist, int T, int k,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(topk_overlap_kernel, dim3(1), dim3(256), 0, s, pred, actual, hist, T, k);
+    return hipGetLastError();
+}
+
 }  // namespace moe

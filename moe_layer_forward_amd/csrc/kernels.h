@@ -34,6 +34,9 @@ bool route_dispatch_small_supported(int T, int E, int k);
 hipError_t launch_route_dispatch_small(int act, const void* x, const float* wg, const float* b, float* logits,
                                        int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* perm,
                                        int32_t* inv, int T, int d, int E, int k, hipStream_t s);
+// tokens sharing j = 0..k experts between two top-k selections
+hipError_t launch_topk_overlap(const int32_t* pred, const int32_t* actual, int32_t* hist, int T, int k,
+                               hipStream_t s);
 // counts = {n}, offsets = {0, n}, perm = 0..n-1: the shared expert as a group
 hipError_t launch_identity_group(int32_t* counts, int32_t* offsets, int32_t* perm, int n, hipStream_t s);
 hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, int max_rows,
@@ -59,6 +62,17 @@ bool skinny_supported(int K, int N, int in_rows);
 hipError_t launch_skinny(int mode, const void* w0, const void* w1, const void* in, int in_rows, void* out,
                          const int32_t* counts, const int32_t* offsets, const int32_t* perm, int N, int K,
                          int topk, int E, int lo, int cap, hipStream_t s);
+// Quantised expert weights on the matrix cores (ffn_dq.hip): int4 (fmt 0,
+// group size gs = 64 or 128, fp16 scales), MXFP4 (1) or MXFP8 (2) with E8M0
+// scales per 32; 128-row tiles of the experts with more than tau rows.
+int dq_max_tiles(int T, int k, int E);
+int dq_plan_ints(int T, int k, int E);
+bool dq_supported(int K, int N);
+hipError_t launch_dq_plan(const int32_t* counts, const int32_t* offsets, int E, int tau, int32_t* tiles,
+                          int max_mt, hipStream_t s);
+hipError_t launch_dq_ffn(int mode, int fmt, int gs, const void* w0, const void* w1, const void* s0, const void* s1,
+                         const void* in, void* out, const int32_t* perm, const int32_t* tiles, int N, int K, int topk,
+                         int max_mt, int in_rows, hipStream_t s);
 int mfma_bm();
 int mfma_max_tiles(int T, int k, int E);
 int mfma_max_small(int E);

@@ -12,7 +12,8 @@ import moe_layer_forward_amd as moe
 from helpers import np_store
 
 DEV = "cuda"
-TOL = {"f32": 1e-5, "bf16": 2e-2, "int4": 2e-2, "int4_tiled": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "int4": 2e-2, "int4_tiled": 2e-2, "int4g64": 2e-2, "mxfp4": 2e-2,
+       "mxfp8": 2e-2}
 FLIP_MARGIN = 1e-5
 
 

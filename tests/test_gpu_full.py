@@ -123,6 +123,23 @@ def test_fine_int4_decode_full(orc, wt):
     _check_layer(orc, cfg, d, y, counts, idx, sel=np.arange(0, cfg.T, 2, dtype=np.int32))
 
 
+@pytest.mark.parametrize("name", ["fine_int4_prefill", "fine_mxfp4_prefill", "mixtral_mxfp8_prefill"])
+def test_quantised_prefill_full(orc, name):
+    """Prefill-sized groups of quantised experts on the dequantising grouped
+    GEMM: the fine-grained int4-g128 layer (E=256, top-8, shared expert) and
+    MXFP4 experts at T=4096, and the Mixtral-shaped layer with MXFP8 experts.
+    Routing on every token; outputs on 16 seeded random tokens (the oracle
+    decodes every weight element per use, so larger samples take minutes)."""
+    cfg = C[name]
+    say(f"full {name} T={cfg.T}")
+    d = device_inputs(cfg)
+    y, counts, idx = run_layer(cfg, d)
+    c = counts.cpu().numpy()
+    say(f"  active experts {(c > 0).sum()}, largest group {c.max()}")
+    sel = np.sort(np.random.default_rng(7).choice(cfg.T, 16, replace=False)).astype(np.int32)
+    _check_layer(orc, cfg, d, y, counts, idx, sel=sel)
+
+
 def test_stack4_full_teacher_forced(orc):
     """Four pre-norm layers with residual; each layer checked on the GPU's own
     input (teacher forcing), plus the per-layer usage histogram."""
@@ -131,6 +148,7 @@ def test_stack4_full_teacher_forced(orc):
     inp = moe_inputs.generate(cfg, seed=0, device=DEV)
     h = inp["x"].to(DEV)
     hist = []
+    pred = None          # layer l+1's experts predicted from layer l's input
     for l in range(cfg.layers):
         L = inp["layers"][l]
         d = {"w_router": L["w_router"].to(DEV), "b_router": None}
@@ -147,6 +165,27 @@ def test_stack4_full_teacher_forced(orc):
         y, counts, idx = run_layer(cfg, d, residual=h)
         say(f"  layer {l}")
         _check_layer(orc, cfg, d, y, counts, idx, residual=h)
+        if pred is not None:
+            # one-layer-ahead prediction scored on the GPU, against the
+            # oracle's count on the same selections (bit-exact)
+            ov = torch.empty(cfg.k + 1, dtype=torch.int32, device=DEV)
+            moe.moe_topk_overlap(shape_of(cfg), pred, idx, ov)
+            torch.cuda.synchronize()
+            ref = orc.topk_overlap(pred.cpu().numpy(), idx.cpu().numpy())
+            assert ov.cpu().numpy().tolist() == ref.tolist()
+            hit = float((np.arange(cfg.k + 1) * ref).sum()) / (cfg.T * cfg.k)
+            say(f"  layer {l}: experts predicted one layer ahead {hit:.3f}")
+        if l + 1 < cfg.layers:
+            # the next layer's router on this layer's normed input (PILOT), a
+            # moe_route call whose selection is checked bit-exact on its logits
+            wr_next = inp["layers"][l + 1]["w_router"]
+            lg = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=DEV)
+            pred = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=DEV)
+            pw = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=DEV)
+            moe.moe_route(shape_of(cfg), n_, wr_next.to(DEV), None, lg, pred, pw)
+            torch.cuda.synchronize()
+            oi, _ = orc.topk(lg.cpu().numpy().astype(np.float64), cfg.k)
+            assert np.array_equal(pred.cpu().numpy(), oi)
         c = counts.cpu().numpy()
         hist += [(l, e, int(c[e])) for e in range(cfg.E) if c[e] > 0]
         h = y.clone()

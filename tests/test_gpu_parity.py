@@ -114,6 +114,23 @@ SMALL = {
     "f32_shared": moe_inputs.MoEConfig(
         "f32_shared", T=20, d=128, E=4, k=2, F=96, act="f32", wt="f32", model="s_f32_sh",
         n_shared=1),
+    # quantised groups above the skinny kernels' range on the dequantising
+    # grouped GEMM (128-row tiles): int4-g128 groups of ~150 rows and a shared
+    # expert over all 300 tokens; every group of int4-g64, MXFP4 and MXFP8
+    # (ragged last N-tiles: F = 320 gate/up columns in 64-wide tiles, d = 448
+    # down rows in 128-wide tiles)
+    "int4_dq": moe_inputs.MoEConfig(
+        "int4_dq", T=300, d=1024, E=4, k=2, F=1024, act="bf16", wt="int4",
+        model="s_int4_dq", n_shared=1, w_std=0.05),
+    "int4g64_dq": moe_inputs.MoEConfig(
+        "int4g64_dq", T=40, d=448, E=6, k=2, F=320, act="bf16", wt="int4g64",
+        model="s_int4g64", n_shared=1, w_std=0.05),
+    "mxfp4_dq": moe_inputs.MoEConfig(
+        "mxfp4_dq", T=200, d=512, E=4, k=2, F=640, act="bf16", wt="mxfp4",
+        model="s_mxfp4", n_shared=1, w_std=0.05),
+    "mxfp8_dq": moe_inputs.MoEConfig(
+        "mxfp8_dq", T=130, d=448, E=5, k=3, F=320, act="bf16", wt="mxfp8",
+        model="s_mxfp8", w_std=0.05),
     # int4 with K above 8192 on the GEMV (gate/up K = 9216, not a multiple of
     # 1024 times at most 8); down K = 512 also on the GEMV
     "int4_wide_gemv": moe_inputs.MoEConfig(
@@ -263,8 +280,8 @@ def _steps(cfg, d, tau=0):
 @pytest.mark.parametrize("tau", [0, -1])
 def test_steps_parity(orc, name, tau):
     cfg = SMALL[name]
-    if tau == -1 and cfg.wt != "bf16":
-        pytest.skip("tau only selects kernels for bf16 weights")
+    if tau == -1 and cfg.wt not in ("bf16", "int4"):
+        pytest.skip("tau only selects kernels for bf16 and int4-g128 weights")
     say(f"steps parity {name} tau={tau}")
     d = device_inputs(cfg)
     g = _steps(cfg, d, tau)
@@ -359,7 +376,9 @@ def test_layer_int4_tiled(orc, name):
     err = tokenwise_rel(np_f64(y), y_f)
     say(f"  max rel {err.max():.3g} flips {flips}")
     assert err.max() < TOL["int4_tiled"]
-    y_rm, _, idx_rm = run_layer(cfg, d)
+    # row-major codes on the same skinny int4 kernels (tau < 0: no group on the
+    # dequantising GEMM): the same arithmetic, bit for bit
+    y_rm, _, idx_rm = run_layer(cfg, d, tau=-1)
     assert torch.equal(idx, idx_rm) and torch.equal(y, y_rm)
 
 
