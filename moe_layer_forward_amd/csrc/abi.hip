@@ -158,12 +158,13 @@ bool shared_as_group(const moe_shape* s) {
 }
 
 int effective_tau(const moe_shape* s);
+int tile_mode(const moe_shape* s);
 
 // Partial tiles the split tail round of the 256-row MFMA kernel may use: at
 // most one per block of its grid, which never exceeds max_mt x N-tiles.
 int part_cap(const moe_shape* s) {
     const int tau = effective_tau(s);
-    if (tau < 0 || s->T <= tau) return 0;
+    if (tau < 0 || s->T <= tau || tile_mode(s) == MFMA_TILES_SMALL) return 0;
     const long nn = std::max(mfma_ntiles_n(0, s->F), mfma_ntiles_n(1, s->d));
     const long c = (long)mfma_max_tiles(s->T, s->k, s->E) * nn;
     return (int)std::min<long>(c, mfma_part_cap());
@@ -203,12 +204,36 @@ bool skinny_applies(const moe_shape* s) {
 int effective_tau(const moe_shape* s) {
     if (s->wt != MOE_BF16) return -1;      // fp32 and int4: GEMV for every group
     if (s->tau < 0) return -1;
+    if (s->tau > 0) return s->tau;
     // default: the skinny kernel up to 64 rows where K gives its items eight
     // or more steps (d, F >= 4096); with shorter rows its per-item reduction
     // and extra token reads cost more than the 64-row MFMA tiles above one
     // token tile
-    if (s->tau == 0) return (skinny_applies(s) && s->d >= 4096 && s->F >= 4096) ? kSkinnyMaxRows : kDefaultTau;
-    return s->tau;
+    const int td = (skinny_applies(s) && s->d >= 4096 && s->F >= 4096) ? kSkinnyMaxRows : kDefaultTau;
+    // when the mean group is at least twice that, groups at or below it are
+    // rare: every group goes to the MFMA tiles (a 64-row tile streams its
+    // expert's weights once, as one GEMV or skinny pass does), and the GEMV
+    // and skinny launches, which would find no work, are left out
+    return (long)s->T * s->k >= 2L * td * s->E ? 0 : td;
+}
+
+// Tile lists of the bf16 grouped GEMM.  Explicit tau: groups up to 128 rows
+// on 64-row tiles, larger ones on 256-row tiles.  Default tau: with T <= 128
+// no group exceeds 128 rows, so only the 64-row list can be filled; with a
+// mean group of at most 64 rows and experts of at most 32 MiB, every group
+// goes to 64-row tiles (a rare group above 128 rows streams its weights once
+// per 64 rows, a few microseconds at that size, against ~20 us for the
+// 256-row launches that would otherwise run empty); with a mean group of at
+// least 512 rows every group goes to 256-row tiles (a rare small group pays
+// padded MFMA work, not extra weight reads).
+int tile_mode(const moe_shape* s) {
+    if (s->tau != 0) return MFMA_TILES_BOTH;
+    const long tk = (long)s->T * s->k;
+    const double expert_bytes = 3.0 * s->F * s->d * 2.0;
+    if (s->T <= 2 * kMfmaSmallRows) return MFMA_TILES_SMALL;
+    if (tk <= (long)kMfmaSmallRows * s->E && expert_bytes <= 32.0 * (1 << 20)) return MFMA_TILES_SMALL;
+    if (tk >= 512L * s->E) return MFMA_TILES_BIG;
+    return MFMA_TILES_BOTH;
 }
 
 // Workspace regions one expert-FFN pass writes: h, the MFMA tile plan and
@@ -233,10 +258,13 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     float* part = b.part_cap ? b.part : nullptr;
     const int part_cap = b.part_cap;
     const int max_mt = mfma_max_tiles(s->T, s->k, s->E);
+    const int tmode = tile_mode(s);
     // quantised groups above dqt rows: the dequantising grouped GEMM
     const int dqf = dq_format(s), dqt = dq_tau(s);
     const bool use_dq = dqf >= 0 && dqt >= 0 && s->T > dqt;
-    const bool skinny_q = dqt != 0;          // some groups stay on the GEMV / skinny int4 kernels
+    // some groups stay on the streaming kernels (GEMV, skinny bf16 or int4):
+    // not when the dequantising GEMM or the MFMA tiles take every group
+    const bool skinny_q = dqt != 0 && !(use_mfma && tau == 0);
     const int dq_mt = dq_max_tiles(s->T, s->k, s->E);
     const int gs = s->wt == MOE_INT4_G64 ? 64 : 128;
     const int max_rows_gemv = use_mfma ? tau : s->T;   // a group holds at most T rows
@@ -244,7 +272,7 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
 
     if (s->T == 0) return MOE_OK;
     if (use_mfma) {
-        rc = hip_check(launch_mfma_plan(counts, offsets, s->E, tau, tiles, max_mt, st), st,
+        rc = hip_check(launch_mfma_plan(counts, offsets, s->T, s->k, s->E, tau, tmode, tiles, max_mt, st), st,
                        "mfma plan", err, err_len);
         if (rc) return rc;
     }
@@ -328,7 +356,8 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
         if (rc) return rc;
     }
     if (use_mfma) {
-        rc = hip_check(launch_mfma_ffn(0, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, max_mt, s->E, s->T, part, part_cap, st),
+        rc = hip_check(launch_mfma_ffn(0, tmode, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, s->T, max_mt,
+                                       s->E, s->T, part, part_cap, st),
                        st, "mfma gate/up", err, err_len);
         if (rc) return rc;
     }
@@ -350,7 +379,8 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
         if (rc) return rc;
     }
     if (use_mfma) {
-        rc = hip_check(launch_mfma_ffn(1, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, max_mt, s->E, s->T * s->k, part, part_cap, st),
+        rc = hip_check(launch_mfma_ffn(1, tmode, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, s->T,
+                                       max_mt, s->E, s->T * s->k, part, part_cap, st),
                        st, "mfma down", err, err_len);
         if (rc) return rc;
     }

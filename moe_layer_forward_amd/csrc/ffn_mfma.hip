@@ -67,17 +67,19 @@ constexpr int MF_STAGE = MF_BM * MF_BK;   // elements of one operand stage
 constexpr int MF_GM = 8;          // M-tiles per scheduling group
 constexpr uint32_t MF_OOB = 0x80000000u;   // beyond any buffer: the range check yields 0
 
-constexpr int MS_BM = 64;          // rows of a small M-tile
+constexpr int MS_BM = kMfmaSmallRows;   // rows of a small M-tile
 
 int mfma_bm() { return MF_BM; }
 // Big tiles: experts with more than 128 rows, in 256-row tiles (the tail
 // tile's weights stream with the expert's other tiles).  Small tiles: experts
 // with at most 128 rows, as one or two 64-row tiles, so a ~50-row group does
-// not pay for a 256-row tile.
+// not pay for a 256-row tile.  With one list only (MFMA_TILES_SMALL / _BIG)
+// every group goes to that list; the bounds hold for any split of T*k rows
+// over E experts.
 int mfma_max_tiles(int T, int k, int E) { return (T * k + MF_BM - 1) / MF_BM + E; }
-int mfma_max_small(int E) { return 2 * E; }
+int mfma_max_small(int T, int k, int E) { return (T * k + MS_BM - 1) / MS_BM + E; }
 int mfma_plan_ints(int T, int k, int E) {
-    return 3 * mfma_max_tiles(T, k, E) + 1 + 3 * mfma_max_small(E) + 1;
+    return 3 * mfma_max_tiles(T, k, E) + 1 + 3 * mfma_max_small(T, k, E) + 1;
 }
 int mfma_part_cap() { return 256; }
 int mfma_ntiles_n(int mode, int N) { return mode == 0 ? (N + 127) / 128 : (N + MF_BN - 1) / MF_BN; }
@@ -88,15 +90,16 @@ int mfma_ntiles_n(int mode, int N) { return mode == 0 ? (N + 127) / 128 : (N + M
 // the small tiles with max_st entries.
 __global__ __launch_bounds__(256) void mfma_plan_kernel(const int32_t* __restrict__ counts,
                                                        const int32_t* __restrict__ offsets, int E,
-                                                       int tau, int32_t* __restrict__ tiles,
+                                                       int tau, int tile_mode, int32_t* __restrict__ tiles,
                                                        int max_mt, int max_st) {
     __shared__ int s[2][2][256];
     const int tid = threadIdx.x;
     int c = 0, nb = 0, ns = 0, rem = 0;
     if (tid < E) {
         c = counts[tid];
-        if (c > tau) {
-            if (c > 2 * MS_BM) {
+        if (c > tau && c > 0) {
+            const bool big = tile_mode == MFMA_TILES_BIG || (tile_mode == MFMA_TILES_BOTH && c > 2 * MS_BM);
+            if (big) {
                 nb = (c + MF_BM - 1) / MF_BM;
             } else {
                 rem = c;
@@ -916,15 +919,18 @@ __global__ __launch_bounds__(256, 2) void mfma_small_kernel(MfmaArgs a) {
     }
 }
 
-hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int E, int tau,
-                            int32_t* tiles, int max_mt, hipStream_t s) {
-    hipLaunchKernelGGL(mfma_plan_kernel, dim3(1), dim3(256), 0, s, counts, offsets, E, tau, tiles,
-                       max_mt, mfma_max_small(E));
+hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int T, int k, int E, int tau,
+                            int tile_mode, int32_t* tiles, int max_mt, hipStream_t s) {
+    if (E > 256 || tile_mode < MFMA_TILES_BOTH || tile_mode > MFMA_TILES_BIG) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mfma_plan_kernel, dim3(1), dim3(256), 0, s, counts, offsets, E, tau, tile_mode, tiles,
+                       max_mt, mfma_max_small(T, k, E));
     return hipGetLastError();
 }
 
-hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void* in, void* out,
-                           const int32_t* perm, const int32_t* tiles, int N, int K, int topk,
+// T_tokens: the T of the layer (with k and E it sizes the small-tile list
+// exactly as launch_mfma_plan did).
+hipError_t launch_mfma_ffn(int mode, int tile_mode, const void* w0, const void* w1, const void* in, void* out,
+                           const int32_t* perm, const int32_t* tiles, int N, int K, int topk, int T_tokens,
                            int max_mt, int E, int in_rows, float* part, int part_cap, hipStream_t s) {
     MfmaArgs a;
     a.w0 = reinterpret_cast<const uint16_t*>(w0);
@@ -937,35 +943,39 @@ hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void*
     a.K = K;
     a.topk = topk;
     a.max_mt = max_mt;
-    a.max_st = mfma_max_small(E);
+    a.max_st = mfma_max_small(T_tokens, topk, E);
     a.in_rows = in_rows;
     a.part = part;
     a.part_cap = part ? part_cap : 0;
     const int n_cu = cu_count();
     const int nN = mfma_ntiles_n(mode, N);
-    // big tiles: one 512-thread block per CU
-    const int slots = max_mt * nN;
-    const int grid = slots < n_cu ? slots : n_cu;
-    // copies from the compute phase need whole K pairs and at least two of them
-    const bool fast = K % (2 * MF_BK) == 0 && K >= 4 * MF_BK;
-    if (mode == 0) {
-        if (fast) hipLaunchKernelGGL((mfma_ffn_kernel<0, true>), dim3(grid), dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((mfma_ffn_kernel<0, false>), dim3(grid), dim3(512), 0, s, a);
-    } else {
-        if (fast) hipLaunchKernelGGL((mfma_ffn_kernel<1, true>), dim3(grid), dim3(512), 0, s, a);
-        else hipLaunchKernelGGL((mfma_ffn_kernel<1, false>), dim3(grid), dim3(512), 0, s, a);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.part_cap > 0) {
-        // sums of the split tail tiles (blocks without such a tile exit at once)
-        if (mode == 0)
-            hipLaunchKernelGGL(mfma_tail_reduce<0>, dim3(MF_BM * 128 / 1024, grid), dim3(256), 0, s, a, grid);
-        else
-            hipLaunchKernelGGL(mfma_tail_reduce<1>, dim3(MF_BM * MF_BN / 1024, grid), dim3(256), 0, s, a, grid);
+    hipError_t e = hipSuccess;
+    if (tile_mode != MFMA_TILES_SMALL) {
+        // big tiles: one 512-thread block per CU
+        const int slots = max_mt * nN;
+        const int grid = slots < n_cu ? slots : n_cu;
+        // copies from the compute phase need whole K pairs and at least two of them
+        const bool fast = K % (2 * MF_BK) == 0 && K >= 4 * MF_BK;
+        if (mode == 0) {
+            if (fast) hipLaunchKernelGGL((mfma_ffn_kernel<0, true>), dim3(grid), dim3(512), 0, s, a);
+            else hipLaunchKernelGGL((mfma_ffn_kernel<0, false>), dim3(grid), dim3(512), 0, s, a);
+        } else {
+            if (fast) hipLaunchKernelGGL((mfma_ffn_kernel<1, true>), dim3(grid), dim3(512), 0, s, a);
+            else hipLaunchKernelGGL((mfma_ffn_kernel<1, false>), dim3(grid), dim3(512), 0, s, a);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (a.part_cap > 0) {
+            // sums of the split tail tiles (blocks without such a tile exit at once)
+            if (mode == 0)
+                hipLaunchKernelGGL(mfma_tail_reduce<0>, dim3(MF_BM * 128 / 1024, grid), dim3(256), 0, s, a, grid);
+            else
+                hipLaunchKernelGGL(mfma_tail_reduce<1>, dim3(MF_BM * MF_BN / 1024, grid), dim3(256), 0, s, a, grid);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
+    if (tile_mode == MFMA_TILES_BIG) return e;
     // small tiles: two blocks per CU
     const int sslots = a.max_st * nN;
     const int sgrid = sslots < 2 * n_cu ? sslots : 2 * n_cu;

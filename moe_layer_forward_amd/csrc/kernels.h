@@ -75,13 +75,19 @@ hipError_t launch_dq_ffn(int mode, int fmt, int gs, const void* w0, const void* 
                          int max_mt, int in_rows, hipStream_t s);
 int mfma_bm();
 int mfma_max_tiles(int T, int k, int E);
-int mfma_max_small(int E);
+int mfma_max_small(int T, int k, int E);
 int mfma_plan_ints(int T, int k, int E);
 int mfma_ntiles_n(int mode, int N);
-hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int E, int tau,
-                            int32_t* tiles, int max_mt, hipStream_t s);
-hipError_t launch_mfma_ffn(int mode, const void* w0, const void* w1, const void* in, void* out,
-                           const int32_t* perm, const int32_t* tiles, int N, int K, int topk,
+// Tile lists of the bf16 grouped GEMM: BOTH puts groups of at most 128 rows
+// on 64-row tiles and larger ones on 256-row tiles; SMALL puts every group on
+// 64-row tiles and BIG every group on 256-row tiles, and the launch then
+// leaves out the kernel whose list is empty.
+enum { MFMA_TILES_BOTH = 0, MFMA_TILES_SMALL = 1, MFMA_TILES_BIG = 2 };
+constexpr int kMfmaSmallRows = 64;
+hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int T, int k, int E, int tau,
+                            int tile_mode, int32_t* tiles, int max_mt, hipStream_t s);
+hipError_t launch_mfma_ffn(int mode, int tile_mode, const void* w0, const void* w1, const void* in, void* out,
+                           const int32_t* perm, const int32_t* tiles, int N, int K, int topk, int T_tokens,
                            int max_mt, int E, int in_rows, float* part, int part_cap, hipStream_t s);
 // partial tiles (256 x 256 fp32 each) the split tail round may use
 int mfma_part_cap();

@@ -496,6 +496,63 @@ def test_mfma_tile_boundaries(orc, name):
         assert err < TOL["bf16"]
 
 
+# Default tile lists by the mean group T*k/E (bf16 weights, tau = 0):
+# at most 64 rows (and small experts) -> every group on 64-row tiles, a group
+# above 128 rows as several of them; at least 512 rows -> every group on
+# 256-row tiles, small groups as ragged ones; a mean group of twice the
+# streaming range or more also sends groups of a few rows to the tiles.
+SINGLE_LIST = {
+    "small_only": moe_inputs.MoEConfig(
+        "small_only", T=256, d=256, E=16, k=4, F=384, act="bf16", wt="bf16",
+        model="s_small_only", w_std=0.05),
+    "big_only": moe_inputs.MoEConfig(
+        "big_only", T=1024, d=320, E=4, k=2, F=384, act="bf16", wt="bf16",
+        model="s_big_only", w_std=0.05),
+}
+
+
+@pytest.mark.parametrize("name", list(SINGLE_LIST))
+def test_single_tile_list(orc, name):
+    """Layer parity where the default picks one tile list.  64-row list:
+    natural routing (groups of ~64 rows), then one expert taking every token
+    of batches of 129, 200 and 256 tokens (three or four 64-row tiles of one
+    expert).  256-row list: natural routing (~512 rows per expert), then a
+    negative bias that leaves one expert fewer and fewer rows (a group below
+    128 rows in one ragged 256-row tile)."""
+    cfg = SINGLE_LIST[name]
+    say(f"single tile list {name}")
+    d = device_inputs(cfg)
+    W, S = oracle_weights(d)
+    wr = np_store(d["w_router"])
+    cases = [(cfg.T, np.zeros(cfg.E, np.float32))]
+    if name == "small_only":
+        for TT in (129, 200, 256):
+            b = np.zeros(cfg.E, np.float32)
+            b[0] = 1e3
+            cases.append((TT, b))
+    else:
+        for lo in (1.5, 3.0, 5.0):
+            b = np.zeros(cfg.E, np.float32)
+            b[3] = -lo
+            cases.append((cfg.T, b))
+    seen = []
+    for TT, b in cases:
+        xs = d["x"][:TT].contiguous()
+        y, c, i = run_layer(cfg, dict(d, b_router=torch.from_numpy(b).to(DEV)), x=xs)
+        gi = i.cpu().numpy()
+        y_f, _, _, _ = orc.layer_forward(np_store(xs), "bf16", "bf16", cfg.k, wr, b, W, forced_idx=gi)
+        err = tokenwise_rel(np_f64(y), y_f).max()
+        cl = c.cpu().tolist()
+        seen.append(cl)
+        say(f"  T={TT} counts {cl} max rel {err:.3g}")
+        assert err < TOL["bf16"]
+        assert np.array_equal(np.asarray(cl), np.bincount(gi.ravel(), minlength=cfg.E))
+    if name == "small_only":
+        assert max(seen[0]) <= 128 and [c[0] for c in seen[1:]] == [129, 200, 256]
+    else:
+        assert min(seen[0]) > 128 and min(c[3] for c in seen[1:]) < 128
+
+
 def test_rmsnorm_parity(orc):
     say("rmsnorm")
     for act in ("f32", "bf16"):
