@@ -267,6 +267,7 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     const bool skinny_q = dqt != 0 && !(use_mfma && tau == 0);
     const int dq_mt = dq_max_tiles(s->T, s->k, s->E);
     const int gs = s->wt == MOE_INT4_G64 ? 64 : 128;
+    const bool dq_staged = use_dq && dq_staged_ok(dqf, gs, s->d) && dq_staged_ok(dqf, gs, s->F);
     const int max_rows_gemv = use_mfma ? tau : s->T;   // a group holds at most T rows
     int rc;
 
@@ -277,7 +278,8 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
         if (rc) return rc;
     }
     if (use_dq) {
-        rc = hip_check(launch_dq_plan(counts, offsets, s->E, dqt, tiles, dq_mt, st), st, "dq plan", err, err_len);
+        rc = hip_check(launch_dq_plan(counts, offsets, s->E, dqt, dq_staged, tiles, dq_mt, st), st, "dq plan", err,
+                       err_len);
         if (rc) return rc;
     }
     // routed experts (g) and the shared expert (q: one expert over all T rows)
@@ -350,8 +352,8 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
         if (rc) return rc;
     }
     if (use_dq) {
-        rc = hip_check(launch_dq_ffn(0, dqf, gs, w->w_gate, w->w_up, w->s_gate, w->s_up, x, h, perm, tiles, s->F,
-                                     s->d, s->k, dq_mt, s->T, st),
+        rc = hip_check(launch_dq_ffn(0, dqf, gs, dq_staged, w->w_gate, w->w_up, w->s_gate, w->s_up, x, h, perm, tiles,
+                                     s->F, s->d, s->k, dq_mt, s->T, st),
                        st, "dq gate/up", err, err_len);
         if (rc) return rc;
     }
@@ -373,8 +375,8 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
         if (rc) return rc;
     }
     if (use_dq) {
-        rc = hip_check(launch_dq_ffn(1, dqf, gs, w->w_down, nullptr, w->s_down, nullptr, h, y_perm, perm, tiles,
-                                     s->d, s->F, s->k, dq_mt, s->T * s->k, st),
+        rc = hip_check(launch_dq_ffn(1, dqf, gs, dq_staged, w->w_down, nullptr, w->s_down, nullptr, h, y_perm, perm,
+                                     tiles, s->d, s->F, s->k, dq_mt, s->T * s->k, st),
                        st, "dq down", err, err_len);
         if (rc) return rc;
     }

@@ -43,6 +43,7 @@
 #include "common.h"
 #include "devinfo.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -289,17 +290,425 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_ffn_kernel(DqArgs a) {
     }
 }
 
-// One 256-thread block: per expert with more than tau rows, ceil(rows/128)
-// tiles; an exclusive scan over the experts places them.
+// ---------------------------------------------------------------------------
+// The staged kernel (K a multiple of 512; int4-g128: of 1024), for shapes
+// where the matrix cores, not the weight stream, bound the pass.
+//
+// Tile: 64 token rows x 256 weight rows (gate/up: 128 gate rows and the 128
+// matching up rows), one 512-thread block per CU, eight waves: wave (wm, wn)
+// multiplies tokens 32 wm .. +31 with weight rows 64 wn .. +63 (gate/up: the
+// gate rows 32 wn .. +31 and the same up rows, so g and u of one (token, f)
+// meet in one lane).  The product is weight-major (weights as the MFMA A
+// operand): a lane's accumulators hold four consecutive output columns of
+// one token, so h and y_perm go out as 8- and 16-byte stores.
+//
+// K runs in stages of 128 (three stages in LDS, one block barrier each):
+// token rows (gathered through perm for gate/up), weight codes and, every few
+// stages, a window of 16 scale bytes per weight row all arrive by
+// global -> LDS copies, issued two stages ahead and counted by hand (vmcnt),
+// whole 128-byte lines for tokens and fp8 codes, half lines for 4-bit codes.
+// The copy stream runs on across the block's tasks: the next task's 64
+// dispatch entries come in by one more copy at the start of a task, so the
+// switch to the next task needs no load the compiler would wait for.
+// LDS rows are XOR-swizzled on their 16-byte chunks so that the fragment
+// reads of 16 consecutive rows hit distinct bank groups.  Within a stage,
+// lane half h of every MFMA covers K 64b + 32h .. +31 of sub-stage b, so a
+// lane's 4-bit codes of a sub-stage are one 16-byte read and one 32-element
+// scale group (MX) or one 64/128-element group (int4) applies to all of them.
+constexpr int DT_BM = 64;
+constexpr int DT_BN = 256;
+constexpr int DT_BK = 128;
+constexpr int DT_NS = 3;            // K stages in LDS
+constexpr int DT_SW = 3;            // scale windows in LDS
+constexpr int DT_GM = 8;            // M-tiles per scheduling group
+constexpr int DT_THREADS = 512;
+constexpr int DT_TOK = DT_BM * DT_BK * 2;        // token bytes of a stage (16 KB)
+
+enum { DT_I4G128 = 0, DT_I4G64 = 1, DT_FP4 = 2, DT_FP8 = 3 };
+
+template <int F>
+struct DtFmt {
+    static constexpr int WROW = F == DT_FP8 ? 128 : 64;         // code bytes per row and stage
+    static constexpr int STAGE = DT_TOK + DT_BN * WROW;
+    static constexpr int WIN = F == DT_I4G128 ? 8 : 4;          // stages per 16-byte scale window
+    static constexpr int WCOPY = DT_BN * WROW / 1024 / 8;       // weight copies per wave and stage
+};
+
+// One dword copy per lane (lane l lands at lds_addr + 4 l).
+__device__ __forceinline__ void dma4(const int32x4_t& desc, uint32_t off, uint32_t lds_addr) {
+    int32x4_t d;
+    d.x = __builtin_amdgcn_readfirstlane(desc.x);
+    d.y = __builtin_amdgcn_readfirstlane(desc.y);
+    d.z = __builtin_amdgcn_readfirstlane(desc.z);
+    d.w = __builtin_amdgcn_readfirstlane(desc.w);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(off), "s"(d), "{m0}"(m0)
+                 : "memory");
+}
+
+// 8 bf16 of MFMA step s (K elements 8s .. 8s+7 of the lane's 32) from the
+// lane's codes c (4-bit: 16 bytes; fp8: 32 bytes in c, c2), times the scale
+template <int F>
+__device__ __forceinline__ dq_bf16x8_t dt_widen(const dq_u32x4_t& c, const dq_u32x4_t& c2, int s, float scale) {
+    uint32_t p[4];
+    if constexpr (F == DT_I4G128 || F == DT_I4G64) {
+        // offset-binary nibbles u = q + 8 in bytes (each byte to fp32 is one
+        // v_cvt_f32_ubyteN), then (u - 8) * scale in fp32 (exact: 4 x 11
+        // significant bits) rounded once to bf16
+        const uint32_t t = c[s] ^ 0x88888888u;
+        const uint32_t lo = t & 0x0F0F0F0Fu, hi = (t >> 4) & 0x0F0F0F0Fu;
+        const float off = -8.0f * scale;
+        p[0] = pack_bf16x2(fmaf((float)((lo >> 0) & 0xffu), scale, off),
+                           fmaf((float)((hi >> 0) & 0xffu), scale, off));
+        p[1] = pack_bf16x2(fmaf((float)((lo >> 8) & 0xffu), scale, off),
+                           fmaf((float)((hi >> 8) & 0xffu), scale, off));
+        p[2] = pack_bf16x2(fmaf((float)((lo >> 16) & 0xffu), scale, off),
+                           fmaf((float)((hi >> 16) & 0xffu), scale, off));
+        p[3] = pack_bf16x2(fmaf((float)((lo >> 24) & 0xffu), scale, off),
+                           fmaf((float)((hi >> 24) & 0xffu), scale, off));
+    } else if constexpr (F == DT_FP4) {
+        const uint32_t w = c[s];
+        p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+        p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+        p[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+        p[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    } else {
+        const uint32_t w0 = s < 2 ? c[2 * s] : c2[2 * s - 4];
+        const uint32_t w1 = s < 2 ? c[2 * s + 1] : c2[2 * s - 3];
+        p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false));
+        p[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true));
+        p[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false));
+        p[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true));
+    }
+    dq_u32x4_t r = {p[0], p[1], p[2], p[3]};
+    return __builtin_bit_cast(dq_bf16x8_t, r);
+}
+
+typedef const __attribute__((address_space(4))) int32_t* dt_cptr;
+
+// wait until at most n (one of the group sizes a wave issues) of this wave's
+// copies are outstanding
+template <int B>
+__device__ __forceinline__ void dt_wait(int n) {
+    if (n == 0) wait_vmcnt<0>();
+    else if (n <= B) wait_vmcnt<B>();
+    else if (n == B + 1) wait_vmcnt<B + 1>();
+    else wait_vmcnt<B + 2>();
+}
+
+template <int MODE, int F>
+__global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
+    using Fm = DtFmt<F>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[DT_NS * Fm::STAGE + DT_SW * DT_BN * 16 + 256];
+    uint8_t* const sc_base = smem + DT_NS * Fm::STAGE;
+    const int32_t* const s_perm = reinterpret_cast<const int32_t*>(sc_base + DT_SW * DT_BN * 16);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int K = a.K, N = a.N;
+    const dt_cptr tl = (dt_cptr)a.tiles;
+    const int max_mt = a.max_mt;
+    const int n_mt = tl[3 * max_mt];
+    const int nN = MODE == 0 ? (N + 127) / 128 : (N + DT_BN - 1) / DT_BN;
+    const int total = n_mt * nN;
+    const int nblk = gridDim.x;
+    // blocks are dealt round-robin to the 8 XCDs: consecutive slots share one
+    const int per = nblk / 8;
+    const int slot = (nblk % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
+    if (slot >= total) return;
+    const int NKB = K / DT_BK;
+    const uint32_t row_bytes = (uint32_t)K * 2u;
+    const uint32_t crow = F == DT_FP8 ? (uint32_t)K : (uint32_t)K / 2u;          // code bytes per row
+    const uint32_t srow = F == DT_I4G128 ? (uint32_t)K / 64u : (uint32_t)K / 32u;  // scale bytes per row
+    const int32x4_t RA = make_desc(a.in, (uint32_t)a.in_rows * row_bytes);
+    const int32x4_t RP = make_desc(a.perm, MODE == 0 ? (uint32_t)a.in_rows * (uint32_t)a.topk * 4u : 0u);
+    constexpr int BASE = 2 + Fm::WCOPY;           // token + code copies of a stage, per wave
+
+    // task t -> (M-tile, N-tile): groups of DT_GM M-tiles x all N-tiles, M fastest
+    auto task_tile = [&](int t, int& mt, int& nt) {
+        const int grp = t / (DT_GM * nN);
+        const int gm0 = grp * DT_GM;
+        const int gsz = min(DT_GM, n_mt - gm0);
+        const int rem = t - grp * DT_GM * nN;
+        mt = gm0 + rem % gsz;
+        nt = rem / gsz;
+    };
+
+    // ---- copy side: the task whose stages are being issued, and the byte
+    // offsets of this lane's two token rows (OOB past the group): copy i of
+    // this wave fills tile rows 8 wave + 4 i .. +3, lane l row + l/16, its
+    // physical chunk l%16 holding logical chunk (l%16) ^ (row%16)
+    int i_e = 0, i_nt = 0, i_rows = 0, i_p0 = 0;
+    uint32_t i_aoff[2];
+    auto set_task = [&](int t) {
+        int mt;
+        task_tile(t, mt, i_nt);
+        i_e = tl[mt];
+        i_p0 = tl[max_mt + mt];
+        i_rows = tl[2 * max_mt + mt];
+    };
+    auto set_rows = [&](const int (&src)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 8 * wave + 4 * i + (lane >> 4);
+            const uint32_t lc = (uint32_t)((lane & 15) ^ (r & 15));
+            i_aoff[i] = r < i_rows ? (uint32_t)src[i] * row_bytes + lc * 16u : DQ_OOB;
+        }
+    };
+
+    // The copies of one stage (kb of the copy-side task) into stage slot st.
+    // A scale window (when kb opens one: waves 0-3, window slot ws) and the
+    // next task's dispatch entries (when asked: wave 0, gate/up) go out at
+    // once; the token and code copies (BASE per wave) are only prepared here
+    // -- descriptor, offset, LDS address -- and go out one by one between the
+    // MFMAs of the current stage (fire).  Returns this wave's number of copies.
+    constexpr int RPC = 1024 / Fm::WROW;           // weight rows per copy
+    constexpr int CPR = Fm::WROW / 16;             // 16-byte chunks per weight row
+    int32x4_t c_desc[BASE];
+    uint32_t c_off[BASE], c_lds[BASE];
+    auto issue = [&](int kb, int st, int ws, int perm_p0) -> int {
+        int n = 0;
+        const size_t eo = (size_t)i_e * N;
+        if (kb % Fm::WIN == 0 && wave < 4) {
+            const bool up = MODE == 0 && wave >= 2;
+            const int gr = MODE == 0 ? i_nt * 128 + 64 * (wave & 1) + lane : i_nt * DT_BN + 64 * wave + lane;
+            const uint32_t wb = F == DT_I4G128 ? (uint32_t)kb * 2u : (uint32_t)kb * 4u;
+            const int32x4_t RS = make_desc((up ? a.s1 : a.s0) + eo * srow, (uint32_t)N * srow);
+            dma16(RS, gr < N ? (uint32_t)gr * srow + wb : DQ_OOB, lds_addr(sc_base + ws * DT_BN * 16 + wave * 1024));
+            ++n;
+        }
+        if (MODE == 0 && perm_p0 >= 0 && wave == 0) {
+            dma4(RP, (uint32_t)(perm_p0 + lane) * 4u, lds_addr(s_perm));
+            ++n;
+        }
+        uint8_t* stage = smem + st * Fm::STAGE;
+        const uint32_t kbyte = (uint32_t)kb * DT_BK * 2u;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            c_desc[i] = RA;
+            c_off[i] = i_aoff[i] == DQ_OOB ? DQ_OOB : i_aoff[i] + kbyte;
+            c_lds[i] = lds_addr(stage + (8 * wave + 4 * i) * 256);
+        }
+        const int32x4_t RW0 = make_desc(a.w0 + eo * crow, (uint32_t)N * crow);
+        const int32x4_t RW1 = make_desc((MODE == 0 ? a.w1 : a.w0) + eo * crow, (uint32_t)N * crow);
+#pragma unroll
+        for (int i = 0; i < Fm::WCOPY; ++i) {
+            const int ci = Fm::WCOPY * wave + i;       // copy index: LDS rows RPC ci ..
+            const int lr = RPC * ci + lane / CPR;
+            const int pc = lane % CPR;
+            const int lc = F == DT_FP8 ? (pc ^ ((lr >> 1) & 7)) : (pc ^ ((lr >> 2) & 3));
+            const bool up = MODE == 0 && RPC * ci >= 128;
+            const int gr = MODE == 0 ? i_nt * 128 + (lr & 127) : i_nt * DT_BN + lr;
+            c_desc[2 + i] = up ? RW1 : RW0;
+            c_off[2 + i] = gr < N ? (uint32_t)gr * crow + (uint32_t)kb * Fm::WROW + (uint32_t)lc * 16u : DQ_OOB;
+            c_lds[2 + i] = lds_addr(stage + DT_TOK + RPC * ci * Fm::WROW);
+        }
+        return n + BASE;
+    };
+    bool c_live = false;                           // a prepared group is waiting to go out
+    auto fire = [&](int i) __attribute__((always_inline)) {
+        if (c_live) dma16(c_desc[i], c_off[i], c_lds[i]);
+    };
+
+    // ---- the first task: its dispatch entries by ordinary loads (no copy in flight yet)
+    set_task(slot);
+    {
+        int src[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 8 * wave + 4 * i + (lane >> 4);
+            src[i] = MODE == 0 ? (r < i_rows ? a.perm[i_p0 + r] / a.topk : 0) : i_p0 + r;
+        }
+        set_rows(src);
+    }
+    // copy-side cursor (task, stage index, LDS slots); windows counted in stream order
+    int i_task = slot, i_kb = 0, i_st = 0, i_win = 0;
+    bool i_live = true, i_fresh = false;
+    // issue the stage at the cursor and advance it.  The first stage of a
+    // later task reads that task's dispatch entries from s_perm: they were
+    // copied with the group of the previous task's first stage, at least two
+    // steps (one wait and one barrier) earlier.
+    auto issue_next = [&](int perm_p0) -> int {
+        c_live = i_live;
+        if (!i_live) return 0;
+        if (i_fresh) {
+            set_task(i_task);
+            int src[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 8 * wave + 4 * i + (lane >> 4);
+                src[i] = MODE == 0 ? s_perm[r] / a.topk : i_p0 + r;
+            }
+            set_rows(src);
+            i_fresh = false;
+        }
+        const int ws = i_win % DT_SW;
+        if (i_kb % Fm::WIN == 0) ++i_win;
+        const int n = issue(i_kb, i_st, ws, perm_p0);
+        i_st = i_st + 1 == DT_NS ? 0 : i_st + 1;
+        if (++i_kb == NKB) {
+            i_kb = 0;
+            i_task += nblk;
+            i_live = i_task < total;
+            i_fresh = i_live;
+        }
+        return n;
+    };
+
+    // ---- compute side
+    const int tr = 32 * wm + r32;                   // the lane's token row in the tile
+    int lr[2];                                      // the lane's weight rows (LDS) of its fragments
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) lr[ni] = MODE == 0 ? ni * 128 + 32 * wn + r32 : 64 * wn + 32 * ni + r32;
+    dq_floatx16 acc[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[ni][v] = 0.f;
+
+    // One stage: 8 steps (sub-stage b = j/4, MFMA step j%4) of two MFMAs;
+    // step j's token fragment is read at step j-1, a sub-stage's codes and
+    // scales two steps before it starts, and after step j's MFMAs copy j of
+    // the next group goes out (scheduling fences keep it there).
+    auto compute = [&](int st, int ws, int kb) __attribute__((always_inline)) {
+        const uint8_t* tok = smem + st * Fm::STAGE;
+        const uint8_t* wts = tok + DT_TOK;
+        const uint8_t* sc = sc_base + ws * DT_BN * 16;
+        dq_u32x4_t c[2][2], c2[2][2];
+        float scale[2][2];
+        auto read_codes = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni) {
+                const int R = lr[ni];
+                if constexpr (F == DT_FP8) {
+                    const int l0 = 4 * b + 2 * h;
+                    c[b][ni] = *reinterpret_cast<const dq_u32x4_t*>(wts + R * 128 + ((l0 ^ ((R >> 1) & 7)) << 4));
+                    c2[b][ni] = *reinterpret_cast<const dq_u32x4_t*>(wts + R * 128 + (((l0 + 1) ^ ((R >> 1) & 7)) << 4));
+                } else {
+                    c[b][ni] = *reinterpret_cast<const dq_u32x4_t*>(wts + R * 64 + (((2 * b + h) ^ ((R >> 2) & 3)) << 4));
+                    c2[b][ni] = c[b][ni];
+                }
+                const uint8_t* sr = sc + R * 16;
+                if constexpr (F == DT_I4G128)
+                    scale[b][ni] = f16_to_f32(*reinterpret_cast<const uint16_t*>(sr + (kb % 8) * 2));
+                else if constexpr (F == DT_I4G64)
+                    scale[b][ni] = f16_to_f32(*reinterpret_cast<const uint16_t*>(sr + ((kb % 4) * 2 + b) * 2));
+                else
+                    scale[b][ni] = dq_e8m0(sr[(kb % 4) * 4 + 2 * b + h]);
+            }
+        };
+        auto read_tok = [&](int j) __attribute__((always_inline)) {
+            const int b = j >> 2, s4 = j & 3;
+            return *reinterpret_cast<const dq_bf16x8_t*>(tok + tr * 256 + (((8 * b + 4 * h + s4) ^ (tr & 15)) << 4));
+        };
+        read_codes(0);
+        dq_bf16x8_t tf[2];
+        tf[0] = read_tok(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int b = j >> 2, s4 = j & 3;
+            if (j + 1 < 8) tf[(j + 1) & 1] = read_tok(j + 1);
+            if (j == 2) read_codes(1);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt_widen<F>(c[b][ni], c2[b][ni], s4, scale[b][ni]),
+                                                                  tf[j & 1], acc[ni], 0, 0, 0);
+            if (j < BASE) {
+                __builtin_amdgcn_sched_barrier(0);
+                fire(j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    // lane l, accumulator element v of fragment ni: token tr, weight row
+    // 8 (v/4) + 4 h + v%4 of the fragment (four consecutive outputs per v/4)
+    auto epilogue = [&](int t) {
+        int mt, nt;
+        task_tile(t, mt, nt);
+        const int p0 = tl[max_mt + mt], rows = tl[2 * max_mt + mt];
+        if (tr < rows) {
+            const size_t orow = (size_t)(p0 + tr) * N;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (MODE == 0) {
+                    const int f = nt * 128 + 32 * wn + 8 * q + 4 * h;
+                    if (f < N) {
+                        uint2 o;
+                        o.x = pack_bf16x2(silu(acc[0][4 * q]) * acc[1][4 * q], silu(acc[0][4 * q + 1]) * acc[1][4 * q + 1]);
+                        o.y = pack_bf16x2(silu(acc[0][4 * q + 2]) * acc[1][4 * q + 2],
+                                          silu(acc[0][4 * q + 3]) * acc[1][4 * q + 3]);
+                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow + f) = o;
+                    }
+                } else {
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni) {
+                        const int n = nt * DT_BN + 64 * wn + 32 * ni + 8 * q + 4 * h;
+                        if (n < N)
+                            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow + n) =
+                                make_float4(acc[ni][4 * q], acc[ni][4 * q + 1], acc[ni][4 * q + 2], acc[ni][4 * q + 3]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[ni][v] = 0.f;
+    };
+
+    // ---- the stream: stage g is issued at step g - 2 (the prologue issues
+    // stages 0 and 1).  Step g: this wave's copies of stage g have landed
+    // once at most the newest group (stage g + 1) is outstanding; the barrier
+    // then publishes stage g to every wave and tells that everyone is done
+    // with stage g - 1, whose slot receives stage g + 2.
+    issue_next(-1);
+#pragma unroll
+    for (int i = 0; i < BASE; ++i) fire(i);
+    int n_prev = issue_next(-1);
+#pragma unroll
+    for (int i = 0; i < BASE; ++i) fire(i);
+    int c_task = slot, c_kb = 0, c_st = 0, c_win = 0;
+    for (;;) {
+        dt_wait<BASE>(n_prev);
+        block_barrier();
+        // at a task's first stage: the next task's dispatch entries go out
+        // with this group and are read when the copy side reaches that task
+        int pp = -1;
+        if (MODE == 0 && c_kb == 0 && c_task + nblk < total) {
+            int mt, nt;
+            task_tile(c_task + nblk, mt, nt);
+            pp = tl[max_mt + mt];
+        }
+        n_prev = issue_next(pp);
+        if (c_kb % Fm::WIN == 0) ++c_win;
+        compute(c_st, (c_win - 1) % DT_SW, c_kb);
+        c_st = c_st + 1 == DT_NS ? 0 : c_st + 1;
+        if (++c_kb == NKB) {
+            epilogue(c_task);
+            c_kb = 0;
+            c_task += nblk;
+            if (c_task >= total) break;
+        }
+    }
+    // every copy has been waited for: the last wait saw no group outstanding
+}
+
+// One 256-thread block: per expert with more than tau rows, ceil(rows/bm)
+// tiles of bm rows; an exclusive scan over the experts places them.
 __global__ __launch_bounds__(256) void dq_plan_kernel(const int32_t* __restrict__ counts,
-                                                     const int32_t* __restrict__ offsets, int E, int tau,
+                                                     const int32_t* __restrict__ offsets, int E, int tau, int bm,
                                                      int32_t* __restrict__ tiles, int max_mt) {
     __shared__ int s[2][256];
     const int tid = threadIdx.x;
     int c = 0, nb = 0;
     if (tid < E) {
         c = counts[tid];
-        if (c > tau && c > 0) nb = (c + DQ_BM - 1) / DQ_BM;
+        if (c > tau && c > 0) nb = (c + bm - 1) / bm;
     }
     int cur = 0;
     s[0][tid] = nb;
@@ -316,8 +725,8 @@ __global__ __launch_bounds__(256) void dq_plan_kernel(const int32_t* __restrict_
         const int b = s[cur][tid] - nb;
         for (int i = 0; i < nb; ++i) {
             tiles[b + i] = tid;
-            tiles[max_mt + b + i] = o0 + i * DQ_BM;
-            tiles[2 * max_mt + b + i] = min(DQ_BM, c - i * DQ_BM);
+            tiles[max_mt + b + i] = o0 + i * bm;
+            tiles[2 * max_mt + b + i] = min(bm, c - i * bm);
         }
     }
     if (tid == 255) tiles[3 * max_mt] = s[cur][255];
@@ -325,7 +734,8 @@ __global__ __launch_bounds__(256) void dq_plan_kernel(const int32_t* __restrict_
 
 }  // namespace
 
-int dq_max_tiles(int T, int k, int E) { return (T * k + DQ_BM - 1) / DQ_BM + E; }
+// bounds for the smaller tile height, so one plan region serves both kernels
+int dq_max_tiles(int T, int k, int E) { return (T * k + DT_BM - 1) / DT_BM + E; }
 int dq_plan_ints(int T, int k, int E) { return 3 * dq_max_tiles(T, k, E) + 1; }
 
 bool dq_supported(int K, int N) {
@@ -333,18 +743,29 @@ bool dq_supported(int K, int N) {
     return K > 0 && K % DQ_PK == 0 && N > 0 && (size_t)N * (size_t)K < ((size_t)1 << 31);
 }
 
-hipError_t launch_dq_plan(const int32_t* counts, const int32_t* offsets, int E, int tau, int32_t* tiles,
-                          int max_mt, hipStream_t s) {
+// The staged kernel: whole 16-byte scale windows per row (K a multiple of
+// 512; int4-g128 of 1024) and at least four stages.
+bool dq_staged_ok(int fmt, int gs, int K) {
+    if (K < 512 || K % 512 != 0) return false;
+    return !(fmt == DQ_INT4 && gs == 128 && K % 1024 != 0);
+}
+
+int dq_tile_rows(bool staged) { return staged ? DT_BM : DQ_BM; }
+
+hipError_t launch_dq_plan(const int32_t* counts, const int32_t* offsets, int E, int tau, bool staged,
+                          int32_t* tiles, int max_mt, hipStream_t s) {
     if (E > 256) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(dq_plan_kernel, dim3(1), dim3(256), 0, s, counts, offsets, E, tau, tiles, max_mt);
+    hipLaunchKernelGGL(dq_plan_kernel, dim3(1), dim3(256), 0, s, counts, offsets, E, tau, dq_tile_rows(staged),
+                       tiles, max_mt);
     return hipGetLastError();
 }
 
-hipError_t launch_dq_ffn(int mode, int fmt, int gs, const void* w0, const void* w1, const void* s0, const void* s1,
-                         const void* in, void* out, const int32_t* perm, const int32_t* tiles, int N, int K, int topk,
-                         int max_mt, int in_rows, hipStream_t s) {
+hipError_t launch_dq_ffn(int mode, int fmt, int gs, bool staged, const void* w0, const void* w1, const void* s0,
+                         const void* s1, const void* in, void* out, const int32_t* perm, const int32_t* tiles, int N,
+                         int K, int topk, int max_mt, int in_rows, hipStream_t s) {
     if (!dq_supported(K, N) || (fmt == DQ_INT4 && (gs != 64 && gs != 128)) || fmt < 0 || fmt > 2)
         return hipErrorInvalidValue;
+    if (staged && (!dq_staged_ok(fmt, gs, K) || N % 4 != 0)) return hipErrorInvalidValue;
     DqArgs a;
     a.w0 = reinterpret_cast<const uint8_t*>(w0);
     a.w1 = reinterpret_cast<const uint8_t*>(w1);
@@ -360,6 +781,26 @@ hipError_t launch_dq_ffn(int mode, int fmt, int gs, const void* w0, const void* 
     a.max_mt = max_mt;
     a.in_rows = in_rows;
     a.gs = fmt == DQ_INT4 ? gs : 32;
+    if (staged) {
+        // one 512-thread block per CU over the (M-tile, N-tile) tasks
+        const int nN = mode == 0 ? (N + 127) / 128 : (N + DT_BN - 1) / DT_BN;
+        const long slots = (long)max_mt * nN;
+        const long cap = cu_count();
+        const int grid = (int)(slots < cap ? slots : cap);
+        const int f = fmt == DQ_MXFP4 ? DT_FP4 : fmt == DQ_MXFP8 ? DT_FP8 : (gs == 128 ? DT_I4G128 : DT_I4G64);
+#define DT_LAUNCH(M, F) hipLaunchKernelGGL((dq_tile_kernel<M, F>), dim3(grid), dim3(DT_THREADS), 0, s, a)
+#define DT_FMTS(M)                               \
+        switch (f) {                             \
+            case DT_I4G128: DT_LAUNCH(M, DT_I4G128); break; \
+            case DT_I4G64: DT_LAUNCH(M, DT_I4G64); break;   \
+            case DT_FP4: DT_LAUNCH(M, DT_FP4); break;       \
+            default: DT_LAUNCH(M, DT_FP8); break;           \
+        }
+        if (mode == 0) { DT_FMTS(0) } else { DT_FMTS(1) }
+#undef DT_FMTS
+#undef DT_LAUNCH
+        return hipGetLastError();
+    }
     const int nN = mode == 0 ? (N + 63) / 64 : (N + 127) / 128;
     const long slots = (long)max_mt * nN;
     const long cap = 2L * cu_count();

@@ -115,9 +115,11 @@ SMALL = {
         "f32_shared", T=20, d=128, E=4, k=2, F=96, act="f32", wt="f32", model="s_f32_sh",
         n_shared=1),
     # quantised groups above the skinny kernels' range on the dequantising
-    # grouped GEMM (128-row tiles): int4-g128 groups of ~150 rows and a shared
-    # expert over all 300 tokens; every group of int4-g64, MXFP4 and MXFP8
-    # (ragged last N-tiles: F = 320 gate/up columns in 64-wide tiles, d = 448
+    # grouped GEMM: int4-g128 groups of ~150 rows and a shared expert over all
+    # 300 tokens on the LDS-staged kernel (K = 1024, 64-row tiles); every group
+    # of int4-g64, MXFP4 and MXFP8 on the register-fed kernel (K of 448, 320,
+    # 512 or 640 is not a multiple of 512 in both passes; 128-row tiles,
+    # ragged last N-tiles: F = 320 gate/up columns in 64-wide tiles, d = 448
     # down rows in 128-wide tiles)
     "int4_dq": moe_inputs.MoEConfig(
         "int4_dq", T=300, d=1024, E=4, k=2, F=1024, act="bf16", wt="int4",
@@ -131,6 +133,19 @@ SMALL = {
     "mxfp8_dq": moe_inputs.MoEConfig(
         "mxfp8_dq", T=130, d=448, E=5, k=3, F=320, act="bf16", wt="mxfp8",
         model="s_mxfp8", w_std=0.05),
+    # the LDS-staged dequantising kernel (both K multiples of 512; int4-g128
+    # of 1024: int4_dq above): 64-row tiles, ragged last M-tiles, K = 512 (the
+    # fewest stages it takes) and, for MXFP8, more tasks than blocks so the
+    # copy stream runs from one task into the next
+    "int4g64_staged": moe_inputs.MoEConfig(
+        "int4g64_staged", T=160, d=512, E=4, k=2, F=1024, act="bf16", wt="int4g64",
+        model="s_i4g64_st", n_shared=1, w_std=0.05),
+    "mxfp4_staged": moe_inputs.MoEConfig(
+        "mxfp4_staged", T=200, d=1024, E=6, k=2, F=512, act="bf16", wt="mxfp4",
+        model="s_mxfp4_st", n_shared=1, w_std=0.05),
+    "mxfp8_staged": moe_inputs.MoEConfig(
+        "mxfp8_staged", T=1024, d=512, E=4, k=2, F=2048, act="bf16", wt="mxfp8",
+        model="s_mxfp8_st", w_std=0.05),
     # int4 with K above 8192 on the GEMV (gate/up K = 9216, not a multiple of
     # 1024 times at most 8); down K = 512 also on the GEMV
     "int4_wide_gemv": moe_inputs.MoEConfig(
