@@ -291,47 +291,55 @@ __global__ __launch_bounds__(DQ_THREADS, 2) void dq_ffn_kernel(DqArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// The staged kernel (K a multiple of 512; int4-g128: of 1024), for shapes
-// where the matrix cores, not the weight stream, bound the pass.
+// The staged kernel, for shapes where the matrix cores, not the weight
+// stream, bound the pass.
 //
-// Tile: 64 token rows x 256 weight rows (gate/up: 128 gate rows and the 128
-// matching up rows), one 512-thread block per CU, eight waves: wave (wm, wn)
-// multiplies tokens 32 wm .. +31 with weight rows 64 wn .. +63 (gate/up: the
-// gate rows 32 wn .. +31 and the same up rows, so g and u of one (token, f)
-// meet in one lane).  The product is weight-major (weights as the MFMA A
-// operand): a lane's accumulators hold four consecutive output columns of
-// one token, so h and y_perm go out as 8- and 16-byte stores.
+// Tile: 64 token rows x 512 weight rows (gate/up: 256 gate rows and the 256
+// matching up rows), one 512-thread block per CU.  Wave w owns 64 weight
+// rows -- gate/up: gate and up rows 32 w .. +31, so g and u of one (token, f)
+// meet in one lane; down: rows 64 w .. +63 -- against all 64 tokens: 2 x 2
+// fragments of v_mfma_f32_32x32x16_bf16, so each weight element is widened
+// by one wave and feeds two MFMAs.  The product is weight-major (weights as
+// the MFMA A operand): a lane's accumulators hold four consecutive output
+// columns of one token, so h and y_perm go out as 8- and 16-byte stores.
 //
-// K runs in stages of 128 (three stages in LDS, one block barrier each):
-// token rows (gathered through perm for gate/up), weight codes and, every few
-// stages, a window of 16 scale bytes per weight row all arrive by
-// global -> LDS copies, issued two stages ahead and counted by hand (vmcnt),
-// whole 128-byte lines for tokens and fp8 codes, half lines for 4-bit codes.
-// The copy stream runs on across the block's tasks: the next task's 64
-// dispatch entries come in by one more copy at the start of a task, so the
-// switch to the next task needs no load the compiler would wait for.
-// LDS rows are XOR-swizzled on their 16-byte chunks so that the fragment
-// reads of 16 consecutive rows hit distinct bank groups.  Within a stage,
-// lane half h of every MFMA covers K 64b + 32h .. +31 of sub-stage b, so a
-// lane's 4-bit codes of a sub-stage are one 16-byte read and one 32-element
-// scale group (MX) or one 64/128-element group (int4) applies to all of them.
+// K runs in stages (128 K for 4-bit codes, 64 K for fp8: 64 code bytes per
+// weight row either way), three stages in LDS, one block barrier each.
+// Token rows (gathered through perm for gate/up), weight codes and, every few
+// stages, an 8-byte window of scales per weight row arrive by global -> LDS
+// copies issued two stages ahead and counted by hand (vmcnt).  The token and
+// code copies of a stage go out one by one between the MFMAs of the stage
+// before; their offsets are worked out once per task.  The copy stream runs
+// on across the block's tasks: the next task's 64 dispatch entries come in
+// by one more copy at the start of a task, so the switch to the next task
+// needs no load the compiler would wait for.  LDS rows are XOR-swizzled on
+// their 16-byte chunks so that the fragment reads of 16 consecutive rows hit
+// distinct bank groups.  Within a 64-K sub-stage, lane half h of every MFMA
+// covers K 32h .. +31 (step s: 32h + 8s .. +7) of both operands, so a lane's
+// codes of a sub-stage are one 16-byte (4-bit) or 32-byte (fp8) read and one
+// scale group covers all of them.
 constexpr int DT_BM = 64;
-constexpr int DT_BN = 256;
-constexpr int DT_BK = 128;
+constexpr int DT_BN = 512;
 constexpr int DT_NS = 3;            // K stages in LDS
 constexpr int DT_SW = 3;            // scale windows in LDS
 constexpr int DT_GM = 8;            // M-tiles per scheduling group
 constexpr int DT_THREADS = 512;
-constexpr int DT_TOK = DT_BM * DT_BK * 2;        // token bytes of a stage (16 KB)
+constexpr int DT_WST = DT_BN * 64;  // code bytes of a stage (32 KB)
 
 enum { DT_I4G128 = 0, DT_I4G64 = 1, DT_FP4 = 2, DT_FP8 = 3 };
 
 template <int F>
 struct DtFmt {
-    static constexpr int WROW = F == DT_FP8 ? 128 : 64;         // code bytes per row and stage
-    static constexpr int STAGE = DT_TOK + DT_BN * WROW;
-    static constexpr int WIN = F == DT_I4G128 ? 8 : 4;          // stages per 16-byte scale window
-    static constexpr int WCOPY = DT_BN * WROW / 1024 / 8;       // weight copies per wave and stage
+    static constexpr int KS = F == DT_FP8 ? 64 : 128;          // K per stage
+    static constexpr int SUB = KS / 64;                        // 64-K sub-stages
+    static constexpr int TROW = KS * 2;                        // token bytes per row and stage
+    static constexpr int TOK = DT_BM * TROW;                   // token bytes of a stage
+    static constexpr int STAGE = TOK + DT_WST;
+    static constexpr int TCOPY = TOK / 1024 / 8;               // token copies per wave and stage
+    static constexpr int BASE = TCOPY + DT_WST / 1024 / 8;     // token + code copies per wave and stage
+    // scale bytes per weight row and stage; stages per 8-byte window
+    static constexpr int SPB = F == DT_I4G128 ? 2 : F == DT_I4G64 ? 4 : F == DT_FP4 ? 4 : 2;
+    static constexpr int WIN = 8 / SPB;
 };
 
 // One dword copy per lane (lane l lands at lds_addr + 4 l).
@@ -348,6 +356,18 @@ __device__ __forceinline__ void dma4(const int32x4_t& desc, uint32_t off, uint32
                  : "memory");
 }
 
+// Byte B of x as fp32 in one instruction (v_cvt_f32_ubyteN: there is no
+// builtin, and from shifts and masks the compiler emits an extract first).
+template <int B>
+__device__ __forceinline__ float dt_ubyte(uint32_t x) {
+    float r;
+    if constexpr (B == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
+    else if constexpr (B == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
+    else if constexpr (B == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
 // 8 bf16 of MFMA step s (K elements 8s .. 8s+7 of the lane's 32) from the
 // lane's codes c (4-bit: 16 bytes; fp8: 32 bytes in c, c2), times the scale
 template <int F>
@@ -360,14 +380,10 @@ __device__ __forceinline__ dq_bf16x8_t dt_widen(const dq_u32x4_t& c, const dq_u3
         const uint32_t t = c[s] ^ 0x88888888u;
         const uint32_t lo = t & 0x0F0F0F0Fu, hi = (t >> 4) & 0x0F0F0F0Fu;
         const float off = -8.0f * scale;
-        p[0] = pack_bf16x2(fmaf((float)((lo >> 0) & 0xffu), scale, off),
-                           fmaf((float)((hi >> 0) & 0xffu), scale, off));
-        p[1] = pack_bf16x2(fmaf((float)((lo >> 8) & 0xffu), scale, off),
-                           fmaf((float)((hi >> 8) & 0xffu), scale, off));
-        p[2] = pack_bf16x2(fmaf((float)((lo >> 16) & 0xffu), scale, off),
-                           fmaf((float)((hi >> 16) & 0xffu), scale, off));
-        p[3] = pack_bf16x2(fmaf((float)((lo >> 24) & 0xffu), scale, off),
-                           fmaf((float)((hi >> 24) & 0xffu), scale, off));
+        p[0] = pack_bf16x2(fmaf(dt_ubyte<0>(lo), scale, off), fmaf(dt_ubyte<0>(hi), scale, off));
+        p[1] = pack_bf16x2(fmaf(dt_ubyte<1>(lo), scale, off), fmaf(dt_ubyte<1>(hi), scale, off));
+        p[2] = pack_bf16x2(fmaf(dt_ubyte<2>(lo), scale, off), fmaf(dt_ubyte<2>(hi), scale, off));
+        p[3] = pack_bf16x2(fmaf(dt_ubyte<3>(lo), scale, off), fmaf(dt_ubyte<3>(hi), scale, off));
     } else if constexpr (F == DT_FP4) {
         const uint32_t w = c[s];
         p[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
@@ -388,45 +404,46 @@ __device__ __forceinline__ dq_bf16x8_t dt_widen(const dq_u32x4_t& c, const dq_u3
 
 typedef const __attribute__((address_space(4))) int32_t* dt_cptr;
 
-// wait until at most n (one of the group sizes a wave issues) of this wave's
-// copies are outstanding
+// wait until at most n (0 or one of the group sizes a wave issues: B, B + 1
+// with the perm copy, B + 2 with a scale window, B + 3 with both) of this
+// wave's copies are outstanding
 template <int B>
 __device__ __forceinline__ void dt_wait(int n) {
     if (n == 0) wait_vmcnt<0>();
     else if (n <= B) wait_vmcnt<B>();
     else if (n == B + 1) wait_vmcnt<B + 1>();
-    else wait_vmcnt<B + 2>();
+    else if (n == B + 2) wait_vmcnt<B + 2>();
+    else wait_vmcnt<B + 3>();
 }
 
 template <int MODE, int F>
 __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
     using Fm = DtFmt<F>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[DT_NS * Fm::STAGE + DT_SW * DT_BN * 16 + 256];
+    constexpr int BASE = Fm::BASE;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[DT_NS * Fm::STAGE + DT_SW * DT_BN * 8 + 256];
     uint8_t* const sc_base = smem + DT_NS * Fm::STAGE;
-    const int32_t* const s_perm = reinterpret_cast<const int32_t*>(sc_base + DT_SW * DT_BN * 16);
+    const int32_t* const s_perm = reinterpret_cast<const int32_t*>(sc_base + DT_SW * DT_BN * 8);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1, wn = wave >> 1;
     const int h = lane >> 5, r32 = lane & 31;
     const int K = a.K, N = a.N;
     const dt_cptr tl = (dt_cptr)a.tiles;
     const int max_mt = a.max_mt;
     const int n_mt = tl[3 * max_mt];
-    const int nN = MODE == 0 ? (N + 127) / 128 : (N + DT_BN - 1) / DT_BN;
+    const int nN = MODE == 0 ? (N + DT_BN / 2 - 1) / (DT_BN / 2) : (N + DT_BN - 1) / DT_BN;
     const int total = n_mt * nN;
     const int nblk = gridDim.x;
     // blocks are dealt round-robin to the 8 XCDs: consecutive slots share one
     const int per = nblk / 8;
     const int slot = (nblk % 8 == 0) ? (blockIdx.x % 8) * per + blockIdx.x / 8 : blockIdx.x;
     if (slot >= total) return;
-    const int NKB = K / DT_BK;
+    const int NKB = K / Fm::KS;
     const uint32_t row_bytes = (uint32_t)K * 2u;
     const uint32_t crow = F == DT_FP8 ? (uint32_t)K : (uint32_t)K / 2u;          // code bytes per row
     const uint32_t srow = F == DT_I4G128 ? (uint32_t)K / 64u : (uint32_t)K / 32u;  // scale bytes per row
     const int32x4_t RA = make_desc(a.in, (uint32_t)a.in_rows * row_bytes);
     const int32x4_t RP = make_desc(a.perm, MODE == 0 ? (uint32_t)a.in_rows * (uint32_t)a.topk * 4u : 0u);
-    constexpr int BASE = 2 + Fm::WCOPY;           // token + code copies of a stage, per wave
 
     // task t -> (M-tile, N-tile): groups of DT_GM M-tiles x all N-tiles, M fastest
     auto task_tile = [&](int t, int& mt, int& nt) {
@@ -438,78 +455,93 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
         nt = rem / gsz;
     };
 
-    // ---- copy side: the task whose stages are being issued, and the byte
-    // offsets of this lane's two token rows (OOB past the group): copy i of
-    // this wave fills tile rows 8 wave + 4 i .. +3, lane l row + l/16, its
-    // physical chunk l%16 holding logical chunk (l%16) ^ (row%16)
+    // ---- copy side.  Wave w copies token rows 8 w .. +7, weight rows
+    // 64 w .. +63 (LDS order: gate/up 256 gate rows, then 256 up rows) and
+    // their scale windows.  Per task: the lane parts of every copy offset.
+    // Token copy i: 4-bit stages, rows 8w + 4i + l/16 with 16 chunks per row;
+    // fp8 stages, rows 8w + l/8 with 8 chunks.  Code copy i: rows
+    // 64w + 16i + l/4, 4 chunks.  Scale copy i: rows 64w + 32i + l/2, dword l%2.
     int i_e = 0, i_nt = 0, i_rows = 0, i_p0 = 0;
-    uint32_t i_aoff[2];
+    uint32_t t_off[Fm::TCOPY], w_off[4], s_off[2];
+    int32x4_t RW[2], RS[2];                    // gate (or down) and up codes and scales of the task's expert
+    auto token_row = [&](int i) {
+        return F == DT_FP8 ? 8 * wave + (lane >> 3) : 8 * wave + 4 * i + (lane >> 4);
+    };
     auto set_task = [&](int t) {
         int mt;
         task_tile(t, mt, i_nt);
         i_e = tl[mt];
         i_p0 = tl[max_mt + mt];
         i_rows = tl[2 * max_mt + mt];
-    };
-    auto set_rows = [&](const int (&src)[2]) {
+        const size_t eo = (size_t)i_e * N;
+        RW[0] = make_desc(a.w0 + eo * crow, (uint32_t)N * crow);
+        RW[1] = make_desc((MODE == 0 ? a.w1 : a.w0) + eo * crow, (uint32_t)N * crow);
+        RS[0] = make_desc(a.s0 + eo * srow, (uint32_t)N * srow);
+        RS[1] = make_desc((MODE == 0 ? a.s1 : a.s0) + eo * srow, (uint32_t)N * srow);
+        const int half = MODE == 0 ? DT_BN / 2 : DT_BN;     // weight rows of one matrix in a tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int lr = 64 * wave + 16 * i + (lane >> 2);
+            const int lc = (lane & 3) ^ ((lr >> 2) & 3);
+            const int gr = i_nt * half + (MODE == 0 ? (lr & (DT_BN / 2 - 1)) : lr);
+            w_off[i] = gr < N ? (uint32_t)gr * crow + (uint32_t)lc * 16u : DQ_OOB;
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int r = 8 * wave + 4 * i + (lane >> 4);
-            const uint32_t lc = (uint32_t)((lane & 15) ^ (r & 15));
-            i_aoff[i] = r < i_rows ? (uint32_t)src[i] * row_bytes + lc * 16u : DQ_OOB;
+            const int lr = 64 * wave + 32 * i + (lane >> 1);
+            const int gr = i_nt * half + (MODE == 0 ? (lr & (DT_BN / 2 - 1)) : lr);
+            s_off[i] = gr < N ? (uint32_t)gr * srow + (uint32_t)(lane & 1) * 4u : DQ_OOB;
+        }
+    };
+    auto set_rows = [&](const int (&src)[Fm::TCOPY]) {
+#pragma unroll
+        for (int i = 0; i < Fm::TCOPY; ++i) {
+            const int r = token_row(i);
+            const int lc = F == DT_FP8 ? ((lane & 7) ^ ((r >> 1) & 7)) : ((lane & 15) ^ (r & 15));
+            t_off[i] = r < i_rows ? (uint32_t)src[i] * row_bytes + (uint32_t)lc * 16u : DQ_OOB;
         }
     };
 
-    // The copies of one stage (kb of the copy-side task) into stage slot st.
-    // A scale window (when kb opens one: waves 0-3, window slot ws) and the
-    // next task's dispatch entries (when asked: wave 0, gate/up) go out at
-    // once; the token and code copies (BASE per wave) are only prepared here
-    // -- descriptor, offset, LDS address -- and go out one by one between the
-    // MFMAs of the current stage (fire).  Returns this wave's number of copies.
-    constexpr int RPC = 1024 / Fm::WROW;           // weight rows per copy
-    constexpr int CPR = Fm::WROW / 16;             // 16-byte chunks per weight row
+    // The copies of stage kb of the copy-side task into stage slot st.  A
+    // scale window (when kb opens one, into window slot ws) and the next
+    // task's dispatch entries (when asked: wave 0, gate/up) go out at once;
+    // the token and code copies are only prepared and go out one by one
+    // between the MFMAs of the current stage (fire).  Returns this wave's
+    // number of copies.
     int32x4_t c_desc[BASE];
     uint32_t c_off[BASE], c_lds[BASE];
+    bool c_live = false;                           // a prepared group is waiting to go out
     auto issue = [&](int kb, int st, int ws, int perm_p0) -> int {
         int n = 0;
-        const size_t eo = (size_t)i_e * N;
-        if (kb % Fm::WIN == 0 && wave < 4) {
-            const bool up = MODE == 0 && wave >= 2;
-            const int gr = MODE == 0 ? i_nt * 128 + 64 * (wave & 1) + lane : i_nt * DT_BN + 64 * wave + lane;
-            const uint32_t wb = F == DT_I4G128 ? (uint32_t)kb * 2u : (uint32_t)kb * 4u;
-            const int32x4_t RS = make_desc((up ? a.s1 : a.s0) + eo * srow, (uint32_t)N * srow);
-            dma16(RS, gr < N ? (uint32_t)gr * srow + wb : DQ_OOB, lds_addr(sc_base + ws * DT_BN * 16 + wave * 1024));
-            ++n;
+        if (kb % Fm::WIN == 0) {
+            const uint32_t wb = (uint32_t)kb * Fm::SPB;
+            const int m = MODE == 0 && wave >= 4 ? 1 : 0;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                dma4(RS[m], s_off[i] == DQ_OOB ? DQ_OOB : s_off[i] + wb,
+                     lds_addr(sc_base + ws * DT_BN * 8 + (64 * wave + 32 * i) * 8));
+            n += 2;
         }
         if (MODE == 0 && perm_p0 >= 0 && wave == 0) {
             dma4(RP, (uint32_t)(perm_p0 + lane) * 4u, lds_addr(s_perm));
             ++n;
         }
         uint8_t* stage = smem + st * Fm::STAGE;
-        const uint32_t kbyte = (uint32_t)kb * DT_BK * 2u;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < Fm::TCOPY; ++i) {
             c_desc[i] = RA;
-            c_off[i] = i_aoff[i] == DQ_OOB ? DQ_OOB : i_aoff[i] + kbyte;
-            c_lds[i] = lds_addr(stage + (8 * wave + 4 * i) * 256);
+            c_off[i] = t_off[i] == DQ_OOB ? DQ_OOB : t_off[i] + (uint32_t)kb * Fm::TROW;
+            c_lds[i] = lds_addr(stage + (8 * wave + (F == DT_FP8 ? 0 : 4 * i)) * Fm::TROW);
         }
-        const int32x4_t RW0 = make_desc(a.w0 + eo * crow, (uint32_t)N * crow);
-        const int32x4_t RW1 = make_desc((MODE == 0 ? a.w1 : a.w0) + eo * crow, (uint32_t)N * crow);
+        const int m = MODE == 0 && wave >= 4 ? 1 : 0;
 #pragma unroll
-        for (int i = 0; i < Fm::WCOPY; ++i) {
-            const int ci = Fm::WCOPY * wave + i;       // copy index: LDS rows RPC ci ..
-            const int lr = RPC * ci + lane / CPR;
-            const int pc = lane % CPR;
-            const int lc = F == DT_FP8 ? (pc ^ ((lr >> 1) & 7)) : (pc ^ ((lr >> 2) & 3));
-            const bool up = MODE == 0 && RPC * ci >= 128;
-            const int gr = MODE == 0 ? i_nt * 128 + (lr & 127) : i_nt * DT_BN + lr;
-            c_desc[2 + i] = up ? RW1 : RW0;
-            c_off[2 + i] = gr < N ? (uint32_t)gr * crow + (uint32_t)kb * Fm::WROW + (uint32_t)lc * 16u : DQ_OOB;
-            c_lds[2 + i] = lds_addr(stage + DT_TOK + RPC * ci * Fm::WROW);
+        for (int i = 0; i < 4; ++i) {
+            c_desc[Fm::TCOPY + i] = RW[m];
+            c_off[Fm::TCOPY + i] = w_off[i] == DQ_OOB ? DQ_OOB : w_off[i] + (uint32_t)kb * 64u;
+            c_lds[Fm::TCOPY + i] = lds_addr(stage + Fm::TOK + (64 * wave + 16 * i) * 64);
         }
         return n + BASE;
     };
-    bool c_live = false;                           // a prepared group is waiting to go out
     auto fire = [&](int i) __attribute__((always_inline)) {
         if (c_live) dma16(c_desc[i], c_off[i], c_lds[i]);
     };
@@ -517,10 +549,10 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
     // ---- the first task: its dispatch entries by ordinary loads (no copy in flight yet)
     set_task(slot);
     {
-        int src[2];
+        int src[Fm::TCOPY];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = 8 * wave + 4 * i + (lane >> 4);
+        for (int i = 0; i < Fm::TCOPY; ++i) {
+            const int r = token_row(i);
             src[i] = MODE == 0 ? (r < i_rows ? a.perm[i_p0 + r] / a.topk : 0) : i_p0 + r;
         }
         set_rows(src);
@@ -528,7 +560,7 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
     // copy-side cursor (task, stage index, LDS slots); windows counted in stream order
     int i_task = slot, i_kb = 0, i_st = 0, i_win = 0;
     bool i_live = true, i_fresh = false;
-    // issue the stage at the cursor and advance it.  The first stage of a
+    // prepare the stage at the cursor and advance it.  The first stage of a
     // later task reads that task's dispatch entries from s_perm: they were
     // copied with the group of the previous task's first stage, at least two
     // steps (one wait and one barrier) earlier.
@@ -537,10 +569,10 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
         if (!i_live) return 0;
         if (i_fresh) {
             set_task(i_task);
-            int src[2];
+            int src[Fm::TCOPY];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = 8 * wave + 4 * i + (lane >> 4);
+            for (int i = 0; i < Fm::TCOPY; ++i) {
+                const int r = token_row(i);
                 src[i] = MODE == 0 ? s_perm[r] / a.topk : i_p0 + r;
             }
             set_rows(src);
@@ -559,113 +591,144 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
         return n;
     };
 
-    // ---- compute side
-    const int tr = 32 * wm + r32;                   // the lane's token row in the tile
-    int lr[2];                                      // the lane's weight rows (LDS) of its fragments
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) lr[ni] = MODE == 0 ? ni * 128 + 32 * wn + r32 : 64 * wn + 32 * ni + r32;
-    dq_floatx16 acc[2];
+    // ---- compute side: the lane's weight rows (LDS) of its two fragments
+    int lr[2];
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
+        lr[ni] = MODE == 0 ? ni * (DT_BN / 2) + 32 * wave + r32 : 64 * wave + 32 * ni + r32;
+    dq_floatx16 acc[2][2];                          // [token fragment][weight fragment]
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[ni][v] = 0.f;
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[t][ni][v] = 0.f;
 
-    // One stage: 8 steps (sub-stage b = j/4, MFMA step j%4) of two MFMAs;
-    // step j's token fragment is read at step j-1, a sub-stage's codes and
-    // scales two steps before it starts, and after step j's MFMAs copy j of
-    // the next group goes out (scheduling fences keep it there).
+    // One stage: 4 SUB steps (sub-stage b = j/4, MFMA step j%4) of four
+    // MFMAs; step j's token fragments are read at step j-2, a sub-stage's
+    // codes and scales three steps before it starts, and the next group's
+    // copies go out between the steps (scheduling fences keep them there).
+    constexpr int STEPS = 4 * Fm::SUB;
     auto compute = [&](int st, int ws, int kb) __attribute__((always_inline)) {
         const uint8_t* tok = smem + st * Fm::STAGE;
-        const uint8_t* wts = tok + DT_TOK;
-        const uint8_t* sc = sc_base + ws * DT_BN * 16;
-        dq_u32x4_t c[2][2], c2[2][2];
-        float scale[2][2];
+        const uint8_t* wts = tok + Fm::TOK;
+        const uint8_t* sc = sc_base + ws * DT_BN * 8 + (kb % Fm::WIN) * Fm::SPB;
+        dq_u32x4_t c[Fm::SUB][2], c2[Fm::SUB][2];
+        float scale[Fm::SUB][2];
         auto read_codes = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni) {
                 const int R = lr[ni];
+                const uint8_t* wr = wts + R * 64;
+                const int sw = (R >> 2) & 3;
                 if constexpr (F == DT_FP8) {
-                    const int l0 = 4 * b + 2 * h;
-                    c[b][ni] = *reinterpret_cast<const dq_u32x4_t*>(wts + R * 128 + ((l0 ^ ((R >> 1) & 7)) << 4));
-                    c2[b][ni] = *reinterpret_cast<const dq_u32x4_t*>(wts + R * 128 + (((l0 + 1) ^ ((R >> 1) & 7)) << 4));
+                    c[b][ni] = *reinterpret_cast<const dq_u32x4_t*>(wr + (((2 * h) ^ sw) << 4));
+                    c2[b][ni] = *reinterpret_cast<const dq_u32x4_t*>(wr + (((2 * h + 1) ^ sw) << 4));
                 } else {
-                    c[b][ni] = *reinterpret_cast<const dq_u32x4_t*>(wts + R * 64 + (((2 * b + h) ^ ((R >> 2) & 3)) << 4));
+                    c[b][ni] = *reinterpret_cast<const dq_u32x4_t*>(wr + (((2 * b + h) ^ sw) << 4));
                     c2[b][ni] = c[b][ni];
                 }
-                const uint8_t* sr = sc + R * 16;
+                const uint8_t* sr = sc + R * 8;
                 if constexpr (F == DT_I4G128)
-                    scale[b][ni] = f16_to_f32(*reinterpret_cast<const uint16_t*>(sr + (kb % 8) * 2));
+                    scale[b][ni] = f16_to_f32(*reinterpret_cast<const uint16_t*>(sr));
                 else if constexpr (F == DT_I4G64)
-                    scale[b][ni] = f16_to_f32(*reinterpret_cast<const uint16_t*>(sr + ((kb % 4) * 2 + b) * 2));
+                    scale[b][ni] = f16_to_f32(*reinterpret_cast<const uint16_t*>(sr + 2 * b));
+                else if constexpr (F == DT_FP4)
+                    scale[b][ni] = dq_e8m0(sr[2 * b + h]);
                 else
-                    scale[b][ni] = dq_e8m0(sr[(kb % 4) * 4 + 2 * b + h]);
+                    scale[b][ni] = dq_e8m0(sr[h]);
             }
         };
-        auto read_tok = [&](int j) __attribute__((always_inline)) {
+        auto read_tok = [&](int j, int t) __attribute__((always_inline)) {
             const int b = j >> 2, s4 = j & 3;
-            return *reinterpret_cast<const dq_bf16x8_t*>(tok + tr * 256 + (((8 * b + 4 * h + s4) ^ (tr & 15)) << 4));
+            const int T = 32 * t + r32;
+            const int ch = F == DT_FP8 ? 4 * h + s4 : 8 * b + 4 * h + s4;
+            const int sw = F == DT_FP8 ? ((T >> 1) & 7) : (T & 15);
+            return *reinterpret_cast<const dq_bf16x8_t*>(tok + T * Fm::TROW + ((ch ^ sw) << 4));
         };
         read_codes(0);
-        dq_bf16x8_t tf[2];
-        tf[0] = read_tok(0);
+        dq_bf16x8_t tf[3][2];                       // token fragments, read two steps ahead
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 2; ++j) {
+            tf[j][0] = read_tok(j, 0);
+            tf[j][1] = read_tok(j, 1);
+        }
+#pragma unroll
+        for (int j = 0; j < STEPS; ++j) {
             const int b = j >> 2, s4 = j & 3;
-            if (j + 1 < 8) tf[(j + 1) & 1] = read_tok(j + 1);
-            if (j == 2) read_codes(1);
+            if (j + 2 < STEPS) {
+                tf[(j + 2) % 3][0] = read_tok(j + 2, 0);
+                tf[(j + 2) % 3][1] = read_tok(j + 2, 1);
+            }
+            if (Fm::SUB > 1 && j == 1) read_codes(1);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dt_widen<F>(c[b][ni], c2[b][ni], s4, scale[b][ni]),
-                                                                  tf[j & 1], acc[ni], 0, 0, 0);
-            if (j < BASE) {
+            for (int ni = 0; ni < 2; ++ni) {
+                const dq_bf16x8_t wf = dt_widen<F>(c[b][ni], c2[b][ni], s4, scale[b][ni]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    acc[t][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, tf[j % 3][t], acc[t][ni], 0, 0, 0);
+            }
+            // copies [j BASE / STEPS, (j + 1) BASE / STEPS) go out after step j
+#pragma unroll
+            for (int i = j * BASE / STEPS; i < (j + 1) * BASE / STEPS; ++i) {
                 __builtin_amdgcn_sched_barrier(0);
-                fire(j);
+                fire(i);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
-    // lane l, accumulator element v of fragment ni: token tr, weight row
-    // 8 (v/4) + 4 h + v%4 of the fragment (four consecutive outputs per v/4)
-    auto epilogue = [&](int t) {
+    // lane l, accumulator element v of fragment (t, ni): token 32 t + l%32,
+    // weight row 8 (v/4) + 4 h + v%4 of the fragment (four consecutive
+    // outputs per v/4)
+    auto epilogue = [&](int task) {
         int mt, nt;
-        task_tile(t, mt, nt);
+        task_tile(task, mt, nt);
         const int p0 = tl[max_mt + mt], rows = tl[2 * max_mt + mt];
-        if (tr < rows) {
-            const size_t orow = (size_t)(p0 + tr) * N;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if constexpr (MODE == 0) {
-                    const int f = nt * 128 + 32 * wn + 8 * q + 4 * h;
-                    if (f < N) {
-                        uint2 o;
-                        o.x = pack_bf16x2(silu(acc[0][4 * q]) * acc[1][4 * q], silu(acc[0][4 * q + 1]) * acc[1][4 * q + 1]);
-                        o.y = pack_bf16x2(silu(acc[0][4 * q + 2]) * acc[1][4 * q + 2],
-                                          silu(acc[0][4 * q + 3]) * acc[1][4 * q + 3]);
-                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow + f) = o;
-                    }
-                } else {
+        for (int t = 0; t < 2; ++t) {
+            const int tr = 32 * t + r32;
+            if (tr < rows) {
+                const size_t orow = (size_t)(p0 + tr) * N;
 #pragma unroll
-                    for (int ni = 0; ni < 2; ++ni) {
-                        const int n = nt * DT_BN + 64 * wn + 32 * ni + 8 * q + 4 * h;
-                        if (n < N)
-                            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow + n) =
-                                make_float4(acc[ni][4 * q], acc[ni][4 * q + 1], acc[ni][4 * q + 2], acc[ni][4 * q + 3]);
+                for (int q = 0; q < 4; ++q) {
+                    if constexpr (MODE == 0) {
+                        const int f = nt * (DT_BN / 2) + 32 * wave + 8 * q + 4 * h;
+                        if (f < N) {
+                            const dq_floatx16& g = acc[t][0];
+                            const dq_floatx16& u = acc[t][1];
+                            uint2 o;
+                            o.x = pack_bf16x2(silu(g[4 * q]) * u[4 * q], silu(g[4 * q + 1]) * u[4 * q + 1]);
+                            o.y = pack_bf16x2(silu(g[4 * q + 2]) * u[4 * q + 2], silu(g[4 * q + 3]) * u[4 * q + 3]);
+                            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow + f) = o;
+                        }
+                    } else {
+#pragma unroll
+                        for (int ni = 0; ni < 2; ++ni) {
+                            const int n = nt * DT_BN + 64 * wave + 32 * ni + 8 * q + 4 * h;
+                            if (n < N)
+                                *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow + n) =
+                                    make_float4(acc[t][ni][4 * q], acc[t][ni][4 * q + 1], acc[t][ni][4 * q + 2],
+                                                acc[t][ni][4 * q + 3]);
+                        }
                     }
                 }
             }
         }
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[ni][v] = 0.f;
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[t][ni][v] = 0.f;
     };
 
-    // ---- the stream: stage g is issued at step g - 2 (the prologue issues
-    // stages 0 and 1).  Step g: this wave's copies of stage g have landed
-    // once at most the newest group (stage g + 1) is outstanding; the barrier
-    // then publishes stage g to every wave and tells that everyone is done
-    // with stage g - 1, whose slot receives stage g + 2.
+    // ---- the stream: stage g is prepared at step g - 2 and its token and
+    // code copies go out during step g - 2's MFMAs (the prologue issues
+    // stages 0 and 1 at once).  Step g: this wave's copies of stage g have
+    // landed once at most the newest group (stage g + 1) is outstanding; the
+    // barrier then publishes stage g to every wave and tells that everyone is
+    // done with stage g - 1, whose slot receives stage g + 2.
     issue_next(-1);
 #pragma unroll
     for (int i = 0; i < BASE; ++i) fire(i);
@@ -676,8 +739,8 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
     for (;;) {
         dt_wait<BASE>(n_prev);
         block_barrier();
-        // at a task's first stage: the next task's dispatch entries go out
-        // with this group and are read when the copy side reaches that task
+        // at a task's first stage the next task's dispatch entries go out
+        // with this group; they are read when the copy side reaches that task
         int pp = -1;
         if (MODE == 0 && c_kb == 0 && c_task + nblk < total) {
             int mt, nt;
@@ -743,11 +806,13 @@ bool dq_supported(int K, int N) {
     return K > 0 && K % DQ_PK == 0 && N > 0 && (size_t)N * (size_t)K < ((size_t)1 << 31);
 }
 
-// The staged kernel: whole 16-byte scale windows per row (K a multiple of
-// 512; int4-g128 of 1024) and at least four stages.
+// The staged kernel: whole stages (128 K for 4-bit codes, 64 K for fp8), at
+// least four of them, and scale rows of whole dwords (the window copies).
 bool dq_staged_ok(int fmt, int gs, int K) {
-    if (K < 512 || K % 512 != 0) return false;
-    return !(fmt == DQ_INT4 && gs == 128 && K % 1024 != 0);
+    if (K % 128 != 0) return false;
+    if (fmt == DQ_MXFP8) return K >= 256;
+    if (K < 512) return false;
+    return !(fmt == DQ_INT4 && gs == 128 && K % 256 != 0);
 }
 
 int dq_tile_rows(bool staged) { return staged ? DT_BM : DQ_BM; }
@@ -783,7 +848,7 @@ hipError_t launch_dq_ffn(int mode, int fmt, int gs, bool staged, const void* w0,
     a.gs = fmt == DQ_INT4 ? gs : 32;
     if (staged) {
         // one 512-thread block per CU over the (M-tile, N-tile) tasks
-        const int nN = mode == 0 ? (N + 127) / 128 : (N + DT_BN - 1) / DT_BN;
+        const int nN = mode == 0 ? (N + DT_BN / 2 - 1) / (DT_BN / 2) : (N + DT_BN - 1) / DT_BN;
         const long slots = (long)max_mt * nN;
         const long cap = cu_count();
         const int grid = (int)(slots < cap ? slots : cap);
