@@ -620,7 +620,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral_decode",
                     choices=["mixtral_decode", "mixtral_prefill", "fine_int4_decode",
-                             "stack4_layer0", "stack4"])
+                             "stack4_layer0", "stack4", "fine_int4_prefill", "fine_mxfp4_prefill",
+                             "mixtral_mxfp8_prefill"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the int4 decode and 4-layer stack legs of the default run")
