@@ -139,9 +139,15 @@ int dq_format(const moe_shape* s) {
 
 // Groups above this many rows run the dequantising GEMM (-1: none does):
 // int4-g128 keeps groups of at most tau rows (0: 32) on the skinny int4
-// kernels; int4-g64 and MX weights run every group on it.
+// kernels -- with the default, once the mean group is twice that, every
+// group goes to the GEMM and the skinny launches (which would find no work)
+// are left out; int4-g64 and MX weights run every group on it.
 int dq_tau(const moe_shape* s) {
-    if (s->wt == MOE_INT4_G128) return s->tau < 0 ? -1 : (s->tau == 0 ? kDefaultInt4Tau : s->tau);
+    if (s->wt == MOE_INT4_G128) {
+        if (s->tau < 0) return -1;
+        if (s->tau > 0) return s->tau;
+        return (long)s->T * s->k >= 2L * kDefaultInt4Tau * s->E ? 0 : kDefaultInt4Tau;
+    }
     return dq_format(s) >= 0 ? 0 : -1;
 }
 

@@ -568,6 +568,30 @@ def test_single_tile_list(orc, name):
         assert min(seen[0]) > 128 and min(c[3] for c in seen[1:]) < 128
 
 
+def test_int4_groups_on_both_sides_of_tau(orc):
+    """int4-g128 with the default tau (32 rows) and a mean group below twice
+    that: groups of at most 32 rows on the skinny int4 kernel, larger ones on
+    the dequantising GEMM, in one call -- expert 0 takes every token (a bias),
+    the runner-ups spread over the rest."""
+    cfg = SMALL["int4_dq"]
+    say("int4 groups on both sides of tau")
+    d = device_inputs(cfg)
+    W, S = oracle_weights(d)
+    wr = np_store(d["w_router"])
+    b = np.zeros(cfg.E, np.float32)
+    b[0] = 1e3
+    for TT in (40, 90):
+        xs = d["x"][:TT].contiguous()
+        y, c, i = run_layer(cfg, dict(d, b_router=torch.from_numpy(b).to(DEV)), x=xs)
+        cl = c.cpu().tolist()
+        y_f, _, _, _ = orc.layer_forward(np_store(xs), "bf16", "int4", cfg.k, wr, b, W, S,
+                                         forced_idx=i.cpu().numpy())
+        err = tokenwise_rel(np_f64(y), y_f).max()
+        say(f"  T={TT} counts {cl} max rel {err:.3g}")
+        assert cl[0] == TT and min(cl[1:]) <= 32 and TT * cfg.k < 2 * 32 * cfg.E
+        assert err < TOL["int4"]
+
+
 def test_rmsnorm_parity(orc):
     say("rmsnorm")
     for act in ("f32", "bf16"):
