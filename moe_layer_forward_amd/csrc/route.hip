@@ -242,6 +242,142 @@ __global__ __launch_bounds__(64 * RQ_WAVES) void router_mfma_kernel(
     }
 }
 
+// Large batches with many experts (T*E >= 2^20, E >= 64): the kernel above
+// gives every 16 x 16 tile its own block, so each x row is read once per 16
+// experts and each router row once per 16 tokens, and every lane splits the
+// router values it multiplies.  Here a 512-thread block owns 64 tokens x 64
+// experts and stages K in chunks of 64 in LDS: the x chunk as bf16, the router
+// chunk split once per block into the same three bf16 terms.  Wave (wm, we,
+// kh) multiplies tokens 32 wm .. +31 with experts 32 we .. +31 over K half kh
+// of every chunk on v_mfma_f32_32x32x16_bf16, three MFMAs (hi, mid, lo) per
+// 16 K (two waves per SIMD); at the end the kh = 1 waves park their sums in
+// LDS and the kh = 0 waves add them (a fixed order: deterministic).  LDS rows
+// are 128 bytes with their 16-byte chunks XOR-swizzled by (row/2)&7.
+constexpr int RTL_T = 64, RTL_E = 64, RTL_K = 64, RTL_THREADS = 512;
+
+typedef float rtl_f16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int rtl_swz(int row, int ch) { return row * RTL_K + ((ch ^ ((row >> 1) & 7)) << 3); }
+
+__global__ __launch_bounds__(RTL_THREADS) void router_tile_kernel(const uint16_t* __restrict__ x,
+                                                                  const float* __restrict__ wg,
+                                                                  const float* __restrict__ bias,
+                                                                  float* __restrict__ logits, int T, int d, int E) {
+    __shared__ __attribute__((aligned(16))) uint16_t sx[2][RTL_T * RTL_K];
+    __shared__ __attribute__((aligned(16))) uint16_t sw[2][3][RTL_E * RTL_K];
+    __shared__ float spart[4][16][64];                   // the kh = 1 waves' sums
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, we = (wave >> 1) & 1, kh = wave >> 2;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int t0 = blockIdx.x * RTL_T, e0 = blockIdx.y * RTL_E;
+    const int nch = (d + RTL_K - 1) / RTL_K;
+    // staging: the x piece tid (row tid/8, 16-byte chunk tid%8) and the router
+    // pieces tid + 512 i (row p/16, 4 floats at 4 (p%16)), i < 2; chunks are
+    // loaded into registers RTL_D chunks ahead (a ring, the loop unrolled by
+    // RTL_D so that every index is static)
+    constexpr int RTL_D = 4;
+    uint4 xr[RTL_D];
+    float4 wr[RTL_D][2];
+    auto load = [&](int c, int u) __attribute__((always_inline)) {
+        const int k0 = c * RTL_K;
+        {
+            const int row = tid >> 3, k = k0 + 8 * (tid & 7);
+            const int t = min(t0 + row, T - 1);          // clamped rows: their results are not stored
+            xr[u] = k < d ? *reinterpret_cast<const uint4*>(x + (size_t)t * d + k) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int p = tid + RTL_THREADS * i, row = p >> 4, k = k0 + 4 * (p & 15);
+            const int e = min(e0 + row, E - 1);
+            wr[u][i] = k < d ? *reinterpret_cast<const float4*>(wg + (size_t)e * d + k)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto store = [&](int u, int buf) __attribute__((always_inline)) {
+        *reinterpret_cast<uint4*>(&sx[buf][rtl_swz(tid >> 3, tid & 7)]) = xr[u];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int p = tid + RTL_THREADS * i, row = p >> 4, c4 = p & 15;
+            const float v[4] = {wr[u][i].x, wr[u][i].y, wr[u][i].z, wr[u][i].w};
+            uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t uu = __float_as_uint(v[q]);
+                const uint32_t uh = uu & 0xffff0000u;
+                const float r1 = v[q] - __uint_as_float(uh);
+                const uint32_t um = __float_as_uint(r1) & 0xffff0000u;
+                const float r2 = r1 - __uint_as_float(um);
+                hi[q] = uh >> 16;
+                mid[q] = um >> 16;
+                lo[q] = __float_as_uint(r2) >> 16;     // exact: r2 has <= 8 significant bits
+            }
+            const int o = rtl_swz(row, c4 >> 1) + 4 * (c4 & 1);
+            *reinterpret_cast<uint2*>(&sw[buf][0][o]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+            *reinterpret_cast<uint2*>(&sw[buf][1][o]) = make_uint2(mid[0] | (mid[1] << 16), mid[2] | (mid[3] << 16));
+            *reinterpret_cast<uint2*>(&sw[buf][2][o]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+        }
+    };
+    // one accumulator per bf16 term, so consecutive MFMAs do not wait on each
+    // other; summed hi + mid + lo at the end
+    rtl_f16 acc3[3];
+#pragma unroll
+    for (int term = 0; term < 3; ++term)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc3[term][v] = 0.f;
+    const int ta = 32 * wm + r32, eb = 32 * we + r32;   // the lane's token (A) and expert (B) rows
+    // chunk c sits in LDS buffer c % 2: chunk c + 1 is split and stored while
+    // chunk c's MFMAs run, then one barrier
+#pragma unroll
+    for (int u = 0; u < RTL_D; ++u)
+        if (u < nch) load(u, u);
+    store(0, 0);
+    if (RTL_D < nch) load(RTL_D, 0);
+    __syncthreads();
+    for (int c0 = 0; c0 < nch; c0 += RTL_D) {
+#pragma unroll
+        for (int u = 0; u < RTL_D; ++u) {
+            const int c = c0 + u;
+            if (c >= nch) break;
+            const int buf = u & 1;              // c % 2 (RTL_D is even)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int ch = 2 * (2 * kh + s2) + h;
+                const rq_bf16x8 A = *reinterpret_cast<const rq_bf16x8*>(&sx[buf][rtl_swz(ta, ch)]);
+#pragma unroll
+                for (int term = 0; term < 3; ++term) {
+                    const rq_bf16x8 B = *reinterpret_cast<const rq_bf16x8*>(&sw[buf][term][rtl_swz(eb, ch)]);
+                    acc3[term] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc3[term], 0, 0, 0);
+                }
+            }
+            if (c + 1 < nch) {
+                const int un = (u + 1) % RTL_D;  // chunk c + 1's register slot
+                store(un, buf ^ 1);
+                if (c + 1 + RTL_D < nch) load(c + 1 + RTL_D, un);
+            }
+            __syncthreads();                    // chunk c + 1 published; chunk c's reads done
+        }
+    }
+    rtl_f16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = (acc3[0][v] + acc3[1][v]) + acc3[2][v];
+    if (kh == 1) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) spart[wave & 3][v][lane] = acc[v];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    // lane l, element v: token 8 (v/4) + 4 h + v%4 of the wave's 32, expert l%32
+    const int e = e0 + eb;
+    if (e < E) {
+        const float bv = bias ? bias[e] : 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int t = t0 + 32 * wm + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (t < T) logits[(size_t)t * E + e] = (acc[v] + spart[wave][v][lane]) + bv;
+        }
+    }
+}
+
 // (value, index) is better than (v2, i2): larger value, or equal value and
 // lower expert index.  NaN was mapped to -inf before, so every unchosen expert
 // stays comparable and exactly k distinct experts are always selected.
@@ -311,6 +447,10 @@ hipError_t launch_route(int act, const void* x, const float* wg, const float* b,
         else hipLaunchKernelGGL((router_logits_kernel<DT_F32, 8>), g1, dim3(RT_THREADS), 0, s, x, wg, b, logits, T, d, E);
     } else if (small) {
         hipLaunchKernelGGL((router_logits_kernel<DT_BF16, 1>), g1, dim3(RT_THREADS), 0, s, x, wg, b, logits, T, d, E);
+    } else if ((long)T * E >= (1L << 20) && E >= RTL_E) {
+        const dim3 g3((T + RTL_T - 1) / RTL_T, (E + RTL_E - 1) / RTL_E);
+        hipLaunchKernelGGL(router_tile_kernel, g3, dim3(RTL_THREADS), 0, s, reinterpret_cast<const uint16_t*>(x), wg, b,
+                           logits, T, d, E);
     } else {
         const dim3 g2((T + 15) / 16, (E + 15) / 16);
         hipLaunchKernelGGL(router_mfma_kernel, g2, dim3(64 * RQ_WAVES), 0, s,

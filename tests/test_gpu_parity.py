@@ -184,10 +184,21 @@ def _check_route(cfg, x, wr, br, L, idx, w, orc):
     np.testing.assert_allclose(w.sum(1), 1.0, atol=1e-6)
 
 
+# Router shapes for the 64 x 64-tile kernel (T*E >= 2^20, E >= 64): whole
+# tiles and K chunks, and a ragged one (T not a multiple of 64, E = 200 with a
+# partial last expert tile, d = 264: a K tail of 8 in the last chunk)
+ROUTE_WIDE = {
+    "route_wide": moe_inputs.MoEConfig("route_wide", T=4096, d=512, E=256, k=8, F=128, act="bf16",
+                                       wt="bf16", model="s_route_wide"),
+    "route_wide_ragged": moe_inputs.MoEConfig("route_wide_ragged", T=5300, d=264, E=200, k=6, F=128,
+                                              act="bf16", wt="bf16", model="s_route_wr"),
+}
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "mixtral_decode", "mixtral_prefill",
-                                  "fine_int4_decode", "stack4"])
+                                  "fine_int4_decode", "stack4", "fine_int4_prefill"] + list(ROUTE_WIDE))
 def test_route_parity(orc, name):
-    cfg = C[name]
+    cfg = ROUTE_WIDE[name] if name in ROUTE_WIDE else C[name]
     say(f"route parity {name}")
     x = moe_inputs.activations(cfg, 0)
     wr = moe_inputs.router_weights(cfg, 0, 0)
