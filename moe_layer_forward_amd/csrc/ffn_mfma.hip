@@ -67,8 +67,19 @@ constexpr int MF_NS = 5;          // LDS stages (copies four K steps ahead)
 constexpr int MF_STAGE = MF_BM * MF_BK;   // elements of one operand stage
 constexpr int MF_GM = 8;          // M-tiles per scheduling group
 constexpr uint32_t MF_OOB = 0x80000000u;   // beyond any buffer: the range check yields 0
+constexpr int kNonTemporal = 2;            // buffer-load cache policy: streamed, not kept
 
 constexpr int MS_BM = kMfmaSmallRows;   // rows of a small M-tile
+
+template <int I>
+using ic = std::integral_constant<int, I>;
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(ic<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 int mfma_bm() { return MF_BM; }
 // Big tiles: experts with more than 128 rows, in 256-row tiles (the tail
@@ -703,12 +714,23 @@ __global__ __launch_bounds__(256) void mfma_tail_reduce(MfmaArgs a, int G) {
 // v_mfma_f32_32x32x16_bf16.  K is staged in pairs of steps like the 256-row
 // kernel (128-byte LDS rows swizzled by (row/2)&7, every copy 8 rows x one
 // whole line): two pair slots of A (8 KiB each) and of B (32 KiB each), 80 KiB
-// of LDS so two blocks share a CU.  Pair j+1 is copied at the second step of
-// pair j-1, two steps before its first fragments are read (fragments are read
-// one step ahead of their MFMAs).  Such tiles stream each weight tile for few
-// rows, so the kernel is bound by the weight stream, not the matrix cores.
+// of LDS so two blocks share a CU.  Such tiles stream each weight tile for
+// few rows, so the kernel is bound by the weight stream, not the matrix cores.
+//
+// The copies go through registers, not buffer_load ... lds: each wave loads
+// its ten lines of a K pair (2 of A, 8 of B; the weight lines non-temporal)
+// into one of two register buffers, and writes them to the LDS pair slot just
+// before the barrier that opens that pair.  A buffer is free again once
+// written, so the loads of pair j+2 go out at the start of pair j and two
+// pairs per wave are in flight through both K steps of a pair.  (The same
+// tiles with LDS-direct copies and one pair in flight streamed the stack
+// layer's weights ~11-14% slower; a third register buffer does not fit two
+// blocks per CU.)  The loop body has no conditions: pairs past the last load
+// as zeros (the range check) and multiply as zeros, so the compiler's wait
+// counts see the same loads in flight at every step.
 constexpr int MS_PSLOT_A = MS_BM * MF_PK;     // elements of an A pair slot
 constexpr int MS_PSLOT_B = MF_BN * MF_PK;     // elements of a B pair slot
+constexpr int MS_RING = 2;                    // register buffers (pairs)
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void mfma_small_kernel(MfmaArgs a) {
@@ -726,7 +748,8 @@ __global__ __launch_bounds__(256, 2) void mfma_small_kernel(MfmaArgs a) {
     const uint32_t row_bytes = (uint32_t)K * 2u;
     const int nk = (K + 31) / 32;
     const int P = (nk + 1) / 2;                   // K pairs (an odd last step runs on zeros)
-    const int32x4_t RA = make_desc(a.in, (uint32_t)a.in_rows * row_bytes);
+    const __amdgpu_buffer_rsrc_t RA = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(a.in), (short)0, (int)((uint32_t)a.in_rows * row_bytes), 0x00020000);
     const uint32_t wmat = (uint32_t)N * row_bytes;
     // copies: wave w fills A rows 16w + 8i + lane/8 (i = 0, 1) and B rows
     // 64w + 8i + lane/8 (i = 0..7), physical chunk lane%8 of the 128-byte row,
@@ -744,7 +767,8 @@ __global__ __launch_bounds__(256, 2) void mfma_small_kernel(MfmaArgs a) {
         const int rows = tl[2 * max_st + st_i];
 
         const uint16_t* wsrc = (MODE == 0 && wave >= 2) ? a.w1 : a.w0;
-        const int32x4_t RB = make_desc(wsrc + (size_t)e * N * K, wmat);
+        const __amdgpu_buffer_rsrc_t RB = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(wsrc + (size_t)e * N * K), (short)0, (int)wmat, 0x00020000);
         uint32_t aoff[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -769,79 +793,84 @@ __global__ __launch_bounds__(256, 2) void mfma_small_kernel(MfmaArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-        // this wave's 10 copies of pair j into pair slot sl
-        auto issue = [&](int j, int sl) __attribute__((always_inline)) {
+        // this wave's ten lines of pair j into register buffer S
+        u32x4_t ra[MS_RING][2], rb[MS_RING][8];
+        auto load = [&](int j, auto slot) __attribute__((always_inline)) {
+            constexpr int S = decltype(slot)::value;
             const int k0 = 2 * j * 32;
             const uint32_t kbyte = (uint32_t)k0 * 2u;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const bool kok = k0 + 8 * (kc0 ^ ((i & 1) << 2)) < K;
-                dma16(RA, (kok && aoff[i] != MF_OOB) ? aoff[i] + kbyte : MF_OOB,
-                      lds_addr(&sA[sl][(wave * 16 + 8 * i) * MF_PK]));
+                ra[S][i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    RA, (kok && aoff[i] != MF_OOB) ? aoff[i] + kbyte : MF_OOB, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const bool kok = k0 + 8 * (kc0 ^ ((i & 1) << 2)) < K;
                 const uint32_t o = boff0 + 8u * (uint32_t)i * row_bytes + ((i & 1) ? (uint32_t)kodd : 0u);
-                dma16(RB, (kok && 8 * i < bn) ? o + kbyte : MF_OOB,
-                      lds_addr(&sB[sl][(wave * 64 + 8 * i) * MF_PK]));
+                rb[S][i] = __builtin_amdgcn_raw_buffer_load_b128(RB, (kok && 8 * i < bn) ? o + kbyte : MF_OOB, 0,
+                                                                 kNonTemporal);
             }
+        };
+        // register buffer S into LDS pair slot sl, each lane at the position
+        // its line belongs to
+        auto store = [&](auto slot, int sl) __attribute__((always_inline)) {
+            constexpr int S = decltype(slot)::value;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                *reinterpret_cast<u32x4_t*>(&sA[sl][(wave * 16 + 8 * i) * MF_PK + 8 * lane]) = ra[S][i];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<u32x4_t*>(&sB[sl][(wave * 64 + 8 * i) * MF_PK + 8 * lane]) = rb[S][i];
         };
         auto brow = [&](int ni) {
             return (MODE == 0) ? ni * 128 + wave * 32 + (lane & 31) : wave * 64 + ni * 32 + (lane & 31);
         };
-        bf16x8_t fa[2][2][2], fb[2][2][2];            // [slot][ks][mi or ni]
-        // fragments of K step kt (pair kt/2, half kt%2) into register slot rs
-        auto read = [&](int kt, int rs) __attribute__((always_inline)) {
+        // K step kt: per 16-K half, two token and two weight fragments, then
+        // their four MFMAs
+        auto step = [&](int kt) __attribute__((always_inline)) {
             const uint16_t* a_ = sA[(kt >> 1) & 1];
             const uint16_t* b_ = sB[(kt >> 1) & 1];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int ch = (kt & 1) * 4 + ks * 2 + (lane >> 5);
+                bf16x8_t fa[2], fb[2];
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi)
-                    fa[rs][ks][mi] = *reinterpret_cast<const bf16x8_t*>(&a_[swz2(mi * 32 + (lane & 31), ch)]);
+                    fa[mi] = *reinterpret_cast<const bf16x8_t*>(&a_[swz2(mi * 32 + (lane & 31), ch)]);
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    fb[rs][ks][ni] = *reinterpret_cast<const bf16x8_t*>(&b_[swz2(brow(ni), ch)]);
-            }
-        };
-        auto mma = [&](int rs) __attribute__((always_inline)) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+                    fb[ni] = *reinterpret_cast<const bf16x8_t*>(&b_[swz2(brow(ni), ch)]);
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                     for (int ni = 0; ni < 2; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[rs][ks][mi], fb[rs][ks][ni],
-                                                                               acc[mi][ni], 0, 0, 0);
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+            }
         };
 
-        // previous tile's stores and reads are done before the slots refill
-        wait_vm(0);
-        block_barrier();
-        issue(0, 0);
-        if (P > 1) {
-            issue(1, 1);
-            __builtin_amdgcn_s_waitcnt(0x0F7A);         // vmcnt(10): pair 0 landed
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0)
-        }
-        block_barrier();
-        read(0, 0);
-        // Step 2j: read step 2j+1, multiply step 2j.  Step 2j+1: pair j+1
-        // landed (the only copies in flight), a barrier (every wave sees it and
-        // has finished reading pair j), copy pair j+2 into pair j's slot, read
-        // step 2j+2, multiply step 2j+1.
-        for (int j = 0; j < P; ++j) {
-            read(2 * j + 1, 1);
-            mma(0);
-            __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): pair j+1 landed
-            __builtin_amdgcn_s_waitcnt(0xC07F);         // lgkmcnt(0): own reads of pair j done
-            block_barrier();
-            if (j + 2 < P) issue(j + 2, j & 1);
-            if (j + 1 < P) read(2 * j + 2, 0);
-            mma(1);
+        // the previous tile's fragment reads are done before slot 0 refills
+        __syncthreads();
+        static_for<0, MS_RING>([&](auto r) { load(decltype(r)::value, r); });
+        store(ic<0>{}, 0);
+        __syncthreads();
+        // Pair j (in LDS slot j&1): load pair j+2 into the buffer pair j came
+        // from (written to LDS in the previous iteration), the two K steps of
+        // pair j, pair j+1 from its buffer into the other slot (whose pair j-1
+        // every wave finished with before the previous barrier), barrier.
+        const int Pp = (P + MS_RING - 1) / MS_RING * MS_RING;
+        for (int j0 = 0; j0 < Pp; j0 += MS_RING) {
+            static_for<0, MS_RING>([&](auto u) {
+                constexpr int U = decltype(u)::value;
+                const int j = j0 + U;
+                load(j + MS_RING, u);
+                __builtin_amdgcn_sched_barrier(0);   // the loads go out first
+                step(2 * j);
+                step(2 * j + 1);
+                store(ic<(U + 1) % MS_RING>{}, (j + 1) & 1);
+                __syncthreads();
+            });
         }
 
         // ---- epilogue; accumulator element v of lane l: column l%32, row 8*(v/4) + 4*(l/32) + v%4
