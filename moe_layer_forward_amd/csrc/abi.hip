@@ -12,6 +12,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 #include <algorithm>
 #include <atomic>
@@ -249,6 +250,7 @@ struct FfnBufs {
     int32_t* tiles;
     float* part;
     int part_cap;
+    bool plan_ready;     // the dispatch kernel already wrote the MFMA tile lists
 };
 
 // The FFN launch sequence of the routed experts, shared by moe_expert_ffn and
@@ -278,7 +280,7 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     int rc;
 
     if (s->T == 0) return MOE_OK;
-    if (use_mfma) {
+    if (use_mfma && !b.plan_ready) {
         rc = hip_check(launch_mfma_plan(counts, offsets, s->T, s->k, s->E, tau, tmode, tiles, max_mt, st), st,
                        "mfma plan", err, err_len);
         if (rc) return rc;
@@ -401,10 +403,10 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
 // y_shared (identity order) and its h the shared region of the workspace.
 int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32_t* counts,
             const int32_t* offsets, const int32_t* perm, float* y_perm, float* y_shared,
-            char* ws, hipStream_t st, char* err, size_t err_len) {
+            char* ws, hipStream_t st, char* err, size_t err_len, bool plan_ready = false) {
     const Layout L = layout(s);
     const FfnBufs b{ws + L.h, reinterpret_cast<int32_t*>(ws + L.tiles), reinterpret_cast<float*>(ws + L.part),
-                    L.part_cap};
+                    L.part_cap, plan_ready};
     void* hs = s->n_shared ? ws + L.hs : nullptr;
     int rc = run_groups(s, x, w, counts, offsets, perm, y_perm, y_shared, b, hs, st, err, err_len);
     if (rc || !shared_as_group(s) || s->T == 0) return rc;
@@ -424,7 +426,7 @@ int run_ffn(const moe_shape* s, const void* x, const moe_weights* w, const int32
     if (rc) return rc;
     // the routed plan and partial tiles are consumed by now (stream order); a
     // one-expert group needs no more of either than the routed experts do
-    const FfnBufs bs{hs, b.tiles, b.part, std::min(part_cap(&sh), L.part_cap)};
+    const FfnBufs bs{hs, b.tiles, b.part, std::min(part_cap(&sh), L.part_cap), false};
     return run_groups(&sh, x, &sw, sid, sid + 1, sid + 3, y_shared, nullptr, bs, nullptr, st, err, err_len);
 }
 
@@ -590,6 +592,7 @@ int moe_layer_forward(const moe_shape* shape, const void* x, const float* w_rout
         return hip_check(launch_dispatch(idx, counts, offsets, perm, inv, 0, shape->k, shape->E, st), st,
                          "dispatch", err, err_len);
     }
+    bool plan_ready = false;
     if (route_dispatch_small_supported(shape->T, shape->E, shape->k)) {
         // a decode batch: router, top-k and dispatch in one launch
         rc = hip_check(launch_route_dispatch_small(shape->act, x, w_router, b_router, logits, idx, gw, counts,
@@ -601,11 +604,22 @@ int moe_layer_forward(const moe_shape* shape, const void* x, const float* w_rout
                                     shape->E, shape->k, st),
                        st, "route", err, err_len);
         if (rc) return rc;
-        rc = hip_check(launch_dispatch(idx, counts, offsets, perm, inv, shape->T, shape->k, shape->E, st), st,
-                       "dispatch", err, err_len);
+        // the routed experts' MFMA tile lists come out of the dispatch kernel
+        const int tau = effective_tau(shape);
+        if (tau >= 0 && shape->T > tau) {
+            const MfmaPlanArgs plan = mfma_plan_args(shape->T, shape->k, shape->E, tau, tile_mode(shape),
+                                                     (int32_t*)(W + L.tiles),
+                                                     mfma_max_tiles(shape->T, shape->k, shape->E));
+            plan_ready = true;
+            rc = hip_check(launch_dispatch(idx, counts, offsets, perm, inv, shape->T, shape->k, shape->E, st, &plan),
+                           st, "dispatch", err, err_len);
+        } else {
+            rc = hip_check(launch_dispatch(idx, counts, offsets, perm, inv, shape->T, shape->k, shape->E, st), st,
+                           "dispatch", err, err_len);
+        }
         if (rc) return rc;
     }
-    rc = run_ffn(shape, x, w, counts, offsets, perm, yp, ys, W, st, err, err_len);
+    rc = run_ffn(shape, x, w, counts, offsets, perm, yp, ys, W, st, err, err_len, plan_ready);
     if (rc) return rc;
     return hip_check(launch_combine(shape->act, yp, inv, gw, ys, residual, y, shape->T, shape->d, shape->k, st),
                      st, "combine", err, err_len);

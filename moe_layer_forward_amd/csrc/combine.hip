@@ -100,16 +100,35 @@ hipError_t launch_combine(int act, const float* yp, const int32_t* inv, const fl
     return hipGetLastError();
 }
 
-// RMSNorm: out = h / sqrt(mean(h^2) + eps) * gamma, fp32 math.
+// RMSNorm: out = h / sqrt(mean(h^2) + eps) * gamma, fp32 math.  One block per
+// token; each thread takes 8-element chunks (one 16-byte load in bf16), sums
+// their squares, and after the block sum scales the same chunks (the second
+// read hits the cache).
+template <int ACT>
+__device__ __forceinline__ void load8(const void* p, size_t i, float (&v)[8]) {
+    if constexpr (ACT == DT_F32) {
+        const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+        const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i);
+        v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x); v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+        v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z); v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+    }
+}
+
 template <int ACT>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ h,
                                                      const float* __restrict__ gamma, float eps,
                                                      void* __restrict__ out, int d) {
     const int t = blockIdx.x;
+    const int nch = d / 8;
     float ss = 0.f;
-    for (int i = threadIdx.x; i < d; i += 256) {
-        const float v = load_act<ACT>(h, (size_t)t * d + i);
-        ss = fmaf(v, v, ss);
+    for (int c = threadIdx.x; c < nch; c += 256) {
+        float v[8];
+        load8<ACT>(h, (size_t)t * d + (size_t)c * 8, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
     }
     ss = wave_sum(ss);
     __shared__ float part[4];
@@ -117,9 +136,30 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ h
     __syncthreads();
     const float tot = part[0] + part[1] + part[2] + part[3];
     const float r = 1.0f / sqrtf(tot / (float)d + eps);
-    for (int i = threadIdx.x; i < d; i += 256) {
-        const float v = load_act<ACT>(h, (size_t)t * d + i);
-        store_act<ACT>(out, (size_t)t * d + i, v * r * (gamma ? gamma[i] : 1.0f));
+    for (int c = threadIdx.x; c < nch; c += 256) {
+        float v[8], g[8];
+        load8<ACT>(h, (size_t)t * d + (size_t)c * 8, v);
+        if (gamma) {
+            load8<DT_F32>(gamma, (size_t)c * 8, g);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[i] = 1.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = v[i] * r * g[i];
+        const size_t o = (size_t)t * d + (size_t)c * 8;
+        if constexpr (ACT == DT_F32) {
+            float* q = reinterpret_cast<float*>(out) + o;
+            *reinterpret_cast<float4*>(q) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(q + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+            uint4 q;
+            q.x = pack_bf16x2(v[0], v[1]);
+            q.y = pack_bf16x2(v[2], v[3]);
+            q.z = pack_bf16x2(v[4], v[5]);
+            q.w = pack_bf16x2(v[6], v[7]);
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + o) = q;
+        }
     }
 }
 

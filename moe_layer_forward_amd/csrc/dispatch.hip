@@ -14,19 +14,24 @@
 // in chunks of 1024: inside a wave, the rank of an element among equal keys
 // comes from 8 ballots on the key bits (peer mask, popcount of lower peers);
 // per-(wave, expert) counts go to an LDS table that is scanned wave-major per
-// expert.  The result equals a stable counting sort, bit for bit.
+// expert.  The result equals a stable counting sort, bit for bit.  The keys of
+// DP_PF rounds are loaded together up front, so a round does not wait on its
+// own global load.  With plan arguments, wave 0 also writes the grouped
+// GEMM's tile lists once the offsets are known (plan.h).
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace moe {
 
 constexpr int DP_THREADS = 1024;
 constexpr int DP_WAVES = DP_THREADS / 64;
 constexpr int DP_MAXE = 256;
+constexpr int DP_PF = 8;      // rounds of keys loaded together
 
 __global__ __launch_bounds__(DP_THREADS) void dispatch_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int n, int E) {
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv, int n, int E, MfmaPlanArgs plan) {
     __shared__ int s_cnt[DP_MAXE];
     __shared__ int s_cursor[DP_MAXE];
     __shared__ int s_wave[DP_WAVES][DP_MAXE];
@@ -59,10 +64,11 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_kernel(
             const int v = __shfl_up(incl, o, 64);
             if (lane >= o) incl += v;
         }
-        int run = incl - sum;
+        int run = incl - sum, o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int e = 4 * lane + j;
+            o[j] = run;
             if (e < E) {
                 counts[e] = c[j];
                 offsets[e] = run;
@@ -71,57 +77,69 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_kernel(
             run += c[j];
         }
         if (lane == 63) offsets[E] = incl;
+        if (plan.tiles) mfma_plan_wave(lane, c, o, E, plan);
     }
     __syncthreads();
 
     // 3. stable placement, 1024 assignments per round
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < n; base += DP_THREADS) {
-        const int a = base + tid;
-        int key = -1;
-        if (a < n) {
-            key = idx[a];
+    for (int base0 = 0; base0 < n; base0 += DP_THREADS * DP_PF) {
+        int keys[DP_PF];
+#pragma unroll
+        for (int r = 0; r < DP_PF; ++r) {
+            const int a = base0 + r * DP_THREADS + tid;
+            keys[r] = a < n ? idx[a] : -1;
+        }
+#pragma unroll
+        for (int r = 0; r < DP_PF; ++r) {
+            const int base = base0 + r * DP_THREADS;
+            if (base >= n) break;
+            const int a = base + tid;
+            int key = keys[r];
             if (key < 0 || key >= E) key = -1;
-        }
-        const bool valid = key >= 0;
-        uint64_t peers = __ballot(valid);
+            const bool valid = key >= 0;
+            uint64_t peers = __ballot(valid);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const bool bit = valid && ((key >> b) & 1);
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
-        const int rank = __popcll(peers & lt_mask);
-        if (valid && rank == 0) s_wave[wave][key] = __popcll(peers);
-        __syncthreads();
-        // per expert: exclusive scan over waves, then advance the cursor
-        if (tid < E) {
-            int run = s_cursor[tid];
-#pragma unroll
-            for (int w = 0; w < DP_WAVES; ++w) {
-                const int c = s_wave[w][tid];
-                s_wave[w][tid] = run;
-                run += c;
+            for (int b = 0; b < 8; ++b) {
+                const bool bit = valid && ((key >> b) & 1);
+                const uint64_t m = __ballot(bit);
+                peers &= bit ? m : ~m;
             }
-            s_cursor[tid] = run;
+            const int rank = __popcll(peers & lt_mask);
+            if (valid && rank == 0) s_wave[wave][key] = __popcll(peers);
+            __syncthreads();
+            // per expert: exclusive scan over waves, then advance the cursor
+            if (tid < E) {
+                int run = s_cursor[tid];
+#pragma unroll
+                for (int w = 0; w < DP_WAVES; ++w) {
+                    const int c = s_wave[w][tid];
+                    s_wave[w][tid] = run;
+                    run += c;
+                }
+                s_cursor[tid] = run;
+            }
+            __syncthreads();
+            if (valid) {
+                const int pos = s_wave[wave][key] + rank;
+                perm[pos] = a;
+                inv[a] = pos;
+            }
+            __syncthreads();
+            // clear the table for the next round
+            for (int i = tid; i < DP_WAVES * DP_MAXE; i += DP_THREADS) (&s_wave[0][0])[i] = 0;
+            __syncthreads();
         }
-        __syncthreads();
-        if (valid) {
-            const int pos = s_wave[wave][key] + rank;
-            perm[pos] = a;
-            inv[a] = pos;
-        }
-        __syncthreads();
-        // clear the table for the next round
-        for (int i = tid; i < DP_WAVES * DP_MAXE; i += DP_THREADS) (&s_wave[0][0])[i] = 0;
-        __syncthreads();
     }
 }
 
 hipError_t launch_dispatch(const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* perm,
-                           int32_t* inv, int T, int k, int E, hipStream_t s) {
+                           int32_t* inv, int T, int k, int E, hipStream_t s, const MfmaPlanArgs* plan) {
+    if (plan && (E > DP_MAXE || plan->tile_mode < MFMA_TILES_BOTH || plan->tile_mode > MFMA_TILES_BIG))
+        return hipErrorInvalidValue;
+    const MfmaPlanArgs p = plan ? *plan : MfmaPlanArgs{nullptr, 0, 0, 0, 0};
     hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(DP_THREADS), 0, s, idx, counts, offsets, perm,
-                       inv, T * k, E);
+                       inv, T * k, E, p);
     return hipGetLastError();
 }
 

@@ -53,6 +53,7 @@
 #include "devinfo.h"
 #include "kernels.h"
 #include "lds_dma.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -60,7 +61,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int MF_BM = 256;
+constexpr int MF_BM = kMfmaBigRows;
 constexpr int MF_BN = 256;
 constexpr int MF_BK = 32;         // K per LDS stage
 constexpr int MF_NS = 5;          // LDS stages (copies four K steps ahead)
@@ -96,61 +97,19 @@ int mfma_plan_ints(int T, int k, int E) {
 int mfma_part_cap() { return 256; }
 int mfma_ntiles_n(int mode, int N) { return mode == 0 ? (N + 127) / 128 : (N + MF_BN - 1) / MF_BN; }
 
-// One 256-thread block: per expert with more than tau rows, its big and small
-// tiles; exclusive scans over the experts place them.  List layout (ints):
-// big: expert[max_mt], row0[max_mt], rows[max_mt], count; then the same for
-// the small tiles with max_st entries.
-__global__ __launch_bounds__(256) void mfma_plan_kernel(const int32_t* __restrict__ counts,
-                                                       const int32_t* __restrict__ offsets, int E,
-                                                       int tau, int tile_mode, int32_t* __restrict__ tiles,
-                                                       int max_mt, int max_st) {
-    __shared__ int s[2][2][256];
-    const int tid = threadIdx.x;
-    int c = 0, nb = 0, ns = 0, rem = 0;
-    if (tid < E) {
-        c = counts[tid];
-        if (c > tau && c > 0) {
-            const bool big = tile_mode == MFMA_TILES_BIG || (tile_mode == MFMA_TILES_BOTH && c > 2 * MS_BM);
-            if (big) {
-                nb = (c + MF_BM - 1) / MF_BM;
-            } else {
-                rem = c;
-                ns = (c + MS_BM - 1) / MS_BM;
-            }
-        }
+// The tile lists (plan.h) from counts and offsets: one wave.
+__global__ __launch_bounds__(64) void mfma_plan_kernel(const int32_t* __restrict__ counts,
+                                                      const int32_t* __restrict__ offsets, int E,
+                                                      MfmaPlanArgs p) {
+    const int lane = threadIdx.x;
+    int c[4], o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = 4 * lane + j;
+        c[j] = e < E ? counts[e] : 0;
+        o[j] = e < E ? offsets[e] : 0;
     }
-    int cur = 0;
-    s[0][0][tid] = nb;
-    s[0][1][tid] = ns;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        int v0 = s[cur][0][tid], v1 = s[cur][1][tid];
-        if (tid >= o) { v0 += s[cur][0][tid - o]; v1 += s[cur][1][tid - o]; }
-        s[cur ^ 1][0][tid] = v0;
-        s[cur ^ 1][1][tid] = v1;
-        cur ^= 1;
-        __syncthreads();
-    }
-    int32_t* small = tiles + 3 * max_mt + 1;
-    if (tid < E) {
-        const int o0 = offsets[tid];
-        const int sb = s[cur][0][tid] - nb, ss = s[cur][1][tid] - ns;
-        for (int i = 0; i < nb; ++i) {
-            tiles[sb + i] = tid;
-            tiles[max_mt + sb + i] = o0 + i * MF_BM;
-            tiles[2 * max_mt + sb + i] = min(MF_BM, c - i * MF_BM);
-        }
-        const int base = o0 + c - rem;
-        for (int j = 0; j < ns; ++j) {
-            small[ss + j] = tid;
-            small[max_st + ss + j] = base + j * MS_BM;
-            small[2 * max_st + ss + j] = min(MS_BM, rem - j * MS_BM);
-        }
-    }
-    if (tid == 255) {
-        tiles[3 * max_mt] = s[cur][0][255];
-        small[3 * max_st] = s[cur][1][255];
-    }
+    mfma_plan_wave(lane, c, o, E, p);
 }
 
 struct MfmaArgs {
@@ -899,11 +858,15 @@ __global__ __launch_bounds__(256, 2) void mfma_small_kernel(MfmaArgs a) {
     }
 }
 
+MfmaPlanArgs mfma_plan_args(int T, int k, int E, int tau, int tile_mode, int32_t* tiles, int max_mt) {
+    return MfmaPlanArgs{tiles, tau, tile_mode, max_mt, mfma_max_small(T, k, E)};
+}
+
 hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int T, int k, int E, int tau,
                             int tile_mode, int32_t* tiles, int max_mt, hipStream_t s) {
     if (E > 256 || tile_mode < MFMA_TILES_BOTH || tile_mode > MFMA_TILES_BIG) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(mfma_plan_kernel, dim3(1), dim3(256), 0, s, counts, offsets, E, tau, tile_mode, tiles,
-                       max_mt, mfma_max_small(T, k, E));
+    hipLaunchKernelGGL(mfma_plan_kernel, dim3(1), dim3(64), 0, s, counts, offsets, E,
+                       mfma_plan_args(T, k, E, tau, tile_mode, tiles, max_mt));
     return hipGetLastError();
 }
 

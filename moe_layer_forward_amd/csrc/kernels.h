@@ -26,8 +26,11 @@ struct GemvArgs {
 
 hipError_t launch_route(int act, const void* x, const float* wg, const float* b, float* logits,
                         int32_t* idx, float* w, int T, int d, int E, int k, hipStream_t s);
+struct MfmaPlanArgs;
+// plan: when non-null, the dispatch kernel also writes the grouped GEMM's
+// tile lists (what launch_mfma_plan would write), saving a launch
 hipError_t launch_dispatch(const int32_t* idx, int32_t* counts, int32_t* offsets, int32_t* perm,
-                           int32_t* inv, int T, int k, int E, hipStream_t s);
+                           int32_t* inv, int T, int k, int E, hipStream_t s, const MfmaPlanArgs* plan = nullptr);
 // router + softmax + top-k + dispatch of a small decode batch in one kernel
 // (T*E within 64 register-held pairs; see route_dispatch_small_supported)
 bool route_dispatch_small_supported(int T, int E, int k);
@@ -90,6 +93,7 @@ enum { MFMA_TILES_BOTH = 0, MFMA_TILES_SMALL = 1, MFMA_TILES_BIG = 2 };
 constexpr int kMfmaSmallRows = 64;
 hipError_t launch_mfma_plan(const int32_t* counts, const int32_t* offsets, int T, int k, int E, int tau,
                             int tile_mode, int32_t* tiles, int max_mt, hipStream_t s);
+MfmaPlanArgs mfma_plan_args(int T, int k, int E, int tau, int tile_mode, int32_t* tiles, int max_mt);
 hipError_t launch_mfma_ffn(int mode, int tile_mode, const void* w0, const void* w1, const void* in, void* out,
                            const int32_t* perm, const int32_t* tiles, int N, int K, int topk, int T_tokens,
                            int max_mt, int E, int in_rows, float* part, int part_cap, hipStream_t s);
