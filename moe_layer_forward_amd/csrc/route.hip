@@ -11,10 +11,11 @@
 // block owns 1 (or 8) tokens x 4 experts, its threads split K in 4-element
 // chunks with the loads of several chunks in flight, and the per-lane partial
 // sums are folded with a transposing wave reduction before a cross-wave sum in
-// LDS.  Larger bf16 batches run on the matrix cores (router_mfma_kernel).  Top-k then runs
-// one wave64 per token: each lane holds up to 4 logits, and k rounds of a
-// shuffle argmax (value descending, expert index ascending on ties) pick the
-// experts.  Selection is made on the fp32 logits (softmax is monotone); the
+// LDS.  Larger bf16 batches run on the matrix cores (router_mfma_kernel; 64 x
+// 64 tiles for large batches with many experts; with at most 16 experts the
+// logits and the top-k share one launch).  Top-k runs one wave64 per token:
+// each lane holds up to 4 logits, and k rounds of a shuffle argmax (value
+// descending, expert index ascending on ties) pick the experts.  Selection is made on the fp32 logits (softmax is monotone); the
 // weights are the softmax of the selected logits, which equals the full
 // softmax renormalised over the selection.
 #include <type_traits>
@@ -183,18 +184,11 @@ __device__ __forceinline__ void split3(const float4& a, const float4& b, rq_u4& 
     }
 }
 
-__global__ __launch_bounds__(64 * RQ_WAVES) void router_mfma_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
-    float* __restrict__ logits, int T, int d, int E) {
-    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane & 15, q = lane >> 4;
-    const int tr = min(t0 + r, T - 1), er = min(e0 + r, E - 1);   // clamped rows: results unused
-    const uint16_t* xrow = x + (size_t)tr * d;
-    const float* wrow = wg + (size_t)er * d;
-    // this wave's K range, in steps of 32 (the last step may be partial: d % 8 == 0)
-    const int nsteps = (d + 31) / 32;
-    const int s0 = nsteps * wave / RQ_WAVES, s1 = nsteps * (wave + 1) / RQ_WAVES;
+// One wave's 16 x 16 tile (tokens of xrow's block x router rows of wrow's
+// block) over K steps [s0, s1) of 32: lane (r, q) loads 8 consecutive K of
+// token row r and of router row r at K = 32 step + 8 q.
+__device__ __forceinline__ rq_f4 router_k_range(const uint16_t* __restrict__ xrow, const float* __restrict__ wrow,
+                                                int s0, int s1, int q, int d) {
     rq_f4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int st = s0; st < s1; st += RQ_U) {
         uint4 xa[RQ_U];
@@ -222,6 +216,20 @@ __global__ __launch_bounds__(64 * RQ_WAVES) void router_mfma_kernel(
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(rq_bf16x8, lo), acc, 0, 0, 0);
         }
     }
+    return acc;
+}
+
+__global__ __launch_bounds__(64 * RQ_WAVES) void router_mfma_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
+    float* __restrict__ logits, int T, int d, int E) {
+    const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, q = lane >> 4;
+    const int tr = min(t0 + r, T - 1), er = min(e0 + r, E - 1);   // clamped rows: results unused
+    // this wave's K range, in steps of 32 (the last step may be partial: d % 8 == 0)
+    const int nsteps = (d + 31) / 32;
+    const int s0 = nsteps * wave / RQ_WAVES, s1 = nsteps * (wave + 1) / RQ_WAVES;
+    const rq_f4 acc = router_k_range(x + (size_t)tr * d, wg + (size_t)er * d, s0, s1, q, d);
     // lane l holds tokens 4(l/16)+v, expert l%16; sum the waves' tiles in order
     __shared__ float part[RQ_WAVES][4][64];
 #pragma unroll
@@ -388,6 +396,42 @@ __device__ __forceinline__ bool better(float v, int i, float v2, int i2) {
 constexpr int TK_MAXPL = 4;   // E <= 256 -> up to 4 logits per lane
 constexpr int TK_MAXK = 16;
 
+// Top-k of one token by one wave: lane l holds logits l + 64 i (live when
+// < E).  k rounds of a shuffle argmax; the owner retires each winner.  Writes
+// the k indices and the softmax of the selected logits (max-subtracted; the
+// first selected is the maximum).  selv: this wave's TK_MAXK floats of LDS.
+__device__ __forceinline__ void topk_wave(float (&v)[TK_MAXPL], bool (&live)[TK_MAXPL], int lane, int k,
+                                          int32_t* __restrict__ idx_row, float* __restrict__ w_row,
+                                          float* selv) {
+    for (int j = 0; j < k; ++j) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < TK_MAXPL; ++i)
+            if (live[i] && better(v[i], lane + 64 * i, bv, bi)) { bv = v[i]; bi = lane + 64 * i; }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            float ov = __shfl_xor(bv, o, MOE_WAVE);
+            int oi = __shfl_xor(bi, o, MOE_WAVE);
+            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+        }
+#pragma unroll
+        for (int i = 0; i < TK_MAXPL; ++i)
+            if (lane + 64 * i == bi) live[i] = false;
+        if (lane == 0) {
+            idx_row[j] = bi;
+            selv[j] = bv;
+        }
+    }
+    if (lane == 0) {
+        const float m = selv[0];
+        float s = 0.f;
+        for (int j = 0; j < k; ++j) s += expf(selv[j] - m);
+        const float inv = 1.0f / s;
+        for (int j = 0; j < k; ++j) w_row[j] = expf(selv[j] - m) * inv;
+    }
+}
+
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                   int32_t* __restrict__ idx,
                                                   float* __restrict__ w, int T, int E, int k) {
@@ -404,35 +448,69 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         float x = live[i] ? logits[(size_t)t * E + e] : -INFINITY;
         v[i] = (x != x) ? -INFINITY : x;
     }
-    for (int j = 0; j < k; ++j) {
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
+    topk_wave(v, live, lane, k, idx + (size_t)t * k, w + (size_t)t * k, selv[wave]);
+}
+
+// Router logits and top-k in one launch for bf16 batches with up to 16
+// experts (the grid of router_mfma_kernel is then one block per 16 tokens
+// anyway): a 1024-thread block owns 16 tokens x all experts.  Its 16 waves
+// split into the ceil(E/16) expert tiles (1, 2 or 4; the kernel takes up to 64
+// experts, but above 16 every block would split the whole router, which the
+// two-launch path spreads over E/16 blocks) times the K ranges that leave;
+// each wave runs the 16 x 16 tile of router_mfma_kernel over its K range, the
+// partial tiles are summed in K-range order in LDS (deterministic), the logits
+// written out, and wave w then selects the top-k of token w with the rule of
+// topk_kernel.
+constexpr int RK_WAVES = 16;
+
+__global__ __launch_bounds__(64 * RK_WAVES) void router_topk_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
+    float* __restrict__ logits, int32_t* __restrict__ idx, float* __restrict__ w, int T, int d, int E, int k) {
+    __shared__ float part[RK_WAVES][4][64];
+    __shared__ float lg[16][64];
+    __shared__ float selv[RK_WAVES][TK_MAXK];
+    const int t0 = blockIdx.x * 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, q = lane >> 4;
+    const int net = E <= 16 ? 1 : (E <= 32 ? 2 : 4);     // expert tiles
+    const int nkr = RK_WAVES / net;                       // K ranges per tile
+    const int et = wave % net, kr = wave / net;
+    const int tr = min(t0 + r, T - 1), er = min(et * 16 + r, E - 1);   // clamped rows: results unused
+    const int nsteps = (d + 31) / 32;
+    const int s0 = nsteps * kr / nkr, s1 = nsteps * (kr + 1) / nkr;
+    const rq_f4 acc = router_k_range(x + (size_t)tr * d, wg + (size_t)er * d, s0, s1, q, d);
 #pragma unroll
-        for (int i = 0; i < TK_MAXPL; ++i)
-            if (live[i] && better(v[i], lane + 64 * i, bv, bi)) { bv = v[i]; bi = lane + 64 * i; }
+    for (int v = 0; v < 4; ++v) part[wave][v][lane] = acc[v];
+    __syncthreads();
+    // wave e' < net sums tile e' over the K ranges in order: lane (r, q)
+    // holds tokens 4q + v of expert 16 e' + r
+    if (wave < net) {
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            float ov = __shfl_xor(bv, o, MOE_WAVE);
-            int oi = __shfl_xor(bi, o, MOE_WAVE);
-            if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-        }
-        // the owner retires the winner
-#pragma unroll
-        for (int i = 0; i < TK_MAXPL; ++i)
-            if (lane + 64 * i == bi) live[i] = false;
-        if (lane == 0) {
-            idx[(size_t)t * k + j] = bi;
-            selv[wave][j] = bv;
+        for (int v = 0; v < 4; ++v) {
+            float sum = part[wave][v][lane];
+            for (int j = 1; j < nkr; ++j) sum += part[wave + j * net][v][lane];
+            const int t = t0 + 4 * q + v, e = wave * 16 + r;
+            if (e < E) {
+                if (bias) sum += bias[e];
+                lg[4 * q + v][e] = sum;
+                if (t < T) logits[(size_t)t * E + e] = sum;
+            }
         }
     }
-    if (lane == 0) {
-        // softmax restricted to the selection, max-subtracted (slot 0 holds the max)
-        const float m = selv[wave][0];
-        float s = 0.f;
-        for (int j = 0; j < k; ++j) s += expf(selv[wave][j] - m);
-        const float inv = 1.0f / s;
-        for (int j = 0; j < k; ++j) w[(size_t)t * k + j] = expf(selv[wave][j] - m) * inv;
+    __syncthreads();
+    const int t = t0 + wave;
+    if (t >= T) return;
+    float v[TK_MAXPL];
+    bool live[TK_MAXPL];
+    live[0] = lane < E;
+    const float xv = live[0] ? lg[wave][lane] : -INFINITY;
+    v[0] = (xv != xv) ? -INFINITY : xv;
+#pragma unroll
+    for (int i = 1; i < TK_MAXPL; ++i) {
+        live[i] = false;
+        v[i] = -INFINITY;
     }
+    topk_wave(v, live, lane, k, idx + (size_t)t * k, w + (size_t)t * k, selv[wave]);
 }
 
 hipError_t launch_route(int act, const void* x, const float* wg, const float* b, float* logits,
@@ -451,6 +529,11 @@ hipError_t launch_route(int act, const void* x, const float* wg, const float* b,
         const dim3 g3((T + RTL_T - 1) / RTL_T, (E + RTL_E - 1) / RTL_E);
         hipLaunchKernelGGL(router_tile_kernel, g3, dim3(RTL_THREADS), 0, s, reinterpret_cast<const uint16_t*>(x), wg, b,
                            logits, T, d, E);
+    } else if (E <= 16) {
+        // logits and top-k in one launch
+        hipLaunchKernelGGL(router_topk_kernel, dim3((T + 15) / 16), dim3(64 * RK_WAVES), 0, s,
+                           reinterpret_cast<const uint16_t*>(x), wg, b, logits, idx, w, T, d, E, k);
+        return hipGetLastError();
     } else {
         const dim3 g2((T + 15) / 16, (E + 15) / 16);
         hipLaunchKernelGGL(router_mfma_kernel, g2, dim3(64 * RQ_WAVES), 0, s,

@@ -192,6 +192,11 @@ ROUTE_WIDE = {
                                        wt="bf16", model="s_route_wide"),
     "route_wide_ragged": moe_inputs.MoEConfig("route_wide_ragged", T=5300, d=264, E=200, k=6, F=128,
                                               act="bf16", wt="bf16", model="s_route_wr"),
+    # logits and top-k in one launch (bf16, T*E >= 4096, E <= 16): a partial
+    # last token tile (T = 1000), a partial expert tile (E = 12) and a K tail
+    # (d = 264: 9 steps of 32 over 16 K ranges, some of them empty)
+    "route_fused_ragged": moe_inputs.MoEConfig("route_fused_ragged", T=1000, d=264, E=12, k=3, F=128,
+                                               act="bf16", wt="bf16", model="s_route_fr"),
 }
 
 
@@ -226,6 +231,21 @@ def test_route_ties_and_degenerate(orc):
     d2 = {"x": x.to(DEV), "w_router": wr[:16].contiguous().to(DEV), "b_router": None}
     L2, idx2, w2 = _route(cfg2, d2)
     _check_route(cfg2, x, wr[:16], None, L2, idx2, w2, orc)
+    # the one-launch bf16 path (T*E >= 4096, E <= 16): exact ties between
+    # duplicated router rows, all-zero tokens, and k = E
+    for E3, k3 in ((16, 4), (16, 16)):
+        cfg3 = moe_inputs.MoEConfig("ties_bf16", T=512, d=64, E=E3, k=k3, F=128, act="bf16", wt="bf16",
+                                    model="ties")
+        x3 = torch.zeros(512, 64)
+        x3[1::2] = torch.randn(256, 64, generator=torch.Generator().manual_seed(3))
+        x3 = x3.to(torch.bfloat16)
+        wr3 = wr[:E3].clone()
+        wr3[9] = wr3[3]
+        d3 = {"x": x3.to(DEV), "w_router": wr3.to(DEV), "b_router": None}
+        L3, idx3, w3 = _route(cfg3, d3)
+        _check_route(cfg3, x3, wr3, None, L3, idx3, w3, orc)
+        assert (idx3[0::2] == np.arange(k3)).all()
+        assert (L3[1::2, 9] == L3[1::2, 3]).all()
 
 
 # --------------------------------------------------------------------- A4
