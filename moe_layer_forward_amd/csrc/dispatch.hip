@@ -8,16 +8,25 @@
 // The pages sort on the host; here the whole step is one GPU workgroup so the
 // layer never leaves the device.
 //
-// gfx950 design: one 1024-thread workgroup (16 wave64s).  The histogram uses
-// LDS integer atomics (order-independent, so deterministic).  One wave scans
-// the E <= 256 bins (4 per lane, a shuffle scan) for the offsets.  Placement walks the assignments
-// in chunks of 1024: inside a wave, the rank of an element among equal keys
-// comes from 8 ballots on the key bits (peer mask, popcount of lower peers);
-// per-(wave, expert) counts go to an LDS table that is scanned wave-major per
-// expert.  The result equals a stable counting sort, bit for bit.  The keys of
-// DP_PF rounds are loaded together up front, so a round does not wait on its
-// own global load.  With plan arguments, wave 0 also writes the grouped
-// GEMM's tile lists once the offsets are known (plan.h).
+// gfx950 design: one 1024-thread workgroup (16 wave64s); wave w owns the
+// contiguous chunk [w C, (w+1) C) of the assignments (C a multiple of 64), so
+// the waves work independently between two barriers:
+//  1. each wave counts the experts of its chunk into its row of a
+//     [wave][expert] LDS table (integer atomics: order-independent);
+//  2. one thread per expert sums its column (the counts) and wave 0 scans
+//     the E <= 256 counts (4 per lane, a shuffle scan) for the offsets; each
+//     expert's column then becomes the start of each wave's run of it
+//     (offset + the counts of the lower waves);
+//  3. each wave walks its chunk in groups of 64 in order: inside a group the
+//     lanes holding the same expert find each other with ballots on the key
+//     bits (peer mask; only the bits E-1 needs), an assignment lands at its
+//     wave's cursor for its expert plus its rank among the lower peers, and
+//     the lowest peer advances the cursor (the wave's own LDS operations stay
+//     in program order).
+// Chunks in wave order, groups in chunk order and ranks in lane order make
+// this the stable counting sort, bit for bit.  With plan arguments, wave 0
+// also writes the grouped GEMM's tile lists once the offsets are known
+// (plan.h).
 #include "common.h"
 #include "kernels.h"
 #include "plan.h"
@@ -27,29 +36,72 @@ namespace moe {
 constexpr int DP_THREADS = 1024;
 constexpr int DP_WAVES = DP_THREADS / 64;
 constexpr int DP_MAXE = 256;
-constexpr int DP_PF = 8;      // rounds of keys loaded together
 
+// Peer mask of this lane's key among the wave's valid lanes (same key); keys
+// below 2^nbits.
+__device__ __forceinline__ uint64_t key_peers(int key, bool valid, int nbits) {
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        if (b >= nbits) break;
+        const bool bit = valid && ((key >> b) & 1);
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    return peers;
+}
+
+// KB: groups of keys a wave holds in registers (all loaded together).  When
+// the wave's chunk fits one such batch, the keys stay in registers from the
+// counting pass to the placement pass.
+template <int KB>
 __global__ __launch_bounds__(DP_THREADS) void dispatch_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ perm, int32_t* __restrict__ inv, int n, int E, MfmaPlanArgs plan) {
+    __shared__ int s_tab[DP_WAVES][DP_MAXE];
     __shared__ int s_cnt[DP_MAXE];
-    __shared__ int s_cursor[DP_MAXE];
-    __shared__ int s_wave[DP_WAVES][DP_MAXE];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // this wave's chunk, in groups of 64 (ngc groups, the same for every wave)
+    const int C = ((n + DP_WAVES - 1) / DP_WAVES + 63) & ~63;
+    const int ngc = C / 64;
+    const int c0 = wave * C, c1 = min(n, c0 + C);
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;      // key bits that can differ
 
-    for (int e = tid; e < DP_MAXE; e += DP_THREADS) s_cnt[e] = 0;
-    for (int i = tid; i < DP_WAVES * DP_MAXE; i += DP_THREADS) (&s_wave[0][0])[i] = 0;
+    for (int i = tid; i < DP_WAVES * DP_MAXE; i += DP_THREADS) (&s_tab[0][0])[i] = 0;
     __syncthreads();
 
-    // 1. histogram
-    for (int a = tid; a < n; a += DP_THREADS) {
-        const int e = idx[a];
-        if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+    int keys[KB];
+    // the keys of KB groups from group g0 of the chunk (invalid: -1)
+    auto load_keys = [&](int g0) {
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            const int i = c0 + 64 * (g0 + u) + lane;
+            const int key = i < c1 ? idx[i] : -1;
+            keys[u] = (key >= 0 && key < E) ? key : -1;
+        }
+    };
+
+    // 1. per-wave counts (LDS integer atomics: order-independent)
+    for (int g0 = 0; g0 < ngc; g0 += KB) {
+        load_keys(g0);
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+            if (g0 + u >= ngc) break;
+            if (keys[u] >= 0) atomicAdd(&s_tab[wave][keys[u]], 1);
+        }
     }
     __syncthreads();
 
-    // 2. exclusive scan over the E bins: wave 0, 4 bins per lane, one barrier
+    // 2. counts, offsets, and each wave's start in each expert's range
+    if (tid < E) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < DP_WAVES; ++w) c += s_tab[w][tid];
+        s_cnt[tid] = c;
+    }
+    __syncthreads();
     if (wave == 0) {
         int c[4], sum = 0;
 #pragma unroll
@@ -72,7 +124,7 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_kernel(
             if (e < E) {
                 counts[e] = c[j];
                 offsets[e] = run;
-                s_cursor[e] = run;
+                s_cnt[e] = run;
             }
             run += c[j];
         }
@@ -80,55 +132,35 @@ __global__ __launch_bounds__(DP_THREADS) void dispatch_kernel(
         if (plan.tiles) mfma_plan_wave(lane, c, o, E, plan);
     }
     __syncthreads();
-
-    // 3. stable placement, 1024 assignments per round
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base0 = 0; base0 < n; base0 += DP_THREADS * DP_PF) {
-        int keys[DP_PF];
+    if (tid < E) {
+        int run = s_cnt[tid];
 #pragma unroll
-        for (int r = 0; r < DP_PF; ++r) {
-            const int a = base0 + r * DP_THREADS + tid;
-            keys[r] = a < n ? idx[a] : -1;
+        for (int w = 0; w < DP_WAVES; ++w) {
+            const int c = s_tab[w][tid];
+            s_tab[w][tid] = run;
+            run += c;
         }
+    }
+    __syncthreads();
+
+    // 3. placement
+    for (int g0 = 0; g0 < ngc; g0 += KB) {
+        if (ngc > KB) load_keys(g0);       // else the keys of pass 1 are still here
 #pragma unroll
-        for (int r = 0; r < DP_PF; ++r) {
-            const int base = base0 + r * DP_THREADS;
-            if (base >= n) break;
-            const int a = base + tid;
-            int key = keys[r];
-            if (key < 0 || key >= E) key = -1;
-            const bool valid = key >= 0;
-            uint64_t peers = __ballot(valid);
-#pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const bool bit = valid && ((key >> b) & 1);
-                const uint64_t m = __ballot(bit);
-                peers &= bit ? m : ~m;
-            }
+        for (int u = 0; u < KB; ++u) {
+            if (g0 + u >= ngc) break;
+            const bool valid = keys[u] >= 0;
+            const uint64_t peers = key_peers(keys[u], valid, nbits);
             const int rank = __popcll(peers & lt_mask);
-            if (valid && rank == 0) s_wave[wave][key] = __popcll(peers);
-            __syncthreads();
-            // per expert: exclusive scan over waves, then advance the cursor
-            if (tid < E) {
-                int run = s_cursor[tid];
-#pragma unroll
-                for (int w = 0; w < DP_WAVES; ++w) {
-                    const int c = s_wave[w][tid];
-                    s_wave[w][tid] = run;
-                    run += c;
-                }
-                s_cursor[tid] = run;
-            }
-            __syncthreads();
             if (valid) {
-                const int pos = s_wave[wave][key] + rank;
-                perm[pos] = a;
-                inv[a] = pos;
+                const int pos = s_tab[wave][keys[u]] + rank;
+                const int i = c0 + 64 * (g0 + u) + lane;
+                perm[pos] = i;
+                inv[i] = pos;
             }
-            __syncthreads();
-            // clear the table for the next round
-            for (int i = tid; i < DP_WAVES * DP_MAXE; i += DP_THREADS) (&s_wave[0][0])[i] = 0;
-            __syncthreads();
+            // every lane of the group has read the cursor (program order
+            // within the wave) before its lowest lane advances it
+            if (valid && rank == 0) s_tab[wave][keys[u]] += __popcll(peers);
         }
     }
 }
@@ -138,8 +170,12 @@ hipError_t launch_dispatch(const int32_t* idx, int32_t* counts, int32_t* offsets
     if (plan && (E > DP_MAXE || plan->tile_mode < MFMA_TILES_BOTH || plan->tile_mode > MFMA_TILES_BIG))
         return hipErrorInvalidValue;
     const MfmaPlanArgs p = plan ? *plan : MfmaPlanArgs{nullptr, 0, 0, 0, 0};
-    hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(DP_THREADS), 0, s, idx, counts, offsets, perm,
-                       inv, T * k, E, p);
+    const int n = T * k;
+    // groups of 64 per wave: up to 8 in one batch, else batches of 32
+    if (n <= DP_WAVES * 64 * 8)
+        hipLaunchKernelGGL(dispatch_kernel<8>, dim3(1), dim3(DP_THREADS), 0, s, idx, counts, offsets, perm, inv, n, E, p);
+    else
+        hipLaunchKernelGGL(dispatch_kernel<32>, dim3(1), dim3(DP_THREADS), 0, s, idx, counts, offsets, perm, inv, n, E, p);
     return hipGetLastError();
 }
 
