@@ -268,6 +268,8 @@ def _dispatch(idx, E, k):
     (16, 2, 8, "random"), (8, 2, 8, "random"), (4096, 2, 8, "zipf"), (64, 8, 256, "random"),
     (512, 6, 64, "random"), (1, 1, 1, "random"), (3, 4, 4, "random"), (1000, 3, 7, "one"),
     (2048, 16, 256, "random"), (5, 2, 200, "random"),
+    # more than 32 groups of 64 per wave: the keys come in several batches
+    (5000, 8, 256, "random"), (9000, 8, 64, "zipf"),
 ])
 def test_dispatch_bit_exact(orc, T, k, E, kind):
     say(f"dispatch T={T} k={k} E={E} {kind}")
