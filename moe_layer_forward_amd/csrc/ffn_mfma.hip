@@ -6,8 +6,9 @@
 // contiguous ([P2] §2.1, expert-affinity scheduling).
 //
 // gfx950 design:
-//  * a device-side plan (one small kernel) turns counts/offsets into a list of
-//    256-row M-tiles, one expert per tile: no host round trip;
+//  * a device-side plan (one wave, plan.h: at the end of the dispatch kernel
+//    inside the layer call, else its own launch) turns counts/offsets into a
+//    list of 256-row M-tiles, one expert per tile: no host round trip;
 //  * a persistent grid of one 512-thread block per CU walks the (M-tile,
 //    N-tile) list.  In every round the 32 CUs of one XCD take 32 consecutive
 //    tiles, and tiles are ordered in groups of 8 M-tiles x all N-tiles with M
@@ -64,8 +65,6 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int MF_BM = kMfmaBigRows;
 constexpr int MF_BN = 256;
 constexpr int MF_BK = 32;         // K per LDS stage
-constexpr int MF_NS = 5;          // LDS stages (copies four K steps ahead)
-constexpr int MF_STAGE = MF_BM * MF_BK;   // elements of one operand stage
 constexpr int MF_GM = 8;          // M-tiles per scheduling group
 constexpr uint32_t MF_OOB = 0x80000000u;   // beyond any buffer: the range check yields 0
 constexpr int kNonTemporal = 2;            // buffer-load cache policy: streamed, not kept
@@ -146,23 +145,6 @@ __device__ __forceinline__ TailSplit tail_split(int W, int G, int nk, int cap) {
     return t;
 }
 
-
-// wait until at most n (0, 8, 16, 24 or 32) vector-memory operations are outstanding
-__device__ __forceinline__ void wait_vm(int n) {
-    if (n >= 32) __builtin_amdgcn_s_waitcnt(0x8F70);        // vmcnt(32)
-    else if (n >= 24) __builtin_amdgcn_s_waitcnt(0x4F78);   // vmcnt(24)
-    else if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
-    else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);    // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0)
-}
-
-// Swizzled element offset of logical 16-byte chunk `ch` (0..3) of tile row
-// `row` in a stage of 32-element (64-byte) rows: four rows share one 256-byte
-// bank line and the chunk is XORed with (row/4)&3, so 16 consecutive rows
-// reading the same logical chunk hit 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row, int ch) {
-    return row * MF_BK + ((ch ^ ((row >> 2) & 3)) << 3);
-}
 
 // Pair slots of the 256-row kernel: K = 64 (two K steps) per 128-byte LDS row,
 // so that every copy instruction moves whole 128-byte lines (8 rows x 128 B).
