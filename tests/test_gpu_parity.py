@@ -430,6 +430,24 @@ def test_layer_int4_tiled(orc, name):
     assert torch.equal(idx, idx_rm) and torch.equal(y, y_rm)
 
 
+@pytest.mark.parametrize("name,tau", [("bf16_small_split", 0), ("bf16_prefill_ragged", 0),
+                                      ("bf16_prefill_stream", 0), ("bf16_prefill_ragged", 16)])
+def test_layer_matches_steps_bitwise(name, tau):
+    """Inside moe_layer_forward the dispatch kernel also writes the grouped
+    GEMM's tile lists; moe_expert_ffn builds them with its own launch.  The
+    lists are the same, so the layer equals the four steps bit for bit, with
+    only 64-row tiles (bf16_small_split), both lists (bf16_prefill_ragged, and
+    with an explicit tau) and only 256-row tiles (bf16_prefill_stream)."""
+    cfg = SMALL[name]
+    say(f"layer vs steps bitwise {name} tau={tau}")
+    d = device_inputs(cfg)
+    y, counts, idx = run_layer(cfg, d, tau=tau)
+    g = _steps(cfg, d, tau=tau)
+    assert np.array_equal(idx.cpu().numpy(), g["idx"])
+    assert np.array_equal(counts.cpu().numpy(), g["counts"])
+    assert np.array_equal(np_f64(y), g["y"])
+
+
 def test_residual_and_determinism(orc):
     cfg = SMALL["bf16_prefill_ragged"]
     say("residual + determinism")
