@@ -286,7 +286,7 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
         if (rc) return rc;
     }
     if (use_dq) {
-        rc = hip_check(launch_dq_plan(counts, offsets, s->E, dqt, dq_staged, tiles, dq_mt, st), st, "dq plan", err,
+        rc = hip_check(launch_dq_plan(counts, offsets, s->E, dqt, dqf, dq_staged, tiles, dq_mt, st), st, "dq plan", err,
                        err_len);
         if (rc) return rc;
     }

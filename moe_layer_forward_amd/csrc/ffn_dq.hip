@@ -332,8 +332,12 @@ template <int F>
 struct DtFmt {
     static constexpr int KS = F == DT_FP8 ? 64 : 128;          // K per stage
     static constexpr int SUB = KS / 64;                        // 64-K sub-stages
+    // token rows of a tile: 128 with fp8 codes (a stage's tokens are half the
+    // 4-bit stage's, so three stages of 128 rows still fit), else 64
+    static constexpr int BM = F == DT_FP8 ? 2 * DT_BM : DT_BM;
+    static constexpr int TT = BM / 32;                         // 32-token MFMA fragments
     static constexpr int TROW = KS * 2;                        // token bytes per row and stage
-    static constexpr int TOK = DT_BM * TROW;                   // token bytes of a stage
+    static constexpr int TOK = BM * TROW;                      // token bytes of a stage
     static constexpr int STAGE = TOK + DT_WST;
     static constexpr int TCOPY = TOK / 1024 / 8;               // token copies per wave and stage
     static constexpr int BASE = TCOPY + DT_WST / 1024 / 8;     // token + code copies per wave and stage
@@ -420,7 +424,7 @@ template <int MODE, int F>
 __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
     using Fm = DtFmt<F>;
     constexpr int BASE = Fm::BASE;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[DT_NS * Fm::STAGE + DT_SW * DT_BN * 8 + 256];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[DT_NS * Fm::STAGE + DT_SW * DT_BN * 8 + Fm::BM * 4];
     uint8_t* const sc_base = smem + DT_NS * Fm::STAGE;
     const int32_t* const s_perm = reinterpret_cast<const int32_t*>(sc_base + DT_SW * DT_BN * 8);
 
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
     uint32_t t_off[Fm::TCOPY], w_off[4], s_off[2];
     int32x4_t RW[2], RS[2];                    // gate (or down) and up codes and scales of the task's expert
     auto token_row = [&](int i) {
-        return F == DT_FP8 ? 8 * wave + (lane >> 3) : 8 * wave + 4 * i + (lane >> 4);
+        return F == DT_FP8 ? 8 * (Fm::TCOPY * wave + i) + (lane >> 3) : 8 * wave + 4 * i + (lane >> 4);
     };
     auto set_task = [&](int t) {
         int mt;
@@ -522,8 +526,9 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
                      lds_addr(sc_base + ws * DT_BN * 8 + (64 * wave + 32 * i) * 8));
             n += 2;
         }
-        if (MODE == 0 && perm_p0 >= 0 && wave == 0) {
-            dma4(RP, (uint32_t)(perm_p0 + lane) * 4u, lds_addr(s_perm));
+        if (MODE == 0 && perm_p0 >= 0 && wave < Fm::BM / 64) {
+            // the next task's BM dispatch entries, 64 per wave of the first BM/64
+            dma4(RP, (uint32_t)(perm_p0 + 64 * wave + lane) * 4u, lds_addr(s_perm + 64 * wave));
             ++n;
         }
         uint8_t* stage = smem + st * Fm::STAGE;
@@ -531,7 +536,7 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
         for (int i = 0; i < Fm::TCOPY; ++i) {
             c_desc[i] = RA;
             c_off[i] = t_off[i] == DQ_OOB ? DQ_OOB : t_off[i] + (uint32_t)kb * Fm::TROW;
-            c_lds[i] = lds_addr(stage + (8 * wave + (F == DT_FP8 ? 0 : 4 * i)) * Fm::TROW);
+            c_lds[i] = lds_addr(stage + (F == DT_FP8 ? 8 * (Fm::TCOPY * wave + i) : 8 * wave + 4 * i) * Fm::TROW);
         }
         const int m = MODE == 0 && wave >= 4 ? 1 : 0;
 #pragma unroll
@@ -596,9 +601,9 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
         lr[ni] = MODE == 0 ? ni * (DT_BN / 2) + 32 * wave + r32 : 64 * wave + 32 * ni + r32;
-    dq_floatx16 acc[2][2];                          // [token fragment][weight fragment]
+    dq_floatx16 acc[Fm::TT][2];                     // [token fragment][weight fragment]
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < Fm::TT; ++t)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
@@ -647,25 +652,24 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
             return *reinterpret_cast<const dq_bf16x8_t*>(tok + T * Fm::TROW + ((ch ^ sw) << 4));
         };
         read_codes(0);
-        dq_bf16x8_t tf[3][2];                       // token fragments, read two steps ahead
+        dq_bf16x8_t tf[3][Fm::TT];                  // token fragments, read two steps ahead
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            tf[j][0] = read_tok(j, 0);
-            tf[j][1] = read_tok(j, 1);
-        }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int t = 0; t < Fm::TT; ++t) tf[j][t] = read_tok(j, t);
 #pragma unroll
         for (int j = 0; j < STEPS; ++j) {
             const int b = j >> 2, s4 = j & 3;
             if (j + 2 < STEPS) {
-                tf[(j + 2) % 3][0] = read_tok(j + 2, 0);
-                tf[(j + 2) % 3][1] = read_tok(j + 2, 1);
+#pragma unroll
+                for (int t = 0; t < Fm::TT; ++t) tf[(j + 2) % 3][t] = read_tok(j + 2, t);
             }
             if (Fm::SUB > 1 && j == 1) read_codes(1);
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni) {
                 const dq_bf16x8_t wf = dt_widen<F>(c[b][ni], c2[b][ni], s4, scale[b][ni]);
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
+                for (int t = 0; t < Fm::TT; ++t)
                     acc[t][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, tf[j % 3][t], acc[t][ni], 0, 0, 0);
             }
             // copies [j BASE / STEPS, (j + 1) BASE / STEPS) go out after step j
@@ -686,7 +690,7 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
         task_tile(task, mt, nt);
         const int p0 = tl[max_mt + mt], rows = tl[2 * max_mt + mt];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < Fm::TT; ++t) {
             const int tr = 32 * t + r32;
             if (tr < rows) {
                 const size_t orow = (size_t)(p0 + tr) * N;
@@ -716,7 +720,7 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
             }
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < Fm::TT; ++t)
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
@@ -815,12 +819,15 @@ bool dq_staged_ok(int fmt, int gs, int K) {
     return !(fmt == DQ_INT4 && gs == 128 && K % 256 != 0);
 }
 
-int dq_tile_rows(bool staged) { return staged ? DT_BM : DQ_BM; }
+int dq_tile_rows(int fmt, bool staged) {
+    if (!staged) return DQ_BM;
+    return fmt == DQ_MXFP8 ? DtFmt<DT_FP8>::BM : DT_BM;
+}
 
-hipError_t launch_dq_plan(const int32_t* counts, const int32_t* offsets, int E, int tau, bool staged,
+hipError_t launch_dq_plan(const int32_t* counts, const int32_t* offsets, int E, int tau, int fmt, bool staged,
                           int32_t* tiles, int max_mt, hipStream_t s) {
     if (E > 256) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(dq_plan_kernel, dim3(1), dim3(256), 0, s, counts, offsets, E, tau, dq_tile_rows(staged),
+    hipLaunchKernelGGL(dq_plan_kernel, dim3(1), dim3(256), 0, s, counts, offsets, E, tau, dq_tile_rows(fmt, staged),
                        tiles, max_mt);
     return hipGetLastError();
 }

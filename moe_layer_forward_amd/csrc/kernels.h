@@ -68,14 +68,14 @@ hipError_t launch_skinny(int mode, const void* w0, const void* w1, const void* i
 // Quantised expert weights on the matrix cores (ffn_dq.hip): int4 (fmt 0,
 // group size gs = 64 or 128, fp16 scales), MXFP4 (1) or MXFP8 (2) with E8M0
 // scales per 32; the experts with more than tau rows, in tiles of
-// dq_tile_rows(staged) rows.  staged: the LDS-staged kernel, for passes whose
-// K dq_staged_ok accepts (both passes of a layer use the same plan).
+// dq_tile_rows(fmt, staged) rows.  staged: the LDS-staged kernel, for passes
+// whose K dq_staged_ok accepts (both passes of a layer use the same plan).
 int dq_max_tiles(int T, int k, int E);
 int dq_plan_ints(int T, int k, int E);
 bool dq_supported(int K, int N);
 bool dq_staged_ok(int fmt, int gs, int K);
-int dq_tile_rows(bool staged);
-hipError_t launch_dq_plan(const int32_t* counts, const int32_t* offsets, int E, int tau, bool staged,
+int dq_tile_rows(int fmt, bool staged);
+hipError_t launch_dq_plan(const int32_t* counts, const int32_t* offsets, int E, int tau, int fmt, bool staged,
                           int32_t* tiles, int max_mt, hipStream_t s);
 hipError_t launch_dq_ffn(int mode, int fmt, int gs, bool staged, const void* w0, const void* w1, const void* s0,
                          const void* s1, const void* in, void* out, const int32_t* perm, const int32_t* tiles, int N,

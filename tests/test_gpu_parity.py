@@ -146,6 +146,16 @@ SMALL = {
     "mxfp8_staged": moe_inputs.MoEConfig(
         "mxfp8_staged", T=1024, d=512, E=4, k=2, F=2048, act="bf16", wt="mxfp8",
         model="s_mxfp8_st", w_std=0.05),
+    # MXFP8 tiles hold 128 token rows: groups of ~100 rows (one partial tile)
+    # next to groups above 128 (a ragged second tile) ...
+    "mxfp8_staged_ragged": moe_inputs.MoEConfig(
+        "mxfp8_staged_ragged", T=300, d=512, E=6, k=2, F=1024, act="bf16", wt="mxfp8",
+        model="s_mxfp8_sr", w_std=0.05),
+    # ... and more gate/up tasks (32 M-tiles x 16 N-tiles) than blocks, so the
+    # copy stream runs from one 128-row task into the next
+    "mxfp8_staged_stream": moe_inputs.MoEConfig(
+        "mxfp8_staged_stream", T=2048, d=256, E=4, k=2, F=4096, act="bf16", wt="mxfp8",
+        model="s_mxfp8_ss", w_std=0.05),
     # int4 with K above 8192 on the GEMV (gate/up K = 9216, not a multiple of
     # 1024 times at most 8); down K = 512 also on the GEMV
     "int4_wide_gemv": moe_inputs.MoEConfig(
