@@ -328,13 +328,16 @@ constexpr int DT_WST = DT_BN * 64;  // code bytes of a stage (32 KB)
 
 enum { DT_I4G128 = 0, DT_I4G64 = 1, DT_FP4 = 2, DT_FP8 = 3 };
 
-template <int F>
+template <int F, bool WIDE>
 struct DtFmt {
     static constexpr int KS = F == DT_FP8 ? 64 : 128;          // K per stage
     static constexpr int SUB = KS / 64;                        // 64-K sub-stages
-    // token rows of a tile: 128 with fp8 codes (a stage's tokens are half the
-    // 4-bit stage's, so three stages of 128 rows still fit), else 64
-    static constexpr int BM = F == DT_FP8 ? 2 * DT_BM : DT_BM;
+    // token rows of a tile: 128 (WIDE) or 64.  Stages in LDS: three (copies
+    // two stages ahead), or two (one ahead) for 128 rows of 4-bit stages,
+    // whose tokens take twice the fp8 stage's bytes
+    static constexpr int BM = WIDE ? 2 * DT_BM : DT_BM;
+    static constexpr int NS = (WIDE && F != DT_FP8) ? 2 : DT_NS;
+    static constexpr int AHEAD = NS - 1;
     static constexpr int TT = BM / 32;                         // 32-token MFMA fragments
     static constexpr int TROW = KS * 2;                        // token bytes per row and stage
     static constexpr int TOK = BM * TROW;                      // token bytes of a stage
@@ -420,12 +423,12 @@ __device__ __forceinline__ void dt_wait(int n) {
     else wait_vmcnt<B + 3>();
 }
 
-template <int MODE, int F>
+template <int MODE, int F, bool WIDE>
 __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
-    using Fm = DtFmt<F>;
+    using Fm = DtFmt<F, WIDE>;
     constexpr int BASE = Fm::BASE;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[DT_NS * Fm::STAGE + DT_SW * DT_BN * 8 + Fm::BM * 4];
-    uint8_t* const sc_base = smem + DT_NS * Fm::STAGE;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Fm::NS * Fm::STAGE + DT_SW * DT_BN * 8 + Fm::BM * 4];
+    uint8_t* const sc_base = smem + Fm::NS * Fm::STAGE;
     const int32_t* const s_perm = reinterpret_cast<const int32_t*>(sc_base + DT_SW * DT_BN * 8);
 
     const int tid = threadIdx.x;
@@ -459,17 +462,20 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
         nt = rem / gsz;
     };
 
-    // ---- copy side.  Wave w copies token rows 8 w .. +7, weight rows
+    // ---- copy side.  Wave w copies token rows BM/8 w .. +BM/8-1, weight rows
     // 64 w .. +63 (LDS order: gate/up 256 gate rows, then 256 up rows) and
     // their scale windows.  Per task: the lane parts of every copy offset.
-    // Token copy i: 4-bit stages, rows 8w + 4i + l/16 with 16 chunks per row;
-    // fp8 stages, rows 8w + l/8 with 8 chunks.  Code copy i: rows
+    // Token copy i: 4-bit stages, rows BM/8 w + 4i + l/16 with 16 chunks per
+    // row; fp8 stages, rows BM/8 w + 8i + l/8 with 8 chunks.  Code copy i: rows
     // 64w + 16i + l/4, 4 chunks.  Scale copy i: rows 64w + 32i + l/2, dword l%2.
     int i_e = 0, i_nt = 0, i_rows = 0, i_p0 = 0;
     uint32_t t_off[Fm::TCOPY], w_off[4], s_off[2];
     int32x4_t RW[2], RS[2];                    // gate (or down) and up codes and scales of the task's expert
+    // token rows BM/8 w .. +BM/8-1 of wave w: copy i holds 8 rows of 128
+    // bytes (fp8 stages) or 4 rows of 256 bytes (4-bit stages)
+    constexpr int RPW = Fm::BM / 8;
     auto token_row = [&](int i) {
-        return F == DT_FP8 ? 8 * (Fm::TCOPY * wave + i) + (lane >> 3) : 8 * wave + 4 * i + (lane >> 4);
+        return F == DT_FP8 ? RPW * wave + 8 * i + (lane >> 3) : RPW * wave + 4 * i + (lane >> 4);
     };
     auto set_task = [&](int t) {
         int mt;
@@ -536,7 +542,7 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
         for (int i = 0; i < Fm::TCOPY; ++i) {
             c_desc[i] = RA;
             c_off[i] = t_off[i] == DQ_OOB ? DQ_OOB : t_off[i] + (uint32_t)kb * Fm::TROW;
-            c_lds[i] = lds_addr(stage + (F == DT_FP8 ? 8 * (Fm::TCOPY * wave + i) : 8 * wave + 4 * i) * Fm::TROW);
+            c_lds[i] = lds_addr(stage + (RPW * wave + (F == DT_FP8 ? 8 * i : 4 * i)) * Fm::TROW);
         }
         const int m = MODE == 0 && wave >= 4 ? 1 : 0;
 #pragma unroll
@@ -586,7 +592,7 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
         const int ws = i_win % DT_SW;
         if (i_kb % Fm::WIN == 0) ++i_win;
         const int n = issue(i_kb, i_st, ws, perm_p0);
-        i_st = i_st + 1 == DT_NS ? 0 : i_st + 1;
+        i_st = i_st + 1 == Fm::NS ? 0 : i_st + 1;
         if (++i_kb == NKB) {
             i_kb = 0;
             i_task += nblk;
@@ -727,21 +733,23 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
                 for (int v = 0; v < 16; ++v) acc[t][ni][v] = 0.f;
     };
 
-    // ---- the stream: stage g is prepared at step g - 2 and its token and
-    // code copies go out during step g - 2's MFMAs (the prologue issues
-    // stages 0 and 1 at once).  Step g: this wave's copies of stage g have
-    // landed once at most the newest group (stage g + 1) is outstanding; the
-    // barrier then publishes stage g to every wave and tells that everyone is
-    // done with stage g - 1, whose slot receives stage g + 2.
-    issue_next(-1);
+    // ---- the stream: stage g is prepared at step g - AHEAD and its token and
+    // code copies go out during that step's MFMAs (the prologue issues the
+    // first AHEAD stages at once).  Step g: this wave's copies of stage g have
+    // landed once at most the newer groups (stage g + 1 with AHEAD = 2, none
+    // with AHEAD = 1) are outstanding; the barrier then publishes stage g to
+    // every wave and tells that everyone is done with stage g - 1, whose slot
+    // receives stage g + AHEAD.
+    int n_prev = 0;
 #pragma unroll
-    for (int i = 0; i < BASE; ++i) fire(i);
-    int n_prev = issue_next(-1);
+    for (int p = 0; p < Fm::AHEAD; ++p) {
+        n_prev = issue_next(-1);
 #pragma unroll
-    for (int i = 0; i < BASE; ++i) fire(i);
+        for (int i = 0; i < BASE; ++i) fire(i);
+    }
     int c_task = slot, c_kb = 0, c_st = 0, c_win = 0;
     for (;;) {
-        dt_wait<BASE>(n_prev);
+        dt_wait<BASE>(Fm::AHEAD == 2 ? n_prev : 0);
         block_barrier();
         // at a task's first stage the next task's dispatch entries go out
         // with this group; they are read when the copy side reaches that task
@@ -754,7 +762,7 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
         n_prev = issue_next(pp);
         if (c_kb % Fm::WIN == 0) ++c_win;
         compute(c_st, (c_win - 1) % DT_SW, c_kb);
-        c_st = c_st + 1 == DT_NS ? 0 : c_st + 1;
+        c_st = c_st + 1 == Fm::NS ? 0 : c_st + 1;
         if (++c_kb == NKB) {
             epilogue(c_task);
             c_kb = 0;
@@ -819,9 +827,16 @@ bool dq_staged_ok(int fmt, int gs, int K) {
     return !(fmt == DQ_INT4 && gs == 128 && K % 256 != 0);
 }
 
+// Token rows of the staged kernel's tiles: 128 for MXFP8 (three stages) and
+// int4 (two stages; int4 widening is VALU-bound, and each widened fragment
+// then feeds four token fragments: 5.48 -> 4.75 ms on the fine-grained int4
+// prefill layer), 64 for MXFP4 (with 128 rows its registers spill and the
+// layer measured 1.6% slower).
+static bool dq_wide(int fmt) { return fmt != DQ_MXFP4; }
+
 int dq_tile_rows(int fmt, bool staged) {
     if (!staged) return DQ_BM;
-    return fmt == DQ_MXFP8 ? DtFmt<DT_FP8>::BM : DT_BM;
+    return dq_wide(fmt) ? 2 * DT_BM : DT_BM;
 }
 
 hipError_t launch_dq_plan(const int32_t* counts, const int32_t* offsets, int E, int tau, int fmt, bool staged,
@@ -860,7 +875,8 @@ hipError_t launch_dq_ffn(int mode, int fmt, int gs, bool staged, const void* w0,
         const long cap = cu_count();
         const int grid = (int)(slots < cap ? slots : cap);
         const int f = fmt == DQ_MXFP4 ? DT_FP4 : fmt == DQ_MXFP8 ? DT_FP8 : (gs == 128 ? DT_I4G128 : DT_I4G64);
-#define DT_LAUNCH(M, F) hipLaunchKernelGGL((dq_tile_kernel<M, F>), dim3(grid), dim3(DT_THREADS), 0, s, a)
+        // the tile height dq_wide gives each format (the plan used the same)
+#define DT_LAUNCH(M, F) hipLaunchKernelGGL((dq_tile_kernel<M, F, F != DT_FP4>), dim3(grid), dim3(DT_THREADS), 0, s, a)
 #define DT_FMTS(M)                               \
         switch (f) {                             \
             case DT_I4G128: DT_LAUNCH(M, DT_I4G128); break; \

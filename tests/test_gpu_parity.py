@@ -140,6 +140,11 @@ SMALL = {
     "int4g64_staged": moe_inputs.MoEConfig(
         "int4g64_staged", T=160, d=512, E=4, k=2, F=1024, act="bf16", wt="int4g64",
         model="s_i4g64_st", n_shared=1, w_std=0.05),
+    # int4 tiles hold 128 token rows with two stages in LDS: more gate/up tasks
+    # (24 M-tiles x 16 N-tiles) than blocks, ragged 128-row tiles
+    "int4g64_staged_stream": moe_inputs.MoEConfig(
+        "int4g64_staged_stream", T=1536, d=512, E=4, k=2, F=4096, act="bf16", wt="int4g64",
+        model="s_i4g64_ss", w_std=0.05),
     "mxfp4_staged": moe_inputs.MoEConfig(
         "mxfp4_staged", T=200, d=1024, E=6, k=2, F=512, act="bf16", wt="mxfp4",
         model="s_mxfp4_st", n_shared=1, w_std=0.05),
