@@ -589,6 +589,11 @@ SINGLE_LIST = {
     "big_only": moe_inputs.MoEConfig(
         "big_only", T=1024, d=320, E=4, k=2, F=384, act="bf16", wt="bf16",
         model="s_big_only", w_std=0.05),
+    # 64-row tiles with a K tail in both passes (d = 264 and F = 200: the last
+    # K pair holds one 8-element chunk) and N not a multiple of the tile width
+    "small_only_ktail": moe_inputs.MoEConfig(
+        "small_only_ktail", T=256, d=264, E=16, k=4, F=200, act="bf16", wt="bf16",
+        model="s_small_kt", w_std=0.05),
 }
 
 
@@ -606,7 +611,7 @@ def test_single_tile_list(orc, name):
     W, S = oracle_weights(d)
     wr = np_store(d["w_router"])
     cases = [(cfg.T, np.zeros(cfg.E, np.float32))]
-    if name == "small_only":
+    if name.startswith("small_only"):
         for TT in (129, 200, 256):
             b = np.zeros(cfg.E, np.float32)
             b[0] = 1e3
@@ -628,7 +633,7 @@ def test_single_tile_list(orc, name):
         say(f"  T={TT} counts {cl} max rel {err:.3g}")
         assert err < TOL["bf16"]
         assert np.array_equal(np.asarray(cl), np.bincount(gi.ravel(), minlength=cfg.E))
-    if name == "small_only":
+    if name.startswith("small_only"):
         assert max(seen[0]) <= 128 and [c[0] for c in seen[1:]] == [129, 200, 256]
     else:
         assert min(seen[0]) > 128 and min(c[3] for c in seen[1:]) < 128
