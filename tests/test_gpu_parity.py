@@ -114,6 +114,34 @@ SMALL = {
     "f32_shared": moe_inputs.MoEConfig(
         "f32_shared", T=20, d=128, E=4, k=2, F=96, act="f32", wt="f32", model="s_f32_sh",
         n_shared=1),
+    # the shape limits moe.h states: k = 16 of E = 256; d and F at 16384 for
+    # bf16 and the quantised formats (bf16 gate/up on the GEMV variant with two
+    # tokens per pass, K from 8192 to 16384; int4 on the GEMV, K above the int4
+    # matrix-core kernel's 8192, one K of a multiple of 1024 and one not; MXFP8
+    # on the dequantising GEMM), at 8192 for fp32, and bf16 groups on the
+    # 256-row tiles with K = 16384 in one projection or the other
+    "limit_k16_e256": moe_inputs.MoEConfig(
+        "limit_k16_e256", T=24, d=128, E=256, k=16, F=64, act="bf16", wt="bf16", model="s_lim_k16"),
+    "limit_bf16_d16384": moe_inputs.MoEConfig(
+        "limit_bf16_d16384", T=6, d=16384, E=3, k=2, F=64, act="bf16", wt="bf16", model="s_lim_bd"),
+    "limit_bf16_f16384": moe_inputs.MoEConfig(
+        "limit_bf16_f16384", T=6, d=64, E=3, k=2, F=16384, act="bf16", wt="bf16", model="s_lim_bf"),
+    "limit_bf16_d16384_tiles": moe_inputs.MoEConfig(
+        "limit_bf16_d16384_tiles", T=320, d=16384, E=2, k=1, F=64, act="bf16", wt="bf16", model="s_lim_bdt"),
+    "limit_bf16_f16384_tiles": moe_inputs.MoEConfig(
+        "limit_bf16_f16384_tiles", T=320, d=64, E=2, k=1, F=16384, act="bf16", wt="bf16", model="s_lim_bft"),
+    "limit_f32_d8192": moe_inputs.MoEConfig(
+        "limit_f32_d8192", T=5, d=8192, E=3, k=2, F=32, act="f32", wt="f32", model="s_lim_fd"),
+    "limit_f32_f8192": moe_inputs.MoEConfig(
+        "limit_f32_f8192", T=5, d=32, E=3, k=2, F=8192, act="f32", wt="f32", model="s_lim_ff"),
+    "limit_int4_d16384": moe_inputs.MoEConfig(
+        "limit_int4_d16384", T=6, d=16384, E=3, k=2, F=128, act="bf16", wt="int4", model="s_lim_id"),
+    "limit_int4_f16384": moe_inputs.MoEConfig(
+        "limit_int4_f16384", T=6, d=128, E=3, k=2, F=16384, act="bf16", wt="int4", model="s_lim_if"),
+    "limit_int4_d16256": moe_inputs.MoEConfig(
+        "limit_int4_d16256", T=6, d=16256, E=3, k=2, F=256, act="bf16", wt="int4", model="s_lim_id2"),
+    "limit_mxfp8_d16384": moe_inputs.MoEConfig(
+        "limit_mxfp8_d16384", T=6, d=16384, E=3, k=2, F=64, act="bf16", wt="mxfp8", model="s_lim_md"),
     # quantised groups above the skinny kernels' range on the dequantising
     # grouped GEMM: int4-g128 groups of ~150 rows and a shared expert over all
     # 300 tokens on the LDS-staged kernel (K = 1024, 64-row tiles); every group
