@@ -257,14 +257,16 @@ class OracleTimer:
             busy = self.threads
             order = np.random.default_rng(0).permutation(cfg.T).tolist()
             value, done, calls, el = self.rate(order, busy, target_s, busy)
-            desc = (f"{cfg.name}: {done} of its {cfg.T} tokens (a fixed seeded random order, {busy} per "
-                    f"call), the whole layer per token (router, top-{cfg.k}, SwiGLU experts, weighted "
-                    f"sum), fp64 ({el:.1f} s)")
+            which = (f"{done} of its {cfg.T} tokens" if done <= cfg.T else
+                     f"{done} tokens (its {cfg.T}, then again from the start)")
+            desc = (f"{cfg.name}: {which} in a fixed seeded random order, {busy} per call, the whole "
+                    f"layer per token (router, top-{cfg.k}, SwiGLU experts, weighted sum), fp64 "
+                    f"({el:.1f} s)")
         v1, d1, _, e1 = self.rate(list(range(cfg.T)), single_thread_tokens, 0.0, 1, max_calls=1)
         return {"value": round(value, 3), "unit": "tokens/s", "cores": busy, "kind": "oracle",
                 "sample": desc, "threads_available": self.threads, "cpu_model": cpu_model(),
                 "single_thread_value": round(v1, 3),
-                "single_thread_sample": f"{d1} tokens on one thread ({e1:.1f} s)"}
+                "single_thread_sample": f"{d1} token{'s' if d1 > 1 else ''} on one thread ({e1:.1f} s)"}
 
 
 # kernel sources of each workload's expert-FFN step: the committed counter
@@ -437,12 +439,64 @@ class Ceilings:
         return self.v[kind]
 
 
-def stack_leg(steps, warmup):
+def stack_oracle_baseline(cfg, inp, hs, nrms, target_s=10.0):
+    """The oracle (oracle/, test infrastructure) through the stack's layers on a
+    fixed seeded random order of its tokens, one token per thread per call:
+    per layer the RMSNorm and the layer (router, top-k, SwiGLU experts,
+    weighted sum, residual), each layer on the GPU's own input to it (the
+    norm's input h_l and the normed rows of the last timed step), so the calls
+    need no GPU-side state.  Plus one token through the layers on one thread."""
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.num_threads()
+    H = [_np_store(h) for h in hs[:cfg.layers]]
+    N = [_np_store(n) for n in nrms]
+    Ls = []
+    for l in range(cfg.layers):
+        L = inp["layers"][l]
+        Ls.append(({n: _np_store(L[n]) for n in ("w_gate", "w_up", "w_down")} | {"s_gate": None, "s_up": None,
+                                                                              "s_down": None},
+                   _np_store(L["w_router"]), inp["gamma"][l].numpy().astype(np.float32)))
+
+    def run(sel):
+        for l, (W, wr, g) in enumerate(Ls):
+            oracle.rmsnorm(H[l][sel], cfg.act, g, inp["eps"])
+            oracle.layer_forward(N[l], cfg.act, cfg.wt, cfg.k, wr, None, W, None, residual=H[l], sel=sel)
+
+    order = np.random.default_rng(0).permutation(cfg.T).astype(np.int32)
+    oracle.set_num_threads(threads)
+    done, calls, i, t0 = 0, 0, 0, time.perf_counter()
+    while True:
+        sel = np.array([order[(i + j) % cfg.T] for j in range(threads)], np.int32)
+        i += threads
+        run(sel)
+        done += threads
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or calls >= 50:
+            break
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    run(order[:1].copy())
+    e1 = time.perf_counter() - t1
+    oracle.set_num_threads(threads)
+    return {"value": round(done / el, 3), "unit": "tokens/s through the 4-layer stack", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"stack4: {done} of its {cfg.T} tokens (a fixed seeded random order, {threads} per call) "
+                       f"through {cfg.layers} layers (RMSNorm, then router, top-{cfg.k}, SwiGLU experts, "
+                       f"weighted sum and residual), each layer on the GPU's input to it, fp64 ({el:.1f} s)"),
+            "threads_available": threads, "cpu_model": cpu_model(),
+            "single_thread_value": round(1.0 / e1, 3),
+            "single_thread_sample": f"1 token through {cfg.layers} layers on one thread ({e1:.1f} s)"}
+
+
+def stack_leg(steps, warmup, cpu=False):
     """The 4-layer pre-norm stack (T=512, d=2048, E=64, top-6, F=1408, bf16):
     per layer h_{l+1} = h_l + MoE_l(rmsnorm(h_l)), as moe_rmsnorm then
     moe_layer_forward with the residual.  Times the whole stack (a step is the
     4 layers) with a HIP event between layers, and returns the per-layer usage
-    histogram (layer, expert, count) of the last step."""
+    histogram (layer, expert, count) of the last step; with cpu, the oracle
+    timed beside it on the host."""
     cfg = moe_inputs.CONFIGS["stack4"]
     log("generating the 4-layer stack on the GPU")
     inp = moe_inputs.generate(cfg, seed=0, device=DEV)
@@ -512,12 +566,25 @@ def stack_leg(steps, warmup):
                            "expert_ffn_bytes": nbytes, "GBps_over_layer": round(gbs, 1),
                            "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4)})
     ms = wall * 1e3 / steps
-    return {"workload": "stack4", "T": cfg.T, "layers": cfg.layers,
+    cpu_obj = None
+    if cpu:
+        log("cpu baseline: oracle through the stack's layers")
+        nrms = []
+        for l in range(cfg.layers):
+            n_l = torch.empty_like(nrm)
+            moe.moe_rmsnorm(nshape, hs[l], gammas[l], inp["eps"], n_l, stream=st)
+            nrms.append(n_l)
+        torch.cuda.synchronize()
+        cpu_obj = stack_oracle_baseline(cfg, inp, hs, nrms)
+    out = {"workload": "stack4", "T": cfg.T, "layers": cfg.layers,
             "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s through the 4-layer stack",
             "ms_per_step": round(ms, 5), "ms_per_step_median": round(float(np.median(stack)), 5),
             "ms_per_step_p99": round(float(np.percentile(stack, 99)), 5), "steps": steps, "warmup": warmup,
             "per_layer": layer_objs, "usage_histogram": counts, "usage_lines": len(lines),
             "next_layer_prediction": pilot}
+    if cpu_obj is not None:
+        out["cpu_baseline"] = cpu_obj
+    return out
 
 
 def low_latency_leg(dcfg, wr, W, orc=None, steps=200, warmup=20):
@@ -662,7 +729,7 @@ def main():
     steps, warmup = args.steps, args.warmup
 
     if args.workload == "stack4":
-        out = stack_leg(steps, warmup)
+        out = stack_leg(steps, warmup, cpu=not args.no_cpu_baseline)
         print(json.dumps(out), flush=True)
         return
 
@@ -740,6 +807,11 @@ def main():
         irun = Runner(icfg, ix, iwr, ibr, iWt, tau=args.tau, wt="int4_tiled")
         ileg = workload_leg(irun, steps, warmup, args.tau, ceilings, icfg.name if args.tau == 0 else None)
         out["int4_decode"] = leg_summary(icfg, ileg, steps, warmup)
+        if not args.no_cpu_baseline:
+            log("cpu baseline: oracle on the int4 decode layer (row-major codes)")
+            iorc = OracleTimer(icfg, irun, iW)
+            out["int4_decode"]["cpu_baseline"] = iorc.baseline(sample=True, single_thread_tokens=1)
+            del iorc
         log(json.dumps(out["int4_decode"]))
         del irun, iWt
         torch.cuda.empty_cache()
@@ -759,7 +831,7 @@ def main():
             del qrun, qW, qx
             torch.cuda.empty_cache()
         del iW
-        out["stack4"] = stack_leg(steps, warmup)
+        out["stack4"] = stack_leg(steps, warmup, cpu=not args.no_cpu_baseline)
         log(json.dumps(out["stack4"]))
     print(json.dumps(out), flush=True)
 
