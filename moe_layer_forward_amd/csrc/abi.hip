@@ -128,6 +128,13 @@ struct Layout {
 bool is_int4(const moe_shape* s) { return s->wt == MOE_INT4_G128 || s->wt == MOE_INT4_G128_TILED; }
 
 constexpr int kDefaultInt4Tau = 32;
+// int4-g128 groups on the dequantising GEMM: a last partial 128-row tile of at
+// most this many rows goes to the skinny int4 kernel instead.  Such a tile
+// would stream and widen its expert's whole weight matrix for a few rows
+// (~11 us of the whole GPU per tile at the fine-grained shape, d = 7168,
+// F = 2048); the skinny kernel streams it at the HBM rate once per token pass
+// (9 rows at d = 7168, 16 at d <= 2048: one or two passes, ~4-7 us).
+constexpr int kDqRemainderRows = 16;
 
 // Format code of the dequantising grouped GEMM for this weight dtype, or -1
 // when it does not serve it (fp32, bf16, tiled int4 codes)
@@ -276,6 +283,13 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     const int dq_mt = dq_max_tiles(s->T, s->k, s->E);
     const int gs = s->wt == MOE_INT4_G64 ? 64 : 128;
     const bool dq_staged = use_dq && dq_staged_ok(dqf, gs, s->d) && dq_staged_ok(dqf, gs, s->F);
+    // int4-g128 with every group on the dequantising GEMM: short last tiles
+    // to the skinny int4 kernel (a one-expert group of T rows has one only
+    // when T leaves a short one)
+    const int dq_bm = use_dq ? dq_tile_rows(dqf, dq_staged) : 0;
+    const bool dq_rem = kDqRemainderRows > 0 && use_dq && dqt == 0 && s->wt == MOE_INT4_G128 && dq_staged &&
+                        i4mfma_supported(s->d, s->F) && i4mfma_supported(s->F, s->d) &&
+                        (s->E > 1 || (s->T % dq_bm != 0 && s->T % dq_bm <= kDqRemainderRows));
     const int max_rows_gemv = use_mfma ? tau : s->T;   // a group holds at most T rows
     int rc;
 
@@ -286,8 +300,9 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
         if (rc) return rc;
     }
     if (use_dq) {
-        rc = hip_check(launch_dq_plan(counts, offsets, s->E, dqt, dqf, dq_staged, tiles, dq_mt, st), st, "dq plan", err,
-                       err_len);
+        rc = hip_check(launch_dq_plan(counts, offsets, s->E, dqt, dqf, dq_staged, tiles, dq_mt,
+                                      dq_rem ? kDqRemainderRows : 0, st),
+                       st, "dq plan", err, err_len);
         if (rc) return rc;
     }
     // routed experts (g) and the shared expert (q: one expert over all T rows)
@@ -359,11 +374,20 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
         rc = pass(0, "gate/up");
         if (rc) return rc;
     }
+    // the remainder rows the dq plan listed, on the skinny int4 kernel
+    auto remainders = [&](int mode, const char* what) -> int {
+        GemvArgs r = g;
+        r.counts = dq_remainders(tiles, dq_mt);
+        r.offsets = r.counts + s->E;
+        r.tau = -1;
+        return hip_check(launch_i4mfma(mode, false, &r, nullptr, st), st, what, err, err_len);
+    };
     if (use_dq) {
         rc = hip_check(launch_dq_ffn(0, dqf, gs, dq_staged, w->w_gate, w->w_up, w->s_gate, w->s_up, x, h, perm, tiles,
                                      s->F, s->d, s->k, dq_mt, s->T, st),
                        st, "dq gate/up", err, err_len);
         if (rc) return rc;
+        if (dq_rem && (rc = remainders(0, "dq gate/up remainders"))) return rc;
     }
     if (use_mfma) {
         rc = hip_check(launch_mfma_ffn(0, tmode, w->w_gate, w->w_up, x, h, perm, tiles, s->F, s->d, s->k, s->T, max_mt,
@@ -387,6 +411,7 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
                                      tiles, s->d, s->F, s->k, dq_mt, s->T * s->k, st),
                        st, "dq down", err, err_len);
         if (rc) return rc;
+        if (dq_rem && (rc = remainders(1, "dq down remainders"))) return rc;
     }
     if (use_mfma) {
         rc = hip_check(launch_mfma_ffn(1, tmode, w->w_down, nullptr, h, y_perm, perm, tiles, s->d, s->F, s->k, s->T,

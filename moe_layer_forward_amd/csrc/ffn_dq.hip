@@ -774,16 +774,32 @@ __global__ __launch_bounds__(DT_THREADS, 1) void dq_tile_kernel(DqArgs a) {
 }
 
 // One 256-thread block: per expert with more than tau rows, ceil(rows/bm)
-// tiles of bm rows; an exclusive scan over the experts places them.
+// tiles of bm rows; an exclusive scan over the experts places them.  With a
+// remainder table (rem: counts [E] then offsets [E]), a group's last partial
+// tile of at most rem_max rows is left out and its rows listed there instead
+// (every other expert's entry is zero).
 __global__ __launch_bounds__(256) void dq_plan_kernel(const int32_t* __restrict__ counts,
                                                      const int32_t* __restrict__ offsets, int E, int tau, int bm,
-                                                     int32_t* __restrict__ tiles, int max_mt) {
+                                                     int32_t* __restrict__ tiles, int max_mt, int rem_max,
+                                                     int32_t* __restrict__ rem) {
     __shared__ int s[2][256];
     const int tid = threadIdx.x;
     int c = 0, nb = 0;
     if (tid < E) {
         c = counts[tid];
-        if (c > tau && c > 0) nb = (c + bm - 1) / bm;
+        int rc = 0;
+        if (c > tau && c > 0) {
+            nb = (c + bm - 1) / bm;
+            const int r = c - (c / bm) * bm;
+            if (rem && r > 0 && r <= rem_max) {
+                nb = c / bm;
+                rc = r;
+            }
+        }
+        if (rem) {
+            rem[tid] = rc;
+            rem[E + tid] = rc ? offsets[tid] + nb * bm : 0;
+        }
     }
     int cur = 0;
     s[0][tid] = nb;
@@ -811,7 +827,7 @@ __global__ __launch_bounds__(256) void dq_plan_kernel(const int32_t* __restrict_
 
 // bounds for the smaller tile height, so one plan region serves both kernels
 int dq_max_tiles(int T, int k, int E) { return (T * k + DT_BM - 1) / DT_BM + E; }
-int dq_plan_ints(int T, int k, int E) { return 3 * dq_max_tiles(T, k, E) + 1; }
+int dq_plan_ints(int T, int k, int E) { return 3 * dq_max_tiles(T, k, E) + 1 + 2 * E; }
 
 bool dq_supported(int K, int N) {
     // whole K pairs; 32-bit buffer offsets of a matrix (fp8: one byte per element)
@@ -839,11 +855,14 @@ int dq_tile_rows(int fmt, bool staged) {
     return dq_wide(fmt) ? 2 * DT_BM : DT_BM;
 }
 
+int32_t* dq_remainders(int32_t* tiles, int max_mt) { return tiles + 3 * max_mt + 1; }
+
 hipError_t launch_dq_plan(const int32_t* counts, const int32_t* offsets, int E, int tau, int fmt, bool staged,
-                          int32_t* tiles, int max_mt, hipStream_t s) {
+                          int32_t* tiles, int max_mt, int rem_max, hipStream_t s) {
     if (E > 256) return hipErrorInvalidValue;
+    int32_t* rem = rem_max > 0 ? dq_remainders(tiles, max_mt) : nullptr;
     hipLaunchKernelGGL(dq_plan_kernel, dim3(1), dim3(256), 0, s, counts, offsets, E, tau, dq_tile_rows(fmt, staged),
-                       tiles, max_mt);
+                       tiles, max_mt, rem_max, rem);
     return hipGetLastError();
 }
 

@@ -75,8 +75,12 @@ int dq_plan_ints(int T, int k, int E);
 bool dq_supported(int K, int N);
 bool dq_staged_ok(int fmt, int gs, int K);
 int dq_tile_rows(int fmt, bool staged);
+// rem_max > 0: a group's last partial tile of at most rem_max rows is left
+// out of the tile list; its rows go to the remainder table dq_remainders()
+// (counts [E], then the offsets of those rows [E]; zero elsewhere).
 hipError_t launch_dq_plan(const int32_t* counts, const int32_t* offsets, int E, int tau, int fmt, bool staged,
-                          int32_t* tiles, int max_mt, hipStream_t s);
+                          int32_t* tiles, int max_mt, int rem_max, hipStream_t s);
+int32_t* dq_remainders(int32_t* tiles, int max_mt);
 hipError_t launch_dq_ffn(int mode, int fmt, int gs, bool staged, const void* w0, const void* w1, const void* s0,
                          const void* s1, const void* in, void* out, const int32_t* perm, const int32_t* tiles, int N,
                          int K, int topk, int max_mt, int in_rows, hipStream_t s);

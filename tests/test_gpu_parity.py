@@ -691,6 +691,40 @@ def test_int4_groups_on_both_sides_of_tau(orc):
         assert err < TOL["int4"]
 
 
+def test_int4_dq_remainders(orc):
+    """int4-g128 with every group on the dequantising GEMM (T*k >= 64 E): a
+    group's last 128-row tile of at most 16 rows runs on the skinny int4
+    kernel instead, a longer one on the GEMM.  Hand-made groups through
+    moe_expert_ffn: remainders 0, 1, 8, 12, 16 and 17, whole groups of 1 to
+    17 rows, an empty expert, and the shared expert over T = 136 (a remainder
+    of 8 rows) and T = 150 (22 rows, on the GEMM)."""
+    cfg = SMALL["int4_dq"]
+    say("int4 dq remainders on the skinny kernel")
+    d = device_inputs(cfg)
+    W, S = oracle_weights(d)
+    cases = {150: ([140, 16, 0, 144], [145, 17, 9, 129], [256, 1, 2, 41]), 136: ([136, 8, 0, 128],)}
+    for T, mixes in cases.items():
+        x = d["x"][:T].contiguous()
+        xs = np_store(x)
+        shape = shape_of(cfg, 0, T=T)
+        ys_ref = orc.shared_ffn(xs, "bf16", "int4", S)
+        ws = torch.empty(moe.moe_workspace_bytes(shape), dtype=torch.uint8, device=DEV)
+        for cs in mixes:
+            assert sum(cs) == T * cfg.k
+            off = np.concatenate([[0], np.cumsum(cs)]).astype(np.int32)
+            perm = np.random.default_rng(sum(cs) + cs[0]).permutation(T * cfg.k).astype(np.int32)
+            yp = torch.empty(T * cfg.k, cfg.d, dtype=torch.float32, device=DEV)
+            ys = torch.empty(T, cfg.d, dtype=torch.float32, device=DEV)
+            moe.moe_expert_ffn(shape, x, weights_struct(d), torch.tensor(cs, dtype=torch.int32, device=DEV),
+                               torch.from_numpy(off).to(DEV), torch.from_numpy(perm).to(DEV), yp, ys, ws)
+            torch.cuda.synchronize()
+            ref = orc.expert_ffn(xs, "bf16", "int4", W, np.array(cs, np.int32), off, perm, cfg.k)
+            e1 = tokenwise_rel(yp.cpu().numpy(), ref).max()
+            e2 = tokenwise_rel(ys.cpu().numpy(), ys_ref).max()
+            say(f"  T={T} counts {cs}: y_perm max rel {e1:.3g}, shared {e2:.3g}")
+            assert e1 < TOL["int4"] and e2 < TOL["int4"]
+
+
 def test_rmsnorm_parity(orc):
     say("rmsnorm")
     for act in ("f32", "bf16"):
