@@ -88,8 +88,10 @@ typedef enum {
  *        d and F are at least 4096, else 16.  Negative forces the GEMV for every group.
  *        int4-g128 (row-major codes): groups of at most tau rows (0: 32) run
  *        the skinny int4 kernels (matrix cores for K a multiple of 1024, else
- *        the GEMV), larger ones the dequantising grouped GEMM; negative keeps
- *        every group on the skinny kernels.  fp32, tiled int4, int4-g64 and
+ *        the GEMV), larger ones the dequantising grouped GEMM (when every group
+ *        runs it, a group's last partial 128-row tile of at most 16 rows goes
+ *        to the skinny matrix-core kernel); negative keeps every group on the
+ *        skinny kernels.  fp32, tiled int4, int4-g64 and
  *        MX weights ignore tau.
  * Limits (MOE_EINVAL otherwise): T >= 0, 1 <= k <= E <= 256, k <= 16,
  *   d, F >= 8 and multiples of 8; int4-g128: d and F multiples of 128;
