@@ -171,6 +171,21 @@ __device__ __forceinline__ void wait_copies(int n) {
 // the compute phase, between the MFMAs, with its offsets worked out during the
 // memory phase before; the memory phase then holds only the fragment reads.
 // Otherwise the copies go out in the memory phase (K tails, single pairs).
+// Task L of the grouped order -> (M-tile, N-tile): groups of MF_GM M-tiles x
+// all N-tiles, M fastest.  Within a group the M position turns by one every
+// 32 N-tiles (one round of a 256-block grid: 256 tasks), so a block does not
+// keep the same M position -- say an expert's ragged last tile -- round after
+// round; the 32 tasks an XCD takes in a round still span MF_GM M-tiles and
+// 4 N-tiles.
+__device__ __forceinline__ void grouped_tile(int L, int n_mt, int nN, int& mt, int& nt) {
+    const int grp = L / (MF_GM * nN);
+    const int gm0 = grp * MF_GM;
+    const int gsz = min(MF_GM, n_mt - gm0);
+    const int rem = L - grp * MF_GM * nN;
+    nt = rem / gsz;
+    mt = gm0 + (rem % gsz + (nt >> 5)) % gsz;
+}
+
 template <int MODE, bool FAST>
 __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
     // A pair slots then B pair slots; pair j of a task (its K steps kb + 2j and
@@ -241,13 +256,8 @@ __global__ __launch_bounds__(512, 1) void mfma_ffn_kernel(MfmaArgs a) {
             c_pi = j * ts.S + sp;
         }
         c_kend = min(K, c_ke * MF_BK);           // element bound of the task's K range
-        // grouped order: GM M-tiles x all N-tiles, M fastest
-        const int grpi = L / (MF_GM * nN);
-        const int gm0 = grpi * MF_GM;
-        const int gsz = min(MF_GM, n_mt - gm0);
-        const int rem = L - grpi * MF_GM * nN;
-        const int mt = gm0 + rem % gsz;
-        c_nt = rem / gsz;
+        int mt;
+        grouped_tile(L, n_mt, nN, mt, c_nt);
         c_e = a.tiles[mt];
         c_p0 = a.tiles[a.max_mt + mt];
         c_rows = a.tiles[2 * a.max_mt + mt];
@@ -615,13 +625,8 @@ __global__ __launch_bounds__(256) void mfma_tail_reduce(MfmaArgs a, int G) {
     constexpr int NC = MODE == 0 ? 128 : MF_BN;      // output columns of a tile
     const int idx = (blockIdx.x * 256 + threadIdx.x) * 4;
     const int row = idx / NC, c = idx - row * NC;
-    const int L = ts.nfull + j;
-    const int grp = L / (MF_GM * nN);
-    const int gm0 = grp * MF_GM;
-    const int gsz = min(MF_GM, n_mt - gm0);
-    const int rem = L - grp * MF_GM * nN;
-    const int mt = gm0 + rem % gsz;
-    const int nt = rem / gsz;
+    int mt, nt;
+    grouped_tile(ts.nfull + j, n_mt, nN, mt, nt);
     const int p0 = a.tiles[a.max_mt + mt];
     const int rows = a.tiles[2 * a.max_mt + mt];
     if (row >= rows) return;
