@@ -345,14 +345,27 @@ def ffn_paths(cfg, counts, tau):
     MFMA tiles; below it, when the largest group exceeds one GEMV pass, the
     skinny MFMA kernel (ceil(rows / 16) 16-token tiles, up to 64 rows) takes
     them all, else the GEMV."""
-    if cfg.wt in ("int4g64", "mxfp4", "mxfp8"):
+    if cfg.wt in ("int4", "mxfp4", "mxfp8"):
+        # groups of at most dqt rows on the skinny kernel (matrix cores when d
+        # and F are multiples of 1024, int4 also at most 8192; else the int4
+        # GEMV), larger ones on the dequantising GEMM; dqt = 0 (every group on
+        # the GEMM, short last tiles on the skinny kernel) once the mean group
+        # reaches 64 rows
+        sk_mfma = cfg.d % 1024 == 0 and cfg.F % 1024 == 0 and (cfg.wt != "int4" or max(cfg.d, cfg.F) <= 8192)
+        if cfg.wt != "int4" and not sk_mfma:
+            return f"{cfg.wt} dequantising MFMA GEMM"
+        skinny = f"{cfg.wt} skinny MFMA" if sk_mfma else "int4 GEMV"
+        if tau < 0:
+            return skinny
+        dqt = tau if tau > 0 else (0 if cfg.T * cfg.k >= 64 * cfg.E else 32)
+        c = [int(v) for v in counts if int(v) > 0]
+        small = any(v <= dqt for v in c)
+        big = any(v > dqt for v in c)
+        gemm = f"{cfg.wt} dequantising MFMA GEMM" + (" (short last tiles on the skinny kernel)"
+                                                    if dqt == 0 and sk_mfma else "")
+        return " + ".join(([skinny] if small else []) + ([gemm] if big else []))
+    if cfg.wt in ("int4g64",):
         return f"{cfg.wt} dequantising MFMA GEMM"
-    if cfg.wt == "int4":
-        t = 32 if tau == 0 else tau
-        big = tau >= 0 and any(int(v) > t for v in counts)
-        skinny = "int4 skinny MFMA" if cfg.d % 1024 == 0 and cfg.F % 1024 == 0 else "int4 GEMV"
-        small = any(0 < int(v) <= t for v in counts) or tau < 0
-        return " + ".join(([skinny] if small else []) + (["int4 dequantising MFMA GEMM"] if big else []))
     if cfg.wt != "bf16" or tau < 0:
         return "GEMV"
     skinny = cfg.act == "bf16" and cfg.d % 64 == 0 and cfg.F % 64 == 0
@@ -819,8 +832,11 @@ def main():
         # grouped GEMM), then MXFP4 experts of that shape and MXFP8 experts of
         # the Mixtral shape
         psteps, pwarm = max(50, steps), max(20, warmup)
-        for name, Wq in (("fine_int4_prefill", iW), ("fine_mxfp4_prefill", None),
-                         ("mixtral_mxfp8_prefill", None)):
+        # and the MX layers at decode (the skinny matrix-core kernel), on the
+        # same weights: the fine-grained MXFP4 layer at T = 64, the
+        # Mixtral-shaped MXFP8 layer at T = 8
+        for name, Wq, dec in (("fine_int4_prefill", iW, None), ("fine_mxfp4_prefill", None, ("fine_mxfp4_decode", 64)),
+                              ("mixtral_mxfp8_prefill", None, ("mixtral_mxfp8_decode", 8))):
             qcfg = moe_inputs.CONFIGS[name]
             log(f"{name}: quantised experts at prefill")
             qx, qwr, qbr, qW = device_layer(qcfg, shared_weights=Wq)
@@ -828,7 +844,17 @@ def main():
             qleg = workload_leg(qrun, psteps, pwarm, args.tau, ceilings)
             out[name] = leg_summary(qcfg, qleg, psteps, pwarm)
             log(json.dumps(out[name]))
-            del qrun, qW, qx
+            del qrun
+            if dec is not None:
+                dname, dT = dec
+                dcfg = qcfg.replace(name=dname, T=dT)
+                log(f"{dname}: the same experts at decode, T={dT}")
+                drun = Runner(dcfg, qx[:dT].contiguous(), qwr, qbr, qW, tau=args.tau)
+                dleg = workload_leg(drun, steps, warmup, args.tau, ceilings)
+                out[dname] = leg_summary(dcfg, dleg, steps, warmup)
+                log(json.dumps(out[dname]))
+                del drun
+            del qW, qx
             torch.cuda.empty_cache()
         del iW
         out["stack4"] = stack_leg(steps, warmup, cpu=not args.no_cpu_baseline)

@@ -91,8 +91,9 @@ typedef enum {
  *        the GEMV), larger ones the dequantising grouped GEMM (when every group
  *        runs it, a group's last partial 128-row tile of at most 16 rows goes
  *        to the skinny matrix-core kernel); negative keeps every group on the
- *        skinny kernels.  fp32, tiled int4, int4-g64 and
- *        MX weights ignore tau.
+ *        skinny kernels.  MXFP4 and MXFP8 with d and F multiples of 1024: the
+ *        same rule on the skinny matrix-core kernel (without the short-tile
+ *        path); other MX shapes, fp32, tiled int4 and int4-g64 ignore tau.
  * Limits (MOE_EINVAL otherwise): T >= 0, 1 <= k <= E <= 256, k <= 16,
  *   d, F >= 8 and multiples of 8; int4-g128: d and F multiples of 128;
  *   int4-g64, MXFP4, MXFP8: multiples of 64.

@@ -127,13 +127,23 @@ struct Layout {
 
 bool is_int4(const moe_shape* s) { return s->wt == MOE_INT4_G128 || s->wt == MOE_INT4_G128_TILED; }
 
+// MX weights whose d and F the skinny matrix-core kernel takes (ffn_i4mfma.hip)
+int mx_fmt(const moe_shape* s) {
+    return s->wt == MOE_MXFP4 ? kFmtFp4 : s->wt == MOE_MXFP8 ? kFmtFp8 : -1;
+}
+bool mx_skinny(const moe_shape* s) {
+    const int f = mx_fmt(s);
+    return f >= 0 && i4mfma_supported(s->d, s->F, f) && i4mfma_supported(s->F, s->d, f);
+}
+
 constexpr int kDefaultInt4Tau = 32;
-// int4-g128 groups on the dequantising GEMM: a last partial 128-row tile of at
-// most this many rows goes to the skinny int4 kernel instead.  Such a tile
-// would stream and widen its expert's whole weight matrix for a few rows
-// (~11 us of the whole GPU per tile at the fine-grained shape, d = 7168,
-// F = 2048); the skinny kernel streams it at the HBM rate once per token pass
-// (9 rows at d = 7168, 16 at d <= 2048: one or two passes, ~4-7 us).
+// int4-g128 groups on the dequantising GEMM: a last partial tile of at most
+// this many rows goes to the skinny matrix-core kernel instead.  Such
+// a tile would stream and widen its expert's whole weight matrix for a few
+// rows (~11 us of the whole GPU per 128-row int4 tile at the fine-grained
+// shape, d = 7168, F = 2048); the skinny kernel streams it at the HBM rate
+// once per token pass (9 rows at d = 7168, 16 at d <= 2048: one or two
+// passes, ~4-7 us).
 constexpr int kDqRemainderRows = 16;
 
 // Format code of the dequantising grouped GEMM for this weight dtype, or -1
@@ -146,12 +156,13 @@ int dq_format(const moe_shape* s) {
 }
 
 // Groups above this many rows run the dequantising GEMM (-1: none does):
-// int4-g128 keeps groups of at most tau rows (0: 32) on the skinny int4
-// kernels -- with the default, once the mean group is twice that, every
-// group goes to the GEMM and the skinny launches (which would find no work)
-// are left out; int4-g64 and MX weights run every group on it.
+// int4-g128, and MX weights whose d and F the skinny kernel takes, keep
+// groups of at most tau rows (0: 32) on the skinny kernels -- with the
+// default, once the mean group is twice that, every group goes to the GEMM
+// and the skinny launches (which would find no work) are left out; int4-g64
+// and other MX shapes run every group on it.
 int dq_tau(const moe_shape* s) {
-    if (s->wt == MOE_INT4_G128) {
+    if (s->wt == MOE_INT4_G128 || mx_skinny(s)) {
         if (s->tau < 0) return -1;
         if (s->tau > 0) return s->tau;
         return (long)s->T * s->k >= 2L * kDefaultInt4Tau * s->E ? 0 : kDefaultInt4Tau;
@@ -166,7 +177,7 @@ int dq_tau(const moe_shape* s) {
 // skinny int4 launches.
 bool shared_as_group(const moe_shape* s) {
     if (!s->n_shared) return false;
-    if (!is_int4(s)) return true;
+    if (!is_int4(s) && !mx_skinny(s)) return true;
     const int t = dq_tau(s);
     return t >= 0 && s->T > t;
 }
@@ -287,7 +298,11 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     // to the skinny int4 kernel (a one-expert group of T rows has one only
     // when T leaves a short one)
     const int dq_bm = use_dq ? dq_tile_rows(dqf, dq_staged) : 0;
-    const bool dq_rem = kDqRemainderRows > 0 && use_dq && dqt == 0 && s->wt == MOE_INT4_G128 && dq_staged &&
+    const int sfmt = mx_fmt(s) >= 0 ? mx_fmt(s) : kFmtInt4;       // the skinny kernel's code format
+    // (int4 only: MXFP4's 64-row GEMM tiles cost less than a second weight
+    // stream on the skinny kernel -- fine-grained prefill 3.92-3.96 -> 4.02 ms
+    // with it -- and no MXFP8 layer here has fine-grained groups)
+    const bool dq_rem = kDqRemainderRows > 0 && use_dq && dqt == 0 && dq_staged && s->wt == MOE_INT4_G128 &&
                         i4mfma_supported(s->d, s->F) && i4mfma_supported(s->F, s->d) &&
                         (s->E > 1 || (s->T % dq_bm != 0 && s->T % dq_bm <= kDqRemainderRows));
     const int max_rows_gemv = use_mfma ? tau : s->T;   // a group holds at most T rows
@@ -316,7 +331,7 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     g.tau = use_mfma ? tau : (use_dq ? dqt : -1);
     GemvArgs q{};
     q.topk = 1; q.T = s->T; q.E = 1; q.tau = -1;
-    const GemvArgs* qp = (s->n_shared && is_int4(s) && !shared_as_group(s)) ? &q : nullptr;
+    const GemvArgs* qp = (s->n_shared && (is_int4(s) || mx_skinny(s)) && !shared_as_group(s)) ? &q : nullptr;
     const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
     const bool tiled = s->wt == MOE_INT4_G128_TILED;
     // bf16 groups below the MFMA tiles: when one of them is larger than a
@@ -338,8 +353,8 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     // one pass (gate/up or down) of the routed and the shared expert: int4 on
     // the matrix cores in one launch, else one GEMV launch each
     auto pass = [&](int mode, const char* what) -> int {
-        if (tiled || (s->wt == MOE_INT4_G128 && i4mfma_supported(g.K, g.N)))
-            return hip_check(launch_i4mfma(mode, tiled, &g, qp, st), st, what, err, err_len);
+        if (tiled || mx_skinny(s) || (s->wt == MOE_INT4_G128 && i4mfma_supported(g.K, g.N)))
+            return hip_check(launch_i4mfma(mode, tiled, &g, qp, st, sfmt), st, what, err, err_len);
         g.rows_per_item = gemv_rows_per_item(s->wt, mode, g.K, g.N, active);
         const int in_rows = mode == 0 ? s->T : s->T * s->k;
         const int lo = skinny_lo(mode, g.K, g.N, in_rows);
@@ -380,7 +395,7 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
         r.counts = dq_remainders(tiles, dq_mt);
         r.offsets = r.counts + s->E;
         r.tau = -1;
-        return hip_check(launch_i4mfma(mode, false, &r, nullptr, st), st, what, err, err_len);
+        return hip_check(launch_i4mfma(mode, false, &r, nullptr, st, sfmt), st, what, err, err_len);
     };
     if (use_dq) {
         rc = hip_check(launch_dq_ffn(0, dqf, gs, dq_staged, w->w_gate, w->w_up, w->s_gate, w->s_up, x, h, perm, tiles,

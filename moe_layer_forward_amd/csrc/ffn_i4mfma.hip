@@ -44,6 +44,19 @@
 //    experts' instead of running as a separate small launch;
 //  * gate and up share each A fragment; the SwiGLU epilogue writes h (bf16),
 //    the down pass writes fp32 rows of y_perm (y_shared for the shared slot).
+//
+// MXFP4 and MXFP8 weights ([P5] §6: models shipped as native MX checkpoints)
+// run the same kernel: the same 128-K groups, lane l holding 32 codes of row
+// l%16 at K = 128 g + 32 (l/16) (16 bytes of E2M1 codes, or 32 of E4M3), but
+// every 32 codes carry their own E8M0 scale, which is exactly the 32 codes a
+// lane holds.  A lane widens its codes with v_cvt_scalef32_pk_bf16_fp4/_fp8,
+// two per instruction and already times the scale (exact in bf16), so the
+// MFMAs accumulate straight into the sums: no offset, no per-group sums, and
+// the token rows are staged in plain element order.  The scale bytes of four
+// groups of a row (16 bytes) go out with the weights of the first of them,
+// into a ring of four such chunks.  fp8 codes take two 16-byte loads per
+// group and matrix, so their ring holds 4 steps instead of 8 (the same bytes
+// in flight).
 #include <type_traits>
 
 #include "common.h"
@@ -78,6 +91,11 @@ __device__ __forceinline__ u32x4_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 
 template <int I>
 using ic = std::integral_constant<int, I>;
+
+// E8M0 scale code -> 2^(code - 127) in fp32 (code 0: 2^-127, a subnormal)
+__device__ __forceinline__ float mx_scale(uint32_t code) {
+    return __uint_as_float(code ? (code << 23) : 0x00400000u);
+}
 
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -130,10 +148,15 @@ struct I4Args {
     int N, K, topk, T, E, tau, P;
 };
 
-template <int MODE, int RING, bool TILED>
+template <int MODE, int RING, bool TILED, int FMT>
 __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     constexpr int G = MODE == 0 ? 2 : 1;
-    static_assert(RING == 8, "the scale prefetch runs 8 steps ahead, as far as the ring");
+    constexpr bool MX = FMT != kFmtInt4;
+    constexpr bool FP8 = FMT == kFmtFp8;
+    constexpr int NW = FP8 ? 2 : 1;             // 16-byte code loads per lane, group and matrix
+    static_assert(MX || RING == 8, "the int4 scale prefetch runs 8 steps ahead, as far as the ring");
+    static_assert(!MX || !TILED, "the tiled layout holds int4 codes");
+    static_assert(RING % 2 == 0 && RING <= 16, "steps are loaded in pairs within the 16-step unroll");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ int s_act[kMaxE + 1], s_cnt[kMaxE + 1], s_off[kMaxE + 1], s_ipref[kMaxE + 2];
     __shared__ int s_tot[2], s_src[16];
@@ -142,8 +165,8 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     const int K = a.K, N = a.N, P = a.P;
     const int NG = K / 128;                                  // scale groups per row (multiple of 8)
     const int nrc = (N + kItemRows - 1) / kItemRows;         // 128-row chunks per matrix
-    const uint32_t rb = (uint32_t)K / 2;                     // packed bytes per row
-    const uint32_t srow = (uint32_t)NG * 2;                  // scale bytes per row
+    const uint32_t rb = FP8 ? (uint32_t)K : (uint32_t)K / 2;          // code bytes per row
+    const uint32_t srow = MX ? (uint32_t)K / 32 : (uint32_t)NG * 2;   // scale bytes per row
     const uint32_t RS = (uint32_t)K * 2 + 16;                // LDS bytes per staged token row
     char* xrows = smem;                                      // P token rows, then the zero row
     float* xsum = reinterpret_cast<float*>(smem + (size_t)(P + 1) * RS);   // [NG][16]
@@ -246,30 +269,47 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     // lane part of a weight offset, and the offset step from one group to the
     // next: row-major (row lrow, bytes 64 g + 16 lq) or tiled (16-row set
     // `wave` of the item, 1 KB per group, lane-ordered 16-byte pieces)
-    const uint32_t woff_l = TILED ? (uint32_t)wave * 16u * rb + (uint32_t)lane * 16u : lrow * rb + lq * 16u;
-    constexpr uint32_t kGroupStep = TILED ? 1024u : 64u;
+    const uint32_t woff_l =
+        TILED ? (uint32_t)wave * 16u * rb + (uint32_t)lane * 16u : lrow * rb + lq * (FP8 ? 32u : 16u);
+    constexpr uint32_t kGroupStep = TILED ? 1024u : (FP8 ? 128u : 64u);
     const uint32_t soff_l = lrow * srow;                      // lane part of a scale offset
     const uint32_t lrow16 = (uint32_t)(lane & 15);
 
     // ---- weight loads of steps q and q+1 into ring slots S, S+1: the two
-    // halves of the same 128-byte lines, back to back (zeros past the range)
-    u32x4_t wq[RING][G];
+    // halves of the same 128-byte lines, back to back (zeros past the range);
+    // MX: at the first step of a four-group chunk (position P16 of the 16-step
+    // unroll a multiple of 4) the chunk's scale bytes go out first
+    u32x4_t wq[RING][G][NW];
+    u32x4_t sq[4][G];                             // MX: scale bytes of four groups, per row
     auto weight_ptr = [&](const Cursor& q, int m) -> const uint8_t* {
         if (q.e >= 0) return (m == 0 ? a.w0 : a.w1) + (size_t)q.e * mat_bytes;
         return m == 0 ? a.sw0 : a.sw1;
     };
-    auto issue_pair = [&](Cursor& q, auto slot) {
-        constexpr int S = decltype(slot)::value;
+    auto scale_ptr = [&](const Cursor& q, int m) -> const uint8_t* {
+        const uint16_t* sp = q.e >= 0 ? (m == 0 ? a.s0 : a.s1) : (m == 0 ? a.ss0 : a.ss1);
+        return reinterpret_cast<const uint8_t*>(sp) + (q.e >= 0 ? (size_t)q.e * N * srow : 0);
+    };
+    auto issue_pair = [&](Cursor& q, auto slot, auto pos) {
+        constexpr int S = decltype(slot)::value, P16 = decltype(pos)::value;
         Cursor q1 = q;
         advance(q1, 1);
         const uint32_t n0 = q.idx < nsteps ? mat_bytes : 0u, n1 = q1.idx < nsteps ? mat_bytes : 0u;
+        if constexpr (MX && P16 % 4 == 0) {
+            // row lrow's scale bytes of groups q.g .. q.g + 3 (q.g is a multiple of 4)
+            const uint32_t so = soff_l + (uint32_t)q.chunk * kItemRows * srow + (uint32_t)q.g * 4u;
+            const uint32_t sn = q.idx < nsteps ? (uint32_t)N * srow : 0u;
+#pragma unroll
+            for (int m = 0; m < G; ++m) sq[(P16 / 4) % 4][m] = ld16(rsrc(scale_ptr(q, m), sn), so);
+        }
         const uint32_t o0 = woff_l + (uint32_t)q.chunk * kItemRows * rb + (uint32_t)q.g * kGroupStep;
         const uint32_t o1 = woff_l + (uint32_t)q1.chunk * kItemRows * rb + (uint32_t)q1.g * kGroupStep;
 #pragma unroll
-        for (int m = 0; m < G; ++m) {
-            wq[S][m] = ld16<TILED ? kNonTemporal : 0>(rsrc(weight_ptr(q, m), n0), o0);
-            wq[S + 1][m] = ld16<TILED ? kNonTemporal : 0>(rsrc(weight_ptr(q1, m), n1), o1);
-        }
+        for (int m = 0; m < G; ++m)
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                wq[S][m][w] = ld16<TILED ? kNonTemporal : 0>(rsrc(weight_ptr(q, m), n0), o0 + 16u * w);
+                wq[S + 1][m][w] = ld16<TILED ? kNonTemporal : 0>(rsrc(weight_ptr(q1, m), n1), o1 + 16u * w);
+            }
         q = q1;
         advance(q, 1);
     };
@@ -304,8 +344,9 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
             const int p = q.o + j0 + tid;
             s_src[tid] = (MODE == 0 && routed && a.perm) ? a.perm[p] / a.topk : p;
         }
-        for (int i = tid; i < NG * 16; i += kThreads)   // group sums of the padded slots
-            if ((i & 15) >= nt) xsum[i] = 0.f;
+        if constexpr (!MX)
+            for (int i = tid; i < NG * 16; i += kThreads)   // group sums of the padded slots
+                if ((i & 15) >= nt) xsum[i] = 0.f;
         __syncthreads();
         // nt rows of K/8 16-byte chunks; nch is a multiple of 128, so every
         // wave is either wholly inside or wholly past the range, and 16
@@ -327,17 +368,24 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
 #pragma unroll
             for (int j = 0; j < B; ++j) {
                 if (i0 + j * kThreads >= total) break;
-                // elements (0,1)(2,3)(4,5)(6,7) -> pairs (0,4)(1,5)(2,6)(3,7)
                 u32x4_t o;
-                o.x = (v[j].x & 0xffffu) | (v[j].z << 16);
-                o.y = (v[j].x >> 16) | (v[j].z & 0xffff0000u);
-                o.z = (v[j].y & 0xffffu) | (v[j].w << 16);
-                o.w = (v[j].y >> 16) | (v[j].w & 0xffff0000u);
+                if constexpr (MX) {
+                    // plain element order: the widened codes come out in it
+                    o = u32x4_t{v[j].x, v[j].y, v[j].z, v[j].w};
+                } else {
+                    // elements (0,1)(2,3)(4,5)(6,7) -> pairs (0,4)(1,5)(2,6)(3,7)
+                    o.x = (v[j].x & 0xffffu) | (v[j].z << 16);
+                    o.y = (v[j].x >> 16) | (v[j].z & 0xffff0000u);
+                    o.z = (v[j].y & 0xffffu) | (v[j].w << 16);
+                    o.w = (v[j].y >> 16) | (v[j].w & 0xffff0000u);
+                }
                 *reinterpret_cast<u32x4_t*>(xrows + (size_t)t[j] * RS + (size_t)ch[j] * 16) = o;
-                float sum = bf16_lo(v[j].x) + bf16_hi(v[j].x) + bf16_lo(v[j].y) + bf16_hi(v[j].y) +
-                            bf16_lo(v[j].z) + bf16_hi(v[j].z) + bf16_lo(v[j].w) + bf16_hi(v[j].w);
-                sum = group_sum<16>(sum);
-                if ((ch[j] & 15) == 0) xsum[(ch[j] >> 4) * 16 + t[j]] = sum;
+                if constexpr (!MX) {
+                    float sum = bf16_lo(v[j].x) + bf16_hi(v[j].x) + bf16_lo(v[j].y) + bf16_hi(v[j].y) +
+                                bf16_lo(v[j].z) + bf16_hi(v[j].z) + bf16_lo(v[j].w) + bf16_hi(v[j].w);
+                    sum = group_sum<16>(sum);
+                    if ((ch[j] & 15) == 0) xsum[(ch[j] >> 4) * 16 + t[j]] = sum;
+                }
             }
         }
         __syncthreads();
@@ -353,22 +401,51 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
 #pragma unroll
     for (int m = 0; m < G; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const Cursor& q, auto slot, auto half) {
+    auto compute = [&](const Cursor& q, auto slot, auto half, auto pos) {
         constexpr int S = decltype(slot)::value,
-                      H = decltype(half)::value;   // group index within its 8-group chunk
-        // the scale of (row n, group g) sits in lane n + 16 (c % 4), register
-        // c / 4 of the row set's scales, c = g / 8
-        const int c8 = q.g >> 3;
-        const int src = (int)((lrow16 + 16u * (uint32_t)(c8 & 3)) << 2);
+                      H = decltype(half)::value,   // group index within its 8-group chunk
+                      P16 = decltype(pos)::value;  // position in the 16-step unroll
         const char* xg = xrows + xa + (uint32_t)q.g * 256u;
         u32x4_t af[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4_t*>(xg + i * 16);
+        if constexpr (MX) {
+            // this lane's 32 codes share the scale of byte 4 (g % 4) + l/16 of the chunk
+#pragma unroll
+            for (int m = 0; m < G; ++m) {
+                const uint32_t code = (sq[(P16 / 4) % 4][m][P16 % 4] >> (8u * lq)) & 0xffu;
+                const float sc = mx_scale(code);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    u32x4_t b;
+                    if constexpr (FP8) {
+                        const uint32_t w0 = wq[S][m][i >> 1][2 * (i & 1)], w1 = wq[S][m][i >> 1][2 * (i & 1) + 1];
+                        b.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false));
+                        b.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true));
+                        b.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false));
+                        b.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true));
+                    } else {
+                        const uint32_t w = wq[S][m][0][i];
+                        b.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+                        b.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+                        b.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+                        b.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+                    }
+                    acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
+                                                                      __builtin_bit_cast(bf16x8_t, b), acc[m], 0, 0, 0);
+                }
+            }
+            return;
+        }
+        // the scale of (row n, group g) sits in lane n + 16 (c % 4), register
+        // c / 4 of the row set's scales, c = g / 8
+        const int c8 = q.g >> 3;
+        const int src = (int)((lrow16 + 16u * (uint32_t)(c8 & 3)) << 2);
         const floatx4 xs = *reinterpret_cast<const floatx4*>(
             reinterpret_cast<const char*>(xsum) + (uint32_t)q.g * 64u + xs_l);
 #pragma unroll
         for (int m = 0; m < G; ++m) {
-            const uint32_t wd[4] = {wq[S][m].x, wq[S][m].y, wq[S][m].z, wq[S][m].w};
+            const uint32_t wd[4] = {wq[S][m][0].x, wq[S][m][0].y, wq[S][m][0].z, wq[S][m][0].w};
             floatx4 c = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -414,10 +491,14 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     // Loads complete in order, so a row set's scales go out as far ahead as
     // the weight ring reaches (8 steps)
     Cursor L = cur;       // next step whose weights are loaded
-    Cursor Sc = cur;      // loads a row set's scales when it reaches its start
-    issue_scales(Sc);
-    advance(Sc, 8);
-    static_for<0, RING / 2>([&](auto k) { issue_pair(L, ic<2 * decltype(k)::value>{}); });
+    Cursor Sc = cur;      // int4: loads a row set's scales when it reaches its start
+    if constexpr (!MX) {
+        issue_scales(Sc);
+        advance(Sc, 8);
+    }
+    static_for<0, RING / 2>([&](auto k) {
+        issue_pair(L, ic<2 * decltype(k)::value>{}, ic<2 * decltype(k)::value>{});
+    });
 
     // One step at unrolled position k (0..15): ring slot k % RING.  Every
     // other step refills the two slots just consumed with the steps RING
@@ -433,21 +514,21 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
                 xa = (tok < (uint32_t)nt ? tok : (uint32_t)P) * RS + lq * 64u;
             }
         }
-        if constexpr (k % 8 == 0) {
+        if constexpr (!MX && k % 8 == 0) {
             if (C.g == 0) {
 #pragma unroll
                 for (int m = 0; m < G; ++m) { scur[m][0] = snext[m][0]; scur[m][1] = snext[m][1]; }
             }
         }
-        compute(C, ic<k % RING>{}, ic<k % 8>{});
-        if constexpr (k % 8 == 0) {
+        compute(C, ic<k % RING>{}, ic<k % 8>{}, ic<k>{});
+        if constexpr (!MX && k % 8 == 0) {
             if (Sc.g == 0) issue_scales(Sc);
             advance(Sc, 8);
         }
         if constexpr (k % 8 == 7) {
             if (C.g == NG - 1) epilogue(C);
         }
-        if constexpr (k % 2 == 1) issue_pair(L, ic<(k - 1) % RING>{});
+        if constexpr (k % 2 == 1) issue_pair(L, ic<(k - 1) % RING>{}, ic<(k - 1 + RING) % 16>{});
         advance(C, 1);
     };
     // nsteps is a multiple of 8 (NG is)
@@ -467,15 +548,20 @@ static int i4_pass_tokens(int K) {
     return (int)p;
 }
 
-bool i4mfma_supported(int K, int N) {
-    // K a multiple of 8 groups of 128, at most 64 groups (two scale registers)
-    if (K % 1024 != 0 || K <= 0 || K > 8192 || N <= 0) return false;
+bool i4mfma_supported(int K, int N, int fmt) {
+    // K a multiple of 8 groups of 128; int4: at most 64 groups (two scale
+    // registers per row set); MX scales come in four-group chunks, no bound
+    if (K % 1024 != 0 || K <= 0 || N <= 0 || (fmt == kFmtInt4 && K > 8192)) return false;
     if (i4_pass_tokens(K) < 1) return false;
     // 32-bit buffer offsets of a matrix, including the padded last chunk
-    return (size_t)(N + kItemRows) * (size_t)(K / 2) < ((size_t)1 << 31);
+    const size_t rb = fmt == kFmtFp8 ? (size_t)K : (size_t)K / 2;
+    return (size_t)(N + kItemRows) * rb < ((size_t)1 << 31);
 }
 
-hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s) {
+hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s,
+                         int fmt) {
+    if (fmt != kFmtInt4 && fmt != kFmtFp4 && fmt != kFmtFp8) return hipErrorInvalidValue;
+    if (tiled && fmt != kFmtInt4) return hipErrorInvalidValue;
     const GemvArgs& g = routed ? *routed : *shared;
     I4Args a{};
     if (routed) {
@@ -510,13 +596,20 @@ hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const Gem
     const size_t lds = (size_t)(a.P + 1) * ((size_t)g.K * 2 + 16) + (size_t)(g.K / 128) * 16 * 4;
 
     const int n_cu = cu_count();
-    // 8 scale groups per wave in flight: 16 KB (gate/up) or 8 KB (down)
-    auto k = mode == 0 ? (tiled ? i4_mfma_kernel<0, 8, true> : i4_mfma_kernel<0, 8, false>)
-                       : (tiled ? i4_mfma_kernel<1, 8, true> : i4_mfma_kernel<1, 8, false>);
+    // 8 scale groups per wave in flight: 16 KB (gate/up) or 8 KB (down); fp8
+    // codes take twice the bytes per group, so 4 groups
+    auto k = mode == 0 ? (fmt == kFmtFp8   ? i4_mfma_kernel<0, 4, false, kFmtFp8>
+                          : fmt == kFmtFp4 ? i4_mfma_kernel<0, 8, false, kFmtFp4>
+                          : tiled          ? i4_mfma_kernel<0, 8, true, kFmtInt4>
+                                           : i4_mfma_kernel<0, 8, false, kFmtInt4>)
+                       : (fmt == kFmtFp8   ? i4_mfma_kernel<1, 4, false, kFmtFp8>
+                          : fmt == kFmtFp4 ? i4_mfma_kernel<1, 8, false, kFmtFp4>
+                          : tiled          ? i4_mfma_kernel<1, 8, true, kFmtInt4>
+                                           : i4_mfma_kernel<1, 8, false, kFmtInt4>);
     // dynamic LDS beyond 64 KB: the budget left next to the static arrays,
     // set once per device and kernel variant
-    static std::atomic<int> attr_set[4][kMaxDevices];
-    const int ki = mode * 2 + (tiled ? 1 : 0);
+    static std::atomic<int> attr_set[8][kMaxDevices];
+    const int ki = mode * 4 + (fmt == kFmtInt4 ? (tiled ? 1 : 0) : fmt + 1);
     per_device_int(attr_set[ki], [&] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)(kLdsBytes - kStaticLds));

@@ -45,12 +45,16 @@ hipError_t launch_identity_group(int32_t* counts, int32_t* offsets, int32_t* per
 hipError_t launch_gemv(int wt, int act, int mode, const GemvArgs& a, int nexp, int max_rows,
                        hipStream_t s);
 int gemv_max_k(int wt);
-// int4-g128 weights on the matrix cores (ffn_i4mfma.hip): K a multiple of 1024.
-// One launch serves the routed experts (counts/offsets set) and, when
-// `shared` is given, the shared expert over all T tokens; either may be null.
-// `tiled`: the weight codes are in the layout launch_pack_int4_tiled writes.
-bool i4mfma_supported(int K, int N);
-hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s);
+// Skinny groups of int4-g128, MXFP4 or MXFP8 weights on the matrix cores
+// (ffn_i4mfma.hip): K a multiple of 1024 (int4: at most 8192).  One launch serves
+// the routed experts (counts/offsets set) and, when `shared` is given, the
+// shared expert over all T tokens; either may be null.  `tiled`: int4 codes
+// in the layout launch_pack_int4_tiled writes.  GemvArgs scale pointers
+// carry the format's scales (fp16 per 128, or E8M0 bytes per 32).
+enum { kFmtInt4 = 0, kFmtFp4 = 1, kFmtFp8 = 2 };
+bool i4mfma_supported(int K, int N, int fmt = kFmtInt4);
+hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s,
+                         int fmt = kFmtInt4);
 hipError_t launch_pack_int4_tiled(const void* src, void* dst, size_t n_mats, int N, int K, hipStream_t s);
 int gemv_rows_per_item(int wt, int mode, int K, int N, int active);
 // tokens one GEMV pass holds in registers (a group with more rows streams its

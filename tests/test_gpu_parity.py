@@ -114,6 +114,25 @@ SMALL = {
     "f32_shared": moe_inputs.MoEConfig(
         "f32_shared", T=20, d=128, E=4, k=2, F=96, act="f32", wt="f32", model="s_f32_sh",
         n_shared=1),
+    # MX experts on the skinny matrix-core kernel (d and F multiples of 1024):
+    # decode batches with the shared expert in the same launch, a down pass
+    # with K = 9216 (past int4's 8192), and groups of ~150 rows on the
+    # dequantising GEMM
+    "mxfp4_skinny": moe_inputs.MoEConfig(
+        "mxfp4_skinny", T=16, d=1024, E=16, k=4, F=1024, act="bf16", wt="mxfp4",
+        model="s_mx4_sk", n_shared=1, w_std=0.05),
+    "mxfp8_skinny": moe_inputs.MoEConfig(
+        "mxfp8_skinny", T=8, d=2048, E=8, k=2, F=1024, act="bf16", wt="mxfp8",
+        model="s_mx8_sk", n_shared=1, w_std=0.05),
+    "mxfp8_skinny_longk": moe_inputs.MoEConfig(
+        "mxfp8_skinny_longk", T=6, d=1024, E=4, k=2, F=9216, act="bf16", wt="mxfp8",
+        model="s_mx8_lk", w_std=0.05),
+    "mxfp4_rem": moe_inputs.MoEConfig(
+        "mxfp4_rem", T=300, d=1024, E=4, k=2, F=1024, act="bf16", wt="mxfp4",
+        model="s_mx4_rem", n_shared=1, w_std=0.05),
+    "mxfp8_rem": moe_inputs.MoEConfig(
+        "mxfp8_rem", T=300, d=1024, E=4, k=2, F=1024, act="bf16", wt="mxfp8",
+        model="s_mx8_rem", n_shared=1, w_std=0.05),
     # the shape limits moe.h states: k = 16 of E = 256; d and F at 16384 for
     # bf16 and the quantised formats (bf16 gate/up on the GEMV variant with two
     # tokens per pass, K from 8192 to 16384; int4 on the GEMV, K above the int4
@@ -371,8 +390,8 @@ def _steps(cfg, d, tau=0):
 @pytest.mark.parametrize("tau", [0, -1])
 def test_steps_parity(orc, name, tau):
     cfg = SMALL[name]
-    if tau == -1 and cfg.wt not in ("bf16", "int4"):
-        pytest.skip("tau only selects kernels for bf16 and int4-g128 weights")
+    if tau == -1 and cfg.wt not in ("bf16", "int4", "mxfp4", "mxfp8"):
+        pytest.skip("tau only selects kernels for bf16, int4-g128 and MX weights")
     say(f"steps parity {name} tau={tau}")
     d = device_inputs(cfg)
     g = _steps(cfg, d, tau)
@@ -667,13 +686,14 @@ def test_single_tile_list(orc, name):
         assert min(seen[0]) > 128 and min(c[3] for c in seen[1:]) < 128
 
 
-def test_int4_groups_on_both_sides_of_tau(orc):
-    """int4-g128 with the default tau (32 rows) and a mean group below twice
-    that: groups of at most 32 rows on the skinny int4 kernel, larger ones on
-    the dequantising GEMM, in one call -- expert 0 takes every token (a bias),
-    the runner-ups spread over the rest."""
-    cfg = SMALL["int4_dq"]
-    say("int4 groups on both sides of tau")
+@pytest.mark.parametrize("name", ["int4_dq", "mxfp4_rem", "mxfp8_rem"])
+def test_int4_groups_on_both_sides_of_tau(orc, name):
+    """int4-g128 and MX weights with the default tau (32 rows) and a mean
+    group below twice that: groups of at most 32 rows on the skinny
+    matrix-core kernel, larger ones on the dequantising GEMM, in one call --
+    expert 0 takes every token (a bias), the runner-ups spread over the rest."""
+    cfg = SMALL[name]
+    say(f"{name}: groups on both sides of tau")
     d = device_inputs(cfg)
     W, S = oracle_weights(d)
     wr = np_store(d["w_router"])
@@ -683,23 +703,25 @@ def test_int4_groups_on_both_sides_of_tau(orc):
         xs = d["x"][:TT].contiguous()
         y, c, i = run_layer(cfg, dict(d, b_router=torch.from_numpy(b).to(DEV)), x=xs)
         cl = c.cpu().tolist()
-        y_f, _, _, _ = orc.layer_forward(np_store(xs), "bf16", "int4", cfg.k, wr, b, W, S,
+        y_f, _, _, _ = orc.layer_forward(np_store(xs), "bf16", cfg.wt, cfg.k, wr, b, W, S,
                                          forced_idx=i.cpu().numpy())
         err = tokenwise_rel(np_f64(y), y_f).max()
         say(f"  T={TT} counts {cl} max rel {err:.3g}")
         assert cl[0] == TT and min(cl[1:]) <= 32 and TT * cfg.k < 2 * 32 * cfg.E
-        assert err < TOL["int4"]
+        assert err < TOL[cfg.wt]
 
 
-def test_int4_dq_remainders(orc):
-    """int4-g128 with every group on the dequantising GEMM (T*k >= 64 E): a
-    group's last 128-row tile of at most 16 rows runs on the skinny int4
-    kernel instead, a longer one on the GEMM.  Hand-made groups through
-    moe_expert_ffn: remainders 0, 1, 8, 12, 16 and 17, whole groups of 1 to
-    17 rows, an empty expert, and the shared expert over T = 136 (a remainder
-    of 8 rows) and T = 150 (22 rows, on the GEMM)."""
-    cfg = SMALL["int4_dq"]
-    say("int4 dq remainders on the skinny kernel")
+@pytest.mark.parametrize("name", ["int4_dq", "mxfp4_rem", "mxfp8_rem"])
+def test_int4_dq_remainders(orc, name):
+    """Weights with every group on the dequantising GEMM (T*k >= 64 E).
+    int4-g128: a group's last partial 128-row tile of at most 16 rows runs on
+    the skinny matrix-core kernel instead, a longer one on the GEMM; MX
+    weights keep every row on the GEMM.  Hand-made groups through
+    moe_expert_ffn: remainders 0, 1, 8, 12, 16 and 17, whole groups of 1 to 17
+    rows, an empty expert, and the shared expert over T = 136 (a remainder of
+    8 rows) and T = 150 (22 rows)."""
+    cfg = SMALL[name]
+    say(f"{name}: dq remainders on the skinny kernel")
     d = device_inputs(cfg)
     W, S = oracle_weights(d)
     cases = {150: ([140, 16, 0, 144], [145, 17, 9, 129], [256, 1, 2, 41]), 136: ([136, 8, 0, 128],)}
@@ -707,7 +729,7 @@ def test_int4_dq_remainders(orc):
         x = d["x"][:T].contiguous()
         xs = np_store(x)
         shape = shape_of(cfg, 0, T=T)
-        ys_ref = orc.shared_ffn(xs, "bf16", "int4", S)
+        ys_ref = orc.shared_ffn(xs, "bf16", cfg.wt, S)
         ws = torch.empty(moe.moe_workspace_bytes(shape), dtype=torch.uint8, device=DEV)
         for cs in mixes:
             assert sum(cs) == T * cfg.k
@@ -718,11 +740,11 @@ def test_int4_dq_remainders(orc):
             moe.moe_expert_ffn(shape, x, weights_struct(d), torch.tensor(cs, dtype=torch.int32, device=DEV),
                                torch.from_numpy(off).to(DEV), torch.from_numpy(perm).to(DEV), yp, ys, ws)
             torch.cuda.synchronize()
-            ref = orc.expert_ffn(xs, "bf16", "int4", W, np.array(cs, np.int32), off, perm, cfg.k)
+            ref = orc.expert_ffn(xs, "bf16", cfg.wt, W, np.array(cs, np.int32), off, perm, cfg.k)
             e1 = tokenwise_rel(yp.cpu().numpy(), ref).max()
             e2 = tokenwise_rel(ys.cpu().numpy(), ys_ref).max()
             say(f"  T={T} counts {cs}: y_perm max rel {e1:.3g}, shared {e2:.3g}")
-            assert e1 < TOL["int4"] and e2 < TOL["int4"]
+            assert e1 < TOL[cfg.wt] and e2 < TOL[cfg.wt]
 
 
 def test_rmsnorm_parity(orc):
