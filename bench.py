@@ -349,8 +349,8 @@ def ffn_paths(cfg, counts, tau):
         # groups of at most dqt rows on the skinny kernel (matrix cores when d
         # and F are multiples of 1024, int4 also at most 8192; else the int4
         # GEMV), larger ones on the dequantising GEMM; dqt = 0 (every group on
-        # the GEMM, short last tiles on the skinny kernel) once the mean group
-        # reaches 64 rows
+        # the GEMM; int4: short last tiles on the skinny kernel) once the mean
+        # group reaches 64 rows
         sk_mfma = cfg.d % 1024 == 0 and cfg.F % 1024 == 0 and (cfg.wt != "int4" or max(cfg.d, cfg.F) <= 8192)
         if cfg.wt != "int4" and not sk_mfma:
             return f"{cfg.wt} dequantising MFMA GEMM"
@@ -362,7 +362,7 @@ def ffn_paths(cfg, counts, tau):
         small = any(v <= dqt for v in c)
         big = any(v > dqt for v in c)
         gemm = f"{cfg.wt} dequantising MFMA GEMM" + (" (short last tiles on the skinny kernel)"
-                                                    if dqt == 0 and sk_mfma else "")
+                                                    if dqt == 0 and sk_mfma and cfg.wt == "int4" else "")
         return " + ".join(([skinny] if small else []) + ([gemm] if big else []))
     if cfg.wt in ("int4g64",):
         return f"{cfg.wt} dequantising MFMA GEMM"
@@ -711,8 +711,9 @@ def main():
                     help="run the workload with this many tokens instead of its own T "
                          "(the config is named <workload>_t<tokens>)")
     ap.add_argument("--int4-layout", choices=["tiled", "row-major"], default="tiled",
-                    help="int4 code layout the layer streams (tiled: packed once with "
-                         "moe_pack_int4_tiled before timing; needs d, F multiples of 1024)")
+                    help="4-bit code layout the layer streams (tiled: packed once with "
+                         "moe_pack_int4_tiled before timing; needs d, F multiples of 1024; "
+                         "int4 up to 8192, MXFP4 at decode-sized groups)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -763,6 +764,15 @@ def main():
         Wrun = moe.layer.pack_int4_tiled(W)
         torch.cuda.synchronize()
         wt = "int4_tiled"
+    elif cfg.wt == "mxfp4" and args.int4_layout == "tiled" and cfg.d % 1024 == 0 and cfg.F % 1024 == 0 \
+            and cfg.T * cfg.k < 64 * cfg.E:
+        # decode-sized groups: every group runs the skinny kernel, which reads
+        # the tiled layout (prefill-sized groups keep row-major codes for the
+        # dequantising GEMM)
+        log("packing MXFP4 codes into the tiled layout")
+        Wrun = moe.layer.pack_int4_tiled(W)
+        torch.cuda.synchronize()
+        wt = "mxfp4_tiled"
     run = Runner(cfg, x, wr, br, Wrun, tau=args.tau, wt=wt)
     if cfg.name == "mixtral_prefill":   # the prefill protocol, whatever the flags
         steps, warmup = max(steps, 50), max(warmup, 20)
@@ -849,11 +859,16 @@ def main():
                 dname, dT = dec
                 dcfg = qcfg.replace(name=dname, T=dT)
                 log(f"{dname}: the same experts at decode, T={dT}")
-                drun = Runner(dcfg, qx[:dT].contiguous(), qwr, qbr, qW, tau=args.tau)
+                dW, dwt = qW, None
+                if qcfg.wt == "mxfp4":
+                    # MXFP4 codes packed once into the tiled layout the skinny kernel streams
+                    dW, dwt = moe.layer.pack_int4_tiled(qW), "mxfp4_tiled"
+                    torch.cuda.synchronize()
+                drun = Runner(dcfg, qx[:dT].contiguous(), qwr, qbr, dW, tau=args.tau, wt=dwt)
                 dleg = workload_leg(drun, steps, warmup, args.tau, ceilings)
                 out[dname] = leg_summary(dcfg, dleg, steps, warmup)
                 log(json.dumps(out[dname]))
-                del drun
+                del drun, dW
             del qW, qx
             torch.cuda.empty_cache()
         del iW

@@ -65,9 +65,14 @@ typedef enum {
     MOE_MXFP4 = 5,          /* weights only: OCP MX fp4, E2M1 codes two per byte (even K
                                index in the low nibble), one E8M0 scale byte per 32
                                consecutive K elements: w = e2m1 * 2^(s - 127) */
-    MOE_MXFP8 = 6           /* weights only: OCP MX fp8, E4M3 codes one per byte, one
+    MOE_MXFP8 = 6,          /* weights only: OCP MX fp8, E4M3 codes one per byte, one
                                E8M0 scale byte per 32 K elements ([P5] §6: models
                                shipped as native MXFP4 / FP8 checkpoints) */
+    MOE_MXFP4_TILED = 7     /* weights only: MXFP4 codes and scales, the code bytes of
+                               every [N][K/2] matrix in the tiled order that
+                               moe_pack_int4_tiled writes (scales stay [N][K/32]);
+                               every group runs the skinny matrix-core kernel; needs d
+                               and F multiples of 1024 */
 } moe_dtype;
 
 /* Shape of one MoE layer call.
@@ -240,9 +245,9 @@ int moe_rmsnorm(const moe_shape *shape, const void *h, const float *gamma, float
 int moe_topk_overlap(const moe_shape *shape, const int32_t *pred_idx, const int32_t *actual_idx,
                      int32_t *hist, void *stream, char *err, size_t err_len);
 
-/* Weight preparation, once per weight set: rewrite int4 code bytes from the
- * row-major layout of MOE_INT4_G128 ([N][K/2] per matrix, [P5] §7.3) into the
- * tiled layout of MOE_INT4_G128_TILED.  The tiled matrix cuts the rows into
+/* Weight preparation, once per weight set: rewrite 4-bit code bytes from the
+ * row-major layout of MOE_INT4_G128 or MOE_MXFP4 ([N][K/2] per matrix, [P5]
+ * §7.3, §6) into the tiled layout of MOE_INT4_G128_TILED / MOE_MXFP4_TILED.  The tiled matrix cuts the rows into
  * sets of 16; set s, 128-element group g (K = 128 g .. 128 g + 127) is 1 KB at
  * byte ((s * K/128) + g) * 1024, made of 64 pieces of 16 bytes: piece
  * 16 q + r (q = 0..3, r = 0..15) is bytes [64 g + 16 q, 64 g + 16 q + 16) of

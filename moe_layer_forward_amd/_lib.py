@@ -16,9 +16,10 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_EUNSUPPORTED = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_INT4_G128, MOE_INT4_G128_TILED = 0, 1, 2, 3
-MOE_INT4_G64, MOE_MXFP4, MOE_MXFP8 = 4, 5, 6
+MOE_INT4_G64, MOE_MXFP4, MOE_MXFP8, MOE_MXFP4_TILED = 4, 5, 6, 7
 DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128, "int4_tiled": MOE_INT4_G128_TILED,
-               "int4g64": MOE_INT4_G64, "mxfp4": MOE_MXFP4, "mxfp8": MOE_MXFP8}
+               "int4g64": MOE_INT4_G64, "mxfp4": MOE_MXFP4, "mxfp8": MOE_MXFP8,
+               "mxfp4_tiled": MOE_MXFP4_TILED}
 
 EXPORTS = ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_forward_noalloc", "moe_workspace_bytes", "moe_rmsnorm", "moe_pack_int4_tiled", "moe_topk_overlap", "moe_strerror")

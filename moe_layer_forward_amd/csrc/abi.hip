@@ -85,7 +85,7 @@ int check_shape(const moe_shape* s, char* err, size_t err_len) {
         return fail(err, err_len, MOE_EINVAL, "n_shared=%d must be 0 or 1", s->n_shared);
     if (s->act != MOE_F32 && s->act != MOE_BF16)
         return fail(err, err_len, MOE_EINVAL, "act=%d is not MOE_F32 or MOE_BF16", s->act);
-    if (s->wt < MOE_F32 || s->wt > MOE_MXFP8)
+    if (s->wt < MOE_F32 || s->wt > MOE_MXFP4_TILED)
         return fail(err, err_len, MOE_EINVAL, "wt=%d is not a moe_dtype", s->wt);
     const bool int4 = s->wt == MOE_INT4_G128 || s->wt == MOE_INT4_G128_TILED;
     const bool quant = s->wt >= MOE_INT4_G128;
@@ -104,10 +104,14 @@ int check_shape(const moe_shape* s, char* err, size_t err_len) {
     if ((s->wt == MOE_BF16 || quant) && ((size_t)s->T * s->k * s->F * 2 >= ((size_t)1 << 31) ||
                                          (size_t)s->T * s->d * 2 >= ((size_t)1 << 31)))
         return fail(err, err_len, MOE_EUNSUPPORTED, "T*k*F and T*d bf16 buffers must stay below 2 GiB");
-    // the tiled layout is read by the int4 MFMA kernel only
+    // the tiled layouts are read by the skinny matrix-core kernel only
     if (s->wt == MOE_INT4_G128_TILED && (!i4mfma_supported(s->d, s->F) || !i4mfma_supported(s->F, s->d)))
         return fail(err, err_len, MOE_EUNSUPPORTED,
                     "tiled int4 weights need d and F multiples of 1024 and at most 8192 (d=%d F=%d)", s->d, s->F);
+    if (s->wt == MOE_MXFP4_TILED &&
+        (!i4mfma_supported(s->d, s->F, kFmtFp4) || !i4mfma_supported(s->F, s->d, kFmtFp4)))
+        return fail(err, err_len, MOE_EUNSUPPORTED, "tiled MXFP4 weights need d and F multiples of 1024 (d=%d F=%d)",
+                    s->d, s->F);
     // the GEMV's register-resident token fragments bound K; the quantised
     // formats are held to the 16384 the header states (the int4 GEMV could
     // take 32768; the dequantising GEMM has no such bound)
@@ -129,8 +133,10 @@ bool is_int4(const moe_shape* s) { return s->wt == MOE_INT4_G128 || s->wt == MOE
 
 // MX weights whose d and F the skinny matrix-core kernel takes (ffn_i4mfma.hip)
 int mx_fmt(const moe_shape* s) {
-    return s->wt == MOE_MXFP4 ? kFmtFp4 : s->wt == MOE_MXFP8 ? kFmtFp8 : -1;
+    return (s->wt == MOE_MXFP4 || s->wt == MOE_MXFP4_TILED) ? kFmtFp4 : s->wt == MOE_MXFP8 ? kFmtFp8 : -1;
 }
+// code bytes in the tiled layout: only the skinny matrix-core kernel reads them
+bool tiled_codes(const moe_shape* s) { return s->wt == MOE_INT4_G128_TILED || s->wt == MOE_MXFP4_TILED; }
 bool mx_skinny(const moe_shape* s) {
     const int f = mx_fmt(s);
     return f >= 0 && i4mfma_supported(s->d, s->F, f) && i4mfma_supported(s->F, s->d, f);
@@ -162,6 +168,7 @@ int dq_format(const moe_shape* s) {
 // and the skinny launches (which would find no work) are left out; int4-g64
 // and other MX shapes run every group on it.
 int dq_tau(const moe_shape* s) {
+    if (tiled_codes(s)) return -1;
     if (s->wt == MOE_INT4_G128 || mx_skinny(s)) {
         if (s->tau < 0) return -1;
         if (s->tau > 0) return s->tau;
@@ -177,6 +184,7 @@ int dq_tau(const moe_shape* s) {
 // skinny int4 launches.
 bool shared_as_group(const moe_shape* s) {
     if (!s->n_shared) return false;
+    if (tiled_codes(s)) return false;
     if (!is_int4(s) && !mx_skinny(s)) return true;
     const int t = dq_tau(s);
     return t >= 0 && s->T > t;
@@ -333,7 +341,7 @@ int run_groups(const moe_shape* s, const void* x, const moe_weights* w, const in
     q.topk = 1; q.T = s->T; q.E = 1; q.tau = -1;
     const GemvArgs* qp = (s->n_shared && (is_int4(s) || mx_skinny(s)) && !shared_as_group(s)) ? &q : nullptr;
     const int active = (s->T * s->k < s->E) ? s->T * s->k : s->E;   // experts that can be hit
-    const bool tiled = s->wt == MOE_INT4_G128_TILED;
+    const bool tiled = tiled_codes(s);
     // bf16 groups below the MFMA tiles: when one of them is larger than a
     // GEMV pass (lo rows), the skinny MFMA kernel (one pass of up to 64
     // tokens) takes every group below the tiles in one balanced launch and

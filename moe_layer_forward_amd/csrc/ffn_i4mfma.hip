@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     constexpr bool FP8 = FMT == kFmtFp8;
     constexpr int NW = FP8 ? 2 : 1;             // 16-byte code loads per lane, group and matrix
     static_assert(MX || RING == 8, "the int4 scale prefetch runs 8 steps ahead, as far as the ring");
-    static_assert(!MX || !TILED, "the tiled layout holds int4 codes");
+    static_assert(!FP8 || !TILED, "the tiled layout holds 4-bit codes");
     static_assert(RING % 2 == 0 && RING <= 16, "steps are loaded in pairs within the 16-step unroll");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ int s_act[kMaxE + 1], s_cnt[kMaxE + 1], s_off[kMaxE + 1], s_ipref[kMaxE + 2];
@@ -561,7 +561,7 @@ bool i4mfma_supported(int K, int N, int fmt) {
 hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s,
                          int fmt) {
     if (fmt != kFmtInt4 && fmt != kFmtFp4 && fmt != kFmtFp8) return hipErrorInvalidValue;
-    if (tiled && fmt != kFmtInt4) return hipErrorInvalidValue;
+    if (tiled && fmt == kFmtFp8) return hipErrorInvalidValue;
     const GemvArgs& g = routed ? *routed : *shared;
     I4Args a{};
     if (routed) {
@@ -599,17 +599,17 @@ hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const Gem
     // 8 scale groups per wave in flight: 16 KB (gate/up) or 8 KB (down); fp8
     // codes take twice the bytes per group, so 4 groups
     auto k = mode == 0 ? (fmt == kFmtFp8   ? i4_mfma_kernel<0, 4, false, kFmtFp8>
-                          : fmt == kFmtFp4 ? i4_mfma_kernel<0, 8, false, kFmtFp4>
+                          : fmt == kFmtFp4 ? (tiled ? i4_mfma_kernel<0, 8, true, kFmtFp4> : i4_mfma_kernel<0, 8, false, kFmtFp4>)
                           : tiled          ? i4_mfma_kernel<0, 8, true, kFmtInt4>
                                            : i4_mfma_kernel<0, 8, false, kFmtInt4>)
                        : (fmt == kFmtFp8   ? i4_mfma_kernel<1, 4, false, kFmtFp8>
-                          : fmt == kFmtFp4 ? i4_mfma_kernel<1, 8, false, kFmtFp4>
+                          : fmt == kFmtFp4 ? (tiled ? i4_mfma_kernel<1, 8, true, kFmtFp4> : i4_mfma_kernel<1, 8, false, kFmtFp4>)
                           : tiled          ? i4_mfma_kernel<1, 8, true, kFmtInt4>
                                            : i4_mfma_kernel<1, 8, false, kFmtInt4>);
     // dynamic LDS beyond 64 KB: the budget left next to the static arrays,
     // set once per device and kernel variant
-    static std::atomic<int> attr_set[8][kMaxDevices];
-    const int ki = mode * 4 + (fmt == kFmtInt4 ? (tiled ? 1 : 0) : fmt + 1);
+    static std::atomic<int> attr_set[10][kMaxDevices];
+    const int ki = mode * 5 + (fmt == kFmtFp8 ? 4 : 2 * fmt + (tiled ? 1 : 0));
     per_device_int(attr_set[ki], [&] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)(kLdsBytes - kStaticLds));

@@ -48,8 +48,8 @@ int gemv_max_k(int wt);
 // Skinny groups of int4-g128, MXFP4 or MXFP8 weights on the matrix cores
 // (ffn_i4mfma.hip): K a multiple of 1024 (int4: at most 8192).  One launch serves
 // the routed experts (counts/offsets set) and, when `shared` is given, the
-// shared expert over all T tokens; either may be null.  `tiled`: int4 codes
-// in the layout launch_pack_int4_tiled writes.  GemvArgs scale pointers
+// shared expert over all T tokens; either may be null.  `tiled`: 4-bit codes
+// (int4 or MXFP4) in the layout launch_pack_int4_tiled writes.  GemvArgs scale pointers
 // carry the format's scales (fp16 per 128, or E8M0 bytes per 32).
 enum { kFmtInt4 = 0, kFmtFp4 = 1, kFmtFp8 = 2 };
 bool i4mfma_supported(int K, int N, int fmt = kFmtInt4);

@@ -58,10 +58,11 @@ class MoELayer:
 
 
 def pack_int4_tiled(weights: dict, stream=None) -> dict:
-    """Copy of an int4 weight dict with every code tensor (w_*, sh_* of shape
-    [..., N, K/2], uint8, row-major) rewritten by moe_pack_int4_tiled into the
-    layout of MOE_INT4_G128_TILED; scales and other entries are passed through.
-    Done once per weight set, before the layer runs with wt="int4_tiled"."""
+    """Copy of an int4 or MXFP4 weight dict with every code tensor (w_*, sh_* of
+    shape [..., N, K/2], uint8, row-major) rewritten by moe_pack_int4_tiled into
+    the tiled layout; scales and other entries are passed through.  Done once
+    per weight set, before the layer runs with wt="int4_tiled" or
+    "mxfp4_tiled"."""
     out = dict(weights)
     for n in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
         t = weights.get(n)
@@ -69,7 +70,7 @@ def pack_int4_tiled(weights: dict, stream=None) -> dict:
             continue
         t = _dev(t)
         if t.dtype != torch.uint8 or t.dim() < 2:
-            raise ValueError(f"{n}: int4 codes must be a uint8 tensor [..., N, K/2]")
+            raise ValueError(f"{n}: 4-bit codes must be a uint8 tensor [..., N, K/2]")
         N, K = t.shape[-2], t.shape[-1] * 2
         dst = torch.empty_like(t)
         _lib.moe_pack_int4_tiled(t, dst, t.numel() // (N * (K // 2)), N, K, stream=stream)

@@ -76,6 +76,8 @@ BAD_SHAPES = [
     (dict(wt="int4_tiled", F=9216), moe.MOE_EUNSUPPORTED),         # K above 8192 (down)
     (dict(wt="int4_tiled", d=4104), moe.MOE_EINVAL),
     (dict(act="f32", wt="int4_tiled", F=4096), moe.MOE_EUNSUPPORTED),
+    (dict(wt="mxfp4_tiled", d=4096 + 64), moe.MOE_EUNSUPPORTED),    # K not a multiple of 1024
+    (dict(wt="mxfp4_tiled", d=4104), moe.MOE_EINVAL),               # not a multiple of 64
 ]
 
 

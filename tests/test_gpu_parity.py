@@ -124,6 +124,9 @@ SMALL = {
     "mxfp8_skinny": moe_inputs.MoEConfig(
         "mxfp8_skinny", T=8, d=2048, E=8, k=2, F=1024, act="bf16", wt="mxfp8",
         model="s_mx8_sk", n_shared=1, w_std=0.05),
+    "mxfp4_wide_k": moe_inputs.MoEConfig(
+        "mxfp4_wide_k", T=20, d=7168, E=4, k=4, F=1024, act="bf16", wt="mxfp4",
+        model="s_mx4_wk", w_std=0.05),
     "mxfp8_skinny_longk": moe_inputs.MoEConfig(
         "mxfp8_skinny_longk", T=6, d=1024, E=4, k=2, F=9216, act="bf16", wt="mxfp8",
         model="s_mx8_lk", w_std=0.05),
@@ -465,17 +468,18 @@ def test_pack_int4_tiled_layout():
     moe.moe_pack_int4_tiled(None, None, 0, 16, 128)
 
 
-TILED = ["int4_mfma_multipass", "int4_mfma_wide_k", "int4_mfma_many"]
+TILED = ["int4_mfma_multipass", "int4_mfma_wide_k", "int4_mfma_many", "mxfp4_skinny", "mxfp4_wide_k"]
 
 
 @pytest.mark.parametrize("name", TILED)
 def test_layer_int4_tiled(orc, name):
-    """Tiled int4 codes: the layer against the oracle (which reads the row-major
-    codes), and bit-identical to the row-major run (same arithmetic)."""
+    """Tiled 4-bit codes (int4 or MXFP4): the layer against the oracle (which
+    reads the row-major codes), and bit-identical to the row-major run (same
+    arithmetic)."""
     cfg = SMALL[name]
-    say(f"layer int4 tiled {name}")
+    say(f"layer {cfg.wt} tiled {name}")
     d = device_inputs(cfg)
-    y, counts, idx = run_layer(cfg, tiled_inputs(d), wt="int4_tiled")
+    y, counts, idx = run_layer(cfg, tiled_inputs(d), wt=f"{cfg.wt}_tiled")
     W, S = oracle_weights(d)
     x = np_store(d["x"])
     wr, br = np_store(d["w_router"]), np_store(d["b_router"])
@@ -485,8 +489,8 @@ def test_layer_int4_tiled(orc, name):
     y_f, _, _, _ = orc.layer_forward(x, cfg.act, cfg.wt, cfg.k, wr, br, W, S, forced_idx=gi)
     err = tokenwise_rel(np_f64(y), y_f)
     say(f"  max rel {err.max():.3g} flips {flips}")
-    assert err.max() < TOL["int4_tiled"]
-    # row-major codes on the same skinny int4 kernels (tau < 0: no group on the
+    assert err.max() < TOL[cfg.wt]
+    # row-major codes on the same skinny kernels (tau < 0: no group on the
     # dequantising GEMM): the same arithmetic, bit for bit
     y_rm, _, idx_rm = run_layer(cfg, d, tau=-1)
     assert torch.equal(idx, idx_rm) and torch.equal(y, y_rm)
