@@ -267,8 +267,9 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     const uint32_t lrow = (uint32_t)(wave * 16 + (lane & 15));
     const uint32_t lq = (uint32_t)(lane >> 4);
     // lane part of a weight offset, and the offset step from one group to the
-    // next: row-major (row lrow, bytes 64 g + 16 lq) or tiled (16-row set
-    // `wave` of the item, 1 KB per group, lane-ordered 16-byte pieces)
+    // next: row-major (row lrow, bytes 64 g + 16 lq; fp8 codes 128 g + 32 lq)
+    // or tiled (16-row set `wave` of the item, 1 KB per group, lane-ordered
+    // 16-byte pieces)
     const uint32_t woff_l =
         TILED ? (uint32_t)wave * 16u * rb + (uint32_t)lane * 16u : lrow * rb + lq * (FP8 ? 32u : 16u);
     constexpr uint32_t kGroupStep = TILED ? 1024u : (FP8 ? 128u : 64u);
