@@ -711,9 +711,9 @@ def main():
                     help="run the workload with this many tokens instead of its own T "
                          "(the config is named <workload>_t<tokens>)")
     ap.add_argument("--int4-layout", choices=["tiled", "row-major"], default="tiled",
-                    help="4-bit code layout the layer streams (tiled: packed once with "
-                         "moe_pack_int4_tiled before timing; needs d, F multiples of 1024; "
-                         "int4 up to 8192, MXFP4 at decode-sized groups)")
+                    help="code layout the layer streams (tiled: packed once with "
+                         "moe_pack_int4_tiled / moe_pack_mxfp8_tiled before timing; needs d, F "
+                         "multiples of 1024; int4 up to 8192, MXFP4 and MXFP8 at decode-sized groups)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters)")
@@ -764,15 +764,15 @@ def main():
         Wrun = moe.layer.pack_int4_tiled(W)
         torch.cuda.synchronize()
         wt = "int4_tiled"
-    elif cfg.wt == "mxfp4" and args.int4_layout == "tiled" and cfg.d % 1024 == 0 and cfg.F % 1024 == 0 \
-            and cfg.T * cfg.k < 64 * cfg.E:
+    elif cfg.wt in ("mxfp4", "mxfp8") and args.int4_layout == "tiled" and cfg.d % 1024 == 0 \
+            and cfg.F % 1024 == 0 and cfg.T * cfg.k < 64 * cfg.E:
         # decode-sized groups: every group runs the skinny kernel, which reads
         # the tiled layout (prefill-sized groups keep row-major codes for the
         # dequantising GEMM)
-        log("packing MXFP4 codes into the tiled layout")
-        Wrun = moe.layer.pack_int4_tiled(W)
+        log(f"packing {cfg.wt.upper()} codes into the tiled layout")
+        Wrun = moe.layer.pack_int4_tiled(W) if cfg.wt == "mxfp4" else moe.layer.pack_mxfp8_tiled(W)
         torch.cuda.synchronize()
-        wt = "mxfp4_tiled"
+        wt = f"{cfg.wt}_tiled"
     run = Runner(cfg, x, wr, br, Wrun, tau=args.tau, wt=wt)
     if cfg.name == "mixtral_prefill":   # the prefill protocol, whatever the flags
         steps, warmup = max(steps, 50), max(warmup, 20)
@@ -860,9 +860,10 @@ def main():
                 dcfg = qcfg.replace(name=dname, T=dT)
                 log(f"{dname}: the same experts at decode, T={dT}")
                 dW, dwt = qW, None
-                if qcfg.wt == "mxfp4":
-                    # MXFP4 codes packed once into the tiled layout the skinny kernel streams
-                    dW, dwt = moe.layer.pack_int4_tiled(qW), "mxfp4_tiled"
+                if qcfg.wt in ("mxfp4", "mxfp8"):
+                    # MX codes packed once into the tiled layout the skinny kernel streams
+                    pack = moe.layer.pack_int4_tiled if qcfg.wt == "mxfp4" else moe.layer.pack_mxfp8_tiled
+                    dW, dwt = pack(qW), f"{qcfg.wt}_tiled"
                     torch.cuda.synchronize()
                 drun = Runner(dcfg, qx[:dT].contiguous(), qwr, qbr, dW, tau=args.tau, wt=dwt)
                 dleg = workload_leg(drun, steps, warmup, args.tau, ceilings)

@@ -68,9 +68,14 @@ typedef enum {
     MOE_MXFP8 = 6,          /* weights only: OCP MX fp8, E4M3 codes one per byte, one
                                E8M0 scale byte per 32 K elements ([P5] §6: models
                                shipped as native MXFP4 / FP8 checkpoints) */
-    MOE_MXFP4_TILED = 7     /* weights only: MXFP4 codes and scales, the code bytes of
+    MOE_MXFP4_TILED = 7,    /* weights only: MXFP4 codes and scales, the code bytes of
                                every [N][K/2] matrix in the tiled order that
                                moe_pack_int4_tiled writes (scales stay [N][K/32]);
+                               every group runs the skinny matrix-core kernel; needs d
+                               and F multiples of 1024 */
+    MOE_MXFP8_TILED = 8     /* weights only: MXFP8 codes and scales, the code bytes of
+                               every [N][K] matrix in the tiled order that
+                               moe_pack_mxfp8_tiled writes (scales stay [N][K/32]);
                                every group runs the skinny matrix-core kernel; needs d
                                and F multiples of 1024 */
 } moe_dtype;
@@ -98,7 +103,7 @@ typedef enum {
  *        to the skinny matrix-core kernel); negative keeps every group on the
  *        skinny kernels.  MXFP4 and MXFP8 with d and F multiples of 1024: the
  *        same rule on the skinny matrix-core kernel (without the short-tile
- *        path); other MX shapes, fp32, tiled int4 and int4-g64 ignore tau.
+ *        path); other MX shapes, fp32, the tiled formats and int4-g64 ignore tau.
  * Limits (MOE_EINVAL otherwise): T >= 0, 1 <= k <= E <= 256, k <= 16,
  *   d, F >= 8 and multiples of 8; int4-g128: d and F multiples of 128;
  *   int4-g64, MXFP4, MXFP8: multiples of 64.
@@ -119,7 +124,7 @@ typedef struct {
  *   w_down:       [E][d][F]   (int4, MXFP4: uint8 [E][d][F/2]; MXFP8: uint8 [E][d][F])
  *   s_*: scales of the quantised formats, NULL otherwise: fp16 [E][N][K/128]
  *        (MOE_INT4_G128, _TILED) or [E][N][K/64] (MOE_INT4_G64); uint8 E8M0
- *        [E][N][K/32] (MOE_MXFP4, MOE_MXFP8).
+ *        [E][N][K/32] (MOE_MXFP4, MOE_MXFP8, _TILED).
  *   sh_*: the shared expert, same layouts with E = 1; NULL when n_shared == 0. */
 typedef struct {
     const void *w_gate, *w_up, *w_down;
@@ -261,6 +266,23 @@ int moe_topk_overlap(const moe_shape *shape, const int32_t *pred_idx, const int3
  * Asynchronous on stream. */
 int moe_pack_int4_tiled(const void *src, void *dst, int64_t n_mats, int32_t N, int32_t K,
                         void *stream, char *err, size_t err_len);
+
+/* Weight preparation, once per weight set: rewrite MXFP8 code bytes (E4M3, one
+ * per byte) from the row-major layout of MOE_MXFP8 ([N][K] per matrix, [P5] §6)
+ * into the tiled layout of MOE_MXFP8_TILED.  The tiled matrix cuts the rows into
+ * sets of 16; set s, 128-element group g (K = 128 g .. 128 g + 127) is 2 KB at
+ * byte ((s * K/128) + g) * 2048, made of 128 pieces of 16 bytes: piece
+ * 64 w + 16 q + r (w = 0..1, q = 0..3, r = 0..15) is bytes
+ * [128 g + 32 q + 16 w, + 16) of row 16 s + r (its K elements
+ * 128 g + 32 q + 16 w .. + 15).  The matrix size (N * K bytes) is unchanged.
+ *   src, dst: device, n_mats * N * K bytes each, 16-byte aligned, not
+ *             overlapping (caller-owned; dst is written, src only read)
+ *   n_mats >= 0 matrices of N rows (N a positive multiple of 16) and K columns
+ *   (K a positive multiple of 128); e.g. w_gate: n_mats = E, N = F, K = d.
+ * MOE_EINVAL for a bad size, a NULL, misaligned or overlapping pointer.
+ * Asynchronous on stream. */
+int moe_pack_mxfp8_tiled(const void *src, void *dst, int64_t n_mats, int32_t N, int32_t K,
+                         void *stream, char *err, size_t err_len);
 
 /* Static text of a moe_status. */
 const char *moe_strerror(int status);

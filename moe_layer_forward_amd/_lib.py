@@ -16,13 +16,14 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_EUNSUPPORTED = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_INT4_G128, MOE_INT4_G128_TILED = 0, 1, 2, 3
-MOE_INT4_G64, MOE_MXFP4, MOE_MXFP8, MOE_MXFP4_TILED = 4, 5, 6, 7
+MOE_INT4_G64, MOE_MXFP4, MOE_MXFP8, MOE_MXFP4_TILED, MOE_MXFP8_TILED = 4, 5, 6, 7, 8
 DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128, "int4_tiled": MOE_INT4_G128_TILED,
                "int4g64": MOE_INT4_G64, "mxfp4": MOE_MXFP4, "mxfp8": MOE_MXFP8,
-               "mxfp4_tiled": MOE_MXFP4_TILED}
+               "mxfp4_tiled": MOE_MXFP4_TILED, "mxfp8_tiled": MOE_MXFP8_TILED}
 
 EXPORTS = ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-           "moe_layer_forward_noalloc", "moe_workspace_bytes", "moe_rmsnorm", "moe_pack_int4_tiled", "moe_topk_overlap", "moe_strerror")
+           "moe_layer_forward_noalloc", "moe_workspace_bytes", "moe_rmsnorm", "moe_pack_int4_tiled",
+           "moe_pack_mxfp8_tiled", "moe_topk_overlap", "moe_strerror")
 
 
 class MoEError(RuntimeError):
@@ -65,12 +66,13 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_rmsnorm.argtypes = [sp, vp, vp, ctypes.c_float, vp, vp, cp, sz]
         L.moe_pack_int4_tiled.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, cp, sz]
+        L.moe_pack_mxfp8_tiled.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, vp, cp, sz]
         L.moe_topk_overlap.argtypes = [sp, i32p, i32p, i32p, vp, cp, sz]
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
         for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
                   "moe_layer_forward", "moe_layer_forward_noalloc", "moe_rmsnorm", "moe_pack_int4_tiled",
-                  "moe_topk_overlap"):
+                  "moe_pack_mxfp8_tiled", "moe_topk_overlap"):
             getattr(L, n).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -162,6 +164,11 @@ def moe_layer_forward_noalloc(shape, x, w_router, b_router, weights, residual, y
 def moe_pack_int4_tiled(src, dst, n_mats, N, K, stream=None):
     """Row-major int4 codes (n_mats x [N][K/2] bytes) -> the tiled layout."""
     return _call("moe_pack_int4_tiled", _ptr(src), _ptr(dst), int(n_mats), int(N), int(K), _stream(stream))
+
+
+def moe_pack_mxfp8_tiled(src, dst, n_mats, N, K, stream=None):
+    """Row-major MXFP8 codes (n_mats x [N][K] bytes) -> the tiled layout."""
+    return _call("moe_pack_mxfp8_tiled", _ptr(src), _ptr(dst), int(n_mats), int(N), int(K), _stream(stream))
 
 
 def moe_topk_overlap(shape, pred_idx, actual_idx, hist, stream=None):

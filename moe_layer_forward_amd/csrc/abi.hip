@@ -85,7 +85,7 @@ int check_shape(const moe_shape* s, char* err, size_t err_len) {
         return fail(err, err_len, MOE_EINVAL, "n_shared=%d must be 0 or 1", s->n_shared);
     if (s->act != MOE_F32 && s->act != MOE_BF16)
         return fail(err, err_len, MOE_EINVAL, "act=%d is not MOE_F32 or MOE_BF16", s->act);
-    if (s->wt < MOE_F32 || s->wt > MOE_MXFP4_TILED)
+    if (s->wt < MOE_F32 || s->wt > MOE_MXFP8_TILED)
         return fail(err, err_len, MOE_EINVAL, "wt=%d is not a moe_dtype", s->wt);
     const bool int4 = s->wt == MOE_INT4_G128 || s->wt == MOE_INT4_G128_TILED;
     const bool quant = s->wt >= MOE_INT4_G128;
@@ -112,6 +112,10 @@ int check_shape(const moe_shape* s, char* err, size_t err_len) {
         (!i4mfma_supported(s->d, s->F, kFmtFp4) || !i4mfma_supported(s->F, s->d, kFmtFp4)))
         return fail(err, err_len, MOE_EUNSUPPORTED, "tiled MXFP4 weights need d and F multiples of 1024 (d=%d F=%d)",
                     s->d, s->F);
+    if (s->wt == MOE_MXFP8_TILED &&
+        (!i4mfma_supported(s->d, s->F, kFmtFp8) || !i4mfma_supported(s->F, s->d, kFmtFp8)))
+        return fail(err, err_len, MOE_EUNSUPPORTED, "tiled MXFP8 weights need d and F multiples of 1024 (d=%d F=%d)",
+                    s->d, s->F);
     // the GEMV's register-resident token fragments bound K; the quantised
     // formats are held to the 16384 the header states (the int4 GEMV could
     // take 32768; the dequantising GEMM has no such bound)
@@ -133,10 +137,14 @@ bool is_int4(const moe_shape* s) { return s->wt == MOE_INT4_G128 || s->wt == MOE
 
 // MX weights whose d and F the skinny matrix-core kernel takes (ffn_i4mfma.hip)
 int mx_fmt(const moe_shape* s) {
-    return (s->wt == MOE_MXFP4 || s->wt == MOE_MXFP4_TILED) ? kFmtFp4 : s->wt == MOE_MXFP8 ? kFmtFp8 : -1;
+    return (s->wt == MOE_MXFP4 || s->wt == MOE_MXFP4_TILED)   ? kFmtFp4
+           : (s->wt == MOE_MXFP8 || s->wt == MOE_MXFP8_TILED) ? kFmtFp8
+                                                               : -1;
 }
 // code bytes in the tiled layout: only the skinny matrix-core kernel reads them
-bool tiled_codes(const moe_shape* s) { return s->wt == MOE_INT4_G128_TILED || s->wt == MOE_MXFP4_TILED; }
+bool tiled_codes(const moe_shape* s) {
+    return s->wt == MOE_INT4_G128_TILED || s->wt == MOE_MXFP4_TILED || s->wt == MOE_MXFP8_TILED;
+}
 bool mx_skinny(const moe_shape* s) {
     const int f = mx_fmt(s);
     return f >= 0 && i4mfma_supported(s->d, s->F, f) && i4mfma_supported(s->F, s->d, f);
@@ -721,6 +729,23 @@ int moe_pack_int4_tiled(const void* src, void* dst, int64_t n_mats, int32_t N, i
     if (a < b + bytes && b < a + bytes) return fail(err, err_len, MOE_EINVAL, "src and dst overlap");
     hipStream_t st = (hipStream_t)stream;
     return hip_check(launch_pack_int4_tiled(src, dst, (size_t)n_mats, N, K, st), st, "pack int4", err, err_len);
+}
+
+int moe_pack_mxfp8_tiled(const void* src, void* dst, int64_t n_mats, int32_t N, int32_t K, void* stream,
+                         char* err, size_t err_len) {
+    if (n_mats < 0) return fail(err, err_len, MOE_EINVAL, "n_mats=%lld is negative", (long long)n_mats);
+    if (N < 16 || N % 16) return fail(err, err_len, MOE_EINVAL, "N=%d must be a positive multiple of 16", N);
+    if (K < 128 || K % 128) return fail(err, err_len, MOE_EINVAL, "K=%d must be a positive multiple of 128", K);
+    const size_t bytes = (size_t)n_mats * (size_t)N * (size_t)K;
+    if (n_mats > 0 && bytes / (size_t)n_mats / (size_t)N != (size_t)K)
+        return fail(err, err_len, MOE_EINVAL, "n_mats * N * K overflows");
+    if (!bytes) return MOE_OK;
+    NEED_PTR(src, "src");
+    NEED_PTR(dst, "dst");
+    const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+    if (a < b + bytes && b < a + bytes) return fail(err, err_len, MOE_EINVAL, "src and dst overlap");
+    hipStream_t st = (hipStream_t)stream;
+    return hip_check(launch_pack_mxfp8_tiled(src, dst, (size_t)n_mats, N, K, st), st, "pack mxfp8", err, err_len);
 }
 
 }  // extern "C"

@@ -155,7 +155,6 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     constexpr bool FP8 = FMT == kFmtFp8;
     constexpr int NW = FP8 ? 2 : 1;             // 16-byte code loads per lane, group and matrix
     static_assert(MX || RING == 8, "the int4 scale prefetch runs 8 steps ahead, as far as the ring");
-    static_assert(!FP8 || !TILED, "the tiled layout holds 4-bit codes");
     static_assert(RING % 2 == 0 && RING <= 16, "steps are loaded in pairs within the 16-step unroll");
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ int s_act[kMaxE + 1], s_cnt[kMaxE + 1], s_off[kMaxE + 1], s_ipref[kMaxE + 2];
@@ -266,13 +265,15 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
     const uint32_t mat_bytes = rb * (uint32_t)N;
     const uint32_t lrow = (uint32_t)(wave * 16 + (lane & 15));
     const uint32_t lq = (uint32_t)(lane >> 4);
-    // lane part of a weight offset, and the offset step from one group to the
-    // next: row-major (row lrow, bytes 64 g + 16 lq; fp8 codes 128 g + 32 lq)
-    // or tiled (16-row set `wave` of the item, 1 KB per group, lane-ordered
-    // 16-byte pieces)
+    // lane part of a weight offset, the offset step from one group to the
+    // next and from a lane's first 16-byte piece of a group to its second
+    // (fp8): row-major (row lrow, bytes 64 g + 16 lq; fp8 codes 128 g + 32 lq)
+    // or tiled (16-row set `wave` of the item, 1 KB per group and piece,
+    // lane-ordered 16-byte pieces)
     const uint32_t woff_l =
         TILED ? (uint32_t)wave * 16u * rb + (uint32_t)lane * 16u : lrow * rb + lq * (FP8 ? 32u : 16u);
-    constexpr uint32_t kGroupStep = TILED ? 1024u : (FP8 ? 128u : 64u);
+    constexpr uint32_t kGroupStep = TILED ? 1024u * NW : (FP8 ? 128u : 64u);
+    constexpr uint32_t kPieceStep = TILED ? 1024u : 16u;
     const uint32_t soff_l = lrow * srow;                      // lane part of a scale offset
     const uint32_t lrow16 = (uint32_t)(lane & 15);
 
@@ -308,8 +309,8 @@ __global__ __launch_bounds__(kThreads, 1) void i4_mfma_kernel(I4Args a) {
         for (int m = 0; m < G; ++m)
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                wq[S][m][w] = ld16<TILED ? kNonTemporal : 0>(rsrc(weight_ptr(q, m), n0), o0 + 16u * w);
-                wq[S + 1][m][w] = ld16<TILED ? kNonTemporal : 0>(rsrc(weight_ptr(q1, m), n1), o1 + 16u * w);
+                wq[S][m][w] = ld16<TILED ? kNonTemporal : 0>(rsrc(weight_ptr(q, m), n0), o0 + kPieceStep * w);
+                wq[S + 1][m][w] = ld16<TILED ? kNonTemporal : 0>(rsrc(weight_ptr(q1, m), n1), o1 + kPieceStep * w);
             }
         q = q1;
         advance(q, 1);
@@ -562,7 +563,6 @@ bool i4mfma_supported(int K, int N, int fmt) {
 hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s,
                          int fmt) {
     if (fmt != kFmtInt4 && fmt != kFmtFp4 && fmt != kFmtFp8) return hipErrorInvalidValue;
-    if (tiled && fmt == kFmtFp8) return hipErrorInvalidValue;
     const GemvArgs& g = routed ? *routed : *shared;
     I4Args a{};
     if (routed) {
@@ -599,18 +599,18 @@ hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const Gem
     const int n_cu = cu_count();
     // 8 scale groups per wave in flight: 16 KB (gate/up) or 8 KB (down); fp8
     // codes take twice the bytes per group, so 4 groups
-    auto k = mode == 0 ? (fmt == kFmtFp8   ? i4_mfma_kernel<0, 4, false, kFmtFp8>
+    auto k = mode == 0 ? (fmt == kFmtFp8   ? (tiled ? i4_mfma_kernel<0, 4, true, kFmtFp8> : i4_mfma_kernel<0, 4, false, kFmtFp8>)
                           : fmt == kFmtFp4 ? (tiled ? i4_mfma_kernel<0, 8, true, kFmtFp4> : i4_mfma_kernel<0, 8, false, kFmtFp4>)
                           : tiled          ? i4_mfma_kernel<0, 8, true, kFmtInt4>
                                            : i4_mfma_kernel<0, 8, false, kFmtInt4>)
-                       : (fmt == kFmtFp8   ? i4_mfma_kernel<1, 4, false, kFmtFp8>
+                       : (fmt == kFmtFp8   ? (tiled ? i4_mfma_kernel<1, 4, true, kFmtFp8> : i4_mfma_kernel<1, 4, false, kFmtFp8>)
                           : fmt == kFmtFp4 ? (tiled ? i4_mfma_kernel<1, 8, true, kFmtFp4> : i4_mfma_kernel<1, 8, false, kFmtFp4>)
                           : tiled          ? i4_mfma_kernel<1, 8, true, kFmtInt4>
                                            : i4_mfma_kernel<1, 8, false, kFmtInt4>);
     // dynamic LDS beyond 64 KB: the budget left next to the static arrays,
     // set once per device and kernel variant
-    static std::atomic<int> attr_set[10][kMaxDevices];
-    const int ki = mode * 5 + (fmt == kFmtFp8 ? 4 : 2 * fmt + (tiled ? 1 : 0));
+    static std::atomic<int> attr_set[12][kMaxDevices];
+    const int ki = mode * 6 + 2 * fmt + (tiled ? 1 : 0);
     per_device_int(attr_set[ki], [&] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)(kLdsBytes - kStaticLds));
@@ -620,36 +620,47 @@ hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const Gem
     return hipGetLastError();
 }
 
-// Row-major int4 codes -> the tiled layout the kernel above streams: within
-// each matrix, 16-byte piece (set, g, q, r) of the output (set-major, then
-// group g, then lane q*16 + r) is bytes [64 g + 16 q, +16) of row 16 set + r.
-// A permutation of 16-byte pieces: one thread per output piece, coalesced
-// stores.
-__global__ __launch_bounds__(256) void pack_int4_tiled_kernel(const u32x4_t* __restrict__ src,
-                                                              u32x4_t* __restrict__ dst, size_t n_pieces,
-                                                              int N, int K) {
-    const size_t per_row = (size_t)K / 32;             // 16-byte pieces per row
+// Row-major code bytes -> the tiled layout the kernel above streams, PW
+// 16-byte pieces per lane and group (4-bit codes 1, fp8 codes 2): within each
+// matrix, 16-byte piece (set, g, w, q*16 + r) of the output (set-major, then
+// group g, then piece w, then lane) is bytes [64 PW g + 16 PW q + 16 w, +16)
+// of row 16 set + r.  A permutation of 16-byte pieces: one thread per output
+// piece, coalesced stores.
+template <int PW>
+__global__ __launch_bounds__(256) void pack_tiled_kernel(const u32x4_t* __restrict__ src,
+                                                         u32x4_t* __restrict__ dst, size_t n_pieces, int N, int K) {
+    const size_t per_row = (size_t)K * PW / 32;        // 16-byte pieces per row
     const size_t per_mat = (size_t)N * per_row;
     const int NG = K / 128;
     for (size_t j = (size_t)blockIdx.x * blockDim.x + threadIdx.x; j < n_pieces;
          j += (size_t)gridDim.x * blockDim.x) {
         const size_t mat = j / per_mat, rem = j - mat * per_mat;
         const int lane = (int)(rem & 63);
-        const size_t t = rem >> 6;
+        const size_t t = (rem >> 6) / PW;
+        const int w = (int)((rem >> 6) - t * PW);
         const size_t set = t / NG;
         const int g = (int)(t - set * NG);
         const size_t row = set * 16 + (lane & 15);
-        dst[j] = src[mat * per_mat + row * per_row + (size_t)g * 4 + (lane >> 4)];
+        dst[j] = src[mat * per_mat + row * per_row + (size_t)g * 4 * PW + (size_t)(lane >> 4) * PW + w];
     }
 }
 
-hipError_t launch_pack_int4_tiled(const void* src, void* dst, size_t n_mats, int N, int K, hipStream_t s) {
-    const size_t n = n_mats * (size_t)N * (size_t)(K / 32);
+template <int PW>
+static hipError_t launch_pack(const void* src, void* dst, size_t n_mats, int N, int K, hipStream_t s) {
+    const size_t n = n_mats * (size_t)N * (size_t)(K / 32) * PW;
     if (n == 0) return hipSuccess;
     const size_t blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(pack_int4_tiled_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s,
+    hipLaunchKernelGGL(pack_tiled_kernel<PW>, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, s,
                        reinterpret_cast<const u32x4_t*>(src), reinterpret_cast<u32x4_t*>(dst), n, N, K);
     return hipGetLastError();
+}
+
+hipError_t launch_pack_int4_tiled(const void* src, void* dst, size_t n_mats, int N, int K, hipStream_t s) {
+    return launch_pack<1>(src, dst, n_mats, N, K, s);
+}
+
+hipError_t launch_pack_mxfp8_tiled(const void* src, void* dst, size_t n_mats, int N, int K, hipStream_t s) {
+    return launch_pack<2>(src, dst, n_mats, N, K, s);
 }
 
 }  // namespace moe

@@ -49,13 +49,16 @@ int gemv_max_k(int wt);
 // (ffn_i4mfma.hip): K a multiple of 1024 (int4: at most 8192).  One launch serves
 // the routed experts (counts/offsets set) and, when `shared` is given, the
 // shared expert over all T tokens; either may be null.  `tiled`: 4-bit codes
-// (int4 or MXFP4) in the layout launch_pack_int4_tiled writes.  GemvArgs scale pointers
+// (int4 or MXFP4) in the layout launch_pack_int4_tiled writes, or fp8 codes in
+// the one launch_pack_mxfp8_tiled writes.  GemvArgs scale pointers
 // carry the format's scales (fp16 per 128, or E8M0 bytes per 32).
 enum { kFmtInt4 = 0, kFmtFp4 = 1, kFmtFp8 = 2 };
 bool i4mfma_supported(int K, int N, int fmt = kFmtInt4);
 hipError_t launch_i4mfma(int mode, bool tiled, const GemvArgs* routed, const GemvArgs* shared, hipStream_t s,
                          int fmt = kFmtInt4);
 hipError_t launch_pack_int4_tiled(const void* src, void* dst, size_t n_mats, int N, int K, hipStream_t s);
+// The same for fp8 codes (MXFP8): two 16-byte pieces per lane and group.
+hipError_t launch_pack_mxfp8_tiled(const void* src, void* dst, size_t n_mats, int N, int K, hipStream_t s);
 int gemv_rows_per_item(int wt, int mode, int K, int N, int active);
 // tokens one GEMV pass holds in registers (a group with more rows streams its
 // weights once per pass)

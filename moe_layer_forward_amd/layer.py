@@ -63,6 +63,18 @@ def pack_int4_tiled(weights: dict, stream=None) -> dict:
     the tiled layout; scales and other entries are passed through.  Done once
     per weight set, before the layer runs with wt="int4_tiled" or
     "mxfp4_tiled"."""
+    return _pack_tiled(weights, 2, _lib.moe_pack_int4_tiled, stream)
+
+
+def pack_mxfp8_tiled(weights: dict, stream=None) -> dict:
+    """Copy of an MXFP8 weight dict with every code tensor (w_*, sh_* of shape
+    [..., N, K], uint8, row-major) rewritten by moe_pack_mxfp8_tiled into the
+    tiled layout; scales and other entries are passed through.  Done once per
+    weight set, before the layer runs with wt="mxfp8_tiled"."""
+    return _pack_tiled(weights, 1, _lib.moe_pack_mxfp8_tiled, stream)
+
+
+def _pack_tiled(weights: dict, per_byte: int, pack, stream) -> dict:
     out = dict(weights)
     for n in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
         t = weights.get(n)
@@ -70,9 +82,9 @@ def pack_int4_tiled(weights: dict, stream=None) -> dict:
             continue
         t = _dev(t)
         if t.dtype != torch.uint8 or t.dim() < 2:
-            raise ValueError(f"{n}: 4-bit codes must be a uint8 tensor [..., N, K/2]")
-        N, K = t.shape[-2], t.shape[-1] * 2
+            raise ValueError(f"{n}: codes must be a uint8 tensor [..., N, K/{per_byte}]")
+        N, K = t.shape[-2], t.shape[-1] * per_byte
         dst = torch.empty_like(t)
-        _lib.moe_pack_int4_tiled(t, dst, t.numel() // (N * (K // 2)), N, K, stream=stream)
+        pack(t, dst, t.numel() // (N * (K // per_byte)), N, K, stream=stream)
         out[n] = dst
     return out

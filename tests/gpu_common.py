@@ -60,10 +60,11 @@ def shape_of(cfg, tau=0, T=None, wt=None):
                           cfg.wt if wt is None else wt, cfg.n_shared, tau)
 
 
-def tiled_inputs(d):
-    """The same inputs with every int4 code tensor packed into the tiled layout
-    (moe_pack_int4_tiled through the C ABI); the oracle keeps reading d."""
-    t = moe.layer.pack_int4_tiled(d)
+def tiled_inputs(d, wt="int4"):
+    """The same inputs with every code tensor packed into the tiled layout
+    (moe_pack_int4_tiled, or moe_pack_mxfp8_tiled for MXFP8 codes, through the
+    C ABI); the oracle keeps reading d."""
+    t = moe.layer.pack_mxfp8_tiled(d) if wt == "mxfp8" else moe.layer.pack_int4_tiled(d)
     torch.cuda.synchronize()
     return t
 

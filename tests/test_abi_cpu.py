@@ -78,6 +78,10 @@ BAD_SHAPES = [
     (dict(act="f32", wt="int4_tiled", F=4096), moe.MOE_EUNSUPPORTED),
     (dict(wt="mxfp4_tiled", d=4096 + 64), moe.MOE_EUNSUPPORTED),    # K not a multiple of 1024
     (dict(wt="mxfp4_tiled", d=4104), moe.MOE_EINVAL),               # not a multiple of 64
+    (dict(wt="mxfp8_tiled", d=4096 + 64), moe.MOE_EUNSUPPORTED),    # K not a multiple of 1024
+    (dict(wt="mxfp8_tiled", F=14336 + 512), moe.MOE_EUNSUPPORTED),  # down K not a multiple of 1024
+    (dict(wt="mxfp8_tiled", d=4104), moe.MOE_EINVAL),               # not a multiple of 64
+    (dict(act="f32", wt="mxfp8_tiled"), moe.MOE_EUNSUPPORTED),
 ]
 
 
@@ -172,6 +176,18 @@ def test_pack_int4_tiled_validation():
             moe.moe_pack_int4_tiled(*args, stream=0)
         assert ei.value.status == moe.MOE_EINVAL, args
     assert moe.moe_pack_int4_tiled(None, None, 0, 16, 128, stream=0) == 0
+
+
+def test_pack_mxfp8_tiled_validation():
+    p, q = 1 << 20, 1 << 30
+    for args in ((p, q, -1, 16, 128), (p, q, 1, 8, 128), (p, q, 1, 24, 128), (p, q, 1, 16, 100),
+                 (p, q, 1, 16, 0), (None, q, 1, 16, 128), (p, None, 1, 16, 128),
+                 (p + 8, q, 1, 16, 128),                 # misaligned
+                 (p, p + 1024, 1, 16, 128)):             # overlapping (2 KB each)
+        with pytest.raises(moe.MoEError) as ei:
+            moe.moe_pack_mxfp8_tiled(*args, stream=0)
+        assert ei.value.status == moe.MOE_EINVAL, args
+    assert moe.moe_pack_mxfp8_tiled(None, None, 0, 16, 128, stream=0) == 0
 
 
 def test_mfma_ceiling_validation():

@@ -140,6 +140,22 @@ def test_quantised_prefill_full(orc, name):
     _check_layer(orc, cfg, d, y, counts, idx, sel=sel)
 
 
+@pytest.mark.parametrize("name,T", [("fine_mxfp4_prefill", 64), ("mixtral_mxfp8_prefill", 8)])
+def test_mx_decode_full(orc, name, T):
+    """The MX layers at decode as the bench times them: the first T tokens of
+    the prefill inputs, the codes packed once into the tiled layout, every
+    group on the skinny matrix-core kernel.  Routing on every token, outputs
+    on every token."""
+    cfg = C[name].replace(name=f"{name}_t{T}", T=T)
+    say(f"full {name} at decode T={T}, tiled codes")
+    d = dict(device_inputs(C[name]))
+    d["x"] = d["x"][:T].contiguous()
+    t = tiled_inputs(d, cfg.wt)
+    y, counts, idx = run_layer(cfg, t, wt=f"{cfg.wt}_tiled")
+    say(f"  active experts {(counts > 0).sum().item()}")
+    _check_layer(orc, cfg, d, y, counts, idx, sel=np.arange(T, dtype=np.int32))
+
+
 def test_stack4_full_teacher_forced(orc):
     """Four pre-norm layers with residual; each layer checked on the GPU's own
     input (teacher forcing), plus the per-layer usage histogram."""

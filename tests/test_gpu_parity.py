@@ -468,18 +468,46 @@ def test_pack_int4_tiled_layout():
     moe.moe_pack_int4_tiled(None, None, 0, 16, 128)
 
 
-TILED = ["int4_mfma_multipass", "int4_mfma_wide_k", "int4_mfma_many", "mxfp4_skinny", "mxfp4_wide_k"]
+def test_pack_mxfp8_tiled_layout():
+    """moe_pack_mxfp8_tiled against the tiled layout as moe.h defines it,
+    written out piece by piece on the host."""
+    for n_mats, N, K in ((3, 48, 256), (1, 16, 384), (2, 128, 1024)):
+        say(f"pack mxfp8 tiled n_mats={n_mats} N={N} K={K}")
+        g = torch.Generator().manual_seed(N + K + 1)
+        src = torch.randint(0, 256, (n_mats, N, K), dtype=torch.uint8, generator=g)
+        dst = torch.full_like(src, 0xA5).to(DEV)
+        moe.moe_pack_mxfp8_tiled(src.to(DEV), dst, n_mats, N, K)
+        torch.cuda.synchronize()
+        got = dst.cpu().numpy().reshape(n_mats, -1)
+        a = src.numpy()
+        want = np.empty_like(got)
+        NG = K // 128
+        for m in range(n_mats):
+            for s_ in range(N // 16):
+                for gi in range(NG):
+                    for w in range(2):
+                        for q in range(4):
+                            for r in range(16):
+                                o = ((s_ * NG + gi) * 128 + 64 * w + 16 * q + r) * 16
+                                c = 128 * gi + 32 * q + 16 * w
+                                want[m, o:o + 16] = a[m, 16 * s_ + r, c:c + 16]
+        assert np.array_equal(got, want)
+    moe.moe_pack_mxfp8_tiled(None, None, 0, 16, 128)
+
+
+TILED = ["int4_mfma_multipass", "int4_mfma_wide_k", "int4_mfma_many", "mxfp4_skinny", "mxfp4_wide_k",
+         "mxfp8_skinny", "mxfp8_skinny_longk"]
 
 
 @pytest.mark.parametrize("name", TILED)
 def test_layer_int4_tiled(orc, name):
-    """Tiled 4-bit codes (int4 or MXFP4): the layer against the oracle (which
+    """Tiled codes (int4, MXFP4 or MXFP8): the layer against the oracle (which
     reads the row-major codes), and bit-identical to the row-major run (same
     arithmetic)."""
     cfg = SMALL[name]
     say(f"layer {cfg.wt} tiled {name}")
     d = device_inputs(cfg)
-    y, counts, idx = run_layer(cfg, tiled_inputs(d), wt=f"{cfg.wt}_tiled")
+    y, counts, idx = run_layer(cfg, tiled_inputs(d, cfg.wt), wt=f"{cfg.wt}_tiled")
     W, S = oracle_weights(d)
     x = np_store(d["x"])
     wr, br = np_store(d["w_router"]), np_store(d["b_router"])
