@@ -56,7 +56,10 @@
 // groups of a row (16 bytes) go out with the weights of the first of them,
 // into a ring of four such chunks.  fp8 codes take two 16-byte loads per
 // group and matrix, so their ring holds 4 steps instead of 8 (the same bytes
-// in flight).
+// in flight).  Row-major fp8 codes give each of those loads 16 rows x four
+// 16-byte pieces 32 bytes apart; their tiled layout (MOE_MXFP8_TILED, written
+// once by moe_pack_mxfp8_tiled) stores each load's 1 KB consecutively, two
+// per group of a 16-row set, which streams ~25% faster at the Mixtral shape.
 #include <type_traits>
 
 #include "common.h"
