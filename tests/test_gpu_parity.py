@@ -524,6 +524,42 @@ def test_layer_int4_tiled(orc, name):
     assert torch.equal(idx, idx_rm) and torch.equal(y, y_rm)
 
 
+@pytest.mark.parametrize("name", ["mxfp4_skinny", "mxfp8_skinny"])
+def test_tiled_edge_cases(orc, name):
+    """Tiled MX codes with a shared expert: T = 0 (counts cleared, nothing
+    else launched with work), T = 1, and every token on the same k experts
+    (groups of all T rows next to empty ones)."""
+    cfg = SMALL[name]
+    wt = f"{cfg.wt}_tiled"
+    say(f"tiled edge cases {name}")
+    d = device_inputs(cfg)
+    t = tiled_inputs(d, cfg.wt)
+    W, S = oracle_weights(d)
+    wr = np_store(d["w_router"])
+    shape = shape_of(cfg, T=0, wt=wt)
+    ws = torch.empty(max(256, moe.moe_workspace_bytes(shape)), dtype=torch.uint8, device=DEV)
+    counts = torch.full((cfg.E,), 5, dtype=torch.int32, device=DEV)
+    moe.moe_layer_forward(shape, d["x"], d["w_router"], d["b_router"], weights_struct(t), None, d["x"],
+                          counts, None, ws)
+    torch.cuda.synchronize()
+    assert (counts.cpu() == 0).all()
+    b = torch.zeros(cfg.E)
+    for j in range(cfg.k):
+        b[j] = 1e3 - 100 * j
+    br = None if d["b_router"] is None else np_store(d["b_router"])
+    for T, bias in ((1, None), (cfg.T, b)):
+        dd = t if bias is None else dict(t, b_router=bias.to(DEV))
+        y, c, i = run_layer(cfg, dd, x=d["x"][:T].contiguous(), wt=wt)
+        if bias is not None:
+            assert c.cpu().tolist()[:cfg.k] == [T] * cfg.k and int(c.sum()) == T * cfg.k
+        y_f, _, _, _ = orc.layer_forward(np_store(d["x"][:T]), cfg.act, cfg.wt, cfg.k, wr,
+                                         br if bias is None else bias.numpy(), W, S,
+                                         forced_idx=i.cpu().numpy())
+        err = tokenwise_rel(np_f64(y), y_f)
+        say(f"  T={T} counts {c.cpu().tolist()} max rel {err.max():.3g}")
+        assert err.max() < TOL[cfg.wt]
+
+
 @pytest.mark.parametrize("name,tau", [("bf16_small_split", 0), ("bf16_prefill_ragged", 0),
                                       ("bf16_prefill_stream", 0), ("bf16_prefill_ragged", 16)])
 def test_layer_matches_steps_bitwise(name, tau):
