@@ -271,7 +271,12 @@ class OracleTimer:
 
 # kernel sources of each workload's expert-FFN step: the committed counter
 # summary is only valid for the sources it was taken on
-TRAFFIC_SOURCES = {"mixtral_decode": ["ffn_gemv.hip", "ffn_skinny.hip", "common.h"], "fine_int4_decode": ["ffn_i4mfma.hip", "common.h"]}
+TRAFFIC_SOURCES = {"mixtral_decode": ["ffn_gemv.hip", "ffn_skinny.hip", "common.h"], "fine_int4_decode": ["ffn_i4mfma.hip", "common.h"],
+                   "fine_mxfp4_decode": ["ffn_i4mfma.hip", "common.h"], "mixtral_mxfp8_decode": ["ffn_i4mfma.hip", "common.h"]}
+
+# the MX layers at decode: the first T tokens of the prefill workload's inputs,
+# the same weights with their codes in the tiled layout
+MX_DECODE = {"fine_mxfp4_decode": ("fine_mxfp4_prefill", 64), "mixtral_mxfp8_decode": ("mixtral_mxfp8_prefill", 8)}
 
 
 def source_digest(key):
@@ -701,7 +706,7 @@ def main():
     ap.add_argument("--workload", default="mixtral_decode",
                     choices=["mixtral_decode", "mixtral_prefill", "fine_int4_decode",
                              "stack4_layer0", "stack4", "fine_int4_prefill", "fine_mxfp4_prefill",
-                             "mixtral_mxfp8_prefill"])
+                             "mixtral_mxfp8_prefill", "fine_mxfp4_decode", "mixtral_mxfp8_decode"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
     ap.add_argument("--no-legs", action="store_true",
                     help="skip the int4 decode and 4-layer stack legs of the default run")
@@ -747,14 +752,18 @@ def main():
         print(json.dumps(out), flush=True)
         return
 
-    name = "stack4" if args.workload == "stack4_layer0" else args.workload
+    name = "stack4" if args.workload == "stack4_layer0" else MX_DECODE.get(args.workload, (args.workload,))[0]
     cfg = moe_inputs.CONFIGS[name]
     if cfg.layers > 1:
         cfg = cfg.replace(layers=1, name="stack4_layer0")
-    if args.tokens > 0:
+    if args.tokens > 0 and args.workload not in MX_DECODE:
         cfg = cfg.replace(name=f"{cfg.name}_t{args.tokens}", T=args.tokens)
     log(f"generating {cfg.name} inputs on the GPU")
     x, wr, br, W = device_layer(cfg)
+    if args.workload in MX_DECODE:
+        # the default run's MX decode leg: the prefill inputs' first T tokens
+        cfg = cfg.replace(name=args.workload, T=MX_DECODE[args.workload][1])
+        x = x[:cfg.T].contiguous()
     wt = cfg.wt
     Wrun = W
     if cfg.wt == "int4" and args.int4_layout == "tiled" and cfg.d % 1024 == 0 and cfg.F % 1024 == 0 \
@@ -845,8 +854,9 @@ def main():
         # and the MX layers at decode (the skinny matrix-core kernel), on the
         # same weights: the fine-grained MXFP4 layer at T = 64, the
         # Mixtral-shaped MXFP8 layer at T = 8
-        for name, Wq, dec in (("fine_int4_prefill", iW, None), ("fine_mxfp4_prefill", None, ("fine_mxfp4_decode", 64)),
-                              ("mixtral_mxfp8_prefill", None, ("mixtral_mxfp8_decode", 8))):
+        for name, Wq, dec in (("fine_int4_prefill", iW, None),
+                              ("fine_mxfp4_prefill", None, ("fine_mxfp4_decode", MX_DECODE["fine_mxfp4_decode"][1])),
+                              ("mixtral_mxfp8_prefill", None, ("mixtral_mxfp8_decode", MX_DECODE["mixtral_mxfp8_decode"][1]))):
             qcfg = moe_inputs.CONFIGS[name]
             log(f"{name}: quantised experts at prefill")
             qx, qwr, qbr, qW = device_layer(qcfg, shared_weights=Wq)
@@ -866,7 +876,7 @@ def main():
                     dW, dwt = pack(qW), f"{qcfg.wt}_tiled"
                     torch.cuda.synchronize()
                 drun = Runner(dcfg, qx[:dT].contiguous(), qwr, qbr, dW, tau=args.tau, wt=dwt)
-                dleg = workload_leg(drun, steps, warmup, args.tau, ceilings)
+                dleg = workload_leg(drun, steps, warmup, args.tau, ceilings, dname if args.tau == 0 else None)
                 out[dname] = leg_summary(dcfg, dleg, steps, warmup)
                 log(json.dumps(out[dname]))
                 del drun, dW
